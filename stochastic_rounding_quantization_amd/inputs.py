@@ -1,0 +1,126 @@
+"""Seeded synthetic inputs for the quantized backward of one linear layer.
+
+This module only draws random numbers and stores them as fp32 or bf16 bit
+patterns.  It holds none of the quantizer's or the GEMMs' arithmetic, so both
+the GPU path and the CPU oracle can be fed from it without sharing any of the
+method.
+
+Distributions follow the workloads of "Efficient Quantization Training with
+Stochastic Rounding via Structured Subspace Randomness": heavy-tailed upstream
+gradients (Introduction: backward gradients are heavy-tailed and span a wide
+dynamic range), Gaussian activations and small Gaussian weights.  The pages
+train on C4 and real checkpoints; these draws stand in for them.
+
+Seeding: every tensor has its own ``numpy.random.default_rng`` stream with
+seed ``1000 * workload_id + k`` (k: G = 1, X = 2, W = 3, A_gate = 4, A_up = 5).
+Values are drawn in float64, rounded to float32, then (where a workload says
+bf16) rounded to bfloat16 with round-to-nearest-even.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+__all__ = [
+    "Workload", "WORKLOADS", "f32_to_bf16_bits", "bf16_bits_to_f32",
+    "student_t", "gaussian", "make_linear_inputs",
+]
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest, ties to even); return uint16 bits."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    bias = np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    out = ((u + bias) >> np.uint32(16)).astype(np.uint16)
+    nan = np.isnan(a)
+    if nan.any():
+        out[nan] = np.uint16(0x7FC0)
+    return out
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Widen bfloat16 bit patterns to float32 (exact)."""
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def student_t(seed: int, shape, nu: float, scale: float) -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    return (scale * rng.standard_t(nu, size=shape)).astype(np.float32)
+
+
+def gaussian(seed: int, shape, std: float) -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    return (std * rng.standard_normal(size=shape)).astype(np.float32)
+
+
+@dataclass(frozen=True)
+class Workload:
+    """One linear layer's backward problem: G [T x D], X [T x d_in], W [D x d_in]."""
+    name: str
+    wid: int                 # seed base: 1000 * wid + k
+    tokens: int              # T
+    d_in: int
+    d_out: int               # D, the hidden dimension of G
+    rows_per_example: int    # S, tokens per example (T % S == 0)
+    dtype: str               # "f32" or "bf16"
+    g_nu: float
+    g_scale: float
+    outlier_frac: float = 0.0    # fraction of tokens scaled by outlier_mult
+    outlier_mult: float = 1.0
+    x_std: float = 1.0
+    w_std: float = 0.02
+    note: str = field(default="", compare=False)
+
+    def scaled(self, tokens: int, d_in: int, d_out: int, rows_per_example: int | None = None,
+               name: str | None = None) -> "Workload":
+        """Same distributions at another shape (for small parity cases)."""
+        return Workload(name or f"{self.name}@{tokens}x{d_in}x{d_out}", self.wid, tokens, d_in, d_out,
+                        rows_per_example or tokens, self.dtype, self.g_nu, self.g_scale,
+                        self.outlier_frac, self.outlier_mult, self.x_std, self.w_std, self.note)
+
+
+WORKLOADS = {
+    # single linear backward, fp32: T=256, d_in=512, d_out=1024
+    "linear-256x512x1024-f32": Workload(
+        "linear-256x512x1024-f32", 1, 256, 512, 1024, 256, "f32", 3.0, 1e-3),
+    # Llama-style FFN down-projection, bf16: T=4096, 11008 -> 4096, 1% outlier tokens x100
+    "down-4096x11008x4096-bf16": Workload(
+        "down-4096x11008x4096-bf16", 2, 4096, 11008, 4096, 4096, "bf16", 2.5, 1e-4,
+        outlier_frac=0.01, outlier_mult=100.0),
+    # Llama-3-8B FFN down-projection, bf16: T=8192 (4 x 2048), 14336 -> 4096
+    "down-8192x14336x4096-bf16": Workload(
+        "down-8192x14336x4096-bf16", 3, 8192, 14336, 4096, 2048, "bf16", 3.0, 1e-4,
+        note="X ~ N(0,1) stands in for the SwiGLU output feeding the down-projection"),
+}
+
+
+def _store(a: np.ndarray, dtype: str) -> np.ndarray:
+    """fp32 -> storage: float32 array, or uint16 bf16 bits."""
+    if dtype == "f32":
+        return np.ascontiguousarray(a, dtype=np.float32)
+    if dtype == "bf16":
+        return f32_to_bf16_bits(a)
+    raise ValueError(dtype)
+
+
+def make_linear_inputs(w: Workload, with_x: bool = True, with_w: bool = True) -> dict:
+    """Draw G, X, W for workload ``w``.
+
+    Returns storage arrays (float32, or uint16 bf16 bit patterns) under keys
+    "G", "X", "W", plus "dtype".
+    """
+    base = 1000 * w.wid
+    T, D, K = w.tokens, w.d_out, w.d_in
+    g = student_t(base + 1, (T, D), w.g_nu, w.g_scale)
+    if w.outlier_frac > 0 and T > 0:
+        rng = np.random.default_rng(base + 6)
+        n = int(round(w.outlier_frac * T))
+        rows = rng.choice(T, n, replace=False)
+        g[rows] *= np.float32(w.outlier_mult)
+    out = {"G": _store(g, w.dtype), "dtype": w.dtype}
+    if with_x:
+        out["X"] = _store(gaussian(base + 2, (T, K), w.x_std), w.dtype)
+    if with_w:
+        out["W"] = _store(gaussian(base + 3, (D, K), w.w_std), w.dtype)
+    return out

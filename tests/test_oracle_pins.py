@@ -1,0 +1,496 @@
+"""Pins for the CPU oracle, against what the pages and mathematics fix (no GPU).
+
+Each test checks an oracle function against something other than itself:
+torch's own Philox engine, exact rational arithmetic, closed forms from the
+pages, library routines (numpy rint, int64 matmul, least squares), brute
+force over every threshold, or Monte-Carlo through the actual Philox draws.
+"""
+import json
+import os
+import shutil
+import subprocess
+import tempfile
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import backward, ec, philox, quantize as oq
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+GOLDEN = json.load(open(os.path.join(HERE, "golden", "worked_example.json")))
+
+
+# ---------------------------------------------------------------- Philox ----
+
+@pytest.fixture(scope="module")
+def torch_philox():
+    """Build tests/philox_torch_ref.cpp against torch's ATen/core/PhiloxRNGEngine.h."""
+    import torch
+    inc = os.path.join(os.path.dirname(torch.__file__), "include")
+    gxx = shutil.which("g++")
+    if gxx is None or not os.path.exists(os.path.join(inc, "ATen", "core", "PhiloxRNGEngine.h")):
+        pytest.skip("g++ or torch's Philox header not available")
+    d = tempfile.mkdtemp()
+    exe = os.path.join(d, "ptr")
+    subprocess.check_call([gxx, "-O1", "-std=c++17", "-I", inc,
+                           os.path.join(HERE, "philox_torch_ref.cpp"), "-o", exe])
+
+    def run(triples):
+        inp = "".join(f"{s} {q} {o}\n" for s, q, o in triples)
+        out = subprocess.run([exe], input=inp, capture_output=True, text=True, check=True).stdout
+        return np.array([[int(w, 16) for w in line.split()] for line in out.strip().splitlines()],
+                        dtype=np.uint32)
+    yield run
+    shutil.rmtree(d, ignore_errors=True)
+
+
+def test_philox_matches_torch_engine(torch_philox):
+    # torch: key = seed, counter[0..1] = offset (block index), counter[2..3] = subsequence.
+    rng = np.random.default_rng(7)
+    triples = [(0, 0, 0), (0, 1, 0), (2**64 - 1, 2**64 - 1, 2**64 - 1), (12345, 3, 2**33 + 5)]
+    triples += [(int(rng.integers(0, 2**63)), int(rng.integers(0, 2**63)), int(rng.integers(0, 2**63)))
+                for _ in range(200)]
+    ref = torch_philox(triples)
+    ctr = np.array([[o & 0xFFFFFFFF, o >> 32, q & 0xFFFFFFFF, q >> 32] for s, q, o in triples],
+                   dtype=np.uint64)
+    got = np.stack([philox.philox4x32_10(ctr[i:i + 1], triples[i][0])[0] for i in range(len(triples))])
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_threshold_maps_use_documented_counters(torch_philox):
+    # SR: element e uses block e>>2 (subsequence layer | tag<<32 with tag 0), word e&3.
+    seed, layer, rows, cols = 99, 5, 3, 10
+    units = philox.sr_threshold_units(seed, layer, rows, cols, row0=2)
+    for t in range(rows):
+        for j in range(cols):
+            e = (t + 2) * cols + j
+            w = torch_philox([(seed, layer, e >> 2)])[0][e & 3]
+            assert units[t, j] == 2 * (int(w) >> 9) + 1
+    # S3R: token t uses block t>>4 with tag 1, word (t>>2)&3, byte t&3, top 7 bits.
+    u = philox.s3r_threshold_units(seed, layer, 40, row0=3)
+    for i in range(40):
+        t = i + 3
+        w = int(torch_philox([(seed, layer | (1 << 32), t >> 4)])[0][(t >> 2) & 3])
+        byte = (w >> (8 * (t & 3))) & 0xFF
+        assert u[i] == 2 * (byte >> 1) + 1
+
+
+def test_philox_bytes_uniform():
+    from scipy import stats
+    w = philox.philox4x32_10(np.stack([np.arange(20000), np.zeros(20000), np.ones(20000) * 3,
+                                       np.zeros(20000)], axis=1).astype(np.uint64), 42)
+    b = w.view(np.uint8).ravel()
+    counts = np.bincount(b, minlength=256)
+    assert stats.chisquare(counts).pvalue > 1e-4
+
+
+# ------------------------------------------------------ rounding operator ----
+
+def _fp32_samples(rng, n):
+    mags = 2.0 ** rng.uniform(-40, 7, n)
+    x = (mags * rng.choice([-1, 1], n)).astype(np.float32)
+    x = np.clip(x, -127.5, 127.5).astype(np.float32)
+    specials = np.array([0.0, -0.0, 1.0, -1.0, 0.5, -0.5, 127.0, -127.0, 2.0 ** -24, -(2.0 ** -24),
+                         2.0 ** -24 - 2.0 ** -48, np.float32(1) - np.float32(2.0 ** -24),
+                         -(2.0 ** -149), 2.0 ** -149, 126.99999], dtype=np.float32)
+    return np.concatenate([x, specials])
+
+
+@pytest.mark.parametrize("bits", [24, 8])
+def test_floor_plus_is_exact_rational_floor(bits):
+    # The page's quantizer Delta*floor(G/Delta + R): check floor(x + r) against exact rationals.
+    rng = np.random.default_rng(bits)
+    x = _fp32_samples(rng, 6000)
+    units = 2 * rng.integers(0, 2 ** (bits - 1), x.size) + 1
+    units[:4] = [1, 2 ** bits - 1, 1, 2 ** bits - 1]
+    r = units.astype(np.float64) / 2.0 ** bits
+    got = oq.floor_plus(x, r)
+    for xi, ui, gi in zip(x, units, got):
+        exact = Fraction(float(xi)) + Fraction(int(ui), 2 ** bits)
+        assert gi == (exact.numerator // exact.denominator), (xi, ui)
+
+
+def test_floor_plus_adversarial_near_integers():
+    # x just below an integer minus r: the float64 sum must not round across the integer.
+    rng = np.random.default_rng(3)
+    for _ in range(4000):
+        u = int(2 * rng.integers(0, 2 ** 23) + 1)
+        n = int(rng.integers(-3, 4))
+        target = Fraction(n) - Fraction(u, 2 ** 24)
+        x0 = np.float32(float(target))
+        for x in (x0, np.nextafter(x0, np.float32(-200)), np.nextafter(x0, np.float32(200))):
+            exact = Fraction(float(x)) + Fraction(u, 2 ** 24)
+            assert oq.floor_plus(np.array([x]), np.array([u / 2 ** 24]))[0] == \
+                exact.numerator // exact.denominator
+
+
+def test_rtne_matches_python_round():
+    # RTNE is Python's round() (ties to even) clamped to the symmetric S8 range.
+    rng = np.random.default_rng(11)
+    x = np.concatenate([rng.uniform(-130, 130, 5000).astype(np.float32),
+                        np.arange(-130, 131).astype(np.float32) + np.float32(0.5)])
+    got = oq.codes_rtne(x)
+    ref = np.array([max(-127, min(127, round(float(v)))) for v in x])
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_dither_equivalence():
+    # S3R page, "Relation to dithering": SR = round-to-nearest after adding the dither (r - 1/2),
+    # except at exact ties.
+    rng = np.random.default_rng(5)
+    x = rng.uniform(-100, 100, 20000).astype(np.float32)
+    u = 2 * rng.integers(0, 128, x.size) + 1
+    r = u / 256.0
+    y = x.astype(np.float64) + (r - 0.5)
+    ties = (y - np.floor(y)) == 0.5
+    assert (~ties).sum() > 19000
+    np.testing.assert_array_equal(oq.floor_plus(x, r)[~ties], np.rint(y)[~ties])
+
+
+# ------------------------------------------------- thresholds and the bias ----
+
+def test_s3r_threshold_grid_bias_bound():
+    # S3R page, "Structured Subspace Randomness": 7-bit thresholds on a half-step-shifted
+    # grid bound the rounding bias by Delta/256.  Enumerate every threshold value.
+    bound = GOLDEN["bounds"]["s3r_threshold_bias"]
+    r_all = (2 * np.arange(128) + 1) / 256.0
+    rng = np.random.default_rng(0)
+    xs = np.concatenate([rng.uniform(-50, 50, 3000), np.linspace(0, 1, 1025)]).astype(np.float32)
+    worst = 0.0
+    for xv in xs:
+        q = oq.floor_plus(np.full(128, xv, np.float32), r_all)
+        worst = max(worst, abs(q.mean() - float(xv)))
+    assert worst <= bound + 1e-12
+    assert worst > bound * 0.9        # the bound is attained on this grid, not loose
+    # every byte value maps onto the 128-point grid, each grid point twice
+    t = philox.s3r_threshold_units(0, 0, 1 << 14)
+    assert set(np.unique(t)) <= set(range(1, 256, 2))
+
+
+def test_worked_example_sr_explainer():
+    # SR explainer, "A worked example": w = 256, g = 0.3: x = 256.3, p = 0.3, RTN -> 256,
+    # SR -> 257 w.p. 0.3, expected 259 after 10 steps.
+    ex = GOLDEN["explainer"]
+    x = np.float32(ex["x"])
+    p_exact = Fraction(float(x)) - 256
+    assert abs(float(p_exact) - ex["p"]) < 1e-4
+    assert float(np.rint(np.float64(x))) == ex["rtn"]
+    # probability of rounding up, by enumerating all 2**23 SR thresholds
+    r_all = (2 * np.arange(2 ** 23, dtype=np.float64) + 1) / 2.0 ** 24
+    up = oq.floor_plus(np.full(r_all.size, x), r_all) - 256
+    assert set(np.unique(up)) == {0.0, 1.0}
+    assert Fraction(int(up.sum()), 2 ** 23) == p_exact     # exactly p on the 23-bit grid
+    # ten steps w <- SR(w + g) through the generator's draws: mean over 4000 trajectories
+    n = 4000
+    w = np.full(n, ex["w"])
+    for step in range(ex["steps"]):
+        r = philox.sr_thresholds(seed=step, layer_id=0, rows=1, cols=n)[0]
+        w = oq.floor_plus((w + np.float32(ex["g"])).astype(np.float32), r)
+    sd = np.sqrt(ex["steps"] * ex["p"] * (1 - ex["p"]) / n)
+    assert abs(w.mean() - ex["expected_after_steps"]) < 4 * sd + 1e-3
+    # S3R's 7-bit grid: P(up) = 38/128, within the Delta/256 bound of p
+    r7 = (2 * np.arange(128) + 1) / 256.0
+    p7 = (oq.floor_plus(np.full(128, x), r7) - 256).mean()
+    assert p7 == 38 / 128 and abs(p7 - float(p_exact)) <= 1 / 256
+
+
+def test_worked_example_in_int8_path():
+    # S3R page: with step 1, 0.3 rounds to 1 w.p. 0.3 (mean 0.3).  A row holding 127 makes
+    # the per-tensor step exactly 1, so x = G' exactly and codes are the rounded values.
+    ex = GOLDEN["s3r_page"]
+    g = np.array([[127.0, np.float32(0.3), np.float32(100.3), -np.float32(0.3)]], np.float32)
+    means = []
+    for seed in range(3000):
+        out = oq.quantize(np.repeat(g, 4, axis=0), "f32", mode=oq.SR, seed=seed)
+        assert out["delta"][0] == np.float32(1.0)
+        means.append(out["Q"].astype(np.float64).mean(axis=0))
+    m = np.mean(means, axis=0)
+    sd = np.sqrt(0.3 * 0.7 / (3000 * 4))
+    assert m[0] == 127
+    assert abs(m[1] - ex["mean"]) < 4 * sd
+    assert abs(m[2] - 100.3) < 4 * sd
+    assert abs(m[3] + 0.3) < 4 * sd
+
+
+# ------------------------------------------------------------ quantizer ----
+
+def _heavy(seed, T, D, scale=1e-3):
+    rng = np.random.default_rng(seed)
+    return (scale * rng.standard_t(3, size=(T, D))).astype(np.float32)
+
+
+@pytest.mark.parametrize("mode", [oq.SR, oq.S3R])
+def test_monte_carlo_unbiased(mode):
+    # S3R page, Lemma 1 / SR explainer "Why it is unbiased": E[Delta*Q] = G' for marginally
+    # uniform thresholds, shared or not; up to Delta/256 on S3R's 7-bit grid.
+    g = _heavy(1, 16, 24)
+    sx = np.random.default_rng(2).uniform(0.5, 2, 16).astype(np.float32)
+    sw = np.random.default_rng(3).uniform(0.5, 2, 24).astype(np.float32)
+    gp = oq.fold(g, sx, sw).astype(np.float64)
+    n = 2500
+    acc = np.zeros_like(gp)
+    for seed in range(n):
+        out = oq.quantize(g, "f32", mode=mode, row_scale=sx, col_scale=sw, seed=seed)
+        acc += out["delta"][0] * out["Q"]
+    mean = acc / n
+    delta = float(out["delta"][0])
+    bias = delta / 256 if mode == oq.S3R else delta * 2.0 ** -24
+    tol = 4.5 * delta * 0.5 / np.sqrt(n) + bias
+    assert np.max(np.abs(mean - gp)) < tol
+
+
+def test_variance_closed_form():
+    # SR explainer, "The variance cost": Var = p(1-p) ulp^2 <= ulp^2/4.
+    p = np.linspace(0.05, 0.95, 19)
+    g = np.concatenate([[127.0], 10 + p]).astype(np.float32)[None, :]
+    G = np.repeat(g, 4096, axis=0)
+    out = oq.quantize(G, "f32", mode=oq.SR, seed=9)
+    q = out["Q"][:, 1:].astype(np.float64)
+    pf = (g[0, 1:].astype(np.float64) - 10)
+    var = q.var(axis=0)
+    np.testing.assert_allclose(var, pf * (1 - pf), atol=4 * 0.25 * np.sqrt(2 / 4096))
+    assert var.max() <= 0.25 + 0.02
+
+
+def test_s3r_direction_structure():
+    # S3R page, "Threshold Broadcasting" / "Broadcasting Makes the Errors Move Together":
+    # under Phi_2D one draw decides the whole token: the rounded-up set is an upper set of
+    # the residual, so equal residuals round the same way.  Independent SR breaks this.
+    rng = np.random.default_rng(4)
+    base = rng.integers(-50, 50, (256, 64)).astype(np.float64)
+    p = rng.choice(np.arange(1, 16) / 16.0, (256, 64))
+    g = np.concatenate([np.full((256, 1), 127.0), base + p], axis=1).astype(np.float32)
+    x = g.astype(np.float64)[:, 1:]
+    res = x - np.floor(x)
+    for mode, expect_monotone in ((oq.S3R, True), (oq.SR, False)):
+        out = oq.quantize(g, "f32", mode=mode, seed=1)
+        up = out["Q"][:, 1:].astype(np.float64) - np.floor(x)
+        monotone = True
+        for t in range(256):
+            order = np.argsort(res[t], kind="stable")
+            u = up[t][order]
+            if np.any(np.diff(u) < 0):
+                monotone = False
+            for v in np.unique(res[t]):
+                if expect_monotone:
+                    assert len(set(up[t][res[t] == v])) == 1
+        assert monotone == expect_monotone
+
+
+def test_shared_threshold_covariance():
+    # S3R page, Lemma 2: residuals spread evenly over [0,1) give Var ~ Delta^2/6 and pairwise
+    # Cov ~ Delta^2/12 under a shared threshold; independent thresholds give Cov ~ 0.
+    D = 32
+    p = (np.arange(D) + 0.5) / D
+    g = np.concatenate([[127.0], 3 + p]).astype(np.float32)[None, :]
+    G = np.repeat(g, 8192, axis=0)
+    for mode, cov_expect in ((oq.S3R, 1 / 12), (oq.SR, 0.0)):
+        out = oq.quantize(G, "f32", mode=mode, seed=2)
+        e = out["Q"][:, 1:].astype(np.float64) - (3 + p)
+        C = np.cov(e, rowvar=False)
+        var_avg = np.mean(np.diag(C))
+        cov_avg = (C.sum() - np.trace(C)) / (D * (D - 1))
+        assert abs(var_avg - 1 / 6) < 0.01
+        assert abs(cov_avg - cov_expect) < 0.01
+
+
+def test_per_tensor_step_and_range():
+    # Delta = max|G'|/127: the element at the max gets code +-127, all codes within [-127, 127].
+    g = _heavy(7, 64, 96)
+    for mode in (oq.RTNE, oq.SR, oq.S3R):
+        out = oq.quantize(g, "f32", mode=mode, seed=3)
+        a = np.max(np.abs(g))
+        assert out["delta"][0] == np.float32(a / np.float32(127))
+        assert np.abs(out["Q"]).max() == 127
+        assert out["Q"].min() >= -127
+
+
+def test_per_token_step():
+    g = _heavy(8, 40, 33)
+    out = oq.quantize(g, "f32", mode=oq.S3R, scale=oq.PER_TOKEN, seed=1)
+    assert out["delta"].shape == (40,)
+    np.testing.assert_array_equal(np.abs(out["Q"]).max(axis=1), 127)
+
+
+def test_forward_operand_rtne_error_bound():
+    # Forward operands: per-row absmax RTNE; |s*Q - X| <= s/2 (+ fp32 rounding) per element.
+    rng = np.random.default_rng(3)
+    X = rng.standard_normal((50, 70)).astype(np.float32)
+    X[3] = 0
+    fo = oq.forward_operand(X, "f32", rows_per_example=10)
+    s = fo["scale"].astype(np.float64)
+    err = np.abs(s[:, None] * fo["Q"] - X)
+    assert np.all(err <= s[:, None] * (0.5 + 1e-5))
+    assert s[3] == 1.0 and not fo["Q"][3].any()
+    np.testing.assert_array_equal(fo["code_colsum"].sum(axis=0), fo["Q"].astype(np.int64).sum(axis=0))
+
+
+def test_flags_nonfinite_and_tiny():
+    g = _heavy(9, 8, 8)
+    g2 = g.copy()
+    g2[2, 3] = np.inf
+    out = oq.quantize(g2, "f32", mode=oq.S3R)
+    assert out["flags"] & oq.FLAG_NONFINITE and not out["Q"].any()
+    out = oq.quantize(g2, "f32", mode=oq.S3R, scale=oq.PER_TOKEN)
+    assert out["row_flags"][2] & oq.FLAG_NONFINITE
+    assert not out["Q"][2].any() and out["Q"][3].any()
+    tiny = np.full((2, 4), 1e-38, np.float32)
+    out = oq.quantize(tiny, "f32", mode=oq.RTNE)
+    assert out["flags"] & oq.FLAG_TINY_STEP and not out["Q"].any()
+    zero = np.zeros((3, 5), np.float32)
+    out = oq.quantize(zero, "f32", mode=oq.SR)
+    assert out["delta"][0] == 1.0 and out["flags"] == 0 and not out["Q"].any()
+
+
+def test_bf16_decode_is_widening():
+    import torch
+    bits = np.random.default_rng(0).integers(0, 2 ** 16, 5000).astype(np.uint16)
+    bits = bits[(bits & 0x7F80) != 0x7F80]          # finite values only
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).float().numpy()
+    np.testing.assert_array_equal(oq.decode(bits, "bf16"), ref)
+
+
+# ------------------------------------------------------------------- EC ----
+
+def test_ec_projection_is_orthogonal_least_squares():
+    # S3R page, "Two-Way Correction": the averages form the orthogonal projection of E_b onto
+    # {1_S a^T + c 1_D^T}.  Compare with a least-squares fit on an explicit basis.
+    rng = np.random.default_rng(6)
+    S, D, B = 6, 5, 3
+    E = rng.standard_normal((B * S, D))
+    eps, ebar, mu = ec.statistics(E, S)
+    P = ec.projection(eps, ebar, mu, S)
+    for b in range(B):
+        basis = []
+        for j in range(D):
+            m = np.zeros((S, D)); m[:, j] = 1; basis.append(m.ravel())
+        for s in range(S):
+            m = np.zeros((S, D)); m[s, :] = 1; basis.append(m.ravel())
+        A = np.stack(basis, axis=1)
+        y = E[b * S:(b + 1) * S].ravel()
+        coef, *_ = np.linalg.lstsq(A, y, rcond=None)
+        np.testing.assert_allclose(P[b * S:(b + 1) * S].ravel(), A @ coef, atol=1e-12)
+    R = E - P
+    np.testing.assert_allclose(R.sum(axis=1), 0, atol=1e-12)                  # every row
+    np.testing.assert_allclose(R.reshape(B, S, D).sum(axis=1), 0, atol=1e-12)  # every column
+    e2, b2, m2 = ec.statistics(P, S)                                            # idempotent
+    np.testing.assert_allclose(ec.projection(e2, b2, m2, S), P, atol=1e-12)
+
+
+def test_theorem1_closed_forms():
+    # S3R page, Theorem 1: centering lowers average variance and average covariance by
+    # Var(mean); for X1 = -Z, X2 = X3 = Z: Var(X1') = 16/9 Var Z, average 8/9 Var Z.
+    M = ec.center(np.eye(3))                     # the centering map as a matrix (rows = outputs)
+    Cz = np.array([[1, -1, -1], [-1, 1, 1], [-1, 1, 1]], float)
+    Cc = M @ Cz @ M.T
+    assert abs(Cc[0, 0] - 16 / 9) < 1e-12
+    assert abs(np.mean(np.diag(Cc)) - 8 / 9) < 1e-12
+    rng = np.random.default_rng(1)
+    for n in (3, 7, 20):
+        L = rng.standard_normal((n, n))
+        C = L @ L.T
+        Mn = ec.center(np.eye(n))
+        Cc = Mn @ C @ Mn.T
+        var_mean = C.sum() / n ** 2
+        avg_var = np.mean(np.diag(C)); avg_var_c = np.mean(np.diag(Cc))
+        off = lambda K: (K.sum() - np.trace(K)) / (n * (n - 1))
+        assert abs((avg_var - avg_var_c) - var_mean) < 1e-9
+        assert abs((off(C) - off(Cc)) - var_mean) < 1e-9
+
+
+# ------------------------------------------------------------ backward ----
+
+def test_int_matmul_exact():
+    rng = np.random.default_rng(2)
+    for (m, k, n) in ((7, 300, 5), (33, 4096, 17)):
+        a = rng.integers(-127, 128, (m, k)).astype(np.int8)
+        b = rng.integers(-127, 128, (k, n)).astype(np.int8)
+        a[0] = 127; b[:, 0] = 127; a[1] = -127
+        np.testing.assert_array_equal(backward.int_matmul(a, b), a.astype(np.int64) @ b.astype(np.int64))
+
+
+def _problem(seed, T, D, K, S, mode=oq.S3R):
+    rng = np.random.default_rng(seed)
+    X = rng.standard_normal((T, K)).astype(np.float32)
+    W = (0.02 * rng.standard_normal((D, K))).astype(np.float32)
+    G = (1e-3 * rng.standard_t(3, (T, D))).astype(np.float32)
+    fx = oq.forward_operand(X, "f32", rows_per_example=S)
+    fw = oq.forward_operand(W, "f32", rows_per_example=D)
+    out = oq.quantize(G, "f32", mode=mode, row_scale=fx["scale"], col_scale=fw["scale"], seed=seed,
+                      rows_per_example=S)
+    E = ec.rounding_error(out["Q"], out["x"], out["delta"])
+    st = ec.statistics(E, S)
+    return dict(G=G, fx=fx, fw=fw, q=out, E=E, st=st, S=S)
+
+
+def test_corrected_gradients_equal_dense_projection_form():
+    # dX_EC = diag(1/s_x) (Delta Q - P(E')) Wq and dW_EC = diag(1/s_w) (Delta Q - P(E'))^T Xq,
+    # with the dense projection; the oracle's factored forms (row sums r_W, input column sums
+    # xs_b, v_b, u_b) must agree.
+    pr = _problem(3, 24, 20, 12, 8)
+    q, fx, fw, S = pr["q"], pr["fx"], pr["fw"], pr["S"]
+    eps, ebar, mu = pr["st"]
+    P = ec.projection(eps, ebar, mu, S)
+    d = float(q["delta"][0])
+    core = d * q["Q"].astype(np.float64) - P
+    # what remains of the corrected gradient's error sums to zero along every row and column
+    remain = core - d * q["x"].astype(np.float64)
+    np.testing.assert_allclose(remain.sum(axis=1), 0, atol=1e-9 * d)
+    np.testing.assert_allclose(remain.reshape(-1, S, remain.shape[1]).sum(axis=1), 0, atol=1e-9 * d)
+    dx_dense = (core @ fw["Q"].astype(np.float64)) / fx["scale"].astype(np.float64)[:, None]
+    dw_dense = (core.T @ fx["Q"].astype(np.float64)) / fw["scale"].astype(np.float64)[:, None]
+    for ecm in (oq.EC_DX_ONLY, oq.EC_TWO_WAY):
+        dx = backward.backward_dx(q["Q"], q["delta"], fw["Q"], fx["scale"], ec=ecm,
+                                  r_W=fw["code_colsum"][0], eps=eps, ebar=ebar, mu=mu,
+                                  rows_per_example=S)
+        np.testing.assert_allclose(dx, dx_dense, rtol=1e-12, atol=1e-12 * np.abs(dx_dense).max())
+    dw = backward.backward_dw(q["Q"], q["delta"], fx["Q"], fw["scale"], ec=oq.EC_TWO_WAY,
+                              xs=fx["code_colsum"], eps=eps, ebar=ebar, mu=mu, rows_per_example=S)
+    np.testing.assert_allclose(dw, dw_dense, rtol=1e-12, atol=1e-12 * np.abs(dw_dense).max())
+    # without correction: Delta Q through the plain products
+    dx0 = backward.backward_dx(q["Q"], q["delta"], fw["Q"], fx["scale"])
+    np.testing.assert_allclose(dx0, (d * q["Q"] @ fw["Q"].astype(np.float64)) / fx["scale"][:, None],
+                               rtol=1e-12)
+    dw0 = backward.backward_dw(q["Q"], q["delta"], fx["Q"], fw["scale"], ec=oq.EC_DX_ONLY)
+    np.testing.assert_allclose(dw0, (d * q["Q"].T.astype(np.float64) @ fx["Q"]) / fw["scale"][:, None],
+                               rtol=1e-12)
+    # sampled rows equal the full result
+    rows = np.array([0, 5, 23])
+    np.testing.assert_array_equal(
+        backward.backward_dx(q["Q"], q["delta"], fw["Q"], fx["scale"], ec=oq.EC_TWO_WAY,
+                             r_W=fw["code_colsum"][0], eps=eps, ebar=ebar, mu=mu,
+                             rows_per_example=S, rows=rows),
+        backward.backward_dx(q["Q"], q["delta"], fw["Q"], fx["scale"], ec=oq.EC_TWO_WAY,
+                             r_W=fw["code_colsum"][0], eps=eps, ebar=ebar, mu=mu,
+                             rows_per_example=S)[rows])
+
+
+def test_corrected_gradients_unbiased_brute_force():
+    # S3R page, "Two-Way Correction": the correction keeps both gradients unbiased.  Enumerate
+    # all 128 x 128 threshold pairs of a 2-token, 3-channel gradient (one example): the mean
+    # corrected dX and dW equal the exact products up to the 7-bit grid's bias.
+    rng = np.random.default_rng(12)
+    T, D, K, S = 2, 3, 4, 2
+    Wq = rng.integers(-127, 128, (D, K)).astype(np.int8)
+    Xq = rng.integers(-127, 128, (T, K)).astype(np.int8)
+    x = np.array([[127.0, -3.3, 0.61], [-12.45, 5.5, -0.2]], np.float32)
+    r_all = (2 * np.arange(128) + 1) / 256.0
+    r_W = Wq.astype(np.int64).sum(axis=0)
+    xs = Xq.astype(np.int64).sum(axis=0)[None]
+    one = np.ones(T, np.float32)
+    dx_sum = np.zeros((T, K)); dw_sum = np.zeros((D, K))
+    for r0 in r_all:
+        for r1 in r_all:
+            q = oq.codes_floor_plus(x, np.array([[r0], [r1]]))
+            E = ec.rounding_error(q, x, np.array([1.0], np.float32))
+            eps, ebar, mu = ec.statistics(E, S)
+            dx_sum += backward.backward_dx(q, np.array([1.0]), Wq, one, ec=oq.EC_TWO_WAY, r_W=r_W,
+                                           eps=eps, ebar=ebar, mu=mu, rows_per_example=S)
+            dw_sum += backward.backward_dw(q, np.array([1.0]), Xq, np.ones(D), ec=oq.EC_TWO_WAY,
+                                           xs=xs, eps=eps, ebar=ebar, mu=mu, rows_per_example=S)
+    n = 128 * 128
+    xd = x.astype(np.float64)
+    bound = 4 / 256
+    assert np.all(np.abs(dx_sum / n - xd @ Wq) <= bound * np.abs(Wq).sum(axis=0)[None] + 1e-9)
+    assert np.all(np.abs(dw_sum / n - xd.T @ Xq) <= bound * np.abs(Xq).sum(axis=0)[None] + 1e-9)
