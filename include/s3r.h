@@ -1,0 +1,184 @@
+/*
+ * s3r.h -- C ABI of libs3r.so: the stochastically rounded INT8 backward pass
+ * of a linear layer on AMD Instinct MI355X (gfx950).
+ *
+ * The method is the one of "Efficient Quantization Training with Stochastic
+ * Rounding via Structured Subspace Randomness" (the S3R page below):
+ *   - section "Quantized Backpropagation with Stochastic Rounding": the
+ *     upstream gradient G [tokens x hidden] is scaled, rounded to S8 and fed
+ *     to two S8 x S8 -> S32 GEMMs, dX = G W^T and dW = X^T G, then rescaled;
+ *     the forward scales s_x (per token) and s_w (per output channel) are
+ *     folded into G, G' = diag(s_x) G diag(s_w), with one step
+ *     Delta = max|G'|/127 and codes Q = SR(G'; R)/Delta (eq. (2)), written
+ *     once for both GEMMs;
+ *   - section "Structured Subspace Randomness": S3R draws one threshold per
+ *     token and shares it across the hidden dimension (Phi_2D);
+ *   - section "Structured Error Correction (S3R-EC)": the per-token and
+ *     per-example per-channel mean rounding errors are subtracted after the
+ *     unchanged GEMMs, from dX and dW (two-way) or from dX only.
+ *
+ * Conventions (all calls):
+ *   - Every tensor pointer is a DEVICE pointer on the current HIP device.
+ *     Matrices are row-major with an explicit leading dimension in ELEMENTS.
+ *   - The caller owns every buffer, including the workspace.  The library
+ *     allocates nothing, never synchronises, and enqueues all work on the
+ *     given stream; results are ready when that stream reaches them.
+ *   - Argument checks happen on the host before anything is enqueued; a
+ *     nonzero return means nothing was enqueued (except S3R_ERR_HIP, which
+ *     reports a launch failure).
+ *   - Calls are stateless and bitwise deterministic: no floating-point
+ *     atomics, all reductions in a fixed order.  Concurrent calls on
+ *     different streams must not share a workspace.
+ *   - Weight layout: W is stored [D x d_in] (PyTorch Linear layout, the
+ *     page's W^T), Wq likewise; X is [T x d_in].
+ */
+#ifndef S3R_H
+#define S3R_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define S3R_OK                0
+#define S3R_ERR_INVALID_ARG  -1  /* null pointer, bad size/leading dim/alignment, T % S != 0 */
+#define S3R_ERR_UNSUPPORTED  -2  /* unsupported dtype / mode / ec / scale combination */
+#define S3R_ERR_WORKSPACE    -3  /* workspace too small */
+#define S3R_ERR_ARCH         -4  /* current device is not gfx950 */
+#define S3R_ERR_HIP          -5  /* a HIP call or kernel launch failed */
+
+/* ---- enums ------------------------------------------------------------- */
+typedef enum { S3R_F32 = 0, S3R_BF16 = 1, S3R_I32_RAW = 2 } s3r_dtype;
+/* Rounding of G' (S3R page, "Compared Configurations"):
+ *   RTNE  deterministic round to nearest even;
+ *   SR    independent SR, one Philox4x32-10 32-bit word per element;
+ *   S3R   one threshold per token shared across the hidden dimension (Phi_2D). */
+typedef enum { S3R_RTNE = 0, S3R_SR = 1, S3R_S3R = 2 } s3r_mode;
+/* S3R-EC (section "Structured Error Correction"): NONE, the dX-only variant,
+ * or the two-way correction of both products.  Requires mode S3R. */
+typedef enum { S3R_EC_NONE = 0, S3R_EC_DX_ONLY = 1, S3R_EC_TWO_WAY = 2 } s3r_ec;
+/* Step granularity.  PER_TENSOR is the page's single step Delta (the only one
+ * the dW GEMM can apply after S32 accumulation).  PER_TOKEN gives one step
+ * per row; it is the forward operands' rule (per-token s_x, per-output-channel
+ * s_w) and is also accepted for G by s3r_quantize and s3r_backward_dx. */
+typedef enum { S3R_PER_TENSOR = 0, S3R_PER_TOKEN = 1 } s3r_scale;
+
+/* Bits OR-ed into the optional device flags word by s3r_quantize. */
+#define S3R_FLAG_NONFINITE  1u  /* an amax was Inf/NaN: affected codes are 0 */
+#define S3R_FLAG_TINY_STEP  2u  /* an amax so small that 127*2^24/amax overflows fp32: codes 0 */
+
+/* Problem descriptor of one quantized tensor G [rows x cols]. */
+typedef struct s3r_qdesc {
+  int64_t  rows;              /* T, tokens (>= 0) */
+  int64_t  cols;              /* D, hidden size of G (>= 0) */
+  int64_t  rows_per_example;  /* S, tokens per example; T % S == 0, S >= 1 */
+  int32_t  mode;              /* s3r_mode */
+  int32_t  ec;                /* s3r_ec */
+  int32_t  scale;             /* s3r_scale */
+  uint32_t layer_id;          /* Philox counter word 2: separates layers */
+  uint64_t seed;              /* Philox key */
+} s3r_qdesc;
+
+/* ---- quantizer ---------------------------------------------------------
+ * s3r_quantize: fold, step, round and (optionally) error statistics.
+ * S3R page, "Quantized Backpropagation with Stochastic Rounding" (eqs. (1),
+ * (2)), "Structured Subspace Randomness" (Phi_2D, 7-bit thresholds on a
+ * half-step grid), "Two-Way Correction" (the two averages of E).
+ *
+ *   G        [T x D] F32 or BF16 (g_dtype), leading dim ld_g >= D.
+ *   row_scale [T] f32 (s_x) or NULL (= 1);  col_scale [D] f32 (s_w) or NULL.
+ *            G'[t,j] = fl(fl(G[t,j] * s_x[t]) * s_w[j]).
+ *   Q        [T x D] int8 codes in [-127, 127], leading dim ld_q >= D.
+ *   delta    [1] (PER_TENSOR) or [T] (PER_TOKEN) f32: Delta = fl(amax/127),
+ *            1 for an all-zero tensor (row).
+ *   code_colsum [B x D] int32 or NULL: per-example column sums of Q
+ *            (B = T/S).  Used by the forward-operand prep to form the
+ *            weight's row sums r_W = Wq^T 1 (S = D rows of W) and the
+ *            per-example input sums xs_b (S tokens of X).
+ *   ec_row [T], ec_col [B x D], ec_mean [B] f32: required iff ec != NONE,
+ *            NULL otherwise.  With E' = Delta_t (q - x), x = G'/Delta:
+ *            ec_row[t] = mean_j E'[t,j]   (eps_t, the token mean),
+ *            ec_col[b,j] = mean_{t in b} E'[t,j]   (the channel means),
+ *            ec_mean[b] = mean over example b of E' (its grand mean).
+ *   flags    device uint32 or NULL: S3R_FLAG_* bits are OR-ed in (the caller
+ *            clears it).
+ *   ws       device workspace of at least s3r_quantize_workspace(desc) bytes,
+ *            256-byte aligned.
+ * Thresholds: SR element (t,j) uses Philox4x32-10 block e>>2 of e = t*D + j
+ * (counter {lo,hi}(e>>2), layer_id, 0; key = seed), word e&3, r =
+ * (2*(w>>9)+1)/2^24; S3R token t uses block t>>4 (counter ..., layer_id, 1),
+ * word (t>>2)&3, byte t&3, r = (2*(byte>>1)+1)/256.  Code = clamp(floor(x+r)).
+ */
+size_t s3r_quantize_workspace(const s3r_qdesc* desc);
+int s3r_quantize(const s3r_qdesc* desc,
+                 const void* G, int32_t g_dtype, int64_t ld_g,
+                 const float* row_scale, const float* col_scale,
+                 int8_t* Q, int64_t ld_q, float* delta,
+                 int32_t* code_colsum,
+                 float* ec_row, float* ec_col, float* ec_mean,
+                 uint32_t* flags,
+                 void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---- backward GEMMs ----------------------------------------------------
+ * Common: Q [T x D] int8 codes with ld_q, delta as written by s3r_quantize
+ * (desc->scale selects [1] or [T]).  INT8 GEMMs on the MFMA units with int32
+ * accumulation.  GEMM operands (Q, Wq, Xq) need 16-byte-aligned base
+ * pointers and leading dims that are multiples of 16; K <= 131072.
+ * out_dt: S3R_F32 (dequantised, corrected per desc->ec) or S3R_I32_RAW (raw
+ * int32 accumulators, no dequantisation, no correction).
+ *
+ * s3r_backward_dx: dX [T x d_in] = diag(1/s_x) (Delta Q - P(E')) Wq.
+ * S3R page, "Quantized Backpropagation" (activation-gradient product) and
+ * "Two-Way Correction" (subtract the averages times W: v_b = ebar_b Wq, and
+ * the token means times the row sums r_W).
+ *   Wq [D x d_in] int8 (ld_w), s_x [T] f32 (NULL = 1),
+ *   r_W [d_in] int32 (required iff ec != NONE), ec_* as from s3r_quantize.
+ *   ws: s3r_backward_workspace(desc, d_in) bytes.
+ */
+int s3r_backward_dx(const s3r_qdesc* desc,
+                    const int8_t* Q, int64_t ld_q, const float* delta,
+                    const int8_t* Wq, int64_t ld_w, int64_t d_in,
+                    const float* s_x, const int32_t* r_W,
+                    const float* ec_row, const float* ec_col, const float* ec_mean,
+                    void* dX, int32_t out_dt, int64_t ld_dx,
+                    void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* s3r_backward_dw: dW [D x d_in] = diag(1/s_w) (Delta Q - P(E'))^T Xq.
+ * S3R page, "Quantized Backpropagation" (weight-gradient product) and
+ * "Two-Way Correction" (subtract the inputs times the same averages:
+ * sum_b ebar_b[j] xs_b[i] + sum_t (eps_t - mu_b) Xq[t,i]).  The correction
+ * applies only for ec == TWO_WAY.  desc->scale must be PER_TENSOR.
+ *   Xq [T x d_in] int8 (ld_x), s_w [D] f32 (NULL = 1),
+ *   xs_b [B x d_in] int32 (required iff ec == TWO_WAY).
+ */
+int s3r_backward_dw(const s3r_qdesc* desc,
+                    const int8_t* Q, int64_t ld_q, const float* delta,
+                    const int8_t* Xq, int64_t ld_x, int64_t d_in,
+                    const float* s_w, const int32_t* xs_b,
+                    const float* ec_row, const float* ec_col, const float* ec_mean,
+                    void* dW, int32_t out_dt, int64_t ld_dw,
+                    void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace for either backward call (the larger of the two). */
+size_t s3r_backward_workspace(const s3r_qdesc* desc, int64_t d_in);
+
+/* ---- measurement aid --------------------------------------------------
+ * s3r_time_next_gemm: record `start` immediately before and `stop` immediately
+ * after the INT8 GEMM kernel launched by the next s3r_backward_dx /
+ * s3r_backward_dw call made on this host thread (on that call's stream), so
+ * hipEventElapsedTime gives that one kernel's duration.  Thread-local; the
+ * request is consumed by that call.  Pass NULLs to cancel.  Returns S3R_OK. */
+int s3r_time_next_gemm(hipEvent_t start, hipEvent_t stop);
+
+/* ---- misc -------------------------------------------------------------- */
+const char* s3r_status_string(int status);
+int s3r_version(void);   /* major*10000 + minor*100 + patch */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* S3R_H */

@@ -1,0 +1,65 @@
+"""The whole backward of one quantized linear layer, composed from the oracle steps.
+
+(Oracle: test use only.)  Order follows the S3R page's pipeline (section
+"Quantized Backpropagation with Stochastic Rounding", Figure 1): forward
+operands X and W are RTNE-quantized per row; the backward folds their scales
+into G, quantizes once, feeds the same codes to both GEMMs and rescales;
+S3R-EC ("Two-Way Correction", "Cost and the dX-Only Variant") subtracts the
+structured part of the rounding error from dX (both variants) and dW (two-way).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import backward, ec as ecm, quantize as oq
+
+
+def forward_operands(X, W, dtype: str, rows_per_example: int):
+    """RTNE per-row quantization of X (per token) and W (per output channel)."""
+    fx = oq.forward_operand(X, dtype, rows_per_example=rows_per_example)
+    fw = oq.forward_operand(W, dtype, rows_per_example=W.shape[0])
+    return fx, fw
+
+
+def quantize_gradient(G, dtype: str, fx, fw, *, mode: int, scale: int, seed: int, layer_id: int,
+                      rows_per_example: int) -> dict:
+    """Quantize G' = diag(s_x) G diag(s_w) once, with the S3R-EC statistics."""
+    q = oq.quantize(G, dtype, mode=mode, scale=scale, row_scale=fx["scale"], col_scale=fw["scale"],
+                    seed=seed, layer_id=layer_id, rows_per_example=rows_per_example)
+    E = ecm.rounding_error(q["Q"], q["x"], q["delta"])
+    q["eps"], q["ebar"], q["mu"] = ecm.statistics(E, rows_per_example)
+    return q
+
+
+def linear_backward(inp: dict, *, mode: int, ec: int, scale: int = oq.PER_TENSOR, seed: int = 0,
+                    layer_id: int = 0, rows_per_example: int, dx_rows=None, dw_rows=None,
+                    fx=None, fw=None) -> dict:
+    """Forward-operand prep, quantizer, dX and dW for the inputs ``inp`` ("G", "X", "W", "dtype").
+
+    dx_rows / dw_rows select output rows (tokens / channels); None computes all.
+    """
+    dtype = inp["dtype"]
+    S = rows_per_example
+    if fx is None or fw is None:
+        fx, fw = forward_operands(inp["X"], inp["W"], dtype, S)
+    q = quantize_gradient(inp["G"], dtype, fx, fw, mode=mode, scale=scale, seed=seed, layer_id=layer_id,
+                          rows_per_example=S)
+    out = {"fx": fx, "fw": fw, "q": q}
+    out["dX"] = backward.backward_dx(q["Q"], q["delta"], fw["Q"], fx["scale"], ec=ec,
+                                     r_W=fw["code_colsum"][0], eps=q["eps"], ebar=q["ebar"], mu=q["mu"],
+                                     rows_per_example=S, rows=dx_rows)
+    if scale == oq.PER_TENSOR:
+        out["dW"] = backward.backward_dw(q["Q"], q["delta"], fx["Q"], fw["scale"], ec=ec, xs=fx["code_colsum"],
+                                         eps=q["eps"], ebar=q["ebar"], mu=q["mu"], rows_per_example=S,
+                                         rows=dw_rows)
+    return out
+
+
+def raw_accumulators(Q, Wq, Xq, dx_rows=None, dw_rows=None):
+    """Exact int32 accumulators of both GEMMs (optionally for a row sample)."""
+    T, D = Q.shape
+    dx_rows = np.arange(T) if dx_rows is None else np.asarray(dx_rows)
+    dw_rows = np.arange(D) if dw_rows is None else np.asarray(dw_rows)
+    acc_dx = backward.int_matmul(Q[dx_rows], Wq)
+    acc_dw = backward.int_matmul(np.ascontiguousarray(Q[:, dw_rows].T), Xq)
+    return acc_dx, acc_dw

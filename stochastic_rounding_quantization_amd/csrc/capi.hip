@@ -1,0 +1,179 @@
+// C ABI of libs3r.so (declared in include/s3r.h): argument checks on the host,
+// then asynchronous launches on the caller's stream.  Nothing here allocates
+// or synchronises.
+#include <string.h>
+
+#include <mutex>
+
+#include "s3r_internal.h"
+
+namespace {
+
+using namespace s3r;
+
+constexpr int64_t kMaxK = 131072;   // int32 accumulators: K * 127^2 < 2^31
+
+bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Current device must be gfx950.  The answer is cached per device id.
+int check_arch() {
+  static std::mutex mu;
+  static int cache[64];  // 0 unknown, 1 ok, 2 not gfx950
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return S3R_ERR_HIP;
+  if (dev < 0 || dev >= 64) return S3R_ERR_ARCH;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cache[dev] == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return S3R_ERR_HIP;
+    cache[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+  }
+  return cache[dev] == 1 ? S3R_OK : S3R_ERR_ARCH;
+}
+
+int check_desc(const s3r_qdesc* d) {
+  if (!d) return S3R_ERR_INVALID_ARG;
+  if (d->rows < 0 || d->cols < 0 || d->rows_per_example < 1) return S3R_ERR_INVALID_ARG;
+  if (d->rows % d->rows_per_example != 0) return S3R_ERR_INVALID_ARG;
+  if (d->rows > (int64_t)1 << 31 || d->cols > (int64_t)1 << 31) return S3R_ERR_INVALID_ARG;
+  if (d->mode < S3R_RTNE || d->mode > S3R_S3R) return S3R_ERR_UNSUPPORTED;
+  if (d->ec < S3R_EC_NONE || d->ec > S3R_EC_TWO_WAY) return S3R_ERR_UNSUPPORTED;
+  if (d->scale != S3R_PER_TENSOR && d->scale != S3R_PER_TOKEN) return S3R_ERR_UNSUPPORTED;
+  return S3R_OK;
+}
+
+int finish(hipError_t e) { return e == hipSuccess ? S3R_OK : S3R_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+size_t s3r_quantize_workspace(const s3r_qdesc* d) {
+  if (check_desc(d) != S3R_OK) return 0;
+  return quant_workspace(d->rows, d->cols, d->rows_per_example, d->ec != S3R_EC_NONE, d->scale, true);
+}
+
+int s3r_quantize(const s3r_qdesc* d, const void* G, int32_t g_dtype, int64_t ld_g, const float* row_scale,
+                 const float* col_scale, int8_t* Q, int64_t ld_q, float* delta, int32_t* code_colsum,
+                 float* ec_row, float* ec_col, float* ec_mean, uint32_t* flags, void* ws, size_t ws_bytes,
+                 hipStream_t stream) {
+  int rc = check_desc(d);
+  if (rc) return rc;
+  if (g_dtype != S3R_F32 && g_dtype != S3R_BF16) return S3R_ERR_UNSUPPORTED;
+  if (d->ec != S3R_EC_NONE && d->mode != S3R_S3R) return S3R_ERR_UNSUPPORTED;
+  const int64_t T = d->rows, D = d->cols;
+  const bool nonempty = T > 0 && D > 0;
+  const int64_t B = T / d->rows_per_example;
+  // a pointer is required exactly when its output is nonempty (empty tensors may be NULL)
+  if (!delta && (d->scale == S3R_PER_TENSOR || T > 0)) return S3R_ERR_INVALID_ARG;
+  if (nonempty && (!G || !Q)) return S3R_ERR_INVALID_ARG;
+  if (ld_g < D || ld_q < D || ld_g < 0 || ld_q < 0) return S3R_ERR_INVALID_ARG;
+  if (d->ec != S3R_EC_NONE) {
+    if ((T > 0 && !ec_row) || (B * D > 0 && !ec_col) || (B > 0 && !ec_mean)) return S3R_ERR_INVALID_ARG;
+  } else if (ec_row || ec_col || ec_mean) {
+    return S3R_ERR_INVALID_ARG;
+  }
+  const size_t need = s3r_quantize_workspace(d);
+  if (ws_bytes < need) return S3R_ERR_WORKSPACE;
+  if (need > 0 && (!ws || ((uintptr_t)ws & 255u))) return S3R_ERR_INVALID_ARG;
+  if ((rc = check_arch())) return rc;
+  QuantArgs a{};
+  a.G = G; a.g_dtype = g_dtype; a.ld_g = ld_g; a.sx = row_scale; a.sw = col_scale;
+  a.Q = Q; a.ld_q = ld_q; a.delta = delta; a.code_colsum = code_colsum;
+  a.ec_row = ec_row; a.ec_col = ec_col; a.ec_mean = ec_mean; a.flags = flags;
+  a.T = T; a.D = D; a.S = d->rows_per_example;
+  a.mode = d->mode; a.ec = d->ec; a.scale = d->scale; a.layer = d->layer_id; a.seed = d->seed;
+  a.ws = (char*)ws;
+  return finish(launch_quantize(a, stream));
+}
+
+size_t s3r_backward_workspace(const s3r_qdesc* d, int64_t d_in) {
+  if (check_desc(d) != S3R_OK || d_in < 0) return 0;
+  const size_t a = dx_workspace(d->rows, d->cols, d_in, d->rows_per_example, d->ec);
+  const size_t b = dw_workspace(d->rows, d->cols, d_in, d->rows_per_example, d->ec);
+  return a > b ? a : b;
+}
+
+static int check_gemm_operand(const int8_t* p, int64_t ld, int64_t cols, bool nonempty) {
+  if (ld < cols || ld < 0) return S3R_ERR_INVALID_ARG;
+  if (nonempty && (!p || !al16(p) || (ld & 15))) return S3R_ERR_INVALID_ARG;
+  return S3R_OK;
+}
+
+int s3r_backward_dx(const s3r_qdesc* d, const int8_t* Q, int64_t ld_q, const float* delta, const int8_t* Wq,
+                    int64_t ld_w, int64_t d_in, const float* s_x, const int32_t* r_W, const float* ec_row,
+                    const float* ec_col, const float* ec_mean, void* dX, int32_t out_dt, int64_t ld_dx, void* ws,
+                    size_t ws_bytes, hipStream_t stream) {
+  int rc = check_desc(d);
+  if (rc) return rc;
+  if (out_dt != S3R_F32 && out_dt != S3R_I32_RAW) return S3R_ERR_UNSUPPORTED;
+  const int64_t T = d->rows, D = d->cols;
+  if (d_in < 0 || D > kMaxK) return S3R_ERR_INVALID_ARG;
+  const bool out_nonempty = T > 0 && d_in > 0;
+  if (!delta || (out_nonempty && !dX) || ld_dx < d_in) return S3R_ERR_INVALID_ARG;
+  if (out_nonempty && ((uintptr_t)dX & 3u)) return S3R_ERR_INVALID_ARG;
+  if ((rc = check_gemm_operand(Q, ld_q, D, T > 0 && D > 0))) return rc;
+  if ((rc = check_gemm_operand(Wq, ld_w, d_in, D > 0 && d_in > 0))) return rc;
+  const bool ec = d->ec != S3R_EC_NONE && out_dt == S3R_F32;
+  if (ec && (!r_W || !ec_row || !ec_col || !ec_mean)) return S3R_ERR_INVALID_ARG;
+  const size_t need = ec ? dx_workspace(T, D, d_in, d->rows_per_example, d->ec) : 0;
+  if (ws_bytes < need || (need && (!ws || ((uintptr_t)ws & 255u)))) return S3R_ERR_WORKSPACE;
+  if ((rc = check_arch())) return rc;
+  DxArgs a{};
+  a.Q = Q; a.ld_q = ld_q; a.delta = delta; a.per_token = d->scale == S3R_PER_TOKEN;
+  a.W = Wq; a.ld_w = ld_w; a.T = T; a.D = D; a.d_in = d_in; a.S = d->rows_per_example;
+  a.sx = s_x; a.rW = r_W; a.ec_row = ec_row; a.ec_col = ec_col; a.ec_mean = ec_mean; a.ec = ec ? d->ec : 0;
+  a.out = dX; a.out_dt = out_dt; a.ld_out = ld_dx; a.ws = (char*)ws;
+  return finish(launch_backward_dx(a, stream));
+}
+
+int s3r_backward_dw(const s3r_qdesc* d, const int8_t* Q, int64_t ld_q, const float* delta, const int8_t* Xq,
+                    int64_t ld_x, int64_t d_in, const float* s_w, const int32_t* xs_b, const float* ec_row,
+                    const float* ec_col, const float* ec_mean, void* dW, int32_t out_dt, int64_t ld_dw, void* ws,
+                    size_t ws_bytes, hipStream_t stream) {
+  int rc = check_desc(d);
+  if (rc) return rc;
+  if (out_dt != S3R_F32 && out_dt != S3R_I32_RAW) return S3R_ERR_UNSUPPORTED;
+  if (d->scale != S3R_PER_TENSOR && out_dt == S3R_F32) return S3R_ERR_UNSUPPORTED;
+  const int64_t T = d->rows, D = d->cols;
+  if (d_in < 0 || T > kMaxK) return S3R_ERR_INVALID_ARG;
+  const bool out_nonempty = D > 0 && d_in > 0;
+  if (!delta || (out_nonempty && !dW) || ld_dw < d_in) return S3R_ERR_INVALID_ARG;
+  if (out_nonempty && ((uintptr_t)dW & 3u)) return S3R_ERR_INVALID_ARG;
+  if ((rc = check_gemm_operand(Q, ld_q, D, T > 0 && D > 0))) return rc;
+  if ((rc = check_gemm_operand(Xq, ld_x, d_in, T > 0 && d_in > 0))) return rc;
+  const bool ec = d->ec == S3R_EC_TWO_WAY && out_dt == S3R_F32;
+  if (ec && (!xs_b || !ec_row || !ec_col || !ec_mean)) return S3R_ERR_INVALID_ARG;
+  const size_t need = ec ? dw_workspace(T, D, d_in, d->rows_per_example, d->ec) : 0;
+  if (ws_bytes < need || (need && (!ws || ((uintptr_t)ws & 255u)))) return S3R_ERR_WORKSPACE;
+  if ((rc = check_arch())) return rc;
+  DwArgs a{};
+  a.Q = Q; a.ld_q = ld_q; a.delta = delta; a.X = Xq; a.ld_x = ld_x;
+  a.T = T; a.D = D; a.d_in = d_in; a.S = d->rows_per_example;
+  a.sw = s_w; a.xs = xs_b; a.ec_row = ec_row; a.ec_col = ec_col; a.ec_mean = ec_mean; a.ec = ec ? d->ec : 0;
+  a.out = dW; a.out_dt = out_dt; a.ld_out = ld_dw; a.ws = (char*)ws;
+  return finish(launch_backward_dw(a, stream));
+}
+
+int s3r_time_next_gemm(hipEvent_t start, hipEvent_t stop) {
+  GemmTiming& t = gemm_timing();
+  t.start = start;
+  t.stop = stop;
+  return S3R_OK;
+}
+
+const char* s3r_status_string(int s) {
+  switch (s) {
+    case S3R_OK: return "ok";
+    case S3R_ERR_INVALID_ARG: return "invalid argument";
+    case S3R_ERR_UNSUPPORTED: return "unsupported combination";
+    case S3R_ERR_WORKSPACE: return "workspace too small";
+    case S3R_ERR_ARCH: return "device is not gfx950";
+    case S3R_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+int s3r_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,517 @@
+// Fused INT8 quantizer of the upstream gradient for gfx950.
+//
+// S3R page, "Quantized Backpropagation with Stochastic Rounding": fold the
+// forward scales into G (G' = diag(s_x) G diag(s_w)), take one step
+// Delta = max|G'|/127 and write the S8 codes Q = SR(G'; R)/Delta once, for
+// both GEMMs.  "Structured Subspace Randomness": S3R shares one threshold per
+// token across the hidden dimension and never materialises R.  "Two-Way
+// Correction": the quantizer knows the rounding error exactly and reduces it
+// to the per-token and per-example per-channel means.
+//
+// Kernels (all HBM-bound for RTNE / S3R / S3R-EC):
+//   amax_tensor  per-tensor max|G'| -> one partial per block       (pass 1)
+//   amax_rows    per-token max|G'| -> step per row                  (pass 1)
+//   quantize     codes + error sums, tile of 64 rows x 512 columns  (pass 2)
+//   finalize_*   fixed-order sums of the per-tile partials          (tiny)
+//
+// Exactness: G' = fl(fl(G*s_x)*s_w), inv = fl(127/amax); the code of
+// floor(x + r) with x = fl(G'*inv) is computed in integers on the 2^-24 grid:
+// X = floor(fl(G'*inv*2^24)), q = (clamp(X) + r*2^24) >> 24.  Scaling by 2^24
+// is exact except where G'*inv is subnormal, and there both forms give the
+// same code.  The build disables FP contraction.
+#include "s3r_internal.h"
+
+namespace s3r {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kRowsPerTile = 64;             // rows of one quantize tile
+constexpr int kColsPerTile = kWave * 8;      // 512 columns: 8 per lane
+constexpr int kAmaxBlocks = 256;
+
+// Load 8 consecutive elements G[row][j0 .. j0+7] as fp32, zero past D.
+template <typename TIn, bool VEC>
+__device__ __forceinline__ void load8(const TIn* __restrict__ row, int64_t j0, int64_t D, float v[8]) {
+  if (VEC && j0 + 8 <= D) {
+    if constexpr (sizeof(TIn) == 2) {
+      const uint4 u = *reinterpret_cast<const uint4*>(row + j0);
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(w[i] << 16);
+        v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+      }
+    } else {
+      const float4 a = *reinterpret_cast<const float4*>(row + j0);
+      const float4 b = *reinterpret_cast<const float4*>(row + j0 + 4);
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+      v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float x = 0.f;
+      if (j0 + i < D) {
+        if constexpr (sizeof(TIn) == 2) x = bf16_to_f32(row[j0 + i]);
+        else x = row[j0 + i];
+      }
+      v[i] = x;
+    }
+  }
+}
+
+__device__ __forceinline__ void load8_scale(const float* __restrict__ sw, int64_t j0, int64_t D,
+                                            bool vec, float v[8]) {
+  if (sw == nullptr) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = 1.f;
+  } else if (vec && j0 + 8 <= D) {
+    const float4 a = *reinterpret_cast<const float4*>(sw + j0);
+    const float4 b = *reinterpret_cast<const float4*>(sw + j0 + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (j0 + i < D) ? sw[j0 + i] : 1.f;
+  }
+}
+
+template <bool VEC>
+__device__ __forceinline__ void store8(int8_t* __restrict__ row, int64_t j0, int64_t D, const int q[8]) {
+  if (VEC && j0 + 8 <= D) {
+    uint2 p;
+    p.x = (uint32_t)(q[0] & 0xFF) | ((uint32_t)(q[1] & 0xFF) << 8) | ((uint32_t)(q[2] & 0xFF) << 16) |
+          ((uint32_t)q[3] << 24);
+    p.y = (uint32_t)(q[4] & 0xFF) | ((uint32_t)(q[5] & 0xFF) << 8) | ((uint32_t)(q[6] & 0xFF) << 16) |
+          ((uint32_t)q[7] << 24);
+    *reinterpret_cast<uint2*>(row + j0) = p;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (j0 + i < D) row[j0 + i] = (int8_t)q[i];
+  }
+}
+
+// |v| as ordered bits: for non-negative floats uint order == float order, and
+// NaN (> 0x7F800000) wins every max, so a NaN anywhere reaches the step.
+__device__ __forceinline__ uint32_t abs_bits(float v) { return __float_as_uint(v) & 0x7FFFFFFFu; }
+
+// Step from amax bits: Delta = fl(a/127), inv = fl(127/a) (a == 0: 1 and 0).
+struct Step { float delta, inv, inv24; uint32_t flag; };
+__device__ __forceinline__ Step make_step(uint32_t abits) {
+  const float a = __uint_as_float(abits);
+  Step s;
+  s.flag = 0;
+  if (abits == 0) { s.delta = 1.f; s.inv = 0.f; s.inv24 = 0.f; return s; }
+  s.delta = __fdiv_rn(a, 127.f);
+  s.inv = __fdiv_rn(127.f, a);
+  s.inv24 = s.inv * 16777216.f;
+  if (!(abits < 0x7F800000u)) s.flag |= S3R_FLAG_NONFINITE;
+  else if (!(__float_as_uint(s.inv24) < 0x7F800000u)) s.flag |= S3R_FLAG_TINY_STEP;
+  return s;
+}
+
+// ---------------------------------------------------------------- pass 1 ----
+template <typename TIn, bool VEC>
+__global__ __launch_bounds__(kThreads) void amax_tensor_kernel(
+    const TIn* __restrict__ G, int64_t ld, int64_t T, int64_t D,
+    const float* __restrict__ sx, const float* __restrict__ sw, uint32_t* __restrict__ part) {
+  const int64_t cpr = (D + 7) / 8;  // 8-element chunks per row
+  uint32_t m = 0;
+  for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
+    const TIn* row = G + t * ld;
+    const float fx = sx ? sx[t] : 1.f;
+    for (int64_t c = threadIdx.x; c < cpr; c += kThreads) {
+      float v[8], s[8];
+      load8<TIn, VEC>(row, c * 8, D, v);
+      load8_scale(sw, c * 8, D, VEC, s);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t b = abs_bits((v[i] * fx) * s[i]);
+        m = m > b ? m : b;
+      }
+    }
+  }
+  __shared__ uint32_t red[kThreads / kWave];
+  m = wave_max_u32(m);
+  if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r = red[0];
+    for (int w = 1; w < kThreads / kWave; ++w) r = r > red[w] ? r : red[w];
+    part[blockIdx.x] = r;
+  }
+}
+
+// Per-token step: one wavefront per row.  Writes amax bits to `abits`, the step
+// to delta[t] and OR-s flags.
+template <typename TIn, bool VEC>
+__global__ __launch_bounds__(kThreads) void amax_rows_kernel(
+    const TIn* __restrict__ G, int64_t ld, int64_t T, int64_t D,
+    const float* __restrict__ sx, const float* __restrict__ sw,
+    uint32_t* __restrict__ abits, float* __restrict__ delta, uint32_t* __restrict__ flags) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t t = (int64_t)blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave;
+  if (t >= T) return;
+  const int64_t cpr = (D + 7) / 8;
+  const TIn* row = G + t * ld;
+  const float fx = sx ? sx[t] : 1.f;
+  uint32_t m = 0;
+  for (int64_t c = lane; c < cpr; c += kWave) {
+    float v[8], s[8];
+    load8<TIn, VEC>(row, c * 8, D, v);
+    load8_scale(sw, c * 8, D, VEC, s);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t b = abs_bits((v[i] * fx) * s[i]);
+      m = m > b ? m : b;
+    }
+  }
+  m = wave_max_u32(m);
+  if (lane == 0) {
+    const Step s = make_step(m);
+    abits[t] = m;
+    delta[t] = (m > 0x7F800000u) ? __uint_as_float(m) : s.delta;
+    if (s.flag && flags) atomicOr(flags, s.flag);
+  }
+}
+
+// ---------------------------------------------------------------- pass 2 ----
+struct QuantTile {
+  int64_t T, D, S, ld_g, ld_q;
+  int tiles_per_example, n_ctiles;
+  uint32_t layer; uint64_t seed;
+};
+
+// MODE: 0 RTNE, 1 SR, 2 S3R.  EC: accumulate rounding errors.  PT: per-token step.
+template <typename TIn, bool VEC, int MODE, bool EC, bool PT, bool COLSUM>
+__global__ __launch_bounds__(kThreads) void quantize_kernel(
+    QuantTile p, const TIn* __restrict__ G, const float* __restrict__ sx, const float* __restrict__ sw,
+    int8_t* __restrict__ Q, float* __restrict__ delta_out, uint32_t* __restrict__ flags,
+    const uint32_t* __restrict__ amax_part, int n_amax_part, const uint32_t* __restrict__ amax_rows,
+    float* __restrict__ row_part, float* __restrict__ col_part, int32_t* __restrict__ colq_part) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int rtile = blockIdx.x;
+  const int ctile = blockIdx.y;
+  const int64_t b = rtile / p.tiles_per_example;
+  const int64_t r0 = b * p.S + (int64_t)(rtile % p.tiles_per_example) * kRowsPerTile;
+  const int64_t r1 = min(r0 + kRowsPerTile, (b + 1) * p.S);
+  const int64_t j0 = (int64_t)ctile * kColsPerTile + lane * 8;
+
+  __shared__ int32_t s_thr[kRowsPerTile];
+  __shared__ uint32_t s_red[kThreads / kWave];
+  __shared__ float s_col[kThreads / kWave][kColsPerTile];
+  __shared__ int32_t s_colq[COLSUM ? kThreads / kWave : 1][COLSUM ? kColsPerTile : 1];
+
+  // per-tensor step from the pass-1 partials (every block reduces them itself)
+  Step st{};
+  if constexpr (!PT) {
+    uint32_t m = 0;
+    for (int i = threadIdx.x; i < n_amax_part; i += kThreads) m = m > amax_part[i] ? m : amax_part[i];
+    m = wave_max_u32(m);
+    if (lane == 0) s_red[wave] = m;
+  }
+  if constexpr (MODE == 2) {
+    if (threadIdx.x < r1 - r0) s_thr[threadIdx.x] = s3r_threshold_units24(r0 + threadIdx.x, p.layer, p.seed);
+  }
+  __syncthreads();
+  if constexpr (!PT) {
+    uint32_t m = s_red[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / kWave; ++w) m = m > s_red[w] ? m : s_red[w];
+    st = make_step(m);
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+      delta_out[0] = (m > 0x7F800000u) ? __uint_as_float(m) : st.delta;
+      if (st.flag && flags) atomicOr(flags, st.flag);
+    }
+  }
+
+  float sw8[8];
+  load8_scale(sw, j0, p.D, VEC, sw8);
+  float col[8];
+  int colq[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) { col[i] = 0.f; colq[i] = 0; }
+
+  for (int64_t t = r0 + wave; t < r1; t += kThreads / kWave) {
+    Step s = st;
+    if constexpr (PT) s = make_step(amax_rows[t]);
+    const float fx = sx ? sx[t] : 1.f;
+    float v[8];
+    if (j0 < p.D) load8<TIn, VEC>(G + t * p.ld_g, j0, p.D, v);
+    else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = 0.f;
+    }
+    int q[8];
+    float e[8];
+    if (s.flag) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) { q[i] = 0; e[i] = 0.f; }
+    } else if constexpr (MODE == 0) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float x = ((v[i] * fx) * sw8[i]) * s.inv;
+        const float r = fminf(fmaxf(__builtin_rintf(x), -127.f), 127.f);
+        q[i] = (int)r;
+        e[i] = (float)q[i] - x;
+      }
+    } else {
+      int32_t R[8];
+      if constexpr (MODE == 2) {
+        const int32_t rt = s_thr[t - r0];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) R[i] = rt;
+      } else {
+        const uint64_t e0 = (uint64_t)t * (uint64_t)p.D + (uint64_t)j0;
+        if ((p.D & 3) == 0) {
+          // elements e0 .. e0+7 with e0 % 4 == 0: exactly two Philox blocks
+          const uint64_t blk = e0 >> 2;
+          const U4 w0 = philox4x32_10((uint32_t)blk, (uint32_t)(blk >> 32), p.layer, kTagSR,
+                                      (uint32_t)p.seed, (uint32_t)(p.seed >> 32));
+          const U4 w1 = philox4x32_10((uint32_t)(blk + 1), (uint32_t)((blk + 1) >> 32), p.layer, kTagSR,
+                                      (uint32_t)p.seed, (uint32_t)(p.seed >> 32));
+          R[0] = sr_units24(w0.x); R[1] = sr_units24(w0.y); R[2] = sr_units24(w0.z); R[3] = sr_units24(w0.w);
+          R[4] = sr_units24(w1.x); R[5] = sr_units24(w1.y); R[6] = sr_units24(w1.z); R[7] = sr_units24(w1.w);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const uint64_t ei = e0 + i;
+            const uint64_t blk = ei >> 2;
+            const U4 w = philox4x32_10((uint32_t)blk, (uint32_t)(blk >> 32), p.layer, kTagSR,
+                                       (uint32_t)p.seed, (uint32_t)(p.seed >> 32));
+            R[i] = sr_units24(u4_word(w, (uint32_t)ei & 3u));
+          }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float x24 = ((v[i] * fx) * sw8[i]) * s.inv24;
+        int32_t X = (int32_t)floorf(x24);
+        X = min(max(X, -(127 << 24)), 127 << 24);
+        q[i] = (X + R[i]) >> 24;
+        e[i] = fmaf(x24, -0x1p-24f, (float)q[i]);
+      }
+    }
+    if (j0 < p.D) store8<VEC>(Q + t * p.ld_q, j0, p.D, q);
+    if constexpr (EC) {
+      float rs = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float ei = (j0 + i < p.D) ? e[i] : 0.f;
+        rs += ei;
+        col[i] += PT ? ei * s.delta : ei;
+      }
+      rs = wave_sum(rs);
+      if (lane == 0) row_part[t * p.n_ctiles + ctile] = rs;
+    }
+    if constexpr (COLSUM) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) colq[i] += q[i];
+    }
+  }
+
+  if constexpr (EC || COLSUM) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if constexpr (EC) s_col[wave][lane * 8 + i] = col[i];
+      if constexpr (COLSUM) s_colq[wave][lane * 8 + i] = colq[i];
+    }
+    __syncthreads();
+    for (int c = threadIdx.x; c < kColsPerTile; c += kThreads) {
+      const int64_t j = (int64_t)ctile * kColsPerTile + c;
+      if (j >= p.D) continue;
+      if constexpr (EC) {
+        float a = s_col[0][c];
+#pragma unroll
+        for (int w = 1; w < kThreads / kWave; ++w) a += s_col[w][c];
+        col_part[(int64_t)rtile * p.D + j] = a;
+      }
+      if constexpr (COLSUM) {
+        int32_t a = s_colq[0][c];
+#pragma unroll
+        for (int w = 1; w < kThreads / kWave; ++w) a += s_colq[w][c];
+        colq_part[(int64_t)rtile * p.D + j] = a;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------- finalize ----
+// Per-example channel means and code column sums: fixed-order sums over the
+// row tiles of each example.
+__global__ __launch_bounds__(kThreads) void finalize_cols_kernel(
+    int64_t B, int64_t D, int64_t S, int tiles_per_example, int per_token,
+    const float* __restrict__ delta, const float* __restrict__ col_part, const int32_t* __restrict__ colq_part,
+    float* __restrict__ ec_col, int32_t* __restrict__ code_colsum) {
+  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (idx >= B * D) return;
+  const int64_t b = idx / D, j = idx % D;
+  if (ec_col) {
+    double a = 0.0;
+    for (int k = 0; k < tiles_per_example; ++k) a += (double)col_part[(b * tiles_per_example + k) * D + j];
+    const double d = per_token ? 1.0 : (double)delta[0];
+    ec_col[idx] = (float)(a * d / (double)S);
+  }
+  if (code_colsum) {
+    int32_t a = 0;
+    for (int k = 0; k < tiles_per_example; ++k) a += colq_part[(b * tiles_per_example + k) * D + j];
+    code_colsum[idx] = a;
+  }
+}
+
+// Token means eps_t and the example's grand mean mu_b: one block per example.
+__global__ __launch_bounds__(kThreads) void finalize_rows_kernel(
+    int64_t D, int64_t S, int n_ctiles, int per_token, const float* __restrict__ delta,
+    const float* __restrict__ row_part, float* __restrict__ ec_row, float* __restrict__ ec_mean) {
+  const int64_t b = blockIdx.x;
+  double acc = 0.0;
+  for (int64_t s = threadIdx.x; s < S; s += kThreads) {
+    const int64_t t = b * S + s;
+    double a = 0.0;
+    for (int k = 0; k < n_ctiles; ++k) a += (double)row_part[t * n_ctiles + k];
+    const double d = per_token ? (double)delta[t] : (double)delta[0];
+    const double eps = D > 0 ? a * d / (double)D : 0.0;
+    ec_row[t] = (float)eps;
+    acc += eps;
+  }
+  __shared__ double red[kThreads];
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int o = kThreads / 2; o > 0; o >>= 1) {
+    if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) ec_mean[b] = (float)(red[0] / (double)S);
+}
+
+// Degenerate shapes (T == 0 or D == 0): steps of 1, zero statistics.
+__global__ void empty_kernel(int64_t T, int64_t D, int64_t B, int per_token, float* delta,
+                             float* ec_row, float* ec_col, float* ec_mean, int32_t* code_colsum) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t nd = per_token ? T : 1;
+  if (i < nd) delta[i] = 1.f;
+  if (ec_row && i < T) ec_row[i] = 0.f;
+  if (ec_mean && i < B) ec_mean[i] = 0.f;
+  if (ec_col && i < B * D) ec_col[i] = 0.f;
+  if (code_colsum && i < B * D) code_colsum[i] = 0;
+}
+
+struct WsLayout {
+  size_t amax_part, amax_rows, row_part, col_part, colq_part, total;
+};
+
+WsLayout ws_layout(int64_t T, int64_t D, int64_t S, int ec, int scale, bool colsum) {
+  WsLayout w{};
+  const int64_t B = S > 0 ? T / S : 0;
+  const int64_t tpe = (S + kRowsPerTile - 1) / kRowsPerTile;
+  const int64_t n_rt = B * tpe;
+  const int64_t n_ct = (D + kColsPerTile - 1) / kColsPerTile;
+  size_t off = 0;
+  w.amax_part = off; off = align_up(off + (scale == S3R_PER_TENSOR ? kAmaxBlocks * 4 : 0), 256);
+  w.amax_rows = off; off = align_up(off + (scale == S3R_PER_TOKEN ? (size_t)T * 4 : 0), 256);
+  w.row_part = off;  off = align_up(off + (ec ? (size_t)T * n_ct * 4 : 0), 256);
+  w.col_part = off;  off = align_up(off + (ec ? (size_t)n_rt * D * 4 : 0), 256);
+  w.colq_part = off; off = align_up(off + (colsum ? (size_t)n_rt * D * 4 : 0), 256);
+  w.total = off;
+  return w;
+}
+
+template <typename TIn, bool VEC, int MODE, bool EC, bool PT, bool COLSUM>
+void launch_q(const QuantArgs& a, const WsLayout& L, const QuantTile& p, dim3 grid, hipStream_t st) {
+  hipLaunchKernelGGL((quantize_kernel<TIn, VEC, MODE, EC, PT, COLSUM>), grid, dim3(kThreads), 0, st, p,
+                     (const TIn*)a.G, a.sx, a.sw, a.Q, a.delta, a.flags,
+                     (const uint32_t*)(a.ws + L.amax_part), kAmaxBlocks, (const uint32_t*)(a.ws + L.amax_rows),
+                     (float*)(a.ws + L.row_part), (float*)(a.ws + L.col_part), (int32_t*)(a.ws + L.colq_part));
+}
+
+template <typename TIn, bool VEC, int MODE, bool EC>
+void dispatch_pt(const QuantArgs& a, const WsLayout& L, const QuantTile& p, dim3 grid, hipStream_t st) {
+  const bool cs = a.code_colsum != nullptr;
+  if (a.scale == S3R_PER_TOKEN) {
+    if (cs) launch_q<TIn, VEC, MODE, EC, true, true>(a, L, p, grid, st);
+    else launch_q<TIn, VEC, MODE, EC, true, false>(a, L, p, grid, st);
+  } else {
+    if (cs) launch_q<TIn, VEC, MODE, EC, false, true>(a, L, p, grid, st);
+    else launch_q<TIn, VEC, MODE, EC, false, false>(a, L, p, grid, st);
+  }
+}
+
+template <typename TIn, bool VEC>
+void dispatch_mode(const QuantArgs& a, const WsLayout& L, const QuantTile& p, dim3 grid, hipStream_t st) {
+  switch (a.mode) {
+    case S3R_RTNE: dispatch_pt<TIn, VEC, 0, false>(a, L, p, grid, st); break;
+    case S3R_SR: dispatch_pt<TIn, VEC, 1, false>(a, L, p, grid, st); break;
+    default:
+      if (a.ec) dispatch_pt<TIn, VEC, 2, true>(a, L, p, grid, st);
+      else dispatch_pt<TIn, VEC, 2, false>(a, L, p, grid, st);
+  }
+}
+
+template <typename TIn, bool VEC>
+void run_quantize(const QuantArgs& a, const WsLayout& L, hipStream_t st) {
+  const TIn* G = (const TIn*)a.G;
+  if (a.scale == S3R_PER_TENSOR) {
+    hipLaunchKernelGGL((amax_tensor_kernel<TIn, VEC>), dim3(kAmaxBlocks), dim3(kThreads), 0, st, G, a.ld_g,
+                       a.T, a.D, a.sx, a.sw, (uint32_t*)(a.ws + L.amax_part));
+  } else {
+    const unsigned nb = (unsigned)((a.T + kThreads / kWave - 1) / (kThreads / kWave));
+    hipLaunchKernelGGL((amax_rows_kernel<TIn, VEC>), dim3(nb), dim3(kThreads), 0, st, G, a.ld_g, a.T, a.D,
+                       a.sx, a.sw, (uint32_t*)(a.ws + L.amax_rows), a.delta, a.flags);
+  }
+  QuantTile p;
+  p.T = a.T; p.D = a.D; p.S = a.S; p.ld_g = a.ld_g; p.ld_q = a.ld_q;
+  p.tiles_per_example = (int)((a.S + kRowsPerTile - 1) / kRowsPerTile);
+  p.n_ctiles = (int)((a.D + kColsPerTile - 1) / kColsPerTile);
+  p.layer = a.layer; p.seed = a.seed;
+  const int64_t B = a.T / a.S;
+  dim3 grid((unsigned)(B * p.tiles_per_example), (unsigned)p.n_ctiles);
+  dispatch_mode<TIn, VEC>(a, L, p, grid, st);
+  if (a.ec || a.code_colsum) {
+    const int64_t n = B * a.D;
+    hipLaunchKernelGGL(finalize_cols_kernel, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+                       st, B, a.D, a.S, p.tiles_per_example, a.scale == S3R_PER_TOKEN ? 1 : 0, a.delta,
+                       (const float*)(a.ws + L.col_part), (const int32_t*)(a.ws + L.colq_part),
+                       a.ec ? a.ec_col : nullptr, a.code_colsum);
+  }
+  if (a.ec) {
+    hipLaunchKernelGGL(finalize_rows_kernel, dim3((unsigned)B), dim3(kThreads), 0, st, a.D, a.S, p.n_ctiles,
+                       a.scale == S3R_PER_TOKEN ? 1 : 0, a.delta, (const float*)(a.ws + L.row_part), a.ec_row,
+                       a.ec_mean);
+  }
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+}  // namespace
+
+size_t quant_workspace(int64_t T, int64_t D, int64_t S, int ec, int scale, bool colsum) {
+  return ws_layout(T, D, S, ec, scale, colsum).total;
+}
+
+hipError_t launch_quantize(const QuantArgs& a, hipStream_t st) {
+  const WsLayout L = ws_layout(a.T, a.D, a.S, a.ec, a.scale, a.code_colsum != nullptr);
+  if (a.T == 0 || a.D == 0) {
+    const int64_t B = a.S > 0 ? a.T / a.S : 0;
+    int64_t n = a.T > 1 ? a.T : 1;
+    if (B * a.D > n) n = B * a.D;
+    hipLaunchKernelGGL(empty_kernel, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0, st, a.T,
+                       a.D, B, a.scale == S3R_PER_TOKEN ? 1 : 0, a.delta, a.ec_row, a.ec_col, a.ec_mean,
+                       a.code_colsum);
+    return hipGetLastError();
+  }
+  const size_t es = a.g_dtype == S3R_BF16 ? 2 : 4;
+  const bool vec = aligned(a.G, 16) && (a.ld_g * (int64_t)es) % 16 == 0 && aligned(a.Q, 8) && a.ld_q % 8 == 0 &&
+                   (a.sw == nullptr || aligned(a.sw, 16));
+  if (a.g_dtype == S3R_BF16) {
+    if (vec) run_quantize<uint16_t, true>(a, L, st);
+    else run_quantize<uint16_t, false>(a, L, st);
+  } else {
+    if (vec) run_quantize<float, true>(a, L, st);
+    else run_quantize<float, false>(a, L, st);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace s3r

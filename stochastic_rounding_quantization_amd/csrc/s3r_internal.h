@@ -1,0 +1,119 @@
+// Internal declarations of libs3r.so: device helpers and kernel launchers.
+// Written for gfx950 (CDNA4): 64-lane wavefronts, MFMA int8, 160 KB LDS.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/s3r.h"
+
+namespace s3r {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- Philox ----
+// Philox4x32-10 (Salmon et al., SC'11): ten rounds of two 32x32->64 products
+// and xors, with the key bumped by the Weyl constants between rounds.
+struct U4 { uint32_t x, y, z, w; };
+
+__device__ __forceinline__ U4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                            uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) { k0 += 0x9E3779B9u; k1 += 0xBB67AE85u; }
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c0 = n0; c1 = (uint32_t)p1; c2 = n2; c3 = (uint32_t)p0;
+  }
+  return U4{c0, c1, c2, c3};
+}
+
+__device__ __forceinline__ uint32_t u4_word(const U4& v, uint32_t i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// Counter tags (word 3 of the counter) separating the threshold streams.
+constexpr uint32_t kTagSR = 0;
+constexpr uint32_t kTagS3R = 1;
+
+// S3R threshold of token t in units of 2^-24: r*2^24 = (2b+1)*2^16, b the top
+// 7 bits of byte t&3 of word (t>>2)&3 of block t>>4.
+__device__ __forceinline__ int32_t s3r_threshold_units24(uint64_t t, uint32_t layer, uint64_t seed) {
+  const uint64_t blk = t >> 4;
+  const U4 v = philox4x32_10((uint32_t)blk, (uint32_t)(blk >> 32), layer, kTagS3R,
+                             (uint32_t)seed, (uint32_t)(seed >> 32));
+  const uint32_t w = u4_word(v, (uint32_t)(t >> 2) & 3u);
+  const uint32_t byte = (w >> (8u * ((uint32_t)t & 3u))) & 0xFFu;
+  return (int32_t)(((byte >> 1) * 2u + 1u) << 16);
+}
+
+// Independent-SR threshold of one 32-bit word, in units of 2^-24: 2*(w>>9)+1.
+__device__ __forceinline__ int32_t sr_units24(uint32_t w) { return (int32_t)(((w >> 9) << 1) | 1u); }
+
+// ------------------------------------------------------------ reductions ----
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) { uint32_t w = __shfl_xor(v, o, kWave); v = v > w ? v : w; }
+  return v;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// ------------------------------------------------------------- launchers ----
+// Quantizer (quantize.hip).
+struct QuantArgs {
+  const void* G; int g_dtype; int64_t ld_g;
+  const float* sx; const float* sw;
+  int8_t* Q; int64_t ld_q;
+  float* delta;
+  int32_t* code_colsum;
+  float* ec_row; float* ec_col; float* ec_mean;
+  uint32_t* flags;
+  int64_t T, D, S;
+  int mode, ec, scale;
+  uint32_t layer; uint64_t seed;
+  char* ws;
+};
+size_t quant_workspace(int64_t T, int64_t D, int64_t S, int ec, int scale, bool colsum);
+hipError_t launch_quantize(const QuantArgs& a, hipStream_t st);
+
+// Backward GEMMs (gemm.hip).
+struct DxArgs {
+  const int8_t* Q; int64_t ld_q; const float* delta; int per_token;
+  const int8_t* W; int64_t ld_w;
+  int64_t T, D, d_in, S;
+  const float* sx; const int32_t* rW;
+  const float* ec_row; const float* ec_col; const float* ec_mean; int ec;
+  void* out; int out_dt; int64_t ld_out;
+  char* ws;
+};
+struct DwArgs {
+  const int8_t* Q; int64_t ld_q; const float* delta;
+  const int8_t* X; int64_t ld_x;
+  int64_t T, D, d_in, S;
+  const float* sw; const int32_t* xs;
+  const float* ec_row; const float* ec_col; const float* ec_mean; int ec;
+  void* out; int out_dt; int64_t ld_out;
+  char* ws;
+};
+// Events to record around the next GEMM launch on this thread (measurement aid).
+struct GemmTiming { hipEvent_t start = nullptr, stop = nullptr; };
+GemmTiming& gemm_timing();
+
+size_t dx_workspace(int64_t T, int64_t D, int64_t d_in, int64_t S, int ec);
+size_t dw_workspace(int64_t T, int64_t D, int64_t d_in, int64_t S, int ec);
+hipError_t launch_backward_dx(const DxArgs& a, hipStream_t st);
+hipError_t launch_backward_dw(const DwArgs& a, hipStream_t st);
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace s3r

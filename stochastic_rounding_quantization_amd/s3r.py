@@ -1,0 +1,261 @@
+"""Thin Python binding of libs3r.so (include/s3r.h).
+
+The functions named ``s3r_*`` mirror the C entry points one to one: they only
+marshal torch tensors (device memory) and the current HIP stream into the C
+call.  Every step of the computation runs in the library's HIP kernels; if the
+library is missing, loading it raises (there is no fallback).
+
+The helpers without the prefix (``quantize``, ``backward_dx``, ``backward_dw``,
+``forward_operand``) allocate outputs and workspaces with torch and then call
+the entry points.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libs3r.so")
+
+S3R_OK = 0
+STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported combination", -3: "workspace too small",
+          -4: "device is not gfx950", -5: "HIP error"}
+S3R_F32, S3R_BF16, S3R_I32_RAW = 0, 1, 2
+RTNE, SR, S3R = 0, 1, 2
+EC_NONE, EC_DX_ONLY, EC_TWO_WAY = 0, 1, 2
+PER_TENSOR, PER_TOKEN = 0, 1
+FLAG_NONFINITE, FLAG_TINY_STEP = 1, 2
+
+EXPORTED = ["s3r_quantize_workspace", "s3r_quantize", "s3r_backward_dx", "s3r_backward_dw",
+            "s3r_backward_workspace", "s3r_time_next_gemm", "s3r_status_string", "s3r_version"]
+
+
+class S3RError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        super().__init__(f"{fn} failed: {STATUS.get(code, code)} ({code})")
+        self.code = code
+
+
+class QDesc(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("rows_per_example", ctypes.c_int64),
+                ("mode", ctypes.c_int32), ("ec", ctypes.c_int32), ("scale", ctypes.c_int32),
+                ("layer_id", ctypes.c_uint32), ("seed", ctypes.c_uint64)]
+
+
+def qdesc(rows, cols, rows_per_example=None, mode=S3R, ec=EC_NONE, scale=PER_TENSOR, layer_id=0, seed=0) -> QDesc:
+    S = rows_per_example if rows_per_example is not None else max(rows, 1)
+    return QDesc(rows, cols, S, mode, ec, scale, layer_id, seed)
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libs3r.so (built in-tree by ``python -m stochastic_rounding_quantization_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run python -m stochastic_rounding_quantization_amd.build")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I64, I32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    DP = ctypes.POINTER(QDesc)
+    L.s3r_quantize_workspace.argtypes = [DP]
+    L.s3r_quantize_workspace.restype = SZ
+    L.s3r_quantize.argtypes = [DP, P, I32, I64, P, P, P, I64, P, P, P, P, P, P, P, SZ, P]
+    L.s3r_quantize.restype = ctypes.c_int
+    L.s3r_backward_dx.argtypes = [DP, P, I64, P, P, I64, I64, P, P, P, P, P, P, I32, I64, P, SZ, P]
+    L.s3r_backward_dx.restype = ctypes.c_int
+    L.s3r_backward_dw.argtypes = [DP, P, I64, P, P, I64, I64, P, P, P, P, P, P, I32, I64, P, SZ, P]
+    L.s3r_backward_dw.restype = ctypes.c_int
+    L.s3r_backward_workspace.argtypes = [DP, I64]
+    L.s3r_backward_workspace.restype = SZ
+    L.s3r_time_next_gemm.argtypes = [P, P]
+    L.s3r_time_next_gemm.restype = ctypes.c_int
+    L.s3r_status_string.argtypes = [ctypes.c_int]
+    L.s3r_status_string.restype = ctypes.c_char_p
+    L.s3r_version.argtypes = []
+    L.s3r_version.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+# ------------------------------------------------------------ marshalling ----
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _ld(t, default=0):
+    if t is None:
+        return default
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError("expected a row-major 2-D tensor (unit column stride)")
+    return t.stride(0)
+
+
+def _stream(stream):
+    if stream is not None:
+        return ctypes.c_void_p(stream)
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check(fn, rc):
+    if rc != S3R_OK:
+        raise S3RError(fn, rc)
+
+
+def _gdtype(t):
+    import torch
+    if t.dtype == torch.float32:
+        return S3R_F32
+    if t.dtype == torch.bfloat16:
+        return S3R_BF16
+    raise ValueError(f"unsupported gradient dtype {t.dtype}")
+
+
+def _odtype(t):
+    import torch
+    if t.dtype == torch.float32:
+        return S3R_F32
+    if t.dtype == torch.int32:
+        return S3R_I32_RAW
+    raise ValueError(f"unsupported output dtype {t.dtype}")
+
+
+def s3r_quantize_workspace(desc: QDesc) -> int:
+    return lib().s3r_quantize_workspace(ctypes.byref(desc))
+
+
+def s3r_quantize(desc: QDesc, G, row_scale, col_scale, Q, delta, code_colsum=None, ec_row=None, ec_col=None,
+                 ec_mean=None, flags=None, ws=None, stream=None, *, rc_only=False):
+    rc = lib().s3r_quantize(ctypes.byref(desc), _ptr(G), _gdtype(G) if G is not None else S3R_F32,
+                            _ld(G, desc.cols), _ptr(row_scale), _ptr(col_scale), _ptr(Q), _ld(Q, desc.cols),
+                            _ptr(delta), _ptr(code_colsum), _ptr(ec_row), _ptr(ec_col), _ptr(ec_mean),
+                            _ptr(flags), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                            _stream(stream))
+    if rc_only:
+        return rc
+    _check("s3r_quantize", rc)
+
+
+def s3r_backward_workspace(desc: QDesc, d_in: int) -> int:
+    return lib().s3r_backward_workspace(ctypes.byref(desc), d_in)
+
+
+def s3r_backward_dx(desc: QDesc, Q, delta, Wq, s_x, r_W, ec_row, ec_col, ec_mean, dX, ws=None, stream=None,
+                    *, rc_only=False):
+    d_in = dX.shape[1]
+    rc = lib().s3r_backward_dx(ctypes.byref(desc), _ptr(Q), _ld(Q, desc.cols), _ptr(delta), _ptr(Wq),
+                               _ld(Wq, d_in), d_in, _ptr(s_x), _ptr(r_W), _ptr(ec_row), _ptr(ec_col),
+                               _ptr(ec_mean), _ptr(dX), _odtype(dX), _ld(dX, d_in), _ptr(ws),
+                               0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+    if rc_only:
+        return rc
+    _check("s3r_backward_dx", rc)
+
+
+def s3r_backward_dw(desc: QDesc, Q, delta, Xq, s_w, xs_b, ec_row, ec_col, ec_mean, dW, ws=None, stream=None,
+                    *, rc_only=False):
+    d_in = dW.shape[1]
+    rc = lib().s3r_backward_dw(ctypes.byref(desc), _ptr(Q), _ld(Q, desc.cols), _ptr(delta), _ptr(Xq),
+                               _ld(Xq, d_in), d_in, _ptr(s_w), _ptr(xs_b), _ptr(ec_row), _ptr(ec_col),
+                               _ptr(ec_mean), _ptr(dW), _odtype(dW), _ld(dW, d_in), _ptr(ws),
+                               0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+    if rc_only:
+        return rc
+    _check("s3r_backward_dw", rc)
+
+
+def s3r_time_next_gemm(start_event, stop_event) -> None:
+    """Record two torch.cuda.Event objects around the next GEMM kernel launched from this thread."""
+    _check("s3r_time_next_gemm", lib().s3r_time_next_gemm(
+        ctypes.c_void_p(start_event.cuda_event) if start_event is not None else None,
+        ctypes.c_void_p(stop_event.cuda_event) if stop_event is not None else None))
+
+
+def s3r_version() -> int:
+    return lib().s3r_version()
+
+
+def s3r_status_string(code: int) -> str:
+    return lib().s3r_status_string(code).decode()
+
+
+# ------------------------------------------------------ allocating helpers ----
+
+def _pad16(n: int) -> int:
+    return (n + 15) // 16 * 16
+
+
+def _workspace(nbytes: int, device):
+    import torch
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device) if nbytes else None
+
+
+def q_buffer(rows: int, cols: int, device):
+    """int8 [rows x cols] view with a leading dimension padded to 16 (what the GEMMs need)."""
+    import torch
+    return torch.empty(rows, _pad16(cols), dtype=torch.int8, device=device)[:, :cols]
+
+
+@dataclass
+class Quantized:
+    Q: object            # int8 [T x D] (leading dim padded to 16)
+    delta: object        # f32 [1] or [T]
+    desc: QDesc
+    code_colsum: object = None
+    ec_row: object = None
+    ec_col: object = None
+    ec_mean: object = None
+    flags: object = None
+
+
+def quantize(G, *, mode=S3R, ec=EC_NONE, scale=PER_TENSOR, row_scale=None, col_scale=None, seed=0, layer_id=0,
+             rows_per_example=None, colsum=False, stream=None) -> Quantized:
+    import torch
+    T, D = G.shape
+    desc = qdesc(T, D, rows_per_example, mode, ec, scale, layer_id, seed)
+    dev = G.device
+    S = desc.rows_per_example
+    B = T // S
+    Q = q_buffer(T, D, dev)
+    delta = torch.empty(T if scale == PER_TOKEN else 1, dtype=torch.float32, device=dev)
+    cs = torch.empty(B, D, dtype=torch.int32, device=dev) if colsum else None
+    e_r = e_c = e_m = None
+    if ec != EC_NONE:
+        e_r = torch.empty(T, dtype=torch.float32, device=dev)
+        e_c = torch.empty(B, D, dtype=torch.float32, device=dev)
+        e_m = torch.empty(B, dtype=torch.float32, device=dev)
+    flags = torch.zeros(1, dtype=torch.int32, device=dev)
+    ws = _workspace(s3r_quantize_workspace(desc), dev)
+    s3r_quantize(desc, G, row_scale, col_scale, Q, delta, cs, e_r, e_c, e_m, flags, ws, stream)
+    return Quantized(Q, delta, desc, cs, e_r, e_c, e_m, flags)
+
+
+def forward_operand(X, rows_per_example=None, stream=None) -> Quantized:
+    """Per-row absmax RTNE of a forward operand (X per token, W per output channel) with code column sums."""
+    return quantize(X, mode=RTNE, ec=EC_NONE, scale=PER_TOKEN, rows_per_example=rows_per_example, colsum=True,
+                    stream=stream)
+
+
+def backward_dx(q: Quantized, Wq, s_x=None, r_W=None, out_dtype=None, stream=None):
+    import torch
+    d_in = Wq.shape[1]
+    T = q.desc.rows
+    dX = torch.empty(T, d_in, dtype=out_dtype or torch.float32, device=Wq.device)
+    ws = _workspace(s3r_backward_workspace(q.desc, d_in), Wq.device)
+    s3r_backward_dx(q.desc, q.Q, q.delta, Wq, s_x, r_W, q.ec_row, q.ec_col, q.ec_mean, dX, ws, stream)
+    return dX
+
+
+def backward_dw(q: Quantized, Xq, s_w=None, xs_b=None, out_dtype=None, stream=None):
+    import torch
+    d_in = Xq.shape[1]
+    D = q.desc.cols
+    dW = torch.empty(D, d_in, dtype=out_dtype or torch.float32, device=Xq.device)
+    ws = _workspace(s3r_backward_workspace(q.desc, d_in), Xq.device)
+    s3r_backward_dw(q.desc, q.Q, q.delta, Xq, s_w, xs_b, q.ec_row, q.ec_col, q.ec_mean, dW, ws, stream)
+    return dW

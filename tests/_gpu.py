@@ -1,0 +1,52 @@
+"""Helpers for the GPU parity tests: host <-> device conversion and the GPU pipeline.
+
+The GPU side goes only through the C ABI (via the thin binding); expected values
+come only from oracle/.
+"""
+import numpy as np
+import torch
+
+from stochastic_rounding_quantization_amd import s3r
+
+DEV = torch.device("cuda:0")
+
+
+def to_dev(a: np.ndarray, dtype: str) -> torch.Tensor:
+    """Storage array (float32 or uint16 bf16 bits) -> device tensor of that dtype."""
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(DEV)
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().numpy()
+
+
+def rel_err(got, exp) -> float:
+    got = np.asarray(got, np.float64)
+    exp = np.asarray(exp, np.float64)
+    scale = np.abs(exp).max() if exp.size else 0.0
+    return float(np.abs(got - exp).max() / scale) if scale > 0 else float(np.abs(got - exp).max() if got.size else 0)
+
+
+def gpu_linear(inp: dict, *, mode, ec, scale=s3r.PER_TENSOR, seed=0, layer_id=0, rows_per_example, dw=True):
+    """Forward-operand prep + quantize + dX (+ dW) on the GPU through the C ABI."""
+    dt = inp["dtype"]
+    G, X, W = to_dev(inp["G"], dt), to_dev(inp["X"], dt), to_dev(inp["W"], dt)
+    S = rows_per_example
+    fx = s3r.forward_operand(X, rows_per_example=S)
+    fw = s3r.forward_operand(W, rows_per_example=W.shape[0])
+    q = s3r.quantize(G, mode=mode, ec=ec, scale=scale, row_scale=fx.delta, col_scale=fw.delta, seed=seed,
+                     layer_id=layer_id, rows_per_example=S)
+    dX = s3r.backward_dx(q, fw.Q, s_x=fx.delta, r_W=fw.code_colsum[0])
+    dW = s3r.backward_dw(q, fx.Q, s_w=fw.delta, xs_b=fx.code_colsum) if dw else None
+    torch.cuda.synchronize()
+    return {"fx": fx, "fw": fw, "q": q, "dX": dX, "dW": dW}
+
+
+def assert_nan_equal(got, exp, what=""):
+    got = np.asarray(got)
+    exp = np.asarray(exp)
+    both_nan = np.isnan(got) & np.isnan(exp)
+    ok = (got == exp) | both_nan
+    assert ok.all(), f"{what}: {int((~ok).sum())} mismatches, first at {np.argwhere(~ok)[:3].tolist()}"

@@ -1,0 +1,263 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, on an MI355X.
+
+Bars: bit-exact INT8 codes, steps, code column sums and int32 accumulators;
+dequantised / corrected dX and dW within 1e-5 of the oracle relative to the
+largest oracle magnitude of the tensor; S3R-EC statistics (fp32 on the GPU,
+fp64 in the oracle) within 1e-5 of their largest magnitude.
+Small cases cover several tiles and ragged tails; the workload-size cases run
+in the launch configuration bench.py times and compare sampled output rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import backward, pipeline, quantize as oq
+from stochastic_rounding_quantization_amd import inputs, s3r
+from tests._gpu import DEV, assert_nan_equal, gpu_linear, host, rel_err, to_dev
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-5
+MODES = [(s3r.RTNE, s3r.EC_NONE), (s3r.SR, s3r.EC_NONE), (s3r.S3R, s3r.EC_NONE),
+         (s3r.S3R, s3r.EC_DX_ONLY), (s3r.S3R, s3r.EC_TWO_WAY)]
+
+
+def _rand_i8(rng, shape):
+    a = rng.integers(-127, 128, shape).astype(np.int8)
+    if a.size:
+        a.flat[0] = 127
+        a.flat[-1] = -127
+    return a
+
+
+def _padded_i8(a: np.ndarray) -> torch.Tensor:
+    r, c = a.shape
+    buf = torch.zeros(r, (c + 15) // 16 * 16 + 16, dtype=torch.int8, device=DEV)
+    v = buf[:, :c]
+    v.copy_(torch.from_numpy(a))
+    return v
+
+
+# ------------------------------------------------------------- GEMMs ----
+
+@pytest.mark.parametrize("M,N,K", [(256, 256, 64), (1, 17, 3), (300, 520, 200), (512, 768, 1024),
+                                   (257, 255, 4100)])
+def test_gemm_raw_accumulators_exact(M, N, K):
+    rng = np.random.default_rng(M * 7 + N * 3 + K)
+    # dX-shaped: Q [M x K] . Wq [K x N]
+    Q = _rand_i8(rng, (M, K))
+    Wq = _rand_i8(rng, (K, N))
+    d = s3r.qdesc(M, K, M, s3r.S3R, s3r.EC_NONE)
+    delta = torch.ones(1, device=DEV)
+    out = torch.full((M, N), -7, dtype=torch.int32, device=DEV)
+    s3r.s3r_backward_dx(d, _padded_i8(Q), delta, _padded_i8(Wq), None, None, None, None, None, out)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(out), backward.int_matmul(Q, Wq))
+    # dW-shaped: Q^T with Q [K x M] . Xq [K x N]
+    Qt = _rand_i8(rng, (K, M))
+    Xq = _rand_i8(rng, (K, N))
+    d = s3r.qdesc(K, M, K, s3r.S3R, s3r.EC_NONE)
+    out = torch.full((M, N), -7, dtype=torch.int32, device=DEV)
+    s3r.s3r_backward_dw(d, _padded_i8(Qt), delta, _padded_i8(Xq), None, None, None, None, None, out)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(out), backward.int_matmul(np.ascontiguousarray(Qt.T), Xq))
+
+
+def test_gemm_output_leading_dim_and_extremes():
+    # all +-127 operands at the int32 bound region, output written with a padded leading dim
+    M, N, K = 96, 80, 4096
+    Q = np.full((M, K), 127, np.int8)
+    Q[1::2] = -127
+    Wq = np.full((K, N), -127, np.int8)
+    d = s3r.qdesc(M, K, M)
+    buf = torch.full((M, N + 13), 5, dtype=torch.int32, device=DEV)
+    s3r.s3r_backward_dx(d, _padded_i8(Q), torch.ones(1, device=DEV), _padded_i8(Wq), None, None, None, None, None,
+                        buf[:, :N])
+    torch.cuda.synchronize()
+    got = host(buf)
+    np.testing.assert_array_equal(got[:, :N], backward.int_matmul(Q, Wq))
+    assert (got[:, N:] == 5).all()
+
+
+# --------------------------------------------------------- quantizer ----
+
+QCASES = [  # (T, D, S, dtype)
+    (256, 1024, 256, "f32"),
+    (64, 100, 32, "bf16"),     # D % 8 != 0: partial last chunk
+    (33, 77, 33, "f32"),       # D % 4 != 0: SR per-element Philox path
+    (1, 1, 1, "bf16"),
+    (192, 600, 64, "bf16"),    # three examples, two column tiles
+]
+
+
+def _grad(T, D, dtype, seed):
+    g = inputs.student_t(seed, (T, D), 3.0, 1e-3)
+    rng = np.random.default_rng(seed)
+    if T > 4:
+        g[rng.choice(T, max(1, T // 50), replace=False)] *= 100
+    sx = rng.uniform(0.01, 0.05, T).astype(np.float32)
+    sw = rng.uniform(1e-4, 5e-4, D).astype(np.float32)
+    store = inputs.f32_to_bf16_bits(g) if dtype == "bf16" else g
+    return store, sx, sw
+
+
+@pytest.mark.parametrize("T,D,S,dtype", QCASES)
+@pytest.mark.parametrize("scale", [s3r.PER_TENSOR, s3r.PER_TOKEN])
+def test_quantize_bit_exact(T, D, S, dtype, scale):
+    store, sx, sw = _grad(T, D, dtype, T * 131 + D)
+    G = to_dev(store, dtype)
+    for mode, ec in MODES:
+        seed, layer = 12345 + mode, 3
+        q = s3r.quantize(G, mode=mode, ec=ec, scale=scale, row_scale=torch.from_numpy(sx).to(DEV),
+                         col_scale=torch.from_numpy(sw).to(DEV), seed=seed, layer_id=layer, rows_per_example=S,
+                         colsum=True)
+        torch.cuda.synchronize()
+        ref = oq.quantize(store, dtype, mode=mode, scale=scale, row_scale=sx, col_scale=sw, seed=seed,
+                          layer_id=layer, rows_per_example=S)
+        tag = f"T={T} D={D} {dtype} mode={mode} ec={ec} scale={scale}"
+        np.testing.assert_array_equal(host(q.Q), ref["Q"], err_msg=tag)
+        np.testing.assert_array_equal(host(q.delta), ref["delta"], err_msg=tag)
+        np.testing.assert_array_equal(host(q.code_colsum), ref["code_colsum"], err_msg=tag)
+        assert int(host(q.flags)[0]) == ref["flags"], tag
+        if ec != s3r.EC_NONE:
+            from oracle import ec as oec
+            E = oec.rounding_error(ref["Q"], ref["x"], ref["delta"])
+            eps, ebar, mu = oec.statistics(E, S)
+            assert rel_err(host(q.ec_row), eps) <= TOL, tag
+            assert rel_err(host(q.ec_col), ebar) <= TOL, tag
+            assert np.abs(host(q.ec_mean) - mu).max() <= TOL * np.abs(E).max(), tag
+
+
+def test_quantize_strided_and_unaligned():
+    # G with a padded leading dim, Q written into a padded buffer; then the scalar path (odd ld).
+    T, D = 40, 72
+    store, sx, sw = _grad(T, D, "f32", 5)
+    ref = oq.quantize(store, "f32", mode=s3r.S3R, seed=9, rows_per_example=T)
+    for pad in (8, 3):
+        Gbuf = torch.zeros(T, D + pad, dtype=torch.float32, device=DEV)
+        Gbuf[:, :D] = torch.from_numpy(store)
+        Qbuf = torch.full((T, D + pad + 1), 99, dtype=torch.int8, device=DEV)
+        d = s3r.qdesc(T, D, T, s3r.S3R, s3r.EC_NONE, seed=9)
+        delta = torch.empty(1, device=DEV)
+        ws = torch.empty(max(s3r.s3r_quantize_workspace(d), 1), dtype=torch.uint8, device=DEV)
+        s3r.s3r_quantize(d, Gbuf[:, :D], None, None, Qbuf[:, :D], delta, ws=ws)
+        torch.cuda.synchronize()
+        got = host(Qbuf)
+        np.testing.assert_array_equal(got[:, :D], ref["Q"])
+        assert (got[:, D:] == 99).all()
+
+
+def test_quantize_degenerate_inputs():
+    dev = DEV
+    # empty tensors
+    for T, D in ((0, 16), (16, 0)):
+        G = torch.zeros(T, D, device=dev)
+        q = s3r.quantize(G, mode=s3r.S3R, ec=s3r.EC_TWO_WAY, rows_per_example=max(T, 1), colsum=True)
+        torch.cuda.synchronize()
+        assert host(q.delta)[0] == 1.0
+        if T:
+            assert not host(q.ec_row).any()
+    # all-zero, NaN, Inf, tiny amax: flags and zero codes, as the oracle
+    base = inputs.student_t(3, (24, 40), 3.0, 1e-3)
+    cases = {"zero": np.zeros((24, 40), np.float32), "nan": base.copy(), "inf": base.copy(),
+             "tiny": np.full((24, 40), 1e-38, np.float32)}
+    cases["nan"][3, 5] = np.nan
+    cases["inf"][7, 1] = -np.inf
+    for name, g in cases.items():
+        for scale in (s3r.PER_TENSOR, s3r.PER_TOKEN):
+            for mode in (s3r.RTNE, s3r.SR, s3r.S3R):
+                q = s3r.quantize(to_dev(g, "f32"), mode=mode, scale=scale, seed=1, rows_per_example=24)
+                torch.cuda.synchronize()
+                ref = oq.quantize(g, "f32", mode=mode, scale=scale, seed=1, rows_per_example=24)
+                tag = f"{name} scale={scale} mode={mode}"
+                np.testing.assert_array_equal(host(q.Q), ref["Q"], err_msg=tag)
+                assert_nan_equal(host(q.delta), ref["delta"], tag)
+                assert int(host(q.flags)[0]) == ref["flags"], tag
+
+
+def test_deterministic():
+    store, sx, sw = _grad(512, 1024, "bf16", 77)
+    G = to_dev(store, "bf16")
+    outs = []
+    for _ in range(2):
+        q = s3r.quantize(G, mode=s3r.S3R, ec=s3r.EC_TWO_WAY, rows_per_example=128, seed=4)
+        W = _padded_i8(_rand_i8(np.random.default_rng(1), (1024, 384)))
+        dX = s3r.backward_dx(q, W, r_W=torch.zeros(384, dtype=torch.int32, device=DEV))
+        torch.cuda.synchronize()
+        outs.append([host(q.Q), host(q.ec_row), host(q.ec_col), host(q.ec_mean), host(dX)])
+    for a, b in zip(*outs):
+        np.testing.assert_array_equal(a.view(np.uint8) if a.dtype == np.int8 else a.view(np.uint32),
+                                      b.view(np.uint8) if b.dtype == np.int8 else b.view(np.uint32))
+
+
+# -------------------------------------------------------- end to end ----
+
+def _check_linear(inp, S, mode, ec, scale=s3r.PER_TENSOR, dx_rows=None, dw_rows=None, seed=0, layer=0):
+    gpu = gpu_linear(inp, mode=mode, ec=ec, scale=scale, seed=seed, layer_id=layer, rows_per_example=S,
+                     dw=(scale == s3r.PER_TENSOR))
+    tag = f"mode={mode} ec={ec} scale={scale}"
+    fx, fw = pipeline.forward_operands(inp["X"], inp["W"], inp["dtype"], S)
+    # forward-operand prep (a0): codes, row steps, column sums bit-exact
+    np.testing.assert_array_equal(host(gpu["fx"].Q), fx["Q"])
+    np.testing.assert_array_equal(host(gpu["fx"].delta), fx["scale"])
+    np.testing.assert_array_equal(host(gpu["fx"].code_colsum), fx["code_colsum"])
+    np.testing.assert_array_equal(host(gpu["fw"].Q), fw["Q"])
+    np.testing.assert_array_equal(host(gpu["fw"].delta), fw["scale"])
+    np.testing.assert_array_equal(host(gpu["fw"].code_colsum), fw["code_colsum"])
+    ref = pipeline.linear_backward(inp, mode=mode, ec=ec, scale=scale, seed=seed, layer_id=layer,
+                                   rows_per_example=S, dx_rows=dx_rows, dw_rows=dw_rows, fx=fx, fw=fw)
+    q = gpu["q"]
+    np.testing.assert_array_equal(host(q.Q), ref["q"]["Q"], err_msg=tag)
+    np.testing.assert_array_equal(host(q.delta), ref["q"]["delta"], err_msg=tag)
+    if ec != s3r.EC_NONE:
+        assert rel_err(host(q.ec_row), ref["q"]["eps"]) <= TOL, tag
+        assert rel_err(host(q.ec_col), ref["q"]["ebar"]) <= TOL, tag
+    dX = host(gpu["dX"])
+    dX = dX if dx_rows is None else dX[dx_rows]
+    e = rel_err(dX, ref["dX"])
+    assert e <= TOL, f"{tag}: dX rel err {e:.3g}"
+    if scale == s3r.PER_TENSOR:
+        dW = host(gpu["dW"])
+        dW = dW if dw_rows is None else dW[dw_rows]
+        e = rel_err(dW, ref["dW"])
+        assert e <= TOL, f"{tag}: dW rel err {e:.3g}"
+    return gpu, ref
+
+
+@pytest.mark.parametrize("mode,ec", MODES)
+def test_linear_256x512x1024_f32(mode, ec):
+    w = inputs.WORKLOADS["linear-256x512x1024-f32"]
+    inp = inputs.make_linear_inputs(w)
+    _check_linear(inp, w.rows_per_example, mode, ec)
+
+
+def test_linear_ragged_multi_example_bf16():
+    # three examples of 128 tokens, ragged D and d_in, both EC variants and per-token steps for dX
+    w = inputs.WORKLOADS["down-4096x11008x4096-bf16"].scaled(384, 300, 700, rows_per_example=128)
+    inp = inputs.make_linear_inputs(w)
+    for mode, ec in ((s3r.S3R, s3r.EC_TWO_WAY), (s3r.S3R, s3r.EC_DX_ONLY), (s3r.SR, s3r.EC_NONE)):
+        _check_linear(inp, 128, mode, ec, seed=7, layer=2)
+    _check_linear(inp, 128, s3r.S3R, s3r.EC_TWO_WAY, scale=s3r.PER_TOKEN, seed=7, layer=2)
+
+
+def _sample_rows(n, k, seed):
+    rng = np.random.default_rng(seed)
+    rows = set(rng.choice(n, min(n, k), replace=False).tolist()) | {0, n - 1, n - 2}
+    return np.array(sorted(rows))
+
+
+@pytest.mark.parametrize("mode,ec", [(s3r.S3R, s3r.EC_TWO_WAY), (s3r.SR, s3r.EC_NONE), (s3r.RTNE, s3r.EC_NONE),
+                                     (s3r.S3R, s3r.EC_DX_ONLY)])
+def test_down_4096x11008x4096_bf16_sampled(mode, ec):
+    w = inputs.WORKLOADS["down-4096x11008x4096-bf16"]
+    inp = inputs.make_linear_inputs(w)
+    _check_linear(inp, w.rows_per_example, mode, ec, dx_rows=_sample_rows(w.tokens, 20, 1),
+                  dw_rows=_sample_rows(w.d_out, 12, 2))
+
+
+def test_down_8192x14336x4096_bf16_sampled():
+    # the bench workload: Llama-8B FFN down-projection, four examples of 2048 tokens, S3R-EC two-way
+    w = inputs.WORKLOADS["down-8192x14336x4096-bf16"]
+    inp = inputs.make_linear_inputs(w)
+    _check_linear(inp, w.rows_per_example, s3r.S3R, s3r.EC_TWO_WAY, dx_rows=_sample_rows(w.tokens, 16, 3),
+                  dw_rows=_sample_rows(w.d_out, 10, 4))

@@ -1,0 +1,120 @@
+"""libs3r.so loads and exports what include/s3r.h declares; host-side checks (no GPU needed).
+
+Argument validation happens before any HIP call, so these error paths run on
+a machine without a GPU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from stochastic_rounding_quantization_amd import s3r
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(s3r.LIB_PATH):
+        from stochastic_rounding_quantization_amd import build
+        build.build()
+    return s3r.lib()
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "s3r.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(s3r_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert set(names) == set(s3r.EXPORTED)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_status(L):
+    assert s3r.s3r_version() == 100
+    assert s3r.s3r_status_string(0) == "ok"
+    assert s3r.s3r_status_string(-3) == "workspace too small"
+
+
+def _call_quantize(L, desc, G=1, gdt=0, ldg=None, Q=1, ldq=None, delta=1, ec=(None, None, None), ws=None,
+                   wsb=0, colsum=None):
+    P = lambda v: None if v is None else ctypes.c_void_p(v)
+    ldg = desc.cols if ldg is None else ldg
+    ldq = desc.cols if ldq is None else ldq
+    return L.s3r_quantize(ctypes.byref(desc) if desc is not None else None, P(G), gdt, ldg, None, None, P(Q), ldq,
+                          P(delta), P(colsum), P(ec[0]), P(ec[1]), P(ec[2]), None, P(ws), wsb, None)
+
+
+def test_quantize_argument_errors(L):
+    d = s3r.qdesc(64, 96, 32, s3r.S3R, s3r.EC_NONE)
+    assert L.s3r_quantize(None, None, 0, 0, None, None, None, 0, None, None, None, None, None, None, None, 0,
+                          None) == -1
+    bad = s3r.qdesc(64, 96, 30)                         # T % S != 0
+    assert _call_quantize(L, bad) == -1
+    assert _call_quantize(L, d, gdt=2) == -2            # int32 gradient
+    assert _call_quantize(L, s3r.qdesc(64, 96, 32, s3r.RTNE, s3r.EC_TWO_WAY), ec=(1, 1, 1)) == -2
+    assert _call_quantize(L, d, ldg=95) == -1           # leading dim < cols
+    assert _call_quantize(L, d, G=None) == -1
+    assert _call_quantize(L, d, delta=None) == -1
+    ecd = s3r.qdesc(64, 96, 32, s3r.S3R, s3r.EC_TWO_WAY)
+    assert _call_quantize(L, ecd) == -1                 # EC outputs missing
+    need = s3r.s3r_quantize_workspace(ecd)
+    assert need > 0
+    assert _call_quantize(L, ecd, ec=(256, 512, 768), ws=4096, wsb=need - 1) == -3
+    assert _call_quantize(L, d, ec=(256, 512, 768)) == -1   # EC outputs without EC
+    m = s3r.qdesc(64, 96, 32, 7)
+    assert _call_quantize(L, m) == -2
+
+
+def test_backward_argument_errors(L):
+    P = ctypes.c_void_p
+    d = s3r.qdesc(64, 96, 32, s3r.S3R, s3r.EC_NONE)
+    args = dict(Q=P(4096), ldq=96, delta=P(16), W=P(8192), ldw=128, din=128, out=P(4096), odt=0, ldo=128)
+
+    def dx(**kw):
+        a = {**args, **kw}
+        return L.s3r_backward_dx(ctypes.byref(d if "d" not in kw else kw["d"]), a["Q"], a["ldq"], a["delta"],
+                                 a["W"], a["ldw"], a["din"], None, None, None, None, None, a["out"], a["odt"],
+                                 a["ldo"], None, 0, None)
+
+    def dw(**kw):
+        a = {**args, **kw}
+        return L.s3r_backward_dw(ctypes.byref(d if "d" not in kw else kw["d"]), a["Q"], a["ldq"], a["delta"],
+                                 a["W"], a["ldw"], a["din"], None, None, None, None, None, a["out"], a["odt"],
+                                 a["ldo"], None, 0, None)
+
+    assert dx(ldq=100) == -1                 # GEMM operand leading dim not a multiple of 16
+    assert dx(Q=P(4097)) == -1               # misaligned operand
+    assert dx(odt=1) == -2                   # bf16 output not offered
+    assert dx(ldo=100) == -1
+    big = s3r.qdesc(64, 200000, 32)
+    assert dx(d=big, ldq=200000) == -1       # K beyond the int32 accumulator bound
+    ecd = s3r.qdesc(64, 96, 32, s3r.S3R, s3r.EC_DX_ONLY)
+    assert dx(d=ecd) == -1                   # correction inputs missing
+    pt = s3r.qdesc(64, 96, 32, s3r.S3R, s3r.EC_NONE, s3r.PER_TOKEN)
+    assert dw(d=pt) == -2                    # dW needs a per-tensor step
+    assert s3r.s3r_backward_workspace(s3r.qdesc(64, 96, 32, s3r.S3R, s3r.EC_TWO_WAY), 128) > 0
+    assert s3r.s3r_backward_workspace(d, 128) == 0
+
+
+def test_no_gpu_reports_hip_error(L):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    d = s3r.qdesc(64, 96, 32, s3r.RTNE)
+    rc = _call_quantize(L, d, ws=4096, wsb=1 << 20)
+    assert rc in (-4, -5)
+
+
+def test_product_path_does_not_import_oracle():
+    # the product path (package + bench entry) must not route through the CPU oracle
+    pkg = os.path.join(ROOT, "stochastic_rounding_quantization_amd")
+    for fn in os.listdir(pkg):
+        if fn.endswith(".py"):
+            src = open(os.path.join(pkg, fn)).read()
+            assert "import oracle" not in src and "from oracle" not in src, fn
