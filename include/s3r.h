@@ -127,7 +127,8 @@ int s3r_quantize(const s3r_qdesc* desc,
  * Common: Q [T x D] int8 codes with ld_q, delta as written by s3r_quantize
  * (desc->scale selects [1] or [T]).  INT8 GEMMs on the MFMA units with int32
  * accumulation.  GEMM operands (Q, Wq, Xq) need 16-byte-aligned base
- * pointers and leading dims that are multiples of 16; K <= 131072.
+ * pointers, leading dims that are multiples of 16 and below 2^24, and
+ * (rows + 320) * ld < 2^32 bytes; K <= 131072.
  * out_dt: S3R_F32 (dequantised, corrected per desc->ec) or S3R_I32_RAW (raw
  * int32 accumulators, no dequantisation, no correction).
  *

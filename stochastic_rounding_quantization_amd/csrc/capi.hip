@@ -94,8 +94,11 @@ size_t s3r_backward_workspace(const s3r_qdesc* d, int64_t d_in) {
   return a > b ? a : b;
 }
 
-static int check_gemm_operand(const int8_t* p, int64_t ld, int64_t cols, bool nonempty) {
-  if (ld < cols || ld < 0) return S3R_ERR_INVALID_ARG;
+static int check_gemm_operand(const int8_t* p, int64_t ld, int64_t rows, int64_t cols, bool nonempty) {
+  // the GEMM addresses each operand through a buffer descriptor with 32-bit byte
+  // offsets, including up to one tile (256 rows, 64 k-rows) past the last row
+  if (ld < cols || ld < 0 || ld >= ((int64_t)1 << 24)) return S3R_ERR_INVALID_ARG;
+  if ((rows + 320) * ld >= ((int64_t)1 << 32)) return S3R_ERR_INVALID_ARG;
   if (nonempty && (!p || !al16(p) || (ld & 15))) return S3R_ERR_INVALID_ARG;
   return S3R_OK;
 }
@@ -112,8 +115,8 @@ int s3r_backward_dx(const s3r_qdesc* d, const int8_t* Q, int64_t ld_q, const flo
   const bool out_nonempty = T > 0 && d_in > 0;
   if (!delta || (out_nonempty && !dX) || ld_dx < d_in) return S3R_ERR_INVALID_ARG;
   if (out_nonempty && ((uintptr_t)dX & 3u)) return S3R_ERR_INVALID_ARG;
-  if ((rc = check_gemm_operand(Q, ld_q, D, T > 0 && D > 0))) return rc;
-  if ((rc = check_gemm_operand(Wq, ld_w, d_in, D > 0 && d_in > 0))) return rc;
+  if ((rc = check_gemm_operand(Q, ld_q, T, D, T > 0 && D > 0))) return rc;
+  if ((rc = check_gemm_operand(Wq, ld_w, D, d_in, D > 0 && d_in > 0))) return rc;
   const bool ec = d->ec != S3R_EC_NONE && out_dt == S3R_F32;
   if (ec && (!r_W || !ec_row || !ec_col || !ec_mean)) return S3R_ERR_INVALID_ARG;
   const size_t need = ec ? dx_workspace(T, D, d_in, d->rows_per_example, d->ec) : 0;
@@ -140,8 +143,8 @@ int s3r_backward_dw(const s3r_qdesc* d, const int8_t* Q, int64_t ld_q, const flo
   const bool out_nonempty = D > 0 && d_in > 0;
   if (!delta || (out_nonempty && !dW) || ld_dw < d_in) return S3R_ERR_INVALID_ARG;
   if (out_nonempty && ((uintptr_t)dW & 3u)) return S3R_ERR_INVALID_ARG;
-  if ((rc = check_gemm_operand(Q, ld_q, D, T > 0 && D > 0))) return rc;
-  if ((rc = check_gemm_operand(Xq, ld_x, d_in, T > 0 && d_in > 0))) return rc;
+  if ((rc = check_gemm_operand(Q, ld_q, T, D, T > 0 && D > 0))) return rc;
+  if ((rc = check_gemm_operand(Xq, ld_x, T, d_in, T > 0 && d_in > 0))) return rc;
   const bool ec = d->ec == S3R_EC_TWO_WAY && out_dt == S3R_F32;
   if (ec && (!xs_b || !ec_row || !ec_col || !ec_mean)) return S3R_ERR_INVALID_ARG;
   const size_t need = ec ? dw_workspace(T, D, d_in, d->rows_per_example, d->ec) : 0;

@@ -12,29 +12,59 @@
 //   dW [D x d_in] = Q^T        . Xq [T x d_in]   A: M-contiguous, B: N-contiguous
 //
 // Tiling: 256 x 256 output tile per 256-thread workgroup (four 64-lane waves,
-// 2 x 2, each 128 x 128 = 4 x 4 blocks of v_mfma_i32_32x32x32_i8), K step 64,
-// LDS double buffer (2 x (16 + 16) KB).  LDS holds every operand K-contiguous:
-// row r of a tile is 64 bytes in four 16-byte chunks, chunk c stored at
-// position c ^ f(r), f(r) = ((r >> 1) ^ (r >> 3)) & 3, so the 16-byte
-// fragment reads of 8 or 16 consecutive rows hit distinct banks.  Operands
-// that are contiguous along M or N are transposed on the way in: each thread
-// loads an 8 (k) x 8 (mn) byte block with eight 8-byte loads and transposes
-// it with byte permutes before one 8-byte LDS write per mn row.
-// Workgroups are numbered so that the 32 consecutive tiles of one XCD share
-// rows of A and columns of B (grouped order), for L2 reuse.
+// 2 x 2, each 128 x 128 = 4 x 4 blocks of v_mfma_i32_32x32x32_i8), K step 64.
+// Operands go from global memory straight into LDS (global_load_lds_dwordx4,
+// 16 bytes per lane, lane l landing at 16*l of a 1 KB block) through a
+// 4-stage ring of 32 KB stages (128 KB), three K steps in flight.  Nothing is
+// transposed on the way in:
+//   K-contiguous tile: 256 rows x 64 B; 16-byte chunk c of row r sits at
+//     position c ^ f(r), f(r) = ((r >> 1) ^ (r >> 3)) & 3; fragments are read
+//     with ds_read_b128 (lane: row l%32, 16 consecutive k).
+//   M/N-contiguous tile: 64 k-rows x 256 B; chunk c of k-row r sits at
+//     c ^ (r & 7); fragments are read with two ds_read_b64_tr_b8: within each
+//     16-lane group, lane L fetches 8 bytes of k-row kb + L/2 at column
+//     nb + 8(L%2), and the hardware hands lane i the bytes of column nb + i
+//     from the 8 k-rows, so a lane ends up with 16 consecutive k of one
+//     column, the same k order the K-contiguous read gives.
+// The chunk position is chosen on the global side (which lane loads which
+// chunk), so the swizzles cost nothing at load time, and the 16-byte reads of
+// 8 or 16 consecutive rows / the 8 k-rows of a transpose read hit distinct
+// banks.  Tiles that cross the matrix edge (or the K tail) take a masked
+// register path that writes zeros past the edge.
+// Workgroups are numbered so that the consecutive tiles of one XCD share rows
+// of A and columns of B (grouped order), for L2 reuse.
 #include "s3r_internal.h"
 
 namespace s3r {
 namespace {
 
+typedef int v2i __attribute__((ext_vector_type(2)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) v2i lds_v2i;
 
 constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int kGemmThreads = 256;
-constexpr int kTileBytes = BM * BK;   // 16 KB per operand tile
+constexpr int kStageBytes = 32768;    // A tile (16 KB) + B tile (16 KB)
+constexpr int kHalf = 16384;
 constexpr int kGroupM = 8;            // grouped tile order: 8 tile-rows per group
 constexpr int kNumXcd = 8;
+
+// The four pipeline stages are separate LDS objects so that the compiler can
+// tell a stage being read from the stages being filled by in-flight DMA.
+__shared__ __attribute__((aligned(1024))) uint8_t g_stage0[kStageBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t g_stage1[kStageBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t g_stage2[kStageBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t g_stage3[kStageBytes];
+
+template <int S>
+__device__ __forceinline__ uint8_t* stage() {
+  if constexpr (S == 0) return g_stage0;
+  else if constexpr (S == 1) return g_stage1;
+  else if constexpr (S == 2) return g_stage2;
+  else return g_stage3;
+}
 
 enum { EPI_RAW = 0, EPI_DX = 1, EPI_DW = 2 };
 
@@ -57,118 +87,164 @@ struct GemmParams {
   int tiles_m, tiles_n;
 };
 
-__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+__device__ __forceinline__ int swz_k(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
-// 4 x 4 byte transpose: out[j] byte i = in[i] byte j.
-__device__ __forceinline__ void transpose4(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3, uint32_t o[4]) {
-  const uint32_t t0 = __builtin_amdgcn_perm(a1, a0, 0x05010400u);  // a0.0 a1.0 a0.1 a1.1
-  const uint32_t t1 = __builtin_amdgcn_perm(a1, a0, 0x07030602u);  // a0.2 a1.2 a0.3 a1.3
-  const uint32_t t2 = __builtin_amdgcn_perm(a3, a2, 0x05010400u);  // a2.0 a3.0 a2.1 a3.1
-  const uint32_t t3 = __builtin_amdgcn_perm(a3, a2, 0x07030602u);  // a2.2 a3.2 a2.3 a3.3
-  o[0] = __builtin_amdgcn_perm(t2, t0, 0x05040100u);               // a0.0 a1.0 a2.0 a3.0
-  o[1] = __builtin_amdgcn_perm(t2, t0, 0x07060302u);               // a0.1 a1.1 a2.1 a3.1
-  o[2] = __builtin_amdgcn_perm(t3, t1, 0x05040100u);
-  o[3] = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
-}
+// s_waitcnt immediates (gfx9 encoding): wait for at most n vector-memory ops / no LDS ops.
+#define S3R_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | 0x70 | 0xF00)
+#define S3R_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(0xC07F)
 
-// ---------------------------------------------------- global -> registers ----
-// K-contiguous operand: rows (m or n) of 64 bytes; thread owns 4 chunks.
-struct KStage { uint4 v[4]; };
-// MN-contiguous operand: 64 k-rows of 256 bytes; thread owns an 8 x 8 block.
-struct MStage { uint2 v[8]; };
+// ------------------------------------------------ tile loads into a stage ----
+// Loads are buffer loads with the LDS bit (16 bytes per lane, lane l landing at
+// 16*l of a 1 KB block of the stage) through a buffer descriptor that spans the
+// whole operand matrix, rows * ld bytes.  The hardware's range check returns
+// zeros past the end of the matrix.  Every operand's K dimension is either its
+// row index (M/N-contiguous operands) or is paired with one that is, so k >= K
+// always multiplies a zero; reads past the M or N edge inside the matrix only
+// reach output rows or columns that are never stored.
+// Each wave fills 4 of the 16 1-KB blocks of the A tile and 4 of the B tile.
+// Block blk, lane l:
+//   K-contiguous: row = 16 blk + l/4, position p = l%4 holds chunk c = p ^ swz_k(row)
+//   M/N-contiguous: k-row = 4 blk + l/16, position p = l%16 holds chunk c = p ^ (k-row & 7)
+constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit dword format (gfx9 family)
 
-template <bool MASKED>
-__device__ __forceinline__ void load_k(KStage& s, const int8_t* __restrict__ P, int64_t ld, int64_t rows,
-                                       int64_t K, int64_t r0, int64_t k0) {
-  const int tid = threadIdx.x;
+struct LoadMap {           // per-thread byte offsets (tile origin + position), for 4 blocks of A and of B
+  uint32_t a_off[4], b_off[4];
+  uint32_t a_step, b_step; // advance per K step (uniform)
+  __amdgpu_buffer_rsrc_t ra, rb;
+};
+
+template <bool A_KMAJOR>
+__device__ __forceinline__ LoadMap make_loadmap(const GemmParams& g, int64_t m0, int64_t n0) {
+  LoadMap m;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int row = it * 64 + (tid >> 2);
-    const int c = tid & 3;
-    const int64_t gr = r0 + row, gk = k0 + c * 16;
-    if (!MASKED) {
-      s.v[it] = *reinterpret_cast<const uint4*>(P + gr * ld + gk);
+  for (int q = 0; q < 4; ++q) {
+    const int blk = wave * 4 + q;
+    if constexpr (A_KMAJOR) {
+      const int row = blk * 16 + (lane >> 2);
+      const int c = (lane & 3) ^ swz_k(row);
+      m.a_off[q] = (uint32_t)((m0 + row) * g.lda + c * 16);
     } else {
-      uint32_t w[4] = {0, 0, 0, 0};
-      if (gr < rows) {
-        const int8_t* p = P + gr * ld + gk;
-        if (gk + 16 <= K) {
-          const uint4 u = *reinterpret_cast<const uint4*>(p);
-          w[0] = u.x; w[1] = u.y; w[2] = u.z; w[3] = u.w;
-        } else {
-          for (int b = 0; b < 16; ++b)
-            if (gk + b < K) w[b >> 2] |= (uint32_t)(uint8_t)p[b] << (8 * (b & 3));
-        }
-      }
-      s.v[it] = make_uint4(w[0], w[1], w[2], w[3]);
+      const int kr = blk * 4 + (lane >> 4);
+      const int c = (lane & 15) ^ (kr & 7);
+      m.a_off[q] = (uint32_t)(kr * g.lda + m0 + c * 16);
     }
+    const int kr = blk * 4 + (lane >> 4);
+    const int c = (lane & 15) ^ (kr & 7);
+    m.b_off[q] = (uint32_t)(kr * g.ldb + n0 + c * 16);
   }
+  m.a_step = (uint32_t)(A_KMAJOR ? BK : BK * g.lda);
+  m.b_step = (uint32_t)(BK * g.ldb);
+  const int64_t a_rows = A_KMAJOR ? g.M : g.K;
+  m.ra = __builtin_amdgcn_make_buffer_rsrc((void*)g.A, (short)0, (int)(uint32_t)(a_rows * g.lda), kRsrcWord3);
+  m.rb = __builtin_amdgcn_make_buffer_rsrc((void*)g.B, (short)0, (int)(uint32_t)(g.K * g.ldb), kRsrcWord3);
+  return m;
 }
 
-__device__ __forceinline__ void store_k(const KStage& s, uint8_t* __restrict__ lds) {
-  const int tid = threadIdx.x;
+template <int S>
+__device__ __forceinline__ void load_stage(const LoadMap& m, int kt) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // LDS DMA base must be wave-uniform
+  const uint32_t sa = (uint32_t)kt * m.a_step, sb = (uint32_t)kt * m.b_step;
 #pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int row = it * 64 + (tid >> 2);
-    const int c = tid & 3;
-    *reinterpret_cast<uint4*>(lds + row * 64 + ((c ^ swz(row)) << 4)) = s.v[it];
-  }
+  for (int q = 0; q < 4; ++q)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(m.ra, (lds_void*)(stage<S>() + (wave * 4 + q) * 1024), 16, m.a_off[q],
+                                             sa, 0, 0);
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(m.rb, (lds_void*)(stage<S>() + kHalf + (wave * 4 + q) * 1024), 16,
+                                             m.b_off[q], sb, 0, 0);
 }
 
-template <bool MASKED>
-__device__ __forceinline__ void load_m(MStage& s, const int8_t* __restrict__ P, int64_t ld, int64_t cols,
-                                       int64_t K, int64_t c0, int64_t k0) {
-  const int tid = threadIdx.x;
-  const int kg = tid >> 5, mg = tid & 31;
-  const int64_t gc = c0 + mg * 8;
+// ------------------------------------------------------------ fragments ----
+struct FragMap {
+  int a_k[2];      // K-contiguous A: byte offset for kk = 0, 1 (block i adds i * 2048)
+  int a_t[4];      // M-contiguous A: byte offset of block i (kk adds 8192, second read 2048)
+  int b_t[4];      // N-contiguous B (within the B half)
+};
+
+template <bool A_KMAJOR>
+__device__ __forceinline__ FragMap make_fragmap() {
+  FragMap f;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int r = lane & 31;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int64_t gk = k0 + kg * 8 + i;
-    if (!MASKED) {
-      s.v[i] = *reinterpret_cast<const uint2*>(P + gk * ld + gc);
-    } else {
-      uint32_t w[2] = {0, 0};
-      if (gk < K) {
-        const int8_t* p = P + gk * ld + gc;
-        if (gc + 8 <= cols) {
-          const uint2 u = *reinterpret_cast<const uint2*>(p);
-          w[0] = u.x; w[1] = u.y;
-        } else {
-          for (int b = 0; b < 8; ++b)
-            if (gc + b < cols) w[b >> 2] |= (uint32_t)(uint8_t)p[b] << (8 * (b & 3));
-        }
-      }
-      s.v[i] = make_uint2(w[0], w[1]);
+  for (int kk = 0; kk < 2; ++kk) {
+    const int c = kk * 2 + (lane >> 5);
+    f.a_k[kk] = (wm * 128 + r) * 64 + ((c ^ swz_k(r)) << 4);
+  }
+  const int grp = lane >> 4, L = lane & 15;
+  const int krow = 16 * (grp >> 1) + (L >> 1);        // k-row for kk = 0, first read; krow & 7 == L >> 1
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ca = (wm * 128 + i * 32 + 16 * (grp & 1)) >> 4;
+    f.a_t[i] = krow * 256 + ((ca ^ (L >> 1)) << 4) + 8 * (L & 1);
+    const int cb = (wn * 128 + i * 32 + 16 * (grp & 1)) >> 4;
+    f.b_t[i] = krow * 256 + ((cb ^ (L >> 1)) << 4) + 8 * (L & 1);
+  }
+  return f;
+}
+
+__device__ __forceinline__ v4i tr_pair(const uint8_t* p) {
+  const v2i lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)p);
+  const v2i hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(p + 2048));   // k-rows + 8
+  return v4i{lo.x, lo.y, hi.x, hi.y};
+}
+
+// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSgMfma = 0x008, kSgDsRead = 0x100;
+
+template <int S, bool A_KMAJOR>
+__device__ __forceinline__ void compute_stage(const FragMap& f, v16i (&acc)[4][4]) {
+  const uint8_t* st = stage<S>();
+  v4i af[2][4], bf[2][4];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (A_KMAJOR) af[kk][i] = *reinterpret_cast<const v4i*>(st + f.a_k[kk] + i * 2048);
+      else af[kk][i] = tr_pair(st + f.a_t[i] + kk * 8192);
     }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bf[kk][j] = tr_pair(st + kHalf + f.b_t[j] + kk * 8192);
   }
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[kk][i], bf[kk][j], acc[i][j], 0, 0, 0);
+  // schedule: the first half-step's reads, then its 16 MFMAs interleaved with the
+  // second half-step's reads, then the second half-step's MFMAs
+  constexpr int NR = A_KMAJOR ? 12 : 16;   // LDS reads per half-step
+  __builtin_amdgcn_sched_group_barrier(kSgDsRead, NR, 0);
+#pragma unroll
+  for (int x = 0; x < NR; ++x) {
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+  }
+  if constexpr (NR < 16) __builtin_amdgcn_sched_group_barrier(kSgMfma, 16 - NR, 0);
+  __builtin_amdgcn_sched_group_barrier(kSgMfma, 16, 0);
 }
 
-__device__ __forceinline__ void store_m(const MStage& s, uint8_t* __restrict__ lds) {
-  const int tid = threadIdx.x;
-  const int kg = tid >> 5, mg = tid & 31;
-  uint32_t lo0[4], lo1[4], hi0[4], hi1[4];
-  // rows k 0..3 / 4..7 of the block, columns mn 0..3 (.x) and 4..7 (.y)
-  transpose4(s.v[0].x, s.v[1].x, s.v[2].x, s.v[3].x, lo0);
-  transpose4(s.v[4].x, s.v[5].x, s.v[6].x, s.v[7].x, lo1);
-  transpose4(s.v[0].y, s.v[1].y, s.v[2].y, s.v[3].y, hi0);
-  transpose4(s.v[4].y, s.v[5].y, s.v[6].y, s.v[7].y, hi1);
-  const int c = kg >> 1, half = (kg & 1) << 3;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int row = mg * 8 + j;
-    const uint2 v = j < 4 ? make_uint2(lo0[j], lo1[j]) : make_uint2(hi0[j - 4], hi1[j - 4]);
-    *reinterpret_cast<uint2*>(lds + row * 64 + ((c ^ swz(row)) << 4) + half) = v;
-  }
+// One K step on stage S = kt % 4: wait for its data (8 loads per later step of
+// this wave may stay in flight), refill stage (S+3)%4 with step kt+3, multiply.
+template <int S, bool A_KMAJOR>
+__device__ __forceinline__ void k_step(const LoadMap& lm, const FragMap& fm, int kt, int nk, v16i (&acc)[4][4]) {
+  const int later = nk - 1 - kt;
+  if (later >= 2) S3R_WAIT_VM(16);
+  else if (later == 1) S3R_WAIT_VM(8);
+  else S3R_WAIT_VM(0);
+  S3R_WAIT_LGKM0();                 // this wave's reads of the stage about to be refilled are done
+  __builtin_amdgcn_s_barrier();
+  if (kt + 3 < nk) load_stage<(S + 3) & 3>(lm, kt + 3);
+  compute_stage<S, A_KMAJOR>(fm, acc);
 }
 
 // ----------------------------------------------------------------- kernel ----
 template <bool A_KMAJOR, int EPI>
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmParams g, EpiParams ep) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * 2 * kTileBytes];
-  // buffer b: A tile at smem + 2b * 16 KB, B tile right after it
-#define S3R_SA(b) (smem + (b) * 2 * kTileBytes)
-#define S3R_SB(b) (smem + (b) * 2 * kTileBytes + kTileBytes)
-
   // XCD-aware numbering: hardware block ids go round-robin over the 8 XCDs;
   // give each XCD a contiguous range of logical tiles.
   const int nblocks = g.tiles_m * g.tiles_n;
@@ -179,7 +255,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmParams g, 
   const int gsz = min(g.tiles_m - first_m, kGroupM);
   const int tm = first_m + (bid % group) % gsz;
   const int tn = (bid % group) / gsz;
+
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  const int nk = (int)((g.K + BK - 1) / BK);
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -191,91 +269,58 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmParams g, 
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = v16i{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
 
-  const bool mn_inside = (m0 + BM <= g.M) && (n0 + BN <= g.N);
-  const int nk = (int)((g.K + BK - 1) / BK);
-
-  KStage ka; MStage ma; MStage mb;
-  auto load_stage = [&](int64_t k0) {
-    if (mn_inside && k0 + BK <= g.K) {
-      if constexpr (A_KMAJOR) load_k<false>(ka, g.A, g.lda, g.M, g.K, m0, k0);
-      else load_m<false>(ma, g.A, g.lda, g.M, g.K, m0, k0);
-      load_m<false>(mb, g.B, g.ldb, g.N, g.K, n0, k0);
-    } else {
-      if constexpr (A_KMAJOR) load_k<true>(ka, g.A, g.lda, g.M, g.K, m0, k0);
-      else load_m<true>(ma, g.A, g.lda, g.M, g.K, m0, k0);
-      load_m<true>(mb, g.B, g.ldb, g.N, g.K, n0, k0);
-    }
-  };
-  auto store_stage = [&](int buf) {
-    if constexpr (A_KMAJOR) store_k(ka, S3R_SA(buf));
-    else store_m(ma, S3R_SA(buf));
-    store_m(mb, S3R_SB(buf));
-  };
-
-  if (nk > 0) {
-    load_stage(0);
-    store_stage(0);
+  const LoadMap lm = make_loadmap<A_KMAJOR>(g, m0, n0);
+  const FragMap fm = make_fragmap<A_KMAJOR>();
+  if (nk > 0) load_stage<0>(lm, 0);
+  if (nk > 1) load_stage<1>(lm, 1);
+  if (nk > 2) load_stage<2>(lm, 2);
+  for (int kt = 0; kt < nk; kt += 4) {
+    k_step<0, A_KMAJOR>(lm, fm, kt, nk, acc);
+    if (kt + 1 < nk) k_step<1, A_KMAJOR>(lm, fm, kt + 1, nk, acc);
+    if (kt + 2 < nk) k_step<2, A_KMAJOR>(lm, fm, kt + 2, nk, acc);
+    if (kt + 3 < nk) k_step<3, A_KMAJOR>(lm, fm, kt + 3, nk, acc);
   }
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) load_stage((int64_t)(kt + 1) * BK);
-    const uint8_t* a_s = S3R_SA(buf);
-    const uint8_t* b_s = S3R_SB(buf);
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int c = kk * 2 + (lane >> 5);
-      v4i af[4], bf[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = wm * 128 + i * 32 + (lane & 31);
-        af[i] = *reinterpret_cast<const v4i*>(a_s + r * 64 + ((c ^ swz(r)) << 4));
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = wn * 128 + j * 32 + (lane & 31);
-        bf[j] = *reinterpret_cast<const v4i*>(b_s + r * 64 + ((c ^ swz(r)) << 4));
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < nk) store_stage(buf ^ 1);
-    __syncthreads();
-  }
+  S3R_WAIT_VM(0);
+  S3R_WAIT_LGKM0();
+  __builtin_amdgcn_s_barrier();
 
-#undef S3R_SA
-#undef S3R_SB
   // ------------------------------------------------------------ epilogue ----
-  // Output layout of a 32x32 block: lane l, register r -> row (r/4)*8 + (l/32)*4 + r%4, column l%32.
-  float* rowf = reinterpret_cast<float*>(smem);   // per-row factors, 4 floats per tile row
+  // 32x32 block output layout: lane l, register r -> row (r/4)*8 + (l/32)*4 + r%4, column l%32.
+  float4* rowf = reinterpret_cast<float4*>(g_stage0);   // per-row factors of the tile
+  float* roweb = reinterpret_cast<float*>(g_stage1);    // dW: ebar[b][row] / s_w[row], b < 8
+  constexpr int kMaxB = 8;
   if constexpr (EPI == EPI_DX) {
-    // alpha = Delta_t / s_x[t], beta = 1 / s_x[t], gamma = (eps_t - mu_b) / s_x[t]
+    // x: Delta_t / s_x[t], y: 1 / s_x[t], z: (eps_t - mu_b) / s_x[t], w: example index
     for (int r = threadIdx.x; r < BM; r += kGemmThreads) {
-      const int64_t t = m0 + r;
-      float a = 0.f, be = 0.f, ga = 0.f;
-      if (t < g.M) {
-        const float d = ep.per_token ? ep.delta[t] : ep.delta[0];
-        const float inv = ep.row_scale ? __fdiv_rn(1.f, ep.row_scale[t]) : 1.f;
-        a = d * inv;
-        be = inv;
-        if (ep.ec) ga = (ep.ec_row[t] - ep.ec_mean[t / ep.S]) * inv;
+      const int64_t tt = m0 + r;
+      float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (tt < g.M) {
+        const float d = ep.per_token ? ep.delta[tt] : ep.delta[0];
+        const float inv = ep.row_scale ? __fdiv_rn(1.f, ep.row_scale[tt]) : 1.f;
+        f.x = d * inv;
+        f.y = inv;
+        if (ep.ec) {
+          const int64_t b = tt / ep.S;
+          f.z = (ep.ec_row[tt] - ep.ec_mean[b]) * inv;
+          f.w = __int_as_float((int)b);
+        }
       }
-      rowf[r * 4 + 0] = a; rowf[r * 4 + 1] = be; rowf[r * 4 + 2] = ga;
+      rowf[r] = f;
     }
     __syncthreads();
   } else if constexpr (EPI == EPI_DW) {
-    // alpha = Delta / s_w[j], beta = 1 / s_w[j]
+    // x: Delta / s_w[j], y: 1 / s_w[j]; roweb[b * BM + r] = ebar[b][j] / s_w[j]
     for (int r = threadIdx.x; r < BM; r += kGemmThreads) {
       const int64_t j = m0 + r;
-      float a = 0.f, be = 0.f;
+      float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
       if (j < g.M) {
         const float inv = ep.row_scale ? __fdiv_rn(1.f, ep.row_scale[j]) : 1.f;
-        a = ep.delta[0] * inv;
-        be = inv;
+        f.x = ep.delta[0] * inv;
+        f.y = inv;
+        if (ep.ec)
+          for (int64_t b = 0; b < ep.B && b < kMaxB; ++b) roweb[b * BM + r] = ep.ebar[b * g.M + j] * inv;
       }
-      rowf[r * 4 + 0] = a; rowf[r * 4 + 1] = be;
+      rowf[r] = f;
     }
     __syncthreads();
   }
@@ -284,11 +329,19 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmParams g, 
   for (int j = 0; j < 4; ++j) {
     const int64_t n = n0 + wn * 128 + j * 32 + (lane & 31);
     const bool n_ok = n < g.N;
-    float cu = 0.f, crw = 0.f;
+    // per-column values of this lane's column
+    float colA = 0.f, colB[kMaxB];
+#pragma unroll
+    for (int b = 0; b < kMaxB; ++b) colB[b] = 0.f;
     if constexpr (EPI == EPI_DX) {
-      if (ep.ec && n_ok) crw = (float)ep.colsum[n];
+      if (ep.ec && n_ok) colA = (float)ep.colsum[n];                    // r_W[n]
     } else if constexpr (EPI == EPI_DW) {
-      if (ep.ec && n_ok) cu = ep.u[n];
+      if (ep.ec && n_ok) {
+        colA = ep.u[n];
+#pragma unroll
+        for (int b = 0; b < kMaxB; ++b)
+          if (b < ep.B) colB[b] = (float)ep.colsum[b * g.N + n];        // xs_b[n]
+      }
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -296,28 +349,46 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmParams g, 
       for (int r = 0; r < 16; ++r) {
         const int lr = wm * 128 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
         const int64_t m = m0 + lr;
-        if (!(n_ok && m < g.M)) continue;
-        const int32_t v = acc[i][j][r];
-        if constexpr (EPI == EPI_RAW) {
-          reinterpret_cast<int32_t*>(ep.out)[m * ep.ld_out + n] = v;
-        } else if constexpr (EPI == EPI_DX) {
-          const float4 f = *reinterpret_cast<const float4*>(rowf + lr * 4);
-          float corr = 0.f;
-          if (ep.ec) corr = fmaf(f.z, crw, f.y * ep.vec[(m / ep.S) * g.N + n]);
-          reinterpret_cast<float*>(ep.out)[m * ep.ld_out + n] = fmaf(f.x, (float)v, -corr);
-        } else {
-          const float4 f = *reinterpret_cast<const float4*>(rowf + lr * 4);
-          float corr = 0.f;
-          if (ep.ec) {
-            float s = cu;
-            for (int64_t b = 0; b < ep.B; ++b) s = fmaf(ep.ebar[b * g.M + m], (float)ep.colsum[b * g.N + n], s);
-            corr = f.y * s;
+        if (n_ok && m < g.M) {
+          const int32_t v = acc[i][j][r];
+          if constexpr (EPI == EPI_RAW) {
+            reinterpret_cast<int32_t*>(ep.out)[m * ep.ld_out + n] = v;
+          } else if constexpr (EPI == EPI_DX) {
+            const float4 f = rowf[lr];
+            float corr = 0.f;
+            if (ep.ec) corr = fmaf(f.z, colA, f.y * ep.vec[(int64_t)__float_as_int(f.w) * g.N + n]);
+            reinterpret_cast<float*>(ep.out)[m * ep.ld_out + n] = fmaf(f.x, (float)v, -corr);
+          } else {
+            const float4 f = rowf[lr];
+            float corr = 0.f;
+            if (ep.ec) {
+              float s = f.y * colA;
+#pragma unroll
+              for (int b = 0; b < kMaxB; ++b)
+                if (b < ep.B) s = fmaf(roweb[b * BM + lr], colB[b], s);
+              corr = s;
+            }
+            reinterpret_cast<float*>(ep.out)[m * ep.ld_out + n] = fmaf(f.x, (float)v, -corr);
           }
-          reinterpret_cast<float*>(ep.out)[m * ep.ld_out + n] = fmaf(f.x, (float)v, -corr);
         }
       }
     }
   }
+}
+
+// dW correction terms of examples 8 .. B-1 (the GEMM epilogue applies examples 0 .. 7):
+// dW[j][i] -= sum_b ebar[b][j] * xs[b][i] / s_w[j].
+__global__ __launch_bounds__(256) void dw_rank_update_kernel(float* __restrict__ dW, int64_t ld, int64_t D,
+                                                             int64_t N, int64_t B, const float* __restrict__ ebar,
+                                                             const int32_t* __restrict__ xs,
+                                                             const float* __restrict__ sw) {
+  const int64_t j = blockIdx.y;
+  const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (n >= N) return;
+  float s = 0.f;
+  for (int64_t b = 8; b < B; ++b) s = fmaf(ebar[b * D + j], (float)xs[b * N + n], s);
+  const float inv = sw ? __fdiv_rn(1.f, sw[j]) : 1.f;
+  dW[j * ld + n] -= inv * s;
 }
 
 // -------------------------------------------------------------- GEMVs ----
@@ -388,6 +459,7 @@ hipError_t fill_zero(float* p, int64_t n, hipStream_t st) {
   return hipGetLastError();
 }
 
+
 __global__ __launch_bounds__(256) void gemv_reduce_kernel(const float* __restrict__ part, int64_t nchunks,
                                                           int64_t count, float* __restrict__ out) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -421,11 +493,12 @@ hipError_t run_gemm(const GemmParams& g, const EpiParams& ep, hipStream_t st) {
   const GemmTiming ev = tm;
   tm = GemmTiming{};
   const int nblocks = g.tiles_m * g.tiles_n;
-  if (ev.start) hipEventRecord(ev.start, st);
+  if (ev.start && hipEventRecord(ev.start, st) != hipSuccess) return hipErrorInvalidValue;
   if (nblocks > 0)
     hipLaunchKernelGGL((gemm_i8_kernel<A_KMAJOR, EPI>), dim3((unsigned)nblocks), dim3(kGemmThreads), 0, st, g, ep);
-  if (ev.stop) hipEventRecord(ev.stop, st);
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (ev.stop && hipEventRecord(ev.stop, st) != hipSuccess && e == hipSuccess) e = hipErrorInvalidValue;
+  return e;
 }
 
 GemmParams make_gemm(const int8_t* A, int64_t lda, const int8_t* B, int64_t ldb, int64_t M, int64_t N, int64_t K) {
@@ -503,7 +576,11 @@ hipError_t launch_backward_dw(const DwArgs& a, hipStream_t st) {
   // dW = Q^T Xq: A[m=j][k=t] = Q[t][j] (M-contiguous), B = Xq [T x d_in] (N-contiguous)
   const GemmParams g = make_gemm(a.Q, a.ld_q, a.X, a.ld_x, a.D, a.d_in, a.T);
   if (a.out_dt == S3R_I32_RAW) return run_gemm<false, EPI_RAW>(g, ep, st);
-  return run_gemm<false, EPI_DW>(g, ep, st);
+  hipError_t e = run_gemm<false, EPI_DW>(g, ep, st);
+  if (e != hipSuccess || !ep.ec || B <= 8 || a.D == 0 || a.d_in == 0) return e;
+  hipLaunchKernelGGL(dw_rank_update_kernel, dim3((unsigned)((a.d_in + 255) / 256), (unsigned)a.D), dim3(256), 0, st,
+                     (float*)a.out, a.ld_out, a.D, a.d_in, B, a.ec_col, a.xs, a.sw);
+  return hipGetLastError();
 }
 
 }  // namespace s3r
