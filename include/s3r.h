@@ -130,7 +130,8 @@ int s3r_quantize(const s3r_qdesc* desc,
  * pointers, leading dims that are multiples of 16 and below 2^24, and
  * (rows + 320) * ld < 2^32 bytes; K <= 131072.
  * out_dt: S3R_F32 (dequantised, corrected per desc->ec) or S3R_I32_RAW (raw
- * int32 accumulators, no dequantisation, no correction).
+ * int32 accumulators, no dequantisation, no correction); the output's leading
+ * dim must be below 2^22 and its base 4-byte aligned.
  *
  * s3r_backward_dx: dX [T x d_in] = diag(1/s_x) (Delta Q - P(E')) Wq.
  * S3R page, "Quantized Backpropagation" (activation-gradient product) and

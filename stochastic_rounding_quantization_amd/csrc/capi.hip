@@ -12,6 +12,7 @@ namespace {
 using namespace s3r;
 
 constexpr int64_t kMaxK = 131072;   // int32 accumulators: K * 127^2 < 2^31
+constexpr int64_t kMaxLdOut = (int64_t)1 << 22;   // one 256-row output tile stays below 2^32 bytes
 
 bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -113,7 +114,7 @@ int s3r_backward_dx(const s3r_qdesc* d, const int8_t* Q, int64_t ld_q, const flo
   const int64_t T = d->rows, D = d->cols;
   if (d_in < 0 || D > kMaxK) return S3R_ERR_INVALID_ARG;
   const bool out_nonempty = T > 0 && d_in > 0;
-  if (!delta || (out_nonempty && !dX) || ld_dx < d_in) return S3R_ERR_INVALID_ARG;
+  if (!delta || (out_nonempty && !dX) || ld_dx < d_in || ld_dx >= kMaxLdOut) return S3R_ERR_INVALID_ARG;
   if (out_nonempty && ((uintptr_t)dX & 3u)) return S3R_ERR_INVALID_ARG;
   if ((rc = check_gemm_operand(Q, ld_q, T, D, T > 0 && D > 0))) return rc;
   if ((rc = check_gemm_operand(Wq, ld_w, D, d_in, D > 0 && d_in > 0))) return rc;
@@ -141,7 +142,7 @@ int s3r_backward_dw(const s3r_qdesc* d, const int8_t* Q, int64_t ld_q, const flo
   const int64_t T = d->rows, D = d->cols;
   if (d_in < 0 || T > kMaxK) return S3R_ERR_INVALID_ARG;
   const bool out_nonempty = D > 0 && d_in > 0;
-  if (!delta || (out_nonempty && !dW) || ld_dw < d_in) return S3R_ERR_INVALID_ARG;
+  if (!delta || (out_nonempty && !dW) || ld_dw < d_in || ld_dw >= kMaxLdOut) return S3R_ERR_INVALID_ARG;
   if (out_nonempty && ((uintptr_t)dW & 3u)) return S3R_ERR_INVALID_ARG;
   if ((rc = check_gemm_operand(Q, ld_q, T, D, T > 0 && D > 0))) return rc;
   if ((rc = check_gemm_operand(Xq, ld_x, T, d_in, T > 0 && d_in > 0))) return rc;

@@ -21,7 +21,9 @@
 //     position c ^ f(r), f(r) = ((r >> 1) ^ (r >> 3)) & 3; fragments are read
 //     with ds_read_b128 (lane: row l%32, 16 consecutive k).
 //   M/N-contiguous tile: 64 k-rows x 256 B; chunk c of k-row r sits at
-//     c ^ (r & 7); fragments are read with two ds_read_b64_tr_b8: within each
+//     c ^ swz_m(r), swz_m(r) = (r & 7) | ((r >> 4) & 1) << 3 (the two
+//     half-waves of a read use k-rows 16 apart and so land in different
+//     halves of the banks); fragments are read with two ds_read_b64_tr_b8: within each
 //     16-lane group, lane L fetches 8 bytes of k-row kb + L/2 at column
 //     nb + 8(L%2), and the hardware hands lane i the bytes of column nb + i
 //     from the 8 k-rows, so a lane ends up with 16 consecutive k of one
@@ -51,22 +53,23 @@ constexpr int kHalf = 16384;
 constexpr int kGroupM = 8;            // grouped tile order: 8 tile-rows per group
 constexpr int kNumXcd = 8;
 
-// The four pipeline stages are separate LDS objects so that the compiler can
-// tell a stage being read from the stages being filled by in-flight DMA.
+// The pipeline stages are separate LDS objects so that the compiler can tell a
+// stage being read from the stages being filled by in-flight DMA.
+constexpr int kStages = 5;            // 5 x 32 KB = the CU's 160 KB of LDS
 __shared__ __attribute__((aligned(1024))) uint8_t g_stage0[kStageBytes];
 __shared__ __attribute__((aligned(1024))) uint8_t g_stage1[kStageBytes];
 __shared__ __attribute__((aligned(1024))) uint8_t g_stage2[kStageBytes];
 __shared__ __attribute__((aligned(1024))) uint8_t g_stage3[kStageBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t g_stage4[kStageBytes];
 
 template <int S>
 __device__ __forceinline__ uint8_t* stage() {
   if constexpr (S == 0) return g_stage0;
   else if constexpr (S == 1) return g_stage1;
   else if constexpr (S == 2) return g_stage2;
-  else return g_stage3;
+  else if constexpr (S == 3) return g_stage3;
+  else return g_stage4;
 }
-
-enum { EPI_RAW = 0, EPI_DX = 1, EPI_DW = 2 };
 
 struct EpiParams {
   const float* delta; int per_token;
@@ -88,6 +91,7 @@ struct GemmParams {
 };
 
 __device__ __forceinline__ int swz_k(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+__device__ __forceinline__ int swz_m(int r) { return (r & 7) | (((r >> 4) & 1) << 3); }
 
 // s_waitcnt immediates (gfx9 encoding): wait for at most n vector-memory ops / no LDS ops.
 #define S3R_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | 0x70 | 0xF00)
@@ -104,7 +108,7 @@ __device__ __forceinline__ int swz_k(int r) { return ((r >> 1) ^ (r >> 3)) & 3; 
 // Each wave fills 4 of the 16 1-KB blocks of the A tile and 4 of the B tile.
 // Block blk, lane l:
 //   K-contiguous: row = 16 blk + l/4, position p = l%4 holds chunk c = p ^ swz_k(row)
-//   M/N-contiguous: k-row = 4 blk + l/16, position p = l%16 holds chunk c = p ^ (k-row & 7)
+//   M/N-contiguous: k-row = 4 blk + l/16, position p = l%16 holds chunk c = p ^ swz_m(k-row)
 constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit dword format (gfx9 family)
 
 struct LoadMap {           // per-thread byte offsets (tile origin + position), for 4 blocks of A and of B
@@ -126,11 +130,11 @@ __device__ __forceinline__ LoadMap make_loadmap(const GemmParams& g, int64_t m0,
       m.a_off[q] = (uint32_t)((m0 + row) * g.lda + c * 16);
     } else {
       const int kr = blk * 4 + (lane >> 4);
-      const int c = (lane & 15) ^ (kr & 7);
+      const int c = (lane & 15) ^ swz_m(kr);
       m.a_off[q] = (uint32_t)(kr * g.lda + m0 + c * 16);
     }
     const int kr = blk * 4 + (lane >> 4);
-    const int c = (lane & 15) ^ (kr & 7);
+    const int c = (lane & 15) ^ swz_m(kr);
     m.b_off[q] = (uint32_t)(kr * g.ldb + n0 + c * 16);
   }
   m.a_step = (uint32_t)(A_KMAJOR ? BK : BK * g.lda);
@@ -174,13 +178,14 @@ __device__ __forceinline__ FragMap make_fragmap() {
     f.a_k[kk] = (wm * 128 + r) * 64 + ((c ^ swz_k(r)) << 4);
   }
   const int grp = lane >> 4, L = lane & 15;
-  const int krow = 16 * (grp >> 1) + (L >> 1);        // k-row for kk = 0, first read; krow & 7 == L >> 1
+  const int krow = 16 * (grp >> 1) + (L >> 1);        // k-row for kk = 0, first read
+  const int x = swz_m(krow);                           // also the swizzle of krow + 8 and krow + 32
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int ca = (wm * 128 + i * 32 + 16 * (grp & 1)) >> 4;
-    f.a_t[i] = krow * 256 + ((ca ^ (L >> 1)) << 4) + 8 * (L & 1);
+    f.a_t[i] = krow * 256 + ((ca ^ x) << 4) + 8 * (L & 1);
     const int cb = (wn * 128 + i * 32 + 16 * (grp & 1)) >> 4;
-    f.b_t[i] = krow * 256 + ((cb ^ (L >> 1)) << 4) + 8 * (L & 1);
+    f.b_t[i] = krow * 256 + ((cb ^ x) << 4) + 8 * (L & 1);
   }
   return f;
 }
@@ -192,58 +197,170 @@ __device__ __forceinline__ v4i tr_pair(const uint8_t* p) {
 }
 
 // Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
-constexpr int kSgMfma = 0x008, kSgDsRead = 0x100;
+constexpr int kSgMfma = 0x008, kSgDsRead = 0x100, kSgVmem = 0x010;
 
+struct Frags { v4i a[4], b[4]; };
+
+// Fragments of half-step kk (k 32kk .. 32kk+31) of stage S.
 template <int S, bool A_KMAJOR>
-__device__ __forceinline__ void compute_stage(const FragMap& f, v16i (&acc)[4][4]) {
+__device__ __forceinline__ void read_frags(const FragMap& f, int kk, Frags& fr) {
   const uint8_t* st = stage<S>();
-  v4i af[2][4], bf[2][4];
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if constexpr (A_KMAJOR) af[kk][i] = *reinterpret_cast<const v4i*>(st + f.a_k[kk] + i * 2048);
-      else af[kk][i] = tr_pair(st + f.a_t[i] + kk * 8192);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) bf[kk][j] = tr_pair(st + kHalf + f.b_t[j] + kk * 8192);
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (A_KMAJOR) fr.a[i] = *reinterpret_cast<const v4i*>(st + f.a_k[kk] + i * 2048);
+    else fr.a[i] = tr_pair(st + f.a_t[i] + kk * 8192);
   }
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[kk][i], bf[kk][j], acc[i][j], 0, 0, 0);
-  // schedule: the first half-step's reads, then its 16 MFMAs interleaved with the
-  // second half-step's reads, then the second half-step's MFMAs
-  constexpr int NR = A_KMAJOR ? 12 : 16;   // LDS reads per half-step
-  __builtin_amdgcn_sched_group_barrier(kSgDsRead, NR, 0);
-#pragma unroll
-  for (int x = 0; x < NR; ++x) {
-    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
-  }
-  if constexpr (NR < 16) __builtin_amdgcn_sched_group_barrier(kSgMfma, 16 - NR, 0);
-  __builtin_amdgcn_sched_group_barrier(kSgMfma, 16, 0);
+  for (int j = 0; j < 4; ++j) fr.b[j] = tr_pair(st + kHalf + f.b_t[j] + kk * 8192);
 }
 
-// One K step on stage S = kt % 4: wait for its data (8 loads per later step of
-// this wave may stay in flight), refill stage (S+3)%4 with step kt+3, multiply.
+__device__ __forceinline__ void mfma16(const Frags& fr, v16i (&acc)[4][4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fr.a[i], fr.b[j], acc[i][j], 0, 0, 0);
+}
+
+// 16 MFMAs with the NR LDS reads issued in between, one after each MFMA, and
+// (NV > 0) the stage refill's NV buffer loads spread over the MFMAs, so the
+// memory pipeline is never handed a burst that stalls instruction issue.
+template <int NR, int NV>
+__device__ __forceinline__ void interleave_schedule() {
+#pragma unroll
+  for (int x = 0; x < 16; ++x) {
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+    if (x < NR) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+    if (NV > 0 && (x % (16 / (NV > 0 ? NV : 1))) == 0) __builtin_amdgcn_sched_group_barrier(kSgVmem, 1, 0);
+  }
+}
+
+// One K step on stage S = kt % kStages.  On entry `cur` holds the stage's
+// first half-step fragments.  The barrier publishes stage kt+1 (this wave has
+// waited for its own loads of it) and retires stage kt-1, which is refilled
+// with step kt+4.  The second half-step's fragments are read during the first
+// half's MFMAs, and the next stage's first fragments during the second half's.
 template <int S, bool A_KMAJOR>
-__device__ __forceinline__ void k_step(const LoadMap& lm, const FragMap& fm, int kt, int nk, v16i (&acc)[4][4]) {
-  const int later = nk - 1 - kt;
-  if (later >= 2) S3R_WAIT_VM(16);
-  else if (later == 1) S3R_WAIT_VM(8);
-  else S3R_WAIT_VM(0);
-  S3R_WAIT_LGKM0();                 // this wave's reads of the stage about to be refilled are done
+__device__ __forceinline__ void k_step(const LoadMap& lm, const FragMap& fm, int kt, int nk, Frags& cur,
+                                       v16i (&acc)[4][4]) {
+  constexpr int NR = A_KMAJOR ? 12 : 16;   // LDS reads per half-step
+  // Every step refills one stage, also past the last step (those loads read past
+  // the end of the data or land in retired stages), so exactly the loads of
+  // stages kt+2 and kt+3 may still be in flight here.
+  S3R_WAIT_VM(16);
+  S3R_WAIT_LGKM0();
   __builtin_amdgcn_s_barrier();
-  if (kt + 3 < nk) load_stage<(S + 3) & 3>(lm, kt + 3);
-  compute_stage<S, A_KMAJOR>(fm, acc);
+  load_stage<(S + 4) % kStages>(lm, kt + 4);
+  Frags nxt;
+  read_frags<S, A_KMAJOR>(fm, 1, nxt);
+  mfma16(cur, acc);
+  interleave_schedule<NR, 8>();
+  // next stage's first fragments (after the last step this reads a stale stage; unused)
+  read_frags<(S + 1) % kStages, A_KMAJOR>(fm, 0, cur);
+  mfma16(nxt, acc);
+  interleave_schedule<NR, 0>();
+}
+
+// ---------------------------------------------------------------- epilogue ----
+// 32x32 block output layout: lane l, register r -> row (r/4)*8 + (l/32)*4 + r%4, column l%32.
+// Stores go through a buffer descriptor over the tile's rows of the output
+// (rows past M fall outside it and are dropped by the range check); columns
+// past N are masked per column block.  Per-row byte offsets are uniform.
+enum { EPI_RAW = 0, EPI_DX = 1, EPI_DW = 2 };
+constexpr int kMaxB = 8;   // examples whose dW correction terms the epilogue applies
+
+__device__ __forceinline__ int row_in_block(int r) { return (r >> 2) * 8 + (r & 3); }
+
+template <int EPI, bool EC, bool GATHER>
+__device__ __forceinline__ void epilogue(const GemmParams& g, const EpiParams& ep, int64_t m0, int64_t n0,
+                                         v16i (&acc)[4][4]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int rows_here = (int)min((int64_t)BM, g.M - m0);
+  const uint32_t esz = 4;
+  const uint32_t ld4 = (uint32_t)ep.ld_out * esz;
+  __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((char*)ep.out + (m0 * ep.ld_out) * esz), (short)0, (int)((uint32_t)rows_here * ld4), kRsrcWord3);
+  const float4* rowf = reinterpret_cast<const float4*>(g_stage0);   // per-row factors
+  const float* roweb = reinterpret_cast<const float*>(g_stage1);    // dW: ebar[b][row] / s_w[row]
+  const int lane_row = wm * 128 + (lane >> 5) * 4;                  // + i*32 + row_in_block(r)
+
+  // per-column values of this lane, one per column block j
+  float colA[4], colV[4], colB[kMaxB][4];
+  bool n_ok[4];
+  uint32_t voff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t n = n0 + wn * 128 + j * 32 + (lane & 31);
+    n_ok[j] = n < g.N;
+    voff[j] = (uint32_t)(lane_row * ld4 + n * esz);
+    colA[j] = 0.f; colV[j] = 0.f;
+#pragma unroll
+    for (int b = 0; b < kMaxB; ++b) colB[b][j] = 0.f;
+    if (EC && n_ok[j]) {
+      if constexpr (EPI == EPI_DX) {
+        colA[j] = (float)ep.colsum[n];                                   // r_W[n]
+        if constexpr (!GATHER) colV[j] = ep.vec[(m0 / ep.S) * g.N + n];  // v_b[n], the tile's example
+      } else if constexpr (EPI == EPI_DW) {
+        colA[j] = ep.u[n];
+#pragma unroll
+        for (int b = 0; b < kMaxB; ++b)
+          if (b < ep.B) colB[b][j] = (float)ep.colsum[b * g.N + n];     // xs_b[n]
+      }
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      // four consecutive rows of this lane: lr = lane_row + i*32 + rq*8 + rr
+      float4 f[4];
+      float eb[4][kMaxB];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int lr = lane_row + i * 32 + rq * 8 + rr;
+        if constexpr (EPI != EPI_RAW) f[rr] = rowf[lr];
+        if constexpr (EPI == EPI_DW && EC) {
+#pragma unroll
+          for (int b = 0; b < kMaxB; ++b) eb[rr][b] = b < ep.B ? roweb[b * BM + lr] : 0.f;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (!n_ok[j]) continue;
+        float gv[4];
+        if constexpr (EPI == EPI_DX && EC && GATHER) {
+          const int64_t n = n0 + wn * 128 + j * 32 + (lane & 31);
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) gv[rr] = ep.vec[(int64_t)__float_as_int(f[rr].w) * g.N + n];
+        }
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int r = rq * 4 + rr;
+          const int32_t v = acc[i][j][r];
+          const uint32_t soff = (uint32_t)(i * 32 + rq * 8 + rr) * ld4;
+          if constexpr (EPI == EPI_RAW) {
+            __builtin_amdgcn_raw_buffer_store_b32(v, ro, voff[j], soff, 0);
+          } else {
+            float corr = 0.f;
+            if constexpr (EC && EPI == EPI_DX) corr = fmaf(f[rr].z, colA[j], f[rr].y * (GATHER ? gv[rr] : colV[j]));
+            if constexpr (EC && EPI == EPI_DW) {
+              float t = f[rr].y * colA[j];
+#pragma unroll
+              for (int b = 0; b < kMaxB; ++b) t = fmaf(eb[rr][b], colB[b][j], t);
+              corr = t;
+            }
+            const float o = fmaf(f[rr].x, (float)v, -corr);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(o), ro, voff[j], soff, 0);
+          }
+        }
+      }
+    }
+  }
 }
 
 // ----------------------------------------------------------------- kernel ----
-template <bool A_KMAJOR, int EPI>
+template <bool A_KMAJOR, int EPI, bool EC>
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmParams g, EpiParams ep) {
   // XCD-aware numbering: hardware block ids go round-robin over the 8 XCDs;
   // give each XCD a contiguous range of logical tiles.
@@ -255,13 +372,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmParams g, 
   const int gsz = min(g.tiles_m - first_m, kGroupM);
   const int tm = first_m + (bid % group) % gsz;
   const int tn = (bid % group) / gsz;
-
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int nk = (int)((g.K + BK - 1) / BK);
-
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
 
   v16i acc[4][4];
 #pragma unroll
@@ -271,24 +383,28 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmParams g, 
 
   const LoadMap lm = make_loadmap<A_KMAJOR>(g, m0, n0);
   const FragMap fm = make_fragmap<A_KMAJOR>();
-  if (nk > 0) load_stage<0>(lm, 0);
-  if (nk > 1) load_stage<1>(lm, 1);
-  if (nk > 2) load_stage<2>(lm, 2);
-  for (int kt = 0; kt < nk; kt += 4) {
-    k_step<0, A_KMAJOR>(lm, fm, kt, nk, acc);
-    if (kt + 1 < nk) k_step<1, A_KMAJOR>(lm, fm, kt + 1, nk, acc);
-    if (kt + 2 < nk) k_step<2, A_KMAJOR>(lm, fm, kt + 2, nk, acc);
-    if (kt + 3 < nk) k_step<3, A_KMAJOR>(lm, fm, kt + 3, nk, acc);
+  load_stage<0>(lm, 0);
+  load_stage<1>(lm, 1);
+  load_stage<2>(lm, 2);
+  load_stage<3>(lm, 3);
+  Frags cur;
+  S3R_WAIT_VM(24);
+  __builtin_amdgcn_s_barrier();
+  read_frags<0, A_KMAJOR>(fm, 0, cur);
+  for (int kt = 0; kt < nk; kt += kStages) {
+    k_step<0, A_KMAJOR>(lm, fm, kt, nk, cur, acc);
+    if (kt + 1 < nk) k_step<1, A_KMAJOR>(lm, fm, kt + 1, nk, cur, acc);
+    if (kt + 2 < nk) k_step<2, A_KMAJOR>(lm, fm, kt + 2, nk, cur, acc);
+    if (kt + 3 < nk) k_step<3, A_KMAJOR>(lm, fm, kt + 3, nk, cur, acc);
+    if (kt + 4 < nk) k_step<4, A_KMAJOR>(lm, fm, kt + 4, nk, cur, acc);
   }
   S3R_WAIT_VM(0);
   S3R_WAIT_LGKM0();
   __builtin_amdgcn_s_barrier();
 
-  // ------------------------------------------------------------ epilogue ----
-  // 32x32 block output layout: lane l, register r -> row (r/4)*8 + (l/32)*4 + r%4, column l%32.
-  float4* rowf = reinterpret_cast<float4*>(g_stage0);   // per-row factors of the tile
-  float* roweb = reinterpret_cast<float*>(g_stage1);    // dW: ebar[b][row] / s_w[row], b < 8
-  constexpr int kMaxB = 8;
+  // per-row factors of the tile into LDS (the stages are free now)
+  float4* rowf = reinterpret_cast<float4*>(g_stage0);
+  float* roweb = reinterpret_cast<float*>(g_stage1);
   if constexpr (EPI == EPI_DX) {
     // x: Delta_t / s_x[t], y: 1 / s_x[t], z: (eps_t - mu_b) / s_x[t], w: example index
     for (int r = threadIdx.x; r < BM; r += kGemmThreads) {
@@ -299,7 +415,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmParams g, 
         const float inv = ep.row_scale ? __fdiv_rn(1.f, ep.row_scale[tt]) : 1.f;
         f.x = d * inv;
         f.y = inv;
-        if (ep.ec) {
+        if (EC) {
           const int64_t b = tt / ep.S;
           f.z = (ep.ec_row[tt] - ep.ec_mean[b]) * inv;
           f.w = __int_as_float((int)b);
@@ -307,7 +423,6 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmParams g, 
       }
       rowf[r] = f;
     }
-    __syncthreads();
   } else if constexpr (EPI == EPI_DW) {
     // x: Delta / s_w[j], y: 1 / s_w[j]; roweb[b * BM + r] = ebar[b][j] / s_w[j]
     for (int r = threadIdx.x; r < BM; r += kGemmThreads) {
@@ -317,62 +432,19 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmParams g, 
         const float inv = ep.row_scale ? __fdiv_rn(1.f, ep.row_scale[j]) : 1.f;
         f.x = ep.delta[0] * inv;
         f.y = inv;
-        if (ep.ec)
-          for (int64_t b = 0; b < ep.B && b < kMaxB; ++b) roweb[b * BM + r] = ep.ebar[b * g.M + j] * inv;
       }
+      if (EC)
+        for (int64_t b = 0; b < ep.B && b < kMaxB; ++b) roweb[b * BM + r] = j < g.M ? ep.ebar[b * g.M + j] * f.y : 0.f;
       rowf[r] = f;
     }
-    __syncthreads();
   }
-
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int64_t n = n0 + wn * 128 + j * 32 + (lane & 31);
-    const bool n_ok = n < g.N;
-    // per-column values of this lane's column
-    float colA = 0.f, colB[kMaxB];
-#pragma unroll
-    for (int b = 0; b < kMaxB; ++b) colB[b] = 0.f;
-    if constexpr (EPI == EPI_DX) {
-      if (ep.ec && n_ok) colA = (float)ep.colsum[n];                    // r_W[n]
-    } else if constexpr (EPI == EPI_DW) {
-      if (ep.ec && n_ok) {
-        colA = ep.u[n];
-#pragma unroll
-        for (int b = 0; b < kMaxB; ++b)
-          if (b < ep.B) colB[b] = (float)ep.colsum[b * g.N + n];        // xs_b[n]
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int lr = wm * 128 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        const int64_t m = m0 + lr;
-        if (n_ok && m < g.M) {
-          const int32_t v = acc[i][j][r];
-          if constexpr (EPI == EPI_RAW) {
-            reinterpret_cast<int32_t*>(ep.out)[m * ep.ld_out + n] = v;
-          } else if constexpr (EPI == EPI_DX) {
-            const float4 f = rowf[lr];
-            float corr = 0.f;
-            if (ep.ec) corr = fmaf(f.z, colA, f.y * ep.vec[(int64_t)__float_as_int(f.w) * g.N + n]);
-            reinterpret_cast<float*>(ep.out)[m * ep.ld_out + n] = fmaf(f.x, (float)v, -corr);
-          } else {
-            const float4 f = rowf[lr];
-            float corr = 0.f;
-            if (ep.ec) {
-              float s = f.y * colA;
-#pragma unroll
-              for (int b = 0; b < kMaxB; ++b)
-                if (b < ep.B) s = fmaf(roweb[b * BM + lr], colB[b], s);
-              corr = s;
-            }
-            reinterpret_cast<float*>(ep.out)[m * ep.ld_out + n] = fmaf(f.x, (float)v, -corr);
-          }
-        }
-      }
-    }
+  __syncthreads();
+  if constexpr (EPI == EPI_DX && EC) {
+    const int64_t last = min(m0 + BM, g.M) - 1;
+    if (m0 / ep.S == last / ep.S) epilogue<EPI, EC, false>(g, ep, m0, n0, acc);
+    else epilogue<EPI, EC, true>(g, ep, m0, n0, acc);
+  } else {
+    epilogue<EPI, EC, false>(g, ep, m0, n0, acc);
   }
 }
 
@@ -487,7 +559,7 @@ size_t gemv_part_bytes(int64_t K, int64_t N, int64_t nb) {
   return align_up((size_t)nchunks * nb * N * 4, 256);
 }
 
-template <bool A_KMAJOR, int EPI>
+template <bool A_KMAJOR, int EPI, bool EC>
 hipError_t run_gemm(const GemmParams& g, const EpiParams& ep, hipStream_t st) {
   GemmTiming& tm = gemm_timing();
   const GemmTiming ev = tm;
@@ -495,7 +567,7 @@ hipError_t run_gemm(const GemmParams& g, const EpiParams& ep, hipStream_t st) {
   const int nblocks = g.tiles_m * g.tiles_n;
   if (ev.start && hipEventRecord(ev.start, st) != hipSuccess) return hipErrorInvalidValue;
   if (nblocks > 0)
-    hipLaunchKernelGGL((gemm_i8_kernel<A_KMAJOR, EPI>), dim3((unsigned)nblocks), dim3(kGemmThreads), 0, st, g, ep);
+    hipLaunchKernelGGL((gemm_i8_kernel<A_KMAJOR, EPI, EC>), dim3((unsigned)nblocks), dim3(kGemmThreads), 0, st, g, ep);
   hipError_t e = hipGetLastError();
   if (ev.stop && hipEventRecord(ev.stop, st) != hipSuccess && e == hipSuccess) e = hipErrorInvalidValue;
   return e;
@@ -549,8 +621,9 @@ hipError_t launch_backward_dx(const DxArgs& a, hipStream_t st) {
     ep.vec = v;
   }
   const GemmParams g = make_gemm(a.Q, a.ld_q, a.W, a.ld_w, a.T, a.d_in, a.D);
-  if (a.out_dt == S3R_I32_RAW) return run_gemm<true, EPI_RAW>(g, ep, st);
-  return run_gemm<true, EPI_DX>(g, ep, st);
+  if (a.out_dt == S3R_I32_RAW) return run_gemm<true, EPI_RAW, false>(g, ep, st);
+  if (ep.ec) return run_gemm<true, EPI_DX, true>(g, ep, st);
+  return run_gemm<true, EPI_DX, false>(g, ep, st);
 }
 
 hipError_t launch_backward_dw(const DwArgs& a, hipStream_t st) {
@@ -575,8 +648,8 @@ hipError_t launch_backward_dw(const DwArgs& a, hipStream_t st) {
   }
   // dW = Q^T Xq: A[m=j][k=t] = Q[t][j] (M-contiguous), B = Xq [T x d_in] (N-contiguous)
   const GemmParams g = make_gemm(a.Q, a.ld_q, a.X, a.ld_x, a.D, a.d_in, a.T);
-  if (a.out_dt == S3R_I32_RAW) return run_gemm<false, EPI_RAW>(g, ep, st);
-  hipError_t e = run_gemm<false, EPI_DW>(g, ep, st);
+  if (a.out_dt == S3R_I32_RAW) return run_gemm<false, EPI_RAW, false>(g, ep, st);
+  hipError_t e = ep.ec ? run_gemm<false, EPI_DW, true>(g, ep, st) : run_gemm<false, EPI_DW, false>(g, ep, st);
   if (e != hipSuccess || !ep.ec || B <= 8 || a.D == 0 || a.d_in == 0) return e;
   hipLaunchKernelGGL(dw_rank_update_kernel, dim3((unsigned)((a.d_in + 255) / 256), (unsigned)a.D), dim3(256), 0, st,
                      (float*)a.out, a.ld_out, a.D, a.d_in, B, a.ec_col, a.xs, a.sw);
