@@ -464,59 +464,89 @@ __global__ __launch_bounds__(256) void dw_rank_update_kernel(float* __restrict__
 }
 
 // -------------------------------------------------------------- GEMVs ----
-// out_part[jc][b][n] = sum over k in chunk jc of coef(b, k) * P[k][n]  (P int8 [K x N])
+// out_part[c][b][n] = sum over rows k of chunk c of coef(b, k) * P[k][n]   (P int8 [K x N])
 // Coefficients: VEC mode coef(b, k) = C[b * K + k] (the channel means ebar);
-// TOKEN mode (b = 0 only) coef(k) = ec_row[k] - ec_mean[k / S].
+// TOKEN mode (one row, b = 0) coef(k) = ec_row[k] - ec_mean[k / S].
+// A block covers 1024 columns (16 per lane, 16-byte loads) and kGvRows rows,
+// split over its 4 waves; the waves' sums are added in LDS in a fixed order.
 constexpr int kGvThreads = 256;
-constexpr int kGvCols = 8;         // columns per thread
-constexpr int kGvRows = 128;       // k rows per chunk
-constexpr int kGvB = 4;            // coefficient rows per pass
+constexpr int kGvColsPerLane = 16;
+constexpr int kGvCols = 64 * kGvColsPerLane;   // 1024 columns per block
+constexpr int kGvRows = 256;                   // rows per chunk (block)
 
+template <int NB>
 __global__ __launch_bounds__(kGvThreads) void gemv_partial_kernel(
     const int8_t* __restrict__ P, int64_t ld, int64_t K, int64_t N, int64_t nb, int token_mode,
     const float* __restrict__ C, const float* __restrict__ ec_row, const float* __restrict__ ec_mean, int64_t S,
     float* __restrict__ part) {
-  const int64_t n0 = ((int64_t)blockIdx.x * kGvThreads + threadIdx.x) * kGvCols;
+  __shared__ float coef[NB][kGvRows];
+  __shared__ float red[4][NB][kGvCols];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t n0 = (int64_t)blockIdx.x * kGvCols + lane * kGvColsPerLane;
   const int64_t k0 = (int64_t)blockIdx.y * kGvRows;
-  const int64_t k1 = min(k0 + kGvRows, K);
-  const int jc = blockIdx.y;
-  for (int64_t b0 = 0; b0 < nb; b0 += kGvB) {
-    float acc[kGvB][kGvCols];
+  const int rows = (int)min((int64_t)kGvRows, K - k0);
+  const int chunk = blockIdx.y;
+  for (int64_t b0 = 0; b0 < nb; b0 += NB) {
+    __syncthreads();
+    for (int r = threadIdx.x; r < kGvRows; r += kGvThreads) {
 #pragma unroll
-    for (int b = 0; b < kGvB; ++b)
-#pragma unroll
-      for (int c = 0; c < kGvCols; ++c) acc[b][c] = 0.f;
-    for (int64_t k = k0; k < k1; ++k) {
-      int8_t w[kGvCols];
-      const int8_t* p = P + k * ld + n0;
-      if (n0 + kGvCols <= N) {
-        const uint2 u = *reinterpret_cast<const uint2*>(p);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) { w[c] = (int8_t)(u.x >> (8 * c)); w[c + 4] = (int8_t)(u.y >> (8 * c)); }
-      } else {
-#pragma unroll
-        for (int c = 0; c < kGvCols; ++c) w[c] = (n0 + c < N) ? p[c] : (int8_t)0;
-      }
-      float cf[kGvB];
-#pragma unroll
-      for (int b = 0; b < kGvB; ++b) {
+      for (int b = 0; b < NB; ++b) {
         float x = 0.f;
-        if (b0 + b < nb) x = token_mode ? ec_row[k] - ec_mean[k / S] : C[(b0 + b) * K + k];
-        cf[b] = x;
+        if (r < rows && b0 + b < nb) {
+          const int64_t k = k0 + r;
+          x = token_mode ? ec_row[k] - ec_mean[k / S] : C[(b0 + b) * K + k];
+        }
+        coef[b][r] = x;
       }
+    }
+    __syncthreads();
+    float acc[NB][kGvColsPerLane];
 #pragma unroll
-      for (int c = 0; c < kGvCols; ++c) {
-        const float wf = (float)w[c];
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int b = 0; b < kGvB; ++b) acc[b][c] = fmaf(cf[b], wf, acc[b][c]);
+      for (int c = 0; c < kGvColsPerLane; ++c) acc[b][c] = 0.f;
+    auto accumulate = [&](const uint32_t (&w)[4], int r) {
+#pragma unroll
+      for (int c = 0; c < kGvColsPerLane; ++c) {
+        const float x = (float)(int8_t)(w[c >> 2] >> (8 * (c & 3)));
+#pragma unroll
+        for (int b = 0; b < NB; ++b) acc[b][c] = fmaf(coef[b][r], x, acc[b][c]);
+      }
+    };
+    if (n0 + kGvColsPerLane <= N && rows == kGvRows) {
+      // full block: 8 rows' 16-byte loads in flight per lane, no branches
+#pragma unroll 1
+      for (int r0 = wave; r0 < kGvRows; r0 += 4 * 8) {
+        uint4 u[8];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) u[x] = *reinterpret_cast<const uint4*>(P + (k0 + r0 + 4 * x) * ld + n0);
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          const uint32_t w[4] = {u[x].x, u[x].y, u[x].z, u[x].w};
+          accumulate(w, r0 + 4 * x);
+        }
+      }
+    } else {
+      for (int r = wave; r < rows; r += 4) {
+        const int8_t* p = P + (k0 + r) * ld + n0;
+        uint32_t w[4] = {0, 0, 0, 0};
+        for (int c = 0; c < kGvColsPerLane; ++c)
+          if (n0 + c < N) w[c >> 2] |= (uint32_t)(uint8_t)p[c] << (8 * (c & 3));
+        accumulate(w, r);
       }
     }
 #pragma unroll
-    for (int b = 0; b < kGvB; ++b) {
-      if (b0 + b >= nb) break;
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int c = 0; c < kGvCols; ++c)
-        if (n0 + c < N) part[((int64_t)jc * nb + b0 + b) * N + n0 + c] = acc[b][c];
+      for (int c = 0; c < kGvColsPerLane; ++c) red[wave][b][lane * kGvColsPerLane + c] = acc[b][c];
+    __syncthreads();
+    for (int i = threadIdx.x; i < NB * kGvCols; i += kGvThreads) {
+      const int b = i / kGvCols, c = i % kGvCols;
+      const int64_t n = (int64_t)blockIdx.x * kGvCols + c;
+      if (b0 + b < nb && n < N) {
+        const float v = ((red[0][b][c] + red[1][b][c]) + red[2][b][c]) + red[3][b][c];
+        part[((int64_t)chunk * nb + b0 + b) * N + n] = v;
+      }
     }
   }
 }
@@ -544,10 +574,13 @@ __global__ __launch_bounds__(256) void gemv_reduce_kernel(const float* __restric
 hipError_t run_gemv(const int8_t* P, int64_t ld, int64_t K, int64_t N, int64_t nb, int token_mode, const float* C,
                     const float* ec_row, const float* ec_mean, int64_t S, float* part, float* out, hipStream_t st) {
   const int64_t nchunks = (K + kGvRows - 1) / kGvRows;
-  const int64_t cols_per_block = (int64_t)kGvThreads * kGvCols;
-  dim3 grid((unsigned)((N + cols_per_block - 1) / cols_per_block), (unsigned)nchunks);
-  hipLaunchKernelGGL(gemv_partial_kernel, grid, dim3(kGvThreads), 0, st, P, ld, K, N, nb, token_mode, C, ec_row,
-                     ec_mean, S, part);
+  dim3 grid((unsigned)((N + kGvCols - 1) / kGvCols), (unsigned)nchunks);
+  if (token_mode || nb == 1)
+    hipLaunchKernelGGL(gemv_partial_kernel<1>, grid, dim3(kGvThreads), 0, st, P, ld, K, N, nb, token_mode, C, ec_row,
+                       ec_mean, S, part);
+  else
+    hipLaunchKernelGGL(gemv_partial_kernel<4>, grid, dim3(kGvThreads), 0, st, P, ld, K, N, nb, token_mode, C, ec_row,
+                       ec_mean, S, part);
   const int64_t count = nb * N;
   hipLaunchKernelGGL(gemv_reduce_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, st, part, nchunks,
                      count, out);

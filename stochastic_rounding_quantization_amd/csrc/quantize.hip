@@ -27,7 +27,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kRowsPerTile = 64;             // rows of one quantize tile
 constexpr int kColsPerTile = kWave * 8;      // 512 columns: 8 per lane
-constexpr int kAmaxBlocks = 256;
+constexpr int kAmaxBlocks = 1024;
 
 // Load 8 consecutive elements G[row][j0 .. j0+7] as fp32, zero past D.
 template <typename TIn, bool VEC>
@@ -112,23 +112,46 @@ __device__ __forceinline__ Step make_step(uint32_t abits) {
 }
 
 // ---------------------------------------------------------------- pass 1 ----
+// kAmaxBlocks blocks, each a contiguous band of rows; a thread loads one
+// 16-byte column chunk of kAmaxRows rows at a time, straight-line when the band
+// and the chunk are full.
+constexpr int kAmaxRows = 8;
+
 template <typename TIn, bool VEC>
 __global__ __launch_bounds__(kThreads) void amax_tensor_kernel(
     const TIn* __restrict__ G, int64_t ld, int64_t T, int64_t D,
     const float* __restrict__ sx, const float* __restrict__ sw, uint32_t* __restrict__ part) {
   const int64_t cpr = (D + 7) / 8;  // 8-element chunks per row
+  const int64_t rpb = (T + gridDim.x - 1) / gridDim.x;   // rows per block
+  const int64_t rb0 = (int64_t)blockIdx.x * rpb, rb1 = min(rb0 + rpb, T);
   uint32_t m = 0;
-  for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
-    const TIn* row = G + t * ld;
-    const float fx = sx ? sx[t] : 1.f;
+  for (int64_t t0 = rb0; t0 < rb1; t0 += kAmaxRows) {
+    const bool rows_full = t0 + kAmaxRows <= rb1;
     for (int64_t c = threadIdx.x; c < cpr; c += kThreads) {
-      float v[8], s[8];
-      load8<TIn, VEC>(row, c * 8, D, v);
+      float v[kAmaxRows][8];
+      float s[8];
       load8_scale(sw, c * 8, D, VEC, s);
+      if (VEC && rows_full && c * 8 + 8 <= D) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t b = abs_bits((v[i] * fx) * s[i]);
-        m = m > b ? m : b;
+        for (int u = 0; u < kAmaxRows; ++u) load8<TIn, true>(G + (t0 + u) * ld, c * 8, D, v[u]);
+      } else {
+#pragma unroll
+        for (int u = 0; u < kAmaxRows; ++u) {
+          if (t0 + u < rb1) load8<TIn, VEC>(G + (t0 + u) * ld, c * 8, D, v[u]);
+          else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[u][i] = 0.f;
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kAmaxRows; ++u) {
+        const float fx = (t0 + u < rb1 && sx) ? sx[t0 + u] : 1.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t b = abs_bits((v[u][i] * fx) * s[i]);
+          m = m > b ? m : b;
+        }
       }
     }
   }
@@ -189,7 +212,8 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
     QuantTile p, const TIn* __restrict__ G, const float* __restrict__ sx, const float* __restrict__ sw,
     int8_t* __restrict__ Q, float* __restrict__ delta_out, uint32_t* __restrict__ flags,
     const uint32_t* __restrict__ amax_part, int n_amax_part, const uint32_t* __restrict__ amax_rows,
-    float* __restrict__ row_part, float* __restrict__ col_part, int32_t* __restrict__ colq_part) {
+    float* __restrict__ row_part, float* __restrict__ col_part, int32_t* __restrict__ colq_part,
+    uint32_t* __restrict__ fin_counter) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int rtile = blockIdx.x;
@@ -198,6 +222,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
   const int64_t r0 = b * p.S + (int64_t)(rtile % p.tiles_per_example) * kRowsPerTile;
   const int64_t r1 = min(r0 + kRowsPerTile, (b + 1) * p.S);
   const int64_t j0 = (int64_t)ctile * kColsPerTile + lane * 8;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *fin_counter = 0u;   // for the finalize kernel
 
   __shared__ int32_t s_thr[kRowsPerTile];
   __shared__ uint32_t s_red[kThreads / kWave];
@@ -234,16 +259,32 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
 #pragma unroll
   for (int i = 0; i < 8; ++i) { col[i] = 0.f; colq[i] = 0; }
 
-  for (int64_t t = r0 + wave; t < r1; t += kThreads / kWave) {
+  // rows t = r0 + wave + 4u: kUnroll rows' loads are issued before any is used
+  constexpr int kUnroll = 4;
+  for (int64_t tb = r0 + wave; tb < r1; tb += (kThreads / kWave) * kUnroll) {
+  float vb[kUnroll][8];
+  if (VEC && tb + (kThreads / kWave) * (kUnroll - 1) < r1 && j0 + 8 <= p.D) {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) load8<TIn, true>(G + (tb + (int64_t)u * (kThreads / kWave)) * p.ld_g, j0, p.D, vb[u]);
+  } else {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t t = tb + (int64_t)u * (kThreads / kWave);
+      if (t < r1 && j0 < p.D) load8<TIn, VEC>(G + t * p.ld_g, j0, p.D, vb[u]);
+      else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) vb[u][i] = 0.f;
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const int64_t t = tb + (int64_t)u * (kThreads / kWave);
+    if (t >= r1) break;
     Step s = st;
     if constexpr (PT) s = make_step(amax_rows[t]);
     const float fx = sx ? sx[t] : 1.f;
-    float v[8];
-    if (j0 < p.D) load8<TIn, VEC>(G + t * p.ld_g, j0, p.D, v);
-    else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = 0.f;
-    }
+    const float* v = vb[u];
     int q[8];
     float e[8];
     if (s.flag) {
@@ -311,6 +352,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
       for (int i = 0; i < 8; ++i) colq[i] += q[i];
     }
   }
+  }
 
   if constexpr (EC || COLSUM) {
 #pragma unroll
@@ -339,51 +381,72 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
 }
 
 // ------------------------------------------------------------- finalize ----
-// Per-example channel means and code column sums: fixed-order sums over the
-// row tiles of each example.
-__global__ __launch_bounds__(kThreads) void finalize_cols_kernel(
-    int64_t B, int64_t D, int64_t S, int tiles_per_example, int per_token,
-    const float* __restrict__ delta, const float* __restrict__ col_part, const int32_t* __restrict__ colq_part,
-    float* __restrict__ ec_col, int32_t* __restrict__ code_colsum) {
-  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (idx >= B * D) return;
-  const int64_t b = idx / D, j = idx % D;
-  if (ec_col) {
-    double a = 0.0;
-    for (int k = 0; k < tiles_per_example; ++k) a += (double)col_part[(b * tiles_per_example + k) * D + j];
-    const double d = per_token ? 1.0 : (double)delta[0];
-    ec_col[idx] = (float)(a * d / (double)S);
-  }
-  if (code_colsum) {
-    int32_t a = 0;
-    for (int k = 0; k < tiles_per_example; ++k) a += colq_part[(b * tiles_per_example + k) * D + j];
-    code_colsum[idx] = a;
-  }
-}
+// One launch.  Blocks [0, ncb): per-example channel means and code column sums,
+// fixed-order sums over the row tiles of each example.  Blocks [ncb, ncb+nrb):
+// token means eps_t of up to 256 rows of one example, and that block's sum of
+// eps; the last row block to finish (counter reset to 0 by the quantize kernel)
+// adds the block sums of each example in order to get its grand mean mu_b.
+constexpr int kFinRows = 256;
 
-// Token means eps_t and the example's grand mean mu_b: one block per example.
-__global__ __launch_bounds__(kThreads) void finalize_rows_kernel(
-    int64_t D, int64_t S, int n_ctiles, int per_token, const float* __restrict__ delta,
-    const float* __restrict__ row_part, float* __restrict__ ec_row, float* __restrict__ ec_mean) {
-  const int64_t b = blockIdx.x;
-  double acc = 0.0;
-  for (int64_t s = threadIdx.x; s < S; s += kThreads) {
-    const int64_t t = b * S + s;
+__global__ __launch_bounds__(kThreads) void finalize_kernel(
+    int64_t B, int64_t D, int64_t S, int tiles_per_example, int n_ctiles, int per_token, int ncb,
+    int blocks_per_example, const float* __restrict__ delta, const float* __restrict__ col_part,
+    const int32_t* __restrict__ colq_part, const float* __restrict__ row_part, float* __restrict__ ec_col,
+    int32_t* __restrict__ code_colsum, float* __restrict__ ec_row, float* __restrict__ ec_mean,
+    double* __restrict__ blk_sum, uint32_t* __restrict__ counter) {
+  if ((int)blockIdx.x < ncb) {
+    const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (idx >= B * D) return;
+    const int64_t b = idx / D, j = idx % D;
+    if (ec_col) {
+      double a = 0.0;
+      for (int k = 0; k < tiles_per_example; ++k) a += (double)col_part[(b * tiles_per_example + k) * D + j];
+      const double d = per_token ? 1.0 : (double)delta[0];
+      ec_col[idx] = (float)(a * d / (double)S);
+    }
+    if (code_colsum) {
+      int32_t a = 0;
+      for (int k = 0; k < tiles_per_example; ++k) a += colq_part[(b * tiles_per_example + k) * D + j];
+      code_colsum[idx] = a;
+    }
+    return;
+  }
+  // row block rb covers rows [b*S + k*256, min(b*S + (k+1)*256, (b+1)*S)) of example b
+  const int rb = (int)blockIdx.x - ncb;
+  const int64_t b = rb / blocks_per_example;
+  const int64_t r0 = b * S + (int64_t)(rb % blocks_per_example) * kFinRows;
+  const int64_t r1 = min(r0 + kFinRows, (b + 1) * S);
+  const int64_t t = r0 + threadIdx.x;
+  double eps = 0.0;
+  if (t < r1) {
     double a = 0.0;
     for (int k = 0; k < n_ctiles; ++k) a += (double)row_part[t * n_ctiles + k];
     const double d = per_token ? (double)delta[t] : (double)delta[0];
-    const double eps = D > 0 ? a * d / (double)D : 0.0;
+    eps = D > 0 ? a * d / (double)D : 0.0;
     ec_row[t] = (float)eps;
-    acc += eps;
   }
   __shared__ double red[kThreads];
-  red[threadIdx.x] = acc;
+  red[threadIdx.x] = eps;
   __syncthreads();
   for (int o = kThreads / 2; o > 0; o >>= 1) {
     if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
     __syncthreads();
   }
-  if (threadIdx.x == 0) ec_mean[b] = (float)(red[0] / (double)S);
+  __shared__ bool last;
+  if (threadIdx.x == 0) {
+    blk_sum[rb] = red[0];
+    __threadfence();
+    const uint32_t done = atomicAdd(counter, 1u);
+    last = done == (uint32_t)(B * blocks_per_example) - 1u;
+  }
+  __syncthreads();
+  if (!last) return;
+  __threadfence();
+  for (int64_t bb = threadIdx.x; bb < B; bb += kThreads) {
+    double a = 0.0;
+    for (int k = 0; k < blocks_per_example; ++k) a += blk_sum[bb * blocks_per_example + k];
+    ec_mean[bb] = (float)(a / (double)S);
+  }
 }
 
 // Degenerate shapes (T == 0 or D == 0): steps of 1, zero statistics.
@@ -399,7 +462,7 @@ __global__ void empty_kernel(int64_t T, int64_t D, int64_t B, int per_token, flo
 }
 
 struct WsLayout {
-  size_t amax_part, amax_rows, row_part, col_part, colq_part, total;
+  size_t amax_part, amax_rows, row_part, col_part, colq_part, blk_sum, counter, total;
 };
 
 WsLayout ws_layout(int64_t T, int64_t D, int64_t S, int ec, int scale, bool colsum) {
@@ -414,6 +477,9 @@ WsLayout ws_layout(int64_t T, int64_t D, int64_t S, int ec, int scale, bool cols
   w.row_part = off;  off = align_up(off + (ec ? (size_t)T * n_ct * 4 : 0), 256);
   w.col_part = off;  off = align_up(off + (ec ? (size_t)n_rt * D * 4 : 0), 256);
   w.colq_part = off; off = align_up(off + (colsum ? (size_t)n_rt * D * 4 : 0), 256);
+  const int64_t bpe = (S + kFinRows - 1) / kFinRows;
+  w.blk_sum = off;   off = align_up(off + (ec ? (size_t)B * bpe * 8 : 0), 256);
+  w.counter = off;   off = align_up(off + 4, 256);
   w.total = off;
   return w;
 }
@@ -423,7 +489,8 @@ void launch_q(const QuantArgs& a, const WsLayout& L, const QuantTile& p, dim3 gr
   hipLaunchKernelGGL((quantize_kernel<TIn, VEC, MODE, EC, PT, COLSUM>), grid, dim3(kThreads), 0, st, p,
                      (const TIn*)a.G, a.sx, a.sw, a.Q, a.delta, a.flags,
                      (const uint32_t*)(a.ws + L.amax_part), kAmaxBlocks, (const uint32_t*)(a.ws + L.amax_rows),
-                     (float*)(a.ws + L.row_part), (float*)(a.ws + L.col_part), (int32_t*)(a.ws + L.colq_part));
+                     (float*)(a.ws + L.row_part), (float*)(a.ws + L.col_part), (int32_t*)(a.ws + L.colq_part),
+                     (uint32_t*)(a.ws + L.counter));
 }
 
 template <typename TIn, bool VEC, int MODE, bool EC>
@@ -469,16 +536,14 @@ void run_quantize(const QuantArgs& a, const WsLayout& L, hipStream_t st) {
   dim3 grid((unsigned)(B * p.tiles_per_example), (unsigned)p.n_ctiles);
   dispatch_mode<TIn, VEC>(a, L, p, grid, st);
   if (a.ec || a.code_colsum) {
-    const int64_t n = B * a.D;
-    hipLaunchKernelGGL(finalize_cols_kernel, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0,
-                       st, B, a.D, a.S, p.tiles_per_example, a.scale == S3R_PER_TOKEN ? 1 : 0, a.delta,
+    const int64_t ncb = (B * a.D + kThreads - 1) / kThreads;
+    const int bpe = (int)((a.S + kFinRows - 1) / kFinRows);
+    const int64_t nrb = a.ec ? B * bpe : 0;
+    hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)(ncb + nrb)), dim3(kThreads), 0, st, B, a.D, a.S,
+                       p.tiles_per_example, p.n_ctiles, a.scale == S3R_PER_TOKEN ? 1 : 0, (int)ncb, bpe, a.delta,
                        (const float*)(a.ws + L.col_part), (const int32_t*)(a.ws + L.colq_part),
-                       a.ec ? a.ec_col : nullptr, a.code_colsum);
-  }
-  if (a.ec) {
-    hipLaunchKernelGGL(finalize_rows_kernel, dim3((unsigned)B), dim3(kThreads), 0, st, a.D, a.S, p.n_ctiles,
-                       a.scale == S3R_PER_TOKEN ? 1 : 0, a.delta, (const float*)(a.ws + L.row_part), a.ec_row,
-                       a.ec_mean);
+                       (const float*)(a.ws + L.row_part), a.ec ? a.ec_col : nullptr, a.code_colsum, a.ec_row,
+                       a.ec_mean, (double*)(a.ws + L.blk_sum), (uint32_t*)(a.ws + L.counter));
   }
 }
 
