@@ -27,6 +27,12 @@ if ROOT not in sys.path:
 PEAK_INT8_TOPS = 5000.0     # MI355X dense INT8 MFMA, TOP/s
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, GB/s
 
+# HBM byte counts of the GEMM kernels, taken with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE and
+# scaled by the same counters' reading for a plain copy of known size.  The file records the
+# sha256 of the kernel source it was measured on; a stale record is not reported.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_down-8192x14336x4096.md")
+GEMM_SOURCE = os.path.join(ROOT, "stochastic_rounding_quantization_amd", "csrc", "gemm.hip")
+
 MODES = {
     "s3r-ec-two-way": (2, 2), "s3r-ec-dx-only": (2, 1), "s3r": (2, 0), "sr": (1, 0), "rtne": (0, 0),
 }
@@ -34,6 +40,36 @@ MODES = {
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def measured_traffic(kernel_key, workload):
+    """HBM bytes per launch of one GEMM kernel from the committed counter summary, or None."""
+    import hashlib
+    import re
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    m = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    src = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
+    if not m or m.group(1) != src or f"workload: {workload}" not in text:
+        return None
+    m = re.search(rf"{kernel_key}_hbm_bytes_per_launch:\s*([0-9]+)", text)
+    return int(m.group(1)) if m else None
+
+
+def copy_calibration(device, nbytes=1 << 30, reps=4):
+    """A plain device-to-device copy of ``nbytes`` (torch's copy kernel), run ``reps`` times.
+
+    Under rocprofv3 --pmc its FETCH_SIZE / WRITE_SIZE per dispatch against the known ``nbytes``
+    gives the factor that turns those counters into bytes."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.int32, device=device).fill_(7)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}), flush=True)
 
 
 def cpu_baseline(inp, w, mode, ec, rows):
@@ -60,7 +96,8 @@ def cpu_baseline(inp, w, mode, ec, rows):
     ops = 2 * 2.0 * rows * w.d_out * w.d_in
     return {"value": ops / dt / 1e12, "unit": "TOP/s", "cores": int(blas_threads), "kind": "oracle",
             "seconds": round(dt, 3),
-            "sample": f"first {rows} tokens ({rows // S} example(s) of {S}) of the workload, full "
+            "sample": ("the whole workload: " if rows == w.tokens else f"first {rows} tokens of the workload: ") +
+                      f"{rows} tokens ({rows // S} example(s) of {S}), "
                       f"D={w.d_out} and d_in={w.d_in}: numpy quantizer (1 thread) + dX + dW with float64 BLAS "
                       f"integer GEMMs ({blas_threads} BLAS threads); forward-operand prep untimed"}
 
@@ -72,7 +109,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="down-8192x14336x4096-bf16")
     ap.add_argument("--mode", default="s3r-ec-two-way", choices=sorted(MODES))
-    ap.add_argument("--cpu-rows", type=int, default=2048, help="tokens in the CPU-oracle sample (0: skip)")
+    ap.add_argument("--cpu-rows", type=int, default=-1,
+                    help="tokens in the CPU-oracle sample (-1: the whole workload, 0: skip)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (reference for HBM byte counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -86,8 +126,11 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
-    s3r.lib()   # fail loudly if the HIP library is missing
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        copy_calibration(dev)
+        return
+    s3r.lib()   # fail loudly if the HIP library is missing
     mode, ec = MODES[args.mode]
     w = inputs.WORKLOADS[args.workload]
     T, D, K, S = w.tokens, w.d_out, w.d_in, w.rows_per_example
@@ -164,8 +207,8 @@ def main():
     value = 2 * gop / (ms_step / 1e3) / 1e3          # TOP/s
     q_bytes = T * D * (2 if inp["dtype"] == "bf16" else 4) + T * D
     q_gbs = q_bytes / (t_q / 1e3) / 1e9
-    dom_name, t_dom = ("gemm dW (gemm_i8_kernel<false, EPI_DW>)", t_gw) if t_gw >= t_gx else \
-        ("gemm dX (gemm_i8_kernel<true, EPI_DX>)", t_gx)
+    dom_key, dom_name, t_dom = ("dw", "gemm dW (gemm_i8_kernel<false, EPI_DW>)", t_gw) if t_gw >= t_gx else \
+        ("dx", "gemm dX (gemm_i8_kernel<true, EPI_DX>)", t_gx)
     achieved = gop / (t_dom / 1e3) / 1e3              # TOP/s
     out = {
         "metric": "S3R-EC backward TOPS (quant+INT8 dX/dW) & quantizer GB/s, % of MI355X peak",
@@ -182,12 +225,14 @@ def main():
         "gemm_tops": {"dx": round(gop / (t_gx / 1e3) / 1e3, 1), "dw": round(gop / (t_gw / 1e3) / 1e3, 1)},
         "roofline": {"kernel": dom_name, "bound": "mfma", "achieved": round(achieved, 1),
                      "peak": PEAK_INT8_TOPS, "unit": "TOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4),
-                     "traffic": None,
+                     "traffic": measured_traffic(dom_key, w.name),
                      "algorithmic": f"2*T*D*d_in = {gop:.1f} GOP per launch (int8 multiply-adds x 2)"},
     }
-    if args.cpu_rows > 0:
-        log(f"CPU oracle baseline on the first {args.cpu_rows} tokens")
-        out["cpu_baseline"] = cpu_baseline(inp, w, mode, ec, min(args.cpu_rows, T))
+    if args.cpu_rows != 0:
+        rows = T if args.cpu_rows < 0 else min(args.cpu_rows, T)
+        rows = max(S, rows // S * S)
+        log(f"CPU oracle baseline on the first {rows} tokens")
+        out["cpu_baseline"] = cpu_baseline(inp, w, mode, ec, rows)
     print(json.dumps(out), flush=True)
 
 
