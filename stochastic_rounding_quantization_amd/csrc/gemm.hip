@@ -270,7 +270,9 @@ constexpr int kMaxB = 8;   // examples whose dW correction terms the epilogue ap
 
 __device__ __forceinline__ int row_in_block(int r) { return (r >> 2) * 8 + (r & 3); }
 
-template <int EPI, bool EC, bool GATHER>
+// NB: number of examples whose dW terms are applied here (a compile-time bound,
+// so the per-element sum has no runtime trip count; slots b >= B hold zeros).
+template <int EPI, bool EC, bool GATHER, int NB>
 __device__ __forceinline__ void epilogue(const GemmParams& g, const EpiParams& ep, int64_t m0, int64_t n0,
                                          v16i (&acc)[4][4]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -285,7 +287,7 @@ __device__ __forceinline__ void epilogue(const GemmParams& g, const EpiParams& e
   const int lane_row = wm * 128 + (lane >> 5) * 4;                  // + i*32 + row_in_block(r)
 
   // per-column values of this lane, one per column block j
-  float colA[4], colV[4], colB[kMaxB][4];
+  float colA[4], colV[4], colB[NB][4];
   bool n_ok[4];
   uint32_t voff[4];
 #pragma unroll
@@ -295,7 +297,7 @@ __device__ __forceinline__ void epilogue(const GemmParams& g, const EpiParams& e
     voff[j] = (uint32_t)(lane_row * ld4 + n * esz);
     colA[j] = 0.f; colV[j] = 0.f;
 #pragma unroll
-    for (int b = 0; b < kMaxB; ++b) colB[b][j] = 0.f;
+    for (int b = 0; b < NB; ++b) colB[b][j] = 0.f;
     if (EC && n_ok[j]) {
       if constexpr (EPI == EPI_DX) {
         colA[j] = (float)ep.colsum[n];                                   // r_W[n]
@@ -303,7 +305,7 @@ __device__ __forceinline__ void epilogue(const GemmParams& g, const EpiParams& e
       } else if constexpr (EPI == EPI_DW) {
         colA[j] = ep.u[n];
 #pragma unroll
-        for (int b = 0; b < kMaxB; ++b)
+        for (int b = 0; b < NB; ++b)
           if (b < ep.B) colB[b][j] = (float)ep.colsum[b * g.N + n];     // xs_b[n]
       }
     }
@@ -315,14 +317,14 @@ __device__ __forceinline__ void epilogue(const GemmParams& g, const EpiParams& e
     for (int rq = 0; rq < 4; ++rq) {
       // four consecutive rows of this lane: lr = lane_row + i*32 + rq*8 + rr
       float4 f[4];
-      float eb[4][kMaxB];
+      float eb[4][NB];
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int lr = lane_row + i * 32 + rq * 8 + rr;
         if constexpr (EPI != EPI_RAW) f[rr] = rowf[lr];
         if constexpr (EPI == EPI_DW && EC) {
 #pragma unroll
-          for (int b = 0; b < kMaxB; ++b) eb[rr][b] = b < ep.B ? roweb[b * BM + lr] : 0.f;
+          for (int b = 0; b < NB; ++b) eb[rr][b] = roweb[b * BM + lr];
         }
       }
 #pragma unroll
@@ -347,7 +349,7 @@ __device__ __forceinline__ void epilogue(const GemmParams& g, const EpiParams& e
             if constexpr (EC && EPI == EPI_DW) {
               float t = f[rr].y * colA[j];
 #pragma unroll
-              for (int b = 0; b < kMaxB; ++b) t = fmaf(eb[rr][b], colB[b][j], t);
+              for (int b = 0; b < NB; ++b) t = fmaf(eb[rr][b], colB[b][j], t);
               corr = t;
             }
             const float o = fmaf(f[rr].x, (float)v, -corr);
@@ -360,7 +362,7 @@ __device__ __forceinline__ void epilogue(const GemmParams& g, const EpiParams& e
 }
 
 // ----------------------------------------------------------------- kernel ----
-template <bool A_KMAJOR, int EPI, bool EC>
+template <bool A_KMAJOR, int EPI, bool EC, int NB>
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmParams g, EpiParams ep) {
   // XCD-aware numbering: hardware block ids go round-robin over the 8 XCDs;
   // give each XCD a contiguous range of logical tiles.
@@ -434,17 +436,18 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmParams g, 
         f.y = inv;
       }
       if (EC)
-        for (int64_t b = 0; b < ep.B && b < kMaxB; ++b) roweb[b * BM + r] = j < g.M ? ep.ebar[b * g.M + j] * f.y : 0.f;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) roweb[b * BM + r] = (b < ep.B && j < g.M) ? ep.ebar[b * g.M + j] * f.y : 0.f;
       rowf[r] = f;
     }
   }
   __syncthreads();
   if constexpr (EPI == EPI_DX && EC) {
     const int64_t last = min(m0 + BM, g.M) - 1;
-    if (m0 / ep.S == last / ep.S) epilogue<EPI, EC, false>(g, ep, m0, n0, acc);
-    else epilogue<EPI, EC, true>(g, ep, m0, n0, acc);
+    if (m0 / ep.S == last / ep.S) epilogue<EPI, EC, false, NB>(g, ep, m0, n0, acc);
+    else epilogue<EPI, EC, true, NB>(g, ep, m0, n0, acc);
   } else {
-    epilogue<EPI, EC, false>(g, ep, m0, n0, acc);
+    epilogue<EPI, EC, false, NB>(g, ep, m0, n0, acc);
   }
 }
 
@@ -592,7 +595,7 @@ size_t gemv_part_bytes(int64_t K, int64_t N, int64_t nb) {
   return align_up((size_t)nchunks * nb * N * 4, 256);
 }
 
-template <bool A_KMAJOR, int EPI, bool EC>
+template <bool A_KMAJOR, int EPI, bool EC, int NB = 1>
 hipError_t run_gemm(const GemmParams& g, const EpiParams& ep, hipStream_t st) {
   GemmTiming& tm = gemm_timing();
   const GemmTiming ev = tm;
@@ -600,7 +603,7 @@ hipError_t run_gemm(const GemmParams& g, const EpiParams& ep, hipStream_t st) {
   const int nblocks = g.tiles_m * g.tiles_n;
   if (ev.start && hipEventRecord(ev.start, st) != hipSuccess) return hipErrorInvalidValue;
   if (nblocks > 0)
-    hipLaunchKernelGGL((gemm_i8_kernel<A_KMAJOR, EPI, EC>), dim3((unsigned)nblocks), dim3(kGemmThreads), 0, st, g, ep);
+    hipLaunchKernelGGL((gemm_i8_kernel<A_KMAJOR, EPI, EC, NB>), dim3((unsigned)nblocks), dim3(kGemmThreads), 0, st, g, ep);
   hipError_t e = hipGetLastError();
   if (ev.stop && hipEventRecord(ev.stop, st) != hipSuccess && e == hipSuccess) e = hipErrorInvalidValue;
   return e;
@@ -682,7 +685,12 @@ hipError_t launch_backward_dw(const DwArgs& a, hipStream_t st) {
   // dW = Q^T Xq: A[m=j][k=t] = Q[t][j] (M-contiguous), B = Xq [T x d_in] (N-contiguous)
   const GemmParams g = make_gemm(a.Q, a.ld_q, a.X, a.ld_x, a.D, a.d_in, a.T);
   if (a.out_dt == S3R_I32_RAW) return run_gemm<false, EPI_RAW, false>(g, ep, st);
-  hipError_t e = ep.ec ? run_gemm<false, EPI_DW, true>(g, ep, st) : run_gemm<false, EPI_DW, false>(g, ep, st);
+  hipError_t e;
+  if (!ep.ec) e = run_gemm<false, EPI_DW, false>(g, ep, st);
+  else if (B <= 1) e = run_gemm<false, EPI_DW, true, 1>(g, ep, st);
+  else if (B <= 2) e = run_gemm<false, EPI_DW, true, 2>(g, ep, st);
+  else if (B <= 4) e = run_gemm<false, EPI_DW, true, 4>(g, ep, st);
+  else e = run_gemm<false, EPI_DW, true, kMaxB>(g, ep, st);
   if (e != hipSuccess || !ep.ec || B <= 8 || a.D == 0 || a.d_in == 0) return e;
   hipLaunchKernelGGL(dw_rank_update_kernel, dim3((unsigned)((a.d_in + 255) / 256), (unsigned)a.D), dim3(256), 0, st,
                      (float*)a.out, a.ld_out, a.D, a.d_in, B, a.ec_col, a.xs, a.sw);

@@ -240,6 +240,15 @@ def test_linear_ragged_multi_example_bf16():
     _check_linear(inp, 128, s3r.S3R, s3r.EC_TWO_WAY, scale=s3r.PER_TOKEN, seed=7, layer=2)
 
 
+@pytest.mark.parametrize("B", [2, 5, 8, 11])
+def test_linear_example_counts(B):
+    # B examples of 40 tokens: GEMM tiles span several examples; the dW epilogue's compile-time
+    # example slots (1, 2, 4, 8) and, past 8 examples, the rank-update kernel
+    w = inputs.WORKLOADS["down-8192x14336x4096-bf16"].scaled(40 * B, 330, 200, rows_per_example=40)
+    inp = inputs.make_linear_inputs(w)
+    _check_linear(inp, 40, s3r.S3R, s3r.EC_TWO_WAY, seed=B, layer=1)
+
+
 def _sample_rows(n, k, seed):
     rng = np.random.default_rng(seed)
     rows = set(rng.choice(n, min(n, k), replace=False).tolist()) | {0, n - 1, n - 2}
