@@ -70,6 +70,8 @@ typedef enum { S3R_PER_TENSOR = 0, S3R_PER_TOKEN = 1 } s3r_scale;
 /* Bits OR-ed into the optional device flags word by s3r_quantize. */
 #define S3R_FLAG_NONFINITE  1u  /* an amax was Inf/NaN: affected codes are 0 */
 #define S3R_FLAG_TINY_STEP  2u  /* an amax so small that 127*2^24/amax overflows fp32: codes 0 */
+#define S3R_FLAG_SYNC_TIMEOUT 4u /* the single-pass quantizer's grid-wide wait timed out (its
+                                    workgroups were not all resident): outputs invalid */
 
 /* Problem descriptor of one quantized tensor G [rows x cols]. */
 typedef struct s3r_qdesc {

@@ -25,7 +25,7 @@ S3R_F32, S3R_BF16, S3R_I32_RAW = 0, 1, 2
 RTNE, SR, S3R = 0, 1, 2
 EC_NONE, EC_DX_ONLY, EC_TWO_WAY = 0, 1, 2
 PER_TENSOR, PER_TOKEN = 0, 1
-FLAG_NONFINITE, FLAG_TINY_STEP = 1, 2
+FLAG_NONFINITE, FLAG_TINY_STEP, FLAG_SYNC_TIMEOUT = 1, 2, 4
 
 EXPORTED = ["s3r_quantize_workspace", "s3r_quantize", "s3r_backward_dx", "s3r_backward_dw",
             "s3r_backward_workspace", "s3r_time_next_gemm", "s3r_status_string", "s3r_version"]

@@ -128,6 +128,48 @@ def test_quantize_bit_exact(T, D, S, dtype, scale):
             assert np.abs(host(q.ec_mean) - mu).max() <= TOL * np.abs(E).max(), tag
 
 
+# Shapes the single-pass (resident) quantizer takes: bf16, per-tensor, D a power of two in
+# [512, 8192].  (T, D, S): the benchmark shape; a band of one row per block; one chunk per
+# thread; a ragged last band (no EC: S has no suitable divisor); EC falls back to two passes.
+RCASES = [(8192, 4096, 2048), (1000, 8192, 1000), (96, 1024, 32), (4097, 2048, 4097), (300, 512, 300)]
+
+
+@pytest.mark.parametrize("T,D,S", RCASES)
+def test_quantize_single_pass_matches_oracle(T, D, S, monkeypatch):
+    store, sx, sw = _grad(T, D, "bf16", T * 7 + D)
+    if T == 96:
+        store[5, 7] = 0x7FC0          # a NaN: flags, zero codes, NaN step
+    G = to_dev(store, "bf16")
+    sx_d, sw_d = torch.from_numpy(sx).to(DEV), torch.from_numpy(sw).to(DEV)
+    for mode, ec in MODES:
+        ref = oq.quantize(store, "bf16", mode=mode, scale=s3r.PER_TENSOR, row_scale=sx, col_scale=sw, seed=77,
+                          layer_id=5, rows_per_example=S)
+        for two_pass in ("0", "1"):
+            monkeypatch.setenv("S3R_QUANTIZE_TWO_PASS", two_pass)
+            q = s3r.quantize(G, mode=mode, ec=ec, row_scale=sx_d, col_scale=sw_d, seed=77, layer_id=5,
+                             rows_per_example=S)
+            torch.cuda.synchronize()
+            tag = f"T={T} D={D} S={S} mode={mode} ec={ec} two_pass={two_pass}"
+            np.testing.assert_array_equal(host(q.Q), ref["Q"], err_msg=tag)
+            assert_nan_equal(host(q.delta), ref["delta"], tag)
+            assert int(host(q.flags)[0]) == ref["flags"], tag
+            if ec != s3r.EC_NONE and not ref["flags"]:
+                from oracle import ec as oec
+                E = oec.rounding_error(ref["Q"], ref["x"], ref["delta"])
+                eps, ebar, mu = oec.statistics(E, S)
+                assert rel_err(host(q.ec_row), eps) <= TOL, tag
+                assert rel_err(host(q.ec_col), ebar) <= TOL, tag
+                assert np.abs(host(q.ec_mean) - mu).max() <= TOL * np.abs(E).max(), tag
+
+
+def test_quantize_single_pass_zero_tensor():
+    G = torch.zeros(64, 512, dtype=torch.bfloat16, device=DEV)
+    q = s3r.quantize(G, mode=s3r.S3R, ec=s3r.EC_TWO_WAY, rows_per_example=64)
+    torch.cuda.synchronize()
+    assert (host(q.Q) == 0).all() and host(q.delta)[0] == 1.0 and int(host(q.flags)[0]) == 0
+    assert (host(q.ec_row) == 0).all() and (host(q.ec_col) == 0).all() and (host(q.ec_mean) == 0).all()
+
+
 def test_quantize_strided_and_unaligned():
     # G with a padded leading dim, Q written into a padded buffer; then the scalar path (odd ld).
     T, D = 40, 72
