@@ -155,8 +155,8 @@ def main():
     e_c = torch.empty(B, D, dtype=torch.float32, device=dev) if ec else None
     e_m = torch.empty(B, dtype=torch.float32, device=dev) if ec else None
     flags = torch.zeros(1, dtype=torch.int32, device=dev)
-    ws_q = torch.empty(max(s3r.s3r_quantize_workspace(desc), 1), dtype=torch.uint8, device=dev)
-    ws_b = torch.empty(max(s3r.s3r_backward_workspace(desc, K), 1), dtype=torch.uint8, device=dev)
+    ws_q = torch.zeros(max(s3r.s3r_quantize_workspace(desc), 1), dtype=torch.uint8, device=dev)
+    ws_b = torch.zeros(max(s3r.s3r_backward_workspace(desc, K), 1), dtype=torch.uint8, device=dev)
     dX = torch.empty(T, K, dtype=torch.float32, device=dev)
     dW = torch.empty(D, K, dtype=torch.float32, device=dev)
     s_x, s_w = fx.delta, fw.delta

@@ -26,9 +26,14 @@
  *   - Argument checks happen on the host before anything is enqueued; a
  *     nonzero return means nothing was enqueued (except S3R_ERR_HIP, which
  *     reports a launch failure).
- *   - Calls are stateless and bitwise deterministic: no floating-point
- *     atomics, all reductions in a fixed order.  Concurrent calls on
- *     different streams must not share a workspace.
+ *   - Results are bitwise deterministic: no floating-point atomics, all
+ *     reductions in a fixed order.
+ *   - Workspaces: the caller zero-fills a workspace once, before its first use
+ *     (hipMemset, torch.zeros).  Its first 64 KiB hold the library's
+ *     synchronization words, which every completed call leaves valid for the
+ *     next call; do not write them.  One workspace may serve quantize and
+ *     backward calls; calls that overlap in time (different streams) must not
+ *     share a workspace.
  *   - Weight layout: W is stored [D x d_in] (PyTorch Linear layout, the
  *     page's W^T), Wq likewise; X is [T x d_in].
  */
@@ -109,7 +114,14 @@ typedef struct s3r_qdesc {
  *   flags    device uint32 or NULL: S3R_FLAG_* bits are OR-ed in (the caller
  *            clears it).
  *   ws       device workspace of at least s3r_quantize_workspace(desc) bytes,
- *            256-byte aligned.
+ *            256-byte aligned, zero-filled before its first use (see above).
+ * Per-tensor steps of bf16 G whose D is a power of two in [512, 8192] and that
+ * fits on chip (T*D up to about 2^25 elements on MI355X) take a single-pass
+ * kernel that reads G from HBM once; it needs every one of its workgroups
+ * (at most one per CU) resident at the same time.  If other work holds CUs
+ * for the whole call, its bounded wait expires, S3R_FLAG_SYNC_TIMEOUT is set
+ * and the outputs are invalid.  Setting S3R_QUANTIZE_TWO_PASS=1 in the
+ * environment selects the two-pass kernels instead (same results).
  * Thresholds: SR element (t,j) uses Philox4x32-10 block e>>2 of e = t*D + j
  * (counter {lo,hi}(e>>2), layer_id, 0; key = seed), word e&3, r =
  * (2*(w>>9)+1)/2^24; S3R token t uses block t>>4 (counter ..., layer_id, 1),
@@ -141,7 +153,7 @@ int s3r_quantize(const s3r_qdesc* desc,
  * the token means times the row sums r_W).
  *   Wq [D x d_in] int8 (ld_w), s_x [T] f32 (NULL = 1),
  *   r_W [d_in] int32 (required iff ec != NONE), ec_* as from s3r_quantize.
- *   ws: s3r_backward_workspace(desc, d_in) bytes.
+ *   ws: s3r_backward_workspace(desc, d_in) bytes (0 without EC), zero-filled once.
  */
 int s3r_backward_dx(const s3r_qdesc* desc,
                     const int8_t* Q, int64_t ld_q, const float* delta,

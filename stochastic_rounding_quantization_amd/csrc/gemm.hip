@@ -467,77 +467,83 @@ __global__ __launch_bounds__(256) void dw_rank_update_kernel(float* __restrict__
 }
 
 // -------------------------------------------------------------- GEMVs ----
-// out_part[c][b][n] = sum over rows k of chunk c of coef(b, k) * P[k][n]   (P int8 [K x N])
+// out[b][n] = sum over rows k of coef(b, k) * P[k][n]   (P int8 [K x N])
 // Coefficients: VEC mode coef(b, k) = C[b * K + k] (the channel means ebar);
 // TOKEN mode (one row, b = 0) coef(k) = ec_row[k] - ec_mean[k / S].
-// A block covers 1024 columns (16 per lane, 16-byte loads) and kGvRows rows,
-// split over its 4 waves; the waves' sums are added in LDS in a fixed order.
+// HBM-bound.  A block covers 512 columns (8 per lane, 8-byte loads) and a band
+// of kGvRows rows, a quarter per wave, with all of a wave's row loads in flight
+// at once; few registers, so many waves per SIMD.  Each band writes its sums
+// part[band][b][n]; gemv_reduce_kernel adds the bands in order in fp64.
 constexpr int kGvThreads = 256;
-constexpr int kGvColsPerLane = 16;
-constexpr int kGvCols = 64 * kGvColsPerLane;   // 1024 columns per block
-constexpr int kGvRows = 256;                   // rows per chunk (block)
+constexpr int kGvColsPerLane = 8;
+constexpr int kGvCols = 64 * kGvColsPerLane;   // 512 columns per block
+constexpr int kGvRows = 64;                    // rows per band
+constexpr int kGvRowsPerWave = kGvRows / 4;
 
 template <int NB>
 __global__ __launch_bounds__(kGvThreads) void gemv_partial_kernel(
     const int8_t* __restrict__ P, int64_t ld, int64_t K, int64_t N, int64_t nb, int token_mode,
     const float* __restrict__ C, const float* __restrict__ ec_row, const float* __restrict__ ec_mean, int64_t S,
     float* __restrict__ part) {
-  __shared__ float coef[NB][kGvRows];
   __shared__ float red[4][NB][kGvCols];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t n0 = (int64_t)blockIdx.x * kGvCols + lane * kGvColsPerLane;
   const int64_t k0 = (int64_t)blockIdx.y * kGvRows;
   const int rows = (int)min((int64_t)kGvRows, K - k0);
-  const int chunk = blockIdx.y;
+  // The band through one buffer descriptor: rows past K read zeros; columns past
+  // N (the last lanes of a ragged row) are cleared by the mask at use.
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(P + k0 * ld), (short)0, (int)((uint32_t)rows * (uint32_t)ld), kRsrcWord3);
+  const uint32_t voff = (uint32_t)n0;
+  uint2 mask = make_uint2(0xFFFFFFFFu, 0xFFFFFFFFu);
+  if (n0 + kGvColsPerLane > N) {
+    const int64_t keep = max((int64_t)0, N - n0);
+    mask.x = keep >= 4 ? 0xFFFFFFFFu : (uint32_t)((1ull << (8 * keep)) - 1);
+    mask.y = keep >= 8 ? 0xFFFFFFFFu : keep <= 4 ? 0u : (uint32_t)((1ull << (8 * (keep - 4))) - 1);
+  }
   for (int64_t b0 = 0; b0 < nb; b0 += NB) {
-    __syncthreads();
-    for (int r = threadIdx.x; r < kGvRows; r += kGvThreads) {
+    uint2 u[kGvRowsPerWave];
+#pragma unroll
+    for (int i = 0; i < kGvRowsPerWave; ++i) {
+      const uint32_t soff = (uint32_t)(wave + 4 * i) * (uint32_t)ld;
+      const auto w = __builtin_amdgcn_raw_buffer_load_b64(rsrc, voff, soff, 0);
+      u[i] = make_uint2(w[0], w[1]);
+    }
+    // lane l holds the coefficients of this wave's row wave + 4l; the row loop
+    // takes them as uniform values with readlane
+    float cf[NB];
+    {
+      const int r = wave + 4 * lane;
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         float x = 0.f;
-        if (r < rows && b0 + b < nb) {
+        if (lane < kGvRowsPerWave && r < rows && b0 + b < nb) {
           const int64_t k = k0 + r;
-          x = token_mode ? ec_row[k] - ec_mean[k / S] : C[(b0 + b) * K + k];
+          x = token_mode ? ec_row[k] - ec_mean[(uint32_t)k / (uint32_t)S] : C[(b0 + b) * K + k];
         }
-        coef[b][r] = x;
+        cf[b] = x;
       }
     }
-    __syncthreads();
     float acc[NB][kGvColsPerLane];
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int c = 0; c < kGvColsPerLane; ++c) acc[b][c] = 0.f;
-    auto accumulate = [&](const uint32_t (&w)[4], int r) {
+#pragma unroll
+    for (int i = 0; i < kGvRowsPerWave; ++i) {
+      float c8[NB];
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        c8[b] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, cf[b]), i));
+      const uint32_t w[2] = {u[i].x & mask.x, u[i].y & mask.y};
 #pragma unroll
       for (int c = 0; c < kGvColsPerLane; ++c) {
         const float x = (float)(int8_t)(w[c >> 2] >> (8 * (c & 3)));
 #pragma unroll
-        for (int b = 0; b < NB; ++b) acc[b][c] = fmaf(coef[b][r], x, acc[b][c]);
-      }
-    };
-    if (n0 + kGvColsPerLane <= N && rows == kGvRows) {
-      // full block: 8 rows' 16-byte loads in flight per lane, no branches
-#pragma unroll 1
-      for (int r0 = wave; r0 < kGvRows; r0 += 4 * 8) {
-        uint4 u[8];
-#pragma unroll
-        for (int x = 0; x < 8; ++x) u[x] = *reinterpret_cast<const uint4*>(P + (k0 + r0 + 4 * x) * ld + n0);
-#pragma unroll
-        for (int x = 0; x < 8; ++x) {
-          const uint32_t w[4] = {u[x].x, u[x].y, u[x].z, u[x].w};
-          accumulate(w, r0 + 4 * x);
-        }
-      }
-    } else {
-      for (int r = wave; r < rows; r += 4) {
-        const int8_t* p = P + (k0 + r) * ld + n0;
-        uint32_t w[4] = {0, 0, 0, 0};
-        for (int c = 0; c < kGvColsPerLane; ++c)
-          if (n0 + c < N) w[c >> 2] |= (uint32_t)(uint8_t)p[c] << (8 * (c & 3));
-        accumulate(w, r);
+        for (int b = 0; b < NB; ++b) acc[b][c] = fmaf(c8[b], x, acc[b][c]);
       }
     }
+    __syncthreads();                              // the previous pass is done with red
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -548,7 +554,7 @@ __global__ __launch_bounds__(kGvThreads) void gemv_partial_kernel(
       const int64_t n = (int64_t)blockIdx.x * kGvCols + c;
       if (b0 + b < nb && n < N) {
         const float v = ((red[0][b][c] + red[1][b][c]) + red[2][b][c]) + red[3][b][c];
-        part[((int64_t)chunk * nb + b0 + b) * N + n] = v;
+        part[((int64_t)blockIdx.y * nb + b0 + b) * N + n] = v;
       }
     }
   }
@@ -565,19 +571,36 @@ hipError_t fill_zero(float* p, int64_t n, hipStream_t st) {
 }
 
 
-__global__ __launch_bounds__(256) void gemv_reduce_kernel(const float* __restrict__ part, int64_t nchunks,
-                                                          int64_t count, float* __restrict__ out) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= count) return;
+// out[i] = sum over bands c of part[c][i], in fp64.  tpi lanes share an output:
+// each adds every tpi-th band in order (eight loads in flight), then an xor
+// butterfly (the same order on every lane) adds the lanes.
+__global__ __launch_bounds__(256) void gemv_reduce_kernel(const float* __restrict__ part, int64_t nbands,
+                                                          int64_t count, int tpi, float* __restrict__ out) {
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t i = g / tpi;
+  const int sub = (int)(g % tpi);
   double a = 0.0;
-  for (int64_t c = 0; c < nchunks; ++c) a += (double)part[c * count + i];
-  out[i] = (float)a;
+  if (i < count) {
+    for (int64_t c = sub; c < nbands; c += 8 * (int64_t)tpi) {
+      float t[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t cc = c + (int64_t)u * tpi;
+        const float v = part[min(cc, nbands - 1) * count + i];
+        t[u] = cc < nbands ? v : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) a += (double)t[u];
+    }
+  }
+  for (int o = 1; o < tpi; o <<= 1) a += __shfl_xor(a, o, 64);
+  if (i < count && sub == 0) out[i] = (float)a;
 }
 
 hipError_t run_gemv(const int8_t* P, int64_t ld, int64_t K, int64_t N, int64_t nb, int token_mode, const float* C,
                     const float* ec_row, const float* ec_mean, int64_t S, float* part, float* out, hipStream_t st) {
-  const int64_t nchunks = (K + kGvRows - 1) / kGvRows;
-  dim3 grid((unsigned)((N + kGvCols - 1) / kGvCols), (unsigned)nchunks);
+  const int64_t nbands = (K + kGvRows - 1) / kGvRows;
+  dim3 grid((unsigned)((N + kGvCols - 1) / kGvCols), (unsigned)nbands);
   if (token_mode || nb == 1)
     hipLaunchKernelGGL(gemv_partial_kernel<1>, grid, dim3(kGvThreads), 0, st, P, ld, K, N, nb, token_mode, C, ec_row,
                        ec_mean, S, part);
@@ -585,14 +608,17 @@ hipError_t run_gemv(const int8_t* P, int64_t ld, int64_t K, int64_t N, int64_t n
     hipLaunchKernelGGL(gemv_partial_kernel<4>, grid, dim3(kGvThreads), 0, st, P, ld, K, N, nb, token_mode, C, ec_row,
                        ec_mean, S, part);
   const int64_t count = nb * N;
-  hipLaunchKernelGGL(gemv_reduce_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, st, part, nchunks,
-                     count, out);
+  int tpi = 1;
+  while (tpi < 16 && tpi * 8 < nbands) tpi *= 2;
+  const int64_t threads = count * tpi;
+  hipLaunchKernelGGL(gemv_reduce_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, part, nbands,
+                     count, tpi, out);
   return hipGetLastError();
 }
 
 size_t gemv_part_bytes(int64_t K, int64_t N, int64_t nb) {
-  const int64_t nchunks = (K + kGvRows - 1) / kGvRows;
-  return align_up((size_t)nchunks * nb * N * 4, 256);
+  const int64_t nbands = (K + kGvRows - 1) / kGvRows;
+  return align_up((size_t)nbands * nb * N * 4, 256);
 }
 
 template <bool A_KMAJOR, int EPI, bool EC, int NB = 1>
@@ -627,13 +653,13 @@ GemmTiming& gemm_timing() {
 size_t dx_workspace(int64_t T, int64_t D, int64_t d_in, int64_t S, int ec) {
   if (!ec || S <= 0) return 0;
   const int64_t B = T / S;
-  return gemv_part_bytes(D, d_in, B) + align_up((size_t)B * d_in * 4, 256);
+  return kWsHeaderBytes + gemv_part_bytes(D, d_in, B) + align_up((size_t)B * d_in * 4, 256);
 }
 
 size_t dw_workspace(int64_t T, int64_t D, int64_t d_in, int64_t S, int ec) {
   (void)D; (void)S;
   if (ec != S3R_EC_TWO_WAY) return 0;
-  return gemv_part_bytes(T, d_in, 1) + align_up((size_t)d_in * 4, 256);
+  return kWsHeaderBytes + gemv_part_bytes(T, d_in, 1) + align_up((size_t)d_in * 4, 256);
 }
 
 hipError_t launch_backward_dx(const DxArgs& a, hipStream_t st) {
@@ -645,8 +671,8 @@ hipError_t launch_backward_dx(const DxArgs& a, hipStream_t st) {
   ep.S = a.S; ep.B = B;
   ep.out = a.out; ep.ld_out = a.ld_out; ep.out_i32 = a.out_dt == S3R_I32_RAW;
   if (ep.ec && a.T > 0 && a.d_in > 0) {
-    float* part = (float*)a.ws;
-    float* v = (float*)(a.ws + gemv_part_bytes(a.D, a.d_in, B));
+    float* part = (float*)(a.ws + kWsHeaderBytes);
+    float* v = (float*)(a.ws + kWsHeaderBytes + gemv_part_bytes(a.D, a.d_in, B));
     if (a.D > 0) {
       hipError_t e = run_gemv(a.W, a.ld_w, a.D, a.d_in, B, 0, a.ec_col, nullptr, nullptr, a.S, part, v, st);
       if (e != hipSuccess) return e;
@@ -671,8 +697,8 @@ hipError_t launch_backward_dw(const DwArgs& a, hipStream_t st) {
   ep.S = a.S; ep.B = B;
   ep.out = a.out; ep.ld_out = a.ld_out; ep.out_i32 = a.out_dt == S3R_I32_RAW;
   if (ep.ec && a.D > 0 && a.d_in > 0) {
-    float* part = (float*)a.ws;
-    float* u = (float*)(a.ws + gemv_part_bytes(a.T, a.d_in, 1));
+    float* part = (float*)(a.ws + kWsHeaderBytes);
+    float* u = (float*)(a.ws + kWsHeaderBytes + gemv_part_bytes(a.T, a.d_in, 1));
     if (a.T > 0) {
       hipError_t e = run_gemv(a.X, a.ld_x, a.T, a.d_in, 1, 1, nullptr, a.ec_row, a.ec_mean, a.S, part, u, st);
       if (e != hipSuccess) return e;

@@ -483,15 +483,13 @@ struct ResParams {
   uint32_t layer; uint64_t seed;
 };
 
-// Block-to-block exchange through per-block slots: slots[b] = (phase << 32) | payload,
-// cleared by the init kernel before each launch.  Cross-block data is written and
-// read with agent-scope atomics, which bypass the per-XCD L2s, so no cache
-// write-back or invalidation is needed; a slot per block avoids a contended
-// counter.
-__global__ void resident_init_kernel(unsigned long long* slots, int n) {
-  for (int i = threadIdx.x; i < n; i += blockDim.x) slots[i] = 0ull;
-}
-
+// Block-to-block exchange through per-block slots in the workspace header:
+// slots[b] = (phase << 32) | payload.  A call with generation g (a header word,
+// advanced by one per call) uses phases 2g+1 and 2g+2, so a slot left by an
+// earlier call never matches; a zero-filled header starts at g = 0.  Cross-block
+// data is written and read with agent-scope atomics, which bypass the per-XCD
+// L2s, so no cache write-back or invalidation is needed; a slot per block avoids
+// a contended counter.
 __device__ __forceinline__ void store_coherent64(unsigned long long* p, unsigned long long v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -569,8 +567,8 @@ __device__ __forceinline__ void decode_bf16x8(const uint4& u, float v[8]) {
 template <int MODE, bool EC>
 __global__ __launch_bounds__(kResThreads, 1) void quantize_resident_kernel(
     ResParams p, const uint16_t* __restrict__ G, const float* __restrict__ sx, const float* __restrict__ sw,
-    int8_t* __restrict__ Q, float* __restrict__ delta_out, uint32_t* __restrict__ flags, unsigned long long* slots,
-    float* __restrict__ col_part, double* __restrict__ blk_sum, float* __restrict__ ec_row,
+    int8_t* __restrict__ Q, float* __restrict__ delta_out, uint32_t* __restrict__ flags, uint32_t* gen_word,
+    unsigned long long* slots, float* __restrict__ col_part, double* __restrict__ blk_sum, float* __restrict__ ec_row,
     float* __restrict__ ec_col, float* __restrict__ ec_mean) {
   __shared__ uint4 s_chunk[kResLdsChunks][kResThreads];        // 128 KB; reused for column sums
   __shared__ int32_t s_thr[kResMaxRows];
@@ -588,6 +586,7 @@ __global__ __launch_bounds__(kResThreads, 1) void quantize_resident_kernel(
   const int64_t r0 = (int64_t)blockIdx.x * p.rows_per_block;
   const int R = p.rows_per_block;
 
+  const uint32_t gen = __hip_atomic_load(gen_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   float sw8[8];
   load8_scale(sw, j0, p.D, true, sw8);
 
@@ -639,7 +638,10 @@ __global__ __launch_bounds__(kResThreads, 1) void quantize_resident_kernel(
   uint32_t bmax = s_red[0];
 #pragma unroll
   for (int w = 1; w < kResThreads / kWave; ++w) bmax = bmax > s_red[w] ? bmax : s_red[w];
-  const uint32_t abits = exchange_max(slots, 1u, bmax, p.nblocks, flags, s_vote);
+  const uint32_t abits = exchange_max(slots, 2u * gen + 1u, bmax, p.nblocks, flags, s_vote);
+  // every block read `gen` before publishing above, so the next call's generation can be set now
+  if (blockIdx.x == 0 && tid == 0)
+    __hip_atomic_store(gen_word, gen + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // ---- pass 2: codes from the held band
   const Step st = make_step(abits);
@@ -781,7 +783,7 @@ __global__ __launch_bounds__(kResThreads, 1) void quantize_resident_kernel(
     a = wave_sum(a);
     if (lane == 0) store_coherent(&blk_sum[blockIdx.x], a);
   }
-  exchange_max(slots + kResMaxBlocks, 2u, 0u, p.nblocks, flags, s_vote);
+  exchange_max(slots + kResMaxBlocks, 2u * gen + 2u, 0u, p.nblocks, flags, s_vote);
 
   // ---- per-example channel means and grand means (every band lies in one example).
   // tpi threads of one wave share an output: each sums every tpi-th band in
@@ -796,7 +798,17 @@ __global__ __launch_bounds__(kResThreads, 1) void quantize_resident_kernel(
   for (int64_t it = ((int64_t)blockIdx.x * kResThreads + tid) / tpi; it < items; it += gthreads / tpi) {
     const int64_t b = it / p.D, j = it - b * p.D;
     double acc = 0.0;
-    for (int64_t k = sub; k < bpe; k += tpi) acc += (double)load_coherent(&col_part[(b * bpe + k) * p.D + j]);
+    for (int64_t k = sub; k < bpe; k += 4 * tpi) {          // four loads in flight, summed in k order
+      float t[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t kk = k + u * tpi;
+        const float v = load_coherent(&col_part[(b * bpe + min(kk, bpe - 1)) * p.D + j]);
+        t[u] = kk < bpe ? v : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc += (double)t[u];
+    }
     for (int o = 1; o < tpi; o <<= 1) acc += __shfl_xor(acc, o, kWave);
     if (sub == 0) ec_col[it] = (float)(acc * dlt / (double)p.S);
   }
@@ -824,7 +836,7 @@ __global__ void empty_kernel(int64_t T, int64_t D, int64_t B, int per_token, flo
 
 struct WsLayout {
   size_t amax_part, amax_rows, row_part, col_part, colq_part, blk_sum, counter, total;
-  size_t res_sync, res_col, res_blk;   // resident path (shares the space of the regions above)
+  size_t res_col, res_blk;   // resident path (shares the space of the regions above)
 };
 
 WsLayout ws_layout(int64_t T, int64_t D, int64_t S, int ec, int scale, bool colsum) {
@@ -833,7 +845,7 @@ WsLayout ws_layout(int64_t T, int64_t D, int64_t S, int ec, int scale, bool cols
   const int64_t tpe = (S + kRowsPerTile - 1) / kRowsPerTile;
   const int64_t n_rt = B * tpe;
   const int64_t n_ct = (D + kColsPerTile - 1) / kColsPerTile;
-  size_t off = 0;
+  size_t off = kWsHeaderBytes;
   w.amax_part = off; off = align_up(off + (scale == S3R_PER_TENSOR ? kAmaxBlocks * 4 : 0), 256);
   w.amax_rows = off; off = align_up(off + (scale == S3R_PER_TOKEN ? (size_t)T * 4 : 0), 256);
   w.row_part = off;  off = align_up(off + (ec ? (size_t)T * n_ct * 4 : 0), 256);
@@ -843,8 +855,7 @@ WsLayout ws_layout(int64_t T, int64_t D, int64_t S, int ec, int scale, bool cols
   w.blk_sum = off;   off = align_up(off + (ec ? (size_t)B * bpe * 8 : 0), 256);
   w.counter = off;   off = align_up(off + 4, 256);
   // resident path: sync words, [blocks x D] column partials, [blocks] eps sums
-  size_t r = 0;
-  w.res_sync = r; r = align_up(r + 2 * kResMaxBlocks * 8, 256);
+  size_t r = kWsHeaderBytes;
   const int64_t nb = std::min<int64_t>(T, kResMaxBlocks);
   w.res_col = r;  r = align_up(r + (scale == S3R_PER_TENSOR && ec ? (size_t)nb * D * 4 : 0), 256);
   w.res_blk = r;  r = align_up(r + (scale == S3R_PER_TENSOR && ec ? (size_t)nb * 8 : 0), 256);
@@ -965,15 +976,13 @@ hipError_t launch_resident(const QuantArgs& a, const WsLayout& L, int R, hipStre
   p.nk = (int)(R / (kResThreads >> p.tc_log2));
   p.nblocks = (int)((a.T + R - 1) / R);
   p.layer = a.layer; p.seed = a.seed;
-  unsigned long long* slots = (unsigned long long*)(a.ws + L.res_sync);
-  hipLaunchKernelGGL(resident_init_kernel, dim3(1), dim3(kResThreads), 0, st, slots, 2 * kResMaxBlocks);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  uint32_t* gen_word = (uint32_t*)(a.ws + kWsGenOffset);
+  unsigned long long* slots = (unsigned long long*)(a.ws + kWsSlotOffset);
   const uint16_t* G = (const uint16_t*)a.G;
   float* col = (float*)(a.ws + L.res_col);
   double* blk = (double*)(a.ws + L.res_blk);
   void* args[] = {&p, (void*)&G, (void*)&a.sx, (void*)&a.sw, (void*)&a.Q, (void*)&a.delta, (void*)&a.flags,
-                  &slots, &col, &blk, (void*)&a.ec_row, (void*)&a.ec_col, (void*)&a.ec_mean};
+                  &gen_word, &slots, &col, &blk, (void*)&a.ec_row, (void*)&a.ec_col, (void*)&a.ec_mean};
   return hipLaunchKernel(reinterpret_cast<const void*>(&quantize_resident_kernel<MODE, EC>),
                          dim3((unsigned)p.nblocks), dim3(kResThreads), args, 0, st);
 }

@@ -116,4 +116,14 @@ hipError_t launch_backward_dw(const DwArgs& a, hipStream_t st);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Every workspace starts with a header of synchronization words shared by all
+// entry points (so one buffer may serve quantize and backward calls that do not
+// overlap in time).  The caller zero-fills a workspace once before its first
+// use; every completed call leaves the header valid for the next one.
+constexpr size_t kWsHeaderBytes = 65536;
+constexpr size_t kWsGenOffset = 0;           // uint32: single-pass quantizer call generation
+constexpr size_t kWsSlotOffset = 256;        // 2 x 1024 uint64: single-pass quantizer exchange slots
+constexpr size_t kWsCounterOffset = 32768;   // 8192 uint32: GEMV column-block arrival counters
+constexpr int kWsMaxCounters = 8192;
+
 }  // namespace s3r

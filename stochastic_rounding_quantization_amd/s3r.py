@@ -192,7 +192,7 @@ def _pad16(n: int) -> int:
 
 def _workspace(nbytes: int, device):
     import torch
-    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device) if nbytes else None
+    return torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=device) if nbytes else None
 
 
 def q_buffer(rows: int, cols: int, device):

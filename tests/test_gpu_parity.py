@@ -181,7 +181,7 @@ def test_quantize_strided_and_unaligned():
         Qbuf = torch.full((T, D + pad + 1), 99, dtype=torch.int8, device=DEV)
         d = s3r.qdesc(T, D, T, s3r.S3R, s3r.EC_NONE, seed=9)
         delta = torch.empty(1, device=DEV)
-        ws = torch.empty(max(s3r.s3r_quantize_workspace(d), 1), dtype=torch.uint8, device=DEV)
+        ws = torch.zeros(max(s3r.s3r_quantize_workspace(d), 1), dtype=torch.uint8, device=DEV)
         s3r.s3r_quantize(d, Gbuf[:, :D], None, None, Qbuf[:, :D], delta, ws=ws)
         torch.cuda.synchronize()
         got = host(Qbuf)
