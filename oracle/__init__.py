@@ -23,9 +23,11 @@ Modules:
   quantize  -- fold, step, RTNE / SR / S3R codes, forward-operand prep
   ec        -- S3R-EC error statistics and the structured projection
   backward  -- exact integer GEMMs, dequantised and corrected dX and dW
+  swiglu    -- the SwiGLU FFN block's backward glue between the down and the
+               gate / up projections (fp32 in a fixed order, bf16 results)
 
 Parity status: every function here is pinned by a test in
-``tests/test_oracle_pins.py`` (against torch's Philox header, exact rational
+``tests/test_oracle_pins.py`` or ``tests/test_oracle_swiglu_pins.py`` (against torch's Philox header, exact rational
 arithmetic, closed forms, library routines or brute force); none is marked
 "parity unpinned".
 """
