@@ -182,6 +182,28 @@ int s3r_backward_dw(const s3r_qdesc* desc,
 /* Workspace for either backward call (the larger of the two). */
 size_t s3r_backward_workspace(const s3r_qdesc* desc, int64_t d_in);
 
+/* ---- SwiGLU FFN block glue --------------------------------------------
+ * s3r_swiglu_backward: the gradients of H = silu(A_gate) * A_up with respect to
+ * the two pre-activations, between the down projection's backward (dH) and the
+ * gate / up projections' backward.  Not part of the method: the S3R page times
+ * a whole SwiGLU FFN block ("Setup", single-block FFN benchmarks; Table III).
+ *   G_up   = dH * silu(A_gate)
+ *   G_gate = dH * A_up * silu'(A_gate),  silu'(a) = s (1 + a (1 - s)),  s = 1/(1 + exp(-a))
+ * Arithmetic: fp32, one rounding per operation in exactly the order written
+ * above, in which s = 1 / (1 + e) with e = exp(-a), silu = a * s, and
+ * exp(x) = Taylor7(r) * 2^n with x clamped to [-104, 89], n = rint(x log2 e),
+ * r = (x - n ln2_hi) - n ln2_lo (ln2_hi = 0.693145751953125,
+ * ln2_lo = 1.4286068203094173e-6, Horner from 1/5040 down to 1); the results
+ * are rounded to bf16 (nearest, ties to even; NaN -> 0x7FC0).
+ *   dH [T x F] f32 (ld_dh), A_gate / A_up [T x F] bf16 bit patterns (ld_a),
+ *   G_gate / G_up [T x F] bf16 bit patterns (ld_g), all device pointers,
+ *   row-major.  16-byte-aligned pointers with ld_dh % 4 == 0 and
+ *   ld_a, ld_g % 8 == 0 take the vector path; any layout is accepted.
+ */
+int s3r_swiglu_backward(int64_t T, int64_t F, const float* dH, int64_t ld_dh,
+                        const uint16_t* A_gate, const uint16_t* A_up, int64_t ld_a,
+                        uint16_t* G_gate, uint16_t* G_up, int64_t ld_g, hipStream_t stream);
+
 /* ---- measurement aid --------------------------------------------------
  * s3r_time_next_gemm: record `start` immediately before and `stop` immediately
  * after the INT8 GEMM kernel launched by the next s3r_backward_dx /

@@ -35,6 +35,11 @@ X_MIN, X_MAX = F(-104.0), F(89.0)      # exp underflows / overflows fp32 beyond 
 def exp32(x: np.ndarray) -> np.ndarray:
     """exp in fp32: clamp, n = rint(x log2 e), r = (x - n ln2_hi) - n ln2_lo, Taylor(r) * 2^n."""
     x = np.asarray(x, dtype=F)
+    with np.errstate(all="ignore"):
+        return _exp32(x)
+
+
+def _exp32(x: np.ndarray) -> np.ndarray:
     xc = np.where(x < X_MIN, X_MIN, np.where(x > X_MAX, X_MAX, x)).astype(F)    # NaN passes through
     n = np.rint((xc * LOG2E).astype(F)).astype(F)
     r = ((xc - (n * LN2_HI).astype(F)).astype(F) - (n * LN2_LO).astype(F)).astype(F)
@@ -61,6 +66,11 @@ def bf16_to_f32(b: np.ndarray) -> np.ndarray:
 def silu_parts(a: np.ndarray):
     """fp32 (s, silu(a), silu'(a)) in the fixed operation order."""
     a = np.asarray(a, dtype=F)
+    with np.errstate(all="ignore"):
+        return _silu_parts(a)
+
+
+def _silu_parts(a: np.ndarray):
     e = exp32(-a)
     s = (F(1.0) / (F(1.0) + e).astype(F)).astype(F)
     silu = (a * s).astype(F)
@@ -73,7 +83,8 @@ def glue(dH: np.ndarray, A_gate_bits: np.ndarray, A_up_bits: np.ndarray):
     dH = np.asarray(dH, dtype=F)
     a = bf16_to_f32(A_gate_bits)
     u = bf16_to_f32(A_up_bits)
-    _, silu, ds = silu_parts(a)
-    g_up = (dH * silu).astype(F)
-    g_gate = ((dH * u).astype(F) * ds).astype(F)
+    with np.errstate(all="ignore"):            # inf * 0 and the like give NaN, as in IEEE fp32
+        _, silu, ds = silu_parts(a)
+        g_up = (dH * silu).astype(F)
+        g_gate = ((dH * u).astype(F) * ds).astype(F)
     return round_bf16(g_gate), round_bf16(g_up)

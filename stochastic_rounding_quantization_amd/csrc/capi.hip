@@ -159,6 +159,16 @@ int s3r_backward_dw(const s3r_qdesc* d, const int8_t* Q, int64_t ld_q, const flo
   return finish(launch_backward_dw(a, stream));
 }
 
+int s3r_swiglu_backward(int64_t T, int64_t F, const float* dH, int64_t ld_dh, const uint16_t* A_gate,
+                        const uint16_t* A_up, int64_t ld_a, uint16_t* G_gate, uint16_t* G_up, int64_t ld_g,
+                        hipStream_t stream) {
+  if (T < 0 || F < 0 || ld_dh < F || ld_a < F || ld_g < F) return S3R_ERR_INVALID_ARG;
+  if (T > 0 && F > 0 && (!dH || !A_gate || !A_up || !G_gate || !G_up)) return S3R_ERR_INVALID_ARG;
+  int rc;
+  if ((rc = check_arch())) return rc;
+  return finish(launch_swiglu_backward(T, F, dH, ld_dh, A_gate, A_up, ld_a, G_gate, G_up, ld_g, stream));
+}
+
 int s3r_time_next_gemm(hipEvent_t start, hipEvent_t stop) {
   GemmTiming& t = gemm_timing();
   t.start = start;
@@ -178,6 +188,6 @@ const char* s3r_status_string(int s) {
   }
 }
 
-int s3r_version(void) { return 100; }
+int s3r_version(void) { return 200; }
 
 }  // extern "C"

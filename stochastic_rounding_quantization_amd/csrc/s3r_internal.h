@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "../../include/s3r.h"
 
 namespace s3r {
@@ -113,6 +115,11 @@ size_t dx_workspace(int64_t T, int64_t D, int64_t d_in, int64_t S, int ec);
 size_t dw_workspace(int64_t T, int64_t D, int64_t d_in, int64_t S, int ec);
 hipError_t launch_backward_dx(const DxArgs& a, hipStream_t st);
 hipError_t launch_backward_dw(const DwArgs& a, hipStream_t st);
+
+// SwiGLU backward glue (swiglu.hip).
+hipError_t launch_swiglu_backward(int64_t T, int64_t F, const float* dH, int64_t ld_dh, const uint16_t* Ag,
+                                  const uint16_t* Au, int64_t ld_a, uint16_t* Gg, uint16_t* Gu, int64_t ld_g,
+                                  hipStream_t st);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

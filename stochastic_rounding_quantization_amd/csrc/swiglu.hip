@@ -1,0 +1,121 @@
+// SwiGLU backward glue of an FFN block, for gfx950 (an HBM-bound elementwise pass).
+//
+// The S3R page times a whole SwiGLU FFN block ("Setup", single-block FFN
+// benchmarks; Table III).  Between the down projection's backward (which gives
+// dH) and the gate / up projections' backward sit the gradients of
+// H = silu(A_gate) * A_up with respect to the two pre-activations:
+//   G_up   = dH * silu(A_gate)
+//   G_gate = dH * A_up * silu'(A_gate),  silu'(a) = s (1 + a (1 - s)),  s = 1 / (1 + exp(-a)).
+// The arithmetic is fixed here (the pages leave it open): fp32, one rounding
+// per operation in the order below (no contraction), an exponential built from
+// a Cody-Waite reduction by ln 2 and the degree-7 Taylor polynomial, results
+// rounded to bf16 (nearest, ties to even).  Every element is independent, so
+// the results do not depend on the launch shape.
+#include "s3r_internal.h"
+
+namespace s3r {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2Hi = 0.693145751953125f;        // 15 significant bits: n * kLn2Hi is exact for |n| < 512
+constexpr float kLn2Lo = 1.4286068203094173e-06f;   // ln 2 - kLn2Hi
+constexpr float kXMin = -104.f, kXMax = 89.f;        // exp under- / overflows fp32 beyond these
+
+__device__ __forceinline__ float exp32(float x) {
+  const float xc = x < kXMin ? kXMin : (x > kXMax ? kXMax : x);   // NaN passes through
+  const float n = __builtin_rintf(xc * kLog2e);
+  const float r = (xc - n * kLn2Hi) - n * kLn2Lo;
+  float p = (float)(1.0 / 5040.0);
+  p = p * r + (float)(1.0 / 720.0);
+  p = p * r + (float)(1.0 / 120.0);
+  p = p * r + (float)(1.0 / 24.0);
+  p = p * r + (float)(1.0 / 6.0);
+  p = p * r + 0.5f;
+  p = p * r + 1.f;
+  p = p * r + 1.f;
+  const int ni = n != n ? 0 : (int)n;
+  return __builtin_ldexpf(p, ni);
+}
+
+__device__ __forceinline__ uint32_t bf16_rne(float v) {
+  const uint32_t u = __float_as_uint(v);
+  if (v != v) return 0x7FC0u;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// (G_gate, G_up) of one element, as bf16 bit patterns.
+__device__ __forceinline__ void glue1(float dh, float a, float u, uint32_t& gg, uint32_t& gu) {
+  const float e = exp32(-a);
+  const float s = __fdiv_rn(1.f, 1.f + e);
+  const float silu = a * s;
+  const float ds = s * (1.f + a * (1.f - s));
+  gu = bf16_rne(dh * silu);
+  gg = bf16_rne((dh * u) * ds);
+}
+
+// One thread: 8 consecutive elements of one row (16-byte loads and stores).
+template <bool VEC>
+__global__ __launch_bounds__(256) void swiglu_backward_kernel(
+    int64_t T, int64_t F, const float* __restrict__ dH, int64_t ld_dh, const uint16_t* __restrict__ Ag,
+    const uint16_t* __restrict__ Au, int64_t ld_a, uint16_t* __restrict__ Gg, uint16_t* __restrict__ Gu,
+    int64_t ld_g) {
+  const int64_t cpr = (F + 7) / 8;
+  const int64_t total = T * cpr;
+  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < total; c += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t t = c / cpr, j0 = (c - t * cpr) * 8;
+    const float* dh = dH + t * ld_dh + j0;
+    const uint16_t* ag = Ag + t * ld_a + j0;
+    const uint16_t* au = Au + t * ld_a + j0;
+    uint16_t* gg = Gg + t * ld_g + j0;
+    uint16_t* gu = Gu + t * ld_g + j0;
+    if (VEC && j0 + 8 <= F) {
+      const float4 h0 = *reinterpret_cast<const float4*>(dh);
+      const float4 h1 = *reinterpret_cast<const float4*>(dh + 4);
+      const uint4 va = *reinterpret_cast<const uint4*>(ag);
+      const uint4 vu = *reinterpret_cast<const uint4*>(au);
+      const float h[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+      const uint32_t wa[4] = {va.x, va.y, va.z, va.w}, wu[4] = {vu.x, vu.y, vu.z, vu.w};
+      uint32_t og[4], ou[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t g0, u0, g1, u1;
+        glue1(h[2 * i], __uint_as_float(wa[i] << 16), __uint_as_float(wu[i] << 16), g0, u0);
+        glue1(h[2 * i + 1], __uint_as_float(wa[i] & 0xFFFF0000u), __uint_as_float(wu[i] & 0xFFFF0000u), g1, u1);
+        og[i] = g0 | (g1 << 16);
+        ou[i] = u0 | (u1 << 16);
+      }
+      *reinterpret_cast<uint4*>(gg) = make_uint4(og[0], og[1], og[2], og[3]);
+      *reinterpret_cast<uint4*>(gu) = make_uint4(ou[0], ou[1], ou[2], ou[3]);
+    } else {
+      for (int i = 0; i < 8 && j0 + i < F; ++i) {
+        uint32_t g, u;
+        glue1(dh[i], bf16_to_f32(ag[i]), bf16_to_f32(au[i]), g, u);
+        gg[i] = (uint16_t)g;
+        gu[i] = (uint16_t)u;
+      }
+    }
+  }
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace
+
+hipError_t launch_swiglu_backward(int64_t T, int64_t F, const float* dH, int64_t ld_dh, const uint16_t* Ag,
+                                  const uint16_t* Au, int64_t ld_a, uint16_t* Gg, uint16_t* Gu, int64_t ld_g,
+                                  hipStream_t st) {
+  if (T == 0 || F == 0) return hipSuccess;
+  const bool vec = aligned16(dH) && aligned16(Ag) && aligned16(Au) && aligned16(Gg) && aligned16(Gu) &&
+                   ld_dh % 4 == 0 && ld_a % 8 == 0 && ld_g % 8 == 0;
+  const int64_t total = T * ((F + 7) / 8);
+  const unsigned blocks = (unsigned)std::min<int64_t>((total + 255) / 256, 8192);
+  if (vec)
+    hipLaunchKernelGGL(swiglu_backward_kernel<true>, dim3(blocks), dim3(256), 0, st, T, F, dH, ld_dh, Ag, Au, ld_a,
+                       Gg, Gu, ld_g);
+  else
+    hipLaunchKernelGGL(swiglu_backward_kernel<false>, dim3(blocks), dim3(256), 0, st, T, F, dH, ld_dh, Ag, Au, ld_a,
+                       Gg, Gu, ld_g);
+  return hipGetLastError();
+}
+
+}  // namespace s3r

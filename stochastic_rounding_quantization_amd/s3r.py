@@ -28,7 +28,8 @@ PER_TENSOR, PER_TOKEN = 0, 1
 FLAG_NONFINITE, FLAG_TINY_STEP, FLAG_SYNC_TIMEOUT = 1, 2, 4
 
 EXPORTED = ["s3r_quantize_workspace", "s3r_quantize", "s3r_backward_dx", "s3r_backward_dw",
-            "s3r_backward_workspace", "s3r_time_next_gemm", "s3r_status_string", "s3r_version"]
+            "s3r_backward_workspace", "s3r_swiglu_backward", "s3r_time_next_gemm", "s3r_status_string",
+            "s3r_version"]
 
 
 class S3RError(RuntimeError):
@@ -71,6 +72,8 @@ def lib() -> ctypes.CDLL:
     L.s3r_backward_dw.restype = ctypes.c_int
     L.s3r_backward_workspace.argtypes = [DP, I64]
     L.s3r_backward_workspace.restype = SZ
+    L.s3r_swiglu_backward.argtypes = [I64, I64, P, I64, P, P, I64, P, P, I64, P]
+    L.s3r_swiglu_backward.restype = ctypes.c_int
     L.s3r_time_next_gemm.argtypes = [P, P]
     L.s3r_time_next_gemm.restype = ctypes.c_int
     L.s3r_status_string.argtypes = [ctypes.c_int]
@@ -167,6 +170,27 @@ def s3r_backward_dw(desc: QDesc, Q, delta, Xq, s_w, xs_b, ec_row, ec_col, ec_mea
     if rc_only:
         return rc
     _check("s3r_backward_dw", rc)
+
+
+def s3r_swiglu_backward(dH, A_gate, A_up, G_gate, G_up, stream=None, *, rc_only=False):
+    """bf16 tensors are passed as torch.bfloat16 (their bit patterns are the C ABI's uint16)."""
+    T, F = dH.shape
+    if A_up.stride() != A_gate.stride() or G_up.stride() != G_gate.stride():
+        raise ValueError("A_gate / A_up and G_gate / G_up must share their layouts")
+    rc = lib().s3r_swiglu_backward(T, F, _ptr(dH), _ld(dH, F), _ptr(A_gate), _ptr(A_up), _ld(A_gate, F),
+                                   _ptr(G_gate), _ptr(G_up), _ld(G_gate, F), _stream(stream))
+    if rc_only:
+        return rc
+    _check("s3r_swiglu_backward", rc)
+
+
+def swiglu_backward(dH, A_gate, A_up, stream=None):
+    """Allocate G_gate, G_up (bf16, like A_gate) and run s3r_swiglu_backward."""
+    import torch
+    G_gate = torch.empty(A_gate.shape, dtype=torch.bfloat16, device=A_gate.device)
+    G_up = torch.empty_like(G_gate)
+    s3r_swiglu_backward(dH, A_gate, A_up, G_gate, G_up, stream)
+    return G_gate, G_up
 
 
 def s3r_time_next_gemm(start_event, stop_event) -> None:

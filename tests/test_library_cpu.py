@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status(L):
-    assert s3r.s3r_version() == 100
+    assert s3r.s3r_version() == 200
     assert s3r.s3r_status_string(0) == "ok"
     assert s3r.s3r_status_string(-3) == "workspace too small"
 
@@ -100,6 +100,20 @@ def test_backward_argument_errors(L):
     assert dw(d=pt) == -2                    # dW needs a per-tensor step
     assert s3r.s3r_backward_workspace(s3r.qdesc(64, 96, 32, s3r.S3R, s3r.EC_TWO_WAY), 128) > 0
     assert s3r.s3r_backward_workspace(d, 128) == 0
+
+
+def test_swiglu_argument_errors(L):
+    P = ctypes.c_void_p
+    ok = dict(T=4, F=16, dH=P(256), ldh=16, Ag=P(512), Au=P(768), lda=16, Gg=P(1024), Gu=P(1280), ldg=16)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return L.s3r_swiglu_backward(a["T"], a["F"], a["dH"], a["ldh"], a["Ag"], a["Au"], a["lda"], a["Gg"],
+                                     a["Gu"], a["ldg"], None)
+
+    assert call(T=-1) == -1
+    assert call(ldh=8) == -1 and call(lda=8) == -1 and call(ldg=8) == -1
+    assert call(dH=None) == -1 and call(Gu=None) == -1
 
 
 def test_no_gpu_reports_hip_error(L):
