@@ -1,16 +1,24 @@
-"""Benchmark of the S3R-EC quantized backward of one linear layer on one MI355X.
+"""Benchmark of the S3R-EC quantized backward on one MI355X.
 
-One step = the whole backward hot path on one batch of synthetic input: the
-fused quantizer (fold, per-tensor step, S3R thresholds, codes, S3R-EC
-statistics), dX (correction GEMV + INT8 GEMM with dequant/correction
-epilogue) and dW (correction GEMV + INT8 GEMM with epilogue).  The forward
-operand prep (RTNE codes of X and W with their scales and column sums) is
-forward-pass work and runs once before timing.
+Default workload: the backward of one Llama-3-8B-shaped SwiGLU FFN block
+(T = 8192 tokens in 4 examples of 2048, d_model 4096, d_ff 14336, bf16).  One
+step = the whole backward on one batch of synthetic input:
+  down projection: quantize G_out (fold, per-tensor step, S3R thresholds,
+    codes, S3R-EC statistics) -> dH (correction GEMV + INT8 GEMM + epilogue)
+    -> dW_down (correction GEMV + INT8 GEMM + epilogue);
+  SwiGLU glue: dH, A_gate, A_up -> G_gate, G_up (bf16);
+  gate and up projections: the same three calls on G_gate and G_up, their dX
+    added into one dX.
+The forward-operand prep (RTNE codes of X, H and the three weights with their
+scales and column sums) is forward-pass work and runs once before timing.
+``--workload down-8192x14336x4096-bf16`` (or another linear workload) times one
+linear layer's backward instead.
 
-Prints one JSON line.  ``value`` is the step's INT8 throughput in TOP/s:
-2 GEMMs x 2*T*D*d_in ops over the measured step time (the quantizer and the
-correction are inside the step).  Extra fields report the quantizer's GB/s
-(algorithmic bytes: one read of G plus one write of Q) and each kernel's time.
+Prints one JSON line.  ``value`` is the step's INT8 throughput in TOP/s: the
+GEMMs' 2*M*N*K ops (6 GEMMs for the block, 2 for a linear layer) over the
+measured step time, with everything else inside the step.  Extra fields report
+the quantizer's GB/s (algorithmic bytes: one read of G plus one write of Q per
+quantize call) and each stage's time.
 """
 from __future__ import annotations
 
@@ -30,7 +38,10 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, GB/s
 # HBM byte counts of the GEMM kernels, taken with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE and
 # scaled by the same counters' reading for a plain copy of known size.  The file records the
 # sha256 of the kernel source it was measured on; a stale record is not reported.
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_down-8192x14336x4096.md")
+TRAFFIC_FILES = {
+    "down-8192x14336x4096-bf16": os.path.join(ROOT, "profiles", "traffic_gemm_down-8192x14336x4096.md"),
+    "ffn-block-8192x4096x14336-bf16": os.path.join(ROOT, "profiles", "traffic_gemm_ffn-block-8192x4096x14336.md"),
+}
 GEMM_SOURCE = os.path.join(ROOT, "stochastic_rounding_quantization_amd", "csrc", "gemm.hip")
 
 MODES = {
@@ -46,9 +57,10 @@ def measured_traffic(kernel_key, workload):
     """HBM bytes per launch of one GEMM kernel from the committed counter summary, or None."""
     import hashlib
     import re
-    if not os.path.exists(TRAFFIC_FILE):
+    path = TRAFFIC_FILES.get(workload)
+    if path is None or not os.path.exists(path):
         return None
-    text = open(TRAFFIC_FILE).read()
+    text = open(path).read()
     m = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
     src = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
     if not m or m.group(1) != src or f"workload: {workload}" not in text:
@@ -102,15 +114,57 @@ def cpu_baseline(inp, w, mode, ec, rows):
                       f"integer GEMMs ({blas_threads} BLAS threads); forward-operand prep untimed"}
 
 
+def block_cpu_baseline(inp, b, mode, ec, rows):
+    """Time the CPU oracle's FFN-block backward on the first ``rows`` tokens (whole examples)."""
+    import numpy as np
+    from oracle import pipeline
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    S = b.rows_per_example
+    sample = {k: (v[:rows] if k in ("G", "X", "H", "A_gate", "A_up") else v) for k, v in inp.items()}
+    t0 = time.perf_counter()
+    r = pipeline.ffn_block_backward(sample, mode=mode, ec=ec, rows_per_example=S)
+    dt = time.perf_counter() - t0
+    assert np.isfinite(r["dX"]).all()
+    ops = 6 * 2.0 * rows * b.d_model * b.d_ff
+    return {"value": ops / dt / 1e12, "unit": "TOP/s", "cores": int(blas_threads), "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": f"first {rows} tokens ({rows // S} example(s) of {S}) of the block, full d_model={b.d_model} "
+                      f"and d_ff={b.d_ff}: three quantizers and the glue in numpy (1 thread), six float64 BLAS "
+                      f"integer GEMMs ({blas_threads} BLAS threads), forward-operand prep inside the timing"}
+
+
+class Timeline:
+    """Named intervals of one step, timed with HIP events on the launch stream."""
+
+    def __init__(self, torch, names, steps):
+        self.torch, self.names = torch, names
+        self.ev = []
+        for _ in range(steps):
+            d = {}
+            for n in names:
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(); b.record()          # creates the underlying HIP events
+                d[n] = (a, b)
+            self.ev.append(d)
+
+    def avg_us(self, name):
+        import numpy as np
+        return float(np.mean([d[name][0].elapsed_time(d[name][1]) for d in self.ev])) * 1e3
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="down-8192x14336x4096-bf16")
+    ap.add_argument("--workload", default="ffn-block-8192x4096x14336-bf16")
     ap.add_argument("--mode", default="s3r-ec-two-way", choices=sorted(MODES))
     ap.add_argument("--cpu-rows", type=int, default=-1,
-                    help="tokens in the CPU-oracle sample (-1: the whole workload, 0: skip)")
+                    help="tokens in the CPU-oracle sample (-1: the default sample, 0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (reference for HBM byte counters) and exit")
     args = ap.parse_args()
@@ -119,7 +173,6 @@ def main():
               "(the multi-GPU path is design-only)", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
     from stochastic_rounding_quantization_amd import inputs, s3r
 
@@ -131,18 +184,152 @@ def main():
         copy_calibration(dev)
         return
     s3r.lib()   # fail loudly if the HIP library is missing
+    if args.workload in inputs.BLOCKS:
+        out = run_block(args, dev, torch, inputs, s3r)
+    else:
+        out = run_linear(args, dev, torch, inputs, s3r)
+    print(json.dumps(out), flush=True)
+
+
+def _to_dev(torch, dev, a, dtype):
+    import numpy as np
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    return torch.from_numpy(a).to(dev)
+
+
+def _timed_steps(torch, step, tl, steps, warmup):
+    log(f"warmup {warmup}")
+    for _ in range(warmup):
+        step(None)
+    torch.cuda.synchronize()
+    log(f"timing {steps} steps")
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(tl.ev[i])
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def _roofline(gemm_us, workload, gop):
+    key = max(gemm_us, key=lambda k: gemm_us[k])
+    achieved = gop / (gemm_us[key] / 1e6) / 1e3
+    return {"kernel": f"gemm {key}", "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_INT8_TOPS,
+            "unit": "TOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4), "traffic": measured_traffic(key, workload),
+            "algorithmic": f"2*M*N*K = {gop:.1f} GOP per launch (int8 multiply-adds x 2)"}
+
+
+def run_block(args, dev, torch, inputs, s3r):
+    mode, ec = MODES[args.mode]
+    b = inputs.BLOCKS[args.workload]
+    T, M, F, S = b.tokens, b.d_model, b.d_ff, b.rows_per_example
+    B = T // S
+    log(f"workload {b.name}: T={T} d_model={M} d_ff={F} S={S} mode={args.mode}; drawing inputs")
+    inp = inputs.make_ffn_block_inputs(b)
+    dv = {k: _to_dev(torch, dev, inp[k], "bf16") for k in ("G", "X", "H", "W_down", "W_gate", "W_up", "A_gate", "A_up")}
+    log("forward-operand prep (untimed)")
+    fx = s3r.forward_operand(dv["X"], rows_per_example=S)
+    fh = s3r.forward_operand(dv["H"], rows_per_example=S)
+    fwd = s3r.forward_operand(dv["W_down"], rows_per_example=M)
+    fwg = s3r.forward_operand(dv["W_gate"], rows_per_example=F)
+    fwu = s3r.forward_operand(dv["W_up"], rows_per_example=F)
+    for k in ("X", "H", "W_down", "W_gate", "W_up"):
+        del dv[k]
+    proj = {  # name: (rows of G, cols of G = D, d_in, layer, forward operand of X, of W)
+        "down": (M, F, 0, fh, fwd), "gate": (F, M, 1, fx, fwg), "up": (F, M, 2, fx, fwu)}
+    st = {}
+    for name, (D, din, layer, fxx, fww) in proj.items():
+        d = s3r.qdesc(T, D, S, mode, ec, s3r.PER_TENSOR, layer_id=layer, seed=0)
+        st[name] = dict(desc=d, Q=s3r.q_buffer(T, D, dev), delta=torch.empty(1, dtype=torch.float32, device=dev),
+                        er=torch.empty(T, dtype=torch.float32, device=dev) if ec else None,
+                        ec=torch.empty(B, D, dtype=torch.float32, device=dev) if ec else None,
+                        em=torch.empty(B, dtype=torch.float32, device=dev) if ec else None,
+                        flags=torch.zeros(1, dtype=torch.int32, device=dev), din=din, fx=fxx, fw=fww)
+    ws_q = torch.zeros(max(s3r.s3r_quantize_workspace(st[n]["desc"]) for n in st), dtype=torch.uint8, device=dev)
+    ws_b = torch.zeros(max(max(s3r.s3r_backward_workspace(st[n]["desc"], st[n]["din"]) for n in st), 1),
+                       dtype=torch.uint8, device=dev)
+    dH = torch.empty(T, F, dtype=torch.float32, device=dev)
+    Gg = torch.empty(T, F, dtype=torch.bfloat16, device=dev)
+    Gu = torch.empty_like(Gg)
+    dX = torch.empty(T, M, dtype=torch.float32, device=dev)
+    dW = {"down": torch.empty(M, F, dtype=torch.float32, device=dev),
+          "gate": torch.empty(F, M, dtype=torch.float32, device=dev),
+          "up": torch.empty(F, M, dtype=torch.float32, device=dev)}
+    G_in = {"down": dv["G"], "gate": Gg, "up": Gu}
+    dX_out = {"down": dH, "gate": dX, "up": dX}
+    names = ["step", "glue"] + [f"quantize_{n}" for n in st] + [f"dx_{n}" for n in st] + [f"dw_{n}" for n in st]
+    tl = Timeline(torch, names, args.steps)
+
+    def linear(name, ev):
+        p = st[name]
+        if ev:
+            ev[f"quantize_{name}"][0].record()
+        s3r.s3r_quantize(p["desc"], G_in[name], p["fx"].delta, p["fw"].delta, p["Q"], p["delta"], None, p["er"],
+                         p["ec"], p["em"], p["flags"], ws_q)
+        if ev:
+            ev[f"quantize_{name}"][1].record()
+            s3r.s3r_time_next_gemm(*ev[f"dx_{name}"])
+        s3r.s3r_backward_dx(p["desc"], p["Q"], p["delta"], p["fw"].Q, p["fx"].delta, p["fw"].code_colsum[0], p["er"],
+                            p["ec"], p["em"], dX_out[name], ws_b, accumulate=(name == "up"))
+        if ev:
+            s3r.s3r_time_next_gemm(*ev[f"dw_{name}"])
+        s3r.s3r_backward_dw(p["desc"], p["Q"], p["delta"], p["fx"].Q, p["fw"].delta, p["fx"].code_colsum, p["er"],
+                            p["ec"], p["em"], dW[name], ws_b)
+
+    def step(ev):
+        if ev:
+            ev["step"][0].record()
+        linear("down", ev)
+        if ev:
+            ev["glue"][0].record()
+        s3r.s3r_swiglu_backward(dH, dv["A_gate"], dv["A_up"], Gg, Gu)
+        if ev:
+            ev["glue"][1].record()
+        linear("gate", ev)
+        linear("up", ev)
+        if ev:
+            ev["step"][1].record()
+
+    ms_step = _timed_steps(torch, step, tl, args.steps, args.warmup)
+    for n in st:
+        assert int(st[n]["flags"].item()) == 0, n
+    gop = 2.0 * T * M * F / 1e9                      # each of the six GEMMs
+    value = 6 * gop / (ms_step / 1e3) / 1e3
+    gemm_us = {f"{k}_{n}": tl.avg_us(f"{k}_{n}") for n in st for k in ("dx", "dw")}
+    q_us = sum(tl.avg_us(f"quantize_{n}") for n in st)
+    q_bytes = (T * M + 2 * T * F) * 3                 # bf16 G read once + int8 Q written, three calls
+    q_gbs = q_bytes / (q_us / 1e6) / 1e9
+    out = {
+        "metric": "S3R-EC backward TOPS (quant+INT8 dX/dW) & quantizer GB/s, % of MI355X peak",
+        "value": round(value, 2), "unit": "TOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "i8", "data": "synthetic",
+        "config": {"workload": b.name, "tokens": T, "d_model": M, "d_ff": F, "rows_per_example": S,
+                   "mode": args.mode, "step_scale": "per-tensor", "g_dtype": "bf16",
+                   "stages": "down (quantize, dX=dH, dW), SwiGLU glue, gate and up (quantize, dX added, dW)"},
+        "frac_of_int8_peak": round(value / PEAK_INT8_TOPS, 4),
+        "quantizer": {"us": round(q_us, 2), "GB_s": round(q_gbs, 1), "frac_of_hbm_peak": round(q_gbs / PEAK_HBM_GBS, 4),
+                      "algorithmic_bytes": q_bytes, "calls": 3},
+        "kernels_us": {**{f"quantize_{n}": round(tl.avg_us(f"quantize_{n}"), 2) for n in st},
+                       **{f"gemm_{k}": round(v, 2) for k, v in gemm_us.items()},
+                       "glue": round(tl.avg_us("glue"), 2), "step_events": round(tl.avg_us("step"), 2)},
+        "gemm_tops": {k: round(gop / (v / 1e6) / 1e3, 1) for k, v in gemm_us.items()},
+        "roofline": _roofline(gemm_us, b.name, gop),
+    }
+    if args.cpu_rows != 0:
+        rows = S if args.cpu_rows < 0 else max(S, min(args.cpu_rows, T) // S * S)
+        log(f"CPU oracle baseline on the first {rows} tokens")
+        out["cpu_baseline"] = block_cpu_baseline(inp, b, mode, ec, rows)
+    return out
+
+
+def run_linear(args, dev, torch, inputs, s3r):
     mode, ec = MODES[args.mode]
     w = inputs.WORKLOADS[args.workload]
     T, D, K, S = w.tokens, w.d_out, w.d_in, w.rows_per_example
     log(f"workload {w.name}: T={T} D={D} d_in={K} S={S} mode={args.mode}; drawing inputs")
     inp = inputs.make_linear_inputs(w)
-
-    def to_dev(a):
-        if inp["dtype"] == "bf16":
-            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
-        return torch.from_numpy(a).to(dev)
-
-    G, X, W = to_dev(inp["G"]), to_dev(inp["X"]), to_dev(inp["W"])
+    G, X, W = (_to_dev(torch, dev, inp[k], inp["dtype"]) for k in ("G", "X", "W"))
     log("forward-operand prep (untimed)")
     fx = s3r.forward_operand(X, rows_per_example=S)
     fw = s3r.forward_operand(W, rows_per_example=D)
@@ -159,57 +346,30 @@ def main():
     ws_b = torch.zeros(max(s3r.s3r_backward_workspace(desc, K), 1), dtype=torch.uint8, device=dev)
     dX = torch.empty(T, K, dtype=torch.float32, device=dev)
     dW = torch.empty(D, K, dtype=torch.float32, device=dev)
-    s_x, s_w = fx.delta, fw.delta
-    r_W, xs = fw.code_colsum[0], fx.code_colsum
+    tl = Timeline(torch, ["step", "quantize", "dx", "dw"], args.steps)
 
-    def ev():
-        e = torch.cuda.Event(enable_timing=True)
-        e.record()          # creates the underlying HIP event
-        return e
+    def step(ev):
+        if ev:
+            ev["step"][0].record()
+            ev["quantize"][0].record()
+        s3r.s3r_quantize(desc, G, fx.delta, fw.delta, Q, delta, None, e_r, e_c, e_m, flags, ws_q)
+        if ev:
+            ev["quantize"][1].record()
+            s3r.s3r_time_next_gemm(*ev["dx"])
+        s3r.s3r_backward_dx(desc, Q, delta, fw.Q, fx.delta, fw.code_colsum[0], e_r, e_c, e_m, dX, ws_b)
+        if ev:
+            s3r.s3r_time_next_gemm(*ev["dw"])
+        s3r.s3r_backward_dw(desc, Q, delta, fx.Q, fw.delta, fx.code_colsum, e_r, e_c, e_m, dW, ws_b)
+        if ev:
+            ev["step"][1].record()
 
-    def step(events=None):
-        if events:
-            events[0].record()
-        s3r.s3r_quantize(desc, G, s_x, s_w, Q, delta, None, e_r, e_c, e_m, flags, ws_q)
-        if events:
-            events[1].record()
-            s3r.s3r_time_next_gemm(events[2], events[3])
-        s3r.s3r_backward_dx(desc, Q, delta, fw.Q, s_x, r_W, e_r, e_c, e_m, dX, ws_b)
-        if events:
-            s3r.s3r_time_next_gemm(events[4], events[5])
-        s3r.s3r_backward_dw(desc, Q, delta, fx.Q, s_w, xs, e_r, e_c, e_m, dW, ws_b)
-        if events:
-            events[6].record()
-
-    log(f"warmup {args.warmup}")
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    evs = [[ev() for _ in range(7)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    log(f"timing {args.steps} steps")
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / args.steps
+    ms_step = _timed_steps(torch, step, tl, args.steps, args.warmup)
     assert int(flags.item()) == 0
-
-    def avg(a, b):
-        return float(np.mean([e[a].elapsed_time(e[b]) for e in evs]))   # ms
-
-    t_q = avg(0, 1)
-    t_gx = avg(2, 3)
-    t_gw = avg(4, 5)
-    t_step_ev = avg(0, 6)
+    t_q, t_gx, t_gw = tl.avg_us("quantize"), tl.avg_us("dx"), tl.avg_us("dw")
     gop = 2.0 * T * D * K / 1e9
-    value = 2 * gop / (ms_step / 1e3) / 1e3          # TOP/s
+    value = 2 * gop / (ms_step / 1e3) / 1e3
     q_bytes = T * D * (2 if inp["dtype"] == "bf16" else 4) + T * D
-    q_gbs = q_bytes / (t_q / 1e3) / 1e9
-    dom_key, dom_name, t_dom = ("dw", "gemm dW (gemm_i8_kernel<false, EPI_DW>)", t_gw) if t_gw >= t_gx else \
-        ("dx", "gemm dX (gemm_i8_kernel<true, EPI_DX>)", t_gx)
-    achieved = gop / (t_dom / 1e3) / 1e3              # TOP/s
+    q_gbs = q_bytes / (t_q / 1e6) / 1e9
     out = {
         "metric": "S3R-EC backward TOPS (quant+INT8 dX/dW) & quantizer GB/s, % of MI355X peak",
         "value": round(value, 2), "unit": "TOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -218,22 +378,19 @@ def main():
         "config": {"workload": w.name, "tokens": T, "d_in": K, "d_out": D, "rows_per_example": S,
                    "mode": args.mode, "step_scale": "per-tensor", "g_dtype": inp["dtype"]},
         "frac_of_int8_peak": round(value / PEAK_INT8_TOPS, 4),
-        "quantizer": {"us": round(t_q * 1e3, 2), "GB_s": round(q_gbs, 1),
+        "quantizer": {"us": round(t_q, 2), "GB_s": round(q_gbs, 1),
                       "frac_of_hbm_peak": round(q_gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": q_bytes},
-        "kernels_us": {"quantize_call": round(t_q * 1e3, 2), "gemm_dx": round(t_gx * 1e3, 2),
-                       "gemm_dw": round(t_gw * 1e3, 2), "step_events": round(t_step_ev * 1e3, 2)},
-        "gemm_tops": {"dx": round(gop / (t_gx / 1e3) / 1e3, 1), "dw": round(gop / (t_gw / 1e3) / 1e3, 1)},
-        "roofline": {"kernel": dom_name, "bound": "mfma", "achieved": round(achieved, 1),
-                     "peak": PEAK_INT8_TOPS, "unit": "TOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4),
-                     "traffic": measured_traffic(dom_key, w.name),
-                     "algorithmic": f"2*T*D*d_in = {gop:.1f} GOP per launch (int8 multiply-adds x 2)"},
+        "kernels_us": {"quantize_call": round(t_q, 2), "gemm_dx": round(t_gx, 2), "gemm_dw": round(t_gw, 2),
+                       "step_events": round(tl.avg_us("step"), 2)},
+        "gemm_tops": {"dx": round(gop / (t_gx / 1e6) / 1e3, 1), "dw": round(gop / (t_gw / 1e6) / 1e3, 1)},
+        "roofline": _roofline({"dx": t_gx, "dw": t_gw}, w.name, gop),
     }
     if args.cpu_rows != 0:
         rows = T if args.cpu_rows < 0 else min(args.cpu_rows, T)
         rows = max(S, rows // S * S)
         log(f"CPU oracle baseline on the first {rows} tokens")
         out["cpu_baseline"] = cpu_baseline(inp, w, mode, ec, rows)
-    print(json.dumps(out), flush=True)
+    return out
 
 
 if __name__ == "__main__":

@@ -57,7 +57,10 @@ extern "C" {
 #define S3R_ERR_HIP          -5  /* a HIP call or kernel launch failed */
 
 /* ---- enums ------------------------------------------------------------- */
-typedef enum { S3R_F32 = 0, S3R_BF16 = 1, S3R_I32_RAW = 2 } s3r_dtype;
+/* S3R_F32_ACC (s3r_backward_dx only): add the f32 result into the f32 output
+ * (dX of two projections of the same input, e.g. the gate and up projections
+ * of a SwiGLU block). */
+typedef enum { S3R_F32 = 0, S3R_BF16 = 1, S3R_I32_RAW = 2, S3R_F32_ACC = 3 } s3r_dtype;
 /* Rounding of G' (S3R page, "Compared Configurations"):
  *   RTNE  deterministic round to nearest even;
  *   SR    independent SR, one Philox4x32-10 32-bit word per element;
@@ -143,8 +146,9 @@ int s3r_quantize(const s3r_qdesc* desc,
  * accumulation.  GEMM operands (Q, Wq, Xq) need 16-byte-aligned base
  * pointers, leading dims that are multiples of 16 and below 2^24, and
  * (rows + 320) * ld < 2^32 bytes; K <= 131072.
- * out_dt: S3R_F32 (dequantised, corrected per desc->ec) or S3R_I32_RAW (raw
- * int32 accumulators, no dequantisation, no correction); the output's leading
+ * out_dt: S3R_F32 (dequantised, corrected per desc->ec), S3R_F32_ACC (the same,
+ * added into the existing output; dX only) or S3R_I32_RAW (raw int32
+ * accumulators, no dequantisation, no correction); the output's leading
  * dim must be below 2^22 and its base 4-byte aligned.
  *
  * s3r_backward_dx: dX [T x d_in] = diag(1/s_x) (Delta Q - P(E')) Wq.

@@ -63,3 +63,28 @@ def raw_accumulators(Q, Wq, Xq, dx_rows=None, dw_rows=None):
     acc_dx = backward.int_matmul(Q[dx_rows], Wq)
     acc_dw = backward.int_matmul(np.ascontiguousarray(Q[:, dw_rows].T), Xq)
     return acc_dx, acc_dw
+
+
+def ffn_block_backward(inp: dict, *, mode: int, ec: int, seed: int = 0, rows_per_example: int) -> dict:
+    """Backward of one SwiGLU FFN block (the S3R page's single-block benchmark, "Setup"; Table III).
+
+    ``inp`` holds the bf16 bit patterns of make_ffn_block_inputs: G (the block's output gradient),
+    X, H, A_gate, A_up, W_down, W_gate, W_up.  Each of the three projections runs the quantized
+    linear backward above (layer ids: down 0, gate 1, up 2).  The down projection's dX, dH, enters
+    the glue in fp32 (the dtype the backward hands over), and the glue's bf16 results are the gate
+    and up projections' upstream gradients; the block's dX is the sum of theirs.
+    """
+    from . import swiglu
+    S = rows_per_example
+    down = linear_backward({"G": inp["G"], "X": inp["H"], "W": inp["W_down"], "dtype": "bf16"}, mode=mode, ec=ec,
+                           seed=seed, layer_id=0, rows_per_example=S)
+    dH = down["dX"].astype(np.float32)
+    g_gate, g_up = swiglu.glue(dH, inp["A_gate"], inp["A_up"])
+    fx = oq.forward_operand(inp["X"], "bf16", rows_per_example=S)
+    out = {"down": down, "G_gate": g_gate, "G_up": g_up}
+    for name, g, w, layer in (("gate", g_gate, inp["W_gate"], 1), ("up", g_up, inp["W_up"], 2)):
+        fw = oq.forward_operand(w, "bf16", rows_per_example=w.shape[0])
+        out[name] = linear_backward({"G": g, "X": inp["X"], "W": w, "dtype": "bf16"}, mode=mode, ec=ec, seed=seed,
+                                    layer_id=layer, rows_per_example=S, fx=fx, fw=fw)
+    out["dX"] = out["gate"]["dX"] + out["up"]["dX"]
+    return out

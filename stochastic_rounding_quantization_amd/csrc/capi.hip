@@ -110,7 +110,7 @@ int s3r_backward_dx(const s3r_qdesc* d, const int8_t* Q, int64_t ld_q, const flo
                     size_t ws_bytes, hipStream_t stream) {
   int rc = check_desc(d);
   if (rc) return rc;
-  if (out_dt != S3R_F32 && out_dt != S3R_I32_RAW) return S3R_ERR_UNSUPPORTED;
+  if (out_dt != S3R_F32 && out_dt != S3R_I32_RAW && out_dt != S3R_F32_ACC) return S3R_ERR_UNSUPPORTED;
   const int64_t T = d->rows, D = d->cols;
   if (d_in < 0 || D > kMaxK) return S3R_ERR_INVALID_ARG;
   const bool out_nonempty = T > 0 && d_in > 0;
@@ -118,7 +118,7 @@ int s3r_backward_dx(const s3r_qdesc* d, const int8_t* Q, int64_t ld_q, const flo
   if (out_nonempty && ((uintptr_t)dX & 3u)) return S3R_ERR_INVALID_ARG;
   if ((rc = check_gemm_operand(Q, ld_q, T, D, T > 0 && D > 0))) return rc;
   if ((rc = check_gemm_operand(Wq, ld_w, D, d_in, D > 0 && d_in > 0))) return rc;
-  const bool ec = d->ec != S3R_EC_NONE && out_dt == S3R_F32;
+  const bool ec = d->ec != S3R_EC_NONE && out_dt != S3R_I32_RAW;
   if (ec && (!r_W || !ec_row || !ec_col || !ec_mean)) return S3R_ERR_INVALID_ARG;
   const size_t need = ec ? dx_workspace(T, D, d_in, d->rows_per_example, d->ec) : 0;
   if (ws_bytes < need || (need && (!ws || ((uintptr_t)ws & 255u)))) return S3R_ERR_WORKSPACE;

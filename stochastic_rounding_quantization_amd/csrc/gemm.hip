@@ -265,7 +265,8 @@ __device__ __forceinline__ void k_step(const LoadMap& lm, const FragMap& fm, int
 // Stores go through a buffer descriptor over the tile's rows of the output
 // (rows past M fall outside it and are dropped by the range check); columns
 // past N are masked per column block.  Per-row byte offsets are uniform.
-enum { EPI_RAW = 0, EPI_DX = 1, EPI_DW = 2 };
+enum { EPI_RAW = 0, EPI_DX = 1, EPI_DW = 2, EPI_DXA = 3 };   // EPI_DXA: dX added into the output
+__host__ __device__ constexpr bool is_dx(int epi) { return epi == EPI_DX || epi == EPI_DXA; }
 constexpr int kMaxB = 8;   // examples whose dW correction terms the epilogue applies
 
 __device__ __forceinline__ int row_in_block(int r) { return (r >> 2) * 8 + (r & 3); }
@@ -299,7 +300,7 @@ __device__ __forceinline__ void epilogue(const GemmParams& g, const EpiParams& e
 #pragma unroll
     for (int b = 0; b < NB; ++b) colB[b][j] = 0.f;
     if (EC && n_ok[j]) {
-      if constexpr (EPI == EPI_DX) {
+      if constexpr (is_dx(EPI)) {
         colA[j] = (float)ep.colsum[n];                                   // r_W[n]
         if constexpr (!GATHER) colV[j] = ep.vec[(m0 / ep.S) * g.N + n];  // v_b[n], the tile's example
       } else if constexpr (EPI == EPI_DW) {
@@ -313,6 +314,18 @@ __device__ __forceinline__ void epilogue(const GemmParams& g, const EpiParams& e
 
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
+    // EPI_DXA: this block-row's current output values, all loads issued before any is used
+    float old[4][4][4];
+    if constexpr (EPI == EPI_DXA) {
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr)
+            old[rq][j][rr] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                ro, voff[j], (uint32_t)(i * 32 + rq * 8 + rr) * ld4, 0));
+    }
 #pragma unroll
     for (int rq = 0; rq < 4; ++rq) {
       // four consecutive rows of this lane: lr = lane_row + i*32 + rq*8 + rr
@@ -331,7 +344,7 @@ __device__ __forceinline__ void epilogue(const GemmParams& g, const EpiParams& e
       for (int j = 0; j < 4; ++j) {
         if (!n_ok[j]) continue;
         float gv[4];
-        if constexpr (EPI == EPI_DX && EC && GATHER) {
+        if constexpr (is_dx(EPI) && EC && GATHER) {
           const int64_t n = n0 + wn * 128 + j * 32 + (lane & 31);
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) gv[rr] = ep.vec[(int64_t)__float_as_int(f[rr].w) * g.N + n];
@@ -345,14 +358,15 @@ __device__ __forceinline__ void epilogue(const GemmParams& g, const EpiParams& e
             __builtin_amdgcn_raw_buffer_store_b32(v, ro, voff[j], soff, 0);
           } else {
             float corr = 0.f;
-            if constexpr (EC && EPI == EPI_DX) corr = fmaf(f[rr].z, colA[j], f[rr].y * (GATHER ? gv[rr] : colV[j]));
+            if constexpr (EC && is_dx(EPI)) corr = fmaf(f[rr].z, colA[j], f[rr].y * (GATHER ? gv[rr] : colV[j]));
             if constexpr (EC && EPI == EPI_DW) {
               float t = f[rr].y * colA[j];
 #pragma unroll
               for (int b = 0; b < NB; ++b) t = fmaf(eb[rr][b], colB[b][j], t);
               corr = t;
             }
-            const float o = fmaf(f[rr].x, (float)v, -corr);
+            float o = fmaf(f[rr].x, (float)v, -corr);
+            if constexpr (EPI == EPI_DXA) o = old[rq][j][rr] + o;
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(o), ro, voff[j], soff, 0);
           }
         }
@@ -407,7 +421,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmParams g, 
   // per-row factors of the tile into LDS (the stages are free now)
   float4* rowf = reinterpret_cast<float4*>(g_stage0);
   float* roweb = reinterpret_cast<float*>(g_stage1);
-  if constexpr (EPI == EPI_DX) {
+  if constexpr (is_dx(EPI)) {
     // x: Delta_t / s_x[t], y: 1 / s_x[t], z: (eps_t - mu_b) / s_x[t], w: example index
     for (int r = threadIdx.x; r < BM; r += kGemmThreads) {
       const int64_t tt = m0 + r;
@@ -442,7 +456,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmParams g, 
     }
   }
   __syncthreads();
-  if constexpr (EPI == EPI_DX && EC) {
+  if constexpr (is_dx(EPI) && EC) {
     const int64_t last = min(m0 + BM, g.M) - 1;
     if (m0 / ep.S == last / ep.S) epilogue<EPI, EC, false, NB>(g, ep, m0, n0, acc);
     else epilogue<EPI, EC, true, NB>(g, ep, m0, n0, acc);
@@ -666,7 +680,7 @@ hipError_t launch_backward_dx(const DxArgs& a, hipStream_t st) {
   const int64_t B = a.S > 0 ? a.T / a.S : 0;
   EpiParams ep{};
   ep.delta = a.delta; ep.per_token = a.per_token; ep.row_scale = a.sx;
-  ep.ec = (a.ec != S3R_EC_NONE) && a.out_dt == S3R_F32;
+  ep.ec = (a.ec != S3R_EC_NONE) && (a.out_dt == S3R_F32 || a.out_dt == S3R_F32_ACC);
   ep.colsum = a.rW; ep.ec_row = a.ec_row; ep.ec_mean = a.ec_mean;
   ep.S = a.S; ep.B = B;
   ep.out = a.out; ep.ld_out = a.ld_out; ep.out_i32 = a.out_dt == S3R_I32_RAW;
@@ -684,6 +698,8 @@ hipError_t launch_backward_dx(const DxArgs& a, hipStream_t st) {
   }
   const GemmParams g = make_gemm(a.Q, a.ld_q, a.W, a.ld_w, a.T, a.d_in, a.D);
   if (a.out_dt == S3R_I32_RAW) return run_gemm<true, EPI_RAW, false>(g, ep, st);
+  if (a.out_dt == S3R_F32_ACC)
+    return ep.ec ? run_gemm<true, EPI_DXA, true>(g, ep, st) : run_gemm<true, EPI_DXA, false>(g, ep, st);
   if (ep.ec) return run_gemm<true, EPI_DX, true>(g, ep, st);
   return run_gemm<true, EPI_DX, false>(g, ep, st);
 }

@@ -24,7 +24,7 @@ import numpy as np
 
 __all__ = [
     "Workload", "WORKLOADS", "f32_to_bf16_bits", "bf16_bits_to_f32",
-    "student_t", "gaussian", "make_linear_inputs",
+    "student_t", "gaussian", "make_linear_inputs", "FfnBlock", "BLOCKS", "make_ffn_block_inputs",
 ]
 
 
@@ -123,4 +123,58 @@ def make_linear_inputs(w: Workload, with_x: bool = True, with_w: bool = True) ->
         out["X"] = _store(gaussian(base + 2, (T, K), w.x_std), w.dtype)
     if with_w:
         out["W"] = _store(gaussian(base + 3, (D, K), w.w_std), w.dtype)
+    return out
+
+
+@dataclass(frozen=True)
+class FfnBlock:
+    """One SwiGLU FFN block: H = silu(X W_gate^T) * (X W_up^T), Y = H W_down^T.
+
+    Its backward takes G_out = dY [T x d_model] and produces dX [T x d_model]
+    and the three weight gradients.  The forward activations (A_gate, A_up and
+    H) are synthetic inputs of the backward, drawn here.
+    """
+    name: str
+    wid: int
+    tokens: int              # T
+    d_model: int
+    d_ff: int
+    rows_per_example: int    # S
+    g_nu: float = 3.0
+    g_scale: float = 1e-4
+    w_std: float = 0.02
+
+    def scaled(self, tokens: int, d_model: int, d_ff: int, rows_per_example: int | None = None) -> "FfnBlock":
+        return FfnBlock(f"{self.name}@{tokens}x{d_model}x{d_ff}", self.wid, tokens, d_model, d_ff,
+                        rows_per_example or tokens, self.g_nu, self.g_scale, self.w_std)
+
+
+BLOCKS = {
+    # Llama-3-8B-shaped FFN block, bf16: T=8192 (4 x 2048), d_model=4096, d_ff=14336
+    "ffn-block-8192x4096x14336-bf16": FfnBlock("ffn-block-8192x4096x14336-bf16", 4, 8192, 4096, 14336, 2048),
+}
+
+
+def make_ffn_block_inputs(b: FfnBlock) -> dict:
+    """bf16 bit patterns: G_out [T x d_model] = g_scale * t(g_nu); X [T x d_model], A_gate and
+    A_up [T x d_ff] ~ N(0, 1); W_gate, W_up [d_ff x d_model] and W_down [d_model x d_ff] ~ N(0, w_std^2);
+    H = silu(A_gate) * A_up evaluated in float64 from the bf16 values and rounded to bf16 (the
+    forward activation the down projection consumed).  Seeds 1000 * wid + k, k: G_out 1, X 2,
+    W_down 3, A_gate 4, A_up 5, W_gate 6, W_up 7."""
+    base = 1000 * b.wid
+    T, M, F = b.tokens, b.d_model, b.d_ff
+    out = {"dtype": "bf16"}
+    out["G"] = f32_to_bf16_bits(student_t(base + 1, (T, M), b.g_nu, b.g_scale))
+    out["X"] = f32_to_bf16_bits(gaussian(base + 2, (T, M), 1.0))
+    out["W_down"] = f32_to_bf16_bits(gaussian(base + 3, (M, F), b.w_std))
+    out["A_gate"] = f32_to_bf16_bits(gaussian(base + 4, (T, F), 1.0))
+    out["A_up"] = f32_to_bf16_bits(gaussian(base + 5, (T, F), 1.0))
+    out["W_gate"] = f32_to_bf16_bits(gaussian(base + 6, (F, M), b.w_std))
+    out["W_up"] = f32_to_bf16_bits(gaussian(base + 7, (F, M), b.w_std))
+    h = np.empty((T, F), np.uint16)
+    for r0 in range(0, T, 1024):                 # bounded float64 temporaries
+        a = bf16_bits_to_f32(out["A_gate"][r0:r0 + 1024]).astype(np.float64)
+        u = bf16_bits_to_f32(out["A_up"][r0:r0 + 1024]).astype(np.float64)
+        h[r0:r0 + 1024] = f32_to_bf16_bits((a / (1.0 + np.exp(-a)) * u).astype(np.float32))
+    out["H"] = h
     return out

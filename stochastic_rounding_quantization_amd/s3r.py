@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(HERE, "libs3r.so")
 S3R_OK = 0
 STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported combination", -3: "workspace too small",
           -4: "device is not gfx950", -5: "HIP error"}
-S3R_F32, S3R_BF16, S3R_I32_RAW = 0, 1, 2
+S3R_F32, S3R_BF16, S3R_I32_RAW, S3R_F32_ACC = 0, 1, 2, 3
 RTNE, SR, S3R = 0, 1, 2
 EC_NONE, EC_DX_ONLY, EC_TWO_WAY = 0, 1, 2
 PER_TENSOR, PER_TOKEN = 0, 1
@@ -119,10 +119,10 @@ def _gdtype(t):
     raise ValueError(f"unsupported gradient dtype {t.dtype}")
 
 
-def _odtype(t):
+def _odtype(t, accumulate=False):
     import torch
     if t.dtype == torch.float32:
-        return S3R_F32
+        return S3R_F32_ACC if accumulate else S3R_F32
     if t.dtype == torch.int32:
         return S3R_I32_RAW
     raise ValueError(f"unsupported output dtype {t.dtype}")
@@ -149,11 +149,11 @@ def s3r_backward_workspace(desc: QDesc, d_in: int) -> int:
 
 
 def s3r_backward_dx(desc: QDesc, Q, delta, Wq, s_x, r_W, ec_row, ec_col, ec_mean, dX, ws=None, stream=None,
-                    *, rc_only=False):
+                    *, accumulate=False, rc_only=False):
     d_in = dX.shape[1]
     rc = lib().s3r_backward_dx(ctypes.byref(desc), _ptr(Q), _ld(Q, desc.cols), _ptr(delta), _ptr(Wq),
                                _ld(Wq, d_in), d_in, _ptr(s_x), _ptr(r_W), _ptr(ec_row), _ptr(ec_col),
-                               _ptr(ec_mean), _ptr(dX), _odtype(dX), _ld(dX, d_in), _ptr(ws),
+                               _ptr(ec_mean), _ptr(dX), _odtype(dX, accumulate), _ld(dX, d_in), _ptr(ws),
                                0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
     if rc_only:
         return rc
@@ -265,13 +265,15 @@ def forward_operand(X, rows_per_example=None, stream=None) -> Quantized:
                     stream=stream)
 
 
-def backward_dx(q: Quantized, Wq, s_x=None, r_W=None, out_dtype=None, stream=None):
+def backward_dx(q: Quantized, Wq, s_x=None, r_W=None, out_dtype=None, stream=None, out=None):
+    """dX of one projection; with ``out`` (f32) the result is added into it."""
     import torch
     d_in = Wq.shape[1]
     T = q.desc.rows
-    dX = torch.empty(T, d_in, dtype=out_dtype or torch.float32, device=Wq.device)
+    dX = out if out is not None else torch.empty(T, d_in, dtype=out_dtype or torch.float32, device=Wq.device)
     ws = _workspace(s3r_backward_workspace(q.desc, d_in), Wq.device)
-    s3r_backward_dx(q.desc, q.Q, q.delta, Wq, s_x, r_W, q.ec_row, q.ec_col, q.ec_mean, dX, ws, stream)
+    s3r_backward_dx(q.desc, q.Q, q.delta, Wq, s_x, r_W, q.ec_row, q.ec_col, q.ec_mean, dX, ws, stream,
+                    accumulate=out is not None)
     return dX
 
 

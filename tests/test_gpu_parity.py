@@ -312,3 +312,35 @@ def test_down_8192x14336x4096_bf16_sampled():
     inp = inputs.make_linear_inputs(w)
     _check_linear(inp, w.rows_per_example, s3r.S3R, s3r.EC_TWO_WAY, dx_rows=_sample_rows(w.tokens, 16, 3),
                   dw_rows=_sample_rows(w.d_out, 10, 4))
+
+
+def test_dx_accumulate_two_projections():
+    # dX of two projections of the same input (the SwiGLU block's gate and up) added into one
+    # output with S3R_F32_ACC: equals the sum of the two oracle products
+    w = inputs.WORKLOADS["down-4096x11008x4096-bf16"].scaled(192, 136, 300, rows_per_example=64)
+    a = inputs.make_linear_inputs(w)
+    raw = inputs.make_linear_inputs(inputs.WORKLOADS["linear-256x512x1024-f32"].scaled(192, 136, 300, 64))
+    b = {"G": inputs.f32_to_bf16_bits(raw["G"]), "X": a["X"], "W": inputs.f32_to_bf16_bits(raw["W"]), "dtype": "bf16"}
+    S = 64
+    fx = s3r.forward_operand(to_dev(a["X"], "bf16"), rows_per_example=S)
+    dX = None
+    refs = []
+    for layer, inp in ((1, a), (2, b)):
+        fw = s3r.forward_operand(to_dev(inp["W"], "bf16"), rows_per_example=inp["W"].shape[0])
+        q = s3r.quantize(to_dev(inp["G"], "bf16"), mode=s3r.S3R, ec=s3r.EC_TWO_WAY, row_scale=fx.delta,
+                         col_scale=fw.delta, seed=3, layer_id=layer, rows_per_example=S)
+        dX = s3r.backward_dx(q, fw.Q, s_x=fx.delta, r_W=fw.code_colsum[0], out=dX)
+        refs.append(pipeline.linear_backward(inp, mode=s3r.S3R, ec=s3r.EC_TWO_WAY, seed=3, layer_id=layer,
+                                             rows_per_example=S)["dX"])
+    torch.cuda.synchronize()
+    e = rel_err(host(dX), refs[0] + refs[1])
+    assert e <= TOL, f"accumulated dX rel err {e:.3g}"
+
+
+def test_gate_projection_ffn_block_size_sampled():
+    # the FFN block's gate / up projection shape: G [8192 x 14336] (two-pass quantizer, 224 MiB of
+    # bf16), W [14336 x 4096], X [8192 x 4096]; S3R-EC two-way, rows sampled
+    w = inputs.WORKLOADS["down-8192x14336x4096-bf16"].scaled(8192, 4096, 14336, rows_per_example=2048)
+    inp = inputs.make_linear_inputs(w)
+    _check_linear(inp, 2048, s3r.S3R, s3r.EC_TWO_WAY, dx_rows=_sample_rows(w.tokens, 6, 5),
+                  dw_rows=_sample_rows(w.d_out, 6, 6), layer=1)
