@@ -48,10 +48,9 @@ def linear_backward(inp: dict, *, mode: int, ec: int, scale: int = oq.PER_TENSOR
     out["dX"] = backward.backward_dx(q["Q"], q["delta"], fw["Q"], fx["scale"], ec=ec,
                                      r_W=fw["code_colsum"][0], eps=q["eps"], ebar=q["ebar"], mu=q["mu"],
                                      rows_per_example=S, rows=dx_rows)
-    if scale == oq.PER_TENSOR:
-        out["dW"] = backward.backward_dw(q["Q"], q["delta"], fx["Q"], fw["scale"], ec=ec, xs=fx["code_colsum"],
-                                         eps=q["eps"], ebar=q["ebar"], mu=q["mu"], rows_per_example=S,
-                                         rows=dw_rows)
+    dw = backward.backward_dw if scale == oq.PER_TENSOR else backward.backward_dw_per_token
+    out["dW"] = dw(q["Q"], q["delta"], fx["Q"], fw["scale"], ec=ec, xs=fx["code_colsum"], eps=q["eps"],
+                   ebar=q["ebar"], mu=q["mu"], rows_per_example=S, rows=dw_rows)
     return out
 
 

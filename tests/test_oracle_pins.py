@@ -494,3 +494,97 @@ def test_corrected_gradients_unbiased_brute_force():
     bound = 4 / 256
     assert np.all(np.abs(dx_sum / n - xd @ Wq) <= bound * np.abs(Wq).sum(axis=0)[None] + 1e-9)
     assert np.all(np.abs(dw_sum / n - xd.T @ Xq) <= bound * np.abs(Xq).sum(axis=0)[None] + 1e-9)
+
+
+# ------------------------------------------------- per-token steps and dW ----
+
+def _per_token_problem(seed, T, D, K, S):
+    rng = np.random.default_rng(seed)
+    X = rng.standard_normal((T, K)).astype(np.float32)
+    W = (0.02 * rng.standard_normal((D, K))).astype(np.float32)
+    G = (1e-3 * rng.standard_t(3, (T, D))).astype(np.float32)
+    G[3] *= 100.0                                   # one outlier token: steps spread over two decades
+    fx = oq.forward_operand(X, "f32", rows_per_example=S)
+    fw = oq.forward_operand(W, "f32", rows_per_example=D)
+    q = oq.quantize(G, "f32", mode=oq.S3R, scale=oq.PER_TOKEN, row_scale=fx["scale"], col_scale=fw["scale"],
+                    seed=seed, rows_per_example=S)
+    eps, ebar, mu = ec.statistics(ec.rounding_error(q["Q"], q["x"], q["delta"]), S)
+    return dict(fx=fx, fw=fw, q=q, eps=eps, ebar=ebar, mu=mu, S=S)
+
+
+def test_requantize_columns_reaches_full_range_and_rtne_bound():
+    # absmax rule: every nonzero column reaches +-127; RTNE keeps |c_i Zq - Z| within half a step
+    # (plus the fp32 roundings of Z, c_i and Z * inv_i, a few 2^-24 relative)
+    pr = _per_token_problem(5, 48, 24, 40, 16)
+    Xq, d = pr["fx"]["Q"], pr["q"]["delta"]
+    Zq, c = backward.requantize_columns(Xq, d)
+    Z = d.astype(np.float64)[:, None] * Xq.astype(np.float64)          # exact products
+    nz = np.abs(Z).max(axis=0) > 0
+    assert np.all(np.abs(Zq[:, nz]).max(axis=0) == 127)
+    assert np.all(Zq[:, ~nz] == 0)
+    err = np.abs(c.astype(np.float64)[None, :] * Zq - Z)
+    assert np.all(err <= c.astype(np.float64)[None, :] * (0.5 + 2.0 ** -16))
+    # the column step is the exact max/127 up to one fp32 rounding
+    a = np.abs(Z).max(axis=0)
+    np.testing.assert_allclose(c[nz], a[nz] / 127, rtol=2.0 ** -22)
+
+
+def test_per_token_dw_reduces_to_per_tensor():
+    # equal steps that are a power of two and input codes whose every column reaches +-127:
+    # Z = Delta Xq exactly, c_i = Delta and Zq = Xq, so the per-token dW equals the per-tensor one
+    rng = np.random.default_rng(8)
+    T, D, K, S = 32, 12, 20, 16
+    Q = rng.integers(-127, 128, (T, D)).astype(np.int8)
+    Xq = rng.integers(-126, 127, (T, K)).astype(np.int8)
+    Xq[rng.integers(0, T, K), np.arange(K)] = 127
+    delta_t = np.full(T, 2.0 ** -9, np.float32)
+    Zq, c = backward.requantize_columns(Xq, delta_t)
+    np.testing.assert_array_equal(Zq, Xq)
+    np.testing.assert_array_equal(c, np.full(K, 2.0 ** -9, np.float32))
+    s_w = rng.uniform(0.5, 2.0, D).astype(np.float32)
+    E = rng.standard_normal((T, D)) * 2.0 ** -10
+    eps, ebar, mu = ec.statistics(E, S)
+    xs = oq.code_colsums(Xq, S)
+    for ecm in (oq.EC_NONE, oq.EC_TWO_WAY):
+        a = backward.backward_dw_per_token(Q, delta_t, Xq, s_w, ec=ecm, xs=xs, eps=eps, ebar=ebar, mu=mu,
+                                           rows_per_example=S)
+        b = backward.backward_dw(Q, delta_t[:1], Xq, s_w, ec=ecm, xs=xs, eps=eps, ebar=ebar, mu=mu,
+                                 rows_per_example=S)
+        np.testing.assert_allclose(a, b, rtol=1e-13, atol=1e-13 * np.abs(b).max())
+
+
+def test_per_token_dw_within_requantization_bound_of_exact_product():
+    # against the exact definition diag(1/s_w) (Q^T diag(Delta) Xq - correction), computed directly
+    # in float64: the only approximation is the per-column requantization, so the difference is at
+    # most sum_t |Q[t, j]| * (half a column step + fp32 slack) / s_w[j]
+    pr = _per_token_problem(9, 64, 20, 36, 16)
+    q, fx, fw, S = pr["q"], pr["fx"], pr["fw"], pr["S"]
+    Qd = q["Q"].astype(np.float64)
+    exact = Qd.T @ (q["delta"].astype(np.float64)[:, None] * fx["Q"].astype(np.float64))
+    P = ec.projection(pr["eps"], pr["ebar"], pr["mu"], S)
+    corr = P.T @ fx["Q"].astype(np.float64)                             # dense form of the correction
+    sw = fw["scale"].astype(np.float64)[:, None]
+    _, c = backward.requantize_columns(fx["Q"], q["delta"])
+    bound = (np.abs(Qd).sum(axis=0)[:, None] * c.astype(np.float64)[None, :] * (0.5 + 2.0 ** -16)) / sw
+    for ecm, sub in ((oq.EC_NONE, 0.0), (oq.EC_TWO_WAY, corr)):
+        dw = backward.backward_dw_per_token(q["Q"], q["delta"], fx["Q"], fw["scale"], ec=ecm,
+                                            xs=fx["code_colsum"], eps=pr["eps"], ebar=pr["ebar"], mu=pr["mu"],
+                                            rows_per_example=S)
+        ref = (exact - sub) / sw
+        assert np.all(np.abs(dw - ref) <= bound + 1e-12 * np.abs(ref).max())
+    # rows select channels exactly
+    rows = np.array([0, 7, 19])
+    full = backward.backward_dw_per_token(q["Q"], q["delta"], fx["Q"], fw["scale"])
+    np.testing.assert_array_equal(
+        backward.backward_dw_per_token(q["Q"], q["delta"], fx["Q"], fw["scale"], rows=rows), full[rows])
+
+
+def test_requantize_columns_flags_zero_codes():
+    # a non-finite step (a flagged token) poisons every column's step (NaN * 0 is NaN): zero codes
+    Xq = np.array([[3, 0, -127], [127, 5, 0]], np.int8)
+    Zq, c = backward.requantize_columns(Xq, np.array([np.nan, 0.5], np.float32))
+    assert np.all(np.isnan(c)) and np.all(Zq == 0)
+    # a column whose absmax is so small that 127 / a overflows fp32 gets zero codes; others are unaffected
+    d = np.array([np.float32(1e-45), np.float32(0.5)], np.float32)
+    Zq, c = backward.requantize_columns(np.array([[1, 0], [0, 100]], np.int8), d)
+    assert Zq[0, 0] == 0 and Zq[1, 1] == 127 and c[1] == np.float32(50.0) / np.float32(127)
