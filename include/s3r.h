@@ -72,7 +72,8 @@ typedef enum { S3R_EC_NONE = 0, S3R_EC_DX_ONLY = 1, S3R_EC_TWO_WAY = 2 } s3r_ec;
 /* Step granularity.  PER_TENSOR is the page's single step Delta (the only one
  * the dW GEMM can apply after S32 accumulation).  PER_TOKEN gives one step
  * per row; it is the forward operands' rule (per-token s_x, per-output-channel
- * s_w) and is also accepted for G by s3r_quantize and s3r_backward_dx. */
+ * s_w) and is also accepted for G by s3r_quantize, s3r_backward_dx and (through
+ * a per-column requantization of the inputs, see there) s3r_backward_dw. */
 typedef enum { S3R_PER_TENSOR = 0, S3R_PER_TOKEN = 1 } s3r_scale;
 
 /* Bits OR-ed into the optional device flags word by s3r_quantize. */
@@ -157,7 +158,8 @@ int s3r_quantize(const s3r_qdesc* desc,
  * the token means times the row sums r_W).
  *   Wq [D x d_in] int8 (ld_w), s_x [T] f32 (NULL = 1),
  *   r_W [d_in] int32 (required iff ec != NONE), ec_* as from s3r_quantize.
- *   ws: s3r_backward_workspace(desc, d_in) bytes (0 without EC), zero-filled once.
+ *   ws: s3r_backward_workspace(desc, d_in) bytes (dX needs none without EC),
+ *   zero-filled once.
  */
 int s3r_backward_dx(const s3r_qdesc* desc,
                     const int8_t* Q, int64_t ld_q, const float* delta,
@@ -171,9 +173,19 @@ int s3r_backward_dx(const s3r_qdesc* desc,
  * S3R page, "Quantized Backpropagation" (weight-gradient product) and
  * "Two-Way Correction" (subtract the inputs times the same averages:
  * sum_b ebar_b[j] xs_b[i] + sum_t (eps_t - mu_b) Xq[t,i]).  The correction
- * applies only for ec == TWO_WAY.  desc->scale must be PER_TENSOR.
+ * applies only for ec == TWO_WAY.
  *   Xq [T x d_in] int8 (ld_x), s_w [D] f32 (NULL = 1),
  *   xs_b [B x d_in] int32 (required iff ec == TWO_WAY).
+ * Per-token steps (desc->scale == PER_TOKEN, delta [T]) are a reading beyond
+ * the page, which explains that only a per-tensor step survives the S32
+ * accumulation over the tokens: the steps are folded into the inputs,
+ * Z = diag(Delta) Xq (fp32 products), Z is requantized per input column i with
+ * the absmax RTNE rule (c_i = fl(max_t |Z[t,i]| / 127), codes
+ * clamp(rint(fl(Z * fl(127 / max))), +-127); columns with a non-finite or
+ * subnormal-range max get zero codes), and dW = diag(1/s_w) (Q^T Zq diag(c) -
+ * correction).  Zq lives in the workspace; S3R_I32_RAW then returns Q^T Zq.
+ * ws: s3r_backward_workspace(desc, d_in) bytes, 256-byte aligned (none is
+ * needed for per-tensor steps without the two-way correction).
  */
 int s3r_backward_dw(const s3r_qdesc* desc,
                     const int8_t* Q, int64_t ld_q, const float* delta,

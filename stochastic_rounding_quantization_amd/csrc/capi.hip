@@ -91,7 +91,7 @@ int s3r_quantize(const s3r_qdesc* d, const void* G, int32_t g_dtype, int64_t ld_
 size_t s3r_backward_workspace(const s3r_qdesc* d, int64_t d_in) {
   if (check_desc(d) != S3R_OK || d_in < 0) return 0;
   const size_t a = dx_workspace(d->rows, d->cols, d_in, d->rows_per_example, d->ec);
-  const size_t b = dw_workspace(d->rows, d->cols, d_in, d->rows_per_example, d->ec);
+  const size_t b = dw_workspace(d->rows, d->cols, d_in, d->rows_per_example, d->ec, d->scale == S3R_PER_TOKEN);
   return a > b ? a : b;
 }
 
@@ -138,7 +138,6 @@ int s3r_backward_dw(const s3r_qdesc* d, const int8_t* Q, int64_t ld_q, const flo
   int rc = check_desc(d);
   if (rc) return rc;
   if (out_dt != S3R_F32 && out_dt != S3R_I32_RAW) return S3R_ERR_UNSUPPORTED;
-  if (d->scale != S3R_PER_TENSOR && out_dt == S3R_F32) return S3R_ERR_UNSUPPORTED;
   const int64_t T = d->rows, D = d->cols;
   if (d_in < 0 || T > kMaxK) return S3R_ERR_INVALID_ARG;
   const bool out_nonempty = D > 0 && d_in > 0;
@@ -148,11 +147,12 @@ int s3r_backward_dw(const s3r_qdesc* d, const int8_t* Q, int64_t ld_q, const flo
   if ((rc = check_gemm_operand(Xq, ld_x, T, d_in, T > 0 && d_in > 0))) return rc;
   const bool ec = d->ec == S3R_EC_TWO_WAY && out_dt == S3R_F32;
   if (ec && (!xs_b || !ec_row || !ec_col || !ec_mean)) return S3R_ERR_INVALID_ARG;
-  const size_t need = ec ? dw_workspace(T, D, d_in, d->rows_per_example, d->ec) : 0;
+  const int per_token = d->scale == S3R_PER_TOKEN;
+  const size_t need = dw_workspace(T, D, d_in, d->rows_per_example, ec ? d->ec : 0, per_token);
   if (ws_bytes < need || (need && (!ws || ((uintptr_t)ws & 255u)))) return S3R_ERR_WORKSPACE;
   if ((rc = check_arch())) return rc;
   DwArgs a{};
-  a.Q = Q; a.ld_q = ld_q; a.delta = delta; a.X = Xq; a.ld_x = ld_x;
+  a.Q = Q; a.ld_q = ld_q; a.delta = delta; a.per_token = per_token; a.X = Xq; a.ld_x = ld_x;
   a.T = T; a.D = D; a.d_in = d_in; a.S = d->rows_per_example;
   a.sw = s_w; a.xs = xs_b; a.ec_row = ec_row; a.ec_col = ec_col; a.ec_mean = ec_mean; a.ec = ec ? d->ec : 0;
   a.out = dW; a.out_dt = out_dt; a.ld_out = ld_dw; a.ws = (char*)ws;

@@ -79,6 +79,7 @@ struct EpiParams {
   // dW: ebar [B x M] f32 (row index j), xs [B x N] int32, u [N] f32
   const int32_t* colsum; const float* ec_row; const float* ec_mean; const float* vec;
   const float* ebar; const float* u;
+  const float* colstep;              // dW with per-token steps: the per-column step c [N] of Zq
   int64_t S, B;
   void* out; int64_t ld_out; int out_i32;
 };
@@ -265,8 +266,11 @@ __device__ __forceinline__ void k_step(const LoadMap& lm, const FragMap& fm, int
 // Stores go through a buffer descriptor over the tile's rows of the output
 // (rows past M fall outside it and are dropped by the range check); columns
 // past N are masked per column block.  Per-row byte offsets are uniform.
-enum { EPI_RAW = 0, EPI_DX = 1, EPI_DW = 2, EPI_DXA = 3 };   // EPI_DXA: dX added into the output
+// EPI_DXA: dX added into the output.  EPI_DWC: dW whose B operand is the per-column
+// requantized Zq of per-token steps, dequantized by its column step c[n].
+enum { EPI_RAW = 0, EPI_DX = 1, EPI_DW = 2, EPI_DXA = 3, EPI_DWC = 4 };
 __host__ __device__ constexpr bool is_dx(int epi) { return epi == EPI_DX || epi == EPI_DXA; }
+__host__ __device__ constexpr bool is_dw(int epi) { return epi == EPI_DW || epi == EPI_DWC; }
 constexpr int kMaxB = 8;   // examples whose dW correction terms the epilogue applies
 
 __device__ __forceinline__ int row_in_block(int r) { return (r >> 2) * 8 + (r & 3); }
@@ -288,7 +292,7 @@ __device__ __forceinline__ void epilogue(const GemmParams& g, const EpiParams& e
   const int lane_row = wm * 128 + (lane >> 5) * 4;                  // + i*32 + row_in_block(r)
 
   // per-column values of this lane, one per column block j
-  float colA[4], colV[4], colB[NB][4];
+  float colA[4], colV[4], colB[NB][4], colS[4];
   bool n_ok[4];
   uint32_t voff[4];
 #pragma unroll
@@ -296,14 +300,15 @@ __device__ __forceinline__ void epilogue(const GemmParams& g, const EpiParams& e
     const int64_t n = n0 + wn * 128 + j * 32 + (lane & 31);
     n_ok[j] = n < g.N;
     voff[j] = (uint32_t)(lane_row * ld4 + n * esz);
-    colA[j] = 0.f; colV[j] = 0.f;
+    colA[j] = 0.f; colV[j] = 0.f; colS[j] = 1.f;
 #pragma unroll
     for (int b = 0; b < NB; ++b) colB[b][j] = 0.f;
+    if constexpr (EPI == EPI_DWC) colS[j] = n_ok[j] ? ep.colstep[n] : 1.f;
     if (EC && n_ok[j]) {
       if constexpr (is_dx(EPI)) {
         colA[j] = (float)ep.colsum[n];                                   // r_W[n]
         if constexpr (!GATHER) colV[j] = ep.vec[(m0 / ep.S) * g.N + n];  // v_b[n], the tile's example
-      } else if constexpr (EPI == EPI_DW) {
+      } else if constexpr (is_dw(EPI)) {
         colA[j] = ep.u[n];
 #pragma unroll
         for (int b = 0; b < NB; ++b)
@@ -335,7 +340,7 @@ __device__ __forceinline__ void epilogue(const GemmParams& g, const EpiParams& e
       for (int rr = 0; rr < 4; ++rr) {
         const int lr = lane_row + i * 32 + rq * 8 + rr;
         if constexpr (EPI != EPI_RAW) f[rr] = rowf[lr];
-        if constexpr (EPI == EPI_DW && EC) {
+        if constexpr (is_dw(EPI) && EC) {
 #pragma unroll
           for (int b = 0; b < NB; ++b) eb[rr][b] = roweb[b * BM + lr];
         }
@@ -359,13 +364,14 @@ __device__ __forceinline__ void epilogue(const GemmParams& g, const EpiParams& e
           } else {
             float corr = 0.f;
             if constexpr (EC && is_dx(EPI)) corr = fmaf(f[rr].z, colA[j], f[rr].y * (GATHER ? gv[rr] : colV[j]));
-            if constexpr (EC && EPI == EPI_DW) {
+            if constexpr (EC && is_dw(EPI)) {
               float t = f[rr].y * colA[j];
 #pragma unroll
               for (int b = 0; b < NB; ++b) t = fmaf(eb[rr][b], colB[b][j], t);
               corr = t;
             }
-            float o = fmaf(f[rr].x, (float)v, -corr);
+            const float scale = EPI == EPI_DWC ? f[rr].x * colS[j] : f[rr].x;
+            float o = fmaf(scale, (float)v, -corr);
             if constexpr (EPI == EPI_DXA) o = old[rq][j][rr] + o;
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(o), ro, voff[j], soff, 0);
           }
@@ -439,14 +445,15 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmParams g, 
       }
       rowf[r] = f;
     }
-  } else if constexpr (EPI == EPI_DW) {
-    // x: Delta / s_w[j], y: 1 / s_w[j]; roweb[b * BM + r] = ebar[b][j] / s_w[j]
+  } else if constexpr (is_dw(EPI)) {
+    // x: Delta / s_w[j] (EPI_DWC: 1 / s_w[j], the step is per column), y: 1 / s_w[j];
+    // roweb[b * BM + r] = ebar[b][j] / s_w[j]
     for (int r = threadIdx.x; r < BM; r += kGemmThreads) {
       const int64_t j = m0 + r;
       float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
       if (j < g.M) {
         const float inv = ep.row_scale ? __fdiv_rn(1.f, ep.row_scale[j]) : 1.f;
-        f.x = ep.delta[0] * inv;
+        f.x = EPI == EPI_DWC ? inv : ep.delta[0] * inv;
         f.y = inv;
       }
       if (EC)
@@ -635,6 +642,135 @@ size_t gemv_part_bytes(int64_t K, int64_t N, int64_t nb) {
   return align_up((size_t)nbands * nb * N * 4, 256);
 }
 
+// ---------------------------------------- per-token steps: dW operand ----
+// With one step Delta_t per token the weight gradient's exact product is
+// Q^T diag(Delta) Xq, which no S8 GEMM applies after its accumulation over the
+// tokens.  The steps are folded into the input codes instead,
+// Z[t][n] = fl(Delta_t * Xq[t][n]), and Z is requantized per column with the
+// forward operands' absmax RTNE rule: c_n = fl(a_n / 127), inv_n = fl(127 / a_n),
+// Zq = clamp(rint(fl(Z * inv_n)), +-127), a_n = max_t |Z[t][n]| (a_n == 0: c = 1,
+// codes 0; a non-finite a_n or inv_n: codes 0).  dW's GEMM then runs on Zq and
+// its epilogue scales column n by c_n.
+// Both kernels: a block covers 512 columns (8 per lane) and a band of kZRows
+// rows, a quarter per wave, through buffer descriptors over the band; no load
+// or store addresses a row past the band.
+constexpr int kZRows = 256;
+constexpr int kZUnroll = 8;
+
+__device__ __forceinline__ void decode_i8x8(uint32_t lo, uint32_t hi, float v[8]) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    v[c] = (float)(int8_t)(lo >> (8 * c));
+    v[c + 4] = (float)(int8_t)(hi >> (8 * c));
+  }
+}
+
+// cbits[n] = max over the band of |fl(Delta_t * Xq[t][n])| as ordered fp32 bits
+// (NaN above every number), combined over the bands with an integer atomic max.
+__global__ __launch_bounds__(256) void zcol_amax_kernel(const int8_t* __restrict__ X, int64_t ld, int64_t T,
+                                                        int64_t N, const float* __restrict__ delta,
+                                                        uint32_t* __restrict__ cbits) {
+  __shared__ uint32_t red[4][512];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t n0 = (int64_t)blockIdx.x * 512 + lane * 8;
+  const int64_t t0 = (int64_t)blockIdx.y * kZRows;
+  const int rows = (int)min((int64_t)kZRows, T - t0);
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(X + t0 * ld), (short)0, (int)((uint32_t)rows * (uint32_t)ld), kRsrcWord3);
+  uint32_t m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int r0 = wave; r0 < rows && n0 < N; r0 += 4 * kZUnroll) {
+    uint2 u[kZUnroll];
+    float d[kZUnroll];
+#pragma unroll
+    for (int k = 0; k < kZUnroll; ++k) {
+      const int r = min(r0 + 4 * k, rows - 1);      // rows past the band repeat its last row, weighted 0
+      const auto w = __builtin_amdgcn_raw_buffer_load_b64(rsrc, (uint32_t)n0, (uint32_t)r * (uint32_t)ld, 0);
+      u[k] = make_uint2(w[0], w[1]);
+      d[k] = r0 + 4 * k < rows ? delta[t0 + r] : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < kZUnroll; ++k) {
+      float v[8];
+      decode_i8x8(u[k].x, u[k].y, v);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const uint32_t b = __float_as_uint(d[k] * v[c]) & 0x7FFFFFFFu;
+        m[c] = m[c] > b ? m[c] : b;
+      }
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < 8; ++c) red[wave][lane * 8 + c] = m[c];
+  __syncthreads();
+  for (int i = threadIdx.x; i < 512; i += 256) {
+    const int64_t n = (int64_t)blockIdx.x * 512 + i;
+    uint32_t a = red[0][i];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) a = a > red[w][i] ? a : red[w][i];
+    if (n < N && a) atomicMax(&cbits[n], a);
+  }
+}
+
+// Zq [T x ldz] from Xq and the column maxima; block row 0 also writes c[n].
+// Columns past N (up to the 8-column boundary) get code 0.
+__global__ __launch_bounds__(256) void zcol_quant_kernel(const int8_t* __restrict__ X, int64_t ld, int64_t T,
+                                                         int64_t N, const float* __restrict__ delta,
+                                                         const uint32_t* __restrict__ cbits, int8_t* __restrict__ Zq,
+                                                         int64_t ldz, float* __restrict__ cval) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t n0 = (int64_t)blockIdx.x * 512 + lane * 8;
+  if (n0 >= N) return;
+  const int64_t t0 = (int64_t)blockIdx.y * kZRows;
+  const int rows = (int)min((int64_t)kZRows, T - t0);
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(X + t0 * ld), (short)0, (int)((uint32_t)rows * (uint32_t)ld), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t zsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(Zq + t0 * ldz), (short)0, (int)((uint32_t)rows * (uint32_t)ldz), kRsrcWord3);
+  float inv[8];
+  bool zero[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const int64_t n = n0 + c;
+    const uint32_t ab = n < N ? cbits[n] : 0u;
+    const float a = __uint_as_float(ab);
+    const float cs = ab == 0 ? 1.f : __fdiv_rn(a, 127.f);
+    inv[c] = ab == 0 ? 0.f : __fdiv_rn(127.f, a);
+    zero[c] = !(ab < 0x7F800000u) || !(__float_as_uint(inv[c]) < 0x7F800000u) || n >= N;
+    if (blockIdx.y == 0 && wave == 0 && n < N) cval[n] = (ab > 0x7F800000u) ? a : cs;
+  }
+  for (int r0 = wave; r0 < rows; r0 += 4 * kZUnroll) {
+    uint2 u[kZUnroll];
+    float d[kZUnroll];
+#pragma unroll
+    for (int k = 0; k < kZUnroll; ++k) {
+      const int r = min(r0 + 4 * k, rows - 1);      // rows past the band repeat its last row, weighted 0
+      const auto w = __builtin_amdgcn_raw_buffer_load_b64(rsrc, (uint32_t)n0, (uint32_t)r * (uint32_t)ld, 0);
+      u[k] = make_uint2(w[0], w[1]);
+      d[k] = r0 + 4 * k < rows ? delta[t0 + r] : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < kZUnroll; ++k) {
+      float v[8];
+      decode_i8x8(u[k].x, u[k].y, v);
+      uint32_t q[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const float z = d[k] * v[c];
+        const float x = fminf(fmaxf(__builtin_rintf(z * inv[c]), -127.f), 127.f);
+        q[c] = zero[c] ? 0u : (uint32_t)(int32_t)x & 0xFFu;
+      }
+      const uint32_t lo = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
+      const uint32_t hi = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
+      const int r = r0 + 4 * k;
+      typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+      if (r < rows)
+        __builtin_amdgcn_raw_buffer_store_b64(v2u{lo, hi}, zsrc, (uint32_t)n0, (uint32_t)r * (uint32_t)ldz, 0);
+    }
+  }
+}
+
+size_t zq_ld(int64_t N) { return (size_t)((N + 15) / 16 * 16); }
+
 template <bool A_KMAJOR, int EPI, bool EC, int NB = 1>
 hipError_t run_gemm(const GemmParams& g, const EpiParams& ep, hipStream_t st) {
   GemmTiming& tm = gemm_timing();
@@ -670,10 +806,29 @@ size_t dx_workspace(int64_t T, int64_t D, int64_t d_in, int64_t S, int ec) {
   return kWsHeaderBytes + gemv_part_bytes(D, d_in, B) + align_up((size_t)B * d_in * 4, 256);
 }
 
-size_t dw_workspace(int64_t T, int64_t D, int64_t d_in, int64_t S, int ec) {
+// dW workspace: header | two-way EC: GEMV band partials, u [d_in] | per-token
+// steps: Zq [T x ldz], column maxima (bits) [d_in], column steps [d_in].
+struct DwLayout { size_t part, u, zq, cbits, cval, total; };
+
+DwLayout dw_layout(int64_t T, int64_t d_in, int ec, int per_token) {
+  DwLayout L{};
+  size_t off = kWsHeaderBytes;
+  if (ec == S3R_EC_TWO_WAY) {
+    L.part = off; off += gemv_part_bytes(T, d_in, 1);
+    L.u = off;    off += align_up((size_t)d_in * 4, 256);
+  }
+  if (per_token) {
+    L.zq = off;    off += align_up((size_t)T * zq_ld(d_in), 256);
+    L.cbits = off; off += align_up((size_t)d_in * 4, 256);
+    L.cval = off;  off += align_up((size_t)d_in * 4, 256);
+  }
+  L.total = off == kWsHeaderBytes ? 0 : off;
+  return L;
+}
+
+size_t dw_workspace(int64_t T, int64_t D, int64_t d_in, int64_t S, int ec, int per_token) {
   (void)D; (void)S;
-  if (ec != S3R_EC_TWO_WAY) return 0;
-  return kWsHeaderBytes + gemv_part_bytes(T, d_in, 1) + align_up((size_t)d_in * 4, 256);
+  return dw_layout(T, d_in, ec, per_token).total;
 }
 
 hipError_t launch_backward_dx(const DxArgs& a, hipStream_t st) {
@@ -706,6 +861,7 @@ hipError_t launch_backward_dx(const DxArgs& a, hipStream_t st) {
 
 hipError_t launch_backward_dw(const DwArgs& a, hipStream_t st) {
   const int64_t B = a.S > 0 ? a.T / a.S : 0;
+  const DwLayout L = dw_layout(a.T, a.d_in, a.ec, a.per_token);
   EpiParams ep{};
   ep.delta = a.delta; ep.per_token = 0; ep.row_scale = a.sw;
   ep.ec = (a.ec == S3R_EC_TWO_WAY) && a.out_dt == S3R_F32;
@@ -713,8 +869,8 @@ hipError_t launch_backward_dw(const DwArgs& a, hipStream_t st) {
   ep.S = a.S; ep.B = B;
   ep.out = a.out; ep.ld_out = a.ld_out; ep.out_i32 = a.out_dt == S3R_I32_RAW;
   if (ep.ec && a.D > 0 && a.d_in > 0) {
-    float* part = (float*)(a.ws + kWsHeaderBytes);
-    float* u = (float*)(a.ws + kWsHeaderBytes + gemv_part_bytes(a.T, a.d_in, 1));
+    float* part = (float*)(a.ws + L.part);
+    float* u = (float*)(a.ws + L.u);
     if (a.T > 0) {
       hipError_t e = run_gemv(a.X, a.ld_x, a.T, a.d_in, 1, 1, nullptr, a.ec_row, a.ec_mean, a.S, part, u, st);
       if (e != hipSuccess) return e;
@@ -724,15 +880,46 @@ hipError_t launch_backward_dw(const DwArgs& a, hipStream_t st) {
     }
     ep.u = u;
   }
-  // dW = Q^T Xq: A[m=j][k=t] = Q[t][j] (M-contiguous), B = Xq [T x d_in] (N-contiguous)
-  const GemmParams g = make_gemm(a.Q, a.ld_q, a.X, a.ld_x, a.D, a.d_in, a.T);
+  // B operand: the input codes, or (per-token steps) their per-column requantization Zq
+  const int8_t* Bop = a.X;
+  int64_t ldb = a.ld_x;
+  if (a.per_token && a.d_in > 0) {
+    uint32_t* cbits = (uint32_t*)(a.ws + L.cbits);
+    float* cval = (float*)(a.ws + L.cval);
+    int8_t* zq = (int8_t*)(a.ws + L.zq);
+    hipError_t e = fill_zero((float*)cbits, a.d_in, st);
+    if (e != hipSuccess) return e;
+    if (a.T > 0) {
+      dim3 grid((unsigned)((a.d_in + 511) / 512), (unsigned)((a.T + kZRows - 1) / kZRows));
+      hipLaunchKernelGGL(zcol_amax_kernel, grid, dim3(256), 0, st, a.X, a.ld_x, a.T, a.d_in, a.delta, cbits);
+      hipLaunchKernelGGL(zcol_quant_kernel, grid, dim3(256), 0, st, a.X, a.ld_x, a.T, a.d_in, a.delta, cbits, zq,
+                         (int64_t)zq_ld(a.d_in), cval);
+    } else {
+      hipLaunchKernelGGL(zcol_quant_kernel, dim3((unsigned)((a.d_in + 511) / 512), 1), dim3(256), 0, st, a.X,
+                         a.ld_x, a.T, a.d_in, a.delta, cbits, zq, (int64_t)zq_ld(a.d_in), cval);
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    Bop = zq;
+    ldb = (int64_t)zq_ld(a.d_in);
+    ep.colstep = cval;
+  }
+  // dW = Q^T B: A[m=j][k=t] = Q[t][j] (M-contiguous), B [T x d_in] (N-contiguous)
+  const GemmParams g = make_gemm(a.Q, a.ld_q, Bop, ldb, a.D, a.d_in, a.T);
   if (a.out_dt == S3R_I32_RAW) return run_gemm<false, EPI_RAW, false>(g, ep, st);
   hipError_t e;
-  if (!ep.ec) e = run_gemm<false, EPI_DW, false>(g, ep, st);
-  else if (B <= 1) e = run_gemm<false, EPI_DW, true, 1>(g, ep, st);
-  else if (B <= 2) e = run_gemm<false, EPI_DW, true, 2>(g, ep, st);
-  else if (B <= 4) e = run_gemm<false, EPI_DW, true, 4>(g, ep, st);
-  else e = run_gemm<false, EPI_DW, true, kMaxB>(g, ep, st);
+  if (a.per_token) {
+    if (!ep.ec) e = run_gemm<false, EPI_DWC, false>(g, ep, st);
+    else if (B <= 1) e = run_gemm<false, EPI_DWC, true, 1>(g, ep, st);
+    else if (B <= 2) e = run_gemm<false, EPI_DWC, true, 2>(g, ep, st);
+    else if (B <= 4) e = run_gemm<false, EPI_DWC, true, 4>(g, ep, st);
+    else e = run_gemm<false, EPI_DWC, true, kMaxB>(g, ep, st);
+  } else {
+    if (!ep.ec) e = run_gemm<false, EPI_DW, false>(g, ep, st);
+    else if (B <= 1) e = run_gemm<false, EPI_DW, true, 1>(g, ep, st);
+    else if (B <= 2) e = run_gemm<false, EPI_DW, true, 2>(g, ep, st);
+    else if (B <= 4) e = run_gemm<false, EPI_DW, true, 4>(g, ep, st);
+    else e = run_gemm<false, EPI_DW, true, kMaxB>(g, ep, st);
+  }
   if (e != hipSuccess || !ep.ec || B <= 8 || a.D == 0 || a.d_in == 0) return e;
   hipLaunchKernelGGL(dw_rank_update_kernel, dim3((unsigned)((a.d_in + 255) / 256), (unsigned)a.D), dim3(256), 0, st,
                      (float*)a.out, a.ld_out, a.D, a.d_in, B, a.ec_col, a.xs, a.sw);

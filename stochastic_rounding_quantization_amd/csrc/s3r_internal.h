@@ -99,7 +99,7 @@ struct DxArgs {
   char* ws;
 };
 struct DwArgs {
-  const int8_t* Q; int64_t ld_q; const float* delta;
+  const int8_t* Q; int64_t ld_q; const float* delta; int per_token;
   const int8_t* X; int64_t ld_x;
   int64_t T, D, d_in, S;
   const float* sw; const int32_t* xs;
@@ -112,7 +112,7 @@ struct GemmTiming { hipEvent_t start = nullptr, stop = nullptr; };
 GemmTiming& gemm_timing();
 
 size_t dx_workspace(int64_t T, int64_t D, int64_t d_in, int64_t S, int ec);
-size_t dw_workspace(int64_t T, int64_t D, int64_t d_in, int64_t S, int ec);
+size_t dw_workspace(int64_t T, int64_t D, int64_t d_in, int64_t S, int ec, int per_token);
 hipError_t launch_backward_dx(const DxArgs& a, hipStream_t st);
 hipError_t launch_backward_dw(const DwArgs& a, hipStream_t st);
 

@@ -39,7 +39,7 @@ def gpu_linear(inp: dict, *, mode, ec, scale=s3r.PER_TENSOR, seed=0, layer_id=0,
     q = s3r.quantize(G, mode=mode, ec=ec, scale=scale, row_scale=fx.delta, col_scale=fw.delta, seed=seed,
                      layer_id=layer_id, rows_per_example=S)
     dX = s3r.backward_dx(q, fw.Q, s_x=fx.delta, r_W=fw.code_colsum[0])
-    dW = s3r.backward_dw(q, fx.Q, s_w=fw.delta, xs_b=fx.code_colsum) if dw else None
+    dW = s3r.backward_dw(q, fx.Q, s_w=fw.delta, xs_b=fx.code_colsum) if dw else None  # any step granularity
     torch.cuda.synchronize()
     return {"fx": fx, "fw": fw, "q": q, "dX": dX, "dW": dW}
 

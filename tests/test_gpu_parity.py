@@ -235,8 +235,7 @@ def test_deterministic():
 # -------------------------------------------------------- end to end ----
 
 def _check_linear(inp, S, mode, ec, scale=s3r.PER_TENSOR, dx_rows=None, dw_rows=None, seed=0, layer=0):
-    gpu = gpu_linear(inp, mode=mode, ec=ec, scale=scale, seed=seed, layer_id=layer, rows_per_example=S,
-                     dw=(scale == s3r.PER_TENSOR))
+    gpu = gpu_linear(inp, mode=mode, ec=ec, scale=scale, seed=seed, layer_id=layer, rows_per_example=S)
     tag = f"mode={mode} ec={ec} scale={scale}"
     fx, fw = pipeline.forward_operands(inp["X"], inp["W"], inp["dtype"], S)
     # forward-operand prep (a0): codes, row steps, column sums bit-exact
@@ -258,11 +257,10 @@ def _check_linear(inp, S, mode, ec, scale=s3r.PER_TENSOR, dx_rows=None, dw_rows=
     dX = dX if dx_rows is None else dX[dx_rows]
     e = rel_err(dX, ref["dX"])
     assert e <= TOL, f"{tag}: dX rel err {e:.3g}"
-    if scale == s3r.PER_TENSOR:
-        dW = host(gpu["dW"])
-        dW = dW if dw_rows is None else dW[dw_rows]
-        e = rel_err(dW, ref["dW"])
-        assert e <= TOL, f"{tag}: dW rel err {e:.3g}"
+    dW = host(gpu["dW"])
+    dW = dW if dw_rows is None else dW[dw_rows]
+    e = rel_err(dW, ref["dW"])
+    assert e <= TOL, f"{tag}: dW rel err {e:.3g}"
     return gpu, ref
 
 
@@ -344,3 +342,48 @@ def test_gate_projection_ffn_block_size_sampled():
     inp = inputs.make_linear_inputs(w)
     _check_linear(inp, 2048, s3r.S3R, s3r.EC_TWO_WAY, dx_rows=_sample_rows(w.tokens, 6, 5),
                   dw_rows=_sample_rows(w.d_out, 6, 6), layer=1)
+
+
+# --------------------------------------------- per-token steps and dW ----
+
+@pytest.mark.parametrize("T,D,d_in,S", [(300, 200, 77, 100), (512, 96, 1100, 256), (40, 33, 8, 40)])
+def test_per_token_dw_requantized_inputs(T, D, d_in, S):
+    # dW with one step per token: the inputs Xq are folded with the steps and requantized per
+    # column (ragged against the 256-row bands and the 8-column lanes); the raw accumulators
+    # Q^T Zq are bit-exact and the dequantized, corrected dW is within the tolerance
+    w = inputs.WORKLOADS["down-4096x11008x4096-bf16"].scaled(T, d_in, D, rows_per_example=S)
+    inp = inputs.make_linear_inputs(w)
+    for ec in (s3r.EC_NONE, s3r.EC_TWO_WAY):
+        gpu, ref = _check_linear(inp, S, s3r.S3R, ec, scale=s3r.PER_TOKEN, seed=T, layer=3)
+        q = gpu["q"]
+        raw = torch.full((D, d_in), -7, dtype=torch.int32, device=DEV)
+        ws = torch.zeros(max(s3r.s3r_backward_workspace(q.desc, d_in), 1), dtype=torch.uint8, device=DEV)
+        s3r.s3r_backward_dw(q.desc, q.Q, q.delta, gpu["fx"].Q, None, None, None, None, None, raw, ws)
+        torch.cuda.synchronize()
+        Zq, _ = backward.requantize_columns(ref["fx"]["Q"], ref["q"]["delta"])
+        np.testing.assert_array_equal(host(raw), backward.int_matmul(np.ascontiguousarray(ref["q"]["Q"].T), Zq))
+
+
+def test_per_token_dw_flagged_token_poisons_steps():
+    # a non-finite gradient row gives that token a non-finite step: every column step of Z is then
+    # NaN and the codes are 0, so dW is NaN throughout, as in the oracle
+    T, D, d_in = 64, 48, 40
+    rng = np.random.default_rng(3)
+    G = (1e-3 * rng.standard_normal((T, D))).astype(np.float32)
+    G[5, 7] = np.inf
+    Xq = _rand_i8(rng, (T, d_in))
+    q = s3r.quantize(to_dev(G, "f32"), mode=s3r.S3R, scale=s3r.PER_TOKEN, seed=2, rows_per_example=T)
+    dW = s3r.backward_dw(q, _padded_i8(Xq))
+    torch.cuda.synchronize()
+    ref = oq.quantize(G, "f32", mode=s3r.S3R, scale=s3r.PER_TOKEN, seed=2, rows_per_example=T)
+    np.testing.assert_array_equal(host(q.delta).view(np.uint32), ref["delta"].view(np.uint32))
+    exp = backward.backward_dw_per_token(ref["Q"], ref["delta"], Xq, np.ones(D, np.float32))
+    assert np.isnan(exp).all() and np.isnan(host(dW)).all()
+
+
+def test_down_8192x14336x4096_bf16_per_token_sampled():
+    # the headline shape with per-token steps for both products (two-way correction), rows sampled
+    w = inputs.WORKLOADS["down-8192x14336x4096-bf16"]
+    inp = inputs.make_linear_inputs(w)
+    _check_linear(inp, w.rows_per_example, s3r.S3R, s3r.EC_TWO_WAY, scale=s3r.PER_TOKEN,
+                  dx_rows=_sample_rows(w.tokens, 8, 7), dw_rows=_sample_rows(w.d_out, 8, 8))

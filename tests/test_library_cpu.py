@@ -97,7 +97,8 @@ def test_backward_argument_errors(L):
     ecd = s3r.qdesc(64, 96, 32, s3r.S3R, s3r.EC_DX_ONLY)
     assert dx(d=ecd) == -1                   # correction inputs missing
     pt = s3r.qdesc(64, 96, 32, s3r.S3R, s3r.EC_NONE, s3r.PER_TOKEN)
-    assert dw(d=pt) == -2                    # dW needs a per-tensor step
+    assert dw(d=pt) == -3                    # per-token dW requantizes the inputs in the workspace
+    assert s3r.s3r_backward_workspace(pt, 128) >= 64 * 128 + 2 * 128 * 4
     assert s3r.s3r_backward_workspace(s3r.qdesc(64, 96, 32, s3r.S3R, s3r.EC_TWO_WAY), 128) > 0
     assert s3r.s3r_backward_workspace(d, 128) == 0
 
