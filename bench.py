@@ -6,9 +6,10 @@ step = the whole backward on one batch of synthetic input:
   down projection: quantize G_out (fold, per-tensor step, S3R thresholds,
     codes, S3R-EC statistics) -> dH (correction GEMV + INT8 GEMM + epilogue)
     -> dW_down (correction GEMV + INT8 GEMM + epilogue);
-  SwiGLU glue: dH, A_gate, A_up -> G_gate, G_up (bf16);
-  gate and up projections: the same three calls on G_gate and G_up, their dX
-    added into one dX.
+  SwiGLU glue: dH, A_gate, A_up -> G_gate, G_up (bf16), and in the same pass
+    the per-tensor amax of each as its projection's quantizer folds it;
+  gate and up projections: quantize with that amax (one read of G), dX
+    (added into one dX) and dW.
 The forward-operand prep (RTNE codes of X, H and the three weights with their
 scales and column sums) is forward-pass work and runs once before timing.
 ``--workload down-8192x14336x4096-bf16`` (or another linear workload) times one
@@ -246,6 +247,8 @@ def run_block(args, dev, torch, inputs, s3r):
                         em=torch.empty(B, dtype=torch.float32, device=dev) if ec else None,
                         flags=torch.zeros(1, dtype=torch.int32, device=dev), din=din, fx=fxx, fw=fww)
     ws_q = torch.zeros(max(s3r.s3r_quantize_workspace(st[n]["desc"]) for n in st), dtype=torch.uint8, device=dev)
+    ws_g = torch.zeros(s3r.s3r_swiglu_amax_workspace(T, F), dtype=torch.uint8, device=dev)
+    amax = torch.zeros(2, dtype=torch.int32, device=dev)     # gate, up: max|G'| bits from the glue
     ws_b = torch.zeros(max(max(s3r.s3r_backward_workspace(st[n]["desc"], st[n]["din"]) for n in st), 1),
                        dtype=torch.uint8, device=dev)
     dH = torch.empty(T, F, dtype=torch.float32, device=dev)
@@ -264,8 +267,13 @@ def run_block(args, dev, torch, inputs, s3r):
         p = st[name]
         if ev:
             ev[f"quantize_{name}"][0].record()
-        s3r.s3r_quantize(p["desc"], G_in[name], p["fx"].delta, p["fw"].delta, p["Q"], p["delta"], None, p["er"],
-                         p["ec"], p["em"], p["flags"], ws_q)
+        if name == "down":
+            s3r.s3r_quantize(p["desc"], G_in[name], p["fx"].delta, p["fw"].delta, p["Q"], p["delta"], None, p["er"],
+                             p["ec"], p["em"], p["flags"], ws_q)
+        else:   # the glue already found the step's amax: one read of G
+            k = 0 if name == "gate" else 1
+            s3r.s3r_quantize_with_amax(p["desc"], G_in[name], p["fx"].delta, p["fw"].delta, amax[k:k + 1], p["Q"],
+                                       p["delta"], p["er"], p["ec"], p["em"], p["flags"], ws_q)
         if ev:
             ev[f"quantize_{name}"][1].record()
             s3r.s3r_time_next_gemm(*ev[f"dx_{name}"])
@@ -282,7 +290,8 @@ def run_block(args, dev, torch, inputs, s3r):
         linear("down", ev)
         if ev:
             ev["glue"][0].record()
-        s3r.s3r_swiglu_backward(dH, dv["A_gate"], dv["A_up"], Gg, Gu)
+        s3r.s3r_swiglu_backward_amax(dH, dv["A_gate"], dv["A_up"], Gg, Gu, fx.delta, fwg.delta, fwu.delta, amax,
+                                     ws_g)
         if ev:
             ev["glue"][1].record()
         linear("gate", ev)
@@ -306,10 +315,12 @@ def run_block(args, dev, torch, inputs, s3r):
         "dtype": "i8", "data": "synthetic",
         "config": {"workload": b.name, "tokens": T, "d_model": M, "d_ff": F, "rows_per_example": S,
                    "mode": args.mode, "step_scale": "per-tensor", "g_dtype": "bf16",
-                   "stages": "down (quantize, dX=dH, dW), SwiGLU glue, gate and up (quantize, dX added, dW)"},
+                   "stages": "down (quantize, dX=dH, dW), SwiGLU glue with the gate/up amax, gate and up "
+                             "(quantize with that amax, dX added, dW)"},
         "frac_of_int8_peak": round(value / PEAK_INT8_TOPS, 4),
         "quantizer": {"us": round(q_us, 2), "GB_s": round(q_gbs, 1), "frac_of_hbm_peak": round(q_gbs / PEAK_HBM_GBS, 4),
-                      "algorithmic_bytes": q_bytes, "calls": 3},
+                      "algorithmic_bytes": q_bytes, "calls": 3,
+                      "note": "gate and up calls take their per-tensor amax from the glue pass (one read of G)"},
         "kernels_us": {**{f"quantize_{n}": round(tl.avg_us(f"quantize_{n}"), 2) for n in st},
                        **{f"gemm_{k}": round(v, 2) for k, v in gemm_us.items()},
                        "glue": round(tl.avg_us("glue"), 2), "step_events": round(tl.avg_us("step"), 2)},

@@ -141,6 +141,26 @@ int s3r_quantize(const s3r_qdesc* desc,
                  uint32_t* flags,
                  void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* s3r_quantize_with_amax: s3r_quantize for a per-tensor step whose amax is
+ * already on the device, so G is read once.  amax_bits [1] (device, read
+ * only) holds max_{t,j} |G'[t,j]| as the bit pattern of a non-negative fp32
+ * (a NaN anywhere gives a NaN pattern, which orders above every number), for
+ * example as written by s3r_swiglu_backward_amax.  With that value the codes,
+ * step, flags and statistics are exactly those s3r_quantize computes.  Same
+ * arguments, layouts and workspace as s3r_quantize except: desc->scale must be
+ * PER_TENSOR (else S3R_ERR_UNSUPPORTED) and there is no code_colsum output.
+ * An amax that does not match G's actual maximum is the caller's error: codes
+ * are still clamped to [-127, 127].
+ */
+int s3r_quantize_with_amax(const s3r_qdesc* desc,
+                           const void* G, int32_t g_dtype, int64_t ld_g,
+                           const float* row_scale, const float* col_scale,
+                           const uint32_t* amax_bits,
+                           int8_t* Q, int64_t ld_q, float* delta,
+                           float* ec_row, float* ec_col, float* ec_mean,
+                           uint32_t* flags,
+                           void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* ---- backward GEMMs ----------------------------------------------------
  * Common: Q [T x D] int8 codes with ld_q, delta as written by s3r_quantize
  * (desc->scale selects [1] or [T]).  INT8 GEMMs on the MFMA units with int32
@@ -219,6 +239,29 @@ size_t s3r_backward_workspace(const s3r_qdesc* desc, int64_t d_in);
 int s3r_swiglu_backward(int64_t T, int64_t F, const float* dH, int64_t ld_dh,
                         const uint16_t* A_gate, const uint16_t* A_up, int64_t ld_a,
                         uint16_t* G_gate, uint16_t* G_up, int64_t ld_g, hipStream_t stream);
+
+/* s3r_swiglu_backward_amax: s3r_swiglu_backward (same arguments, arithmetic
+ * and results) and, from the same pass, the per-tensor amax that the gate and
+ * up projections' quantizers need, so that s3r_quantize_with_amax reads each
+ * result once.  S3R page, "Quantized Backpropagation with Stochastic Rounding"
+ * (the step of the folded gradient, Delta = max|G'|/127).
+ *   row_scale [T] f32 (s_x of the block input) or NULL (= 1);
+ *   col_scale_gate, col_scale_up [F] f32 (s_w of W_gate, W_up) or NULL.
+ *   amax_bits [2] device uint32, written:
+ *     [0] = max |fl(fl(G_gate[t,j] * s_x[t]) * s_w_gate[j])|,
+ *     [1] = the same for G_up with s_w_up,
+ *   over the bf16 results, as ordered fp32 bit patterns (NaN above every
+ *   number; 0 for an empty tensor) -- the values s3r_quantize would find for
+ *   G_gate and G_up with those scales.
+ *   ws: s3r_swiglu_amax_workspace(T, F) bytes, 256-byte aligned (per-block
+ *   partial maxima after the common 64 KiB header).
+ */
+size_t s3r_swiglu_amax_workspace(int64_t T, int64_t F);
+int s3r_swiglu_backward_amax(int64_t T, int64_t F, const float* dH, int64_t ld_dh,
+                             const uint16_t* A_gate, const uint16_t* A_up, int64_t ld_a,
+                             uint16_t* G_gate, uint16_t* G_up, int64_t ld_g,
+                             const float* row_scale, const float* col_scale_gate, const float* col_scale_up,
+                             uint32_t* amax_bits, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ---- measurement aid --------------------------------------------------
  * s3r_time_next_gemm: record `start` immediately before and `stop` immediately

@@ -88,6 +88,43 @@ int s3r_quantize(const s3r_qdesc* d, const void* G, int32_t g_dtype, int64_t ld_
   return finish(launch_quantize(a, stream));
 }
 
+int s3r_quantize_with_amax(const s3r_qdesc* d, const void* G, int32_t g_dtype, int64_t ld_g, const float* row_scale,
+                           const float* col_scale, const uint32_t* amax_bits, int8_t* Q, int64_t ld_q, float* delta,
+                           float* ec_row, float* ec_col, float* ec_mean, uint32_t* flags, void* ws, size_t ws_bytes,
+                           hipStream_t stream) {
+  int rc = check_desc(d);
+  if (rc) return rc;
+  if (d->scale != S3R_PER_TENSOR) return S3R_ERR_UNSUPPORTED;
+  if (!amax_bits) return S3R_ERR_INVALID_ARG;
+  if (d->rows == 0 || d->cols == 0)   // nothing to quantize: the step of an empty tensor is 1
+    return s3r_quantize(d, G, g_dtype, ld_g, row_scale, col_scale, Q, ld_q, delta, nullptr, ec_row, ec_col, ec_mean,
+                        flags, ws, ws_bytes, stream);
+  if (g_dtype != S3R_F32 && g_dtype != S3R_BF16) return S3R_ERR_UNSUPPORTED;
+  if (d->ec != S3R_EC_NONE && d->mode != S3R_S3R) return S3R_ERR_UNSUPPORTED;
+  const int64_t T = d->rows, D = d->cols;
+  const int64_t B = T / d->rows_per_example;
+  if (!delta || !G || !Q) return S3R_ERR_INVALID_ARG;
+  if (ld_g < D || ld_q < D) return S3R_ERR_INVALID_ARG;
+  if (d->ec != S3R_EC_NONE) {
+    if (!ec_row || (B * D > 0 && !ec_col) || (B > 0 && !ec_mean)) return S3R_ERR_INVALID_ARG;
+  } else if (ec_row || ec_col || ec_mean) {
+    return S3R_ERR_INVALID_ARG;
+  }
+  const size_t need = s3r_quantize_workspace(d);
+  if (ws_bytes < need) return S3R_ERR_WORKSPACE;
+  if (need > 0 && (!ws || ((uintptr_t)ws & 255u))) return S3R_ERR_INVALID_ARG;
+  if ((rc = check_arch())) return rc;
+  QuantArgs a{};
+  a.G = G; a.g_dtype = g_dtype; a.ld_g = ld_g; a.sx = row_scale; a.sw = col_scale;
+  a.Q = Q; a.ld_q = ld_q; a.delta = delta; a.code_colsum = nullptr;
+  a.ec_row = ec_row; a.ec_col = ec_col; a.ec_mean = ec_mean; a.flags = flags;
+  a.T = T; a.D = D; a.S = d->rows_per_example;
+  a.mode = d->mode; a.ec = d->ec; a.scale = d->scale; a.layer = d->layer_id; a.seed = d->seed;
+  a.ws = (char*)ws;
+  a.amax_in = amax_bits;
+  return finish(launch_quantize(a, stream));
+}
+
 size_t s3r_backward_workspace(const s3r_qdesc* d, int64_t d_in) {
   if (check_desc(d) != S3R_OK || d_in < 0) return 0;
   const size_t a = dx_workspace(d->rows, d->cols, d_in, d->rows_per_example, d->ec);
@@ -167,6 +204,26 @@ int s3r_swiglu_backward(int64_t T, int64_t F, const float* dH, int64_t ld_dh, co
   int rc;
   if ((rc = check_arch())) return rc;
   return finish(launch_swiglu_backward(T, F, dH, ld_dh, A_gate, A_up, ld_a, G_gate, G_up, ld_g, stream));
+}
+
+size_t s3r_swiglu_amax_workspace(int64_t T, int64_t F) {
+  if (T < 0 || F < 0) return 0;
+  return swiglu_amax_workspace(T, F);
+}
+
+int s3r_swiglu_backward_amax(int64_t T, int64_t F, const float* dH, int64_t ld_dh, const uint16_t* A_gate,
+                             const uint16_t* A_up, int64_t ld_a, uint16_t* G_gate, uint16_t* G_up, int64_t ld_g,
+                             const float* row_scale, const float* col_scale_gate, const float* col_scale_up,
+                             uint32_t* amax_bits, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (T < 0 || F < 0 || ld_dh < F || ld_a < F || ld_g < F) return S3R_ERR_INVALID_ARG;
+  if (T > 0 && F > 0 && (!dH || !A_gate || !A_up || !G_gate || !G_up)) return S3R_ERR_INVALID_ARG;
+  if (!amax_bits) return S3R_ERR_INVALID_ARG;
+  if (ws_bytes < swiglu_amax_workspace(T, F)) return S3R_ERR_WORKSPACE;
+  if (!ws || ((uintptr_t)ws & 255u)) return S3R_ERR_INVALID_ARG;
+  int rc;
+  if ((rc = check_arch())) return rc;
+  return finish(launch_swiglu_backward_amax(T, F, dH, ld_dh, A_gate, A_up, ld_a, G_gate, G_up, ld_g, row_scale,
+                                            col_scale_gate, col_scale_up, amax_bits, (char*)ws, stream));
 }
 
 int s3r_time_next_gemm(hipEvent_t start, hipEvent_t stop) {

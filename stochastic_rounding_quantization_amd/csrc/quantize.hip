@@ -867,7 +867,8 @@ template <typename TIn, bool VEC, int MODE, bool EC, bool PT, bool COLSUM>
 void launch_q(const QuantArgs& a, const WsLayout& L, const QuantTile& p, dim3 grid, hipStream_t st) {
   hipLaunchKernelGGL((quantize_kernel<TIn, VEC, MODE, EC, PT, COLSUM>), grid, dim3(kThreads), 0, st, p,
                      (const TIn*)a.G, a.sx, a.sw, a.Q, a.delta, a.flags,
-                     (const uint32_t*)(a.ws + L.amax_part), kAmaxBlocks, (const uint32_t*)(a.ws + L.amax_rows),
+                     a.amax_in ? a.amax_in : (const uint32_t*)(a.ws + L.amax_part), a.amax_in ? 1 : kAmaxBlocks,
+                     (const uint32_t*)(a.ws + L.amax_rows),
                      (float*)(a.ws + L.row_part), (float*)(a.ws + L.col_part), (int32_t*)(a.ws + L.colq_part),
                      (uint32_t*)(a.ws + L.counter));
 }
@@ -899,8 +900,9 @@ template <typename TIn, bool VEC>
 void run_quantize(const QuantArgs& a, const WsLayout& L, hipStream_t st) {
   const TIn* G = (const TIn*)a.G;
   if (a.scale == S3R_PER_TENSOR) {
-    hipLaunchKernelGGL((amax_tensor_kernel<TIn, VEC>), dim3(kAmaxBlocks), dim3(kThreads), 0, st, G, a.ld_g,
-                       a.T, a.D, a.sx, a.sw, (uint32_t*)(a.ws + L.amax_part));
+    if (!a.amax_in)   // otherwise the step comes from the caller's amax: G is read once
+      hipLaunchKernelGGL((amax_tensor_kernel<TIn, VEC>), dim3(kAmaxBlocks), dim3(kThreads), 0, st, G, a.ld_g,
+                         a.T, a.D, a.sx, a.sw, (uint32_t*)(a.ws + L.amax_part));
   } else {
     const unsigned nb = (unsigned)((a.T + kThreads / kWave - 1) / (kThreads / kWave));
     hipLaunchKernelGGL((amax_rows_kernel<TIn, VEC>), dim3(nb), dim3(kThreads), 0, st, G, a.ld_g, a.T, a.D,
@@ -1015,7 +1017,7 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t st) {
   const size_t es = a.g_dtype == S3R_BF16 ? 2 : 4;
   const bool vec = aligned(a.G, 16) && (a.ld_g * (int64_t)es) % 16 == 0 && aligned(a.Q, 8) && a.ld_q % 8 == 0 &&
                    (a.sw == nullptr || aligned(a.sw, 16));
-  if (vec && !resident_disabled()) {
+  if (vec && !a.amax_in && !resident_disabled()) {
     const int R = resident_rows(a, resident_capacity());
     if (R > 0) return run_resident(a, L, R, st);
   }

@@ -84,6 +84,7 @@ struct QuantArgs {
   int mode, ec, scale;
   uint32_t layer; uint64_t seed;
   char* ws;
+  const uint32_t* amax_in;   // per-tensor amax bits already known on the device, or null
 };
 size_t quant_workspace(int64_t T, int64_t D, int64_t S, int ec, int scale, bool colsum);
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t st);
@@ -120,6 +121,12 @@ hipError_t launch_backward_dw(const DwArgs& a, hipStream_t st);
 hipError_t launch_swiglu_backward(int64_t T, int64_t F, const float* dH, int64_t ld_dh, const uint16_t* Ag,
                                   const uint16_t* Au, int64_t ld_a, uint16_t* Gg, uint16_t* Gu, int64_t ld_g,
                                   hipStream_t st);
+
+size_t swiglu_amax_workspace(int64_t T, int64_t F);
+hipError_t launch_swiglu_backward_amax(int64_t T, int64_t F, const float* dH, int64_t ld_dh, const uint16_t* Ag,
+                                       const uint16_t* Au, int64_t ld_a, uint16_t* Gg, uint16_t* Gu, int64_t ld_g,
+                                       const float* sx, const float* swg, const float* swu, uint32_t* amax_bits,
+                                       char* ws, hipStream_t st);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

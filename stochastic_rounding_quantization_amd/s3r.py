@@ -27,9 +27,9 @@ EC_NONE, EC_DX_ONLY, EC_TWO_WAY = 0, 1, 2
 PER_TENSOR, PER_TOKEN = 0, 1
 FLAG_NONFINITE, FLAG_TINY_STEP, FLAG_SYNC_TIMEOUT = 1, 2, 4
 
-EXPORTED = ["s3r_quantize_workspace", "s3r_quantize", "s3r_backward_dx", "s3r_backward_dw",
-            "s3r_backward_workspace", "s3r_swiglu_backward", "s3r_time_next_gemm", "s3r_status_string",
-            "s3r_version"]
+EXPORTED = ["s3r_quantize_workspace", "s3r_quantize", "s3r_quantize_with_amax", "s3r_backward_dx",
+            "s3r_backward_dw", "s3r_backward_workspace", "s3r_swiglu_backward", "s3r_swiglu_amax_workspace",
+            "s3r_swiglu_backward_amax", "s3r_time_next_gemm", "s3r_status_string", "s3r_version"]
 
 
 class S3RError(RuntimeError):
@@ -66,6 +66,8 @@ def lib() -> ctypes.CDLL:
     L.s3r_quantize_workspace.restype = SZ
     L.s3r_quantize.argtypes = [DP, P, I32, I64, P, P, P, I64, P, P, P, P, P, P, P, SZ, P]
     L.s3r_quantize.restype = ctypes.c_int
+    L.s3r_quantize_with_amax.argtypes = [DP, P, I32, I64, P, P, P, P, I64, P, P, P, P, P, P, SZ, P]
+    L.s3r_quantize_with_amax.restype = ctypes.c_int
     L.s3r_backward_dx.argtypes = [DP, P, I64, P, P, I64, I64, P, P, P, P, P, P, I32, I64, P, SZ, P]
     L.s3r_backward_dx.restype = ctypes.c_int
     L.s3r_backward_dw.argtypes = [DP, P, I64, P, P, I64, I64, P, P, P, P, P, P, I32, I64, P, SZ, P]
@@ -74,6 +76,10 @@ def lib() -> ctypes.CDLL:
     L.s3r_backward_workspace.restype = SZ
     L.s3r_swiglu_backward.argtypes = [I64, I64, P, I64, P, P, I64, P, P, I64, P]
     L.s3r_swiglu_backward.restype = ctypes.c_int
+    L.s3r_swiglu_amax_workspace.argtypes = [I64, I64]
+    L.s3r_swiglu_amax_workspace.restype = SZ
+    L.s3r_swiglu_backward_amax.argtypes = [I64, I64, P, I64, P, P, I64, P, P, I64, P, P, P, P, P, SZ, P]
+    L.s3r_swiglu_backward_amax.restype = ctypes.c_int
     L.s3r_time_next_gemm.argtypes = [P, P]
     L.s3r_time_next_gemm.restype = ctypes.c_int
     L.s3r_status_string.argtypes = [ctypes.c_int]
@@ -144,6 +150,18 @@ def s3r_quantize(desc: QDesc, G, row_scale, col_scale, Q, delta, code_colsum=Non
     _check("s3r_quantize", rc)
 
 
+def s3r_quantize_with_amax(desc: QDesc, G, row_scale, col_scale, amax_bits, Q, delta, ec_row=None, ec_col=None,
+                           ec_mean=None, flags=None, ws=None, stream=None, *, rc_only=False):
+    rc = lib().s3r_quantize_with_amax(ctypes.byref(desc), _ptr(G), _gdtype(G) if G is not None else S3R_F32,
+                                      _ld(G, desc.cols), _ptr(row_scale), _ptr(col_scale), _ptr(amax_bits), _ptr(Q),
+                                      _ld(Q, desc.cols), _ptr(delta), _ptr(ec_row), _ptr(ec_col), _ptr(ec_mean),
+                                      _ptr(flags), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                                      _stream(stream))
+    if rc_only:
+        return rc
+    _check("s3r_quantize_with_amax", rc)
+
+
 def s3r_backward_workspace(desc: QDesc, d_in: int) -> int:
     return lib().s3r_backward_workspace(ctypes.byref(desc), d_in)
 
@@ -182,6 +200,25 @@ def s3r_swiglu_backward(dH, A_gate, A_up, G_gate, G_up, stream=None, *, rc_only=
     if rc_only:
         return rc
     _check("s3r_swiglu_backward", rc)
+
+
+def s3r_swiglu_amax_workspace(T: int, F: int) -> int:
+    return lib().s3r_swiglu_amax_workspace(T, F)
+
+
+def s3r_swiglu_backward_amax(dH, A_gate, A_up, G_gate, G_up, row_scale, col_scale_gate, col_scale_up, amax_bits,
+                             ws, stream=None, *, rc_only=False):
+    """Glue and the gate / up amax (uint32 [2] device tensor amax_bits) in one pass."""
+    T, F = dH.shape
+    if A_up.stride() != A_gate.stride() or G_up.stride() != G_gate.stride():
+        raise ValueError("A_gate / A_up and G_gate / G_up must share their layouts")
+    rc = lib().s3r_swiglu_backward_amax(T, F, _ptr(dH), _ld(dH, F), _ptr(A_gate), _ptr(A_up), _ld(A_gate, F),
+                                        _ptr(G_gate), _ptr(G_up), _ld(G_gate, F), _ptr(row_scale),
+                                        _ptr(col_scale_gate), _ptr(col_scale_up), _ptr(amax_bits), _ptr(ws),
+                                        0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+    if rc_only:
+        return rc
+    _check("s3r_swiglu_backward_amax", rc)
 
 
 def swiglu_backward(dH, A_gate, A_up, stream=None):

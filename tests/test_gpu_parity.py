@@ -387,3 +387,38 @@ def test_down_8192x14336x4096_bf16_per_token_sampled():
     inp = inputs.make_linear_inputs(w)
     _check_linear(inp, w.rows_per_example, s3r.S3R, s3r.EC_TWO_WAY, scale=s3r.PER_TOKEN,
                   dx_rows=_sample_rows(w.tokens, 8, 7), dw_rows=_sample_rows(w.d_out, 8, 8))
+
+
+# ------------------------------------------------ quantize with a known amax ----
+
+@pytest.mark.parametrize("mode,ec", [(s3r.S3R, s3r.EC_TWO_WAY), (s3r.SR, s3r.EC_NONE), (s3r.RTNE, s3r.EC_NONE)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_quantize_with_amax_equals_quantize(mode, ec, dtype):
+    # with the amax supplied (here the oracle's), one pass over G gives the oracle's codes, step and
+    # statistics; a shape that would otherwise take the single-pass resident kernel
+    T, D, S = 1024, 2048, 256
+    w = inputs.WORKLOADS["down-4096x11008x4096-bf16"].scaled(T, 64, D, rows_per_example=S)
+    inp = inputs.make_linear_inputs(w)
+    g = inp["G"] if dtype == "bf16" else oq.decode(inp["G"], "bf16")
+    rng = np.random.default_rng(1)
+    sx = rng.uniform(0.01, 0.05, T).astype(np.float32)
+    sw = rng.uniform(1e-4, 1e-3, D).astype(np.float32)
+    ref = pipeline.quantize_gradient(g, dtype, {"scale": sx}, {"scale": sw}, mode=mode, scale=oq.PER_TENSOR,
+                                     seed=5, layer_id=2, rows_per_example=S)
+    a = np.abs(oq.fold(oq.decode(g, dtype), sx, sw)).max()
+    amax = torch.from_numpy(np.array([a], np.float32).view(np.int32)).to(DEV)
+    d = s3r.qdesc(T, D, S, mode, ec, layer_id=2, seed=5)
+    Q = s3r.q_buffer(T, D, DEV)
+    delta = torch.empty(1, device=DEV)
+    st = (torch.empty(T, device=DEV), torch.empty(T // S, D, device=DEV), torch.empty(T // S, device=DEV)) if ec \
+        else (None, None, None)
+    ws = torch.zeros(s3r.s3r_quantize_workspace(d), dtype=torch.uint8, device=DEV)
+    s3r.s3r_quantize_with_amax(d, to_dev(g, dtype), torch.from_numpy(sx).to(DEV), torch.from_numpy(sw).to(DEV), amax,
+                               Q, delta, *st, None, ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(Q), ref["Q"])
+    np.testing.assert_array_equal(host(delta), ref["delta"])
+    if ec:
+        assert rel_err(host(st[0]), ref["eps"]) <= TOL
+        assert rel_err(host(st[1]), ref["ebar"]) <= TOL
+        assert np.abs(host(st[2]) - ref["mu"]).max() <= TOL * np.abs(ref["eps"]).max()

@@ -81,3 +81,106 @@ def test_glue_ffn_block_size_sampled():
     ref_g, ref_u = sg.glue(dH[rows], ag[rows], au[rows])
     np.testing.assert_array_equal(_bits(gg)[rows], ref_g)
     np.testing.assert_array_equal(_bits(gu)[rows], ref_u)
+
+
+# ------------------------------------------------------ glue + amax ----
+
+def _amax_bits(g_bits, sx, sw):
+    """The oracle quantizer's per-tensor amax of fold(G) as fp32 bits (NaN -> any NaN pattern)."""
+    from oracle import quantize as oq
+    x = oq.fold(oq.decode(g_bits, "bf16"), sx, sw)
+    a = np.float32(np.abs(x).max()) if x.size else np.float32(0)
+    return int(np.array([a], np.float32).view(np.uint32)[0])
+
+
+def _check_amax(got, exp):
+    if exp > 0x7F800000:
+        assert got > 0x7F800000, (hex(got), hex(exp))
+    else:
+        assert got == exp, (hex(got), hex(exp))
+
+
+def _glue_amax(dH, ag, au, sx, swg, swu):
+    T, F = dH.shape
+    gg = torch.empty(T, F, dtype=torch.bfloat16, device=DEV)
+    gu = torch.empty_like(gg)
+    amax = torch.full((2,), 0x5A5A5A5A, dtype=torch.int32, device=DEV)
+    ws = torch.zeros(s3r.s3r_swiglu_amax_workspace(T, F), dtype=torch.uint8, device=DEV)
+    dev = lambda a: None if a is None else torch.from_numpy(a).to(DEV)
+    s3r.s3r_swiglu_backward_amax(torch.from_numpy(dH).to(DEV), _bf16_dev(ag), _bf16_dev(au), gg, gu, dev(sx),
+                                 dev(swg), dev(swu), amax, ws)
+    torch.cuda.synchronize()
+    return _bits(gg), _bits(gu), host(amax).view(np.uint32)
+
+
+@pytest.mark.parametrize("T,F,scaled", [(300, 1100, True), (64, 512, False), (1024, 14336, True), (7, 9, True)])
+def test_glue_amax_matches_quantizer_amax(T, F, scaled):
+    # the glue's results are bit-exact and its two amax values are the quantizer's own
+    # max |fl(fl(G * s_x) * s_w)| of those results (ragged tiles; full d_ff at 1024 tokens)
+    dH, ag, au = _draw(T, F, T + F)
+    rng = np.random.default_rng(F)
+    sx = rng.uniform(0.01, 0.05, T).astype(np.float32) if scaled else None
+    swg = rng.uniform(1e-4, 1e-3, F).astype(np.float32) if scaled else None
+    swu = rng.uniform(1e-4, 1e-3, F).astype(np.float32) if scaled else None
+    gg, gu, amax = _glue_amax(dH, ag, au, sx, swg, swu)
+    ref_g, ref_u = sg.glue(dH, ag, au)
+    np.testing.assert_array_equal(gg, ref_g)
+    np.testing.assert_array_equal(gu, ref_u)
+    _check_amax(int(amax[0]), _amax_bits(ref_g, sx, swg))
+    _check_amax(int(amax[1]), _amax_bits(ref_u, sx, swu))
+
+
+def test_glue_amax_non_finite_and_strided():
+    # a NaN or Inf result reaches the amax (NaN orders above Inf); unaligned layouts take the scalar path
+    T, F = 6, 40
+    dH, ag, au = _draw(T, F, 5)
+    dH[2, 3] = np.inf
+    ref_g, ref_u = sg.glue(dH, ag, au)
+    for pad in (0, 3):
+        dHb = torch.zeros(T, F + pad, device=DEV)
+        dHb[:, :F] = torch.from_numpy(dH)
+        Ab = torch.zeros(2, T, F + pad, dtype=torch.bfloat16, device=DEV)
+        Ab[0, :, :F] = _bf16_dev(ag)
+        Ab[1, :, :F] = _bf16_dev(au)
+        Gb = torch.zeros(2, T, F + pad, dtype=torch.bfloat16, device=DEV)
+        amax = torch.zeros(2, dtype=torch.int32, device=DEV)
+        ws = torch.zeros(s3r.s3r_swiglu_amax_workspace(T, F), dtype=torch.uint8, device=DEV)
+        s3r.s3r_swiglu_backward_amax(dHb[:, :F], Ab[0, :, :F], Ab[1, :, :F], Gb[0, :, :F], Gb[1, :, :F], None, None,
+                                     None, amax, ws)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(_bits(Gb[0, :, :F]), ref_g)
+        np.testing.assert_array_equal(_bits(Gb[1, :, :F]), ref_u)
+        got = host(amax).view(np.uint32)
+        _check_amax(int(got[0]), _amax_bits(ref_g, None, None))
+        _check_amax(int(got[1]), _amax_bits(ref_u, None, None))
+
+
+def test_glue_amax_then_quantize_with_amax_equals_oracle_chain():
+    # gate / up stage of the block: glue (with amax) -> quantize_with_amax equals the oracle's glue ->
+    # quantize (its own amax) on codes, step and S3R-EC statistics
+    from oracle import pipeline, quantize as oq
+    T, F, S = 512, 1100, 128
+    dH, ag, au = _draw(T, F, 99)
+    rng = np.random.default_rng(4)
+    sx = rng.uniform(0.01, 0.05, T).astype(np.float32)
+    swg = rng.uniform(1e-4, 1e-3, F).astype(np.float32)
+    gg, gu, amax = _glue_amax(dH, ag, au, sx, swg, None)
+    ref_g, _ = sg.glue(dH, ag, au)
+    np.testing.assert_array_equal(gg, ref_g)
+    d = s3r.qdesc(T, F, S, s3r.S3R, s3r.EC_TWO_WAY, layer_id=1, seed=11)
+    Q = s3r.q_buffer(T, F, DEV)
+    delta = torch.empty(1, device=DEV)
+    er, ecl, em = torch.empty(T, device=DEV), torch.empty(T // S, F, device=DEV), torch.empty(T // S, device=DEV)
+    ws = torch.zeros(s3r.s3r_quantize_workspace(d), dtype=torch.uint8, device=DEV)
+    amax_d = torch.from_numpy(amax[:1].view(np.int32).copy()).to(DEV)
+    s3r.s3r_quantize_with_amax(d, _bf16_dev(gg), torch.from_numpy(sx).to(DEV), torch.from_numpy(swg).to(DEV), amax_d,
+                               Q, delta, er, ecl, em, None, ws)
+    torch.cuda.synchronize()
+    fx, fw = {"scale": sx}, {"scale": swg}
+    ref = pipeline.quantize_gradient(ref_g, "bf16", fx, fw, mode=oq.S3R, scale=oq.PER_TENSOR, seed=11, layer_id=1,
+                                     rows_per_example=S)
+    np.testing.assert_array_equal(host(Q), ref["Q"])
+    np.testing.assert_array_equal(host(delta), ref["delta"])
+    for got, exp in ((er, ref["eps"]), (ecl, ref["ebar"])):
+        e = np.abs(host(got) - exp).max() / np.abs(exp).max()
+        assert e <= 1e-5, e

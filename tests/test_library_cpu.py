@@ -117,6 +117,34 @@ def test_swiglu_argument_errors(L):
     assert call(dH=None) == -1 and call(Gu=None) == -1
 
 
+def test_swiglu_amax_and_quantize_with_amax_argument_errors(L):
+    P = ctypes.c_void_p
+    ok = dict(T=4, F=16, dH=P(256), ldh=16, Ag=P(512), Au=P(768), lda=16, Gg=P(1024), Gu=P(1280), ldg=16,
+              amax=P(2048), ws=P(4096), wsb=1 << 20)
+
+    def glue(**kw):
+        a = {**ok, **kw}
+        return L.s3r_swiglu_backward_amax(a["T"], a["F"], a["dH"], a["ldh"], a["Ag"], a["Au"], a["lda"], a["Gg"],
+                                          a["Gu"], a["ldg"], None, None, None, a["amax"], a["ws"], a["wsb"], None)
+
+    assert glue(T=-1) == -1 and glue(ldg=8) == -1 and glue(dH=None) == -1
+    assert glue(amax=None) == -1                     # the amax output is required
+    assert glue(wsb=1024) == -3                      # workspace below s3r_swiglu_amax_workspace
+    assert glue(ws=P(4100)) == -1                    # workspace not 256-byte aligned
+    assert s3r.s3r_swiglu_amax_workspace(8192, 14336) > 65536
+
+    def qa(desc, amax=P(64), G=P(1), Q=P(1), delta=P(1), ec=(None, None, None), wsb=0, ws=None):
+        return L.s3r_quantize_with_amax(ctypes.byref(desc), G, 0, desc.cols, None, None, amax, Q, desc.cols, delta,
+                                        ec[0], ec[1], ec[2], None, ws, wsb, None)
+
+    d = s3r.qdesc(64, 96, 32, s3r.S3R, s3r.EC_NONE)
+    assert qa(s3r.qdesc(64, 96, 32, s3r.S3R, s3r.EC_NONE, s3r.PER_TOKEN)) == -2   # per-tensor steps only
+    assert qa(d, amax=None) == -1
+    assert qa(d, Q=None) == -1
+    assert qa(s3r.qdesc(64, 96, 32, s3r.S3R, s3r.EC_TWO_WAY)) == -1               # statistics outputs missing
+    assert qa(d, wsb=0) in (-3, -4, -5)                                           # workspace or no device
+
+
 def test_no_gpu_reports_hip_error(L):
     import torch
     if torch.cuda.is_available():
