@@ -26,7 +26,8 @@ channel-mean error and S x_bar_b the per-example input column sums xs_b):
         u_b   = sum_{t in b} (eps_t - mu_b) * Xq[t, :]
 
 "Cost and the dX-Only Variant": the dX-only variant keeps only the activation
-gradient's term.  Everything is float64; integer products are exact.
+gradient's term.  The ablation of Table II ("dW-only corr.") keeps only the
+weight gradient's term (EC_DW_ONLY).  Everything is float64; integer products are exact.
 
 Per-token steps and dW (a reading beyond the pages).  The S3R page explains
 that only a per-tensor step can be applied after the S32 accumulation of the
@@ -43,7 +44,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .quantize import EC_NONE, EC_DX_ONLY, EC_TWO_WAY  # noqa: F401
+from .quantize import EC_NONE, EC_DX_ONLY, EC_TWO_WAY, EC_DW_ONLY  # noqa: F401
 from .quantize import codes_rtne, step_from_amax
 
 
@@ -66,7 +67,7 @@ def _delta_rows(delta: np.ndarray, rows: np.ndarray) -> np.ndarray:
 
 def backward_dx(Q, delta, Wq, s_x, *, ec=EC_NONE, r_W=None, eps=None, ebar=None, mu=None,
                 rows_per_example=None, rows=None) -> np.ndarray:
-    """Dequantised (and, unless ec == EC_NONE, corrected) dX [len(rows), d_in] in float64.
+    """Dequantised (and, for EC_DX_ONLY or EC_TWO_WAY, corrected) dX [len(rows), d_in] in float64.
 
     ``rows`` selects output rows (tokens); default all.  Rows are independent,
     so a sample is computed exactly as the full result would be.
@@ -75,7 +76,7 @@ def backward_dx(Q, delta, Wq, s_x, *, ec=EC_NONE, r_W=None, eps=None, ebar=None,
     rows = np.arange(T) if rows is None else np.asarray(rows)
     acc = int_matmul(Q[rows], Wq).astype(np.float64)
     out = _delta_rows(delta, rows)[:, None] * acc
-    if ec != EC_NONE:
+    if ec in (EC_DX_ONLY, EC_TWO_WAY):
         S = rows_per_example
         b = rows // S
         v = np.asarray(ebar, np.float64) @ Wq.astype(np.float64)         # [B, d_in]
@@ -86,7 +87,7 @@ def backward_dx(Q, delta, Wq, s_x, *, ec=EC_NONE, r_W=None, eps=None, ebar=None,
 
 def backward_dw(Q, delta, Xq, s_w, *, ec=EC_NONE, xs=None, eps=None, ebar=None, mu=None,
                 rows_per_example=None, rows=None) -> np.ndarray:
-    """Dequantised (and, for EC_TWO_WAY, corrected) dW [len(rows), d_in] in float64.
+    """Dequantised (and, for EC_TWO_WAY or EC_DW_ONLY, corrected) dW [len(rows), d_in] in float64.
 
     ``rows`` selects output rows (channels j of the gradient).  Requires a
     per-tensor step (one Delta for the whole of Q).
@@ -97,7 +98,7 @@ def backward_dw(Q, delta, Xq, s_w, *, ec=EC_NONE, xs=None, eps=None, ebar=None, 
     rows = np.arange(D) if rows is None else np.asarray(rows)
     acc = int_matmul(np.ascontiguousarray(Q[:, rows].T), Xq).astype(np.float64)
     out = d[0] * acc
-    if ec == EC_TWO_WAY:
+    if ec in (EC_TWO_WAY, EC_DW_ONLY):
         out -= _dw_correction(Q.shape[0], Xq, xs, eps, ebar, mu, rows_per_example, rows)
     return out / np.asarray(s_w, np.float64)[rows][:, None]
 
@@ -130,7 +131,7 @@ def backward_dw_per_token(Q, delta_t, Xq, s_w, *, ec=EC_NONE, xs=None, eps=None,
                           rows_per_example=None, rows=None) -> np.ndarray:
     """dW [len(rows), d_in] (float64) for per-token steps Delta_t, via the per-column requantized Z.
 
-    The correction terms (EC_TWO_WAY) are those of the per-tensor case: the
+    The correction terms (EC_TWO_WAY, EC_DW_ONLY) are those of the per-tensor case: the
     statistics already carry Delta_t (E' = Delta_t (q - x)), and the inputs enter
     through their exact codes Xq.
     """
@@ -139,7 +140,7 @@ def backward_dw_per_token(Q, delta_t, Xq, s_w, *, ec=EC_NONE, xs=None, eps=None,
     Zq, c = requantize_columns(Xq, delta_t)
     acc = int_matmul(np.ascontiguousarray(Q[:, rows].T), Zq).astype(np.float64)
     out = c.astype(np.float64)[None, :] * acc
-    if ec == EC_TWO_WAY:
+    if ec in (EC_TWO_WAY, EC_DW_ONLY):
         out -= _dw_correction(Q.shape[0], Xq, xs, eps, ebar, mu, rows_per_example, rows)
     return out / np.asarray(s_w, np.float64)[rows][:, None]
 

@@ -22,10 +22,10 @@ def forward_operands(X, W, dtype: str, rows_per_example: int):
 
 
 def quantize_gradient(G, dtype: str, fx, fw, *, mode: int, scale: int, seed: int, layer_id: int,
-                      rows_per_example: int) -> dict:
+                      rows_per_example: int, stream: int = 0) -> dict:
     """Quantize G' = diag(s_x) G diag(s_w) once, with the S3R-EC statistics."""
     q = oq.quantize(G, dtype, mode=mode, scale=scale, row_scale=fx["scale"], col_scale=fw["scale"],
-                    seed=seed, layer_id=layer_id, rows_per_example=rows_per_example)
+                    seed=seed, layer_id=layer_id, rows_per_example=rows_per_example, stream=stream)
     E = ecm.rounding_error(q["Q"], q["x"], q["delta"])
     q["eps"], q["ebar"], q["mu"] = ecm.statistics(E, rows_per_example)
     return q
@@ -52,6 +52,30 @@ def linear_backward(inp: dict, *, mode: int, ec: int, scale: int = oq.PER_TENSOR
     out["dW"] = dw(q["Q"], q["delta"], fx["Q"], fw["scale"], ec=ec, xs=fx["code_colsum"], eps=q["eps"],
                    ebar=q["ebar"], mu=q["mu"], rows_per_example=S, rows=dw_rows)
     return out
+
+
+def linear_backward_twice(inp: dict, *, mode_dx: int, mode_dw: int, seed: int = 0, layer_id: int = 0,
+                          rows_per_example: int, fx=None, fw=None) -> dict:
+    """The conventional configuration: G quantized separately for the two products.
+
+    S3R page, "Quantized Backpropagation with Stochastic Rounding": conventional
+    quantized training draws independent thresholds R^LHS and R^RHS for the
+    activation-gradient and the weight-gradient products (independent SR as in
+    AQT); Table II's causal ablation also mixes Phi_2D and Phi_bcast between the
+    two.  Here the dX operand uses threshold stream 0 and the dW operand stream 1;
+    there is no correction.
+    """
+    dtype = inp["dtype"]
+    S = rows_per_example
+    if fx is None or fw is None:
+        fx, fw = forward_operands(inp["X"], inp["W"], dtype, S)
+    qx = quantize_gradient(inp["G"], dtype, fx, fw, mode=mode_dx, scale=oq.PER_TENSOR, seed=seed,
+                           layer_id=layer_id, rows_per_example=S, stream=0)
+    qw = quantize_gradient(inp["G"], dtype, fx, fw, mode=mode_dw, scale=oq.PER_TENSOR, seed=seed,
+                           layer_id=layer_id, rows_per_example=S, stream=1)
+    dX = backward.backward_dx(qx["Q"], qx["delta"], fw["Q"], fx["scale"])
+    dW = backward.backward_dw(qw["Q"], qw["delta"], fx["Q"], fw["scale"])
+    return {"fx": fx, "fw": fw, "q_dx": qx, "q_dw": qw, "dX": dX, "dW": dW}
 
 
 def raw_accumulators(Q, Wq, Xq, dx_rows=None, dw_rows=None):

@@ -33,9 +33,9 @@ import numpy as np
 
 from . import philox
 
-RTNE, SR, S3R = 0, 1, 2
+RTNE, SR, S3R, S3R_BCAST = 0, 1, 2, 3
 PER_TENSOR, PER_TOKEN = 0, 1
-EC_NONE, EC_DX_ONLY, EC_TWO_WAY = 0, 1, 2
+EC_NONE, EC_DX_ONLY, EC_TWO_WAY, EC_DW_ONLY = 0, 1, 2, 3
 
 FLAG_NONFINITE = 1
 FLAG_TINY_STEP = 2
@@ -104,18 +104,26 @@ def codes_floor_plus(x: np.ndarray, r: np.ndarray) -> np.ndarray:
     return np.clip(floor_plus(x, r), -127, 127).astype(np.int8)
 
 
-def thresholds(mode: int, seed: int, layer_id: int, T: int, D: int, row0: int = 0):
-    """Thresholds r (float64) broadcastable to [T, D] for the stochastic modes."""
+def thresholds(mode: int, seed: int, layer_id: int, T: int, D: int, row0: int = 0, rows_per_example=None,
+               stream: int = 0):
+    """Thresholds r (float64) broadcastable to [T, D] for the stochastic modes.
+
+    SR: one per element; S3R: one per token (Phi_2D); S3R_BCAST: one per
+    example of rows_per_example tokens (Phi_bcast).  ``stream`` selects an
+    independent draw (0: the tensor shared by both products).
+    """
     if mode == SR:
-        return philox.sr_thresholds(seed, layer_id, T, D, row0)
+        return philox.sr_thresholds(seed, layer_id, T, D, row0, stream)
     if mode == S3R:
-        return philox.s3r_thresholds(seed, layer_id, T, row0)[:, None]
+        return philox.s3r_thresholds(seed, layer_id, T, row0, stream)[:, None]
+    if mode == S3R_BCAST:
+        return philox.bcast_thresholds(seed, layer_id, T, rows_per_example, row0, stream)[:, None]
     raise ValueError(mode)
 
 
 def quantize(g_store: np.ndarray, dtype: str, *, mode: int, scale: int = PER_TENSOR,
              row_scale=None, col_scale=None, seed: int = 0, layer_id: int = 0,
-             rows_per_example: int | None = None) -> dict:
+             rows_per_example: int | None = None, stream: int = 0) -> dict:
     """Quantize one gradient tensor; returns codes, steps and the fp32 values x.
 
     Keys: "Q" int8 [T, D]; "delta" f32 ([1] per tensor, [T] per token);
@@ -144,7 +152,7 @@ def quantize(g_store: np.ndarray, dtype: str, *, mode: int, scale: int = PER_TEN
     if mode == RTNE:
         q = codes_rtne(x)
     else:
-        q = codes_floor_plus(x, thresholds(mode, seed, layer_id, T, D))
+        q = codes_floor_plus(x, thresholds(mode, seed, layer_id, T, D, rows_per_example=S, stream=stream))
     q[bad] = 0
     flags = np.uint32(np.bitwise_or.reduce(row_flags)) if T else np.uint32(0)
     return {"Q": q, "delta": delta.astype(F32), "x": x, "flags": int(flags),

@@ -76,6 +76,27 @@ def test_threshold_maps_use_documented_counters(torch_philox):
         assert u[i] == 2 * (byte >> 1) + 1
 
 
+def test_bcast_and_stream_counters(torch_philox):
+    # Phi_bcast: example b uses block b>>4 with tag 2, word (b>>2)&3, byte b&3; stream s adds
+    # 65536*s to counter word 3 (torch: subsequence word 1 holds counter word 3)
+    seed, layer, S = 7, 9, 5
+    r = philox.bcast_thresholds(seed, layer, 43, S, row0=4, stream=1)
+    for i in range(43):
+        b = (i + 4) // S
+        w = int(torch_philox([(seed, layer | ((2 + 65536) << 32), b >> 4)])[0][(b >> 2) & 3])
+        byte = (w >> (8 * (b & 3))) & 0xFF
+        assert r[i] == (2 * (byte >> 1) + 1) / 256
+    u = philox.sr_threshold_units(seed, layer, 2, 6, stream=1)
+    for e in range(12):
+        w = int(torch_philox([(seed, layer | (65536 << 32), e >> 2)])[0][e & 3])
+        assert u.flat[e] == 2 * (w >> 9) + 1
+    # stream 0 is the default draw; another stream is a different one
+    np.testing.assert_array_equal(philox.s3r_threshold_units(seed, layer, 64, stream=0),
+                                  philox.s3r_threshold_units(seed, layer, 64))
+    assert np.mean(philox.s3r_threshold_units(seed, layer, 64, stream=1) ==
+                   philox.s3r_threshold_units(seed, layer, 64)) < 0.2
+
+
 def test_philox_bytes_uniform():
     from scipy import stats
     w = philox.philox4x32_10(np.stack([np.arange(20000), np.zeros(20000), np.ones(20000) * 3,
@@ -220,7 +241,7 @@ def _heavy(seed, T, D, scale=1e-3):
     return (scale * rng.standard_t(3, size=(T, D))).astype(np.float32)
 
 
-@pytest.mark.parametrize("mode", [oq.SR, oq.S3R])
+@pytest.mark.parametrize("mode", [oq.SR, oq.S3R, oq.S3R_BCAST])
 def test_monte_carlo_unbiased(mode):
     # S3R page, Lemma 1 / SR explainer "Why it is unbiased": E[Delta*Q] = G' for marginally
     # uniform thresholds, shared or not; up to Delta/256 on S3R's 7-bit grid.
@@ -231,11 +252,11 @@ def test_monte_carlo_unbiased(mode):
     n = 2500
     acc = np.zeros_like(gp)
     for seed in range(n):
-        out = oq.quantize(g, "f32", mode=mode, row_scale=sx, col_scale=sw, seed=seed)
+        out = oq.quantize(g, "f32", mode=mode, row_scale=sx, col_scale=sw, seed=seed, rows_per_example=8)
         acc += out["delta"][0] * out["Q"]
     mean = acc / n
     delta = float(out["delta"][0])
-    bias = delta / 256 if mode == oq.S3R else delta * 2.0 ** -24
+    bias = delta * 2.0 ** -24 if mode == oq.SR else delta / 256
     tol = 4.5 * delta * 0.5 / np.sqrt(n) + bias
     assert np.max(np.abs(mean - gp)) < tol
 
@@ -588,3 +609,86 @@ def test_requantize_columns_flags_zero_codes():
     d = np.array([np.float32(1e-45), np.float32(0.5)], np.float32)
     Zq, c = backward.requantize_columns(np.array([[1, 0], [0, 100]], np.int8), d)
     assert Zq[0, 0] == 0 and Zq[1, 1] == 127 and c[1] == np.float32(50.0) / np.float32(127)
+
+
+# ----------------------------------------------- ablation configurations ----
+
+def test_bcast_shares_one_threshold_per_example():
+    # S3R page, "Threshold Broadcasting", Phi_bcast: R[b, s, h] = u_b -- one draw decides every
+    # token and channel of an example: elements with equal residual round the same way across
+    # all tokens of the example, and different examples draw independently
+    rng = np.random.default_rng(14)
+    S, B, D = 32, 16, 24
+    p = rng.choice(np.arange(1, 8) / 8.0, (B * S, D))
+    base = rng.integers(-40, 40, (B * S, D)).astype(np.float64)
+    g = np.concatenate([np.full((B * S, 1), 127.0), base + p], axis=1).astype(np.float32)
+    out = oq.quantize(g, "f32", mode=oq.S3R_BCAST, seed=3, rows_per_example=S)
+    up = out["Q"][:, 1:].astype(np.float64) - np.floor(base + p)
+    for b in range(B):
+        ub, pb = up[b * S:(b + 1) * S], p[b * S:(b + 1) * S]
+        for v in np.unique(pb):
+            assert len(set(ub[pb == v])) == 1
+    thr = philox.bcast_thresholds(3, 0, B * S, S)
+    assert len(np.unique(thr.reshape(B, S), axis=1)[0]) == 1 and len(np.unique(thr)) > 4
+
+
+def _rel_err(a, b):
+    return float(np.linalg.norm(a - b) / np.linalg.norm(b))
+
+
+def test_ablation_error_statistics_single_layer():
+    # Table II-style statistics on one synthetic layer (statistics, not parity; S3R page, "Gradient
+    # error", Propositions 1-2, Corollary 1): relative errors of dX and dW against the exact
+    # products, averaged over seeds.  In a single layer:
+    #  - each token's dX error has the same law under Phi_2D and Phi_bcast (both share a token's
+    #    threshold across its channels), and the correction (two-way or dX-only) brings it below
+    #    independent SR's; the dW-only correction leaves dX as uncorrected S3R;
+    #  - Phi_bcast correlates the tokens of an example, so its uncorrected dW error is far above
+    #    Phi_2D's, and the two-way (or dW-only) correction removes most of it;
+    #  - quantizing twice (separate draws for the two products) gives each product the error of
+    #    its own configuration.
+    T, D, K, S = 256, 64, 48, 64
+    rng = np.random.default_rng(21)
+    G = (1e-3 * rng.standard_t(3, (T, D))).astype(np.float32)
+    # inputs with nonzero channel means (as after an activation): the per-example input means
+    # x_bar_b carry the tokens' common error into dW
+    X = (1.0 + rng.standard_normal((T, K))).astype(np.float32)
+    W = (0.02 * rng.standard_normal((D, K))).astype(np.float32)
+    fx = oq.forward_operand(X, "f32", rows_per_example=S)
+    fw = oq.forward_operand(W, "f32", rows_per_example=D)
+    gp = oq.fold(G, fx["scale"], fw["scale"]).astype(np.float64)
+    dx_ex = (gp @ fw["Q"].astype(np.float64)) / fx["scale"].astype(np.float64)[:, None]
+    dw_ex = (gp.T @ fx["Q"].astype(np.float64)) / fw["scale"].astype(np.float64)[:, None]
+    from oracle import pipeline
+    cfg = {"sr": (oq.SR, oq.EC_NONE), "s3r": (oq.S3R, oq.EC_NONE), "ec2": (oq.S3R, oq.EC_TWO_WAY),
+           "ecdx": (oq.S3R, oq.EC_DX_ONLY), "ecdw": (oq.S3R, oq.EC_DW_ONLY), "bc": (oq.S3R_BCAST, oq.EC_NONE),
+           "bc_ec2": (oq.S3R_BCAST, oq.EC_TWO_WAY), "bc_ecdw": (oq.S3R_BCAST, oq.EC_DW_ONLY)}
+    err = {k: [0.0, 0.0] for k in cfg}
+    err["mix_dx2d_dwbc"] = [0.0, 0.0]
+    err["mix_dxbc_dw2d"] = [0.0, 0.0]
+    n = 24
+    for seed in range(n):
+        for k, (mode, ecv) in cfg.items():
+            q = pipeline.quantize_gradient(G, "f32", fx, fw, mode=mode, scale=oq.PER_TENSOR, seed=seed, layer_id=0,
+                                           rows_per_example=S)
+            dx = backward.backward_dx(q["Q"], q["delta"], fw["Q"], fx["scale"], ec=ecv, r_W=fw["code_colsum"][0],
+                                      eps=q["eps"], ebar=q["ebar"], mu=q["mu"], rows_per_example=S)
+            dw = backward.backward_dw(q["Q"], q["delta"], fx["Q"], fw["scale"], ec=ecv, xs=fx["code_colsum"],
+                                      eps=q["eps"], ebar=q["ebar"], mu=q["mu"], rows_per_example=S)
+            err[k][0] += _rel_err(dx, dx_ex) / n
+            err[k][1] += _rel_err(dw, dw_ex) / n
+        for k, (mdx, mdw) in (("mix_dx2d_dwbc", (oq.S3R, oq.S3R_BCAST)), ("mix_dxbc_dw2d", (oq.S3R_BCAST, oq.S3R))):
+            r = pipeline.linear_backward_twice({"G": G, "X": X, "W": W, "dtype": "f32"}, mode_dx=mdx, mode_dw=mdw,
+                                               seed=seed, rows_per_example=S, fx=fx, fw=fw)
+            err[k][0] += _rel_err(r["dX"], dx_ex) / n
+            err[k][1] += _rel_err(r["dW"], dw_ex) / n
+    dx = {k: v[0] for k, v in err.items()}
+    dw = {k: v[1] for k, v in err.items()}
+    assert dx["ec2"] < dx["sr"] and dx["ecdx"] < dx["sr"]
+    assert dx["ecdw"] == pytest.approx(dx["s3r"], rel=1e-12)
+    assert dx["bc"] == pytest.approx(dx["s3r"], rel=0.15)
+    assert dw["bc"] > 2.5 * dw["s3r"]
+    assert dw["bc_ec2"] < 0.5 * dw["bc"] and dw["bc_ecdw"] == pytest.approx(dw["bc_ec2"], rel=1e-12)
+    assert dx["mix_dx2d_dwbc"] == pytest.approx(dx["s3r"], rel=0.15)
+    assert dw["mix_dx2d_dwbc"] > 2.5 * dw["s3r"]
+    assert dw["mix_dxbc_dw2d"] == pytest.approx(dw["s3r"], rel=0.25)
