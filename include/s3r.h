@@ -64,11 +64,15 @@ typedef enum { S3R_F32 = 0, S3R_BF16 = 1, S3R_I32_RAW = 2, S3R_F32_ACC = 3 } s3r
 /* Rounding of G' (S3R page, "Compared Configurations"):
  *   RTNE  deterministic round to nearest even;
  *   SR    independent SR, one Philox4x32-10 32-bit word per element;
- *   S3R   one threshold per token shared across the hidden dimension (Phi_2D). */
-typedef enum { S3R_RTNE = 0, S3R_SR = 1, S3R_S3R = 2 } s3r_mode;
+ *   S3R   one threshold per token shared across the hidden dimension (Phi_2D);
+ *   S3R_BCAST  one threshold per example of rows_per_example tokens, shared by
+ *         all its tokens and channels (Phi_bcast, the page's ablation). */
+typedef enum { S3R_RTNE = 0, S3R_SR = 1, S3R_S3R = 2, S3R_S3R_BCAST = 3 } s3r_mode;
 /* S3R-EC (section "Structured Error Correction"): NONE, the dX-only variant,
- * or the two-way correction of both products.  Requires mode S3R. */
-typedef enum { S3R_EC_NONE = 0, S3R_EC_DX_ONLY = 1, S3R_EC_TWO_WAY = 2 } s3r_ec;
+ * the two-way correction of both products, or (the ablation of Table II,
+ * "dW-only corr.") the weight-gradient term alone.  Requires mode S3R or
+ * S3R_BCAST. */
+typedef enum { S3R_EC_NONE = 0, S3R_EC_DX_ONLY = 1, S3R_EC_TWO_WAY = 2, S3R_EC_DW_ONLY = 3 } s3r_ec;
 /* Step granularity.  PER_TENSOR is the page's single step Delta (the only one
  * the dW GEMM can apply after S32 accumulation).  PER_TOKEN gives one step
  * per row; it is the forward operands' rule (per-token s_x, per-output-channel
@@ -92,6 +96,11 @@ typedef struct s3r_qdesc {
   int32_t  scale;             /* s3r_scale */
   uint32_t layer_id;          /* Philox counter word 2: separates layers */
   uint64_t seed;              /* Philox key */
+  uint32_t stream;            /* threshold stream, 0..65535: 0 is the one draw shared by both
+                                 backward products; quantizing G a second time for the weight
+                                 gradient with stream 1 gives the independent draw R^RHS of the
+                                 conventional configuration ("Quantized Backpropagation...") */
+  uint32_t reserved;          /* must be 0 */
 } s3r_qdesc;
 
 /* ---- quantizer ---------------------------------------------------------
@@ -129,7 +138,9 @@ typedef struct s3r_qdesc {
  * Thresholds: SR element (t,j) uses Philox4x32-10 block e>>2 of e = t*D + j
  * (counter {lo,hi}(e>>2), layer_id, 0; key = seed), word e&3, r =
  * (2*(w>>9)+1)/2^24; S3R token t uses block t>>4 (counter ..., layer_id, 1),
- * word (t>>2)&3, byte t&3, r = (2*(byte>>1)+1)/256.  Code = clamp(floor(x+r)).
+ * word (t>>2)&3, byte t&3, r = (2*(byte>>1)+1)/256; S3R_BCAST uses the same map
+ * on the example index b = t / rows_per_example with tag 2.  Counter word 3 is
+ * tag + 65536 * stream.  Code = clamp(floor(x+r)).
  */
 size_t s3r_quantize_workspace(const s3r_qdesc* desc);
 int s3r_quantize(const s3r_qdesc* desc,
@@ -175,9 +186,11 @@ int s3r_quantize_with_amax(const s3r_qdesc* desc,
  * s3r_backward_dx: dX [T x d_in] = diag(1/s_x) (Delta Q - P(E')) Wq.
  * S3R page, "Quantized Backpropagation" (activation-gradient product) and
  * "Two-Way Correction" (subtract the averages times W: v_b = ebar_b Wq, and
- * the token means times the row sums r_W).
+ * the token means times the row sums r_W).  The correction applies for
+ * ec == DX_ONLY or TWO_WAY.
  *   Wq [D x d_in] int8 (ld_w), s_x [T] f32 (NULL = 1),
- *   r_W [d_in] int32 (required iff ec != NONE), ec_* as from s3r_quantize.
+ *   r_W [d_in] int32 (required iff the correction applies), ec_* as from
+ *   s3r_quantize.
  *   ws: s3r_backward_workspace(desc, d_in) bytes (dX needs none without EC),
  *   zero-filled once.
  */
@@ -193,9 +206,9 @@ int s3r_backward_dx(const s3r_qdesc* desc,
  * S3R page, "Quantized Backpropagation" (weight-gradient product) and
  * "Two-Way Correction" (subtract the inputs times the same averages:
  * sum_b ebar_b[j] xs_b[i] + sum_t (eps_t - mu_b) Xq[t,i]).  The correction
- * applies only for ec == TWO_WAY.
+ * applies for ec == TWO_WAY or DW_ONLY.
  *   Xq [T x d_in] int8 (ld_x), s_w [D] f32 (NULL = 1),
- *   xs_b [B x d_in] int32 (required iff ec == TWO_WAY).
+ *   xs_b [B x d_in] int32 (required iff the correction applies).
  * Per-token steps (desc->scale == PER_TOKEN, delta [T]) are a reading beyond
  * the page, which explains that only a per-tensor step survives the S32
  * accumulation over the tokens: the steps are folded into the inputs,

@@ -37,10 +37,16 @@ int check_desc(const s3r_qdesc* d) {
   if (d->rows < 0 || d->cols < 0 || d->rows_per_example < 1) return S3R_ERR_INVALID_ARG;
   if (d->rows % d->rows_per_example != 0) return S3R_ERR_INVALID_ARG;
   if (d->rows > (int64_t)1 << 31 || d->cols > (int64_t)1 << 31) return S3R_ERR_INVALID_ARG;
-  if (d->mode < S3R_RTNE || d->mode > S3R_S3R) return S3R_ERR_UNSUPPORTED;
-  if (d->ec < S3R_EC_NONE || d->ec > S3R_EC_TWO_WAY) return S3R_ERR_UNSUPPORTED;
+  if (d->mode < S3R_RTNE || d->mode > S3R_S3R_BCAST) return S3R_ERR_UNSUPPORTED;
+  if (d->ec < S3R_EC_NONE || d->ec > S3R_EC_DW_ONLY) return S3R_ERR_UNSUPPORTED;
   if (d->scale != S3R_PER_TENSOR && d->scale != S3R_PER_TOKEN) return S3R_ERR_UNSUPPORTED;
+  if (d->stream > 65535 || d->reserved != 0) return S3R_ERR_INVALID_ARG;
   return S3R_OK;
+}
+
+bool shared_threshold(int mode) { return mode == S3R_S3R || mode == S3R_S3R_BCAST; }
+bool dx_corrected(int ec) { return ec == S3R_EC_DX_ONLY || ec == S3R_EC_TWO_WAY; }
+bool dw_corrected(int ec) { return ec == S3R_EC_TWO_WAY || ec == S3R_EC_DW_ONLY;
 }
 
 int finish(hipError_t e) { return e == hipSuccess ? S3R_OK : S3R_ERR_HIP; }
@@ -61,7 +67,7 @@ int s3r_quantize(const s3r_qdesc* d, const void* G, int32_t g_dtype, int64_t ld_
   int rc = check_desc(d);
   if (rc) return rc;
   if (g_dtype != S3R_F32 && g_dtype != S3R_BF16) return S3R_ERR_UNSUPPORTED;
-  if (d->ec != S3R_EC_NONE && d->mode != S3R_S3R) return S3R_ERR_UNSUPPORTED;
+  if (d->ec != S3R_EC_NONE && !shared_threshold(d->mode)) return S3R_ERR_UNSUPPORTED;
   const int64_t T = d->rows, D = d->cols;
   const bool nonempty = T > 0 && D > 0;
   const int64_t B = T / d->rows_per_example;
@@ -84,6 +90,7 @@ int s3r_quantize(const s3r_qdesc* d, const void* G, int32_t g_dtype, int64_t ld_
   a.ec_row = ec_row; a.ec_col = ec_col; a.ec_mean = ec_mean; a.flags = flags;
   a.T = T; a.D = D; a.S = d->rows_per_example;
   a.mode = d->mode; a.ec = d->ec; a.scale = d->scale; a.layer = d->layer_id; a.seed = d->seed;
+  a.stream = d->stream;
   a.ws = (char*)ws;
   return finish(launch_quantize(a, stream));
 }
@@ -100,7 +107,7 @@ int s3r_quantize_with_amax(const s3r_qdesc* d, const void* G, int32_t g_dtype, i
     return s3r_quantize(d, G, g_dtype, ld_g, row_scale, col_scale, Q, ld_q, delta, nullptr, ec_row, ec_col, ec_mean,
                         flags, ws, ws_bytes, stream);
   if (g_dtype != S3R_F32 && g_dtype != S3R_BF16) return S3R_ERR_UNSUPPORTED;
-  if (d->ec != S3R_EC_NONE && d->mode != S3R_S3R) return S3R_ERR_UNSUPPORTED;
+  if (d->ec != S3R_EC_NONE && !shared_threshold(d->mode)) return S3R_ERR_UNSUPPORTED;
   const int64_t T = d->rows, D = d->cols;
   const int64_t B = T / d->rows_per_example;
   if (!delta || !G || !Q) return S3R_ERR_INVALID_ARG;
@@ -120,6 +127,7 @@ int s3r_quantize_with_amax(const s3r_qdesc* d, const void* G, int32_t g_dtype, i
   a.ec_row = ec_row; a.ec_col = ec_col; a.ec_mean = ec_mean; a.flags = flags;
   a.T = T; a.D = D; a.S = d->rows_per_example;
   a.mode = d->mode; a.ec = d->ec; a.scale = d->scale; a.layer = d->layer_id; a.seed = d->seed;
+  a.stream = d->stream;
   a.ws = (char*)ws;
   a.amax_in = amax_bits;
   return finish(launch_quantize(a, stream));
@@ -127,8 +135,9 @@ int s3r_quantize_with_amax(const s3r_qdesc* d, const void* G, int32_t g_dtype, i
 
 size_t s3r_backward_workspace(const s3r_qdesc* d, int64_t d_in) {
   if (check_desc(d) != S3R_OK || d_in < 0) return 0;
-  const size_t a = dx_workspace(d->rows, d->cols, d_in, d->rows_per_example, d->ec);
-  const size_t b = dw_workspace(d->rows, d->cols, d_in, d->rows_per_example, d->ec, d->scale == S3R_PER_TOKEN);
+  const size_t a = dx_workspace(d->rows, d->cols, d_in, d->rows_per_example, dx_corrected(d->ec) ? d->ec : 0);
+  const size_t b = dw_workspace(d->rows, d->cols, d_in, d->rows_per_example, dw_corrected(d->ec) ? d->ec : 0,
+                                d->scale == S3R_PER_TOKEN);
   return a > b ? a : b;
 }
 
@@ -155,7 +164,7 @@ int s3r_backward_dx(const s3r_qdesc* d, const int8_t* Q, int64_t ld_q, const flo
   if (out_nonempty && ((uintptr_t)dX & 3u)) return S3R_ERR_INVALID_ARG;
   if ((rc = check_gemm_operand(Q, ld_q, T, D, T > 0 && D > 0))) return rc;
   if ((rc = check_gemm_operand(Wq, ld_w, D, d_in, D > 0 && d_in > 0))) return rc;
-  const bool ec = d->ec != S3R_EC_NONE && out_dt != S3R_I32_RAW;
+  const bool ec = dx_corrected(d->ec) && out_dt != S3R_I32_RAW;
   if (ec && (!r_W || !ec_row || !ec_col || !ec_mean)) return S3R_ERR_INVALID_ARG;
   const size_t need = ec ? dx_workspace(T, D, d_in, d->rows_per_example, d->ec) : 0;
   if (ws_bytes < need || (need && (!ws || ((uintptr_t)ws & 255u)))) return S3R_ERR_WORKSPACE;
@@ -182,7 +191,7 @@ int s3r_backward_dw(const s3r_qdesc* d, const int8_t* Q, int64_t ld_q, const flo
   if (out_nonempty && ((uintptr_t)dW & 3u)) return S3R_ERR_INVALID_ARG;
   if ((rc = check_gemm_operand(Q, ld_q, T, D, T > 0 && D > 0))) return rc;
   if ((rc = check_gemm_operand(Xq, ld_x, T, d_in, T > 0 && d_in > 0))) return rc;
-  const bool ec = d->ec == S3R_EC_TWO_WAY && out_dt == S3R_F32;
+  const bool ec = dw_corrected(d->ec) && out_dt == S3R_F32;
   if (ec && (!xs_b || !ec_row || !ec_col || !ec_mean)) return S3R_ERR_INVALID_ARG;
   const int per_token = d->scale == S3R_PER_TOKEN;
   const size_t need = dw_workspace(T, D, d_in, d->rows_per_example, ec ? d->ec : 0, per_token);

@@ -813,7 +813,7 @@ struct DwLayout { size_t part, u, zq, cbits, cval, total; };
 DwLayout dw_layout(int64_t T, int64_t d_in, int ec, int per_token) {
   DwLayout L{};
   size_t off = kWsHeaderBytes;
-  if (ec == S3R_EC_TWO_WAY) {
+  if (ec == S3R_EC_TWO_WAY || ec == S3R_EC_DW_ONLY) {
     L.part = off; off += gemv_part_bytes(T, d_in, 1);
     L.u = off;    off += align_up((size_t)d_in * 4, 256);
   }
@@ -864,7 +864,7 @@ hipError_t launch_backward_dw(const DwArgs& a, hipStream_t st) {
   const DwLayout L = dw_layout(a.T, a.d_in, a.ec, a.per_token);
   EpiParams ep{};
   ep.delta = a.delta; ep.per_token = 0; ep.row_scale = a.sw;
-  ep.ec = (a.ec == S3R_EC_TWO_WAY) && a.out_dt == S3R_F32;
+  ep.ec = (a.ec == S3R_EC_TWO_WAY || a.ec == S3R_EC_DW_ONLY) && a.out_dt == S3R_F32;
   ep.colsum = a.xs; ep.ebar = a.ec_col; ep.ec_row = a.ec_row; ep.ec_mean = a.ec_mean;
   ep.S = a.S; ep.B = B;
   ep.out = a.out; ep.ld_out = a.ld_out; ep.out_i32 = a.out_dt == S3R_I32_RAW;

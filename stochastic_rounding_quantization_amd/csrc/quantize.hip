@@ -208,6 +208,8 @@ struct QuantTile {
   int64_t T, D, S, ld_g, ld_q;
   int tiles_per_example, n_ctiles;
   uint32_t layer; uint64_t seed;
+  uint32_t stream_word;   // 65536 * threshold stream, added to counter word 3
+  int bcast;              // shared-threshold mode: one threshold per example (Phi_bcast), not per token
 };
 
 // MODE: 0 RTNE, 1 SR, 2 S3R.  EC: accumulate rounding errors.  PT: per-token step.
@@ -242,7 +244,8 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
     if (lane == 0) s_red[wave] = m;
   }
   if constexpr (MODE == 2) {
-    if (threadIdx.x < r1 - r0) s_thr[threadIdx.x] = s3r_threshold_units24(r0 + threadIdx.x, p.layer, p.seed);
+    if (threadIdx.x < r1 - r0)
+      s_thr[threadIdx.x] = row_threshold_units24(r0 + threadIdx.x, p.layer, p.seed, p.bcast, p.S, p.stream_word);
   }
   __syncthreads();
   if constexpr (!PT) {
@@ -313,9 +316,9 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
         if ((p.D & 3) == 0) {
           // elements e0 .. e0+7 with e0 % 4 == 0: exactly two Philox blocks
           const uint64_t blk = e0 >> 2;
-          const U4 w0 = philox4x32_10((uint32_t)blk, (uint32_t)(blk >> 32), p.layer, kTagSR,
+          const U4 w0 = philox4x32_10((uint32_t)blk, (uint32_t)(blk >> 32), p.layer, kTagSR + p.stream_word,
                                       (uint32_t)p.seed, (uint32_t)(p.seed >> 32));
-          const U4 w1 = philox4x32_10((uint32_t)(blk + 1), (uint32_t)((blk + 1) >> 32), p.layer, kTagSR,
+          const U4 w1 = philox4x32_10((uint32_t)(blk + 1), (uint32_t)((blk + 1) >> 32), p.layer, kTagSR + p.stream_word,
                                       (uint32_t)p.seed, (uint32_t)(p.seed >> 32));
           R[0] = sr_units24(w0.x); R[1] = sr_units24(w0.y); R[2] = sr_units24(w0.z); R[3] = sr_units24(w0.w);
           R[4] = sr_units24(w1.x); R[5] = sr_units24(w1.y); R[6] = sr_units24(w1.z); R[7] = sr_units24(w1.w);
@@ -324,7 +327,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
           for (int i = 0; i < 8; ++i) {
             const uint64_t ei = e0 + i;
             const uint64_t blk = ei >> 2;
-            const U4 w = philox4x32_10((uint32_t)blk, (uint32_t)(blk >> 32), p.layer, kTagSR,
+            const U4 w = philox4x32_10((uint32_t)blk, (uint32_t)(blk >> 32), p.layer, kTagSR + p.stream_word,
                                        (uint32_t)p.seed, (uint32_t)(p.seed >> 32));
             R[i] = sr_units24(u4_word(w, (uint32_t)ei & 3u));
           }
@@ -481,6 +484,8 @@ struct ResParams {
   int nk;               // chunks per thread, R / TR (<= 16)
   int nblocks;
   uint32_t layer; uint64_t seed;
+  uint32_t stream_word;
+  int bcast;
 };
 
 // Block-to-block exchange through per-block slots in the workspace header:
@@ -611,7 +616,8 @@ __global__ __launch_bounds__(kResThreads, 1) void quantize_resident_kernel(
     for (int i = tid; i < R; i += kResThreads) {
       const bool ok = r0 + i < p.T;
       s_fx[i] = (sx && ok) ? sx[r0 + i] : 1.f;
-      if constexpr (MODE == 2) s_thr[i] = ok ? s3r_threshold_units24(r0 + i, p.layer, p.seed) : 0;
+      if constexpr (MODE == 2)
+        s_thr[i] = ok ? row_threshold_units24(r0 + i, p.layer, p.seed, p.bcast, p.S, p.stream_word) : 0;
     }
     __syncthreads();
     auto amax_slot = [&](int k, const uint4& u) {
@@ -685,9 +691,9 @@ __global__ __launch_bounds__(kResThreads, 1) void quantize_resident_kernel(
           for (int i = 0; i < 8; ++i) Rt[i] = rt;
         } else {
           const uint64_t blk = ((uint64_t)t * (uint64_t)p.D + (uint64_t)j0) >> 2;
-          const U4 w0 = philox4x32_10((uint32_t)blk, (uint32_t)(blk >> 32), p.layer, kTagSR,
+          const U4 w0 = philox4x32_10((uint32_t)blk, (uint32_t)(blk >> 32), p.layer, kTagSR + p.stream_word,
                                       (uint32_t)p.seed, (uint32_t)(p.seed >> 32));
-          const U4 w1 = philox4x32_10((uint32_t)(blk + 1), (uint32_t)((blk + 1) >> 32), p.layer, kTagSR,
+          const U4 w1 = philox4x32_10((uint32_t)(blk + 1), (uint32_t)((blk + 1) >> 32), p.layer, kTagSR + p.stream_word,
                                       (uint32_t)p.seed, (uint32_t)(p.seed >> 32));
           Rt[0] = sr_units24(w0.x); Rt[1] = sr_units24(w0.y); Rt[2] = sr_units24(w0.z); Rt[3] = sr_units24(w0.w);
           Rt[4] = sr_units24(w1.x); Rt[5] = sr_units24(w1.y); Rt[6] = sr_units24(w1.z); Rt[7] = sr_units24(w1.w);
@@ -913,6 +919,8 @@ void run_quantize(const QuantArgs& a, const WsLayout& L, hipStream_t st) {
   p.tiles_per_example = (int)((a.S + kRowsPerTile - 1) / kRowsPerTile);
   p.n_ctiles = (int)((a.D + kColsPerTile - 1) / kColsPerTile);
   p.layer = a.layer; p.seed = a.seed;
+  p.stream_word = a.stream << 16;
+  p.bcast = a.mode == S3R_S3R_BCAST;
   const int64_t B = a.T / a.S;
   dim3 grid((unsigned)(B * p.tiles_per_example), (unsigned)p.n_ctiles);
   dispatch_mode<TIn, VEC>(a, L, p, grid, st);
@@ -978,6 +986,8 @@ hipError_t launch_resident(const QuantArgs& a, const WsLayout& L, int R, hipStre
   p.nk = (int)(R / (kResThreads >> p.tc_log2));
   p.nblocks = (int)((a.T + R - 1) / R);
   p.layer = a.layer; p.seed = a.seed;
+  p.stream_word = a.stream << 16;
+  p.bcast = a.mode == S3R_S3R_BCAST;
   uint32_t* gen_word = (uint32_t*)(a.ws + kWsGenOffset);
   unsigned long long* slots = (unsigned long long*)(a.ws + kWsSlotOffset);
   const uint16_t* G = (const uint16_t*)a.G;

@@ -36,19 +36,31 @@ __device__ __forceinline__ uint32_t u4_word(const U4& v, uint32_t i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
-// Counter tags (word 3 of the counter) separating the threshold streams.
+// Counter tags (word 3 of the counter) separating the threshold streams; a
+// second, independent stream s adds 65536 * s (the conventional configuration
+// that quantizes the gradient separately for the weight-gradient product).
 constexpr uint32_t kTagSR = 0;
 constexpr uint32_t kTagS3R = 1;
+constexpr uint32_t kTagBcast = 2;
 
-// S3R threshold of token t in units of 2^-24: r*2^24 = (2b+1)*2^16, b the top
-// 7 bits of byte t&3 of word (t>>2)&3 of block t>>4.
-__device__ __forceinline__ int32_t s3r_threshold_units24(uint64_t t, uint32_t layer, uint64_t seed) {
-  const uint64_t blk = t >> 4;
-  const U4 v = philox4x32_10((uint32_t)blk, (uint32_t)(blk >> 32), layer, kTagS3R,
+// Per-token (S3R, tag kTagS3R) or per-example (Phi_bcast, tag kTagBcast, i the
+// example index) threshold of index i in units of 2^-24: r*2^24 = (2b+1)*2^16,
+// b the top 7 bits of byte i&3 of word (i>>2)&3 of block i>>4.
+__device__ __forceinline__ int32_t s3r_threshold_units24(uint64_t i, uint32_t layer, uint64_t seed, uint32_t word3) {
+  const uint64_t blk = i >> 4;
+  const U4 v = philox4x32_10((uint32_t)blk, (uint32_t)(blk >> 32), layer, word3,
                              (uint32_t)seed, (uint32_t)(seed >> 32));
-  const uint32_t w = u4_word(v, (uint32_t)(t >> 2) & 3u);
-  const uint32_t byte = (w >> (8u * ((uint32_t)t & 3u))) & 0xFFu;
+  const uint32_t w = u4_word(v, (uint32_t)(i >> 2) & 3u);
+  const uint32_t byte = (w >> (8u * ((uint32_t)i & 3u))) & 0xFFu;
   return (int32_t)(((byte >> 1) * 2u + 1u) << 16);
+}
+
+// Threshold of row t for the shared-threshold modes: per token, or (bcast) per
+// example of S rows.
+__device__ __forceinline__ int32_t row_threshold_units24(uint64_t t, uint32_t layer, uint64_t seed, bool bcast,
+                                                         int64_t S, uint32_t stream_word) {
+  return bcast ? s3r_threshold_units24(t / (uint64_t)S, layer, seed, kTagBcast + stream_word)
+               : s3r_threshold_units24(t, layer, seed, kTagS3R + stream_word);
 }
 
 // Independent-SR threshold of one 32-bit word, in units of 2^-24: 2*(w>>9)+1.
@@ -83,6 +95,7 @@ struct QuantArgs {
   int64_t T, D, S;
   int mode, ec, scale;
   uint32_t layer; uint64_t seed;
+  uint32_t stream;           // threshold stream (0: the shared draw)
   char* ws;
   const uint32_t* amax_in;   // per-tensor amax bits already known on the device, or null
 };

@@ -101,11 +101,11 @@ __global__ __launch_bounds__(256) void swiglu_backward_kernel(
 // The same glue, and in the same pass the per-tensor amax that the gate and up
 // projections' quantizers need: max |fl(fl(G * s_x[t]) * s_w[j])| over the
 // bf16-rounded results (the quantizer's fold of its own input), as ordered fp32
-// bits (NaN above every number).  A block covers 512 columns (8 per lane) and a
-// band of kAmaxBandRows rows, a quarter per wave, so the column scales of a
-// lane stay in registers; each block writes its two maxima to part[0][block]
-// and part[1][block], and swiglu_amax_finalize_kernel reduces them.
-constexpr int kAmaxBandRows = 128;
+// bits (NaN above every number).  Same thread mapping as the plain glue (8
+// consecutive elements of a row per thread, grid-stride over the chunks); each
+// block writes its two maxima to part[0][block] and part[1][block], and
+// swiglu_amax_finalize_kernel reduces them.
+constexpr int kAmaxGlueBlocks = 4096;
 
 __device__ __forceinline__ uint32_t fold_abs_bits(uint32_t bf16, float fx, float sw) {
   return __float_as_uint((__uint_as_float(bf16 << 16) * fx) * sw) & 0x7FFFFFFFu;
@@ -118,55 +118,60 @@ __global__ __launch_bounds__(256) void swiglu_amax_kernel(
     int64_t ld_g, const float* __restrict__ sx, const float* __restrict__ swg, const float* __restrict__ swu,
     uint32_t* __restrict__ part) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t j0 = (int64_t)blockIdx.x * 512 + lane * 8;
-  const int64_t t0 = (int64_t)blockIdx.y * kAmaxBandRows;
-  const int64_t t1 = min(t0 + kAmaxBandRows, T);
-  const int nblk = gridDim.x * gridDim.y, bid = blockIdx.y * gridDim.x + blockIdx.x;
+  const int64_t cpr = (F + 7) / 8;
+  const int64_t total = T * cpr;
   uint32_t mg = 0, mu = 0;
-  if (j0 < F) {
-    const int nc = (int)min((int64_t)8, F - j0);
-    float cg[8], cu[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      cg[i] = (swg && i < nc) ? swg[j0 + i] : 1.f;
-      cu[i] = (swu && i < nc) ? swu[j0 + i] : 1.f;
-    }
-    for (int64_t t = t0 + wave; t < t1; t += 4) {
-      const float fx = sx ? sx[t] : 1.f;
-      const float* dh = dH + t * ld_dh + j0;
-      const uint16_t* ag = Ag + t * ld_a + j0;
-      const uint16_t* au = Au + t * ld_a + j0;
-      uint16_t* gg = Gg + t * ld_g + j0;
-      uint16_t* gu = Gu + t * ld_g + j0;
-      if (VEC && nc == 8) {
-        const float4 h0 = *reinterpret_cast<const float4*>(dh);
-        const float4 h1 = *reinterpret_cast<const float4*>(dh + 4);
-        const uint4 va = *reinterpret_cast<const uint4*>(ag);
-        const uint4 vu = *reinterpret_cast<const uint4*>(au);
-        const float h[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
-        const uint32_t wa[4] = {va.x, va.y, va.z, va.w}, wu[4] = {vu.x, vu.y, vu.z, vu.w};
-        uint32_t og[4], ou[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          uint32_t g0, u0, g1, u1;
-          glue1(h[2 * i], __uint_as_float(wa[i] << 16), __uint_as_float(wu[i] << 16), g0, u0);
-          glue1(h[2 * i + 1], __uint_as_float(wa[i] & 0xFFFF0000u), __uint_as_float(wu[i] & 0xFFFF0000u), g1, u1);
-          og[i] = g0 | (g1 << 16);
-          ou[i] = u0 | (u1 << 16);
-          mg = max(mg, max(fold_abs_bits(g0, fx, cg[2 * i]), fold_abs_bits(g1, fx, cg[2 * i + 1])));
-          mu = max(mu, max(fold_abs_bits(u0, fx, cu[2 * i]), fold_abs_bits(u1, fx, cu[2 * i + 1])));
-        }
-        *reinterpret_cast<uint4*>(gg) = make_uint4(og[0], og[1], og[2], og[3]);
-        *reinterpret_cast<uint4*>(gu) = make_uint4(ou[0], ou[1], ou[2], ou[3]);
+  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < total; c += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t t = c / cpr, j0 = (c - t * cpr) * 8;
+    const float fx = sx ? sx[t] : 1.f;
+    const float* dh = dH + t * ld_dh + j0;
+    const uint16_t* ag = Ag + t * ld_a + j0;
+    const uint16_t* au = Au + t * ld_a + j0;
+    uint16_t* gg = Gg + t * ld_g + j0;
+    uint16_t* gu = Gu + t * ld_g + j0;
+    if (VEC && j0 + 8 <= F) {
+      const float4 h0 = *reinterpret_cast<const float4*>(dh);
+      const float4 h1 = *reinterpret_cast<const float4*>(dh + 4);
+      const uint4 va = *reinterpret_cast<const uint4*>(ag);
+      const uint4 vu = *reinterpret_cast<const uint4*>(au);
+      float cg[8], cu[8];
+      if (swg) {
+        const float4 a = *reinterpret_cast<const float4*>(swg + j0), b = *reinterpret_cast<const float4*>(swg + j0 + 4);
+        cg[0] = a.x; cg[1] = a.y; cg[2] = a.z; cg[3] = a.w; cg[4] = b.x; cg[5] = b.y; cg[6] = b.z; cg[7] = b.w;
       } else {
-        for (int i = 0; i < nc; ++i) {
-          uint32_t g, u;
-          glue1(dh[i], bf16_to_f32(ag[i]), bf16_to_f32(au[i]), g, u);
-          gg[i] = (uint16_t)g;
-          gu[i] = (uint16_t)u;
-          mg = max(mg, fold_abs_bits(g, fx, cg[i]));
-          mu = max(mu, fold_abs_bits(u, fx, cu[i]));
-        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) cg[i] = 1.f;
+      }
+      if (swu) {
+        const float4 a = *reinterpret_cast<const float4*>(swu + j0), b = *reinterpret_cast<const float4*>(swu + j0 + 4);
+        cu[0] = a.x; cu[1] = a.y; cu[2] = a.z; cu[3] = a.w; cu[4] = b.x; cu[5] = b.y; cu[6] = b.z; cu[7] = b.w;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) cu[i] = 1.f;
+      }
+      const float h[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+      const uint32_t wa[4] = {va.x, va.y, va.z, va.w}, wu[4] = {vu.x, vu.y, vu.z, vu.w};
+      uint32_t og[4], ou[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t g0, u0, g1, u1;
+        glue1(h[2 * i], __uint_as_float(wa[i] << 16), __uint_as_float(wu[i] << 16), g0, u0);
+        glue1(h[2 * i + 1], __uint_as_float(wa[i] & 0xFFFF0000u), __uint_as_float(wu[i] & 0xFFFF0000u), g1, u1);
+        og[i] = g0 | (g1 << 16);
+        ou[i] = u0 | (u1 << 16);
+        mg = max(mg, max(fold_abs_bits(g0, fx, cg[2 * i]), fold_abs_bits(g1, fx, cg[2 * i + 1])));
+        mu = max(mu, max(fold_abs_bits(u0, fx, cu[2 * i]), fold_abs_bits(u1, fx, cu[2 * i + 1])));
+      }
+      *reinterpret_cast<uint4*>(gg) = make_uint4(og[0], og[1], og[2], og[3]);
+      *reinterpret_cast<uint4*>(gu) = make_uint4(ou[0], ou[1], ou[2], ou[3]);
+    } else {
+      for (int i = 0; i < 8 && j0 + i < F; ++i) {
+        uint32_t g, u;
+        glue1(dh[i], bf16_to_f32(ag[i]), bf16_to_f32(au[i]), g, u);
+        gg[i] = (uint16_t)g;
+        gu[i] = (uint16_t)u;
+        mg = max(mg, fold_abs_bits(g, fx, swg ? swg[j0 + i] : 1.f));
+        mu = max(mu, fold_abs_bits(u, fx, swu ? swu[j0 + i] : 1.f));
       }
     }
   }
@@ -177,8 +182,7 @@ __global__ __launch_bounds__(256) void swiglu_amax_kernel(
   __syncthreads();
   if (threadIdx.x < 2) {
     const int k = threadIdx.x;
-    const uint32_t m = max(max(red[k][0], red[k][1]), max(red[k][2], red[k][3]));
-    part[(int64_t)k * nblk + bid] = m;
+    part[(int64_t)k * gridDim.x + blockIdx.x] = max(max(red[k][0], red[k][1]), max(red[k][2], red[k][3]));
   }
 }
 
@@ -206,7 +210,7 @@ __global__ __launch_bounds__(256) void swiglu_amax_finalize_kernel(const uint32_
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 int64_t amax_blocks(int64_t T, int64_t F) {
-  return ((F + 511) / 512) * ((T + kAmaxBandRows - 1) / kAmaxBandRows);
+  return std::min<int64_t>((T * ((F + 7) / 8) + 255) / 256, kAmaxGlueBlocks);
 }
 
 }  // namespace
@@ -223,14 +227,14 @@ hipError_t launch_swiglu_backward_amax(int64_t T, int64_t F, const float* dH, in
   const int64_t nblk = amax_blocks(T, F);
   if (nblk > 0) {
     const bool vec = aligned16(dH) && aligned16(Ag) && aligned16(Au) && aligned16(Gg) && aligned16(Gu) &&
-                     ld_dh % 4 == 0 && ld_a % 8 == 0 && ld_g % 8 == 0;
-    dim3 grid((unsigned)((F + 511) / 512), (unsigned)((T + kAmaxBandRows - 1) / kAmaxBandRows));
+                     ld_dh % 4 == 0 && ld_a % 8 == 0 && ld_g % 8 == 0 && (!swg || aligned16(swg)) &&
+                     (!swu || aligned16(swu));
     if (vec)
-      hipLaunchKernelGGL(swiglu_amax_kernel<true>, grid, dim3(256), 0, st, T, F, dH, ld_dh, Ag, Au, ld_a, Gg, Gu,
-                         ld_g, sx, swg, swu, part);
+      hipLaunchKernelGGL(swiglu_amax_kernel<true>, dim3((unsigned)nblk), dim3(256), 0, st, T, F, dH, ld_dh, Ag, Au,
+                         ld_a, Gg, Gu, ld_g, sx, swg, swu, part);
     else
-      hipLaunchKernelGGL(swiglu_amax_kernel<false>, grid, dim3(256), 0, st, T, F, dH, ld_dh, Ag, Au, ld_a, Gg, Gu,
-                         ld_g, sx, swg, swu, part);
+      hipLaunchKernelGGL(swiglu_amax_kernel<false>, dim3((unsigned)nblk), dim3(256), 0, st, T, F, dH, ld_dh, Ag, Au,
+                         ld_a, Gg, Gu, ld_g, sx, swg, swu, part);
   }
   hipLaunchKernelGGL(swiglu_amax_finalize_kernel, dim3(1), dim3(256), 0, st, part, (int)nblk, amax_bits);
   return hipGetLastError();

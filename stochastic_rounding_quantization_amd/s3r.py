@@ -22,8 +22,8 @@ S3R_OK = 0
 STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported combination", -3: "workspace too small",
           -4: "device is not gfx950", -5: "HIP error"}
 S3R_F32, S3R_BF16, S3R_I32_RAW, S3R_F32_ACC = 0, 1, 2, 3
-RTNE, SR, S3R = 0, 1, 2
-EC_NONE, EC_DX_ONLY, EC_TWO_WAY = 0, 1, 2
+RTNE, SR, S3R, S3R_BCAST = 0, 1, 2, 3
+EC_NONE, EC_DX_ONLY, EC_TWO_WAY, EC_DW_ONLY = 0, 1, 2, 3
 PER_TENSOR, PER_TOKEN = 0, 1
 FLAG_NONFINITE, FLAG_TINY_STEP, FLAG_SYNC_TIMEOUT = 1, 2, 4
 
@@ -41,12 +41,14 @@ class S3RError(RuntimeError):
 class QDesc(ctypes.Structure):
     _fields_ = [("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("rows_per_example", ctypes.c_int64),
                 ("mode", ctypes.c_int32), ("ec", ctypes.c_int32), ("scale", ctypes.c_int32),
-                ("layer_id", ctypes.c_uint32), ("seed", ctypes.c_uint64)]
+                ("layer_id", ctypes.c_uint32), ("seed", ctypes.c_uint64), ("stream", ctypes.c_uint32),
+                ("reserved", ctypes.c_uint32)]
 
 
-def qdesc(rows, cols, rows_per_example=None, mode=S3R, ec=EC_NONE, scale=PER_TENSOR, layer_id=0, seed=0) -> QDesc:
+def qdesc(rows, cols, rows_per_example=None, mode=S3R, ec=EC_NONE, scale=PER_TENSOR, layer_id=0, seed=0,
+          stream=0) -> QDesc:
     S = rows_per_example if rows_per_example is not None else max(rows, 1)
-    return QDesc(rows, cols, S, mode, ec, scale, layer_id, seed)
+    return QDesc(rows, cols, S, mode, ec, scale, layer_id, seed, stream, 0)
 
 
 _lib = None
@@ -275,10 +277,10 @@ class Quantized:
 
 
 def quantize(G, *, mode=S3R, ec=EC_NONE, scale=PER_TENSOR, row_scale=None, col_scale=None, seed=0, layer_id=0,
-             rows_per_example=None, colsum=False, stream=None) -> Quantized:
+             rows_per_example=None, colsum=False, stream=None, threshold_stream=0) -> Quantized:
     import torch
     T, D = G.shape
-    desc = qdesc(T, D, rows_per_example, mode, ec, scale, layer_id, seed)
+    desc = qdesc(T, D, rows_per_example, mode, ec, scale, layer_id, seed, threshold_stream)
     dev = G.device
     S = desc.rows_per_example
     B = T // S

@@ -422,3 +422,57 @@ def test_quantize_with_amax_equals_quantize(mode, ec, dtype):
         assert rel_err(host(st[0]), ref["eps"]) <= TOL
         assert rel_err(host(st[1]), ref["ebar"]) <= TOL
         assert np.abs(host(st[2]) - ref["mu"]).max() <= TOL * np.abs(ref["eps"]).max()
+
+
+# --------------------------------------------------- ablation configurations ----
+
+@pytest.mark.parametrize("mode,ec", [(s3r.S3R_BCAST, s3r.EC_NONE), (s3r.S3R_BCAST, s3r.EC_TWO_WAY),
+                                     (s3r.S3R_BCAST, s3r.EC_DX_ONLY), (s3r.S3R, s3r.EC_DW_ONLY),
+                                     (s3r.S3R_BCAST, s3r.EC_DW_ONLY)])
+def test_ablation_configurations(mode, ec):
+    # Phi_bcast (one threshold per example) and the dW-only correction: codes bit-exact, dX / dW
+    # within the tolerance; three examples with ragged shapes; both quantizer paths (a D that
+    # qualifies for the single-pass kernel, and one that does not)
+    for (T, d_in, D, S) in ((384, 300, 700, 128), (1024, 96, 512, 256)):
+        w = inputs.WORKLOADS["down-4096x11008x4096-bf16"].scaled(T, d_in, D, rows_per_example=S)
+        inp = inputs.make_linear_inputs(w)
+        _check_linear(inp, S, mode, ec, seed=D, layer=4)
+
+
+@pytest.mark.parametrize("mode", [s3r.SR, s3r.S3R, s3r.S3R_BCAST])
+def test_second_threshold_stream(mode):
+    # quantizing G a second time with threshold stream 1 (the conventional configuration's
+    # independent R^RHS) gives the oracle's stream-1 codes, different from stream 0's
+    T, D, S = 512, 1100, 128
+    w = inputs.WORKLOADS["down-4096x11008x4096-bf16"].scaled(T, 64, D, rows_per_example=S)
+    inp = inputs.make_linear_inputs(w)
+    G = to_dev(inp["G"], "bf16")
+    codes = []
+    for stream in (0, 1):
+        q = s3r.quantize(G, mode=mode, seed=3, layer_id=2, rows_per_example=S, threshold_stream=stream)
+        torch.cuda.synchronize()
+        ref = oq.quantize(inp["G"], "bf16", mode=mode, seed=3, layer_id=2, rows_per_example=S, stream=stream)
+        np.testing.assert_array_equal(host(q.Q), ref["Q"])
+        codes.append(ref["Q"])
+    assert (codes[0] != codes[1]).any()
+
+
+def test_quantize_twice_backward_equals_oracle():
+    # Table II's causal ablation: dX from Phi_bcast codes (stream 0), dW from Phi_2D codes (stream 1)
+    T, d_in, D, S = 256, 200, 320, 64
+    w = inputs.WORKLOADS["down-4096x11008x4096-bf16"].scaled(T, d_in, D, rows_per_example=S)
+    inp = inputs.make_linear_inputs(w)
+    G, X, W = (to_dev(inp[k], "bf16") for k in ("G", "X", "W"))
+    fx = s3r.forward_operand(X, rows_per_example=S)
+    fw = s3r.forward_operand(W, rows_per_example=D)
+    qx = s3r.quantize(G, mode=s3r.S3R_BCAST, row_scale=fx.delta, col_scale=fw.delta, seed=1, rows_per_example=S)
+    qw = s3r.quantize(G, mode=s3r.S3R, row_scale=fx.delta, col_scale=fw.delta, seed=1, rows_per_example=S,
+                      threshold_stream=1)
+    dX = s3r.backward_dx(qx, fw.Q, s_x=fx.delta)
+    dW = s3r.backward_dw(qw, fx.Q, s_w=fw.delta)
+    torch.cuda.synchronize()
+    ref = pipeline.linear_backward_twice(inp, mode_dx=s3r.S3R_BCAST, mode_dw=s3r.S3R, seed=1, rows_per_example=S)
+    np.testing.assert_array_equal(host(qx.Q), ref["q_dx"]["Q"])
+    np.testing.assert_array_equal(host(qw.Q), ref["q_dw"]["Q"])
+    assert rel_err(host(dX), ref["dX"]) <= TOL
+    assert rel_err(host(dW), ref["dW"]) <= TOL

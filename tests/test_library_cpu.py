@@ -58,6 +58,13 @@ def test_quantize_argument_errors(L):
     assert _call_quantize(L, bad) == -1
     assert _call_quantize(L, d, gdt=2) == -2            # int32 gradient
     assert _call_quantize(L, s3r.qdesc(64, 96, 32, s3r.RTNE, s3r.EC_TWO_WAY), ec=(1, 1, 1)) == -2
+    assert _call_quantize(L, s3r.qdesc(64, 96, 32, s3r.SR, s3r.EC_DW_ONLY), ec=(1, 1, 1)) == -2
+    assert _call_quantize(L, s3r.qdesc(64, 96, 32, 4)) == -2                      # no such mode
+    assert _call_quantize(L, s3r.qdesc(64, 96, 32, s3r.S3R, 4)) == -2             # no such correction
+    assert _call_quantize(L, s3r.qdesc(64, 96, 32, stream=65536)) == -1           # stream beyond 16 bits
+    r = s3r.qdesc(64, 96, 32)
+    r.reserved = 1
+    assert _call_quantize(L, r) == -1
     assert _call_quantize(L, d, ldg=95) == -1           # leading dim < cols
     assert _call_quantize(L, d, G=None) == -1
     assert _call_quantize(L, d, delta=None) == -1
