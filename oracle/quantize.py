@@ -123,8 +123,12 @@ def thresholds(mode: int, seed: int, layer_id: int, T: int, D: int, row0: int = 
 
 def quantize(g_store: np.ndarray, dtype: str, *, mode: int, scale: int = PER_TENSOR,
              row_scale=None, col_scale=None, seed: int = 0, layer_id: int = 0,
-             rows_per_example: int | None = None, stream: int = 0) -> dict:
+             rows_per_example: int | None = None, stream: int = 0, row0: int = 0) -> dict:
     """Quantize one gradient tensor; returns codes, steps and the fp32 values x.
+
+    ``row0`` is the global index of the first row: thresholds are keyed on the
+    global token (element) index, so a slice of rows quantized with its offset
+    draws the same thresholds as in the whole tensor.
 
     Keys: "Q" int8 [T, D]; "delta" f32 ([1] per tensor, [T] per token);
     "x" f32 [T, D] (G'/Delta as the quantizer sees it, zero where flagged);
@@ -152,7 +156,8 @@ def quantize(g_store: np.ndarray, dtype: str, *, mode: int, scale: int = PER_TEN
     if mode == RTNE:
         q = codes_rtne(x)
     else:
-        q = codes_floor_plus(x, thresholds(mode, seed, layer_id, T, D, rows_per_example=S, stream=stream))
+        q = codes_floor_plus(x, thresholds(mode, seed, layer_id, T, D, row0=row0, rows_per_example=S,
+                                           stream=stream))
     q[bad] = 0
     flags = np.uint32(np.bitwise_or.reduce(row_flags)) if T else np.uint32(0)
     return {"Q": q, "delta": delta.astype(F32), "x": x, "flags": int(flags),

@@ -25,6 +25,7 @@ import numpy as np
 __all__ = [
     "Workload", "WORKLOADS", "f32_to_bf16_bits", "bf16_bits_to_f32",
     "student_t", "gaussian", "make_linear_inputs", "FfnBlock", "BLOCKS", "make_ffn_block_inputs",
+    "MoeExperts", "MOE", "zipf_counts", "make_moe_inputs",
 ]
 
 
@@ -178,3 +179,65 @@ def make_ffn_block_inputs(b: FfnBlock) -> dict:
         h[r0:r0 + 1024] = f32_to_bf16_bits((a / (1.0 + np.exp(-a)) * u).astype(np.float32))
     out["H"] = h
     return out
+
+
+@dataclass(frozen=True)
+class MoeExperts:
+    """The expert path of a mixture-of-experts FFN: top-k routing of ``tokens`` tokens over
+    ``experts`` experts gives tokens * top_k rows, sorted by expert (expert e owns rows
+    [offsets[e], offsets[e+1])).  Each expert is a linear layer; this is the backward of the
+    experts' down projection: G [R x d_model], the expert inputs H [R x d_ff] and the weights
+    W [experts x d_model x d_ff].  Rows per expert follow Zipf(zipf_s)."""
+    name: str
+    wid: int
+    tokens: int
+    top_k: int
+    experts: int
+    d_model: int
+    d_ff: int
+    zipf_s: float = 1.1
+    g_nu: float = 3.0
+    g_scale: float = 1e-4
+    w_std: float = 0.02
+
+    @property
+    def rows(self) -> int:
+        return self.tokens * self.top_k
+
+    def scaled(self, tokens: int, experts: int, d_model: int, d_ff: int) -> "MoeExperts":
+        return MoeExperts(f"{self.name}@{tokens}x{experts}x{d_model}x{d_ff}", self.wid, tokens, self.top_k,
+                          experts, d_model, d_ff, self.zipf_s, self.g_nu, self.g_scale, self.w_std)
+
+
+MOE = {
+    # 64 experts, top-2 over 16384 tokens (32768 expert rows), d_model 2048, d_ff 1408
+    "moe-64x16384-top2-2048x1408-bf16": MoeExperts("moe-64x16384-top2-2048x1408-bf16", 5, 16384, 2, 64, 2048, 1408),
+}
+
+
+def zipf_counts(rows: int, experts: int, s: float) -> np.ndarray:
+    """Rows per expert proportional to k^-s (k = 1 .. experts), rounded by largest remainder so
+    that they sum to ``rows`` (int64 [experts], largest first)."""
+    w = np.arange(1, experts + 1, dtype=np.float64) ** -s
+    share = rows * w / w.sum()
+    base = np.floor(share).astype(np.int64)
+    rest = rows - int(base.sum())
+    order = np.argsort(-(share - base), kind="stable")
+    base[order[:rest]] += 1
+    return base
+
+
+def make_moe_inputs(m: MoeExperts) -> dict:
+    """bf16 bit patterns G [R x d_model] = g_scale * t(g_nu), H [R x d_ff] ~ N(0, 1) and
+    W [experts x d_model x d_ff] ~ N(0, w_std^2); "counts" (Zipf sizes dealt to the experts in a
+    seeded random order, as a router would) and "offsets" int64 [experts + 1].  Seeds
+    1000 * wid + k, k: G 1, H 2, W 3, expert order 8."""
+    base = 1000 * m.wid
+    R, E, M, F = m.rows, m.experts, m.d_model, m.d_ff
+    counts = zipf_counts(R, E, m.zipf_s)
+    counts = counts[np.random.default_rng(base + 8).permutation(E)]
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    return {"dtype": "bf16", "counts": counts, "offsets": offsets,
+            "G": f32_to_bf16_bits(student_t(base + 1, (R, M), m.g_nu, m.g_scale)),
+            "X": f32_to_bf16_bits(gaussian(base + 2, (R, F), 1.0)),
+            "W": f32_to_bf16_bits(gaussian(base + 3, (E, M, F), m.w_std))}

@@ -692,3 +692,75 @@ def test_ablation_error_statistics_single_layer():
     assert dx["mix_dx2d_dwbc"] == pytest.approx(dx["s3r"], rel=0.15)
     assert dw["mix_dx2d_dwbc"] > 2.5 * dw["s3r"]
     assert dw["mix_dxbc_dw2d"] == pytest.approx(dw["s3r"], rel=0.25)
+
+
+# ------------------------------------------------------ MoE expert path ----
+
+def _moe_inputs(counts, D, K, seed, dtype="f32"):
+    rng = np.random.default_rng(seed)
+    R = int(sum(counts))
+    inp = {"dtype": dtype, "offsets": np.concatenate([[0], np.cumsum(counts)]).astype(np.int64),
+           "G": (1e-3 * rng.standard_t(3, (R, D))).astype(np.float32),
+           "X": rng.standard_normal((R, K)).astype(np.float32),
+           "W": (0.02 * rng.standard_normal((len(counts), D, K))).astype(np.float32)}
+    return inp
+
+
+def test_moe_one_expert_is_the_dense_path():
+    from oracle import moe, pipeline
+    inp = _moe_inputs([96], 40, 24, 3)
+    for mode, ecv in ((oq.S3R, oq.EC_TWO_WAY), (oq.SR, oq.EC_NONE), (oq.S3R, oq.EC_DX_ONLY)):
+        g = moe.grouped_backward(inp, mode=mode, ec=ecv, seed=4, layer_id=2)
+        d = pipeline.linear_backward({"G": inp["G"], "X": inp["X"], "W": inp["W"][0], "dtype": "f32"}, mode=mode,
+                                     ec=ecv, seed=4, layer_id=2, rows_per_example=96)
+        np.testing.assert_array_equal(g["Q"][0], d["q"]["Q"])
+        np.testing.assert_array_equal(g["dX"], d["dX"])
+        np.testing.assert_array_equal(g["dW"][0], d["dW"])
+
+
+@pytest.mark.parametrize("mode", [oq.SR, oq.S3R])
+def test_moe_thresholds_follow_the_global_row(mode):
+    # thresholds are keyed on the global row: with equal steps (every expert holds the tensor's
+    # largest |G'|) and unit fold scales, the experts' codes are the rows of one whole-tensor quantization
+    from oracle import moe
+    counts = [5, 17, 0, 40, 1, 33]
+    inp = _moe_inputs(counts, 24, 8, 6)
+    off = inp["offsets"]
+    for e in range(len(counts)):
+        if counts[e]:
+            inp["G"][off[e], 0] = np.float32(1.0)
+    inp["G"] = np.clip(inp["G"], -1.0, 1.0).astype(np.float32)
+    ones_x = {"Q": np.zeros((off[-1], 8), np.int8), "scale": np.ones(off[-1], np.float32)}
+    fws = [{"Q": np.zeros((24, 8), np.int8), "scale": np.ones(24, np.float32), "code_colsum": np.zeros((1, 8))}
+           for _ in counts]
+    g = moe.grouped_backward(inp, mode=mode, ec=oq.EC_NONE, seed=9, layer_id=1, fx=ones_x, fws=fws,
+                             xs=np.zeros((len(counts), 8)))
+    whole = oq.quantize(inp["G"], "f32", mode=mode, seed=9, layer_id=1)
+    for e in range(len(counts)):
+        np.testing.assert_array_equal(g["Q"][e], whole["Q"][off[e]:off[e + 1]])
+
+
+def test_moe_correction_per_expert_and_empty_expert():
+    # the correction's projection is taken per expert: what remains of each expert's error sums
+    # to zero along its rows and its columns; an empty expert has step 1 and a zero dW
+    from oracle import moe
+    counts = [30, 0, 12, 50]
+    inp = _moe_inputs(counts, 20, 16, 8)
+    g = moe.grouped_backward(inp, mode=oq.S3R, ec=oq.EC_TWO_WAY, seed=1)
+    for e, n in enumerate(counts):
+        if n == 0:
+            assert g["delta"][e][0] == 1.0 and not g["dW"][e].any()
+            continue
+        d = float(g["delta"][e][0])
+        P = ec.projection(g["eps"][e], g["ebar"][e], g["mu"][e], n)
+        rem = d * g["Q"][e].astype(np.float64) - P - d * g["x"][e].astype(np.float64)
+        np.testing.assert_allclose(rem.sum(axis=1), 0, atol=1e-9 * d)
+        np.testing.assert_allclose(rem.sum(axis=0), 0, atol=1e-9 * d)
+
+
+def test_zipf_counts_largest_remainder():
+    from stochastic_rounding_quantization_amd import inputs
+    c = inputs.zipf_counts(32768, 64, 1.1)
+    assert c.sum() == 32768 and np.all(np.diff(c) <= 0)
+    share = 32768 * np.arange(1, 65) ** -1.1 / (np.arange(1, 65) ** -1.1).sum()
+    assert np.all(np.abs(c - share) < 1)
