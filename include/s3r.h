@@ -85,6 +85,8 @@ typedef enum { S3R_PER_TENSOR = 0, S3R_PER_TOKEN = 1 } s3r_scale;
 #define S3R_FLAG_TINY_STEP  2u  /* an amax so small that 127*2^24/amax overflows fp32: codes 0 */
 #define S3R_FLAG_SYNC_TIMEOUT 4u /* the single-pass quantizer's grid-wide wait timed out (its
                                     workgroups were not all resident): outputs invalid */
+#define S3R_FLAG_BAD_GROUPS 8u  /* grouped calls: the group offsets are not a non-decreasing
+                                   sequence from 0 to the row count; nothing was computed */
 
 /* Problem descriptor of one quantized tensor G [rows x cols]. */
 typedef struct s3r_qdesc {
@@ -230,6 +232,68 @@ int s3r_backward_dw(const s3r_qdesc* desc,
 
 /* Workspace for either backward call (the larger of the two). */
 size_t s3r_backward_workspace(const s3r_qdesc* desc, int64_t d_in);
+
+/* ---- grouped (mixture-of-experts) calls ---------------------------------
+ * The expert path of an MoE layer: every row-indexed tensor (G, Q, X, Xq, dX,
+ * s_x, ec_row) holds its rows sorted by group (expert), group e owning rows
+ * [offsets[e], offsets[e+1]).  Each group is one linear layer with its own
+ * weight; its backward is the dense path above applied to its rows, with the
+ * group as the one example of the correction.  S3R page, Table IV and the MoE
+ * paragraph after it (the correction over the expert-sorted rows).
+ *   groups   G, 1 .. 4096;
+ *   offsets  DEVICE int64 [G+1], non-decreasing from 0 to desc->rows (the
+ *            router's output stays on the device: grids are sized by bounds
+ *            and each workgroup looks its group up).  If the offsets are not
+ *            valid, S3R_FLAG_BAD_GROUPS is raised in *flags (when given) and
+ *            nothing is computed: the outputs keep their contents.
+ *   desc     rows = R (< 2^31) sorted rows, cols = D; rows_per_example is not
+ *            used (pass 1); mode RTNE, SR or S3R (not S3R_BCAST); thresholds
+ *            are keyed on the global row index exactly as in s3r_quantize.
+ *   ws       s3r_grouped_workspace(desc, G, d_in) bytes serve all three calls
+ *            (256-byte aligned, zero-filled once).
+ * Empty groups are allowed: their step is 1, their statistics 0, their dW 0.
+ */
+size_t s3r_grouped_workspace(const s3r_qdesc* desc, int64_t groups, int64_t d_in);
+
+/* s3r_grouped_quantize: per-group per-tensor steps delta [G] (PER_TENSOR;
+ * Delta_e = fl(max over the group's rows of |G'| / 127)), or per-row steps
+ * delta [R] (PER_TOKEN).  col_scale [G x D] (each group's s_w) or NULL;
+ * row_scale [R] or NULL.  ec_row [R], ec_col [G x D], ec_mean [G] as in
+ * s3r_quantize with the group as the example (ec requires mode S3R).
+ * code_colsum [G x D] (per-group column sums of the codes) only with
+ * RTNE + PER_TOKEN + EC_NONE: the forward-operand prep of the experts' inputs
+ * (the correction's xs_e). */
+int s3r_grouped_quantize(const s3r_qdesc* desc, int64_t groups, const int64_t* offsets,
+                         const void* G, int32_t g_dtype, int64_t ld_g,
+                         const float* row_scale, const float* col_scale,
+                         int8_t* Q, int64_t ld_q, float* delta, int32_t* code_colsum,
+                         float* ec_row, float* ec_col, float* ec_mean,
+                         uint32_t* flags, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* s3r_grouped_backward_dx: dX rows of group e = diag(1/s_x)(Delta_e Q_e - P(E'_e)) Wq_e.
+ * Wq_e = Wq + e * w_group_stride bytes, each [D x d_in] with ld_w (16-byte
+ * aligned stride >= D * ld_w); r_W [G x d_in] (each expert's code column sums);
+ * delta [G] per-tensor steps (PER_TENSOR only).  Same operand rules, output
+ * dtypes and correction variants as s3r_backward_dx. */
+int s3r_grouped_backward_dx(const s3r_qdesc* desc, int64_t groups, const int64_t* offsets,
+                            const int8_t* Q, int64_t ld_q, const float* delta,
+                            const int8_t* Wq, int64_t ld_w, int64_t w_group_stride, int64_t d_in,
+                            const float* s_x, const int32_t* r_W,
+                            const float* ec_row, const float* ec_col, const float* ec_mean,
+                            void* dX, int32_t out_dt, int64_t ld_dx, uint32_t* flags,
+                            void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* s3r_grouped_backward_dw: dW_e = diag(1/s_w,e)(Delta_e Q_e - P(E'_e))^T Xq_e for
+ * every group, into dW + e * dw_group_stride elements (each [D x d_in] with
+ * ld_dw, stride >= D * ld_dw).  s_w [G x D], xs [G x d_in] (per-group column
+ * sums of Xq).  The groups run largest first.  PER_TENSOR only. */
+int s3r_grouped_backward_dw(const s3r_qdesc* desc, int64_t groups, const int64_t* offsets,
+                            const int8_t* Q, int64_t ld_q, const float* delta,
+                            const int8_t* Xq, int64_t ld_x, int64_t d_in,
+                            const float* s_w, const int32_t* xs,
+                            const float* ec_row, const float* ec_col, const float* ec_mean,
+                            void* dW, int32_t out_dt, int64_t ld_dw, int64_t dw_group_stride, uint32_t* flags,
+                            void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ---- SwiGLU FFN block glue --------------------------------------------
  * s3r_swiglu_backward: the gradients of H = silu(A_gate) * A_up with respect to

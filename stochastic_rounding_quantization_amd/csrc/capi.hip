@@ -3,6 +3,7 @@
 // or synchronises.
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "s3r_internal.h"
@@ -233,6 +234,112 @@ int s3r_swiglu_backward_amax(int64_t T, int64_t F, const float* dH, int64_t ld_d
   if ((rc = check_arch())) return rc;
   return finish(launch_swiglu_backward_amax(T, F, dH, ld_dh, A_gate, A_up, ld_a, G_gate, G_up, ld_g, row_scale,
                                             col_scale_gate, col_scale_up, amax_bits, (char*)ws, stream));
+}
+
+// ---- grouped (MoE expert) calls
+static int check_groups(const s3r_qdesc* d, int64_t groups, const int64_t* offsets) {
+  if (groups < 1 || groups > kMaxGroups || !offsets) return S3R_ERR_INVALID_ARG;
+  if (d->rows >= ((int64_t)1 << 31)) return S3R_ERR_INVALID_ARG;
+  if (d->mode == S3R_S3R_BCAST) return S3R_ERR_UNSUPPORTED;
+  return S3R_OK;
+}
+
+size_t s3r_grouped_workspace(const s3r_qdesc* d, int64_t groups, int64_t d_in) {
+  if (check_desc(d) != S3R_OK || groups < 1 || groups > kMaxGroups || d_in < 0) return 0;
+  const int ec = d->ec != S3R_EC_NONE;
+  size_t w = grouped_quant_workspace(d->rows, d->cols, groups, ec, d->scale, d->scale == S3R_PER_TOKEN);
+  w = std::max(w, grouped_dx_workspace(d->rows, d->cols, d_in, groups, dx_corrected(d->ec)));
+  w = std::max(w, grouped_dw_workspace(d->rows, d->cols, d_in, groups, dw_corrected(d->ec)));
+  return w;
+}
+
+int s3r_grouped_quantize(const s3r_qdesc* d, int64_t groups, const int64_t* offsets, const void* G, int32_t g_dtype,
+                         int64_t ld_g, const float* row_scale, const float* col_scale, int8_t* Q, int64_t ld_q,
+                         float* delta, int32_t* code_colsum, float* ec_row, float* ec_col, float* ec_mean,
+                         uint32_t* flags, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int rc = check_desc(d);
+  if (rc || (rc = check_groups(d, groups, offsets))) return rc;
+  if (g_dtype != S3R_F32 && g_dtype != S3R_BF16) return S3R_ERR_UNSUPPORTED;
+  if (d->ec != S3R_EC_NONE && d->mode != S3R_S3R) return S3R_ERR_UNSUPPORTED;
+  if (code_colsum && !(d->scale == S3R_PER_TOKEN && d->mode == S3R_RTNE && d->ec == S3R_EC_NONE))
+    return S3R_ERR_UNSUPPORTED;
+  const int64_t R = d->rows, D = d->cols;
+  if (!delta || (R > 0 && D > 0 && (!G || !Q)) || ld_g < D || ld_q < D) return S3R_ERR_INVALID_ARG;
+  if (d->ec != S3R_EC_NONE) {
+    if (!ec_row || !ec_col || !ec_mean) return S3R_ERR_INVALID_ARG;
+  } else if (ec_row || ec_col || ec_mean) {
+    return S3R_ERR_INVALID_ARG;
+  }
+  const size_t need = grouped_quant_workspace(R, D, groups, d->ec != S3R_EC_NONE, d->scale, code_colsum != nullptr);
+  if (ws_bytes < need) return S3R_ERR_WORKSPACE;
+  if (!ws || ((uintptr_t)ws & 255u)) return S3R_ERR_INVALID_ARG;
+  if ((rc = check_arch())) return rc;
+  QuantArgs a{};
+  a.G = G; a.g_dtype = g_dtype; a.ld_g = ld_g; a.sx = row_scale; a.sw = col_scale;
+  a.Q = Q; a.ld_q = ld_q; a.delta = delta; a.code_colsum = code_colsum;
+  a.ec_row = ec_row; a.ec_col = ec_col; a.ec_mean = ec_mean; a.flags = flags;
+  a.T = R; a.D = D; a.S = 1;
+  a.mode = d->mode; a.ec = d->ec; a.scale = d->scale; a.layer = d->layer_id; a.seed = d->seed;
+  a.stream = d->stream;
+  a.ws = (char*)ws;
+  return finish(launch_grouped_quantize(a, groups, offsets, stream));
+}
+
+int s3r_grouped_backward_dx(const s3r_qdesc* d, int64_t groups, const int64_t* offsets, const int8_t* Q, int64_t ld_q,
+                            const float* delta, const int8_t* Wq, int64_t ld_w, int64_t w_group_stride, int64_t d_in,
+                            const float* s_x, const int32_t* r_W, const float* ec_row, const float* ec_col,
+                            const float* ec_mean, void* dX, int32_t out_dt, int64_t ld_dx, uint32_t* flags, void* ws,
+                            size_t ws_bytes, hipStream_t stream) {
+  int rc = check_desc(d);
+  if (rc || (rc = check_groups(d, groups, offsets))) return rc;
+  if (d->scale != S3R_PER_TENSOR) return S3R_ERR_UNSUPPORTED;
+  if (out_dt != S3R_F32 && out_dt != S3R_I32_RAW && out_dt != S3R_F32_ACC) return S3R_ERR_UNSUPPORTED;
+  const int64_t R = d->rows, D = d->cols;
+  if (d_in < 0 || D > kMaxK) return S3R_ERR_INVALID_ARG;
+  if (!delta || (R > 0 && d_in > 0 && !dX) || ld_dx < d_in || ld_dx >= kMaxLdOut) return S3R_ERR_INVALID_ARG;
+  if (R > 0 && d_in > 0 && ((uintptr_t)dX & 3u)) return S3R_ERR_INVALID_ARG;
+  if ((rc = check_gemm_operand(Q, ld_q, R, D, R > 0 && D > 0))) return rc;
+  if ((rc = check_gemm_operand(Wq, ld_w, D, d_in, D > 0 && d_in > 0))) return rc;
+  if (D > 0 && d_in > 0 && (w_group_stride < D * ld_w || (w_group_stride & 15))) return S3R_ERR_INVALID_ARG;
+  const bool ec = dx_corrected(d->ec) && out_dt != S3R_I32_RAW;
+  if (ec && (!r_W || !ec_row || !ec_col || !ec_mean)) return S3R_ERR_INVALID_ARG;
+  const size_t need = grouped_dx_workspace(R, D, d_in, groups, ec);
+  if (ws_bytes < need || !ws || ((uintptr_t)ws & 255u)) return S3R_ERR_WORKSPACE;
+  if ((rc = check_arch())) return rc;
+  DxArgs a{};
+  a.Q = Q; a.ld_q = ld_q; a.delta = delta; a.per_token = 0;
+  a.W = Wq; a.ld_w = ld_w; a.T = R; a.D = D; a.d_in = d_in; a.S = 1;
+  a.sx = s_x; a.rW = r_W; a.ec_row = ec_row; a.ec_col = ec_col; a.ec_mean = ec_mean; a.ec = ec ? d->ec : 0;
+  a.out = dX; a.out_dt = out_dt; a.ld_out = ld_dx; a.ws = (char*)ws;
+  return finish(launch_grouped_backward_dx(a, groups, offsets, w_group_stride, flags, stream));
+}
+
+int s3r_grouped_backward_dw(const s3r_qdesc* d, int64_t groups, const int64_t* offsets, const int8_t* Q, int64_t ld_q,
+                            const float* delta, const int8_t* Xq, int64_t ld_x, int64_t d_in, const float* s_w,
+                            const int32_t* xs, const float* ec_row, const float* ec_col, const float* ec_mean,
+                            void* dW, int32_t out_dt, int64_t ld_dw, int64_t dw_group_stride, uint32_t* flags,
+                            void* ws, size_t ws_bytes, hipStream_t stream) {
+  int rc = check_desc(d);
+  if (rc || (rc = check_groups(d, groups, offsets))) return rc;
+  if (d->scale != S3R_PER_TENSOR) return S3R_ERR_UNSUPPORTED;
+  if (out_dt != S3R_F32 && out_dt != S3R_I32_RAW) return S3R_ERR_UNSUPPORTED;
+  const int64_t R = d->rows, D = d->cols;
+  if (d_in < 0 || R > kMaxK) return S3R_ERR_INVALID_ARG;
+  if (!delta || (D > 0 && d_in > 0 && !dW) || ld_dw < d_in || ld_dw >= kMaxLdOut) return S3R_ERR_INVALID_ARG;
+  if (D > 0 && d_in > 0 && (((uintptr_t)dW & 3u) || dw_group_stride < D * ld_dw)) return S3R_ERR_INVALID_ARG;
+  if ((rc = check_gemm_operand(Q, ld_q, R, D, R > 0 && D > 0))) return rc;
+  if ((rc = check_gemm_operand(Xq, ld_x, R, d_in, R > 0 && d_in > 0))) return rc;
+  const bool ec = dw_corrected(d->ec) && out_dt == S3R_F32;
+  if (ec && (!xs || !ec_row || !ec_col || !ec_mean)) return S3R_ERR_INVALID_ARG;
+  const size_t need = grouped_dw_workspace(R, D, d_in, groups, ec);
+  if (ws_bytes < need || !ws || ((uintptr_t)ws & 255u)) return S3R_ERR_WORKSPACE;
+  if ((rc = check_arch())) return rc;
+  DwArgs a{};
+  a.Q = Q; a.ld_q = ld_q; a.delta = delta; a.per_token = 0; a.X = Xq; a.ld_x = ld_x;
+  a.T = R; a.D = D; a.d_in = d_in; a.S = 1;
+  a.sw = s_w; a.xs = xs; a.ec_row = ec_row; a.ec_col = ec_col; a.ec_mean = ec_mean; a.ec = ec ? d->ec : 0;
+  a.out = dW; a.out_dt = out_dt; a.ld_out = ld_dw; a.ws = (char*)ws;
+  return finish(launch_grouped_backward_dw(a, groups, offsets, dw_group_stride, flags, stream));
 }
 
 int s3r_time_next_gemm(hipEvent_t start, hipEvent_t stop) {

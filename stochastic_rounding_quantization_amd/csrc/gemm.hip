@@ -382,18 +382,86 @@ __device__ __forceinline__ void epilogue(const GemmParams& g, const EpiParams& e
 }
 
 // ----------------------------------------------------------------- kernel ----
-template <bool A_KMAJOR, int EPI, bool EC, int NB>
-__global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmParams g, EpiParams ep) {
-  // XCD-aware numbering: hardware block ids go round-robin over the 8 XCDs;
-  // give each XCD a contiguous range of logical tiles.
-  const int nblocks = g.tiles_m * g.tiles_n;
-  int bid = blockIdx.x;
-  if (nblocks % kNumXcd == 0) bid = (bid % kNumXcd) * (nblocks / kNumXcd) + bid / kNumXcd;
-  const int group = kGroupM * g.tiles_n;
-  const int first_m = (bid / group) * kGroupM;
-  const int gsz = min(g.tiles_m - first_m, kGroupM);
-  const int tm = first_m + (bid % group) % gsz;
-  const int tn = (bid % group) / gsz;
+// Grouped launches (GRP != 0): rows sorted by group, group e owning rows
+// [offsets[e], offsets[e+1]).  GRP_DX: a row tile of one group's Q against
+// its own weight codes (B + e * b_stride); the grid is an upper bound on the
+// groups' row tiles times the column tiles.  GRP_DW: one output matrix per
+// group (out + e * out_stride), K = the group's rows; groups are taken largest
+// first (order[]), so the longest K loops start first.  Each workgroup rebases
+// the operand, output and epilogue pointers to its group, after which the
+// dense kernel body runs unchanged.  Nothing runs if the offsets were invalid.
+enum { GRP_NONE = 0, GRP_DX = 1, GRP_DW = 2 };
+template <typename T>
+__device__ __forceinline__ const T* advance(const T* p, int64_t k) { return p ? p + k : p; }
+struct GroupGemm {
+  const int64_t* offsets; const int32_t* tiles256; const int32_t* order; const uint32_t* status;
+  int64_t G;
+  int64_t b_stride;      // GRP_DX: bytes between the groups' B operands
+  int64_t out_stride;    // GRP_DW: elements between the groups' outputs
+  int tiles_m_all;       // GRP_DX: the grid's row-tile bound
+};
+
+template <bool A_KMAJOR, int EPI, bool EC, int NB, int GRP = GRP_NONE>
+__global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmParams g, EpiParams ep, GroupGemm gg) {
+  int tm, tn;
+  if constexpr (GRP == GRP_NONE) {
+    // XCD-aware numbering: hardware block ids go round-robin over the 8 XCDs;
+    // give each XCD a contiguous range of logical tiles.
+    const int nblocks = g.tiles_m * g.tiles_n;
+    int bid = blockIdx.x;
+    if (nblocks % kNumXcd == 0) bid = (bid % kNumXcd) * (nblocks / kNumXcd) + bid / kNumXcd;
+    const int group = kGroupM * g.tiles_n;
+    const int first_m = (bid / group) * kGroupM;
+    const int gsz = min(g.tiles_m - first_m, kGroupM);
+    tm = first_m + (bid % group) % gsz;
+    tn = (bid % group) / gsz;
+  } else if constexpr (GRP == GRP_DX) {
+    if (gg.status[0] != 0) return;
+    const int nblocks = gg.tiles_m_all * g.tiles_n;
+    int bid = blockIdx.x;
+    if (nblocks % kNumXcd == 0) bid = (bid % kNumXcd) * (nblocks / kNumXcd) + bid / kNumXcd;
+    const int mt = bid / g.tiles_n;
+    const int e = find_group(gg.tiles256, gg.G, mt);
+    if (e < 0) return;
+    const int64_t r0 = gg.offsets[e], n = gg.offsets[e + 1] - r0;
+    g.A += r0 * g.lda;
+    g.M = n;
+    g.B += e * gg.b_stride;
+    ep.delta += e;
+    ep.row_scale = advance(ep.row_scale, r0);
+    ep.ec_row = advance(ep.ec_row, r0);
+    ep.ec_mean = advance(ep.ec_mean, e);
+    ep.colsum = advance(ep.colsum, e * g.N);
+    ep.vec = advance(ep.vec, e * g.N);
+    ep.out = (char*)ep.out + r0 * ep.ld_out * 4;
+    ep.S = n > 0 ? n : 1;
+    ep.B = 1;
+    tm = mt - gg.tiles256[e];
+    tn = bid % g.tiles_n;
+  } else {
+    if (gg.status[0] != 0) return;
+    const int per = g.tiles_m * g.tiles_n;
+    const int slot = blockIdx.x / per, local = blockIdx.x % per;
+    if (slot >= gg.G) return;
+    const int e = gg.order[slot];
+    const int64_t r0 = gg.offsets[e], n = gg.offsets[e + 1] - r0;
+    g.A += r0 * g.lda;            // Q rows of the group: the K dimension of Q^T
+    g.B += r0 * g.ldb;
+    g.K = n;
+    ep.delta += e;
+    ep.row_scale = advance(ep.row_scale, e * g.M);
+    ep.ebar = advance(ep.ebar, e * g.M);
+    ep.colsum = advance(ep.colsum, e * g.N);
+    ep.u = advance(ep.u, e * g.N);
+    ep.out = (char*)ep.out + e * gg.out_stride * 4;
+    ep.S = n > 0 ? n : 1;
+    ep.B = 1;
+    const int group = kGroupM * g.tiles_n;
+    const int first_m = (local / group) * kGroupM;
+    const int gsz = min(g.tiles_m - first_m, kGroupM);
+    tm = first_m + (local % group) % gsz;
+    tn = (local % group) / gsz;
+  }
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int nk = (int)((g.K + BK - 1) / BK);
 
@@ -501,18 +569,33 @@ constexpr int kGvCols = 64 * kGvColsPerLane;   // 512 columns per block
 constexpr int kGvRows = 64;                    // rows per band
 constexpr int kGvRowsPerWave = kGvRows / 4;
 
+// Grouped launches: gridDim.z groups of VEC mode, group z using P + z * pstride
+// and coefficients C + z * nb * K (its outputs are vectors z*nb .. z*nb+nb-1);
+// or (goff != null) grouped TOKEN mode, band blockIdx.y being a 64-row tile of
+// one group (tables from the group offsets), coef(k) = ec_row[k] - ec_mean[e].
 template <int NB>
 __global__ __launch_bounds__(kGvThreads) void gemv_partial_kernel(
     const int8_t* __restrict__ P, int64_t ld, int64_t K, int64_t N, int64_t nb, int token_mode,
     const float* __restrict__ C, const float* __restrict__ ec_row, const float* __restrict__ ec_mean, int64_t S,
-    float* __restrict__ part) {
+    float* __restrict__ part, int64_t pstride, const int64_t* __restrict__ goff, const int32_t* __restrict__ gtiles,
+    int64_t G) {
   __shared__ float red[4][NB][kGvCols];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t n0 = (int64_t)blockIdx.x * kGvCols + lane * kGvColsPerLane;
-  const int64_t k0 = (int64_t)blockIdx.y * kGvRows;
-  const int rows = (int)min((int64_t)kGvRows, K - k0);
-  // The band through one buffer descriptor: rows past K read zeros; columns past
-  // N (the last lanes of a ragged row) are cleared by the mask at use.
+  int64_t k0 = (int64_t)blockIdx.y * kGvRows;
+  int rows = (int)min((int64_t)kGvRows, K - k0);
+  int grp = -1;
+  if (goff) {
+    grp = find_group(gtiles, G, blockIdx.y);
+    if (grp < 0) return;
+    k0 = goff[grp] + (int64_t)(blockIdx.y - gtiles[grp]) * kGvRows;
+    rows = (int)min((int64_t)kGvRows, goff[grp + 1] - k0);
+  }
+  P += blockIdx.z * pstride;
+  if (C) C += blockIdx.z * nb * K;
+  const int64_t nb_all = nb * gridDim.z, zb = blockIdx.z * nb;
+  // The band through one buffer descriptor (no load addresses a row past it);
+  // columns past N (the last lanes of a ragged row) are cleared by the mask at use.
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(P + k0 * ld), (short)0, (int)((uint32_t)rows * (uint32_t)ld), kRsrcWord3);
   const uint32_t voff = (uint32_t)n0;
@@ -526,7 +609,8 @@ __global__ __launch_bounds__(kGvThreads) void gemv_partial_kernel(
     uint2 u[kGvRowsPerWave];
 #pragma unroll
     for (int i = 0; i < kGvRowsPerWave; ++i) {
-      const uint32_t soff = (uint32_t)(wave + 4 * i) * (uint32_t)ld;
+      // rows past the band repeat its last row; their coefficients are 0
+      const uint32_t soff = (uint32_t)min(wave + 4 * i, rows - 1) * (uint32_t)ld;
       const auto w = __builtin_amdgcn_raw_buffer_load_b64(rsrc, voff, soff, 0);
       u[i] = make_uint2(w[0], w[1]);
     }
@@ -540,7 +624,8 @@ __global__ __launch_bounds__(kGvThreads) void gemv_partial_kernel(
         float x = 0.f;
         if (lane < kGvRowsPerWave && r < rows && b0 + b < nb) {
           const int64_t k = k0 + r;
-          x = token_mode ? ec_row[k] - ec_mean[(uint32_t)k / (uint32_t)S] : C[(b0 + b) * K + k];
+          x = token_mode ? ec_row[k] - ec_mean[grp >= 0 ? (int64_t)grp : (int64_t)((uint64_t)k / (uint64_t)S)]
+                         : C[(b0 + b) * K + k];
         }
         cf[b] = x;
       }
@@ -575,7 +660,7 @@ __global__ __launch_bounds__(kGvThreads) void gemv_partial_kernel(
       const int64_t n = (int64_t)blockIdx.x * kGvCols + c;
       if (b0 + b < nb && n < N) {
         const float v = ((red[0][b][c] + red[1][b][c]) + red[2][b][c]) + red[3][b][c];
-        part[((int64_t)blockIdx.y * nb + b0 + b) * N + n] = v;
+        part[((int64_t)blockIdx.y * nb_all + zb + b0 + b) * N + n] = v;
       }
     }
   }
@@ -624,10 +709,10 @@ hipError_t run_gemv(const int8_t* P, int64_t ld, int64_t K, int64_t N, int64_t n
   dim3 grid((unsigned)((N + kGvCols - 1) / kGvCols), (unsigned)nbands);
   if (token_mode || nb == 1)
     hipLaunchKernelGGL(gemv_partial_kernel<1>, grid, dim3(kGvThreads), 0, st, P, ld, K, N, nb, token_mode, C, ec_row,
-                       ec_mean, S, part);
+                       ec_mean, S, part, (int64_t)0, (const int64_t*)nullptr, (const int32_t*)nullptr, (int64_t)0);
   else
     hipLaunchKernelGGL(gemv_partial_kernel<4>, grid, dim3(kGvThreads), 0, st, P, ld, K, N, nb, token_mode, C, ec_row,
-                       ec_mean, S, part);
+                       ec_mean, S, part, (int64_t)0, (const int64_t*)nullptr, (const int32_t*)nullptr, (int64_t)0);
   const int64_t count = nb * N;
   int tpi = 1;
   while (tpi < 16 && tpi * 8 < nbands) tpi *= 2;
@@ -635,6 +720,19 @@ hipError_t run_gemv(const int8_t* P, int64_t ld, int64_t K, int64_t N, int64_t n
   hipLaunchKernelGGL(gemv_reduce_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, part, nbands,
                      count, tpi, out);
   return hipGetLastError();
+}
+
+// out[e][n] = sum over the 64-row bands k of group e (tiles[e] .. tiles[e+1]) of
+// part[k][n], in order, fp64; zero for an empty group.
+__global__ __launch_bounds__(256) void grouped_band_reduce_kernel(const float* __restrict__ part,
+                                                                  const int32_t* __restrict__ tiles, int64_t G,
+                                                                  int64_t N, float* __restrict__ out) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= G * N) return;
+  const int64_t e = idx / N, n = idx - e * N;
+  double a = 0.0;
+  for (int k = tiles[e]; k < tiles[e + 1]; ++k) a += (double)part[(int64_t)k * N + n];
+  out[idx] = (float)a;
 }
 
 size_t gemv_part_bytes(int64_t K, int64_t N, int64_t nb) {
@@ -771,15 +869,17 @@ __global__ __launch_bounds__(256) void zcol_quant_kernel(const int8_t* __restric
 
 size_t zq_ld(int64_t N) { return (size_t)((N + 15) / 16 * 16); }
 
-template <bool A_KMAJOR, int EPI, bool EC, int NB = 1>
-hipError_t run_gemm(const GemmParams& g, const EpiParams& ep, hipStream_t st) {
+template <bool A_KMAJOR, int EPI, bool EC, int NB = 1, int GRP = GRP_NONE>
+hipError_t run_gemm(const GemmParams& g, const EpiParams& ep, hipStream_t st, const GroupGemm& gg = GroupGemm{}) {
   GemmTiming& tm = gemm_timing();
   const GemmTiming ev = tm;
   tm = GemmTiming{};
-  const int nblocks = g.tiles_m * g.tiles_n;
+  const int nblocks = GRP == GRP_NONE ? g.tiles_m * g.tiles_n
+                      : GRP == GRP_DX ? gg.tiles_m_all * g.tiles_n : (int)gg.G * g.tiles_m * g.tiles_n;
   if (ev.start && hipEventRecord(ev.start, st) != hipSuccess) return hipErrorInvalidValue;
   if (nblocks > 0)
-    hipLaunchKernelGGL((gemm_i8_kernel<A_KMAJOR, EPI, EC, NB>), dim3((unsigned)nblocks), dim3(kGemmThreads), 0, st, g, ep);
+    hipLaunchKernelGGL((gemm_i8_kernel<A_KMAJOR, EPI, EC, NB, GRP>), dim3((unsigned)nblocks), dim3(kGemmThreads), 0,
+                       st, g, ep, gg);
   hipError_t e = hipGetLastError();
   if (ev.stop && hipEventRecord(ev.stop, st) != hipSuccess && e == hipSuccess) e = hipErrorInvalidValue;
   return e;
@@ -924,6 +1024,108 @@ hipError_t launch_backward_dw(const DwArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(dw_rank_update_kernel, dim3((unsigned)((a.d_in + 255) / 256), (unsigned)a.D), dim3(256), 0, st,
                      (float*)a.out, a.ld_out, a.D, a.d_in, B, a.ec_col, a.xs, a.sw);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------- grouped calls ----
+// Workspace: header | group tables | dX: v band partials [bands(D) x G x N], v [G x N]
+//                                  | dW: u band partials [R/64 + G bands x N], u [G x N]
+struct GroupedBwLayout { size_t tables, part, vec, total; };
+
+GroupedBwLayout grouped_bw_layout(int64_t R, int64_t D, int64_t d_in, int64_t G, bool dx, bool ec) {
+  GroupedBwLayout L{};
+  size_t off = kWsHeaderBytes;
+  L.tables = off; off = align_up(off + group_tables_bytes(G), 256);
+  if (ec) {
+    const int64_t bands = dx ? (D + kGvRows - 1) / kGvRows : R / kGvRows + G;
+    L.part = off; off = align_up(off + (size_t)bands * (dx ? G : 1) * d_in * 4, 256);
+    L.vec = off;  off = align_up(off + (size_t)G * d_in * 4, 256);
+  }
+  L.total = off;
+  return L;
+}
+
+size_t grouped_dx_workspace(int64_t R, int64_t D, int64_t d_in, int64_t G, int ec) {
+  return grouped_bw_layout(R, D, d_in, G, true, ec != 0).total;
+}
+size_t grouped_dw_workspace(int64_t R, int64_t D, int64_t d_in, int64_t G, int ec) {
+  return grouped_bw_layout(R, D, d_in, G, false, ec != 0).total;
+}
+
+// dX rows of every group: Q rows of group e times its weight codes W + e * w_stride.
+hipError_t launch_grouped_backward_dx(const DxArgs& a, int64_t G, const int64_t* offsets, int64_t w_stride,
+                                      uint32_t* flags, hipStream_t st) {
+  const GroupedBwLayout L = grouped_bw_layout(a.T, a.D, a.d_in, G, true, a.ec != 0);
+  const GroupTables tab = group_tables(a.ws + L.tables, G, offsets);
+  hipError_t e = launch_group_tables(tab, a.T, flags, st);
+  if (e != hipSuccess || a.d_in == 0 || a.T == 0) return e;
+  EpiParams ep{};
+  ep.delta = a.delta; ep.per_token = 0; ep.row_scale = a.sx;
+  ep.ec = (a.ec != S3R_EC_NONE) && (a.out_dt == S3R_F32 || a.out_dt == S3R_F32_ACC);
+  ep.colsum = a.rW; ep.ec_row = a.ec_row; ep.ec_mean = a.ec_mean;
+  ep.S = 1; ep.B = 1;
+  ep.out = a.out; ep.ld_out = a.ld_out; ep.out_i32 = a.out_dt == S3R_I32_RAW;
+  if (ep.ec) {
+    float* part = (float*)(a.ws + L.part);
+    float* v = (float*)(a.ws + L.vec);
+    if (a.D > 0) {
+      // v_e = ebar_e . W_e for every group: gridDim.z = G
+      const int64_t nbands = (a.D + kGvRows - 1) / kGvRows;
+      dim3 grid((unsigned)((a.d_in + kGvCols - 1) / kGvCols), (unsigned)nbands, (unsigned)G);
+      hipLaunchKernelGGL(gemv_partial_kernel<1>, grid, dim3(kGvThreads), 0, st, a.W, a.ld_w, a.D, a.d_in, (int64_t)1,
+                         0, a.ec_col, (const float*)nullptr, (const float*)nullptr, (int64_t)1, part, w_stride,
+                         (const int64_t*)nullptr, (const int32_t*)nullptr, (int64_t)0);
+      const int64_t count = G * a.d_in;
+      int tpi = 1;
+      while (tpi < 16 && tpi * 8 < nbands) tpi *= 2;
+      hipLaunchKernelGGL(gemv_reduce_kernel, dim3((unsigned)((count * tpi + 255) / 256)), dim3(256), 0, st, part,
+                         nbands, count, tpi, v);
+    } else {
+      e = fill_zero(v, G * a.d_in, st);
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    ep.vec = v;
+  }
+  GemmParams g = make_gemm(a.Q, a.ld_q, a.W, a.ld_w, a.T, a.d_in, a.D);
+  GroupGemm gg{offsets, tab.tiles256, tab.order, tab.status, G, w_stride, 0, (int)(a.T / BM + G)};
+  if (a.out_dt == S3R_I32_RAW) return run_gemm<true, EPI_RAW, false, 1, GRP_DX>(g, ep, st, gg);
+  if (a.out_dt == S3R_F32_ACC)
+    return ep.ec ? run_gemm<true, EPI_DXA, true, 1, GRP_DX>(g, ep, st, gg)
+                 : run_gemm<true, EPI_DXA, false, 1, GRP_DX>(g, ep, st, gg);
+  return ep.ec ? run_gemm<true, EPI_DX, true, 1, GRP_DX>(g, ep, st, gg)
+               : run_gemm<true, EPI_DX, false, 1, GRP_DX>(g, ep, st, gg);
+}
+
+// dW_e = Q_e^T X_e of every group into out + e * out_stride (per-tensor steps).
+hipError_t launch_grouped_backward_dw(const DwArgs& a, int64_t G, const int64_t* offsets, int64_t out_stride,
+                                      uint32_t* flags, hipStream_t st) {
+  const GroupedBwLayout L = grouped_bw_layout(a.T, a.D, a.d_in, G, false, a.ec != 0);
+  const GroupTables tab = group_tables(a.ws + L.tables, G, offsets);
+  hipError_t e = launch_group_tables(tab, a.T, flags, st);
+  if (e != hipSuccess || a.d_in == 0 || a.D == 0) return e;
+  EpiParams ep{};
+  ep.delta = a.delta; ep.per_token = 0; ep.row_scale = a.sw;
+  ep.ec = (a.ec == S3R_EC_TWO_WAY || a.ec == S3R_EC_DW_ONLY) && a.out_dt == S3R_F32;
+  ep.colsum = a.xs; ep.ebar = a.ec_col; ep.ec_row = a.ec_row; ep.ec_mean = a.ec_mean;
+  ep.S = 1; ep.B = 1;
+  ep.out = a.out; ep.ld_out = a.ld_out; ep.out_i32 = a.out_dt == S3R_I32_RAW;
+  if (ep.ec) {
+    float* part = (float*)(a.ws + L.part);
+    float* u = (float*)(a.ws + L.vec);
+    const int64_t bands = a.T / kGvRows + G;
+    dim3 grid((unsigned)((a.d_in + kGvCols - 1) / kGvCols), (unsigned)bands, 1);
+    hipLaunchKernelGGL(gemv_partial_kernel<1>, grid, dim3(kGvThreads), 0, st, a.X, a.ld_x, a.T, a.d_in, (int64_t)1, 1,
+                       (const float*)nullptr, a.ec_row, a.ec_mean, (int64_t)1, part, (int64_t)0, offsets,
+                       (const int32_t*)tab.tiles64, G);
+    hipLaunchKernelGGL(grouped_band_reduce_kernel, dim3((unsigned)((G * a.d_in + 255) / 256)), dim3(256), 0, st, part,
+                       (const int32_t*)tab.tiles64, G, a.d_in, u);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    ep.u = u;
+  }
+  GemmParams g = make_gemm(a.Q, a.ld_q, a.X, a.ld_x, a.D, a.d_in, a.T);
+  GroupGemm gg{offsets, tab.tiles256, tab.order, tab.status, G, 0, out_stride, 0};
+  if (a.out_dt == S3R_I32_RAW) return run_gemm<false, EPI_RAW, false, 1, GRP_DW>(g, ep, st, gg);
+  return ep.ec ? run_gemm<false, EPI_DW, true, 1, GRP_DW>(g, ep, st, gg)
+               : run_gemm<false, EPI_DW, false, 1, GRP_DW>(g, ep, st, gg);
 }
 
 }  // namespace s3r

@@ -213,20 +213,42 @@ struct QuantTile {
 };
 
 // MODE: 0 RTNE, 1 SR, 2 S3R.  EC: accumulate rounding errors.  PT: per-token step.
-template <typename TIn, bool VEC, int MODE, bool EC, bool PT, bool COLSUM>
+// Grouped problems: rows sorted by group, per-group steps and statistics (the
+// group is the example), per-group column scales sw + e * D.
+struct GroupArgs {
+  const int64_t* offsets; const int32_t* tiles64; const uint32_t* amax; int64_t G;
+};
+
+template <typename TIn, bool VEC, int MODE, bool EC, bool PT, bool COLSUM, bool GR = false>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(
     QuantTile p, const TIn* __restrict__ G, const float* __restrict__ sx, const float* __restrict__ sw,
     int8_t* __restrict__ Q, float* __restrict__ delta_out, uint32_t* __restrict__ flags,
     const uint32_t* __restrict__ amax_part, int n_amax_part, const uint32_t* __restrict__ amax_rows,
     float* __restrict__ row_part, float* __restrict__ col_part, int32_t* __restrict__ colq_part,
-    uint32_t* __restrict__ fin_counter) {
+    uint32_t* __restrict__ fin_counter, GroupArgs gr) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int rtile = blockIdx.x;
   const int ctile = blockIdx.y;
-  const int64_t b = rtile / p.tiles_per_example;
-  const int64_t r0 = b * p.S + (int64_t)(rtile % p.tiles_per_example) * kRowsPerTile;
-  const int64_t r1 = min(r0 + kRowsPerTile, (b + 1) * p.S);
+  int64_t b, r0, r1;
+  bool first_tile;               // this row tile writes its group's (or the tensor's) step
+  if constexpr (GR) {
+    const int e = find_group(gr.tiles64, gr.G, rtile);
+    if (e < 0) return;           // past the last tile of the last group
+    b = e;
+    r0 = gr.offsets[e] + (int64_t)(rtile - gr.tiles64[e]) * kRowsPerTile;
+    r1 = min(r0 + kRowsPerTile, gr.offsets[e + 1]);
+    first_tile = rtile == gr.tiles64[e];
+    if (sw) sw += e * p.D;
+    amax_part = gr.amax + e;
+    n_amax_part = 1;
+    delta_out += e;
+  } else {
+    b = rtile / p.tiles_per_example;
+    r0 = b * p.S + (int64_t)(rtile % p.tiles_per_example) * kRowsPerTile;
+    r1 = min(r0 + kRowsPerTile, (b + 1) * p.S);
+    first_tile = rtile == 0;
+  }
   const int64_t j0 = (int64_t)ctile * kColsPerTile + lane * 8;
   if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *fin_counter = 0u;   // for the finalize kernel
 
@@ -253,7 +275,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
 #pragma unroll
     for (int w = 1; w < kThreads / kWave; ++w) m = m > s_red[w] ? m : s_red[w];
     st = make_step(m);
-    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+    if (first_tile && blockIdx.y == 0 && threadIdx.x == 0) {
       delta_out[0] = (m > 0x7F800000u) ? __uint_as_float(m) : st.delta;
       if (st.flag && flags) atomicOr(flags, st.flag);
     }
@@ -828,6 +850,129 @@ __global__ __launch_bounds__(kResThreads, 1) void quantize_resident_kernel(
   }
 }
 
+// --------------------------------------------------------- grouped path ----
+// Pass 1 of a grouped per-tensor quantizer: one block per 64-row tile of a
+// group (the same tiling as the code pass), all D columns; the tile's max of
+// |G'| (column scales of its group) goes to amax[e] with an integer atomic max
+// (order-free, so the result is deterministic).
+template <typename TIn, bool VEC>
+__global__ __launch_bounds__(kThreads) void grouped_amax_kernel(
+    const TIn* __restrict__ G, int64_t ld, int64_t D, const float* __restrict__ sx, const float* __restrict__ sw,
+    GroupArgs gr, uint32_t* __restrict__ amax) {
+  const int e = find_group(gr.tiles64, gr.G, blockIdx.x);
+  if (e < 0) return;
+  const int64_t r0 = gr.offsets[e] + (int64_t)(blockIdx.x - gr.tiles64[e]) * kRowsPerTile;
+  const int64_t r1 = min(r0 + kRowsPerTile, gr.offsets[e + 1]);
+  const float* swe = sw ? sw + e * D : nullptr;
+  const int64_t cpr = (D + 7) / 8;
+  uint32_t m = 0;
+  for (int64_t t0 = r0; t0 < r1; t0 += kAmaxRows) {
+    const bool rows_full = t0 + kAmaxRows <= r1;
+    for (int64_t c = threadIdx.x; c < cpr; c += kThreads) {
+      float v[kAmaxRows][8];
+      float s[8];
+      load8_scale(swe, c * 8, D, VEC, s);
+#pragma unroll
+      for (int u = 0; u < kAmaxRows; ++u) {
+        if (rows_full || t0 + u < r1) load8<TIn, VEC>(G + (t0 + u) * ld, c * 8, D, v[u]);
+        else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) v[u][i] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kAmaxRows; ++u) {
+        const float fx = (t0 + u < r1 && sx) ? sx[t0 + u] : 1.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t b = abs_bits((v[u][i] * fx) * s[i]);
+          m = m > b ? m : b;
+        }
+      }
+    }
+  }
+  __shared__ uint32_t red[kThreads / kWave];
+  m = wave_max_u32(m);
+  if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r = red[0];
+    for (int w = 1; w < kThreads / kWave; ++w) r = r > red[w] ? r : red[w];
+    if (r) atomicMax(&amax[e], r);
+  }
+}
+
+// The group of row t: offsets[e] <= t < offsets[e+1] (binary search; t < offsets[G]).
+__device__ __forceinline__ int row_group(const int64_t* __restrict__ offsets, int64_t G, int64_t t) {
+  int lo = 0, hi = (int)G;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (offsets[mid] <= t) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// Blocks [0, ncb): per-group channel means and code column sums, fixed-order
+// sums over the group's row tiles.  Blocks past ncb: token means eps_t (EC).
+__global__ __launch_bounds__(kThreads) void grouped_finalize_kernel(
+    int64_t D, int64_t R, int n_ctiles, int per_token, int ncb, GroupArgs gr, const float* __restrict__ delta,
+    const float* __restrict__ col_part, const int32_t* __restrict__ colq_part, const float* __restrict__ row_part,
+    float* __restrict__ ec_col, int32_t* __restrict__ code_colsum, float* __restrict__ ec_row) {
+  if ((int)blockIdx.x < ncb) {
+    const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (idx >= gr.G * D) return;
+    const int64_t e = idx / D, j = idx - e * D;
+    const int k0 = gr.tiles64[e], k1 = gr.tiles64[e + 1];
+    const int64_t n = gr.offsets[e + 1] - gr.offsets[e];
+    if (ec_col) {
+      double a = 0.0;
+      for (int k = k0; k < k1; ++k) a += (double)col_part[(int64_t)k * D + j];
+      const double d = per_token ? 1.0 : (double)delta[e];
+      ec_col[idx] = n > 0 ? (float)(a * d / (double)n) : 0.f;
+    }
+    if (code_colsum) {
+      int32_t a = 0;
+      for (int k = k0; k < k1; ++k) a += colq_part[(int64_t)k * D + j];
+      code_colsum[idx] = a;
+    }
+    return;
+  }
+  const int64_t t = (int64_t)(blockIdx.x - ncb) * kThreads + threadIdx.x;
+  if (t >= R) return;
+  const int e = row_group(gr.offsets, gr.G, t);
+  double a = 0.0;
+  for (int k = 0; k < n_ctiles; ++k) a += (double)row_part[t * n_ctiles + k];
+  const double d = per_token ? (double)delta[t] : (double)delta[e];
+  ec_row[t] = D > 0 ? (float)(a * d / (double)D) : 0.f;
+}
+
+// ec_mean[e]: mean of the group's token means, one block per group, fixed order.
+// Nothing is read when the offsets were found invalid.
+__global__ __launch_bounds__(kThreads) void grouped_mean_kernel(const int64_t* __restrict__ offsets,
+                                                                const uint32_t* __restrict__ status,
+                                                                const float* __restrict__ ec_row,
+                                                                float* __restrict__ ec_mean) {
+  const int64_t e = blockIdx.x;
+  const bool ok = status[0] == 0;
+  const int64_t a = ok ? offsets[e] : 0, b = ok ? offsets[e + 1] : 0;
+  double s = 0.0;
+  for (int64_t t = a + threadIdx.x; t < b; t += kThreads) s += (double)ec_row[t];
+  __shared__ double red[kThreads];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int o = kThreads / 2; o > 0; o >>= 1) {
+    if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) ec_mean[e] = b > a ? (float)(red[0] / (double)(b - a)) : 0.f;
+}
+
+// Steps of 1 for empty groups under a per-tensor step (no code tile writes them).
+__global__ void grouped_empty_steps_kernel(const int64_t* __restrict__ offsets, int64_t G, float* __restrict__ delta) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e < G && offsets[e + 1] == offsets[e]) delta[e] = 1.f;
+}
+
 // Degenerate shapes (T == 0 or D == 0): steps of 1, zero statistics.
 __global__ void empty_kernel(int64_t T, int64_t D, int64_t B, int per_token, float* delta,
                              float* ec_row, float* ec_col, float* ec_mean, int32_t* code_colsum) {
@@ -876,7 +1021,7 @@ void launch_q(const QuantArgs& a, const WsLayout& L, const QuantTile& p, dim3 gr
                      a.amax_in ? a.amax_in : (const uint32_t*)(a.ws + L.amax_part), a.amax_in ? 1 : kAmaxBlocks,
                      (const uint32_t*)(a.ws + L.amax_rows),
                      (float*)(a.ws + L.row_part), (float*)(a.ws + L.col_part), (int32_t*)(a.ws + L.colq_part),
-                     (uint32_t*)(a.ws + L.counter));
+                     (uint32_t*)(a.ws + L.counter), GroupArgs{});
 }
 
 template <typename TIn, bool VEC, int MODE, bool EC>
@@ -1007,7 +1152,110 @@ hipError_t run_resident(const QuantArgs& a, const WsLayout& L, int R, hipStream_
   }
 }
 
+struct GroupedWs { size_t tables, counter, amax_rows, row_part, col_part, colq_part, total; };
+
+GroupedWs grouped_ws(int64_t R, int64_t D, int64_t Gn, int ec, int scale, bool colsum) {
+  GroupedWs w{};
+  const int64_t n_rt = R / kRowsPerTile + Gn;                 // bound on the groups' 64-row tiles
+  const int64_t n_ct = (D + kColsPerTile - 1) / kColsPerTile;
+  size_t off = kWsHeaderBytes;
+  w.tables = off;    off = align_up(off + group_tables_bytes(Gn), 256);
+  w.counter = off;   off = align_up(off + 4, 256);
+  w.amax_rows = off; off = align_up(off + (scale == S3R_PER_TOKEN ? (size_t)R * 4 : 0), 256);
+  w.row_part = off;  off = align_up(off + (ec ? (size_t)R * n_ct * 4 : 0), 256);
+  w.col_part = off;  off = align_up(off + (ec ? (size_t)n_rt * D * 4 : 0), 256);
+  w.colq_part = off; off = align_up(off + (colsum ? (size_t)n_rt * D * 4 : 0), 256);
+  w.total = off;
+  return w;
+}
+
+template <typename TIn, bool VEC, int MODE, bool EC, bool PT, bool COLSUM>
+void launch_gq(const QuantArgs& a, const GroupedWs& L, const QuantTile& p, const GroupArgs& gr, dim3 grid,
+               hipStream_t st) {
+  hipLaunchKernelGGL((quantize_kernel<TIn, VEC, MODE, EC, PT, COLSUM, true>), grid, dim3(kThreads), 0, st, p,
+                     (const TIn*)a.G, a.sx, a.sw, a.Q, a.delta, a.flags, gr.amax, 1,
+                     (const uint32_t*)(a.ws + L.amax_rows), (float*)(a.ws + L.row_part), (float*)(a.ws + L.col_part),
+                     (int32_t*)(a.ws + L.colq_part), (uint32_t*)(a.ws + L.counter), gr);
+}
+
+template <typename TIn, bool VEC>
+void run_grouped(const QuantArgs& a, const GroupedWs& L, const GroupArgs& gr, const uint32_t* status,
+                 hipStream_t st) {
+  const TIn* G = (const TIn*)a.G;
+  const int64_t n_rt = a.T / kRowsPerTile + gr.G;
+  if (a.scale == S3R_PER_TENSOR) {
+    hipLaunchKernelGGL((grouped_amax_kernel<TIn, VEC>), dim3((unsigned)n_rt), dim3(kThreads), 0, st, G, a.ld_g, a.D,
+                       a.sx, a.sw, gr, (uint32_t*)gr.amax);
+    hipLaunchKernelGGL(grouped_empty_steps_kernel, dim3((unsigned)((gr.G + 255) / 256)), dim3(256), 0, st,
+                       gr.offsets, gr.G, a.delta);
+  } else {
+    const unsigned nb = (unsigned)((a.T + kThreads / kWave - 1) / (kThreads / kWave));
+    hipLaunchKernelGGL((amax_rows_kernel<TIn, VEC>), dim3(nb), dim3(kThreads), 0, st, G, a.ld_g, a.T, a.D,
+                       a.sx, a.sw, (uint32_t*)(a.ws + L.amax_rows), a.delta, a.flags);
+  }
+  QuantTile p{};
+  p.T = a.T; p.D = a.D; p.S = 1; p.ld_g = a.ld_g; p.ld_q = a.ld_q;
+  p.tiles_per_example = 1;
+  p.n_ctiles = (int)((a.D + kColsPerTile - 1) / kColsPerTile);
+  p.layer = a.layer; p.seed = a.seed;
+  p.stream_word = a.stream << 16;
+  p.bcast = 0;
+  dim3 grid((unsigned)n_rt, (unsigned)p.n_ctiles);
+  const bool cs = a.code_colsum != nullptr;
+  const bool pt = a.scale == S3R_PER_TOKEN;
+  switch (a.mode) {
+    case S3R_RTNE:
+      if (pt) { if (cs) launch_gq<TIn, VEC, 0, false, true, true>(a, L, p, gr, grid, st);
+                else launch_gq<TIn, VEC, 0, false, true, false>(a, L, p, gr, grid, st); }
+      else launch_gq<TIn, VEC, 0, false, false, false>(a, L, p, gr, grid, st);
+      break;
+    case S3R_SR: launch_gq<TIn, VEC, 1, false, false, false>(a, L, p, gr, grid, st); break;
+    default:
+      if (a.ec) launch_gq<TIn, VEC, 2, true, false, false>(a, L, p, gr, grid, st);
+      else launch_gq<TIn, VEC, 2, false, false, false>(a, L, p, gr, grid, st);
+  }
+  if (a.ec || cs) {
+    const int64_t ncb = (gr.G * a.D + kThreads - 1) / kThreads;
+    const int64_t nrb = a.ec ? (a.T + kThreads - 1) / kThreads : 0;
+    hipLaunchKernelGGL(grouped_finalize_kernel, dim3((unsigned)(ncb + nrb)), dim3(kThreads), 0, st, a.D, a.T,
+                       p.n_ctiles, pt ? 1 : 0, (int)ncb, gr, a.delta, (const float*)(a.ws + L.col_part),
+                       (const int32_t*)(a.ws + L.colq_part), (const float*)(a.ws + L.row_part),
+                       a.ec ? a.ec_col : nullptr, a.code_colsum, a.ec_row);
+    if (a.ec)
+      hipLaunchKernelGGL(grouped_mean_kernel, dim3((unsigned)gr.G), dim3(kThreads), 0, st, gr.offsets, status,
+                         a.ec_row, a.ec_mean);
+  }
+}
+
 }  // namespace
+
+size_t grouped_quant_workspace(int64_t R, int64_t D, int64_t Gn, int ec, int scale, bool colsum) {
+  return grouped_ws(R, D, Gn, ec, scale, colsum).total;
+}
+
+// Grouped quantizer: per-group per-tensor steps (or per-token steps), the
+// group as the correction's example, per-group column scales.  Supported:
+// RTNE / SR / S3R per tensor, S3R-EC, and RTNE per token with code column sums
+// (the forward operands' prep).
+hipError_t launch_grouped_quantize(const QuantArgs& a, int64_t Gn, const int64_t* offsets, hipStream_t st) {
+  const GroupedWs L = grouped_ws(a.T, a.D, Gn, a.ec, a.scale, a.code_colsum != nullptr);
+  const GroupTables tab = group_tables(a.ws + L.tables, Gn, offsets);
+  hipError_t e = launch_group_tables(tab, a.T, a.flags, st);
+  if (e != hipSuccess) return e;
+  GroupArgs gr{offsets, tab.tiles64, tab.amax, Gn};
+  if (a.D == 0) return hipSuccess;
+  const size_t es = a.g_dtype == S3R_BF16 ? 2 : 4;
+  const bool vec = aligned(a.G, 16) && (a.ld_g * (int64_t)es) % 16 == 0 && aligned(a.Q, 8) && a.ld_q % 8 == 0 &&
+                   (a.sw == nullptr || (aligned(a.sw, 16) && a.D % 4 == 0));
+  if (a.g_dtype == S3R_BF16) {
+    if (vec) run_grouped<uint16_t, true>(a, L, gr, tab.status, st);
+    else run_grouped<uint16_t, false>(a, L, gr, tab.status, st);
+  } else {
+    if (vec) run_grouped<float, true>(a, L, gr, tab.status, st);
+    else run_grouped<float, false>(a, L, gr, tab.status, st);
+  }
+  return hipGetLastError();
+}
 
 size_t quant_workspace(int64_t T, int64_t D, int64_t S, int ec, int scale, bool colsum) {
   return ws_layout(T, D, S, ec, scale, colsum).total;

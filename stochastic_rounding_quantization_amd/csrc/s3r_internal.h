@@ -101,6 +101,8 @@ struct QuantArgs {
 };
 size_t quant_workspace(int64_t T, int64_t D, int64_t S, int ec, int scale, bool colsum);
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t st);
+size_t grouped_quant_workspace(int64_t R, int64_t D, int64_t Gn, int ec, int scale, bool colsum);
+hipError_t launch_grouped_quantize(const QuantArgs& a, int64_t Gn, const int64_t* offsets, hipStream_t st);
 
 // Backward GEMMs (gemm.hip).
 struct DxArgs {
@@ -129,6 +131,12 @@ size_t dx_workspace(int64_t T, int64_t D, int64_t d_in, int64_t S, int ec);
 size_t dw_workspace(int64_t T, int64_t D, int64_t d_in, int64_t S, int ec, int per_token);
 hipError_t launch_backward_dx(const DxArgs& a, hipStream_t st);
 hipError_t launch_backward_dw(const DwArgs& a, hipStream_t st);
+size_t grouped_dx_workspace(int64_t R, int64_t D, int64_t d_in, int64_t G, int ec);
+size_t grouped_dw_workspace(int64_t R, int64_t D, int64_t d_in, int64_t G, int ec);
+hipError_t launch_grouped_backward_dx(const DxArgs& a, int64_t G, const int64_t* offsets, int64_t w_stride,
+                                      uint32_t* flags, hipStream_t st);
+hipError_t launch_grouped_backward_dw(const DwArgs& a, int64_t G, const int64_t* offsets, int64_t out_stride,
+                                     uint32_t* flags, hipStream_t st);
 
 // SwiGLU backward glue (swiglu.hip).
 hipError_t launch_swiglu_backward(int64_t T, int64_t F, const float* dH, int64_t ld_dh, const uint16_t* Ag,
@@ -142,6 +150,33 @@ hipError_t launch_swiglu_backward_amax(int64_t T, int64_t F, const float* dH, in
                                        char* ws, hipStream_t st);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Grouped problems (groups.hip): tables derived on the device from the group
+// offsets, in a workspace region of group_tables_bytes(G).  At most kMaxGroups groups.
+constexpr int64_t kMaxGroups = 4096;
+struct GroupTables {
+  const int64_t* offsets;   // [G+1] (caller's, device)
+  int64_t G;
+  int32_t* tiles64;         // [G+1] prefix sums of ceil(n_e / 64)
+  int32_t* tiles256;        // [G+1] prefix sums of ceil(n_e / 256)
+  int32_t* order;           // [G] groups by descending rows
+  uint32_t* status;         // [1] 0: offsets valid; 1: invalid (tables empty)
+  uint32_t* amax;           // [G] cleared; the grouped quantizer's per-group amax bits
+};
+size_t group_tables_bytes(int64_t G);
+GroupTables group_tables(char* base, int64_t G, const int64_t* offsets);
+hipError_t launch_group_tables(const GroupTables& t, int64_t R, uint32_t* flags, hipStream_t st);
+
+// The group e with tiles[e] <= i < tiles[e+1] (binary search), or -1 past the last tile.
+__device__ __forceinline__ int find_group(const int32_t* __restrict__ tiles, int64_t G, int64_t i) {
+  if (i >= tiles[G]) return -1;
+  int lo = 0, hi = (int)G;                 // tiles[lo] <= i < tiles[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (tiles[mid] <= i) lo = mid; else hi = mid;
+  }
+  return lo;
+}
 
 // Every workspace starts with a header of synchronization words shared by all
 // entry points (so one buffer may serve quantize and backward calls that do not

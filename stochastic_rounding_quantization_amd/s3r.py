@@ -25,11 +25,13 @@ S3R_F32, S3R_BF16, S3R_I32_RAW, S3R_F32_ACC = 0, 1, 2, 3
 RTNE, SR, S3R, S3R_BCAST = 0, 1, 2, 3
 EC_NONE, EC_DX_ONLY, EC_TWO_WAY, EC_DW_ONLY = 0, 1, 2, 3
 PER_TENSOR, PER_TOKEN = 0, 1
-FLAG_NONFINITE, FLAG_TINY_STEP, FLAG_SYNC_TIMEOUT = 1, 2, 4
+FLAG_NONFINITE, FLAG_TINY_STEP, FLAG_SYNC_TIMEOUT, FLAG_BAD_GROUPS = 1, 2, 4, 8
 
 EXPORTED = ["s3r_quantize_workspace", "s3r_quantize", "s3r_quantize_with_amax", "s3r_backward_dx",
             "s3r_backward_dw", "s3r_backward_workspace", "s3r_swiglu_backward", "s3r_swiglu_amax_workspace",
-            "s3r_swiglu_backward_amax", "s3r_time_next_gemm", "s3r_status_string", "s3r_version"]
+            "s3r_swiglu_backward_amax", "s3r_grouped_workspace", "s3r_grouped_quantize",
+            "s3r_grouped_backward_dx", "s3r_grouped_backward_dw", "s3r_time_next_gemm", "s3r_status_string",
+            "s3r_version"]
 
 
 class S3RError(RuntimeError):
@@ -82,6 +84,16 @@ def lib() -> ctypes.CDLL:
     L.s3r_swiglu_amax_workspace.restype = SZ
     L.s3r_swiglu_backward_amax.argtypes = [I64, I64, P, I64, P, P, I64, P, P, I64, P, P, P, P, P, SZ, P]
     L.s3r_swiglu_backward_amax.restype = ctypes.c_int
+    L.s3r_grouped_workspace.argtypes = [DP, I64, I64]
+    L.s3r_grouped_workspace.restype = SZ
+    L.s3r_grouped_quantize.argtypes = [DP, I64, P, P, I32, I64, P, P, P, I64, P, P, P, P, P, P, P, SZ, P]
+    L.s3r_grouped_quantize.restype = ctypes.c_int
+    L.s3r_grouped_backward_dx.argtypes = [DP, I64, P, P, I64, P, P, I64, I64, I64, P, P, P, P, P, P, I32, I64, P, P,
+                                          SZ, P]
+    L.s3r_grouped_backward_dx.restype = ctypes.c_int
+    L.s3r_grouped_backward_dw.argtypes = [DP, I64, P, P, I64, P, P, I64, I64, P, P, P, P, P, P, I32, I64, I64, P, P,
+                                          SZ, P]
+    L.s3r_grouped_backward_dw.restype = ctypes.c_int
     L.s3r_time_next_gemm.argtypes = [P, P]
     L.s3r_time_next_gemm.restype = ctypes.c_int
     L.s3r_status_string.argtypes = [ctypes.c_int]
@@ -221,6 +233,59 @@ def s3r_swiglu_backward_amax(dH, A_gate, A_up, G_gate, G_up, row_scale, col_scal
     if rc_only:
         return rc
     _check("s3r_swiglu_backward_amax", rc)
+
+
+def s3r_grouped_workspace(desc: QDesc, groups: int, d_in: int) -> int:
+    return lib().s3r_grouped_workspace(ctypes.byref(desc), groups, d_in)
+
+
+def _nbytes(ws):
+    return 0 if ws is None else ws.numel() * ws.element_size()
+
+
+def s3r_grouped_quantize(desc: QDesc, offsets, G, row_scale, col_scale, Q, delta, code_colsum=None, ec_row=None,
+                         ec_col=None, ec_mean=None, flags=None, ws=None, stream=None, *, rc_only=False):
+    """offsets: int64 device tensor [groups + 1]; col_scale [groups x D] (or None)."""
+    rc = lib().s3r_grouped_quantize(ctypes.byref(desc), offsets.numel() - 1, _ptr(offsets), _ptr(G),
+                                    _gdtype(G) if G is not None else S3R_F32, _ld(G, desc.cols), _ptr(row_scale),
+                                    _ptr(col_scale), _ptr(Q), _ld(Q, desc.cols), _ptr(delta), _ptr(code_colsum),
+                                    _ptr(ec_row), _ptr(ec_col), _ptr(ec_mean), _ptr(flags), _ptr(ws), _nbytes(ws),
+                                    _stream(stream))
+    if rc_only:
+        return rc
+    _check("s3r_grouped_quantize", rc)
+
+
+def s3r_grouped_backward_dx(desc: QDesc, offsets, Q, delta, Wq, s_x, r_W, ec_row, ec_col, ec_mean, dX, flags=None,
+                            ws=None, stream=None, *, accumulate=False, rc_only=False):
+    """Wq: int8 [groups x D x d_in] (3-D, rows with unit stride)."""
+    d_in = dX.shape[1]
+    if Wq.dim() != 3 or Wq.stride(2) != 1:
+        raise ValueError("expected Wq as [groups x D x d_in] with unit column stride")
+    rc = lib().s3r_grouped_backward_dx(ctypes.byref(desc), offsets.numel() - 1, _ptr(offsets), _ptr(Q),
+                                       _ld(Q, desc.cols), _ptr(delta), _ptr(Wq), Wq.stride(1), Wq.stride(0), d_in,
+                                       _ptr(s_x), _ptr(r_W), _ptr(ec_row), _ptr(ec_col), _ptr(ec_mean), _ptr(dX),
+                                       _odtype(dX, accumulate), _ld(dX, d_in), _ptr(flags), _ptr(ws), _nbytes(ws),
+                                       _stream(stream))
+    if rc_only:
+        return rc
+    _check("s3r_grouped_backward_dx", rc)
+
+
+def s3r_grouped_backward_dw(desc: QDesc, offsets, Q, delta, Xq, s_w, xs, ec_row, ec_col, ec_mean, dW, flags=None,
+                            ws=None, stream=None, *, rc_only=False):
+    """dW: float32 / int32 [groups x D x d_in] (3-D, unit column stride)."""
+    d_in = Xq.shape[1]
+    if dW.dim() != 3 or dW.stride(2) != 1:
+        raise ValueError("expected dW as [groups x D x d_in] with unit column stride")
+    rc = lib().s3r_grouped_backward_dw(ctypes.byref(desc), offsets.numel() - 1, _ptr(offsets), _ptr(Q),
+                                       _ld(Q, desc.cols), _ptr(delta), _ptr(Xq), _ld(Xq, d_in), d_in, _ptr(s_w),
+                                       _ptr(xs), _ptr(ec_row), _ptr(ec_col), _ptr(ec_mean), _ptr(dW), _odtype(dW),
+                                       dW.stride(1), dW.stride(0), _ptr(flags), _ptr(ws), _nbytes(ws),
+                                       _stream(stream))
+    if rc_only:
+        return rc
+    _check("s3r_grouped_backward_dw", rc)
 
 
 def swiglu_backward(dH, A_gate, A_up, stream=None):

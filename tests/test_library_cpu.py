@@ -7,6 +7,8 @@ import ctypes
 import os
 import re
 
+import numpy as np
+
 import pytest
 
 from stochastic_rounding_quantization_amd import s3r
@@ -150,6 +152,60 @@ def test_swiglu_amax_and_quantize_with_amax_argument_errors(L):
     assert qa(d, Q=None) == -1
     assert qa(s3r.qdesc(64, 96, 32, s3r.S3R, s3r.EC_TWO_WAY)) == -1               # statistics outputs missing
     assert qa(d, wsb=0) in (-3, -4, -5)                                           # workspace or no device
+
+
+class _FakeDev:
+    """Stands in for a device tensor in the binding's marshalling (never dereferenced on the host)."""
+
+    def __init__(self, shape, stride, addr=1 << 20, elem=1, dtype=None):
+        import torch
+        self._shape, self._stride, self._addr, self._elem = shape, stride, addr, elem
+        self.shape = shape
+        self.dtype = dtype or {1: torch.int8, 4: torch.float32, 8: torch.int64}[elem]
+
+    def data_ptr(self):
+        return self._addr
+
+    def dim(self):
+        return len(self._shape)
+
+    def stride(self, i=None):
+        return self._stride if i is None else self._stride[i]
+
+    def numel(self):
+        n = 1
+        for d in self._shape:
+            n *= d
+        return n
+
+    def element_size(self):
+        return self._elem
+
+
+def test_grouped_binding_marshals_valid_arguments(L):
+    # through the Python binding with consistent shapes, every check passes and (without a GPU)
+    # the call stops at the device check: the argument order matches the C declarations
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    R, D, d_in, E = 96, 64, 48, 4
+    desc = s3r.qdesc(R, D, 1, s3r.S3R, s3r.EC_TWO_WAY)
+    ws = _FakeDev((s3r.s3r_grouped_workspace(desc, E, d_in),), (1,), addr=1 << 24)
+    off = _FakeDev((E + 1,), (1,), elem=8)
+    f32 = lambda *shape: _FakeDev(shape, tuple(int(np.prod(shape[i + 1:])) for i in range(len(shape))), elem=4)
+    Q = _FakeDev((R, D), (D, 1))
+    st = (f32(R), f32(E, D), f32(E))
+    expect = (-4, -5)
+    assert s3r.s3r_grouped_quantize(desc, off, f32(R, D), f32(R), f32(E, D), Q, f32(E), None, *st, None, ws, 0,
+                                    rc_only=True) in expect
+    Wq = _FakeDev((E, D, d_in), (D * 48, 48, 1))
+    dX = f32(R, d_in)
+    assert s3r.s3r_grouped_backward_dx(desc, off, Q, f32(E), Wq, f32(R), f32(E, d_in), *st, dX, None, ws, 0,
+                                       rc_only=True) in expect
+    dW = f32(E, D, d_in)
+    Xq = _FakeDev((R, d_in), (48, 1))
+    assert s3r.s3r_grouped_backward_dw(desc, off, Q, f32(E), Xq, f32(E, D), f32(E, d_in), *st, dW, None, ws, 0,
+                                       rc_only=True) in expect
 
 
 def test_no_gpu_reports_hip_error(L):
