@@ -29,6 +29,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
@@ -187,6 +189,8 @@ def main():
     s3r.lib()   # fail loudly if the HIP library is missing
     if args.workload in inputs.BLOCKS:
         out = run_block(args, dev, torch, inputs, s3r)
+    elif args.workload in inputs.MOE:
+        out = run_moe(args, dev, torch, inputs, s3r)
     else:
         out = run_linear(args, dev, torch, inputs, s3r)
     print(json.dumps(out), flush=True)
@@ -331,6 +335,112 @@ def run_block(args, dev, torch, inputs, s3r):
         rows = S if args.cpu_rows < 0 else max(S, min(args.cpu_rows, T) // S * S)
         log(f"CPU oracle baseline on the first {rows} tokens")
         out["cpu_baseline"] = block_cpu_baseline(inp, b, mode, ec, rows)
+    return out
+
+
+def moe_cpu_baseline(inp, m, mode, ec, experts):
+    """Time the CPU oracle's grouped backward on a bounded sample: a few whole experts."""
+    from oracle import moe
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    fx, fws, xs = moe.forward_operands(inp["X"], inp["W"], "bf16", inp["offsets"])
+    t0 = time.perf_counter()
+    moe.grouped_backward(inp, mode=mode, ec=ec, fx=fx, fws=fws, xs=xs, experts=experts)
+    dt = time.perf_counter() - t0
+    rows = int(sum(inp["counts"][e] for e in experts))
+    ops = 2 * 2.0 * rows * m.d_model * m.d_ff
+    return {"value": ops / dt / 1e12, "unit": "TOP/s", "cores": int(blas_threads), "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": f"{len(experts)} experts ({rows} of {m.rows} rows), full d_model={m.d_model} and d_ff={m.d_ff}: "
+                      f"numpy quantizer (1 thread) + dX + dW with float64 BLAS integer GEMMs ({blas_threads} BLAS "
+                      f"threads); forward-operand prep untimed"}
+
+
+def run_moe(args, dev, torch, inputs, s3r):
+    """The MoE expert path: 64 experts' down projections over 32768 expert-sorted rows."""
+    mode, ec = MODES[args.mode]
+    m = inputs.MOE[args.workload]
+    R, E, M, F = m.rows, m.experts, m.d_model, m.d_ff
+    log(f"workload {m.name}: rows={R} experts={E} d_model={M} d_ff={F} mode={args.mode}; drawing inputs")
+    inp = inputs.make_moe_inputs(m)
+    off = torch.from_numpy(inp["offsets"]).to(dev)
+    flags = torch.zeros(1, dtype=torch.int32, device=dev)
+    log("forward-operand prep (untimed)")
+    X = _to_dev(torch, dev, inp["X"], "bf16")
+    xdesc = s3r.qdesc(R, F, 1, s3r.RTNE, s3r.EC_NONE, s3r.PER_TOKEN)
+    Xq = s3r.q_buffer(R, F, dev)
+    sx = torch.empty(R, device=dev)
+    xs = torch.empty(E, F, dtype=torch.int32, device=dev)
+    ws = torch.zeros(s3r.s3r_grouped_workspace(xdesc, E, F), dtype=torch.uint8, device=dev)
+    s3r.s3r_grouped_quantize(xdesc, off, X, None, None, Xq, sx, xs, flags=flags, ws=ws)
+    W = _to_dev(torch, dev, inp["W"].reshape(E * M, F), "bf16")
+    ld = (F + 15) // 16 * 16
+    wbuf = torch.empty(E * M, ld, dtype=torch.int8, device=dev)
+    wdesc = s3r.qdesc(E * M, F, M, s3r.RTNE, s3r.EC_NONE, s3r.PER_TOKEN)
+    sw = torch.empty(E * M, device=dev)
+    rW = torch.empty(E, F, dtype=torch.int32, device=dev)
+    wws = torch.zeros(max(s3r.s3r_quantize_workspace(wdesc), 1), dtype=torch.uint8, device=dev)
+    s3r.s3r_quantize(wdesc, W, None, None, wbuf[:, :F], sw, rW, ws=wws)
+    Wq = wbuf.view(E, M, ld)[:, :, :F]
+    del X, W, wws
+    G = _to_dev(torch, dev, inp["G"], "bf16")
+    desc = s3r.qdesc(R, M, 1, mode, ec, s3r.PER_TENSOR, layer_id=0, seed=0)
+    Q = s3r.q_buffer(R, M, dev)
+    delta = torch.empty(E, device=dev)
+    st = (torch.empty(R, device=dev), torch.empty(E, M, device=dev), torch.empty(E, device=dev)) if ec \
+        else (None, None, None)
+    ws = torch.zeros(s3r.s3r_grouped_workspace(desc, E, F), dtype=torch.uint8, device=dev)
+    dX = torch.empty(R, F, device=dev)
+    dW = torch.empty(E, M, F, device=dev)
+    tl = Timeline(torch, ["step", "quantize", "dx", "dw"], args.steps)
+
+    def step(ev):
+        if ev:
+            ev["step"][0].record()
+            ev["quantize"][0].record()
+        s3r.s3r_grouped_quantize(desc, off, G, sx, sw.view(E, M), Q, delta, None, *st, flags, ws)
+        if ev:
+            ev["quantize"][1].record()
+            s3r.s3r_time_next_gemm(*ev["dx"])
+        s3r.s3r_grouped_backward_dx(desc, off, Q, delta, Wq, sx, rW, *st, dX, flags, ws)
+        if ev:
+            s3r.s3r_time_next_gemm(*ev["dw"])
+        s3r.s3r_grouped_backward_dw(desc, off, Q, delta, Xq, sw.view(E, M), xs, *st, dW, flags, ws)
+        if ev:
+            ev["step"][1].record()
+
+    ms_step = _timed_steps(torch, step, tl, args.steps, args.warmup)
+    assert int(flags.item()) == 0
+    t_q, t_gx, t_gw = tl.avg_us("quantize"), tl.avg_us("dx"), tl.avg_us("dw")
+    gop = 2.0 * R * M * F / 1e9                     # each of the two grouped GEMMs
+    value = 2 * gop / (ms_step / 1e3) / 1e3
+    q_bytes = R * M * 3
+    counts = inp["counts"]
+    out = {
+        "metric": "S3R-EC backward TOPS (quant+INT8 dX/dW) & quantizer GB/s, % of MI355X peak",
+        "value": round(value, 2), "unit": "TOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "i8", "data": "synthetic",
+        "config": {"workload": m.name, "rows": R, "experts": E, "top_k": m.top_k, "tokens": m.tokens,
+                   "d_model": M, "d_ff": F, "expert_rows_max": int(counts.max()), "expert_rows_min": int(counts.min()),
+                   "mode": args.mode, "step_scale": "per-tensor per expert", "g_dtype": "bf16",
+                   "stages": "experts' down projections: grouped quantize, grouped dX, grouped dW"},
+        "frac_of_int8_peak": round(value / PEAK_INT8_TOPS, 4),
+        "quantizer": {"us": round(t_q, 2), "GB_s": round(q_bytes / (t_q / 1e6) / 1e9, 1),
+                      "frac_of_hbm_peak": round(q_bytes / (t_q / 1e6) / 1e9 / PEAK_HBM_GBS, 4),
+                      "algorithmic_bytes": q_bytes},
+        "kernels_us": {"quantize_call": round(t_q, 2), "gemm_dx": round(t_gx, 2), "gemm_dw": round(t_gw, 2),
+                       "step_events": round(tl.avg_us("step"), 2)},
+        "gemm_tops": {"dx": round(gop / (t_gx / 1e6) / 1e3, 1), "dw": round(gop / (t_gw / 1e6) / 1e3, 1)},
+        "roofline": _roofline({"dx": t_gx, "dw": t_gw}, m.name, gop),
+    }
+    if args.cpu_rows != 0:
+        experts = list(range(E))
+        log("CPU oracle baseline on every expert (the whole workload)")
+        out["cpu_baseline"] = moe_cpu_baseline(inp, m, mode, ec, experts)
     return out
 
 

@@ -723,16 +723,22 @@ hipError_t run_gemv(const int8_t* P, int64_t ld, int64_t K, int64_t N, int64_t n
 }
 
 // out[e][n] = sum over the 64-row bands k of group e (tiles[e] .. tiles[e+1]) of
-// part[k][n], in order, fp64; zero for an empty group.
+// part[k][n], fp64, zero for an empty group.  16 lanes share an output: each
+// adds every 16th band in order, then a fixed xor butterfly adds the lanes.
 __global__ __launch_bounds__(256) void grouped_band_reduce_kernel(const float* __restrict__ part,
                                                                   const int32_t* __restrict__ tiles, int64_t G,
                                                                   int64_t N, float* __restrict__ out) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= G * N) return;
-  const int64_t e = idx / N, n = idx - e * N;
+  constexpr int kLanes = 16;
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t idx = g / kLanes;
+  const int sub = (int)(g % kLanes);
+  const bool ok = idx < G * N;
+  const int64_t e = ok ? idx / N : 0, n = ok ? idx - e * N : 0;
+  const int k1 = ok ? tiles[e + 1] : 0;
   double a = 0.0;
-  for (int k = tiles[e]; k < tiles[e + 1]; ++k) a += (double)part[(int64_t)k * N + n];
-  out[idx] = (float)a;
+  for (int k = (ok ? tiles[e] : 0) + sub; k < k1; k += kLanes) a += (double)part[(int64_t)k * N + n];
+  for (int o = 1; o < kLanes; o <<= 1) a += __shfl_xor(a, o, 64);
+  if (ok && sub == 0) out[idx] = (float)a;
 }
 
 size_t gemv_part_bytes(int64_t K, int64_t N, int64_t nb) {
@@ -1116,7 +1122,8 @@ hipError_t launch_grouped_backward_dw(const DwArgs& a, int64_t G, const int64_t*
     hipLaunchKernelGGL(gemv_partial_kernel<1>, grid, dim3(kGvThreads), 0, st, a.X, a.ld_x, a.T, a.d_in, (int64_t)1, 1,
                        (const float*)nullptr, a.ec_row, a.ec_mean, (int64_t)1, part, (int64_t)0, offsets,
                        (const int32_t*)tab.tiles64, G);
-    hipLaunchKernelGGL(grouped_band_reduce_kernel, dim3((unsigned)((G * a.d_in + 255) / 256)), dim3(256), 0, st, part,
+    hipLaunchKernelGGL(grouped_band_reduce_kernel, dim3((unsigned)((G * a.d_in * 16 + 255) / 256)), dim3(256), 0, st,
+                       part,
                        (const int32_t*)tab.tiles64, G, a.d_in, u);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     ep.u = u;

@@ -851,9 +851,9 @@ __global__ __launch_bounds__(kResThreads, 1) void quantize_resident_kernel(
 }
 
 // --------------------------------------------------------- grouped path ----
-// Pass 1 of a grouped per-tensor quantizer: one block per 64-row tile of a
-// group (the same tiling as the code pass), all D columns; the tile's max of
-// |G'| (column scales of its group) goes to amax[e] with an integer atomic max
+// Pass 1 of a grouped per-tensor quantizer: one block per (64-row tile of a
+// group, 512 columns), the tiling of the code pass; the block's max of |G'|
+// (column scales of its group) goes to amax[e] with an integer atomic max
 // (order-free, so the result is deterministic).
 template <typename TIn, bool VEC>
 __global__ __launch_bounds__(kThreads) void grouped_amax_kernel(
@@ -861,28 +861,30 @@ __global__ __launch_bounds__(kThreads) void grouped_amax_kernel(
     GroupArgs gr, uint32_t* __restrict__ amax) {
   const int e = find_group(gr.tiles64, gr.G, blockIdx.x);
   if (e < 0) return;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int64_t r0 = gr.offsets[e] + (int64_t)(blockIdx.x - gr.tiles64[e]) * kRowsPerTile;
   const int64_t r1 = min(r0 + kRowsPerTile, gr.offsets[e + 1]);
-  const float* swe = sw ? sw + e * D : nullptr;
-  const int64_t cpr = (D + 7) / 8;
+  const int64_t j0 = (int64_t)blockIdx.y * kColsPerTile + lane * 8;
+  float s[8];
+  load8_scale(sw ? sw + e * D : nullptr, j0, D, VEC, s);
   uint32_t m = 0;
-  for (int64_t t0 = r0; t0 < r1; t0 += kAmaxRows) {
-    const bool rows_full = t0 + kAmaxRows <= r1;
-    for (int64_t c = threadIdx.x; c < cpr; c += kThreads) {
-      float v[kAmaxRows][8];
-      float s[8];
-      load8_scale(swe, c * 8, D, VEC, s);
+  constexpr int kU = 4;
+  if (j0 < D) {
+    for (int64_t tb = r0 + wave; tb < r1; tb += (kThreads / kWave) * kU) {
+      float v[kU][8];
 #pragma unroll
-      for (int u = 0; u < kAmaxRows; ++u) {
-        if (rows_full || t0 + u < r1) load8<TIn, VEC>(G + (t0 + u) * ld, c * 8, D, v[u]);
+      for (int u = 0; u < kU; ++u) {
+        const int64_t t = tb + (int64_t)u * (kThreads / kWave);
+        if (t < r1) load8<TIn, VEC>(G + t * ld, j0, D, v[u]);
         else {
 #pragma unroll
           for (int i = 0; i < 8; ++i) v[u][i] = 0.f;
         }
       }
 #pragma unroll
-      for (int u = 0; u < kAmaxRows; ++u) {
-        const float fx = (t0 + u < r1 && sx) ? sx[t0 + u] : 1.f;
+      for (int u = 0; u < kU; ++u) {
+        const int64_t t = tb + (int64_t)u * (kThreads / kWave);
+        const float fx = (t < r1 && sx) ? sx[t] : 1.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const uint32_t b = abs_bits((v[u][i] * fx) * s[i]);
@@ -893,7 +895,7 @@ __global__ __launch_bounds__(kThreads) void grouped_amax_kernel(
   }
   __shared__ uint32_t red[kThreads / kWave];
   m = wave_max_u32(m);
-  if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = m;
+  if (lane == 0) red[wave] = m;
   __syncthreads();
   if (threadIdx.x == 0) {
     uint32_t r = red[0];
@@ -912,29 +914,40 @@ __device__ __forceinline__ int row_group(const int64_t* __restrict__ offsets, in
   return lo;
 }
 
-// Blocks [0, ncb): per-group channel means and code column sums, fixed-order
-// sums over the group's row tiles.  Blocks past ncb: token means eps_t (EC).
+// Blocks [0, ncb): per-group channel means and code column sums; kFinLanes
+// lanes share an item, each adding every kFinLanes-th row tile of the group in
+// order, then a fixed xor butterfly adds the lanes (a long group's sum is not
+// one serial chain).  Blocks past ncb: token means eps_t (EC).
+constexpr int kFinLanes = 16;
+
 __global__ __launch_bounds__(kThreads) void grouped_finalize_kernel(
     int64_t D, int64_t R, int n_ctiles, int per_token, int ncb, GroupArgs gr, const float* __restrict__ delta,
     const float* __restrict__ col_part, const int32_t* __restrict__ colq_part, const float* __restrict__ row_part,
     float* __restrict__ ec_col, int32_t* __restrict__ code_colsum, float* __restrict__ ec_row) {
   if ((int)blockIdx.x < ncb) {
-    const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (idx >= gr.G * D) return;
-    const int64_t e = idx / D, j = idx - e * D;
-    const int k0 = gr.tiles64[e], k1 = gr.tiles64[e + 1];
+    const int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int64_t idx = g / kFinLanes;
+    const int sub = (int)(g % kFinLanes);
+    const bool ok = idx < gr.G * D;            // the item count is uniform over a lane group
+    const int64_t e = ok ? idx / D : 0, j = ok ? idx - e * D : 0;
+    const int k0 = ok ? gr.tiles64[e] : 0, k1 = ok ? gr.tiles64[e + 1] : 0;
+    double a = 0.0;
+    int32_t aq = 0;
+    for (int k = k0 + sub; k < k1; k += kFinLanes) {
+      if (ec_col) a += (double)col_part[(int64_t)k * D + j];
+      if (code_colsum) aq += colq_part[(int64_t)k * D + j];
+    }
+    for (int o = 1; o < kFinLanes; o <<= 1) {
+      a += __shfl_xor(a, o, kWave);
+      aq += __shfl_xor(aq, o, kWave);
+    }
+    if (!ok || sub != 0) return;
     const int64_t n = gr.offsets[e + 1] - gr.offsets[e];
     if (ec_col) {
-      double a = 0.0;
-      for (int k = k0; k < k1; ++k) a += (double)col_part[(int64_t)k * D + j];
       const double d = per_token ? 1.0 : (double)delta[e];
       ec_col[idx] = n > 0 ? (float)(a * d / (double)n) : 0.f;
     }
-    if (code_colsum) {
-      int32_t a = 0;
-      for (int k = k0; k < k1; ++k) a += colq_part[(int64_t)k * D + j];
-      code_colsum[idx] = a;
-    }
+    if (code_colsum) code_colsum[idx] = aq;
     return;
   }
   const int64_t t = (int64_t)(blockIdx.x - ncb) * kThreads + threadIdx.x;
@@ -1184,8 +1197,9 @@ void run_grouped(const QuantArgs& a, const GroupedWs& L, const GroupArgs& gr, co
   const TIn* G = (const TIn*)a.G;
   const int64_t n_rt = a.T / kRowsPerTile + gr.G;
   if (a.scale == S3R_PER_TENSOR) {
-    hipLaunchKernelGGL((grouped_amax_kernel<TIn, VEC>), dim3((unsigned)n_rt), dim3(kThreads), 0, st, G, a.ld_g, a.D,
-                       a.sx, a.sw, gr, (uint32_t*)gr.amax);
+    hipLaunchKernelGGL((grouped_amax_kernel<TIn, VEC>),
+                       dim3((unsigned)n_rt, (unsigned)((a.D + kColsPerTile - 1) / kColsPerTile)), dim3(kThreads), 0,
+                       st, G, a.ld_g, a.D, a.sx, a.sw, gr, (uint32_t*)gr.amax);
     hipLaunchKernelGGL(grouped_empty_steps_kernel, dim3((unsigned)((gr.G + 255) / 256)), dim3(256), 0, st,
                        gr.offsets, gr.G, a.delta);
   } else {
@@ -1215,7 +1229,7 @@ void run_grouped(const QuantArgs& a, const GroupedWs& L, const GroupArgs& gr, co
       else launch_gq<TIn, VEC, 2, false, false, false>(a, L, p, gr, grid, st);
   }
   if (a.ec || cs) {
-    const int64_t ncb = (gr.G * a.D + kThreads - 1) / kThreads;
+    const int64_t ncb = (gr.G * a.D * kFinLanes + kThreads - 1) / kThreads;
     const int64_t nrb = a.ec ? (a.T + kThreads - 1) / kThreads : 0;
     hipLaunchKernelGGL(grouped_finalize_kernel, dim3((unsigned)(ncb + nrb)), dim3(kThreads), 0, st, a.D, a.T,
                        p.n_ctiles, pt ? 1 : 0, (int)ncb, gr, a.delta, (const float*)(a.ws + L.col_part),
