@@ -288,9 +288,112 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
 #pragma unroll
   for (int i = 0; i < 8; ++i) { col[i] = 0.f; colq[i] = 0; }
 
+  // Fast path (contiguous bf16 G, a full 64-row tile, 8 columns in range, per-tensor step):
+  // all 16 rows of this wave (t = r0 + wave + 4k) are loaded up front as raw bf16, 16 loads in
+  // flight, and coded as they arrive; the 16 row sums of the errors are one reduce-scatter
+  // across the wave at the end.
+  bool done = false;
+  if constexpr (sizeof(TIn) == 2 && VEC && !PT && !COLSUM) {
+    constexpr int kWR = kRowsPerTile / (kThreads / kWave);   // 16 rows per wave
+    if (r1 - r0 == kRowsPerTile && j0 + 8 <= p.D && (MODE != 1 || (p.D & 3) == 0)) {
+      done = true;
+      uint4 raw[kWR];
+#pragma unroll
+      for (int k = 0; k < kWR; ++k)
+        raw[k] = *reinterpret_cast<const uint4*>(G + (r0 + wave + 4 * k) * p.ld_g + j0);
+      float rsum[kWR];
+#pragma unroll
+      for (int k = 0; k < kWR; ++k) {
+        const int64_t t = r0 + wave + 4 * k;
+        const float fx = sx ? sx[t] : 1.f;
+        float v[8];
+        const uint32_t w[4] = {raw[k].x, raw[k].y, raw[k].z, raw[k].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v[2 * i] = __uint_as_float(w[i] << 16);
+          v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+        }
+        int q[8];
+        float es = 0.f;
+        if (st.flag) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) q[i] = 0;
+        } else if constexpr (MODE == 0) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float x = ((v[i] * fx) * sw8[i]) * st.inv;
+            q[i] = (int)fminf(fmaxf(__builtin_rintf(x), -127.f), 127.f);
+            if constexpr (EC) {
+              const float e = (float)q[i] - x;
+              es += e;
+              col[i] += e;
+            }
+          }
+        } else {
+          int32_t R[8];
+          if constexpr (MODE == 2) {
+            const int32_t rt = s_thr[t - r0];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) R[i] = rt;
+          } else {
+            const uint64_t blk = ((uint64_t)t * (uint64_t)p.D + (uint64_t)j0) >> 2;   // D % 4 == 0 here
+            const U4 w0 = philox4x32_10((uint32_t)blk, (uint32_t)(blk >> 32), p.layer, kTagSR + p.stream_word,
+                                        (uint32_t)p.seed, (uint32_t)(p.seed >> 32));
+            const U4 w1 = philox4x32_10((uint32_t)(blk + 1), (uint32_t)((blk + 1) >> 32), p.layer,
+                                        kTagSR + p.stream_word, (uint32_t)p.seed, (uint32_t)(p.seed >> 32));
+            R[0] = sr_units24(w0.x); R[1] = sr_units24(w0.y); R[2] = sr_units24(w0.z); R[3] = sr_units24(w0.w);
+            R[4] = sr_units24(w1.x); R[5] = sr_units24(w1.y); R[6] = sr_units24(w1.z); R[7] = sr_units24(w1.w);
+          }
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float x24 = ((v[i] * fx) * sw8[i]) * st.inv24;
+            int32_t X;
+            asm("v_cvt_flr_i32_f32 %0, %1" : "=v"(X) : "v"(x24));   // floor; x24 is finite here
+            X = min(max(X, -(127 << 24)), 127 << 24);
+            q[i] = (X + R[i]) >> 24;
+            if constexpr (EC) {
+              const float e = fmaf(x24, -0x1p-24f, (float)q[i]);
+              es += e;
+              col[i] += e;
+            }
+          }
+        }
+        rsum[k] = es;
+        store8<true>(Q + t * p.ld_q, j0, p.D, q);
+      }
+      if constexpr (EC) {
+        // reduce-scatter of the 16 row sums: afterwards lane l holds row k = l >> 2
+        float r8[8], r4[4], r2[2], r1s;
+        const bool hi32 = lane & 32, hi16 = lane & 16, hi8 = lane & 8, hi4 = lane & 4;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float send = hi32 ? rsum[i] : rsum[i + 8];
+          r8[i] = (hi32 ? rsum[i + 8] : rsum[i]) + __shfl_xor(send, 32, kWave);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float send = hi16 ? r8[i] : r8[i + 4];
+          r4[i] = (hi16 ? r8[i + 4] : r8[i]) + __shfl_xor(send, 16, kWave);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const float send = hi8 ? r4[i] : r4[i + 2];
+          r2[i] = (hi8 ? r4[i + 2] : r4[i]) + __shfl_xor(send, 8, kWave);
+        }
+        {
+          const float send = hi4 ? r2[0] : r2[1];
+          r1s = (hi4 ? r2[1] : r2[0]) + __shfl_xor(send, 4, kWave);
+        }
+        r1s += __shfl_xor(r1s, 2, kWave);
+        r1s += __shfl_xor(r1s, 1, kWave);
+        if ((lane & 3) == 0) row_part[(r0 + wave + 4 * (lane >> 2)) * p.n_ctiles + ctile] = r1s;
+      }
+    }
+  }
+
   // rows t = r0 + wave + 4u: kUnroll rows' loads are issued before any is used
   constexpr int kUnroll = 4;
-  for (int64_t tb = r0 + wave; tb < r1; tb += (kThreads / kWave) * kUnroll) {
+  for (int64_t tb = r0 + wave; tb < r1 && !done; tb += (kThreads / kWave) * kUnroll) {
   float vb[kUnroll][8];
   if (VEC && tb + (kThreads / kWave) * (kUnroll - 1) < r1 && j0 + 8 <= p.D) {
 #pragma unroll
