@@ -519,6 +519,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
 // eps; the last row block to finish (counter reset to 0 by the quantize kernel)
 // adds the block sums of each example in order to get its grand mean mu_b.
 constexpr int kFinRows = 256;
+constexpr int kColLanes = 8;
 
 __global__ __launch_bounds__(kThreads) void finalize_kernel(
     int64_t B, int64_t D, int64_t S, int tiles_per_example, int n_ctiles, int per_token, int ncb,
@@ -527,20 +528,30 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(
     int32_t* __restrict__ code_colsum, float* __restrict__ ec_row, float* __restrict__ ec_mean,
     double* __restrict__ blk_sum, uint32_t* __restrict__ counter) {
   if ((int)blockIdx.x < ncb) {
-    const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (idx >= B * D) return;
-    const int64_t b = idx / D, j = idx % D;
+    // kColLanes lanes share an item: each adds every kColLanes-th row tile of the example in
+    // order, then a fixed xor butterfly adds the lanes
+    const int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int64_t idx = g / kColLanes;
+    const int sub = (int)(g % kColLanes);
+    const bool ok = idx < B * D;                 // uniform over a lane group
+    const int64_t b = ok ? idx / D : 0, j = ok ? idx % D : 0;
+    double a = 0.0;
+    int32_t aq = 0;
+    for (int k = sub; k < tiles_per_example; k += kColLanes) {
+      const int64_t at = (b * tiles_per_example + k) * D + j;
+      if (ec_col) a += (double)col_part[at];
+      if (code_colsum) aq += colq_part[at];
+    }
+    for (int o = 1; o < kColLanes; o <<= 1) {
+      a += __shfl_xor(a, o, kWave);
+      aq += __shfl_xor(aq, o, kWave);
+    }
+    if (!ok || sub != 0) return;
     if (ec_col) {
-      double a = 0.0;
-      for (int k = 0; k < tiles_per_example; ++k) a += (double)col_part[(b * tiles_per_example + k) * D + j];
       const double d = per_token ? 1.0 : (double)delta[0];
       ec_col[idx] = (float)(a * d / (double)S);
     }
-    if (code_colsum) {
-      int32_t a = 0;
-      for (int k = 0; k < tiles_per_example; ++k) a += colq_part[(b * tiles_per_example + k) * D + j];
-      code_colsum[idx] = a;
-    }
+    if (code_colsum) code_colsum[idx] = aq;
     return;
   }
   // row block rb covers rows [b*S + k*256, min(b*S + (k+1)*256, (b+1)*S)) of example b
@@ -1186,7 +1197,7 @@ void run_quantize(const QuantArgs& a, const WsLayout& L, hipStream_t st) {
   dim3 grid((unsigned)(B * p.tiles_per_example), (unsigned)p.n_ctiles);
   dispatch_mode<TIn, VEC>(a, L, p, grid, st);
   if (a.ec || a.code_colsum) {
-    const int64_t ncb = (B * a.D + kThreads - 1) / kThreads;
+    const int64_t ncb = (B * a.D * kColLanes + kThreads - 1) / kThreads;
     const int bpe = (int)((a.S + kFinRows - 1) / kFinRows);
     const int64_t nrb = a.ec ? B * bpe : 0;
     hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)(ncb + nrb)), dim3(kThreads), 0, st, B, a.D, a.S,
