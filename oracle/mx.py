@@ -141,8 +141,16 @@ def pack(codes: np.ndarray) -> np.ndarray:
 
 
 def backward(G, X, W, *, mode: int, ec: int, rows_per_example: int, seed: int = 0, layer_id: int = 0,
-             stream: int = 0, dx_rows=None, dw_rows=None) -> dict:
-    """The MXFP4 quantized backward of one linear layer (fp32 inputs G [T x D], X [T x d_in], W [D x d_in])."""
+             stream: int = 0, dx_rows=None, dw_rows=None, cols=None) -> dict:
+    """The MXFP4 quantized backward of one linear layer (fp32 inputs G [T x D], X [T x d_in], W [D x d_in]).
+
+    dx_rows / dw_rows select rows of dX / dW, cols the columns (inputs) of both:
+    W's blocks run along D and X's along T, so a column of either is quantized
+    on its own and the selection changes no value.
+    """
+    if cols is not None:
+        cols = np.asarray(cols)
+        X, W = np.asarray(X)[:, cols], np.asarray(W)[:, cols]
     G = np.asarray(G, F32)
     T, D = G.shape
     S = rows_per_example

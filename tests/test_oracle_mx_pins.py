@@ -135,3 +135,18 @@ def test_mx_thresholds_are_the_int8_paths():
 def test_pack_low_nibble_first():
     c = np.array([[1, 2, 15, 8]], np.uint8)
     np.testing.assert_array_equal(mx.pack(c), np.array([[0x21, 0x8F]], np.uint8))
+
+
+def test_mx_backward_selection_changes_no_value():
+    # selecting rows of dX / dW and columns of both equals slicing the full result
+    rng = np.random.default_rng(8)
+    T, D, K, S = 64, 64, 48, 32
+    G = (rng.standard_t(3, (T, D)) * 1e-3).astype(np.float32)
+    X = rng.standard_normal((T, K)).astype(np.float32)
+    W = (0.02 * rng.standard_normal((D, K))).astype(np.float32)
+    full = mx.backward(G, X, W, mode=oq.SR, ec=oq.EC_TWO_WAY, rows_per_example=S, seed=1)
+    rows, cr, cols = np.array([0, 33, 63]), np.array([5, 40]), np.array([1, 17, 47])
+    part = mx.backward(G, X, W, mode=oq.SR, ec=oq.EC_TWO_WAY, rows_per_example=S, seed=1, dx_rows=rows,
+                       dw_rows=cr, cols=cols)
+    np.testing.assert_allclose(part["dX"], full["dX"][np.ix_(rows, cols)], rtol=1e-13, atol=1e-18)
+    np.testing.assert_allclose(part["dW"], full["dW"][np.ix_(cr, cols)], rtol=1e-13, atol=1e-18)
