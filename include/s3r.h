@@ -340,10 +340,100 @@ int s3r_swiglu_backward_amax(int64_t T, int64_t F, const float* dH, int64_t ld_d
                              const float* row_scale, const float* col_scale_gate, const float* col_scale_up,
                              uint32_t* amax_bits, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* ---- MXFP4 variant ------------------------------------------------------
+ * The 4-bit setting the S3R page names as the one where deterministic
+ * rounding of the backward fails (Introduction; Related Work, on NVFP4 /
+ * MXFP4 training recipes).  The page fixes none of the 4-bit arithmetic; the
+ * readings (OCP microscaling MXFP4 with the page's rounding carried over):
+ *   codes    E2M1 (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6; code = sign << 3 |
+ *            index), two per byte, the first element in the low nibble;
+ *   scales   one E8M0 byte per 32 consecutive elements along a GEMM's
+ *            contraction: 2^k with k the smallest integer such that
+ *            max|block| <= 6 * 2^k (nothing saturates), clamped to
+ *            [-127, 127]; an all-zero block has k = -127; a block with a
+ *            non-finite element gets byte 255 (NaN), zero codes and
+ *            S3R_FLAG_NONFINITE;
+ *   rounding y = g / 2^k onto the grid with spacing s (0.5 below |y| 2, 1
+ *            below 4, 2 up to 6): RTNE s * rint(y / s); SR and S3R the exact
+ *            floor s * floor(y / s + r) with the thresholds of s3r_quantize
+ *            (same Philox counters, same element and token indices);
+ *   layout   every GEMM operand is K-major: G is quantized twice, Q_h [T x D]
+ *            blocked along D (the dX operand) and Q_t [D x T] = G^T blocked
+ *            along T (the dW operand), both with the same thresholds; the
+ *            forward operands are stored transposed (Wt [d_in x D] from W
+ *            [D x d_in], Xt [d_in x T] from X [T x d_in]), RTNE;
+ *   EC       S3R-EC per quantization on E = dequant(Q) - G, with the INT8
+ *            path's statistics (eps_t, ebar_b, mu_b) and projection, all in
+ *            dequantized units (no per-token / per-channel scale folding: the
+ *            block scales take its place).
+ * Shapes: T, D and rows_per_example multiples of 128 (a 128-element step of
+ * the FP4 matrix cores), T, D < 2^24; scale must be S3R_PER_TENSOR (it names
+ * no scale here); mode RTNE, SR or S3R; ec requires S3R.  Byte leading
+ * dimensions (ld_*) of codes are multiples of 16 with 16-byte aligned bases
+ * (Q_h: a multiple of 4); of scales, multiples of 4 (operand rows are read
+ * as 4-byte words).  Device pointers throughout, row-major.
+ */
+
+/* s3r_mx_workspace: bytes of ws for s3r_mx_quantize and both backward calls
+ * (256-byte aligned; no initial contents required). */
+size_t s3r_mx_workspace(const s3r_qdesc* desc, int64_t d_in);
+size_t s3r_mx_operand_workspace(int64_t rows, int64_t cols);
+
+/* s3r_mx_operand: the forward operand M [rows x cols] (f32 or bf16, ld
+ * elements) to RTNE MXFP4 blocked along the rows, stored transposed: Mt
+ * [cols x rows/2] codes (ld_t bytes), Mt_scales [cols x rows/32] (ld_ts).
+ * W [D x d_in] gives Wt for dX, X [T x d_in] gives Xt for dW.  colsum
+ * (optional, f32 [rows/rows_per_example x cols]): per-group column sums of the
+ * dequantized operand in groups of rows_per_example rows (a multiple of 128
+ * dividing rows) -- r_W with rows_per_example = D, xs_b with the examples'
+ * length.  rows a multiple of 128. */
+int s3r_mx_operand(int64_t rows, int64_t cols, int64_t rows_per_example,
+                   const void* M, int32_t dtype, int64_t ld,
+                   uint8_t* Mt, int64_t ld_t, uint8_t* Mt_scales, int64_t ld_ts,
+                   float* colsum, uint32_t* flags, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* s3r_mx_quantize: G [T x D] (f32 or bf16) to Q_h (codes [T x D/2], scales
+ * [T x D/32]) and Q_t (codes [D x T/2], scales [D x T/32]).  With EC: the
+ * statistics of each quantization's error, ec_row_* [T] (eps_t), ec_col_*
+ * [B x D] (ebar_b), ec_mean_* [B] (mu_b); all six pointers given exactly when
+ * desc->ec != S3R_EC_NONE.  Both quantizations are written whatever the
+ * variant. */
+int s3r_mx_quantize(const s3r_qdesc* desc, const void* G, int32_t g_dtype, int64_t ld_g,
+                    uint8_t* Qh, int64_t ld_qh, uint8_t* Qh_scales, int64_t ld_qhs,
+                    uint8_t* Qt, int64_t ld_qt, uint8_t* Qt_scales, int64_t ld_qts,
+                    float* ec_row_h, float* ec_col_h, float* ec_mean_h,
+                    float* ec_row_t, float* ec_col_t, float* ec_mean_t,
+                    uint32_t* flags, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* s3r_mx_backward_dx: dX [T x d_in] f32 = dq(Q_h) dq(W) - v_b - (eps_t - mu_b) r_W
+ * with v_b = ebar_b dq(W) (S3R page, "Structured Error Correction": the
+ * projection's two terms); the correction only with ec DX_ONLY or TWO_WAY,
+ * which need r_W [d_in] (s3r_mx_operand's colsum of W with rows_per_example
+ * = D) and the _h statistics.  fp32 accumulation in the matrix cores. */
+int s3r_mx_backward_dx(const s3r_qdesc* desc, const uint8_t* Qh, int64_t ld_qh,
+                       const uint8_t* Qh_scales, int64_t ld_qhs,
+                       const uint8_t* Wt, int64_t ld_wt, const uint8_t* Wt_scales, int64_t ld_wts,
+                       int64_t d_in, const float* r_W,
+                       const float* ec_row_h, const float* ec_col_h, const float* ec_mean_h,
+                       float* dX, int64_t ld_dx, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* s3r_mx_backward_dw: dW [D x d_in] f32 = dq(G)^T dq(X), from Q_t and Xt,
+ * minus sum_b ebar'_b xs_b^T and 1 u'^T with u' = sum_t (eps'_t - mu'_b)
+ * dq(X)[t,:] (the _t statistics); the correction only with ec TWO_WAY or
+ * DW_ONLY, which need xs [B x d_in] (s3r_mx_operand's colsum of X with the
+ * examples' length) and B = T / rows_per_example <= 8. */
+int s3r_mx_backward_dw(const s3r_qdesc* desc, const uint8_t* Qt, int64_t ld_qt,
+                       const uint8_t* Qt_scales, int64_t ld_qts,
+                       const uint8_t* Xt, int64_t ld_xt, const uint8_t* Xt_scales, int64_t ld_xts,
+                       int64_t d_in, const float* xs,
+                       const float* ec_row_t, const float* ec_col_t, const float* ec_mean_t,
+                       float* dW, int64_t ld_dw, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* ---- measurement aid --------------------------------------------------
  * s3r_time_next_gemm: record `start` immediately before and `stop` immediately
- * after the INT8 GEMM kernel launched by the next s3r_backward_dx /
- * s3r_backward_dw call made on this host thread (on that call's stream), so
+ * after the GEMM kernel launched by the next s3r_backward_dx / s3r_backward_dw
+ * (INT8) or s3r_mx_backward_dx / s3r_mx_backward_dw (FP4) call made on this
+ * host thread (on that call's stream), so
  * hipEventElapsedTime gives that one kernel's duration.  Thread-local; the
  * request is consumed by that call.  Pass NULLs to cancel.  Returns S3R_OK. */
 int s3r_time_next_gemm(hipEvent_t start, hipEvent_t stop);

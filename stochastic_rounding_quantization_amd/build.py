@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libs3r.so")
-SOURCES = ["capi.hip", "quantize.hip", "gemm.hip", "swiglu.hip", "groups.hip"]
+SOURCES = ["capi.hip", "quantize.hip", "gemm.hip", "swiglu.hip", "groups.hip", "mx.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -342,6 +342,130 @@ int s3r_grouped_backward_dw(const s3r_qdesc* d, int64_t groups, const int64_t* o
   return finish(launch_grouped_backward_dw(a, groups, offsets, dw_group_stride, flags, stream));
 }
 
+// ---- MXFP4 variant
+static bool mul_of(int64_t x, int64_t m) { return x >= 0 && x % m == 0; }
+static int check_mx_desc(const s3r_qdesc* d) {
+  int rc = check_desc(d);
+  if (rc) return rc;
+  if (d->scale != S3R_PER_TENSOR || d->mode == S3R_S3R_BCAST) return S3R_ERR_UNSUPPORTED;
+  if (d->ec != S3R_EC_NONE && d->mode != S3R_S3R) return S3R_ERR_UNSUPPORTED;
+  if (!mul_of(d->rows, 128) || !mul_of(d->cols, 128) || !mul_of(d->rows_per_example, 128)) return S3R_ERR_INVALID_ARG;
+  if (d->rows == 0 || d->cols == 0 || d->rows >= ((int64_t)1 << 24) || d->cols >= ((int64_t)1 << 24))
+    return S3R_ERR_INVALID_ARG;
+  return S3R_OK;
+}
+
+size_t s3r_mx_operand_workspace(int64_t rows, int64_t cols) {
+  if (rows <= 0 || cols <= 0) return 0;
+  return mx_operand_workspace(rows, cols);
+}
+
+size_t s3r_mx_workspace(const s3r_qdesc* d, int64_t d_in) {
+  if (check_mx_desc(d) != S3R_OK || d_in < 0) return 0;
+  return std::max(mx_quant_workspace(d->rows, d->cols, d->ec != S3R_EC_NONE),
+                  mx_backward_workspace(d->rows, d_in, d->rows / d->rows_per_example));
+}
+
+int s3r_mx_operand(int64_t rows, int64_t cols, int64_t rows_per_example, const void* M, int32_t dtype, int64_t ld,
+                   uint8_t* Mt, int64_t ld_t, uint8_t* Mt_scales, int64_t ld_ts, float* colsum, uint32_t* flags,
+                   void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (dtype != S3R_F32 && dtype != S3R_BF16) return S3R_ERR_UNSUPPORTED;
+  if (rows <= 0 || cols <= 0 || !mul_of(rows, 128) || rows >= ((int64_t)1 << 24) || cols >= ((int64_t)1 << 24))
+    return S3R_ERR_INVALID_ARG;
+  if (rows_per_example < 128 || rows % rows_per_example || rows_per_example % 128) return S3R_ERR_INVALID_ARG;
+  if (!M || !Mt || !Mt_scales || ld < cols || ld_t < rows / 2 || ld_ts < rows / 32) return S3R_ERR_INVALID_ARG;
+  if ((ld_t & 15) || !al16(Mt)) return S3R_ERR_INVALID_ARG;
+  if (ws_bytes < s3r_mx_operand_workspace(rows, cols)) return S3R_ERR_WORKSPACE;
+  if (!ws || ((uintptr_t)ws & 255u)) return S3R_ERR_INVALID_ARG;
+  int rc;
+  if ((rc = check_arch())) return rc;
+  MxOperandArgs a{};
+  a.M = M; a.dtype = dtype; a.ld = ld; a.R = rows; a.C = cols; a.S = rows_per_example;
+  a.Mt = Mt; a.ld_t = ld_t; a.Mts = Mt_scales; a.ld_ts = ld_ts; a.colsum = colsum; a.flags = flags; a.ws = (char*)ws;
+  return finish(launch_mx_operand(a, stream));
+}
+
+int s3r_mx_quantize(const s3r_qdesc* d, const void* G, int32_t g_dtype, int64_t ld_g, uint8_t* Qh, int64_t ld_qh,
+                    uint8_t* Qh_scales, int64_t ld_qhs, uint8_t* Qt, int64_t ld_qt, uint8_t* Qt_scales, int64_t ld_qts,
+                    float* ec_row_h, float* ec_col_h, float* ec_mean_h, float* ec_row_t, float* ec_col_t,
+                    float* ec_mean_t, uint32_t* flags, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int rc = check_mx_desc(d);
+  if (rc) return rc;
+  if (g_dtype != S3R_F32 && g_dtype != S3R_BF16) return S3R_ERR_UNSUPPORTED;
+  const int64_t T = d->rows, D = d->cols;
+  if (!G || !Qh || !Qh_scales || !Qt || !Qt_scales || ld_g < D) return S3R_ERR_INVALID_ARG;
+  if (ld_qh < D / 2 || (ld_qh & 3) || ld_qhs < D / 32 || ld_qt < T / 2 || (ld_qt & 15) || ld_qts < T / 32)
+    return S3R_ERR_INVALID_ARG;
+  if (!al16(Qt) || ((uintptr_t)Qh & 3u)) return S3R_ERR_INVALID_ARG;
+  const bool ec = d->ec != S3R_EC_NONE;
+  if (ec != (ec_row_h && ec_col_h && ec_mean_h && ec_row_t && ec_col_t && ec_mean_t)) return S3R_ERR_INVALID_ARG;
+  if (ws_bytes < mx_quant_workspace(T, D, ec)) return S3R_ERR_WORKSPACE;
+  if (!ws || ((uintptr_t)ws & 255u)) return S3R_ERR_INVALID_ARG;
+  if ((rc = check_arch())) return rc;
+  MxQuantArgs a{};
+  a.G = G; a.g_dtype = g_dtype; a.ld_g = ld_g; a.T = T; a.D = D; a.S = d->rows_per_example;
+  a.mode = d->mode; a.ec = ec; a.layer = d->layer_id; a.seed = d->seed; a.stream = d->stream;
+  a.Qh = Qh; a.ld_qh = ld_qh; a.Qhs = Qh_scales; a.ld_qhs = ld_qhs;
+  a.Qt = Qt; a.ld_qt = ld_qt; a.Qts = Qt_scales; a.ld_qts = ld_qts;
+  a.ec_row_h = ec_row_h; a.ec_col_h = ec_col_h; a.ec_mean_h = ec_mean_h;
+  a.ec_row_t = ec_row_t; a.ec_col_t = ec_col_t; a.ec_mean_t = ec_mean_t;
+  a.flags = flags; a.ws = (char*)ws;
+  return finish(launch_mx_quantize(a, stream));
+}
+
+static int check_mx_operand(const uint8_t* p, int64_t ld, const uint8_t* s, int64_t lds, int64_t rows, int64_t K) {
+  if (!p || !s || !al16(p) || (ld & 15) || ld < K / 2 || ((uintptr_t)s & 3u) || (lds & 3) || lds < K / 32)
+    return S3R_ERR_INVALID_ARG;
+  if ((rows + 256) * ld >= ((int64_t)1 << 32) || (rows + 256) * lds >= ((int64_t)1 << 32)) return S3R_ERR_INVALID_ARG;
+  return S3R_OK;
+}
+
+int s3r_mx_backward_dx(const s3r_qdesc* d, const uint8_t* Qh, int64_t ld_qh, const uint8_t* Qh_scales, int64_t ld_qhs,
+                       const uint8_t* Wt, int64_t ld_wt, const uint8_t* Wt_scales, int64_t ld_wts, int64_t d_in,
+                       const float* r_W, const float* ec_row_h, const float* ec_col_h, const float* ec_mean_h,
+                       float* dX, int64_t ld_dx, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int rc = check_mx_desc(d);
+  if (rc) return rc;
+  const int64_t T = d->rows, D = d->cols, B = T / d->rows_per_example;
+  if (d_in < 1 || !dX || ld_dx < d_in || ld_dx >= ((int64_t)1 << 22) || ((uintptr_t)dX & 3u)) return S3R_ERR_INVALID_ARG;
+  if ((rc = check_mx_operand(Qh, ld_qh, Qh_scales, ld_qhs, T, D))) return rc;
+  if ((rc = check_mx_operand(Wt, ld_wt, Wt_scales, ld_wts, d_in, D))) return rc;
+  const bool ec = d->ec == S3R_EC_DX_ONLY || d->ec == S3R_EC_TWO_WAY;
+  if (ec && (!r_W || !ec_row_h || !ec_col_h || !ec_mean_h)) return S3R_ERR_INVALID_ARG;
+  if (ws_bytes < mx_backward_workspace(T, d_in, B)) return S3R_ERR_WORKSPACE;
+  if (!ws || ((uintptr_t)ws & 255u)) return S3R_ERR_INVALID_ARG;
+  if ((rc = check_arch())) return rc;
+  MxBwArgs a{};
+  a.A = Qh; a.lda = ld_qh; a.As = Qh_scales; a.ldas = ld_qhs; a.B = Wt; a.ldb = ld_wt; a.Bs = Wt_scales; a.ldbs = ld_wts;
+  a.T = T; a.D = D; a.d_in = d_in; a.S = d->rows_per_example; a.K = D; a.ec = ec;
+  a.vcol = r_W; a.ec_row = ec_row_h; a.ec_col = ec_col_h; a.ec_mean = ec_mean_h;
+  a.out = dX; a.ld_out = ld_dx; a.ws = (char*)ws;
+  return finish(launch_mx_backward_dx(a, stream));
+}
+
+int s3r_mx_backward_dw(const s3r_qdesc* d, const uint8_t* Qt, int64_t ld_qt, const uint8_t* Qt_scales, int64_t ld_qts,
+                       const uint8_t* Xt, int64_t ld_xt, const uint8_t* Xt_scales, int64_t ld_xts, int64_t d_in,
+                       const float* xs, const float* ec_row_t, const float* ec_col_t, const float* ec_mean_t,
+                       float* dW, int64_t ld_dw, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int rc = check_mx_desc(d);
+  if (rc) return rc;
+  const int64_t T = d->rows, D = d->cols, B = T / d->rows_per_example;
+  if (d_in < 1 || !dW || ld_dw < d_in || ld_dw >= ((int64_t)1 << 22) || ((uintptr_t)dW & 3u)) return S3R_ERR_INVALID_ARG;
+  if ((rc = check_mx_operand(Qt, ld_qt, Qt_scales, ld_qts, D, T))) return rc;
+  if ((rc = check_mx_operand(Xt, ld_xt, Xt_scales, ld_xts, d_in, T))) return rc;
+  const bool ec = d->ec == S3R_EC_TWO_WAY || d->ec == S3R_EC_DW_ONLY;
+  if (ec && (!xs || !ec_row_t || !ec_col_t || !ec_mean_t || B > 8)) return S3R_ERR_INVALID_ARG;
+  if (ws_bytes < mx_backward_workspace(T, d_in, B)) return S3R_ERR_WORKSPACE;
+  if (!ws || ((uintptr_t)ws & 255u)) return S3R_ERR_INVALID_ARG;
+  if ((rc = check_arch())) return rc;
+  MxBwArgs a{};
+  a.A = Qt; a.lda = ld_qt; a.As = Qt_scales; a.ldas = ld_qts; a.B = Xt; a.ldb = ld_xt; a.Bs = Xt_scales; a.ldbs = ld_xts;
+  a.T = T; a.D = D; a.d_in = d_in; a.S = d->rows_per_example; a.K = T; a.ec = ec;
+  a.vcol = xs; a.ec_row = ec_row_t; a.ec_col = ec_col_t; a.ec_mean = ec_mean_t;
+  a.out = dW; a.ld_out = ld_dw; a.ws = (char*)ws;
+  return finish(launch_mx_backward_dw(a, stream));
+}
+
 int s3r_time_next_gemm(hipEvent_t start, hipEvent_t stop) {
   GemmTiming& t = gemm_timing();
   t.start = start;

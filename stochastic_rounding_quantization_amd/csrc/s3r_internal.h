@@ -138,6 +138,39 @@ hipError_t launch_grouped_backward_dx(const DxArgs& a, int64_t G, const int64_t*
 hipError_t launch_grouped_backward_dw(const DwArgs& a, int64_t G, const int64_t* offsets, int64_t out_stride,
                                      uint32_t* flags, hipStream_t st);
 
+// MXFP4 variant (mx.hip).
+struct MxQuantArgs {
+  const void* G; int g_dtype; int64_t ld_g;
+  int64_t T, D, S;
+  int mode, ec; uint32_t layer; uint64_t seed; uint32_t stream;
+  uint8_t* Qh; int64_t ld_qh; uint8_t* Qhs; int64_t ld_qhs;
+  uint8_t* Qt; int64_t ld_qt; uint8_t* Qts; int64_t ld_qts;
+  float* ec_row_h; float* ec_col_h; float* ec_mean_h;
+  float* ec_row_t; float* ec_col_t; float* ec_mean_t;
+  uint32_t* flags; char* ws;
+};
+struct MxOperandArgs {
+  const void* M; int dtype; int64_t ld; int64_t R, C, S;
+  uint8_t* Mt; int64_t ld_t; uint8_t* Mts; int64_t ld_ts;
+  float* colsum; uint32_t* flags; char* ws;
+};
+struct MxBwArgs {        // out [rows x d_in] = A [rows x K] . B [d_in x K]^T - correction
+  const uint8_t* A; int64_t lda; const uint8_t* As; int64_t ldas;
+  const uint8_t* B; int64_t ldb; const uint8_t* Bs; int64_t ldbs;
+  int64_t T, D, d_in, S, K;
+  int ec;
+  const float* vcol;     // dX: r_W [d_in]; dW: xs [B x d_in]
+  const float* ec_row; const float* ec_col; const float* ec_mean;
+  float* out; int64_t ld_out; char* ws;
+};
+size_t mx_quant_workspace(int64_t T, int64_t D, int ec);
+size_t mx_operand_workspace(int64_t R, int64_t C);
+size_t mx_backward_workspace(int64_t T, int64_t d_in, int64_t B);
+hipError_t launch_mx_quantize(const MxQuantArgs& a, hipStream_t st);
+hipError_t launch_mx_operand(const MxOperandArgs& a, hipStream_t st);
+hipError_t launch_mx_backward_dx(const MxBwArgs& a, hipStream_t st);
+hipError_t launch_mx_backward_dw(const MxBwArgs& a, hipStream_t st);
+
 // SwiGLU backward glue (swiglu.hip).
 hipError_t launch_swiglu_backward(int64_t T, int64_t F, const float* dH, int64_t ld_dh, const uint16_t* Ag,
                                   const uint16_t* Au, int64_t ld_a, uint16_t* Gg, uint16_t* Gu, int64_t ld_g,

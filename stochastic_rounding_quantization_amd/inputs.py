@@ -96,6 +96,15 @@ WORKLOADS = {
 }
 
 
+# The 4-bit (MXFP4) variant of the Llama-3-8B down-projection backward: the same shape with
+# Student-t(nu=3) gradients; G is rounded to E2M1 with one E8M0 scale per 32 elements.
+MX_WORKLOADS = {
+    "mx-down-8192x14336x4096-bf16": Workload(
+        "mx-down-8192x14336x4096-bf16", 6, 8192, 14336, 4096, 2048, "bf16", 3.0, 1e-4,
+        note="MXFP4 operands; X ~ N(0,1) stands in for the SwiGLU output"),
+}
+
+
 def _store(a: np.ndarray, dtype: str) -> np.ndarray:
     """fp32 -> storage: float32 array, or uint16 bf16 bits."""
     if dtype == "f32":

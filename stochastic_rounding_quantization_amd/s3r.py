@@ -30,8 +30,9 @@ FLAG_NONFINITE, FLAG_TINY_STEP, FLAG_SYNC_TIMEOUT, FLAG_BAD_GROUPS = 1, 2, 4, 8
 EXPORTED = ["s3r_quantize_workspace", "s3r_quantize", "s3r_quantize_with_amax", "s3r_backward_dx",
             "s3r_backward_dw", "s3r_backward_workspace", "s3r_swiglu_backward", "s3r_swiglu_amax_workspace",
             "s3r_swiglu_backward_amax", "s3r_grouped_workspace", "s3r_grouped_quantize",
-            "s3r_grouped_backward_dx", "s3r_grouped_backward_dw", "s3r_time_next_gemm", "s3r_status_string",
-            "s3r_version"]
+            "s3r_grouped_backward_dx", "s3r_grouped_backward_dw", "s3r_mx_workspace", "s3r_mx_operand_workspace",
+            "s3r_mx_operand", "s3r_mx_quantize", "s3r_mx_backward_dx", "s3r_mx_backward_dw", "s3r_time_next_gemm",
+            "s3r_status_string", "s3r_version"]
 
 
 class S3RError(RuntimeError):
@@ -94,6 +95,14 @@ def lib() -> ctypes.CDLL:
     L.s3r_grouped_backward_dw.argtypes = [DP, I64, P, P, I64, P, P, I64, I64, P, P, P, P, P, P, I32, I64, I64, P, P,
                                           SZ, P]
     L.s3r_grouped_backward_dw.restype = ctypes.c_int
+    L.s3r_mx_workspace.argtypes = [DP, I64]
+    L.s3r_mx_workspace.restype = SZ
+    L.s3r_mx_operand_workspace.argtypes = [I64, I64]
+    L.s3r_mx_operand_workspace.restype = SZ
+    L.s3r_mx_operand.argtypes = [I64, I64, I64, P, I32, I64, P, I64, P, I64, P, P, P, SZ, P]
+    L.s3r_mx_quantize.argtypes = [DP, P, I32, I64, P, I64, P, I64, P, I64, P, I64, P, P, P, P, P, P, P, P, SZ, P]
+    L.s3r_mx_backward_dx.argtypes = [DP, P, I64, P, I64, P, I64, P, I64, I64, P, P, P, P, P, I64, P, SZ, P]
+    L.s3r_mx_backward_dw.argtypes = [DP, P, I64, P, I64, P, I64, P, I64, I64, P, P, P, P, P, I64, P, SZ, P]
     L.s3r_time_next_gemm.argtypes = [P, P]
     L.s3r_time_next_gemm.restype = ctypes.c_int
     L.s3r_status_string.argtypes = [ctypes.c_int]
@@ -288,6 +297,69 @@ def s3r_grouped_backward_dw(desc: QDesc, offsets, Q, delta, Xq, s_w, xs, ec_row,
     _check("s3r_grouped_backward_dw", rc)
 
 
+def s3r_mx_workspace(desc: QDesc, d_in: int) -> int:
+    return lib().s3r_mx_workspace(ctypes.byref(desc), d_in)
+
+
+def s3r_mx_operand_workspace(rows: int, cols: int) -> int:
+    return lib().s3r_mx_operand_workspace(rows, cols)
+
+
+def s3r_mx_operand(M, Mt, Mt_scales, colsum=None, rows_per_example=None, flags=None, ws=None, stream=None, *,
+                   rc_only=False):
+    """M [rows x cols] f32/bf16 -> Mt uint8 [cols x rows/2], Mt_scales uint8 [cols x rows/32]."""
+    rows, cols = M.shape
+    S = rows if rows_per_example is None else rows_per_example
+    rc = lib().s3r_mx_operand(rows, cols, S, _ptr(M), _gdtype(M), _ld(M, cols), _ptr(Mt), _ld(Mt, rows // 2),
+                              _ptr(Mt_scales), _ld(Mt_scales, rows // 32), _ptr(colsum), _ptr(flags), _ptr(ws),
+                              _nbytes(ws), _stream(stream))
+    if rc_only:
+        return rc
+    _check("s3r_mx_operand", rc)
+
+
+def s3r_mx_quantize(desc: QDesc, G, Qh, Qh_scales, Qt, Qt_scales, ec_row_h=None, ec_col_h=None, ec_mean_h=None,
+                    ec_row_t=None, ec_col_t=None, ec_mean_t=None, flags=None, ws=None, stream=None, *,
+                    rc_only=False):
+    T, D = desc.rows, desc.cols
+    rc = lib().s3r_mx_quantize(ctypes.byref(desc), _ptr(G), _gdtype(G) if G is not None else S3R_F32, _ld(G, D),
+                               _ptr(Qh), _ld(Qh, D // 2), _ptr(Qh_scales), _ld(Qh_scales, D // 32), _ptr(Qt),
+                               _ld(Qt, T // 2), _ptr(Qt_scales), _ld(Qt_scales, T // 32), _ptr(ec_row_h),
+                               _ptr(ec_col_h), _ptr(ec_mean_h), _ptr(ec_row_t), _ptr(ec_col_t), _ptr(ec_mean_t),
+                               _ptr(flags), _ptr(ws), _nbytes(ws), _stream(stream))
+    if rc_only:
+        return rc
+    _check("s3r_mx_quantize", rc)
+
+
+def s3r_mx_backward_dx(desc: QDesc, Qh, Qh_scales, Wt, Wt_scales, r_W, ec_row_h, ec_col_h, ec_mean_h, dX, ws=None,
+                       stream=None, *, rc_only=False):
+    """Wt uint8 [d_in x D/2] codes, Wt_scales [d_in x D/32]; dX f32 [T x d_in]."""
+    d_in = dX.shape[1]
+    D = desc.cols
+    rc = lib().s3r_mx_backward_dx(ctypes.byref(desc), _ptr(Qh), _ld(Qh, D // 2), _ptr(Qh_scales),
+                                  _ld(Qh_scales, D // 32), _ptr(Wt), _ld(Wt, D // 2), _ptr(Wt_scales),
+                                  _ld(Wt_scales, D // 32), d_in, _ptr(r_W), _ptr(ec_row_h), _ptr(ec_col_h),
+                                  _ptr(ec_mean_h), _ptr(dX), _ld(dX, d_in), _ptr(ws), _nbytes(ws), _stream(stream))
+    if rc_only:
+        return rc
+    _check("s3r_mx_backward_dx", rc)
+
+
+def s3r_mx_backward_dw(desc: QDesc, Qt, Qt_scales, Xt, Xt_scales, xs, ec_row_t, ec_col_t, ec_mean_t, dW, ws=None,
+                       stream=None, *, rc_only=False):
+    """Xt uint8 [d_in x T/2] codes, Xt_scales [d_in x T/32]; dW f32 [D x d_in]."""
+    d_in = dW.shape[1]
+    T = desc.rows
+    rc = lib().s3r_mx_backward_dw(ctypes.byref(desc), _ptr(Qt), _ld(Qt, T // 2), _ptr(Qt_scales),
+                                  _ld(Qt_scales, T // 32), _ptr(Xt), _ld(Xt, T // 2), _ptr(Xt_scales),
+                                  _ld(Xt_scales, T // 32), d_in, _ptr(xs), _ptr(ec_row_t), _ptr(ec_col_t),
+                                  _ptr(ec_mean_t), _ptr(dW), _ld(dW, d_in), _ptr(ws), _nbytes(ws), _stream(stream))
+    if rc_only:
+        return rc
+    _check("s3r_mx_backward_dw", rc)
+
+
 def swiglu_backward(dH, A_gate, A_up, stream=None):
     """Allocate G_gate, G_up (bf16, like A_gate) and run s3r_swiglu_backward."""
     import torch
@@ -388,4 +460,69 @@ def backward_dw(q: Quantized, Xq, s_w=None, xs_b=None, out_dtype=None, stream=No
     dW = torch.empty(D, d_in, dtype=out_dtype or torch.float32, device=Xq.device)
     ws = _workspace(s3r_backward_workspace(q.desc, d_in), Xq.device)
     s3r_backward_dw(q.desc, q.Q, q.delta, Xq, s_w, xs_b, q.ec_row, q.ec_col, q.ec_mean, dW, ws, stream)
+    return dW
+
+
+# ------------------------------------------------------------ MXFP4 helpers ----
+
+@dataclass
+class MxQuantized:
+    Qh: object           # uint8 [T x D/2] E2M1 codes, blocks along D
+    Qh_scales: object    # uint8 [T x D/32] E8M0
+    Qt: object           # uint8 [D x T/2] codes of G^T, blocks along T
+    Qt_scales: object    # uint8 [D x T/32]
+    desc: QDesc
+    ec_h: tuple = (None, None, None)   # (eps_t [T], ebar [B x D], mu [B]) of Q_h's error
+    ec_t: tuple = (None, None, None)   # the same for Q_t
+    flags: object = None
+
+
+def mx_quantize(G, *, mode=S3R, ec=EC_NONE, seed=0, layer_id=0, rows_per_example=None, stream=None,
+                threshold_stream=0) -> MxQuantized:
+    import torch
+    T, D = G.shape
+    desc = qdesc(T, D, rows_per_example, mode, ec, PER_TENSOR, layer_id, seed, threshold_stream)
+    dev = G.device
+    B = T // desc.rows_per_example
+    u8 = dict(dtype=torch.uint8, device=dev)
+    Qh, Qhs = torch.empty(T, D // 2, **u8), torch.empty(T, D // 32, **u8)
+    Qt, Qts = torch.empty(D, T // 2, **u8), torch.empty(D, T // 32, **u8)
+    ec_h = ec_t = (None, None, None)
+    if ec != EC_NONE:
+        f32 = dict(dtype=torch.float32, device=dev)
+        ec_h = (torch.empty(T, **f32), torch.empty(B, D, **f32), torch.empty(B, **f32))
+        ec_t = (torch.empty(T, **f32), torch.empty(B, D, **f32), torch.empty(B, **f32))
+    flags = torch.zeros(1, dtype=torch.int32, device=dev)
+    ws = _workspace(s3r_mx_workspace(desc, 0), dev)
+    s3r_mx_quantize(desc, G, Qh, Qhs, Qt, Qts, *ec_h, *ec_t, flags, ws, stream)
+    return MxQuantized(Qh, Qhs, Qt, Qts, desc, ec_h, ec_t, flags)
+
+
+def mx_operand(M, rows_per_example=None, colsum=True, stream=None):
+    """RTNE MXFP4 of a forward operand, stored transposed: (Mt, Mt_scales, colsum or None)."""
+    import torch
+    rows, cols = M.shape
+    S = rows if rows_per_example is None else rows_per_example
+    dev = M.device
+    Mt = torch.empty(cols, rows // 2, dtype=torch.uint8, device=dev)
+    Mts = torch.empty(cols, rows // 32, dtype=torch.uint8, device=dev)
+    cs = torch.empty(rows // S, cols, dtype=torch.float32, device=dev) if colsum else None
+    ws = _workspace(s3r_mx_operand_workspace(rows, cols), dev)
+    s3r_mx_operand(M, Mt, Mts, cs, S, None, ws, stream)
+    return Mt, Mts, cs
+
+
+def mx_backward_dx(q: MxQuantized, Wt, Wt_scales, r_W=None, stream=None):
+    import torch
+    dX = torch.empty(q.desc.rows, Wt.shape[0], dtype=torch.float32, device=Wt.device)
+    ws = _workspace(s3r_mx_workspace(q.desc, Wt.shape[0]), Wt.device)
+    s3r_mx_backward_dx(q.desc, q.Qh, q.Qh_scales, Wt, Wt_scales, r_W, *q.ec_h, dX, ws, stream)
+    return dX
+
+
+def mx_backward_dw(q: MxQuantized, Xt, Xt_scales, xs=None, stream=None):
+    import torch
+    dW = torch.empty(q.desc.cols, Xt.shape[0], dtype=torch.float32, device=Xt.device)
+    ws = _workspace(s3r_mx_workspace(q.desc, Xt.shape[0]), Xt.device)
+    s3r_mx_backward_dw(q.desc, q.Qt, q.Qt_scales, Xt, Xt_scales, xs, *q.ec_t, dW, ws, stream)
     return dW
