@@ -37,6 +37,7 @@ if ROOT not in sys.path:
 
 PEAK_INT8_TOPS = 5000.0     # MI355X dense INT8 MFMA, TOP/s
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, GB/s
+PEAK_FP4_TFLOPS = 10100.0   # MI355X dense FP4 (MXFP4) MFMA, TFLOP/s
 
 # HBM byte counts of the GEMM kernels, taken with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE and
 # scaled by the same counters' reading for a plain copy of known size.  The file records the
@@ -191,6 +192,8 @@ def main():
         out = run_block(args, dev, torch, inputs, s3r)
     elif args.workload in inputs.MOE:
         out = run_moe(args, dev, torch, inputs, s3r)
+    elif args.workload in inputs.MX_WORKLOADS:
+        out = run_mx(args, dev, torch, inputs, s3r)
     else:
         out = run_linear(args, dev, torch, inputs, s3r)
     print(json.dumps(out), flush=True)
@@ -511,6 +514,108 @@ def run_linear(args, dev, torch, inputs, s3r):
         rows = max(S, rows // S * S)
         log(f"CPU oracle baseline on the first {rows} tokens")
         out["cpu_baseline"] = cpu_baseline(inp, w, mode, ec, rows)
+    return out
+
+
+def mx_cpu_baseline(inp, w, mode, ec, rows):
+    """Time the CPU oracle's MXFP4 backward on the first ``rows`` tokens (whole examples)."""
+    import numpy as np
+    from oracle import mx
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    from stochastic_rounding_quantization_amd import inputs
+    S = w.rows_per_example
+    f32 = lambda a: inputs.bf16_bits_to_f32(a) if inp["dtype"] == "bf16" else np.asarray(a, np.float32)
+    G, X, W = f32(inp["G"][:rows]), f32(inp["X"][:rows]), f32(inp["W"])
+    t0 = time.perf_counter()
+    r = mx.backward(G, X, W, mode=mode, ec=ec, rows_per_example=S, seed=0)
+    dt = time.perf_counter() - t0
+    assert np.isfinite(r["dX"]).all() and np.isfinite(r["dW"]).all()
+    ops = 2 * 2.0 * rows * w.d_out * w.d_in
+    return {"value": ops / dt / 1e12, "unit": "TOP/s", "cores": int(blas_threads), "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": f"first {rows} tokens ({rows // S} example(s) of {S}), D={w.d_out}, d_in={w.d_in}: numpy "
+                      f"MXFP4 quantization of G (both blockings), X and W, statistics, and dX + dW as float64 "
+                      f"BLAS products of the dequantized operands ({blas_threads} BLAS threads), all timed"}
+
+
+def run_mx(args, dev, torch, inputs, s3r):
+    mode, ec = MODES[args.mode]
+    if mode == 3:
+        raise SystemExit("the MXFP4 path has no per-example threshold mode")
+    w = inputs.MX_WORKLOADS[args.workload]
+    T, D, K, S = w.tokens, w.d_out, w.d_in, w.rows_per_example
+    log(f"workload {w.name}: T={T} D={D} d_in={K} S={S} mode={args.mode}; drawing inputs")
+    inp = inputs.make_linear_inputs(w)
+    G, X, W = (_to_dev(torch, dev, inp[k], inp["dtype"]) for k in ("G", "X", "W"))
+    log("forward-operand prep (untimed): RTNE MXFP4 of W and X, transposed, with column sums")
+    Wt, Wts, rW = s3r.mx_operand(W, rows_per_example=D)
+    Xt, Xts, xs = s3r.mx_operand(X, rows_per_example=S)
+    del X, W
+    desc = s3r.qdesc(T, D, S, mode, ec, s3r.PER_TENSOR, layer_id=0, seed=0)
+    B = T // S
+    u8 = dict(dtype=torch.uint8, device=dev)
+    Qh, Qhs = torch.empty(T, D // 2, **u8), torch.empty(D // 128, 4 * T, **u8)
+    Qt, Qts = torch.empty(D, T // 2, **u8), torch.empty(T // 128, 4 * D, **u8)
+    f32 = dict(dtype=torch.float32, device=dev)
+    st_h = (torch.empty(T, **f32), torch.empty(B, D, **f32), torch.empty(B, **f32)) if ec else (None,) * 3
+    st_t = (torch.empty(T, **f32), torch.empty(B, D, **f32), torch.empty(B, **f32)) if ec else (None,) * 3
+    flags = torch.zeros(1, dtype=torch.int32, device=dev)
+    ws = torch.zeros(max(s3r.s3r_mx_workspace(desc, K), 1), **u8)
+    dX = torch.empty(T, K, **f32)
+    dW = torch.empty(D, K, **f32)
+    tl = Timeline(torch, ["step", "quantize", "dx", "dw"], args.steps)
+
+    def step(ev):
+        if ev:
+            ev["step"][0].record()
+            ev["quantize"][0].record()
+        s3r.s3r_mx_quantize(desc, G, Qh, Qhs, Qt, Qts, *st_h, *st_t, flags, ws)
+        if ev:
+            ev["quantize"][1].record()
+            s3r.s3r_time_next_gemm(*ev["dx"])
+        s3r.s3r_mx_backward_dx(desc, Qh, Qhs, Wt, Wts, rW[0], *st_h, dX, ws)
+        if ev:
+            s3r.s3r_time_next_gemm(*ev["dw"])
+        s3r.s3r_mx_backward_dw(desc, Qt, Qts, Xt, Xts, xs, *st_t, dW, ws)
+        if ev:
+            ev["step"][1].record()
+
+    ms_step = _timed_steps(torch, step, tl, args.steps, args.warmup)
+    assert int(flags.item()) == 0
+    t_q, t_gx, t_gw = tl.avg_us("quantize"), tl.avg_us("dx"), tl.avg_us("dw")
+    gop = 2.0 * T * D * K / 1e9
+    value = 2 * gop / (ms_step / 1e3) / 1e3
+    el = 2 if inp["dtype"] == "bf16" else 4
+    q_bytes = int(T * D * (el + 2 * (0.5 + 1 / 32)))
+    q_gbs = q_bytes / (t_q / 1e6) / 1e9
+    key = "dx" if t_gx >= t_gw else "dw"
+    achieved = gop / (max(t_gx, t_gw) / 1e6) / 1e3
+    out = {
+        "metric": "S3R-EC backward TOPS (quant+INT8 dX/dW) & quantizer GB/s, % of MI355X peak",
+        "value": round(value, 2), "unit": "TOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp4", "data": "synthetic",
+        "config": {"workload": w.name, "tokens": T, "d_in": K, "d_out": D, "rows_per_example": S,
+                   "mode": args.mode, "format": "MXFP4 (E2M1, E8M0 per 32 along the contraction)",
+                   "g_dtype": inp["dtype"]},
+        "frac_of_fp4_peak": round(value / PEAK_FP4_TFLOPS, 4),
+        "quantizer": {"us": round(t_q, 2), "GB_s": round(q_gbs, 1),
+                      "frac_of_hbm_peak": round(q_gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": q_bytes},
+        "kernels_us": {"quantize_call": round(t_q, 2), "gemm_dx": round(t_gx, 2), "gemm_dw": round(t_gw, 2),
+                       "step_events": round(tl.avg_us("step"), 2)},
+        "gemm_tops": {"dx": round(gop / (t_gx / 1e6) / 1e3, 1), "dw": round(gop / (t_gw / 1e6) / 1e3, 1)},
+        "roofline": {"kernel": f"mx gemm {key}", "bound": "mfma", "achieved": round(achieved, 1),
+                     "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP4_TFLOPS, 4),
+                     "traffic": None, "algorithmic": f"2*M*N*K = {gop:.1f} GFLOP per launch (FP4 products)"},
+    }
+    if args.cpu_rows != 0:
+        rows = S if args.cpu_rows < 0 else max(S, min(args.cpu_rows, T) // S * S)
+        log(f"CPU oracle baseline on the first {rows} tokens")
+        out["cpu_baseline"] = mx_cpu_baseline(inp, w, mode, ec, rows)
     return out
 
 

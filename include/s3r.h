@@ -347,8 +347,13 @@ int s3r_swiglu_backward_amax(int64_t T, int64_t F, const float* dH, int64_t ld_d
  * readings (OCP microscaling MXFP4 with the page's rounding carried over):
  *   codes    E2M1 (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6; code = sign << 3 |
  *            index), two per byte, the first element in the low nibble;
+ *            a matrix of R rows and K (contraction) columns is R x K/2 bytes;
  *   scales   one E8M0 byte per 32 consecutive elements along a GEMM's
- *            contraction: 2^k with k the smallest integer such that
+ *            contraction, grouped by steps of 128: the K/128 steps are rows of
+ *            ld_s bytes, step j holding R 4-byte words (row r's blocks 4j ..
+ *            4j+3), so the scale of (row r, block b) is at
+ *            (b / 4) * ld_s + 4 r + b % 4  (ld_s >= 4 R, a multiple of 4);
+ *            the value is 2^k with k the smallest integer such that
  *            max|block| <= 6 * 2^k (nothing saturates), clamped to
  *            [-127, 127]; an all-zero block has k = -127; a block with a
  *            non-finite element gets byte 255 (NaN), zero codes and
@@ -370,8 +375,9 @@ int s3r_swiglu_backward_amax(int64_t T, int64_t F, const float* dH, int64_t ld_d
  * the FP4 matrix cores), T, D < 2^24; scale must be S3R_PER_TENSOR (it names
  * no scale here); mode RTNE, SR or S3R; ec requires S3R.  Byte leading
  * dimensions (ld_*) of codes are multiples of 16 with 16-byte aligned bases
- * (Q_h: a multiple of 4); of scales, multiples of 4 (operand rows are read
- * as 4-byte words).  Device pointers throughout, row-major.
+ * (Q_h: a multiple of 4); of scales, multiples of 4 with 4-byte aligned
+ * bases (a GEMM step reads its rows' scale words as one contiguous run).
+ * Device pointers throughout, row-major.
  */
 
 /* s3r_mx_workspace: bytes of ws for s3r_mx_quantize and both backward calls
@@ -381,7 +387,8 @@ size_t s3r_mx_operand_workspace(int64_t rows, int64_t cols);
 
 /* s3r_mx_operand: the forward operand M [rows x cols] (f32 or bf16, ld
  * elements) to RTNE MXFP4 blocked along the rows, stored transposed: Mt
- * [cols x rows/2] codes (ld_t bytes), Mt_scales [cols x rows/32] (ld_ts).
+ * [cols x rows/2] codes (ld_t bytes), Mt_scales [rows/128][cols][4] (ld_ts
+ * bytes per step).
  * W [D x d_in] gives Wt for dX, X [T x d_in] gives Xt for dW.  colsum
  * (optional, f32 [rows/rows_per_example x cols]): per-group column sums of the
  * dequantized operand in groups of rows_per_example rows (a multiple of 128
@@ -393,7 +400,7 @@ int s3r_mx_operand(int64_t rows, int64_t cols, int64_t rows_per_example,
                    float* colsum, uint32_t* flags, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* s3r_mx_quantize: G [T x D] (f32 or bf16) to Q_h (codes [T x D/2], scales
- * [T x D/32]) and Q_t (codes [D x T/2], scales [D x T/32]).  With EC: the
+ * [D/128][T][4]) and Q_t (codes [D x T/2], scales [T/128][D][4]).  With EC: the
  * statistics of each quantization's error, ec_row_* [T] (eps_t), ec_col_*
  * [B x D] (ebar_b), ec_mean_* [B] (mu_b); all six pointers given exactly when
  * desc->ec != S3R_EC_NONE.  Both quantizations are written whatever the

@@ -373,7 +373,7 @@ int s3r_mx_operand(int64_t rows, int64_t cols, int64_t rows_per_example, const v
   if (rows <= 0 || cols <= 0 || !mul_of(rows, 128) || rows >= ((int64_t)1 << 24) || cols >= ((int64_t)1 << 24))
     return S3R_ERR_INVALID_ARG;
   if (rows_per_example < 128 || rows % rows_per_example || rows_per_example % 128) return S3R_ERR_INVALID_ARG;
-  if (!M || !Mt || !Mt_scales || ld < cols || ld_t < rows / 2 || ld_ts < rows / 32) return S3R_ERR_INVALID_ARG;
+  if (!M || !Mt || !Mt_scales || ld < cols || ld_t < rows / 2 || ld_ts < 4 * cols) return S3R_ERR_INVALID_ARG;
   if ((ld_t & 15) || !al16(Mt)) return S3R_ERR_INVALID_ARG;
   if (ws_bytes < s3r_mx_operand_workspace(rows, cols)) return S3R_ERR_WORKSPACE;
   if (!ws || ((uintptr_t)ws & 255u)) return S3R_ERR_INVALID_ARG;
@@ -394,7 +394,7 @@ int s3r_mx_quantize(const s3r_qdesc* d, const void* G, int32_t g_dtype, int64_t 
   if (g_dtype != S3R_F32 && g_dtype != S3R_BF16) return S3R_ERR_UNSUPPORTED;
   const int64_t T = d->rows, D = d->cols;
   if (!G || !Qh || !Qh_scales || !Qt || !Qt_scales || ld_g < D) return S3R_ERR_INVALID_ARG;
-  if (ld_qh < D / 2 || (ld_qh & 3) || ld_qhs < D / 32 || ld_qt < T / 2 || (ld_qt & 15) || ld_qts < T / 32)
+  if (ld_qh < D / 2 || (ld_qh & 3) || ld_qhs < 4 * T || ld_qt < T / 2 || (ld_qt & 15) || ld_qts < 4 * D)
     return S3R_ERR_INVALID_ARG;
   if (!al16(Qt) || ((uintptr_t)Qh & 3u)) return S3R_ERR_INVALID_ARG;
   const bool ec = d->ec != S3R_EC_NONE;
@@ -414,9 +414,9 @@ int s3r_mx_quantize(const s3r_qdesc* d, const void* G, int32_t g_dtype, int64_t 
 }
 
 static int check_mx_operand(const uint8_t* p, int64_t ld, const uint8_t* s, int64_t lds, int64_t rows, int64_t K) {
-  if (!p || !s || !al16(p) || (ld & 15) || ld < K / 2 || ((uintptr_t)s & 3u) || (lds & 3) || lds < K / 32)
+  if (!p || !s || !al16(p) || (ld & 15) || ld < K / 2 || ((uintptr_t)s & 3u) || (lds & 3) || lds < 4 * rows)
     return S3R_ERR_INVALID_ARG;
-  if ((rows + 256) * ld >= ((int64_t)1 << 32) || (rows + 256) * lds >= ((int64_t)1 << 32)) return S3R_ERR_INVALID_ARG;
+  if ((rows + 256) * ld >= ((int64_t)1 << 32) || (K / 128 + 1) * lds >= ((int64_t)1 << 32)) return S3R_ERR_INVALID_ARG;
   return S3R_OK;
 }
 

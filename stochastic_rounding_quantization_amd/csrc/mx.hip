@@ -13,7 +13,10 @@
 //           to 6; RTNE s * rint(y / s); SR / S3R the exact floor
 //           s * floor(y / s + r) with the INT8 path's thresholds;
 //   layout  two E2M1 codes per byte, the first in the low nibble; scales one
-//           byte per block.
+//           byte per block, grouped by K step of 128 (4 blocks): for a
+//           matrix of R rows the scales of step j are R 4-byte words (row r's
+//           blocks 4j .. 4j+3), so byte (r, b) sits at (b / 4) ld + 4 r + b % 4.
+//           A GEMM step then reads its rows' scale words contiguously.
 // Every GEMM operand is K-major (the contraction contiguous): G is quantized
 // twice, Q_h [T x D] blocked along D for dX and Q_t [D x T] (G transposed,
 // blocked along T) for dW, with the same thresholds; the forward operands W
@@ -91,8 +94,8 @@ struct MxQuant {
 // ------------------------------------------ blocks along the columns ----
 // Source M [R x C] row-major, blocks of 32 along C.  A block of 256 threads
 // covers 64 rows x 512 columns; a lane handles 8 consecutive elements, four
-// lanes a block.  Out: codes [R x C/2] (row-major, ld_out bytes), scales
-// [R x C/32] (ld_s bytes).  With EC: the error row sums of each row over the
+// lanes a block.  Out: codes [R x C/2] (row-major, ld_out bytes), scales in
+// the step-grouped layout [C/128][R][4] (ld_s bytes per step).  With EC: the error row sums of each row over the
 // tile's 512 columns (row_part[t * n_ct + ctile]) and the error column sums of
 // the tile's 64 rows (col_part[rtile * C + j]).
 template <typename TIn, bool EC>
@@ -158,7 +161,7 @@ __global__ __launch_bounds__(256) void mx_quant_rows_kernel(MxQuant p, const TIn
     }
     if (active) {
       *reinterpret_cast<uint32_t*>(out + t * ld_out + j0 / 2) = packed;
-      if ((lane & 3) == 0) sc[t * ld_s + j0 / 32] = (uint8_t)sb;
+      if ((lane & 3) == 0) sc[(j0 / 128) * ld_s + t * 4 + ((j0 / 32) & 3)] = (uint8_t)sb;
       if (bad && flags && (lane & 3) == 0) atomicOr(flags, S3R_FLAG_NONFINITE);
     }
     rs[k] = es;
@@ -201,7 +204,7 @@ __global__ __launch_bounds__(256) void mx_quant_rows_kernel(MxQuant p, const TIn
 
 // ------------------------------------------------ blocks along the rows ----
 // Source M [R x C] row-major, blocks of 32 along R, output transposed:
-// codes [C x R/2] (row c holds column c of M), scales [C x R/32].  A block of
+// codes [C x R/2] (row c holds column c of M), scales [R/128][C][4].  A block of
 // 256 threads covers 128 rows x 64 columns: lane = column, wave = one 32-row
 // block.  Per thread: the amax of its 32 values, the scale, 32 codes = 16
 // bytes written contiguously (the four waves write 64 contiguous bytes of an
@@ -260,7 +263,7 @@ __global__ __launch_bounds__(256) void mx_quant_cols_kernel(MxQuant p, const TIn
   }
   if (active) {
     *reinterpret_cast<uint4*>(out + c * ld_out + t0 / 2) = make_uint4(w[0], w[1], w[2], w[3]);
-    sc[c * ld_s + t0 / 32] = (uint8_t)sb;
+    sc[(t0 / 128) * ld_s + c * 4 + ((t0 / 32) & 3)] = (uint8_t)sb;
     if (bad && flags) atomicOr(flags, S3R_FLAG_NONFINITE);
     const int64_t rblk = t0 / 32;
     if constexpr (EC) col_part[rblk * p.C + c] = csum;
@@ -357,7 +360,7 @@ __global__ __launch_bounds__(256) void mx_mean_kernel(int64_t S, const float* __
 
 // ------------------------------------------------------------- FP4 GEMM ----
 // out [M x N] (f32) = A [M x K] . B [N x K]^T with both operands MXFP4 and
-// K-major: codes 2 per byte (ld in bytes), E8M0 scales [rows x K/32].  256 x
+// K-major: codes 2 per byte (ld in bytes), E8M0 scales [K/128][rows][4].  256 x
 // 256 tile per 256-thread workgroup, four waves of 128 x 128 (4 x 4 blocks of
 // v_mfma_scale_f32_32x32x64_f8f6f4), K step 128 (64 bytes per row).  A stage
 // holds the A and B tiles (256 rows x 64 B each, 16-byte chunks swizzled as
@@ -369,7 +372,20 @@ __global__ __launch_bounds__(256) void mx_mean_kernel(int64_t S, const float* __
 // Output: lane l, register r -> row (r / 4) 8 + (l / 32) 4 + r % 4, column l % 32.
 constexpr int kMxStages = 4;
 constexpr int kMxStageBytes = 32768 + 2048;
-__shared__ __attribute__((aligned(1024))) uint8_t g_mx[kMxStages][kMxStageBytes];
+// Four separate LDS objects rather than one indexed array: the compiler then
+// sees that a step's LDS reads and the DMA refilling another stage touch
+// different memory, and does not drain every outstanding load before the reads.
+__shared__ __attribute__((aligned(1024))) uint8_t g_mx0[kMxStageBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t g_mx1[kMxStageBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t g_mx2[kMxStageBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t g_mx3[kMxStageBytes];
+template <int S>
+__device__ __forceinline__ uint8_t* mx_stage() {
+  if constexpr (S == 0) return g_mx0;
+  else if constexpr (S == 1) return g_mx1;
+  else if constexpr (S == 2) return g_mx2;
+  else return g_mx3;
+}
 
 struct MxGemm {
   const uint8_t* A; int64_t lda; const uint8_t* As; int64_t ldas;
@@ -390,31 +406,97 @@ constexpr int kMxMaxB = 8;
 
 __device__ __forceinline__ int mx_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
+struct MxRsrc { __amdgpu_buffer_rsrc_t a, b, sa, sb, z; int nk; };
+
+// Stage kt of the K loop; past the last step (kt >= nk) every load goes through
+// an empty descriptor and lands zeros, which add nothing to the accumulators.
 __device__ __forceinline__ void mx_load_stage(const MxGemm& g, uint8_t* st, int64_t m0, int64_t n0, int kt,
-                                              __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
-                                              __amdgpu_buffer_rsrc_t rsa, __amdgpu_buffer_rsrc_t rsb) {
+                                              const MxRsrc& r) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool live = kt < r.nk;
+  const MxRsrc rs{live ? r.a : r.z, live ? r.b : r.z, live ? r.sa : r.z, live ? r.sb : r.z, r.z, r.nk};
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int blk = wave * 4 + q;
     const int row = blk * 16 + (lane >> 2);
     const int c = (lane & 3) ^ mx_swz(row);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(st + blk * 1024), 16,
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.a, (lds_void*)(st + blk * 1024), 16,
                                              (uint32_t)((m0 + row) * g.lda + c * 16), (uint32_t)kt * 64u, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(st + 16384 + blk * 1024), 16,
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.b, (lds_void*)(st + 16384 + blk * 1024), 16,
                                              (uint32_t)((n0 + row) * g.ldb + c * 16), (uint32_t)kt * 64u, 0, 0);
   }
   // scale words: this wave's 64 rows of A and of B, one dword per lane
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void*)(st + 32768 + wave * 256), 4,
-                                           (uint32_t)((m0 + wave * 64 + lane) * g.ldas), (uint32_t)kt * 4u, 0, 0);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void*)(st + 33792 + wave * 256), 4,
-                                           (uint32_t)((n0 + wave * 64 + lane) * g.ldbs), (uint32_t)kt * 4u, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.sa, (lds_void*)(st + 32768 + wave * 256), 4,
+                                           (uint32_t)((m0 + wave * 64 + lane) * 4), (uint32_t)(kt * g.ldas), 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.sb, (lds_void*)(st + 33792 + wave * 256), 4,
+                                           (uint32_t)((n0 + wave * 64 + lane) * 4), (uint32_t)(kt * g.ldbs), 0, 0);
 }
 
 // s_waitcnt: at most n vector-memory ops outstanding, no LDS ops.
 #define S3R_MX_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | 0x70 | 0xF00)
 #define S3R_MX_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(0xC07F)
+
+constexpr int kMxSgMfma = 0x008, kMxSgDsRead = 0x100, kMxSgVmem = 0x010;
+
+// One K step (128 elements) on stage S = kt % 4: wait for this wave's loads of
+// the stage, barrier (all waves' loads visible; the stage read in the previous
+// step is retired), refill that retired stage with step kt + 3, then 2 x 16
+// MFMAs with the second half-step's fragments read during the first half's.
+template <int S>
+__device__ __forceinline__ void mx_step(const MxGemm& g, int64_t m0, int64_t n0, int kt, const MxRsrc& rs,
+                                        v16f (&acc)[4][4]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int r31 = lane & 31, hk = lane >> 5;
+  S3R_MX_WAIT_VM(20);
+  S3R_MX_WAIT_LGKM0();
+  __builtin_amdgcn_s_barrier();
+  mx_load_stage(g, mx_stage<(S + 3) % 4>(), m0, n0, kt + 3, rs);
+  const uint8_t* st = mx_stage<S>();
+  uint32_t sa[4], sb[4];
+  v8i fa[2][4], fb[2][4];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    const int c = kk * 2 + hk;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ra_ = wm * 128 + i * 32 + r31, rb_ = wn * 128 + i * 32 + r31;
+      const uint4 x = *reinterpret_cast<const uint4*>(st + ra_ * 64 + ((c ^ mx_swz(ra_)) << 4));
+      const uint4 y = *reinterpret_cast<const uint4*>(st + 16384 + rb_ * 64 + ((c ^ mx_swz(rb_)) << 4));
+      fa[kk][i] = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
+      fb[kk][i] = v8i{(int)y.x, (int)y.y, (int)y.z, (int)y.w, 0, 0, 0, 0};
+    }
+    if (kk == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sa[i] = *reinterpret_cast<const uint32_t*>(st + 32768 + (wm * 128 + i * 32 + r31) * 4);
+        sb[i] = *reinterpret_cast<const uint32_t*>(st + 33792 + (wn * 128 + i * 32 + r31) * 4);
+      }
+    }
+  }
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    const int sh = 8 * (kk * 2 + hk);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[kk][i], fb[kk][j], acc[i][j], 4, 4, 0,
+                                                                    (int)((sa[i] >> sh) & 0xFFu), 0,
+                                                                    (int)((sb[j] >> sh) & 0xFFu));
+  }
+  // schedule: the first half-step's fragment and scale reads, then its MFMAs with
+  // the second half-step's reads between them, and the refill's 10 buffer loads
+  // spread one per MFMA pair, so that no burst of loads stalls the MFMA issue
+  __builtin_amdgcn_sched_group_barrier(kMxSgDsRead, 16, 0);
+#pragma unroll
+  for (int x = 0; x < 32; ++x) {
+    __builtin_amdgcn_sched_group_barrier(kMxSgMfma, 1, 0);
+    if (x < 8) __builtin_amdgcn_sched_group_barrier(kMxSgDsRead, 1, 0);
+    if ((x & 1) && x < 20) __builtin_amdgcn_sched_group_barrier(kMxSgVmem, 1, 0);
+  }
+}
 
 template <bool DW, bool EC, int NB>
 __global__ __launch_bounds__(256, 1) void mx_gemm_kernel(MxGemm g, MxEpi ep) {
@@ -432,8 +514,8 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_kernel(MxGemm g, MxEpi ep) {
   // descriptors over whole operands: rows past M (N) read zeros
   const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)g.A, (short)0, (int)(uint32_t)(g.M * g.lda), kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc((void*)g.B, (short)0, (int)(uint32_t)(g.N * g.ldb), kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc((void*)g.As, (short)0, (int)(uint32_t)(g.M * g.ldas), kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc((void*)g.Bs, (short)0, (int)(uint32_t)(g.N * g.ldbs), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc((void*)g.As, (short)0, (int)(uint32_t)(nk * g.ldas), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc((void*)g.Bs, (short)0, (int)(uint32_t)(nk * g.ldbs), kRsrcWord3);
 
   v16f acc[4][4];
 #pragma unroll
@@ -443,55 +525,31 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_kernel(MxGemm g, MxEpi ep) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  for (int s = 0; s < kMxStages - 1; ++s)
-    if (s < nk) mx_load_stage(g, g_mx[s], m0, n0, s, ra, rb, rsa, rsb);
-  const int r31 = lane & 31, hk = lane >> 5;
-  for (int kt = 0; kt < nk; ++kt) {
-    // stage kt has landed when at most the later stages' loads (10 per stage per lane) remain
-    const int later = min(nk - 1 - kt, kMxStages - 2);
-    if (later >= 2) S3R_MX_WAIT_VM(20);
-    else if (later == 1) S3R_MX_WAIT_VM(10);
-    else S3R_MX_WAIT_VM(0);
-    __builtin_amdgcn_s_barrier();
-    if (kt + kMxStages - 1 < nk) mx_load_stage(g, g_mx[(kt + kMxStages - 1) % kMxStages], m0, n0, kt + kMxStages - 1, ra, rb, rsa, rsb);
-    const uint8_t* st = g_mx[kt % kMxStages];
-    uint32_t sa[4], sb[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sa[i] = *reinterpret_cast<const uint32_t*>(st + 32768 + (wm * 128 + i * 32 + r31) * 4);
-      sb[i] = *reinterpret_cast<const uint32_t*>(st + 33792 + (wn * 128 + i * 32 + r31) * 4);
-    }
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      v8i fa[4], fb[4];
-      const int c = kk * 2 + hk;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int ra_ = wm * 128 + i * 32 + r31, rb_ = wn * 128 + i * 32 + r31;
-        const uint4 x = *reinterpret_cast<const uint4*>(st + ra_ * 64 + ((c ^ mx_swz(ra_)) << 4));
-        const uint4 y = *reinterpret_cast<const uint4*>(st + 16384 + rb_ * 64 + ((c ^ mx_swz(rb_)) << 4));
-        fa[i] = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
-        fb[i] = v8i{(int)y.x, (int)y.y, (int)y.z, (int)y.w, 0, 0, 0, 0};
-      }
-      const int sh = 8 * (kk * 2 + hk);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], 4, 4, 0,
-                                                                      (int)((sa[i] >> sh) & 0xFFu), 0,
-                                                                      (int)((sb[j] >> sh) & 0xFFu));
-    }
+  // Stages 0..2 up front; every step refills one stage, so a step always finds
+  // exactly the loads of the two following stages in flight.
+  // The step count is rounded up to a multiple of 4 (the stage ring's period);
+  // the extra steps multiply zeros.
+  const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc((void*)g.A, (short)0, 0, kRsrcWord3);
+  const MxRsrc rs{ra, rb, rsa, rsb, rz, nk};
+  mx_load_stage(g, mx_stage<0>(), m0, n0, 0, rs);
+  mx_load_stage(g, mx_stage<1>(), m0, n0, 1, rs);
+  mx_load_stage(g, mx_stage<2>(), m0, n0, 2, rs);
+  for (int kt = 0; kt < nk; kt += 4) {
+    mx_step<0>(g, m0, n0, kt, rs, acc);
+    mx_step<1>(g, m0, n0, kt + 1, rs, acc);
+    mx_step<2>(g, m0, n0, kt + 2, rs, acc);
+    mx_step<3>(g, m0, n0, kt + 3, rs, acc);
   }
   S3R_MX_WAIT_VM(0);
   S3R_MX_WAIT_LGKM0();
   __builtin_amdgcn_s_barrier();
+  const int r31 = lane & 31, hk = lane >> 5;
 
   // epilogue: per-row values of the tile staged in LDS (the stages are free now),
   // per-column values in registers
-  float* s_rowc = reinterpret_cast<float*>(g_mx[0]);             // dX: eps_t - mu_b; dW: ebar[b][row] (b-major)
-  int* s_rowb = reinterpret_cast<int*>(g_mx[1]);                 // dX: the row's example, relative to the tile's first
-  float* s_v = reinterpret_cast<float*>(g_mx[2]);                // dX: v[b0 + b][tile column], b < NB
+  float* s_rowc = reinterpret_cast<float*>(mx_stage<0>());             // dX: eps_t - mu_b; dW: ebar[b][row] (b-major)
+  int* s_rowb = reinterpret_cast<int*>(mx_stage<1>());                // dX: the row's example, relative to the tile's first
+  float* s_v = reinterpret_cast<float*>(mx_stage<2>());               // dX: v[b0 + b][tile column], b < NB
   const int64_t b_first = DW ? 0 : m0 / ep.S;
   if constexpr (EC) {
     for (int r = threadIdx.x; r < 256; r += 256) {
@@ -584,37 +642,73 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_kernel(MxGemm g, MxEpi ep) {
 }
 
 // ------------------------------------------------ correction products ----
-// out[b][n] = sum over k of coef[b][k] * dequant(P[n][k]), P an MXFP4 matrix
-// [N x K] (K-major codes, scales [N x K/32]); one wave per row n, fixed order
-// (lane-strided partial sums, then an xor butterfly), fp32 partials.
-template <int NB>
+// out[b][n] = sum over k of coef[b][k] * dequant(P[n][k]) for b < nb, P an MXFP4
+// matrix [N x K] (K-major codes, scales [K/128][N][4]).  A block of 4 waves owns
+// 4 * RPW rows (RPW per wave); K runs in chunks of 2048 in which lane l takes
+// the 32-element block l: its 16 code bytes, its scale, and the chunk's
+// coefficients from LDS, stored [b][i4][lane] (float4 units) so that a wave's
+// reads are conflict-free.  Fixed order: per-lane sums, then an xor butterfly.
+constexpr int kRdChunk = 2048;
+
+__device__ __forceinline__ float e2m1_times(uint32_t c, float sc) { return e2m1_value(c) * sc; }
+
+template <int NB, int RPW>
 __global__ __launch_bounds__(256) void mx_rowdot_kernel(const uint8_t* __restrict__ P, int64_t ldp,
                                                         const uint8_t* __restrict__ Ps, int64_t ldps, int64_t N,
                                                         int64_t K, int nb, const float* __restrict__ coef,
                                                         float* __restrict__ out) {
-  const int lane = threadIdx.x & 63;
-  const int64_t n = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (n >= N) return;
-  float acc[NB];
+  __shared__ float4 s_c[NB][8][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t n0 = ((int64_t)blockIdx.x * 4 + wave) * RPW;
+  float acc[RPW][NB];
 #pragma unroll
-  for (int b = 0; b < NB; ++b) acc[b] = 0.f;
-  for (int64_t k0 = (int64_t)lane * 8; k0 < K; k0 += 512) {          // 8 elements per lane
-    const uint32_t w = *reinterpret_cast<const uint32_t*>(P + n * ldp + k0 / 2);
-    const float sc = __builtin_ldexpf(1.f, (int)Ps[n * ldps + k0 / 32] - 127);
+  for (int r = 0; r < RPW; ++r)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float x = e2m1_value((w >> (4 * i)) & 15u) * sc;
+    for (int b = 0; b < NB; ++b) acc[r][b] = 0.f;
+  for (int64_t kc = 0; kc < K; kc += kRdChunk) {
+    __syncthreads();                                    // the previous chunk's coefficients are consumed
+    for (int x = threadIdx.x; x < NB * kRdChunk; x += 256) {
+      const int b = x / kRdChunk, e = x % kRdChunk;    // element e of the chunk -> lane e / 32, i4 (e % 32) / 4
+      const float v = (b < nb && kc + e < K) ? coef[(int64_t)b * K + kc + e] : 0.f;
+      reinterpret_cast<float*>(&s_c[b][(e & 31) >> 2][e >> 5])[e & 3] = v;
+    }
+    __syncthreads();
+    const int64_t k = kc + lane * 32;
+    if (k >= K) continue;
 #pragma unroll
-      for (int b = 0; b < NB; ++b)
-        if (b < nb) acc[b] = fmaf(coef[(int64_t)b * K + k0 + i], x, acc[b]);
+    for (int r = 0; r < RPW; ++r) {
+      const int64_t n = n0 + r;
+      if (n >= N) break;
+      const uint4 w = *reinterpret_cast<const uint4*>(P + n * ldp + k / 2);
+      const float sc = __builtin_ldexpf(1.f, (int)Ps[(k / 128) * ldps + n * 4 + ((k / 32) & 3)] - 127);
+      const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int i4 = 0; i4 < 8; ++i4) {
+        const uint32_t word = wv[i4 >> 1] >> (16 * (i4 & 1));
+        const float x0 = e2m1_times(word & 15u, sc), x1 = e2m1_times((word >> 4) & 15u, sc);
+        const float x2 = e2m1_times((word >> 8) & 15u, sc), x3 = e2m1_times((word >> 12) & 15u, sc);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          if (b >= nb) break;
+          const float4 c = s_c[b][i4][lane];
+          float a = acc[r][b];
+          a = fmaf(c.x, x0, a);
+          a = fmaf(c.y, x1, a);
+          a = fmaf(c.z, x2, a);
+          a = fmaf(c.w, x3, a);
+          acc[r][b] = a;
+        }
+      }
     }
   }
 #pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    float a = acc[b];
-    for (int o = 32; o > 0; o >>= 1) a += __shfl_xor(a, o, 64);
-    if (lane == 0 && b < nb) out[(int64_t)b * N + n] = a;
-  }
+  for (int r = 0; r < RPW; ++r)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      float a = acc[r][b];
+      for (int o = 32; o > 0; o >>= 1) a += __shfl_xor(a, o, 64);
+      if (lane == 0 && b < nb && n0 + r < N) out[(int64_t)b * N + n0 + r] = a;
+    }
 }
 
 // c[t] = ec_row[t] - ec_mean[t / S]
@@ -743,9 +837,10 @@ hipError_t launch_mx_backward_dx(const MxBwArgs& a, hipStream_t st) {
   if (a.ec) {
     float* v = (float*)(a.ws + kWsHeaderBytes);
     // v_b[i] = sum_j ebar_b[j] dq(W)[j][i]: rows of the K-major Wt [d_in x D], eight examples per pass
-    for (int64_t b0 = 0; b0 < B; b0 += 8)
-      hipLaunchKernelGGL(mx_rowdot_kernel<8>, dim3((unsigned)((a.d_in + 3) / 4)), dim3(256), 0, st, a.B, a.ldb, a.Bs,
-                         a.ldbs, a.d_in, a.K, (int)min((int64_t)8, B - b0), a.ec_col + b0 * a.K, v + b0 * a.d_in);
+    for (int64_t b0 = 0; b0 < B; b0 += 4)
+      hipLaunchKernelGGL((mx_rowdot_kernel<4, 8>), dim3((unsigned)((a.d_in + 31) / 32)), dim3(256), 0, st, a.B, a.ldb,
+                         a.Bs, a.ldbs, a.d_in, a.K, (int)min((int64_t)4, B - b0), a.ec_col + b0 * a.K,
+                         v + b0 * a.d_in);
     ep.ec_row = a.ec_row; ep.ec_mean = a.ec_mean; ep.vec = v; ep.rW = a.vcol;
   }
   const MxGemm g = make_mx_gemm(a.A, a.lda, a.As, a.ldas, a.B, a.ldb, a.Bs, a.ldbs, a.T, a.d_in, a.K);
@@ -764,8 +859,8 @@ hipError_t launch_mx_backward_dw(const MxBwArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(mx_token_coef_kernel, dim3((unsigned)((a.T + 255) / 256)), dim3(256), 0, st, a.T, a.S,
                        a.ec_row, a.ec_mean, coef);
     // u[i] = sum_t (eps_t - mu_b) dq(X)[t][i]: rows of the K-major Xt [d_in x T]
-    hipLaunchKernelGGL(mx_rowdot_kernel<1>, dim3((unsigned)((a.d_in + 3) / 4)), dim3(256), 0, st, a.B, a.ldb, a.Bs,
-                       a.ldbs, a.d_in, a.T, 1, (const float*)coef, u);
+    hipLaunchKernelGGL((mx_rowdot_kernel<1, 8>), dim3((unsigned)((a.d_in + 31) / 32)), dim3(256), 0, st, a.B, a.ldb,
+                       a.Bs, a.ldbs, a.d_in, a.T, 1, (const float*)coef, u);
     ep.ebar = a.ec_col; ep.xs = a.vcol; ep.u = u;
   }
   // dW [D x d_in] = Qt [D x T] . Xt [d_in x T]^T

@@ -52,16 +52,22 @@ def gpu_mx(inp, *, mode, ec, S, seed=0, layer_id=0):
     return dict(q=q, Wt=Wt, Wts=Wts, rW=rW, Xt=Xt, Xts=Xts, xs=xs, dX=dX, dW=dW)
 
 
+def step_grouped(scale):
+    """Scales [R x K/32] (one byte per row and block) -> the library's layout [K/128][R][4]."""
+    R, nb = scale.shape
+    return np.ascontiguousarray(scale.reshape(R, nb // 4, 4).transpose(1, 0, 2)).reshape(nb // 4, 4 * R)
+
+
 def _check_quant(gpu, ref):
     q = gpu["q"]
     np.testing.assert_array_equal(host(q.Qh), mx.pack(ref["qh"]["codes"]))
-    np.testing.assert_array_equal(host(q.Qh_scales), ref["qh"]["scale"])
+    np.testing.assert_array_equal(host(q.Qh_scales), step_grouped(ref["qh"]["scale"]))
     np.testing.assert_array_equal(host(q.Qt), mx.pack(ref["qt"]["codes"].T))
-    np.testing.assert_array_equal(host(q.Qt_scales), ref["qt"]["scale"])
+    np.testing.assert_array_equal(host(q.Qt_scales), step_grouped(ref["qt"]["scale"]))
     np.testing.assert_array_equal(host(gpu["Wt"]), mx.pack(ref["fw"]["codes"].T))
-    np.testing.assert_array_equal(host(gpu["Wts"]), ref["fw"]["scale"])
+    np.testing.assert_array_equal(host(gpu["Wts"]), step_grouped(ref["fw"]["scale"]))
     np.testing.assert_array_equal(host(gpu["Xt"]), mx.pack(ref["fx"]["codes"].T))
-    np.testing.assert_array_equal(host(gpu["Xts"]), ref["fx"]["scale"])
+    np.testing.assert_array_equal(host(gpu["Xts"]), step_grouped(ref["fx"]["scale"]))
     assert int(host(q.flags)[0]) == 0
 
 
@@ -137,9 +143,11 @@ def test_mx_zero_and_nonfinite_blocks():
         assert ref["flag"]
         c = ref["codes"] if axis == 1 else ref["codes"].T
         np.testing.assert_array_equal(host(codes), mx.pack(c))
-        np.testing.assert_array_equal(host(scales), ref["scale"])
+        np.testing.assert_array_equal(host(scales), step_grouped(ref["scale"]))
     assert int(host(q.flags)[0]) & s3r.FLAG_NONFINITE
-    assert host(q.Qh_scales)[5, 1] == 0 and host(q.Qt_scales)[7, 2] == 0 and host(q.Qh_scales)[9, 3] == 255
+    # (row 5, block 1), (channel 7, block 2), (row 9, block 3): step 0, byte 4 r + b
+    assert host(q.Qh_scales)[0, 4 * 5 + 1] == 0 and host(q.Qt_scales)[0, 4 * 7 + 2] == 0
+    assert host(q.Qh_scales)[0, 4 * 9 + 3] == 255
 
 
 def test_mx_headline_workload_sampled():
@@ -159,9 +167,9 @@ def test_mx_headline_workload_sampled():
                       rows_per_example=S, seed=0, dx_rows=rows, dw_rows=crow, cols=cols)
     q = gpu["q"]
     np.testing.assert_array_equal(host(q.Qh), mx.pack(ref["qh"]["codes"]))
-    np.testing.assert_array_equal(host(q.Qh_scales), ref["qh"]["scale"])
+    np.testing.assert_array_equal(host(q.Qh_scales), step_grouped(ref["qh"]["scale"]))
     np.testing.assert_array_equal(host(q.Qt), mx.pack(ref["qt"]["codes"].T))
-    np.testing.assert_array_equal(host(q.Qt_scales), ref["qt"]["scale"])
+    np.testing.assert_array_equal(host(q.Qt_scales), step_grouped(ref["qt"]["scale"]))
     np.testing.assert_array_equal(host(gpu["Wt"][cols]), mx.pack(ref["fw"]["codes"].T))
     np.testing.assert_array_equal(host(gpu["Xt"][cols]), mx.pack(ref["fx"]["codes"].T))
     for nm, st in (("h", q.ec_h), ("t", q.ec_t)):

@@ -216,8 +216,8 @@ def test_mx_argument_errors(L):
 
     def q(desc, G=P(1 << 20), Qh=P(1 << 21), Qt=P(1 << 22), ld_qt=None, ec=ec6, wsb=1 << 24, ws=P(1 << 23)):
         return L.s3r_mx_quantize(ctypes.byref(desc), G, 0, desc.cols, Qh, desc.cols // 2, P(1 << 19),
-                                 desc.cols // 32, Qt, desc.rows // 2 if ld_qt is None else ld_qt, P(1 << 18),
-                                 desc.rows // 32, *ec, None, ws, wsb, None)
+                                 4 * desc.rows, Qt, desc.rows // 2 if ld_qt is None else ld_qt, P(1 << 18),
+                                 4 * desc.cols, *ec, None, ws, wsb, None)
 
     assert q(s3r.qdesc(T, 96, 128, s3r.S3R)) == -1                      # D not a multiple of 128
     assert q(s3r.qdesc(T, D, 64, s3r.S3R)) == -1                        # rows per example not a multiple of 128
@@ -231,21 +231,21 @@ def test_mx_argument_errors(L):
     assert q(ok, ws=P((1 << 23) + 64)) == -1
     assert s3r.s3r_mx_workspace(s3r.qdesc(T, 96, 128), d_in) == 0
 
-    def dx(desc, ld_wt=D // 2, ldws=D // 32, Wt=P(1 << 24), ec=True, wsb=1 << 24):
+    def dx(desc, ld_wt=D // 2, ldws=4 * d_in, Wt=P(1 << 24), ec=True, wsb=1 << 24):
         e = ec6[:3] if ec else [None] * 3
-        return L.s3r_mx_backward_dx(ctypes.byref(desc), P(1 << 20), D // 2, P(1 << 19), D // 32, Wt, ld_wt,
+        return L.s3r_mx_backward_dx(ctypes.byref(desc), P(1 << 20), D // 2, P(1 << 19), 4 * T, Wt, ld_wt,
                                     P(1 << 18), ldws, d_in, ec6[3], *e, P(1 << 25), d_in, P(1 << 23), wsb, None)
 
     assert dx(ok, ld_wt=D // 2 - 16) == -1                              # codes ld below K/2
-    assert dx(ok, ldws=3) == -1                                         # scale ld below K/32
+    assert dx(ok, ldws=4 * d_in - 4) == -1                              # scale step stride below 4 rows
     assert dx(ok, Wt=P((1 << 24) + 4)) == -1
     assert dx(ok, ec=False) == -1                                       # TWO_WAY needs the statistics
     assert dx(ok, wsb=0) == -3
 
     def dw(desc, xs=ec6[3]):
         R = desc.rows
-        return L.s3r_mx_backward_dw(ctypes.byref(desc), P(1 << 20), R // 2, P(1 << 19), R // 32, P(1 << 24),
-                                    R // 2, P(1 << 18), R // 32, d_in, xs, *ec6[:3], P(1 << 25), d_in, P(1 << 23),
+        return L.s3r_mx_backward_dw(ctypes.byref(desc), P(1 << 20), R // 2, P(1 << 19), 4 * D, P(1 << 24),
+                                    R // 2, P(1 << 18), 4 * d_in, d_in, xs, *ec6[:3], P(1 << 25), d_in, P(1 << 23),
                                     1 << 24, None)
 
     assert dw(ok, xs=None) == -1
@@ -253,7 +253,7 @@ def test_mx_argument_errors(L):
     assert dw(s3r.qdesc(128 * 9, D, 128, s3r.S3R, s3r.EC_DX_ONLY)) in (-4, -5)  # dW uncorrected: any B
 
     def op(rows=T, cols=d_in, S=T, ld_t=T // 2, wsb=1 << 20):
-        return L.s3r_mx_operand(rows, cols, S, P(1 << 20), 0, cols, P(1 << 21), ld_t, P(1 << 19), rows // 32,
+        return L.s3r_mx_operand(rows, cols, S, P(1 << 20), 0, cols, P(1 << 21), ld_t, P(1 << 19), 4 * cols,
                                 None, None, P(1 << 23), wsb, None)
 
     assert op(rows=200) == -1 and op(S=96) == -1 and op(ld_t=T // 2 - 16) == -1 and op(ld_t=T // 2 + 4) == -1
@@ -272,14 +272,14 @@ def test_mx_binding_marshals_valid_arguments(L):
     u8 = lambda r, c: _FakeDev((r, c), (c, 1), dtype=torch.uint8)
     st = (f32(T), f32(2, D), f32(2))
     expect = (-4, -5)
-    assert s3r.s3r_mx_quantize(desc, f32(T, D), u8(T, D // 2), u8(T, D // 32), u8(D, T // 2), u8(D, T // 32),
+    assert s3r.s3r_mx_quantize(desc, f32(T, D), u8(T, D // 2), u8(D // 128, 4 * T), u8(D, T // 2), u8(T // 128, 4 * D),
                                *st, *st, None, ws, 0, rc_only=True) in expect
-    assert s3r.s3r_mx_backward_dx(desc, u8(T, D // 2), u8(T, D // 32), u8(d_in, D // 2), u8(d_in, D // 32),
+    assert s3r.s3r_mx_backward_dx(desc, u8(T, D // 2), u8(D // 128, 4 * T), u8(d_in, D // 2), u8(D // 128, 4 * d_in),
                                   f32(d_in), *st, f32(T, d_in), ws, 0, rc_only=True) in expect
-    assert s3r.s3r_mx_backward_dw(desc, u8(D, T // 2), u8(D, T // 32), u8(d_in, T // 2), u8(d_in, T // 32),
+    assert s3r.s3r_mx_backward_dw(desc, u8(D, T // 2), u8(T // 128, 4 * D), u8(d_in, T // 2), u8(T // 128, 4 * d_in),
                                   f32(2, d_in), *st, f32(D, d_in), ws, 0, rc_only=True) in expect
     ows = _FakeDev((s3r.s3r_mx_operand_workspace(T, d_in),), (1,), addr=1 << 24)
-    assert s3r.s3r_mx_operand(f32(T, d_in), u8(d_in, T // 2), u8(d_in, T // 32), f32(2, d_in), 128, None, ows, 0,
+    assert s3r.s3r_mx_operand(f32(T, d_in), u8(d_in, T // 2), u8(T // 128, 4 * d_in), f32(2, d_in), 128, None, ows, 0,
                               rc_only=True) in expect
 
 
