@@ -400,7 +400,9 @@ int s3r_mx_operand(int64_t rows, int64_t cols, int64_t rows_per_example,
                    float* colsum, uint32_t* flags, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* s3r_mx_quantize: G [T x D] (f32 or bf16) to Q_h (codes [T x D/2], scales
- * [D/128][T][4]) and Q_t (codes [D x T/2], scales [T/128][D][4]).  With EC: the
+ * [D/128][T][4]) and Q_t (codes [D x T/2], scales [T/128][D][4]).  G is read
+ * in 16-byte pieces: its base is 16-byte aligned and ld_g a multiple of 8
+ * (bf16) or 4 (f32) elements.  With EC: the
  * statistics of each quantization's error, ec_row_* [T] (eps_t), ec_col_*
  * [B x D] (ebar_b), ec_mean_* [B] (mu_b); all six pointers given exactly when
  * desc->ec != S3R_EC_NONE.  Both quantizations are written whatever the

@@ -363,7 +363,7 @@ size_t s3r_mx_operand_workspace(int64_t rows, int64_t cols) {
 size_t s3r_mx_workspace(const s3r_qdesc* d, int64_t d_in) {
   if (check_mx_desc(d) != S3R_OK || d_in < 0) return 0;
   return std::max(mx_quant_workspace(d->rows, d->cols, d->ec != S3R_EC_NONE),
-                  mx_backward_workspace(d->rows, d_in, d->rows / d->rows_per_example));
+                  mx_backward_workspace(d->rows, d->cols, d_in, d->rows / d->rows_per_example));
 }
 
 int s3r_mx_operand(int64_t rows, int64_t cols, int64_t rows_per_example, const void* M, int32_t dtype, int64_t ld,
@@ -394,6 +394,7 @@ int s3r_mx_quantize(const s3r_qdesc* d, const void* G, int32_t g_dtype, int64_t 
   if (g_dtype != S3R_F32 && g_dtype != S3R_BF16) return S3R_ERR_UNSUPPORTED;
   const int64_t T = d->rows, D = d->cols;
   if (!G || !Qh || !Qh_scales || !Qt || !Qt_scales || ld_g < D) return S3R_ERR_INVALID_ARG;
+  if (!al16(G) || (ld_g * (g_dtype == S3R_BF16 ? 2 : 4)) % 16) return S3R_ERR_INVALID_ARG;   // 16-byte row chunks
   if (ld_qh < D / 2 || (ld_qh & 3) || ld_qhs < 4 * T || ld_qt < T / 2 || (ld_qt & 15) || ld_qts < 4 * D)
     return S3R_ERR_INVALID_ARG;
   if (!al16(Qt) || ((uintptr_t)Qh & 3u)) return S3R_ERR_INVALID_ARG;
@@ -432,7 +433,7 @@ int s3r_mx_backward_dx(const s3r_qdesc* d, const uint8_t* Qh, int64_t ld_qh, con
   if ((rc = check_mx_operand(Wt, ld_wt, Wt_scales, ld_wts, d_in, D))) return rc;
   const bool ec = d->ec == S3R_EC_DX_ONLY || d->ec == S3R_EC_TWO_WAY;
   if (ec && (!r_W || !ec_row_h || !ec_col_h || !ec_mean_h)) return S3R_ERR_INVALID_ARG;
-  if (ws_bytes < mx_backward_workspace(T, d_in, B)) return S3R_ERR_WORKSPACE;
+  if (ws_bytes < mx_backward_workspace(T, D, d_in, B)) return S3R_ERR_WORKSPACE;
   if (!ws || ((uintptr_t)ws & 255u)) return S3R_ERR_INVALID_ARG;
   if ((rc = check_arch())) return rc;
   MxBwArgs a{};
@@ -455,7 +456,7 @@ int s3r_mx_backward_dw(const s3r_qdesc* d, const uint8_t* Qt, int64_t ld_qt, con
   if ((rc = check_mx_operand(Xt, ld_xt, Xt_scales, ld_xts, d_in, T))) return rc;
   const bool ec = d->ec == S3R_EC_TWO_WAY || d->ec == S3R_EC_DW_ONLY;
   if (ec && (!xs || !ec_row_t || !ec_col_t || !ec_mean_t || B > 8)) return S3R_ERR_INVALID_ARG;
-  if (ws_bytes < mx_backward_workspace(T, d_in, B)) return S3R_ERR_WORKSPACE;
+  if (ws_bytes < mx_backward_workspace(T, D, d_in, B)) return S3R_ERR_WORKSPACE;
   if (!ws || ((uintptr_t)ws & 255u)) return S3R_ERR_INVALID_ARG;
   if ((rc = check_arch())) return rc;
   MxBwArgs a{};

@@ -48,34 +48,6 @@ __device__ __forceinline__ int block_scale_byte(uint32_t abits) {
 // 2^-k as fp32 for a scale byte (k = byte - 127), exact for every k in [-127, 127].
 __device__ __forceinline__ float inv_scale(int byte) { return __builtin_ldexpf(1.f, 127 - byte); }
 
-// E2M1 code (sign << 3 | index) of y, |y| <= 6: RTNE (R < 0) or floor(y / s + r) with
-// R = r * 2^24.  The floor is exact: t = y / s * 2^24 is an exact power-of-two scaling
-// (|t| < 2^28), X = floor(t) by one conversion, and floor(y / s + r) = (X + R) >> 24.
-__device__ __forceinline__ uint32_t e2m1_code(float y, int32_t R, float& qv) {
-  const float a = fabsf(y);
-  const float s = a < 2.f ? 0.5f : (a < 4.f ? 1.f : 2.f);
-  const float ys = y * (a < 2.f ? 2.f : (a < 4.f ? 1.f : 0.5f));  // y / s, exact: s is a power of two
-  int32_t n;                                                      // the multiple of s
-  if (R < 0) {
-    n = (int32_t)__builtin_rintf(ys);
-  } else {
-    const float t = ys * 16777216.f;
-    int32_t X;
-    asm("v_cvt_flr_i32_f32 %0, %1" : "=v"(X) : "v"(t));
-    n = (X + R) >> 24;
-  }
-  qv = (float)n * s;                                              // a grid value in [-6, 6]
-  const float m = fabsf(qv);
-  // index into 0, 0.5, 1, 1.5, 2, 3, 4, 6
-  const uint32_t idx = m < 2.f ? (uint32_t)(m * 2.f) : (m < 4.f ? (uint32_t)m + 2u : (m < 5.f ? 6u : 7u));
-  return (qv < 0.f ? 8u : 0u) | idx;
-}
-
-__device__ __forceinline__ float e2m1_value(uint32_t c) {
-  const uint32_t i = c & 7u;
-  const float m = i < 4u ? 0.5f * (float)i : (i == 4u ? 2.f : (i == 5u ? 3.f : (i == 6u ? 4.f : 6.f)));
-  return (c & 8u) ? -m : m;
-}
 
 template <typename TIn>
 __device__ __forceinline__ float load_elem(const TIn* p) {
@@ -91,214 +63,378 @@ struct MxQuant {
   int64_t D_index;          // SR element index e = t * D_index + j (G's row-major index)
 };
 
-// ------------------------------------------ blocks along the columns ----
-// Source M [R x C] row-major, blocks of 32 along C.  A block of 256 threads
-// covers 64 rows x 512 columns; a lane handles 8 consecutive elements, four
-// lanes a block.  Out: codes [R x C/2] (row-major, ld_out bytes), scales in
-// the step-grouped layout [C/128][R][4] (ld_s bytes per step).  With EC: the error row sums of each row over the
-// tile's 512 columns (row_part[t * n_ct + ctile]) and the error column sums of
-// the tile's 64 rows (col_part[rtile * C + j]).
-template <typename TIn, bool EC>
-__global__ __launch_bounds__(256) void mx_quant_rows_kernel(MxQuant p, const TIn* __restrict__ M,
-                                                            uint8_t* __restrict__ out, int64_t ld_out,
-                                                            uint8_t* __restrict__ sc, int64_t ld_s,
-                                                            float* __restrict__ row_part, float* __restrict__ col_part,
-                                                            uint32_t* __restrict__ flags) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t r0 = (int64_t)blockIdx.x * 64;
-  const int64_t j0 = (int64_t)blockIdx.y * 512 + lane * 8;
-  const int n_ct = (int)((p.C + 511) / 512);
-  __shared__ float s_col[4][512];
-  float col[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) col[i] = 0.f;
-  const bool active = j0 < p.C;                     // C % 32 == 0: a lane is all in or all out
-  float rs[16];
-#pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    const int64_t t = r0 + wave + 4 * k;
-    float v[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = active ? load_elem<TIn>(M + t * p.ld + j0 + i) : 0.f;
-    uint32_t m = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) m = max(m, __float_as_uint(v[i]) & 0x7FFFFFFFu);
-    m = max(m, (uint32_t)__shfl_xor((int)m, 1, 64));
-    m = max(m, (uint32_t)__shfl_xor((int)m, 2, 64));
-    const int sb = block_scale_byte(m);
-    const bool bad = sb == 255;
-    const float inv = bad ? 0.f : inv_scale(sb);
-    int32_t Rt[8];
-    if (p.mode == 2) {
-      const int32_t r = s3r_threshold_units24(t, p.layer, p.seed, kTagS3R + p.stream_word);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) Rt[i] = r;
-    } else if (p.mode == 1) {
-#pragma unroll
-      for (int i = 0; i < 8; i += 4) {
-        const uint64_t e = (uint64_t)t * (uint64_t)p.D_index + (uint64_t)(j0 + i);   // e % 4 == 0
-        const U4 w = philox4x32_10((uint32_t)(e >> 2), (uint32_t)(e >> 34), p.layer, kTagSR + p.stream_word,
-                                   (uint32_t)p.seed, (uint32_t)(p.seed >> 32));
-        Rt[i] = sr_units24(w.x); Rt[i + 1] = sr_units24(w.y); Rt[i + 2] = sr_units24(w.z); Rt[i + 3] = sr_units24(w.w);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) Rt[i] = -1;
-    }
-    uint32_t packed = 0;
-    float es = 0.f;
-    const float scale = bad ? 0.f : __builtin_ldexpf(1.f, sb - 127);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float qv;
-      const uint32_t c = bad ? 0u : e2m1_code(v[i] * inv, Rt[i], qv);
-      packed |= c << (4 * i);
-      if constexpr (EC) {
-        const float e = bad ? 0.f : qv * scale - v[i];
-        es += e;
-        col[i] += e;
-      }
-    }
-    if (active) {
-      *reinterpret_cast<uint32_t*>(out + t * ld_out + j0 / 2) = packed;
-      if ((lane & 3) == 0) sc[(j0 / 128) * ld_s + t * 4 + ((j0 / 32) & 3)] = (uint8_t)sb;
-      if (bad && flags && (lane & 3) == 0) atomicOr(flags, S3R_FLAG_NONFINITE);
-    }
-    rs[k] = es;
+// E2M1 code of v in a block with scale exponent k (kp1 = k + 1), on the
+// block's grid in units of the spacing s = 2^(M - k - 2), M = max(e(v), k + 1)
+// with e(v) the frexp exponent (|v| = m 2^e, m in [0.5, 1)), taken from the
+// exponent field (zero and subnormals give -126 <= k + 1): s is 0.5, 1 or 2
+// as |v / 2^k| lies below 2, in [2, 4) or in [4, 6].  t = v / s * 2^24 is an
+// exact power-of-two scaling; n = floor(t / 2^24 + R / 2^24) = (floor(t) + R)
+// >> 24 (SR / S3R, R the threshold in units of 2^-24) or rint(v / s) (RTNE).
+// |n| + 2 (M - k - 1) is the index into 0, 0.5, 1, 1.5, 2, 3, 4, 6, and the
+// dequantized value n s 2^k = n 2^(M - 2).
+template <bool RT>
+__device__ __forceinline__ uint32_t e2m1_round(float v, int kp1, int32_t R, int& n, int& M) {
+  M = max((int)((__float_as_uint(v) >> 23) & 0xFFu) - 126, kp1);
+  if constexpr (RT) {
+    n = (int)__builtin_rintf(__builtin_ldexpf(v, 2 - M));
+  } else {
+    const float t = __builtin_ldexpf(v, 26 - M);
+    int32_t X;
+    asm("v_cvt_flr_i32_f32 %0, %1" : "=v"(X) : "v"(t));
+    n = (X + R) >> 24;
   }
-  if constexpr (EC) {
-    // reduce-scatter of the 16 row sums across the wave: lane l then holds row k = l >> 2
-    float r8[8], r4[4], r2[2], r1;
-    const bool hi32 = lane & 32, hi16 = lane & 16, hi8 = lane & 8, hi4 = lane & 4;
+  const uint32_t idx = (uint32_t)(abs(n) + 2 * (M - kp1));
+  return (n < 0 ? 8u : 0u) | idx;
+}
+
+// Scale byte of a block of 32 values (255: a non-finite value in the block).
+__device__ __forceinline__ int mx_scale(const float (&v)[32]) {
+  uint32_t m = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float send = hi32 ? rs[i] : rs[i + 8];
-      r8[i] = (hi32 ? rs[i + 8] : rs[i]) + __shfl_xor(send, 32, 64);
-    }
+  for (int i = 0; i < 32; ++i) m = max(m, __float_as_uint(v[i]) & 0x7FFFFFFFu);
+  return block_scale_byte(m);
+}
+
+// Element i of a block with scale byte sb: its code ORed into w[i / 8], and
+// (EC) its error dequant - v.  A non-finite block (sb 255) gets zero codes and
+// zero errors.
+template <bool RT>
+__device__ __forceinline__ float mx_elem(float v, int sb, int32_t R, int i, uint32_t (&w)[4]) {
+  int n, M;
+  const uint32_t c = e2m1_round<RT>(v, sb - 126, R, n, M);
+  const bool bad = sb == 255;
+  w[i >> 3] |= (bad ? 0u : c) << (4 * (i & 7));
+  return bad ? 0.f : __builtin_ldexpf((float)n, M - 2) - v;
+}
+
+// Quantize 32 values with one block scale: codes packed 8 per word into w[4],
+// (EC) the errors into e[32]; returns the scale byte.
+template <bool EC, bool RT>
+__device__ __forceinline__ int mx_block(const float (&v)[32], const int32_t (&R)[32], uint32_t (&w)[4],
+                                        float (&e)[32]) {
+  const int sb = mx_scale(v);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float send = hi16 ? r8[i] : r8[i + 4];
-      r4[i] = (hi16 ? r8[i + 4] : r8[i]) + __shfl_xor(send, 16, 64);
-    }
+  for (int q = 0; q < 4; ++q) w[q] = 0u;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const float send = hi8 ? r4[i] : r4[i + 2];
-      r2[i] = (hi8 ? r4[i + 2] : r4[i]) + __shfl_xor(send, 8, 64);
-    }
-    {
-      const float send = hi4 ? r2[0] : r2[1];
-      r1 = (hi4 ? r2[1] : r2[0]) + __shfl_xor(send, 4, 64);
-    }
-    r1 += __shfl_xor(r1, 2, 64);
-    r1 += __shfl_xor(r1, 1, 64);
-    if ((lane & 3) == 0) row_part[(r0 + wave + 4 * (lane >> 2)) * n_ct + blockIdx.y] = r1;
+  for (int i = 0; i < 32; ++i) {
+    const float x = mx_elem<RT>(v[i], sb, R[i], i, w);
+    if constexpr (EC) e[i] = x;
+  }
+  return sb;
+}
+
+// ------------------------------------------- both blockings of G, fused ----
+// One read of G gives Q_h (blocks of 32 along D) and Q_t (blocks of 32 along
+// T, stored transposed).  A block of 256 threads owns a tile of 64 tokens x
+// 256 channels, staged in LDS as read:
+//   phase A  thread (row tid / 8 + 32 h, block tid % 8), h = 0, 1: 32
+//            consecutive elements of a row (coalesced 16-byte loads) and its
+//            Q_h block: scale byte and 16 code bytes;
+//   phase B  thread (channels 2 p, 2 p + 1 with p = tid % 128, token block
+//            tid / 128): 2 x 32 elements from LDS, two Q_t blocks: scale
+//            bytes and 16 code bytes into rows 2 p, 2 p + 1 of Q_t.
+// Thresholds: S3R per token from LDS; SR per element from the same counters as
+// the INT8 path (element e = t D + j, word e % 4 of counter e / 4).  In phase
+// B a counter's four channels belong to two adjacent lanes: each draws the
+// counters of every other token and the two swap the word pairs.
+// EC partials (fixed order, fp32): E_h row sums over the tile's channels
+// (rph[t * n_ct + ctile]) and column sums over its 64 tokens (cph[ttile * D +
+// j]), both from phase A by lane reductions; E_t column sums per 32-token
+// block (cpt[tblk * D + j]) and row sums over the tile's channels (rpt[t *
+// n_ct + ctile]) from phase B.
+constexpr int kFusedRows = 64, kFusedCols = 256;
+
+template <typename TIn>
+struct FusedLds {
+  static constexpr int kPad = 16 / (int)sizeof(TIn);        // one 16-byte chunk per row
+  TIn g[kFusedRows][kFusedCols + kPad];
+  int32_t thr[kFusedRows];
+  float colh[4][kFusedCols];
+  float red[4][32];
+};
+
+template <typename TIn>
+__device__ __forceinline__ void load32(const TIn* src, float (&v)[32], bool active) {
+  if constexpr (sizeof(TIn) == 2) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) s_col[wave][lane * 8 + i] = col[i];
-    __syncthreads();
-    for (int c = threadIdx.x; c < 512; c += 256) {
-      const int64_t j = (int64_t)blockIdx.y * 512 + c;
-      if (j < p.C) col_part[(int64_t)blockIdx.x * p.C + j] = ((s_col[0][c] + s_col[1][c]) + s_col[2][c]) + s_col[3][c];
+    for (int q = 0; q < 4; ++q) {
+      const uint4 w = active ? reinterpret_cast<const uint4*>(src)[q] : make_uint4(0u, 0u, 0u, 0u);
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[q * 8 + 2 * i] = __uint_as_float(ww[i] << 16);
+        v[q * 8 + 2 * i + 1] = __uint_as_float(ww[i] & 0xFFFF0000u);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const float4 w = active ? reinterpret_cast<const float4*>(src)[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+      v[q * 4] = w.x; v[q * 4 + 1] = w.y; v[q * 4 + 2] = w.z; v[q * 4 + 3] = w.w;
     }
   }
 }
 
-// ------------------------------------------------ blocks along the rows ----
-// Source M [R x C] row-major, blocks of 32 along R, output transposed:
-// codes [C x R/2] (row c holds column c of M), scales [R/128][C][4].  A block of
-// 256 threads covers 128 rows x 64 columns: lane = column, wave = one 32-row
-// block.  Per thread: the amax of its 32 values, the scale, 32 codes = 16
-// bytes written contiguously (the four waves write 64 contiguous bytes of an
-// output row).  VSUM: the column sums of the dequantized values of the block
-// (vsum_part[rblk * C + c]).  EC: the error column sums (col_part[rblk * C + c])
-// and the error row sums over the tile's 64 columns (row_part[t * n_ct + ctile]).
-template <typename TIn, bool EC, bool VSUM>
-__global__ __launch_bounds__(256) void mx_quant_cols_kernel(MxQuant p, const TIn* __restrict__ M,
-                                                            uint8_t* __restrict__ out, int64_t ld_out,
-                                                            uint8_t* __restrict__ sc, int64_t ld_s,
-                                                            float* __restrict__ row_part, float* __restrict__ col_part,
-                                                            float* __restrict__ vsum_part, uint32_t* __restrict__ flags) {
+// two adjacent channels of one staged row
+__device__ __forceinline__ void lds_pair(const uint16_t* p, float& a, float& b) {
+  const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
+  a = __uint_as_float(w << 16);
+  b = __uint_as_float(w & 0xFFFF0000u);
+}
+__device__ __forceinline__ void lds_pair(const float* p, float& a, float& b) {
+  const float2 w = *reinterpret_cast<const float2*>(p);
+  a = w.x;
+  b = w.y;
+}
+
+template <typename TIn, bool EC, int MODE>
+__global__ __launch_bounds__(256, sizeof(TIn) == 2 ? 3 : 2) void mx_quant_fused_kernel(MxQuant p, const TIn* __restrict__ G,
+                                                             uint8_t* __restrict__ Qh, int64_t ld_qh,
+                                                             uint8_t* __restrict__ Qhs, int64_t ld_qhs,
+                                                             uint8_t* __restrict__ Qt, int64_t ld_qt,
+                                                             uint8_t* __restrict__ Qts, int64_t ld_qts,
+                                                             float* __restrict__ rph, float* __restrict__ cph,
+                                                             float* __restrict__ rpt, float* __restrict__ cpt,
+                                                             uint32_t* __restrict__ flags) {
+  constexpr bool RT = MODE == 0;
+  __shared__ __attribute__((aligned(16))) FusedLds<TIn> L;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t t0 = (int64_t)blockIdx.x * kFusedRows, c0 = (int64_t)blockIdx.y * kFusedCols;
+  const int n_ct = (int)((p.C + kFusedCols - 1) / kFusedCols);
+  const uint32_t key0 = (uint32_t)p.seed, key1 = (uint32_t)(p.seed >> 32);
+  if (MODE == 2 && tid < kFusedRows)
+    L.thr[tid] = s3r_threshold_units24(t0 + tid, p.layer, p.seed, kTagS3R + p.stream_word);
+  __syncthreads();
+  bool any_bad = false;
+
+  // ---- phase A: Q_h
+  const int cb = tid & 7;
+  const int64_t ca = c0 + cb * 32;
+  const bool act_a = ca < p.C;                       // C % 32 == 0
+  float ecol[EC ? 32 : 1];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = (tid >> 3) + 32 * h;
+    const int64_t t = t0 + r;
+    float v[32];
+    load32<TIn>(G + t * p.ld + ca, v, act_a);
+    {
+      // stage the raw tile
+      constexpr int kChunks = 32 * (int)sizeof(TIn) / 16;
+#pragma unroll
+      for (int q = 0; q < kChunks; ++q) {
+        uint4 x;
+        if constexpr (sizeof(TIn) == 2) {
+          x = make_uint4((__float_as_uint(v[q * 8]) >> 16) | (__float_as_uint(v[q * 8 + 1]) & 0xFFFF0000u),
+                         (__float_as_uint(v[q * 8 + 2]) >> 16) | (__float_as_uint(v[q * 8 + 3]) & 0xFFFF0000u),
+                         (__float_as_uint(v[q * 8 + 4]) >> 16) | (__float_as_uint(v[q * 8 + 5]) & 0xFFFF0000u),
+                         (__float_as_uint(v[q * 8 + 6]) >> 16) | (__float_as_uint(v[q * 8 + 7]) & 0xFFFF0000u));
+        } else {
+          x = make_uint4(__float_as_uint(v[q * 4]), __float_as_uint(v[q * 4 + 1]), __float_as_uint(v[q * 4 + 2]),
+                         __float_as_uint(v[q * 4 + 3]));
+        }
+        reinterpret_cast<uint4*>(&L.g[r][cb * 32])[q] = x;
+      }
+    }
+    const int sb = mx_scale(v);
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+    float es = 0.f;
+    const int32_t rs3 = MODE == 2 ? L.thr[r] : -1;
+#pragma unroll
+    for (int i4 = 0; i4 < 8; ++i4) {
+      int32_t R4[4] = {rs3, rs3, rs3, rs3};
+      if constexpr (MODE == 1) {
+        const uint64_t e = (uint64_t)t * (uint64_t)p.D_index + (uint64_t)(ca + 4 * i4);   // e % 4 == 0
+        const U4 u = philox4x32_10((uint32_t)(e >> 2), (uint32_t)(e >> 34), p.layer, kTagSR + p.stream_word,
+                                   key0, key1);
+        R4[0] = sr_units24(u.x); R4[1] = sr_units24(u.y); R4[2] = sr_units24(u.z); R4[3] = sr_units24(u.w);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = 4 * i4 + j;
+        const float x = mx_elem<RT>(v[i], sb, R4[j], i, w);
+        if constexpr (EC) {
+          es += x;
+          ecol[i] = h == 0 ? x : ecol[i] + x;
+        }
+      }
+    }
+    if (act_a) {
+      *reinterpret_cast<uint4*>(Qh + t * ld_qh + ca / 2) = make_uint4(w[0], w[1], w[2], w[3]);
+      const int64_t blk = ca / 32;
+      Qhs[(blk / 4) * ld_qhs + t * 4 + (blk & 3)] = (uint8_t)sb;
+      any_bad |= sb == 255;
+    }
+    if constexpr (EC) {
+      es += __shfl_xor(es, 1, 64);
+      es += __shfl_xor(es, 2, 64);
+      es += __shfl_xor(es, 4, 64);
+      if (cb == 0) rph[t * n_ct + blockIdx.y] = es;
+    }
+    asm volatile("" ::: "memory");                   // the second item's loads after the first's work
+  }
+  if constexpr (EC) {
+    // E_h column sums over the tile's 64 rows: the lanes with this block (lane bits 5..3 vary)
+    // reduce-scatter the 32 columns, 4 per lane, then the 4 waves add through LDS
+#pragma unroll
+    for (int o = 16; o >= 4; o >>= 1) {
+      const bool hi = lane & (2 * o);      // lane bits 5, 4, 3 for o = 16, 8, 4
+#pragma unroll
+      for (int i = 0; i < o; ++i) {
+        const float send = hi ? ecol[i] : ecol[i + o];
+        ecol[i] = (hi ? ecol[i + o] : ecol[i]) + __shfl_xor(send, 2 * o, 64);
+      }
+    }
+    const int j0 = cb * 32 + ((lane >> 5) & 1) * 16 + ((lane >> 4) & 1) * 8 + ((lane >> 3) & 1) * 4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) L.colh[wave][j0 + j] = ecol[j];
+  }
+  __syncthreads();
+  if constexpr (EC) {
+    const int64_t c = c0 + tid;
+    if (c < p.C) cph[(t0 / 64) * p.C + c] = ((L.colh[0][tid] + L.colh[1][tid]) + L.colh[2][tid]) + L.colh[3][tid];
+  }
+
+  // ---- phase B: Q_t, channels c0 + 2 pp, + 1, tokens t0 + 32 tb ..
+  const int pp = tid & 127, tb = tid >> 7;
+  const int64_t cpair = c0 + 2 * pp;
+  const bool act_b = cpair < p.C;                    // C even: both channels or neither
+  // first pass over the staged column pair: the two block scales; the values are read again below
+  uint32_t ma = 0, mb = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    float xa, xb;
+    lds_pair(&L.g[32 * tb + i][2 * pp], xa, xb);
+    ma = max(ma, __float_as_uint(xa) & 0x7FFFFFFFu);
+    mb = max(mb, __float_as_uint(xb) & 0x7FFFFFFFu);
+  }
+  const int sba = block_scale_byte(ma), sbb = block_scale_byte(mb);
+  uint32_t wa[4] = {0u, 0u, 0u, 0u}, wb[4] = {0u, 0u, 0u, 0u};
+  float csa = 0.f, csb = 0.f;
+  const int q = pp & 1;                              // SR: lane parity within a 4-channel counter
+  // four groups of 8 rows, not unrolled (few live registers); after each group the code
+  // words shift down one place, so wa[g] ends holding group g's eight codes
+#pragma unroll 1
+  for (int g = 0; g < 4; ++g) {
+    float xs[8];                                     // EC: this thread's two channels' errors, rows 8g ..
+    uint32_t ga[4] = {0u, 0u, 0u, 0u}, gb[4] = {0u, 0u, 0u, 0u};   // codes land in word 0
+#pragma unroll
+    for (int mm = 0; mm < 4; ++mm) {
+      const int r2 = 32 * tb + 8 * g + 2 * mm;       // staged rows r2, r2 + 1
+      int32_t ra[2], rb[2];
+      if constexpr (MODE == 2) {
+        ra[0] = rb[0] = L.thr[r2];
+        ra[1] = rb[1] = L.thr[r2 + 1];
+      } else if constexpr (MODE == 1) {
+        // this lane draws the counter of token r2 + q (channels cpair - 2q .. + 3) and swaps the
+        // other channel pair's words with its neighbour, which drew token r2 + 1 - q
+        const int64_t tq = t0 + r2 + q;
+        const uint64_t e = (uint64_t)tq * (uint64_t)p.D_index + (uint64_t)(cpair - 2 * q);
+        const U4 u = philox4x32_10((uint32_t)(e >> 2), (uint32_t)(e >> 34), p.layer, kTagSR + p.stream_word,
+                                   key0, key1);
+        const uint32_t own0 = q ? u.z : u.x, own1 = q ? u.w : u.y;
+        const uint32_t give0 = q ? u.x : u.z, give1 = q ? u.y : u.w;
+        const uint32_t got0 = (uint32_t)__shfl_xor((int)give0, 1, 64);
+        const uint32_t got1 = (uint32_t)__shfl_xor((int)give1, 1, 64);
+        ra[q] = sr_units24(own0); rb[q] = sr_units24(own1);
+        ra[1 - q] = sr_units24(got0); rb[1 - q] = sr_units24(got1);
+      } else {
+        ra[0] = ra[1] = rb[0] = rb[1] = -1;
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int i = 2 * mm + j;                    // position within the group's code word
+        float va, vb;
+        lds_pair(&L.g[r2 + j][2 * pp], va, vb);
+        const float xa = mx_elem<RT>(va, sba, ra[j], i, ga);
+        const float xb = mx_elem<RT>(vb, sbb, rb[j], i, gb);
+        if constexpr (EC) {
+          csa += xa;
+          csb += xb;
+          xs[i] = xa + xb;
+        }
+      }
+    }
+    wa[0] = wa[1]; wa[1] = wa[2]; wa[2] = wa[3]; wa[3] = ga[0];
+    wb[0] = wb[1]; wb[1] = wb[2]; wb[2] = wb[3]; wb[3] = gb[0];
+    if constexpr (EC) {
+      // the 8 rows over the lanes that differ in bits 5..3 (reduce-scatter: lane keeps row
+      // 8g + lane / 8), then over bits 2..0; the two waves of this token block add through LDS
+#pragma unroll
+      for (int o = 4; o >= 1; o >>= 1) {
+        const bool hi = lane & (8 * o);
+#pragma unroll
+        for (int i = 0; i < o; ++i) {
+          const float send = hi ? xs[i] : xs[i + o];
+          xs[i] = (hi ? xs[i + o] : xs[i]) + __shfl_xor(send, 8 * o, 64);
+        }
+      }
+      float x = xs[0];
+      x += __shfl_xor(x, 1, 64);
+      x += __shfl_xor(x, 2, 64);
+      x += __shfl_xor(x, 4, 64);
+      if ((lane & 7) == 0) L.red[wave][8 * g + (lane >> 3)] = x;
+    }
+  }
+  const int64_t tblk = t0 / 32 + tb;
+  if (act_b) {
+    *reinterpret_cast<uint4*>(Qt + cpair * ld_qt + tblk * 16) = make_uint4(wa[0], wa[1], wa[2], wa[3]);
+    *reinterpret_cast<uint4*>(Qt + (cpair + 1) * ld_qt + tblk * 16) = make_uint4(wb[0], wb[1], wb[2], wb[3]);
+    uint8_t* sp = Qts + (tblk / 4) * ld_qts + cpair * 4 + (tblk & 3);
+    sp[0] = (uint8_t)sba;
+    sp[4] = (uint8_t)sbb;
+    any_bad |= sba == 255 || sbb == 255;
+  }
+  if (any_bad && flags) atomicOr(flags, S3R_FLAG_NONFINITE);
+  if constexpr (EC) {
+    if (act_b) {
+      cpt[tblk * p.C + cpair] = csa;
+      cpt[tblk * p.C + cpair + 1] = csb;
+    }
+    __syncthreads();
+    if (tid < kFusedRows) {
+      const int b2 = tid >> 5, i = tid & 31;
+      rpt[(t0 + tid) * n_ct + blockIdx.y] = L.red[2 * b2][i] + L.red[2 * b2 + 1][i];
+    }
+  }
+}
+
+// --------------------------------------------- forward-operand prep ----
+// RTNE MXFP4 of a forward operand M [R x C] row-major, blocks of 32 along R,
+// output transposed: codes [C x R/2] (row c holds column c of M), scales
+// [R/128][C][4].  A block of 256 threads covers 128 rows x 64 columns: lane =
+// column, wave = one 32-row block; per thread the block's scale and 16 code
+// bytes (the four waves write 64 contiguous bytes of an output row).  VSUM:
+// the column sums of the dequantized values of each block (vsum_part[rblk * C
+// + c]).
+template <typename TIn, bool VSUM>
+__global__ __launch_bounds__(256) void mx_operand_kernel(MxQuant p, const TIn* __restrict__ M,
+                                                         uint8_t* __restrict__ out, int64_t ld_out,
+                                                         uint8_t* __restrict__ sc, int64_t ld_s,
+                                                         float* __restrict__ vsum_part, uint32_t* __restrict__ flags) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t c = (int64_t)blockIdx.y * 64 + lane;
   const int64_t t0 = (int64_t)blockIdx.x * 128 + wave * 32;        // this wave's block of 32 rows
   const bool active = c < p.C;
-  const int n_ct = (int)((p.C + 63) / 64);
-  __shared__ int32_t s_thr[128];
-  if (p.mode == 2 && threadIdx.x < 128)
-    s_thr[threadIdx.x] = s3r_threshold_units24((int64_t)blockIdx.x * 128 + threadIdx.x, p.layer, p.seed,
-                                               kTagS3R + p.stream_word);
-  __syncthreads();
   float v[32];
 #pragma unroll
   for (int i = 0; i < 32; ++i) v[i] = active ? load_elem<TIn>(M + (t0 + i) * p.ld + c) : 0.f;
-  uint32_t m = 0;
+  int32_t R[32];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) m = max(m, __float_as_uint(v[i]) & 0x7FFFFFFFu);
-  const int sb = block_scale_byte(m);
-  const bool bad = sb == 255;
-  const float inv = bad ? 0.f : inv_scale(sb);
-  const float scale = bad ? 0.f : __builtin_ldexpf(1.f, sb - 127);
-  uint32_t w[4] = {0u, 0u, 0u, 0u};
-  float es[32];
-  float csum = 0.f, vsum = 0.f;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const int64_t t = t0 + i;
-    int32_t R = -1;
-    if (p.mode == 2) {
-      R = s_thr[wave * 32 + i];
-    } else if (p.mode == 1) {
-      const uint64_t e = (uint64_t)t * (uint64_t)p.D_index + (uint64_t)c;
-      const U4 u = philox4x32_10((uint32_t)(e >> 2), (uint32_t)(e >> 34), p.layer, kTagSR + p.stream_word,
-                                 (uint32_t)p.seed, (uint32_t)(p.seed >> 32));
-      R = sr_units24(u4_word(u, (uint32_t)e & 3u));
-    }
-    float qv;
-    const uint32_t code = bad ? 0u : e2m1_code(v[i] * inv, R, qv);
-    w[i >> 3] |= code << (4 * (i & 7));
-    const float dq = bad ? 0.f : qv * scale;
-    const float e = bad ? 0.f : dq - v[i];
-    es[i] = active ? e : 0.f;
-    csum += e;
-    vsum += dq;
-  }
+  for (int i = 0; i < 32; ++i) R[i] = -1;
+  uint32_t w[4];
+  float e[32];
+  const int sb = mx_block<VSUM, true>(v, R, w, e);
   if (active) {
     *reinterpret_cast<uint4*>(out + c * ld_out + t0 / 2) = make_uint4(w[0], w[1], w[2], w[3]);
     sc[(t0 / 128) * ld_s + c * 4 + ((t0 / 32) & 3)] = (uint8_t)sb;
-    if (bad && flags) atomicOr(flags, S3R_FLAG_NONFINITE);
-    const int64_t rblk = t0 / 32;
-    if constexpr (EC) col_part[rblk * p.C + c] = csum;
-    if constexpr (VSUM) vsum_part[rblk * p.C + c] = vsum;
-  }
-  if constexpr (EC) {
-    // row sums of the 32 rows over the wave's 64 columns: reduce-scatter, lane l then holds row l >> 1
-    float h16[16], h8[8], h4[4], h2[2], h1;
-    const bool b32 = lane & 32, b16 = lane & 16, b8 = lane & 8, b4 = lane & 4, b2 = lane & 2;
+    if (sb == 255 && flags) atomicOr(flags, S3R_FLAG_NONFINITE);
+    if constexpr (VSUM) {
+      float vsum = 0.f;                                  // dequantized = error + value
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float send = b32 ? es[i] : es[i + 16];
-      h16[i] = (b32 ? es[i + 16] : es[i]) + __shfl_xor(send, 32, 64);
+      for (int i = 0; i < 32; ++i) vsum += sb == 255 ? 0.f : e[i] + v[i];
+      vsum_part[(t0 / 32) * p.C + c] = vsum;
     }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float send = b16 ? h16[i] : h16[i + 8];
-      h8[i] = (b16 ? h16[i + 8] : h16[i]) + __shfl_xor(send, 16, 64);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float send = b8 ? h8[i] : h8[i + 4];
-      h4[i] = (b8 ? h8[i + 4] : h8[i]) + __shfl_xor(send, 8, 64);
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const float send = b4 ? h4[i] : h4[i + 2];
-      h2[i] = (b4 ? h4[i + 2] : h4[i]) + __shfl_xor(send, 4, 64);
-    }
-    {
-      const float send = b2 ? h2[0] : h2[1];
-      h1 = (b2 ? h2[1] : h2[0]) + __shfl_xor(send, 2, 64);
-    }
-    h1 += __shfl_xor(h1, 1, 64);
-    if ((lane & 1) == 0) row_part[(t0 + (lane >> 1)) * n_ct + blockIdx.y] = h1;
   }
 }
 
@@ -439,62 +575,83 @@ __device__ __forceinline__ void mx_load_stage(const MxGemm& g, uint8_t* st, int6
 
 constexpr int kMxSgMfma = 0x008, kMxSgDsRead = 0x100, kMxSgVmem = 0x010;
 
-// One K step (128 elements) on stage S = kt % 4: wait for this wave's loads of
-// the stage, barrier (all waves' loads visible; the stage read in the previous
-// step is retired), refill that retired stage with step kt + 3, then 2 x 16
-// MFMAs with the second half-step's fragments read during the first half's.
-template <int S>
-__device__ __forceinline__ void mx_step(const MxGemm& g, int64_t m0, int64_t n0, int kt, const MxRsrc& rs,
-                                        v16f (&acc)[4][4]) {
+// Fragments of one half-step (kk: K elements 64 kk .. 64 kk + 63 of the step)
+// of a stage: lane l holds rows (columns) i * 32 + l % 32 of its wave's 128,
+// 16 bytes at chunk 2 kk + l / 32; and the stage's scale words of those rows.
+struct MxFrag { v8i a[4], b[4]; };
+
+__device__ __forceinline__ void mx_read_frag(const uint8_t* st, int kk, MxFrag& f) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int r31 = lane & 31, hk = lane >> 5;
-  S3R_MX_WAIT_VM(20);
+  const int r31 = lane & 31, c = kk * 2 + (lane >> 5);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ra_ = wm * 128 + i * 32 + r31, rb_ = wn * 128 + i * 32 + r31;
+    const uint4 x = *reinterpret_cast<const uint4*>(st + ra_ * 64 + ((c ^ mx_swz(ra_)) << 4));
+    const uint4 y = *reinterpret_cast<const uint4*>(st + 16384 + rb_ * 64 + ((c ^ mx_swz(rb_)) << 4));
+    f.a[i] = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
+    f.b[i] = v8i{(int)y.x, (int)y.y, (int)y.z, (int)y.w, 0, 0, 0, 0};
+  }
+}
+
+__device__ __forceinline__ void mx_read_scales(const uint8_t* st, uint32_t (&sa)[4], uint32_t (&sb)[4]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int r31 = lane & 31;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    sa[i] = *reinterpret_cast<const uint32_t*>(st + 32768 + (wm * 128 + i * 32 + r31) * 4);
+    sb[i] = *reinterpret_cast<const uint32_t*>(st + 33792 + (wn * 128 + i * 32 + r31) * 4);
+  }
+}
+
+__device__ __forceinline__ void mx_mfma16(const MxFrag& f, const uint32_t (&sa)[4], const uint32_t (&sb)[4], int kk,
+                                          v16f (&acc)[4][4]) {
+  const int sh = 8 * (kk * 2 + ((threadIdx.x & 63) >> 5));
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], 4, 4, 0,
+                                                                  (int)((sa[i] >> sh) & 0xFFu), 0,
+                                                                  (int)((sb[j] >> sh) & 0xFFu));
+}
+
+// One K step (128 elements) on stage S = kt % 4.  On entry `cur` holds the
+// stage's first half-step fragments and (sa, sb) its scale words.  First half:
+// 16 MFMAs while the second half-step's fragments are read.  Then this wave
+// waits for its loads of stage kt + 1 and a barrier makes every wave's loads of
+// it visible (and retires stage kt - 1, which no wave reads any more); the
+// retired stage is refilled with step kt + 3.  Second half: 16 MFMAs while the
+// next stage's first fragments and scale words are read into cur / (sa, sb),
+// with the refill's 10 buffer loads spread between them.  The MFMAs after the
+// barrier need nothing from LDS that is not already in registers.
+template <int S>
+__device__ __forceinline__ void mx_step(const MxGemm& g, int64_t m0, int64_t n0, int kt, const MxRsrc& rs,
+                                        MxFrag& cur, uint32_t (&sa)[4], uint32_t (&sb)[4], v16f (&acc)[4][4]) {
+  MxFrag nx;
+  mx_read_frag(mx_stage<S>(), 1, nx);
+  mx_mfma16(cur, sa, sb, 0, acc);
+#pragma unroll
+  for (int x = 0; x < 16; ++x) {
+    __builtin_amdgcn_sched_group_barrier(kMxSgMfma, 1, 0);
+    if (x < 8) __builtin_amdgcn_sched_group_barrier(kMxSgDsRead, 1, 0);
+  }
+  S3R_MX_WAIT_VM(10);
   S3R_MX_WAIT_LGKM0();
   __builtin_amdgcn_s_barrier();
   mx_load_stage(g, mx_stage<(S + 3) % 4>(), m0, n0, kt + 3, rs);
-  const uint8_t* st = mx_stage<S>();
-  uint32_t sa[4], sb[4];
-  v8i fa[2][4], fb[2][4];
+  uint32_t ca[4], cb[4];
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
-    const int c = kk * 2 + hk;
+  for (int i = 0; i < 4; ++i) { ca[i] = sa[i]; cb[i] = sb[i]; }
+  mx_read_frag(mx_stage<(S + 1) % 4>(), 0, cur);
+  mx_read_scales(mx_stage<(S + 1) % 4>(), sa, sb);
+  mx_mfma16(nx, ca, cb, 1, acc);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ra_ = wm * 128 + i * 32 + r31, rb_ = wn * 128 + i * 32 + r31;
-      const uint4 x = *reinterpret_cast<const uint4*>(st + ra_ * 64 + ((c ^ mx_swz(ra_)) << 4));
-      const uint4 y = *reinterpret_cast<const uint4*>(st + 16384 + rb_ * 64 + ((c ^ mx_swz(rb_)) << 4));
-      fa[kk][i] = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
-      fb[kk][i] = v8i{(int)y.x, (int)y.y, (int)y.z, (int)y.w, 0, 0, 0, 0};
-    }
-    if (kk == 0) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sa[i] = *reinterpret_cast<const uint32_t*>(st + 32768 + (wm * 128 + i * 32 + r31) * 4);
-        sb[i] = *reinterpret_cast<const uint32_t*>(st + 33792 + (wn * 128 + i * 32 + r31) * 4);
-      }
-    }
-  }
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
-    const int sh = 8 * (kk * 2 + hk);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[kk][i], fb[kk][j], acc[i][j], 4, 4, 0,
-                                                                    (int)((sa[i] >> sh) & 0xFFu), 0,
-                                                                    (int)((sb[j] >> sh) & 0xFFu));
-  }
-  // schedule: the first half-step's fragment and scale reads, then its MFMAs with
-  // the second half-step's reads between them, and the refill's 10 buffer loads
-  // spread one per MFMA pair, so that no burst of loads stalls the MFMA issue
-  __builtin_amdgcn_sched_group_barrier(kMxSgDsRead, 16, 0);
-#pragma unroll
-  for (int x = 0; x < 32; ++x) {
+  for (int x = 0; x < 16; ++x) {
     __builtin_amdgcn_sched_group_barrier(kMxSgMfma, 1, 0);
-    if (x < 8) __builtin_amdgcn_sched_group_barrier(kMxSgDsRead, 1, 0);
-    if ((x & 1) && x < 20) __builtin_amdgcn_sched_group_barrier(kMxSgVmem, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kMxSgDsRead, 1, 0);
+    if (x < 10) __builtin_amdgcn_sched_group_barrier(kMxSgVmem, 1, 0);
   }
 }
 
@@ -525,8 +682,8 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_kernel(MxGemm g, MxEpi ep) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // Stages 0..2 up front; every step refills one stage, so a step always finds
-  // exactly the loads of the two following stages in flight.
+  // Stages 0..2 up front; every step refills one stage, so at a step's wait
+  // exactly the loads of the stage after next may still be in flight.
   // The step count is rounded up to a multiple of 4 (the stage ring's period);
   // the extra steps multiply zeros.
   const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc((void*)g.A, (short)0, 0, kRsrcWord3);
@@ -534,11 +691,17 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_kernel(MxGemm g, MxEpi ep) {
   mx_load_stage(g, mx_stage<0>(), m0, n0, 0, rs);
   mx_load_stage(g, mx_stage<1>(), m0, n0, 1, rs);
   mx_load_stage(g, mx_stage<2>(), m0, n0, 2, rs);
+  S3R_MX_WAIT_VM(20);
+  __builtin_amdgcn_s_barrier();
+  MxFrag cur;
+  uint32_t sa[4], sb[4];
+  mx_read_frag(mx_stage<0>(), 0, cur);
+  mx_read_scales(mx_stage<0>(), sa, sb);
   for (int kt = 0; kt < nk; kt += 4) {
-    mx_step<0>(g, m0, n0, kt, rs, acc);
-    mx_step<1>(g, m0, n0, kt + 1, rs, acc);
-    mx_step<2>(g, m0, n0, kt + 2, rs, acc);
-    mx_step<3>(g, m0, n0, kt + 3, rs, acc);
+    mx_step<0>(g, m0, n0, kt, rs, cur, sa, sb, acc);
+    mx_step<1>(g, m0, n0, kt + 1, rs, cur, sa, sb, acc);
+    mx_step<2>(g, m0, n0, kt + 2, rs, cur, sa, sb, acc);
+    mx_step<3>(g, m0, n0, kt + 3, rs, cur, sa, sb, acc);
   }
   S3R_MX_WAIT_VM(0);
   S3R_MX_WAIT_LGKM0();
@@ -642,73 +805,105 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_kernel(MxGemm g, MxEpi ep) {
 }
 
 // ------------------------------------------------ correction products ----
-// out[b][n] = sum over k of coef[b][k] * dequant(P[n][k]) for b < nb, P an MXFP4
-// matrix [N x K] (K-major codes, scales [K/128][N][4]).  A block of 4 waves owns
-// 4 * RPW rows (RPW per wave); K runs in chunks of 2048 in which lane l takes
-// the 32-element block l: its 16 code bytes, its scale, and the chunk's
-// coefficients from LDS, stored [b][i4][lane] (float4 units) so that a wave's
-// reads are conflict-free.  Fixed order: per-lane sums, then an xor butterfly.
+// part[kc][b][n] = sum over k in chunk kc of coef[b][k] * dequant(P[n][k]) for
+// b < nb, P an MXFP4 matrix [N x K] (K-major codes, scales [K/128][N][4]).
+// Block (x, y): rows 32x .. 32x+31 (RPW = 8 per wave), K chunk y of 2048, in
+// which lane l takes the 32-element block l: its 16 code bytes, its scale and
+// the chunk's coefficients from LDS, stored [b][i4][lane] (float4 units) so a
+// wave's reads are conflict-free.  Codes decode branch-free to signed
+// multiples of 0.5 (the magnitudes 0 .. 6 are 0 1 2 3 4 6 8 12 halves); the
+// block scale / 2 multiplies the lane's sum.  Fixed order: per-lane sums, a
+// reduce-scatter of the RPW x NB sums across the wave, and mx_sum_parts over
+// the chunks.
 constexpr int kRdChunk = 2048;
+constexpr uint32_t kE2M1Halves = 0xC8643210u;
 
-__device__ __forceinline__ float e2m1_times(uint32_t c, float sc) { return e2m1_value(c) * sc; }
+__device__ __forceinline__ float e2m1_halves(uint32_t c) {
+  const int u = (int)((kE2M1Halves >> (4u * (c & 7u))) & 15u);
+  return (float)((c & 8u) ? -u : u);
+}
 
 template <int NB, int RPW>
 __global__ __launch_bounds__(256) void mx_rowdot_kernel(const uint8_t* __restrict__ P, int64_t ldp,
                                                         const uint8_t* __restrict__ Ps, int64_t ldps, int64_t N,
                                                         int64_t K, int nb, const float* __restrict__ coef,
-                                                        float* __restrict__ out) {
+                                                        float* __restrict__ part) {
+  constexpr int V = RPW * NB;                           // sums per wave: 8 or 32
+  static_assert(V == 8 || V == 32, "reduce-scatter shape");
   __shared__ float4 s_c[NB][8][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t n0 = ((int64_t)blockIdx.x * 4 + wave) * RPW;
-  float acc[RPW][NB];
+  const int64_t kc = (int64_t)blockIdx.y * kRdChunk;
+  for (int x = threadIdx.x; x < NB * kRdChunk; x += 256) {
+    const int b = x / kRdChunk, e = x % kRdChunk;      // element e of the chunk -> lane e / 32, i4 (e % 32) / 4
+    const float v = (b < nb && kc + e < K) ? coef[(int64_t)b * K + kc + e] : 0.f;
+    reinterpret_cast<float*>(&s_c[b][(e & 31) >> 2][e >> 5])[e & 3] = v;
+  }
+  __syncthreads();
+  const int64_t k = kc + lane * 32;
+  const bool kv = k < K;
+  // all rows' loads first (rows past N re-read row N - 1; their sums are not stored)
+  uint4 wr[RPW];
+  int sbr[RPW];
 #pragma unroll
-  for (int r = 0; r < RPW; ++r)
+  for (int r = 0; r < RPW; ++r) {
+    const int64_t n = min(n0 + r, N - 1);
+    wr[r] = kv ? *reinterpret_cast<const uint4*>(P + n * ldp + k / 2) : make_uint4(0u, 0u, 0u, 0u);
+    sbr[r] = kv ? (int)Ps[(k / 128) * ldps + n * 4 + ((k / 32) & 3)] : 127;
+  }
+  float acc[V];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) acc[r][b] = 0.f;
-  for (int64_t kc = 0; kc < K; kc += kRdChunk) {
-    __syncthreads();                                    // the previous chunk's coefficients are consumed
-    for (int x = threadIdx.x; x < NB * kRdChunk; x += 256) {
-      const int b = x / kRdChunk, e = x % kRdChunk;    // element e of the chunk -> lane e / 32, i4 (e % 32) / 4
-      const float v = (b < nb && kc + e < K) ? coef[(int64_t)b * K + kc + e] : 0.f;
-      reinterpret_cast<float*>(&s_c[b][(e & 31) >> 2][e >> 5])[e & 3] = v;
-    }
-    __syncthreads();
-    const int64_t k = kc + lane * 32;
-    if (k >= K) continue;
+  for (int r = 0; r < RPW; ++r) {
+    const uint32_t wv[4] = {wr[r].x, wr[r].y, wr[r].z, wr[r].w};
+    float a[NB];
 #pragma unroll
-    for (int r = 0; r < RPW; ++r) {
-      const int64_t n = n0 + r;
-      if (n >= N) break;
-      const uint4 w = *reinterpret_cast<const uint4*>(P + n * ldp + k / 2);
-      const float sc = __builtin_ldexpf(1.f, (int)Ps[(k / 128) * ldps + n * 4 + ((k / 32) & 3)] - 127);
-      const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
+    for (int b = 0; b < NB; ++b) a[b] = 0.f;
 #pragma unroll
-      for (int i4 = 0; i4 < 8; ++i4) {
-        const uint32_t word = wv[i4 >> 1] >> (16 * (i4 & 1));
-        const float x0 = e2m1_times(word & 15u, sc), x1 = e2m1_times((word >> 4) & 15u, sc);
-        const float x2 = e2m1_times((word >> 8) & 15u, sc), x3 = e2m1_times((word >> 12) & 15u, sc);
+    for (int i4 = 0; i4 < 8; ++i4) {
+      const uint32_t word = wv[i4 >> 1] >> (16 * (i4 & 1));
+      const float x0 = e2m1_halves(word), x1 = e2m1_halves(word >> 4);
+      const float x2 = e2m1_halves(word >> 8), x3 = e2m1_halves(word >> 12);
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          if (b >= nb) break;
-          const float4 c = s_c[b][i4][lane];
-          float a = acc[r][b];
-          a = fmaf(c.x, x0, a);
-          a = fmaf(c.y, x1, a);
-          a = fmaf(c.z, x2, a);
-          a = fmaf(c.w, x3, a);
-          acc[r][b] = a;
-        }
+      for (int b = 0; b < NB; ++b) {
+        const float4 c = s_c[b][i4][lane];
+        a[b] = fmaf(c.x, x0, a[b]);
+        a[b] = fmaf(c.y, x1, a[b]);
+        a[b] = fmaf(c.z, x2, a[b]);
+        a[b] = fmaf(c.w, x3, a[b]);
       }
     }
+    const float half_scale = __builtin_ldexpf(1.f, sbr[r] - 128);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[r * NB + b] = a[b] * half_scale;
   }
+  // reduce-scatter of the V sums over the lane bits 5 .. log2(64 / V), then the remaining low bits
+  constexpr int kLow = 64 / V;                          // lanes that end up sharing one sum
 #pragma unroll
-  for (int r = 0; r < RPW; ++r)
+  for (int o = V / 2; o >= 1; o >>= 1) {
+    const int bit = o * kLow;
+    const bool hi = lane & bit;
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      float a = acc[r][b];
-      for (int o = 32; o > 0; o >>= 1) a += __shfl_xor(a, o, 64);
-      if (lane == 0 && b < nb && n0 + r < N) out[(int64_t)b * N + n0 + r] = a;
+    for (int i = 0; i < o; ++i) {
+      const float send = hi ? acc[i] : acc[i + o];
+      acc[i] = (hi ? acc[i + o] : acc[i]) + __shfl_xor(send, bit, 64);
     }
+  }
+  float tot = acc[0];
+#pragma unroll
+  for (int o = 1; o < kLow; o <<= 1) tot += __shfl_xor(tot, o, 64);
+  const int vi = lane / kLow, r = vi / NB, b = vi % NB;
+  if (lane % kLow == 0 && b < nb && n0 + r < N) part[((int64_t)blockIdx.y * NB + b) * N + n0 + r] = tot;
+}
+
+// out[b][n] = sum over the chunks kc (in order) of part[kc][b][n], b < nb, NB slots per chunk.
+__global__ void mx_sum_parts_kernel(int64_t N, int nb, int NB, int nkc, const float* __restrict__ part,
+                                    float* __restrict__ out) {
+  const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (x >= (int64_t)nb * N) return;
+  const int64_t b = x / N, n = x % N;
+  float s = 0.f;
+  for (int kc = 0; kc < nkc; ++kc) s += part[((int64_t)kc * NB + b) * N + n];
+  out[x] = s;
 }
 
 // c[t] = ec_row[t] - ec_mean[t / S]
@@ -730,9 +925,10 @@ MxQuantWs mx_quant_ws(int64_t T, int64_t D, bool ec) {
   MxQuantWs w{};
   size_t off = kWsHeaderBytes;
   if (ec) {
-    w.rph = off; off = align_up(off + (size_t)T * ((D + 511) / 512) * 4, 256);
+    const size_t n_ct = (size_t)((D + kFusedCols - 1) / kFusedCols);
+    w.rph = off; off = align_up(off + (size_t)T * n_ct * 4, 256);
     w.cph = off; off = align_up(off + (size_t)(T / 64) * D * 4, 256);
-    w.rpt = off; off = align_up(off + (size_t)T * ((D + 63) / 64) * 4, 256);
+    w.rpt = off; off = align_up(off + (size_t)T * n_ct * 4, 256);
     w.cpt = off; off = align_up(off + (size_t)(T / 32) * D * 4, 256);
   }
   w.total = off;
@@ -747,30 +943,34 @@ hipError_t mx_quant_both(const MxQuantArgs& a, const MxQuantWs& L, hipStream_t s
   const TIn* G = (const TIn*)a.G;
   float* rph = (float*)(a.ws + L.rph); float* cph = (float*)(a.ws + L.cph);
   float* rpt = (float*)(a.ws + L.rpt); float* cpt = (float*)(a.ws + L.cpt);
-  const dim3 gh((unsigned)(a.T / 64), (unsigned)((a.D + 511) / 512));
-  const dim3 gt((unsigned)(a.T / 128), (unsigned)((a.D + 63) / 64));
+  const int n_ct = (int)((a.D + kFusedCols - 1) / kFusedCols);
+  const dim3 grid((unsigned)(a.T / kFusedRows), (unsigned)n_ct);
+  float* np_ = nullptr;
   if (a.ec) {
-    hipLaunchKernelGGL((mx_quant_rows_kernel<TIn, true>), gh, dim3(256), 0, st, p, G, a.Qh, a.ld_qh, a.Qhs, a.ld_qhs,
-                       rph, cph, a.flags);
-    hipLaunchKernelGGL((mx_quant_cols_kernel<TIn, true, false>), gt, dim3(256), 0, st, p, G, a.Qt, a.ld_qt, a.Qts,
-                       a.ld_qts, rpt, cpt, (float*)nullptr, a.flags);
+    // EC requires S3R
+    hipLaunchKernelGGL((mx_quant_fused_kernel<TIn, true, 2>), grid, dim3(256), 0, st, p, G, a.Qh, a.ld_qh, a.Qhs,
+                       a.ld_qhs, a.Qt, a.ld_qt, a.Qts, a.ld_qts, rph, cph, rpt, cpt, a.flags);
     const int64_t B = a.T / a.S;
     const int64_t ncb = (B * a.D * 8 + 255) / 256, nrb = (a.T + 255) / 256;
-    hipLaunchKernelGGL(mx_finalize_kernel, dim3((unsigned)(ncb + nrb)), dim3(256), 0, st, B, a.D, a.S, 64,
-                       (int)((a.D + 511) / 512), (int)ncb, (const float*)cph, (const float*)nullptr,
-                       (const float*)rph, a.ec_col_h, (float*)nullptr, a.ec_row_h, a.T);
-    hipLaunchKernelGGL(mx_finalize_kernel, dim3((unsigned)(ncb + nrb)), dim3(256), 0, st, B, a.D, a.S, 32,
-                       (int)((a.D + 63) / 64), (int)ncb, (const float*)cpt, (const float*)nullptr,
-                       (const float*)rpt, a.ec_col_t, (float*)nullptr, a.ec_row_t, a.T);
+    hipLaunchKernelGGL(mx_finalize_kernel, dim3((unsigned)(ncb + nrb)), dim3(256), 0, st, B, a.D, a.S, 64, n_ct,
+                       (int)ncb, (const float*)cph, (const float*)nullptr, (const float*)rph, a.ec_col_h,
+                       (float*)nullptr, a.ec_row_h, a.T);
+    hipLaunchKernelGGL(mx_finalize_kernel, dim3((unsigned)(ncb + nrb)), dim3(256), 0, st, B, a.D, a.S, 32, n_ct,
+                       (int)ncb, (const float*)cpt, (const float*)nullptr, (const float*)rpt, a.ec_col_t,
+                       (float*)nullptr, a.ec_row_t, a.T);
     hipLaunchKernelGGL(mx_mean_kernel, dim3((unsigned)B), dim3(256), 0, st, a.S, (const float*)a.ec_row_h,
                        a.ec_mean_h);
     hipLaunchKernelGGL(mx_mean_kernel, dim3((unsigned)B), dim3(256), 0, st, a.S, (const float*)a.ec_row_t,
                        a.ec_mean_t);
+  } else if (a.mode == 0) {
+    hipLaunchKernelGGL((mx_quant_fused_kernel<TIn, false, 0>), grid, dim3(256), 0, st, p, G, a.Qh, a.ld_qh, a.Qhs,
+                       a.ld_qhs, a.Qt, a.ld_qt, a.Qts, a.ld_qts, np_, np_, np_, np_, a.flags);
+  } else if (a.mode == 1) {
+    hipLaunchKernelGGL((mx_quant_fused_kernel<TIn, false, 1>), grid, dim3(256), 0, st, p, G, a.Qh, a.ld_qh, a.Qhs,
+                       a.ld_qhs, a.Qt, a.ld_qt, a.Qts, a.ld_qts, np_, np_, np_, np_, a.flags);
   } else {
-    hipLaunchKernelGGL((mx_quant_rows_kernel<TIn, false>), gh, dim3(256), 0, st, p, G, a.Qh, a.ld_qh, a.Qhs, a.ld_qhs,
-                       (float*)nullptr, (float*)nullptr, a.flags);
-    hipLaunchKernelGGL((mx_quant_cols_kernel<TIn, false, false>), gt, dim3(256), 0, st, p, G, a.Qt, a.ld_qt, a.Qts,
-                       a.ld_qts, (float*)nullptr, (float*)nullptr, (float*)nullptr, a.flags);
+    hipLaunchKernelGGL((mx_quant_fused_kernel<TIn, false, 2>), grid, dim3(256), 0, st, p, G, a.Qh, a.ld_qh, a.Qhs,
+                       a.ld_qhs, a.Qt, a.ld_qt, a.Qts, a.ld_qts, np_, np_, np_, np_, a.flags);
   }
   return hipGetLastError();
 }
@@ -782,16 +982,16 @@ hipError_t mx_operand_t(const MxOperandArgs& a, hipStream_t st) {
   float* vsp = (float*)(a.ws + kWsHeaderBytes);
   const dim3 gt((unsigned)(a.R / 128), (unsigned)((a.C + 63) / 64));
   if (a.colsum) {
-    hipLaunchKernelGGL((mx_quant_cols_kernel<TIn, false, true>), gt, dim3(256), 0, st, p, (const TIn*)a.M, a.Mt,
-                       a.ld_t, a.Mts, a.ld_ts, (float*)nullptr, (float*)nullptr, vsp, a.flags);
+    hipLaunchKernelGGL((mx_operand_kernel<TIn, true>), gt, dim3(256), 0, st, p, (const TIn*)a.M, a.Mt, a.ld_t, a.Mts,
+                       a.ld_ts, vsp, a.flags);
     const int64_t B = a.R / a.S;
     const int64_t ncb = (B * a.C * 8 + 255) / 256;
     hipLaunchKernelGGL(mx_finalize_kernel, dim3((unsigned)ncb), dim3(256), 0, st, B, a.C, a.S, 32, 1, (int)ncb,
                        (const float*)nullptr, (const float*)vsp, (const float*)nullptr, (float*)nullptr, a.colsum,
                        (float*)nullptr, (int64_t)0);
   } else {
-    hipLaunchKernelGGL((mx_quant_cols_kernel<TIn, false, false>), gt, dim3(256), 0, st, p, (const TIn*)a.M, a.Mt,
-                       a.ld_t, a.Mts, a.ld_ts, (float*)nullptr, (float*)nullptr, (float*)nullptr, a.flags);
+    hipLaunchKernelGGL((mx_operand_kernel<TIn, false>), gt, dim3(256), 0, st, p, (const TIn*)a.M, a.Mt, a.ld_t,
+                       a.Mts, a.ld_ts, (float*)nullptr, a.flags);
   }
   return hipGetLastError();
 }
@@ -816,10 +1016,33 @@ MxGemm make_mx_gemm(const uint8_t* A, int64_t lda, const uint8_t* As, int64_t ld
 
 size_t mx_quant_workspace(int64_t T, int64_t D, int ec) { return mx_quant_ws(T, D, ec != 0).total; }
 size_t mx_operand_workspace(int64_t R, int64_t C) { return kWsHeaderBytes + align_up((size_t)(R / 32) * C * 4, 256); }
-size_t mx_backward_workspace(int64_t T, int64_t d_in, int64_t B) {
+// Backward workspace: v [B x d_in] (dX) | coef [T] and u [d_in] (dW) | the GEMVs' chunk partials.
+size_t mx_backward_workspace(int64_t T, int64_t D, int64_t d_in, int64_t B) {
+  const int64_t parts = max(((D + kRdChunk - 1) / kRdChunk) * 4, (T + kRdChunk - 1) / kRdChunk);
   return kWsHeaderBytes + align_up((size_t)B * d_in * 4, 256) + align_up((size_t)T * 4, 256) +
-         align_up((size_t)d_in * 4, 256);
+         align_up((size_t)d_in * 4, 256) + align_up((size_t)parts * d_in * 4, 256);
 }
+
+namespace {
+// coef [nb x K] (row stride K) against the rows of P [N x K] into out [nb x N], NB <= 4 or 1.
+template <int NB>
+void run_rowdot(const MxBwArgs& a, int64_t N, int64_t K, int nb, const float* coef, float* out, float* part,
+                hipStream_t st) {
+  const int nkc = (int)((K + kRdChunk - 1) / kRdChunk);
+  float* dst = nkc == 1 ? out : part;
+  hipLaunchKernelGGL((mx_rowdot_kernel<NB, 8>), dim3((unsigned)((N + 31) / 32), (unsigned)nkc), dim3(256), 0, st,
+                     a.B, a.ldb, a.Bs, a.ldbs, N, K, nb, coef, dst);
+  if (nkc > 1)
+    hipLaunchKernelGGL(mx_sum_parts_kernel, dim3((unsigned)((nb * N + 255) / 256)), dim3(256), 0, st, N, nb, NB, nkc,
+                       (const float*)part, out);
+}
+
+float* mx_parts(const MxBwArgs& a) {
+  const int64_t B = a.T / a.S;
+  return (float*)(a.ws + kWsHeaderBytes + align_up((size_t)B * a.d_in * 4, 256) + align_up((size_t)a.T * 4, 256) +
+                  align_up((size_t)a.d_in * 4, 256));
+}
+}  // namespace
 
 hipError_t launch_mx_quantize(const MxQuantArgs& a, hipStream_t st) {
   const MxQuantWs L = mx_quant_ws(a.T, a.D, a.ec != 0);
@@ -836,11 +1059,10 @@ hipError_t launch_mx_backward_dx(const MxBwArgs& a, hipStream_t st) {
   ep.S = a.S; ep.B = B; ep.out = a.out; ep.ld_out = a.ld_out;
   if (a.ec) {
     float* v = (float*)(a.ws + kWsHeaderBytes);
-    // v_b[i] = sum_j ebar_b[j] dq(W)[j][i]: rows of the K-major Wt [d_in x D], eight examples per pass
+    // v_b[i] = sum_j ebar_b[j] dq(W)[j][i]: rows of the K-major Wt [d_in x D], four examples per pass
     for (int64_t b0 = 0; b0 < B; b0 += 4)
-      hipLaunchKernelGGL((mx_rowdot_kernel<4, 8>), dim3((unsigned)((a.d_in + 31) / 32)), dim3(256), 0, st, a.B, a.ldb,
-                         a.Bs, a.ldbs, a.d_in, a.K, (int)min((int64_t)4, B - b0), a.ec_col + b0 * a.K,
-                         v + b0 * a.d_in);
+      run_rowdot<4>(a, a.d_in, a.K, (int)min((int64_t)4, B - b0), a.ec_col + b0 * a.K, v + b0 * a.d_in, mx_parts(a),
+                    st);
     ep.ec_row = a.ec_row; ep.ec_mean = a.ec_mean; ep.vec = v; ep.rW = a.vcol;
   }
   const MxGemm g = make_mx_gemm(a.A, a.lda, a.As, a.ldas, a.B, a.ldb, a.Bs, a.ldbs, a.T, a.d_in, a.K);
@@ -859,8 +1081,7 @@ hipError_t launch_mx_backward_dw(const MxBwArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(mx_token_coef_kernel, dim3((unsigned)((a.T + 255) / 256)), dim3(256), 0, st, a.T, a.S,
                        a.ec_row, a.ec_mean, coef);
     // u[i] = sum_t (eps_t - mu_b) dq(X)[t][i]: rows of the K-major Xt [d_in x T]
-    hipLaunchKernelGGL((mx_rowdot_kernel<1, 8>), dim3((unsigned)((a.d_in + 31) / 32)), dim3(256), 0, st, a.B, a.ldb,
-                       a.Bs, a.ldbs, a.d_in, a.T, 1, (const float*)coef, u);
+    run_rowdot<1>(a, a.d_in, a.T, 1, coef, u, mx_parts(a), st);
     ep.ebar = a.ec_col; ep.xs = a.vcol; ep.u = u;
   }
   // dW [D x d_in] = Qt [D x T] . Xt [d_in x T]^T

@@ -165,7 +165,7 @@ struct MxBwArgs {        // out [rows x d_in] = A [rows x K] . B [d_in x K]^T - 
 };
 size_t mx_quant_workspace(int64_t T, int64_t D, int ec);
 size_t mx_operand_workspace(int64_t R, int64_t C);
-size_t mx_backward_workspace(int64_t T, int64_t d_in, int64_t B);
+size_t mx_backward_workspace(int64_t T, int64_t D, int64_t d_in, int64_t B);
 hipError_t launch_mx_quantize(const MxQuantArgs& a, hipStream_t st);
 hipError_t launch_mx_operand(const MxOperandArgs& a, hipStream_t st);
 hipError_t launch_mx_backward_dx(const MxBwArgs& a, hipStream_t st);

@@ -134,6 +134,7 @@ def test_mx_zero_and_nonfinite_blocks():
     g[64:96, 7] = 0.0                 # an all-zero block along T
     g[9, 100] = np.inf                # non-finite: its blocks get the NaN scale and zero codes
     g[10, 3] = 1e-41                  # a subnormal in an otherwise normal block
+    g[20, 64:96] = np.linspace(-3e-39, 2e-39, 32, dtype=np.float32)   # a block of subnormals (k = -127)
     G = to_dev(g, "f32")
     q = s3r.mx_quantize(G, mode=s3r.S3R, seed=1)
     torch.cuda.synchronize()

@@ -227,6 +227,7 @@ def test_mx_argument_errors(L):
     assert q(ok, ec=[None] * 6) == -1                                   # statistics outputs missing
     assert q(s3r.qdesc(T, D, 128, s3r.S3R), ec=[None] * 6, ld_qt=T // 2 + 8) == -1   # Qt ld not 16-aligned
     assert q(ok, Qt=P((1 << 22) + 8)) == -1                              # Qt base not 16-aligned
+    assert q(ok, G=P((1 << 20) + 4)) == -1                               # G not 16-byte aligned
     assert q(ok, wsb=16) == -3
     assert q(ok, ws=P((1 << 23) + 64)) == -1
     assert s3r.s3r_mx_workspace(s3r.qdesc(T, 96, 128), d_in) == 0
