@@ -498,29 +498,27 @@ __global__ __launch_bounds__(256) void mx_mean_kernel(int64_t S, const float* __
 // out [M x N] (f32) = A [M x K] . B [N x K]^T with both operands MXFP4 and
 // K-major: codes 2 per byte (ld in bytes), E8M0 scales [K/128][rows][4].  256 x
 // 256 tile per 256-thread workgroup, four waves of 128 x 128 (4 x 4 blocks of
-// v_mfma_scale_f32_32x32x64_f8f6f4), K step 128 (64 bytes per row).  A stage
-// holds the A and B tiles (256 rows x 64 B each, 16-byte chunks swizzled as
-// c ^ f(row)) and their scale words (one 4-byte word per row = the 4 blocks of
-// the K step), all moved global -> LDS by buffer-load DMA; a ring of 4 stages.
+// v_mfma_scale_f32_32x32x64_f8f6f4).  A stage covers 256 elements of K: the A
+// and B tiles are 256 rows x 128 bytes each (a whole cache line per row and
+// stage, 16-byte chunks swizzled as c ^ f(row)) plus the rows' scale words of
+// the stage's two 128-element steps, all moved global -> LDS by buffer-load
+// DMA; two stages alternate, the next one loading while the current one feeds
+// 64 MFMAs per wave.
 // Operand lane layout of the FP4 MFMA (checked on the device): lane l holds row
 // (or column) l % 32 and K elements 32 (l / 32) .. + 31, 16 bytes, the first in
 // the low nibble; byte 0 of its scale register is that (row, K block)'s E8M0.
 // Output: lane l, register r -> row (r / 4) 8 + (l / 32) 4 + r % 4, column l % 32.
-constexpr int kMxStages = 4;
-constexpr int kMxStageBytes = 32768 + 2048;
-// Four separate LDS objects rather than one indexed array: the compiler then
-// sees that a step's LDS reads and the DMA refilling another stage touch
+constexpr int kMxStageBytes = 65536 + 4096;
+constexpr int kMxScaleA = 65536, kMxScaleB = 65536 + 2048;   // [step][row] words per operand
+// Two separate LDS objects rather than one indexed array: the compiler then
+// sees that a stage's LDS reads and the DMA filling the other stage touch
 // different memory, and does not drain every outstanding load before the reads.
 __shared__ __attribute__((aligned(1024))) uint8_t g_mx0[kMxStageBytes];
 __shared__ __attribute__((aligned(1024))) uint8_t g_mx1[kMxStageBytes];
-__shared__ __attribute__((aligned(1024))) uint8_t g_mx2[kMxStageBytes];
-__shared__ __attribute__((aligned(1024))) uint8_t g_mx3[kMxStageBytes];
 template <int S>
 __device__ __forceinline__ uint8_t* mx_stage() {
   if constexpr (S == 0) return g_mx0;
-  else if constexpr (S == 1) return g_mx1;
-  else if constexpr (S == 2) return g_mx2;
-  else return g_mx3;
+  else return g_mx1;
 }
 
 struct MxGemm {
@@ -540,33 +538,42 @@ struct MxEpi {
 };
 constexpr int kMxMaxB = 8;
 
-__device__ __forceinline__ int mx_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+// Position of 16-byte chunk c (0..7) of a 128-byte tile row: eight consecutive rows put a
+// given chunk in eight different 16-byte bank groups, and rows r, r + 8 in different ones.
+__device__ __forceinline__ int mx_pos(int r, int c) { return c ^ (r & 7) ^ ((r >> 3) & 1); }
 
-struct MxRsrc { __amdgpu_buffer_rsrc_t a, b, sa, sb, z; int nk; };
+struct MxRsrc { __amdgpu_buffer_rsrc_t a, b, sa, sb, z; int nk, ns; };
 
-// Stage kt of the K loop; past the last step (kt >= nk) every load goes through
-// an empty descriptor and lands zeros, which add nothing to the accumulators.
-__device__ __forceinline__ void mx_load_stage(const MxGemm& g, uint8_t* st, int64_t m0, int64_t n0, int kt,
+// Stage ks (K elements 256 ks ..): each wave moves 8 row-blocks of 8 rows x 128 bytes of A
+// and of B (lane l: row 8 blk + l / 8, the chunk that belongs at position l % 8) and its
+// 64 rows' scale words of both steps.  Past the last stage every load goes through an empty
+// descriptor (zeros); a step past K within the last stage loads zero scales and codes that
+// are never multiplied (its MFMAs are skipped).
+__device__ __forceinline__ void mx_load_stage(const MxGemm& g, uint8_t* st, int64_t m0, int64_t n0, int ks,
                                               const MxRsrc& r) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const bool live = kt < r.nk;
-  const MxRsrc rs{live ? r.a : r.z, live ? r.b : r.z, live ? r.sa : r.z, live ? r.sb : r.z, r.z, r.nk};
+  const bool live = ks < r.ns;
+  const __amdgpu_buffer_rsrc_t ra = live ? r.a : r.z, rb = live ? r.b : r.z;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int blk = wave * 4 + q;
-    const int row = blk * 16 + (lane >> 2);
-    const int c = (lane & 3) ^ mx_swz(row);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.a, (lds_void*)(st + blk * 1024), 16,
-                                             (uint32_t)((m0 + row) * g.lda + c * 16), (uint32_t)kt * 64u, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.b, (lds_void*)(st + 16384 + blk * 1024), 16,
-                                             (uint32_t)((n0 + row) * g.ldb + c * 16), (uint32_t)kt * 64u, 0, 0);
+  for (int q = 0; q < 8; ++q) {
+    const int blk = wave * 8 + q;
+    const int row = blk * 8 + (lane >> 3);
+    const int c = mx_pos(row, lane & 7);             // the position map is an involution
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(st + blk * 1024), 16,
+                                             (uint32_t)((m0 + row) * g.lda + c * 16), (uint32_t)ks * 128u, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(st + 32768 + blk * 1024), 16,
+                                             (uint32_t)((n0 + row) * g.ldb + c * 16), (uint32_t)ks * 128u, 0, 0);
   }
-  // scale words: this wave's 64 rows of A and of B, one dword per lane
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.sa, (lds_void*)(st + 32768 + wave * 256), 4,
-                                           (uint32_t)((m0 + wave * 64 + lane) * 4), (uint32_t)(kt * g.ldas), 0, 0);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.sb, (lds_void*)(st + 33792 + wave * 256), 4,
-                                           (uint32_t)((n0 + wave * 64 + lane) * 4), (uint32_t)(kt * g.ldbs), 0, 0);
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub) {
+    const int kt = 2 * ks + sub;
+    const bool lk = kt < r.nk;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(lk ? r.sa : r.z, (lds_void*)(st + kMxScaleA + sub * 1024 + wave * 256), 4,
+                                             (uint32_t)((m0 + wave * 64 + lane) * 4), (uint32_t)(kt * g.ldas), 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(lk ? r.sb : r.z, (lds_void*)(st + kMxScaleB + sub * 1024 + wave * 256), 4,
+                                             (uint32_t)((n0 + wave * 64 + lane) * 4), (uint32_t)(kt * g.ldbs), 0, 0);
+  }
 }
 
 // s_waitcnt: at most n vector-memory ops outstanding, no LDS ops.
@@ -575,33 +582,32 @@ __device__ __forceinline__ void mx_load_stage(const MxGemm& g, uint8_t* st, int6
 
 constexpr int kMxSgMfma = 0x008, kMxSgDsRead = 0x100, kMxSgVmem = 0x010;
 
-// Fragments of one half-step (kk: K elements 64 kk .. 64 kk + 63 of the step)
-// of a stage: lane l holds rows (columns) i * 32 + l % 32 of its wave's 128,
-// 16 bytes at chunk 2 kk + l / 32; and the stage's scale words of those rows.
+// Fragments of half-step h (0..3: K elements 64 h .. 64 h + 63 of the stage): lane l holds
+// rows (columns) i * 32 + l % 32 of its wave's 128, the 16 bytes of chunk 2 h + l / 32.
 struct MxFrag { v8i a[4], b[4]; };
 
-__device__ __forceinline__ void mx_read_frag(const uint8_t* st, int kk, MxFrag& f) {
+__device__ __forceinline__ void mx_read_frag(const uint8_t* st, int h, MxFrag& f) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int r31 = lane & 31, c = kk * 2 + (lane >> 5);
+  const int r31 = lane & 31, c = h * 2 + (lane >> 5);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int ra_ = wm * 128 + i * 32 + r31, rb_ = wn * 128 + i * 32 + r31;
-    const uint4 x = *reinterpret_cast<const uint4*>(st + ra_ * 64 + ((c ^ mx_swz(ra_)) << 4));
-    const uint4 y = *reinterpret_cast<const uint4*>(st + 16384 + rb_ * 64 + ((c ^ mx_swz(rb_)) << 4));
+    const uint4 x = *reinterpret_cast<const uint4*>(st + ra_ * 128 + (mx_pos(ra_, c) << 4));
+    const uint4 y = *reinterpret_cast<const uint4*>(st + 32768 + rb_ * 128 + (mx_pos(rb_, c) << 4));
     f.a[i] = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
     f.b[i] = v8i{(int)y.x, (int)y.y, (int)y.z, (int)y.w, 0, 0, 0, 0};
   }
 }
 
-__device__ __forceinline__ void mx_read_scales(const uint8_t* st, uint32_t (&sa)[4], uint32_t (&sb)[4]) {
+__device__ __forceinline__ void mx_read_scales(const uint8_t* st, int sub, uint32_t (&sa)[4], uint32_t (&sb)[4]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int r31 = lane & 31;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    sa[i] = *reinterpret_cast<const uint32_t*>(st + 32768 + (wm * 128 + i * 32 + r31) * 4);
-    sb[i] = *reinterpret_cast<const uint32_t*>(st + 33792 + (wn * 128 + i * 32 + r31) * 4);
+    sa[i] = *reinterpret_cast<const uint32_t*>(st + kMxScaleA + sub * 1024 + (wm * 128 + i * 32 + r31) * 4);
+    sb[i] = *reinterpret_cast<const uint32_t*>(st + kMxScaleB + sub * 1024 + (wn * 128 + i * 32 + r31) * 4);
   }
 }
 
@@ -617,41 +623,47 @@ __device__ __forceinline__ void mx_mfma16(const MxFrag& f, const uint32_t (&sa)[
                                                                   (int)((sb[j] >> sh) & 0xFFu));
 }
 
-// One K step (128 elements) on stage S = kt % 4.  On entry `cur` holds the
-// stage's first half-step fragments and (sa, sb) its scale words.  First half:
-// 16 MFMAs while the second half-step's fragments are read.  Then this wave
-// waits for its loads of stage kt + 1 and a barrier makes every wave's loads of
-// it visible (and retires stage kt - 1, which no wave reads any more); the
-// retired stage is refilled with step kt + 3.  Second half: 16 MFMAs while the
-// next stage's first fragments and scale words are read into cur / (sa, sb),
-// with the refill's 10 buffer loads spread between them.  The MFMAs after the
-// barrier need nothing from LDS that is not already in registers.
-template <int S>
-__device__ __forceinline__ void mx_step(const MxGemm& g, int64_t m0, int64_t n0, int kt, const MxRsrc& rs,
-                                        MxFrag& cur, uint32_t (&sa)[4], uint32_t (&sb)[4], v16f (&acc)[4][4]) {
-  MxFrag nx;
-  mx_read_frag(mx_stage<S>(), 1, nx);
-  mx_mfma16(cur, sa, sb, 0, acc);
+// 16 MFMAs with NR LDS reads and NV buffer loads spread between them.
+template <int NR, int NV>
+__device__ __forceinline__ void mx_interleave() {
 #pragma unroll
   for (int x = 0; x < 16; ++x) {
     __builtin_amdgcn_sched_group_barrier(kMxSgMfma, 1, 0);
-    if (x < 8) __builtin_amdgcn_sched_group_barrier(kMxSgDsRead, 1, 0);
+    if (x < NR) __builtin_amdgcn_sched_group_barrier(kMxSgDsRead, 1, 0);
+    if (x < NV) __builtin_amdgcn_sched_group_barrier(kMxSgVmem, 1, 0);
   }
-  S3R_MX_WAIT_VM(10);
+}
+
+// Stage ks on buffer S = ks % 2.  This wave's loads of it have landed (the wait) and the
+// barrier makes every wave's visible and retires the other buffer (read in the previous
+// stage), which is refilled with stage ks + 1 while this one feeds 4 x 16 MFMAs, each
+// group's fragments read during the previous group.  The second step's MFMAs are skipped
+// when it lies past K.
+template <int S>
+__device__ __forceinline__ void mx_stage_step(const MxGemm& g, int64_t m0, int64_t n0, int ks, const MxRsrc& rs,
+                                              v16f (&acc)[4][4]) {
+  S3R_MX_WAIT_VM(0);
   S3R_MX_WAIT_LGKM0();
   __builtin_amdgcn_s_barrier();
-  mx_load_stage(g, mx_stage<(S + 3) % 4>(), m0, n0, kt + 3, rs);
-  uint32_t ca[4], cb[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) { ca[i] = sa[i]; cb[i] = sb[i]; }
-  mx_read_frag(mx_stage<(S + 1) % 4>(), 0, cur);
-  mx_read_scales(mx_stage<(S + 1) % 4>(), sa, sb);
-  mx_mfma16(nx, ca, cb, 1, acc);
-#pragma unroll
-  for (int x = 0; x < 16; ++x) {
-    __builtin_amdgcn_sched_group_barrier(kMxSgMfma, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(kMxSgDsRead, 1, 0);
-    if (x < 10) __builtin_amdgcn_sched_group_barrier(kMxSgVmem, 1, 0);
+  const uint8_t* st = mx_stage<S>();
+  uint32_t sa0[4], sb0[4], sa1[4], sb1[4];
+  MxFrag f0, f1;
+  mx_read_frag(st, 0, f0);
+  mx_read_scales(st, 0, sa0, sb0);
+  mx_load_stage(g, mx_stage<S ^ 1>(), m0, n0, ks + 1, rs);
+  mx_read_frag(st, 1, f1);
+  mx_read_scales(st, 1, sa1, sb1);
+  mx_mfma16(f0, sa0, sb0, 0, acc);
+  __builtin_amdgcn_sched_group_barrier(kMxSgDsRead, 16, 0);
+  mx_interleave<16, 10>();
+  mx_read_frag(st, 2, f0);
+  mx_mfma16(f1, sa0, sb0, 1, acc);
+  mx_interleave<8, 10>();
+  if (2 * ks + 1 < rs.nk) {
+    mx_read_frag(st, 3, f1);
+    mx_mfma16(f0, sa1, sb1, 0, acc);
+    mx_interleave<8, 0>();
+    mx_mfma16(f1, sa1, sb1, 1, acc);
   }
 }
 
@@ -682,26 +694,15 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_kernel(MxGemm g, MxEpi ep) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // Stages 0..2 up front; every step refills one stage, so at a step's wait
-  // exactly the loads of the stage after next may still be in flight.
-  // The step count is rounded up to a multiple of 4 (the stage ring's period);
-  // the extra steps multiply zeros.
+  // Stage 0 up front; each stage loads the next.  The stage count is rounded up to
+  // even (the two buffers' period): a stage past K multiplies zeros.
   const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc((void*)g.A, (short)0, 0, kRsrcWord3);
-  const MxRsrc rs{ra, rb, rsa, rsb, rz, nk};
+  const int ns = (int)((g.K + 255) / 256);
+  const MxRsrc rs{ra, rb, rsa, rsb, rz, nk, ns};
   mx_load_stage(g, mx_stage<0>(), m0, n0, 0, rs);
-  mx_load_stage(g, mx_stage<1>(), m0, n0, 1, rs);
-  mx_load_stage(g, mx_stage<2>(), m0, n0, 2, rs);
-  S3R_MX_WAIT_VM(20);
-  __builtin_amdgcn_s_barrier();
-  MxFrag cur;
-  uint32_t sa[4], sb[4];
-  mx_read_frag(mx_stage<0>(), 0, cur);
-  mx_read_scales(mx_stage<0>(), sa, sb);
-  for (int kt = 0; kt < nk; kt += 4) {
-    mx_step<0>(g, m0, n0, kt, rs, cur, sa, sb, acc);
-    mx_step<1>(g, m0, n0, kt + 1, rs, cur, sa, sb, acc);
-    mx_step<2>(g, m0, n0, kt + 2, rs, cur, sa, sb, acc);
-    mx_step<3>(g, m0, n0, kt + 3, rs, cur, sa, sb, acc);
+  for (int ks = 0; ks < ns; ks += 2) {
+    mx_stage_step<0>(g, m0, n0, ks, rs, acc);
+    mx_stage_step<1>(g, m0, n0, ks + 1, rs, acc);
   }
   S3R_MX_WAIT_VM(0);
   S3R_MX_WAIT_LGKM0();
@@ -710,9 +711,9 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_kernel(MxGemm g, MxEpi ep) {
 
   // epilogue: per-row values of the tile staged in LDS (the stages are free now),
   // per-column values in registers
-  float* s_rowc = reinterpret_cast<float*>(mx_stage<0>());             // dX: eps_t - mu_b; dW: ebar[b][row] (b-major)
+  float* s_rowc = reinterpret_cast<float*>(mx_stage<0>());            // dX: eps_t - mu_b; dW: ebar[b][row] (b-major)
   int* s_rowb = reinterpret_cast<int*>(mx_stage<1>());                // dX: the row's example, relative to the tile's first
-  float* s_v = reinterpret_cast<float*>(mx_stage<2>());               // dX: v[b0 + b][tile column], b < NB
+  float* s_v = reinterpret_cast<float*>(mx_stage<1>() + 4096);        // dX: v[b0 + b][tile column], b < NB
   const int64_t b_first = DW ? 0 : m0 / ep.S;
   if constexpr (EC) {
     for (int r = threadIdx.x; r < 256; r += 256) {
@@ -807,7 +808,7 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_kernel(MxGemm g, MxEpi ep) {
 // ------------------------------------------------ correction products ----
 // part[kc][b][n] = sum over k in chunk kc of coef[b][k] * dequant(P[n][k]) for
 // b < nb, P an MXFP4 matrix [N x K] (K-major codes, scales [K/128][N][4]).
-// Block (x, y): rows 32x .. 32x+31 (RPW = 8 per wave), K chunk y of 2048, in
+// Block (x, y): rows 4 RPW x .. (RPW per wave), K chunk y of 2048, in
 // which lane l takes the 32-element block l: its 16 code bytes, its scale and
 // the chunk's coefficients from LDS, stored [b][i4][lane] (float4 units) so a
 // wave's reads are conflict-free.  Codes decode branch-free to signed
@@ -828,8 +829,8 @@ __global__ __launch_bounds__(256) void mx_rowdot_kernel(const uint8_t* __restric
                                                         const uint8_t* __restrict__ Ps, int64_t ldps, int64_t N,
                                                         int64_t K, int nb, const float* __restrict__ coef,
                                                         float* __restrict__ part) {
-  constexpr int V = RPW * NB;                           // sums per wave: 8 or 32
-  static_assert(V == 8 || V == 32, "reduce-scatter shape");
+  constexpr int V = RPW * NB;                           // sums per wave
+  static_assert(V == 4 || V == 8 || V == 16 || V == 32, "reduce-scatter shape");
   __shared__ float4 s_c[NB][8][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t n0 = ((int64_t)blockIdx.x * 4 + wave) * RPW;
@@ -1030,8 +1031,9 @@ void run_rowdot(const MxBwArgs& a, int64_t N, int64_t K, int nb, const float* co
                 hipStream_t st) {
   const int nkc = (int)((K + kRdChunk - 1) / kRdChunk);
   float* dst = nkc == 1 ? out : part;
-  hipLaunchKernelGGL((mx_rowdot_kernel<NB, 8>), dim3((unsigned)((N + 31) / 32), (unsigned)nkc), dim3(256), 0, st,
-                     a.B, a.ldb, a.Bs, a.ldbs, N, K, nb, coef, dst);
+  constexpr int RPW = 4;                               // 16 rows per block: enough blocks to hide latency
+  hipLaunchKernelGGL((mx_rowdot_kernel<NB, RPW>), dim3((unsigned)((N + 4 * RPW - 1) / (4 * RPW)), (unsigned)nkc),
+                     dim3(256), 0, st, a.B, a.ldb, a.Bs, a.ldbs, N, K, nb, coef, dst);
   if (nkc > 1)
     hipLaunchKernelGGL(mx_sum_parts_kernel, dim3((unsigned)((nb * N + 255) / 256)), dim3(256), 0, st, N, nb, NB, nkc,
                        (const float*)part, out);
