@@ -167,6 +167,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="ffn-block-8192x4096x14336-bf16")
     ap.add_argument("--mode", default="s3r-ec-two-way", choices=sorted(MODES))
+    ap.add_argument("--streams", type=int, default=1, choices=(1, 2),
+                    help="FFN block: 2 runs the dW products on a second stream beside the dX chain (faster step; "
+                         "the overlapped kernels' event times then include sharing the GPU)")
     ap.add_argument("--cpu-rows", type=int, default=-1,
                     help="tokens in the CPU-oracle sample (-1: the default sample, 0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -258,6 +261,10 @@ def run_block(args, dev, torch, inputs, s3r):
     amax = torch.zeros(2, dtype=torch.int32, device=dev)     # gate, up: max|G'| bits from the glue
     ws_b = torch.zeros(max(max(s3r.s3r_backward_workspace(st[n]["desc"], st[n]["din"]) for n in st), 1),
                        dtype=torch.uint8, device=dev)
+    # dW products on a second stream (default priority), each after its quantize; dW of the down
+    # projection also waits for dH, so the dX GEMM that the roofline is taken on runs alone
+    s2 = torch.cuda.Stream() if args.streams == 2 else None
+    ws_b2 = torch.zeros_like(ws_b) if s2 is not None else ws_b
     dH = torch.empty(T, F, dtype=torch.float32, device=dev)
     Gg = torch.empty(T, F, dtype=torch.bfloat16, device=dev)
     Gu = torch.empty_like(Gg)
@@ -286,10 +293,14 @@ def run_block(args, dev, torch, inputs, s3r):
             s3r.s3r_time_next_gemm(*ev[f"dx_{name}"])
         s3r.s3r_backward_dx(p["desc"], p["Q"], p["delta"], p["fw"].Q, p["fx"].delta, p["fw"].code_colsum[0], p["er"],
                             p["ec"], p["em"], dX_out[name], ws_b, accumulate=(name == "up"))
+        if s2 is not None:
+            e = torch.cuda.Event()
+            e.record()
+            s2.wait_event(e)
         if ev:
             s3r.s3r_time_next_gemm(*ev[f"dw_{name}"])
         s3r.s3r_backward_dw(p["desc"], p["Q"], p["delta"], p["fx"].Q, p["fw"].delta, p["fx"].code_colsum, p["er"],
-                            p["ec"], p["em"], dW[name], ws_b)
+                            p["ec"], p["em"], dW[name], ws_b2, stream=None if s2 is None else s2.cuda_stream)
 
     def step(ev):
         if ev:
@@ -303,6 +314,10 @@ def run_block(args, dev, torch, inputs, s3r):
             ev["glue"][1].record()
         linear("gate", ev)
         linear("up", ev)
+        if s2 is not None:
+            e = torch.cuda.Event()
+            e.record(s2)
+            torch.cuda.current_stream().wait_event(e)
         if ev:
             ev["step"][1].record()
 
