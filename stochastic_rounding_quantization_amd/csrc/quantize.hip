@@ -289,21 +289,26 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
   for (int i = 0; i < 8; ++i) { col[i] = 0.f; colq[i] = 0; }
 
   // Fast path (contiguous bf16 G, a full 64-row tile, 8 columns in range, per-tensor step):
-  // all 16 rows of this wave (t = r0 + wave + 4k) are loaded up front as raw bf16, 16 loads in
-  // flight, and coded as they arrive; the 16 row sums of the errors are one reduce-scatter
-  // across the wave at the end.
+  // the 16 rows of this wave (t = r0 + wave + 4k) are loaded as raw bf16 in groups of 4, each
+  // group's loads issued when the previous group's codes are stored (the other waves of the
+  // SIMD cover the latency); the 16 row sums of the errors are one reduce-scatter across the
+  // wave at the end.
   bool done = false;
   if constexpr (sizeof(TIn) == 2 && VEC && !PT && !COLSUM) {
     constexpr int kWR = kRowsPerTile / (kThreads / kWave);   // 16 rows per wave
     if (r1 - r0 == kRowsPerTile && j0 + 8 <= p.D && (MODE != 1 || (p.D & 3) == 0)) {
       done = true;
+      constexpr int kGroup = 4;
       uint4 raw[kWR];
-#pragma unroll
-      for (int k = 0; k < kWR; ++k)
-        raw[k] = *reinterpret_cast<const uint4*>(G + (r0 + wave + 4 * k) * p.ld_g + j0);
       float rsum[kWR];
 #pragma unroll
       for (int k = 0; k < kWR; ++k) {
+        if (k % kGroup == 0) {
+          asm volatile("" ::: "memory");            // this group's loads after the previous group's stores
+#pragma unroll
+          for (int kk = k; kk < k + kGroup; ++kk)
+            raw[kk] = *reinterpret_cast<const uint4*>(G + (r0 + wave + 4 * kk) * p.ld_g + j0);
+        }
         const int64_t t = r0 + wave + 4 * k;
         const float fx = sx ? sx[t] : 1.f;
         float v[8];
