@@ -114,6 +114,25 @@ def test_mx_tiles_and_tails_bf16(T, D, d_in, S):
     assert rel_err(host(gpu["dW"]), ref["dW"]) < TOL
 
 
+def test_mx_many_examples_dx_correction():
+    # nine examples: the dX correction's GEMV runs in passes of four examples (4 + 4 + 1);
+    # the dW correction takes at most eight, so the two-way variant is refused
+    T, D, d_in, S = 128 * 9, 256, 136, 128
+    inp = _problem(T, D, d_in, "f32", 5)
+    gpu = gpu_mx(inp, mode=oq.S3R, ec=oq.EC_DX_ONLY, S=S, seed=4)
+    ref = mx.backward(_f32(inp, "G"), _f32(inp, "X"), _f32(inp, "W"), mode=oq.S3R, ec=oq.EC_DX_ONLY,
+                      rows_per_example=S, seed=4)
+    _check_quant(gpu, ref)
+    _check_stats(gpu, ref, S)
+    assert rel_err(host(gpu["dX"]), ref["dX"]) < TOL
+    assert rel_err(host(gpu["dW"]), ref["dW"]) < TOL
+    q = s3r.mx_quantize(to_dev(inp["G"], "f32"), mode=s3r.S3R, ec=s3r.EC_TWO_WAY, rows_per_example=S)
+    Xt, Xts, xs = s3r.mx_operand(to_dev(inp["X"], "f32"), rows_per_example=S)
+    dW = torch.empty(D, d_in, device=DEV)
+    ws = torch.zeros(s3r.s3r_mx_workspace(q.desc, d_in), dtype=torch.uint8, device=DEV)
+    assert s3r.s3r_mx_backward_dw(q.desc, q.Qt, q.Qt_scales, Xt, Xts, xs, *q.ec_t, dW, ws, rc_only=True) == -1
+
+
 def test_mx_sr_second_stream_and_layer():
     T, D, d_in = 256, 256, 96
     inp = _problem(T, D, d_in, "f32", 3)
