@@ -290,9 +290,8 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
 
   // Fast path (contiguous bf16 G, a full 64-row tile, 8 columns in range, per-tensor step):
   // the 16 rows of this wave (t = r0 + wave + 4k) are loaded as raw bf16 in groups of 4, each
-  // group's loads issued when the previous group's codes are stored (the other waves of the
-  // SIMD cover the latency); the 16 row sums of the errors are one reduce-scatter across the
-  // wave at the end.
+  // group's loads issued when the previous group's coding starts (one group ahead); the 16 row
+  // sums of the errors are one reduce-scatter across the wave at the end.
   bool done = false;
   if constexpr (sizeof(TIn) == 2 && VEC && !PT && !COLSUM) {
     constexpr int kWR = kRowsPerTile / (kThreads / kWave);   // 16 rows per wave
@@ -301,16 +300,23 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
       constexpr int kGroup = 4;
       uint4 raw[kWR];
       float rsum[kWR];
+      // the 16 rows' s_x, lane k holding row k's, read out per row with readlane: a per-row
+      // load would wait on every load in flight, the rows' G included
+      const float sx_rows = (sx && lane < kWR) ? sx[r0 + wave + 4 * lane] : 1.f;
+#pragma unroll
+      for (int kk = 0; kk < kGroup; ++kk)
+        raw[kk] = *reinterpret_cast<const uint4*>(G + (r0 + wave + 4 * kk) * p.ld_g + j0);
 #pragma unroll
       for (int k = 0; k < kWR; ++k) {
-        if (k % kGroup == 0) {
-          asm volatile("" ::: "memory");            // this group's loads after the previous group's stores
+        if (k % kGroup == 0 && k + kGroup < kWR) {
+          __builtin_amdgcn_sched_barrier(0);        // the next group's loads, in row order
 #pragma unroll
-          for (int kk = k; kk < k + kGroup; ++kk)
+          for (int kk = k + kGroup; kk < k + 2 * kGroup; ++kk)
             raw[kk] = *reinterpret_cast<const uint4*>(G + (r0 + wave + 4 * kk) * p.ld_g + j0);
+          __builtin_amdgcn_sched_barrier(0);
         }
         const int64_t t = r0 + wave + 4 * k;
-        const float fx = sx ? sx[t] : 1.f;
+        const float fx = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sx_rows), k));
         float v[8];
         const uint32_t w[4] = {raw[k].x, raw[k].y, raw[k].z, raw[k].w};
 #pragma unroll
