@@ -421,9 +421,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmParams g, 
     int bid = blockIdx.x;
     if (nblocks % kNumXcd == 0) bid = (bid % kNumXcd) * (nblocks / kNumXcd) + bid / kNumXcd;
     const int mt = bid / g.tiles_n;
-    const int e = find_group(gg.tiles256, gg.G, mt);
-    if (e < 0) return;
-    const int64_t r0 = gg.offsets[e], n = gg.offsets[e + 1] - r0;
+    const GroupHit h = find_group_wave(gg.tiles256, gg.offsets, gg.G, mt);
+    if (h.e < 0) return;
+    const int e = h.e;
+    const int64_t r0 = h.r0, n = h.r1 - r0;
     g.A += r0 * g.lda;
     g.M = n;
     g.B += e * gg.b_stride;
@@ -436,7 +437,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmParams g, 
     ep.out = (char*)ep.out + r0 * ep.ld_out * 4;
     ep.S = n > 0 ? n : 1;
     ep.B = 1;
-    tm = mt - gg.tiles256[e];
+    tm = mt - h.t0;
     tn = bid % g.tiles_n;
   } else {
     if (gg.status[0] != 0) return;
@@ -586,10 +587,11 @@ __global__ __launch_bounds__(kGvThreads) void gemv_partial_kernel(
   int rows = (int)min((int64_t)kGvRows, K - k0);
   int grp = -1;
   if (goff) {
-    grp = find_group(gtiles, G, blockIdx.y);
-    if (grp < 0) return;
-    k0 = goff[grp] + (int64_t)(blockIdx.y - gtiles[grp]) * kGvRows;
-    rows = (int)min((int64_t)kGvRows, goff[grp + 1] - k0);
+    const GroupHit h = find_group_wave(gtiles, goff, G, blockIdx.y);
+    if (h.e < 0) return;
+    grp = h.e;
+    k0 = h.r0 + (int64_t)(blockIdx.y - h.t0) * kGvRows;
+    rows = (int)min((int64_t)kGvRows, h.r1 - k0);
   }
   P += blockIdx.z * pstride;
   if (C) C += blockIdx.z * nb * K;

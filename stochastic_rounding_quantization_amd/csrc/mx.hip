@@ -536,7 +536,6 @@ struct MxEpi {
   int64_t S, B;
   float* out; int64_t ld_out;
 };
-constexpr int kMxMaxB = 8;
 
 // Position of 16-byte chunk c (0..7) of a 128-byte tile row: eight consecutive rows put a
 // given chunk in eight different 16-byte bank groups, and rows r, r + 8 in different ones.

@@ -233,12 +233,13 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
   int64_t b, r0, r1;
   bool first_tile;               // this row tile writes its group's (or the tensor's) step
   if constexpr (GR) {
-    const int e = find_group(gr.tiles64, gr.G, rtile);
-    if (e < 0) return;           // past the last tile of the last group
+    const GroupHit h = find_group_wave(gr.tiles64, gr.offsets, gr.G, rtile);
+    if (h.e < 0) return;         // past the last tile of the last group
+    const int e = h.e;
     b = e;
-    r0 = gr.offsets[e] + (int64_t)(rtile - gr.tiles64[e]) * kRowsPerTile;
-    r1 = min(r0 + kRowsPerTile, gr.offsets[e + 1]);
-    first_tile = rtile == gr.tiles64[e];
+    r0 = h.r0 + (int64_t)(rtile - h.t0) * kRowsPerTile;
+    r1 = min(r0 + kRowsPerTile, h.r1);
+    first_tile = rtile == h.t0;
     if (sw) sw += e * p.D;
     amax_part = gr.amax + e;
     n_amax_part = 1;
@@ -984,23 +985,71 @@ template <typename TIn, bool VEC>
 __global__ __launch_bounds__(kThreads) void grouped_amax_kernel(
     const TIn* __restrict__ G, int64_t ld, int64_t D, const float* __restrict__ sx, const float* __restrict__ sw,
     GroupArgs gr, uint32_t* __restrict__ amax) {
-  const int e = find_group(gr.tiles64, gr.G, blockIdx.x);
-  if (e < 0) return;
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  const int64_t r0 = gr.offsets[e] + (int64_t)(blockIdx.x - gr.tiles64[e]) * kRowsPerTile;
-  const int64_t r1 = min(r0 + kRowsPerTile, gr.offsets[e + 1]);
+  const GroupHit h = find_group_wave(gr.tiles64, gr.offsets, gr.G, blockIdx.x);
+  if (h.e < 0) return;
+  const int e = h.e;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int64_t r0 = h.r0 + (int64_t)(blockIdx.x - h.t0) * kRowsPerTile;
+  const int64_t r1 = min(r0 + kRowsPerTile, h.r1);
   const int64_t j0 = (int64_t)blockIdx.y * kColsPerTile + lane * 8;
   float s[8];
   load8_scale(sw ? sw + e * D : nullptr, j0, D, VEC, s);
   uint32_t m = 0;
-  constexpr int kU = 4;
-  if (j0 < D) {
-    for (int64_t tb = r0 + wave; tb < r1; tb += (kThreads / kWave) * kU) {
+  constexpr int kW = kThreads / kWave;
+  // Lanes with eight whole columns: every row of the wave's share loaded at
+  // once with no branch around a load, so the loads overlap instead of waiting
+  // in turn.  Rows past the group re-read its last row, and the other lanes
+  // read their row's first eight columns (D >= 8); both are masked.
+  const bool full = VEC && j0 + 8 <= D;
+  if (VEC && D >= 8) {
+    constexpr int kRB = sizeof(TIn) == 2 ? kRowsPerTile / kW : kRowsPerTile / kW / 2;
+    const TIn* __restrict__ col = G + (full ? j0 : 0);
+#pragma unroll 1
+    for (int64_t tb = r0 + wave; tb < r1; tb += kW * kRB) {
+      uint4 w[kRB][sizeof(TIn) / 2];     // the raw rows: eight bf16 or eight f32 values each
+      float fx[kRB];
+#pragma unroll
+      for (int u = 0; u < kRB; ++u) {
+        const int64_t t = min(tb + (int64_t)u * kW, r1 - 1);
+        const uint4* row = reinterpret_cast<const uint4*>(col + t * ld);
+#pragma unroll
+        for (int h = 0; h < (int)(sizeof(TIn) / 2); ++h) w[u][h] = row[h];
+        fx[u] = sx ? sx[t] : 1.f;
+      }
+#pragma unroll
+      for (int u = 0; u < kRB; ++u) {
+        const bool ok = full && tb + (int64_t)u * kW < r1;
+        float v[8];
+        if constexpr (sizeof(TIn) == 2) {
+          const uint32_t x[4] = {w[u][0].x, w[u][0].y, w[u][0].z, w[u][0].w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __uint_as_float(x[i] << 16);
+            v[2 * i + 1] = __uint_as_float(x[i] & 0xFFFF0000u);
+          }
+        } else {
+          const uint32_t x[8] = {w[u][0].x, w[u][0].y, w[u][0].z, w[u][0].w,
+                                 w[u][1].x, w[u][1].y, w[u][1].z, w[u][1].w};
+#pragma unroll
+          for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(x[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t b = abs_bits((v[i] * fx[u]) * s[i]);
+          m = (ok && b > m) ? b : m;
+        }
+      }
+    }
+  }
+  if (!full && j0 < D) {                  // a ragged last column group, or unaligned rows
+    constexpr int kU = 4;
+    for (int64_t tb = r0 + wave; tb < r1; tb += kW * kU) {
       float v[kU][8];
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
-        const int64_t t = tb + (int64_t)u * (kThreads / kWave);
-        if (t < r1) load8<TIn, VEC>(G + t * ld, j0, D, v[u]);
+        const int64_t t = tb + (int64_t)u * kW;
+        if (t < r1) load8<TIn, false>(G + t * ld, j0, D, v[u]);
         else {
 #pragma unroll
           for (int i = 0; i < 8; ++i) v[u][i] = 0.f;
@@ -1008,7 +1057,7 @@ __global__ __launch_bounds__(kThreads) void grouped_amax_kernel(
       }
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
-        const int64_t t = tb + (int64_t)u * (kThreads / kWave);
+        const int64_t t = tb + (int64_t)u * kW;
         const float fx = (t < r1 && sx) ? sx[t] : 1.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {

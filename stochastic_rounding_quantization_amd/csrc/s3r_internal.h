@@ -200,15 +200,47 @@ size_t group_tables_bytes(int64_t G);
 GroupTables group_tables(char* base, int64_t G, const int64_t* offsets);
 hipError_t launch_group_tables(const GroupTables& t, int64_t R, uint32_t* flags, hipStream_t st);
 
-// The group e with tiles[e] <= i < tiles[e+1] (binary search), or -1 past the last tile.
-__device__ __forceinline__ int find_group(const int32_t* __restrict__ tiles, int64_t G, int64_t i) {
-  if (i >= tiles[G]) return -1;
-  int lo = 0, hi = (int)G;                 // tiles[lo] <= i < tiles[hi]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (tiles[mid] <= i) lo = mid; else hi = mid;
+// The group e with tiles[e] <= i < tiles[e+1], its first tile tiles[e] and its
+// rows [offsets[e], offsets[e+1]), found by the whole wave in a 64-ary search:
+// one round of loads per level and a ballot across the lanes, one level for up
+// to 64 groups.  The last level also loads the candidates' offsets, so group
+// and rows arrive in one round of loads instead of a chain of dependent ones.
+// Every lane of the wave must be active; the result is wave-uniform.
+// e = -1 past the last tile of the last group.
+struct GroupHit { int e; int32_t t0; int64_t r0, r1; };
+__device__ __forceinline__ GroupHit find_group_wave(const int32_t* __restrict__ tiles,
+                                                    const int64_t* __restrict__ offsets, int64_t G, int64_t i) {
+  const int lane = (int)(threadIdx.x & 63);
+  const int32_t total = tiles[G];
+  int lo = 0, hi = (int)G;                 // tiles[lo] <= i < tiles[hi] when i < total
+  while (hi - lo > 64) {
+    const int step = (hi - lo + 63) / 64;
+    const int c = lo + lane * step;
+    const uint64_t m = __builtin_amdgcn_ballot_w64(c < hi && tiles[c] <= i);   // a prefix of the lanes
+    const int last = m ? 63 - __builtin_clzll(m) : 0;
+    lo += last * step;
+    hi = min(lo + step, hi);
   }
-  return lo;
+  const int c = lo + lane;
+  int32_t tc = 0;
+  int64_t o0 = 0, o1 = 0;
+  bool hit = false;
+  if (c < hi) {
+    tc = tiles[c];
+    o0 = offsets[c];
+    o1 = offsets[c + 1];
+    hit = tc <= i;
+  }
+  const uint64_t m = __builtin_amdgcn_ballot_w64(hit);
+  const int last = m ? 63 - __builtin_clzll(m) : 0;
+  GroupHit h;
+  h.e = (m != 0 && i < total) ? lo + last : -1;
+  h.t0 = __builtin_amdgcn_readlane(tc, last);
+  h.r0 = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(o0 >> 32), last) << 32) |
+                   (uint32_t)__builtin_amdgcn_readlane((int)o0, last));
+  h.r1 = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(o1 >> 32), last) << 32) |
+                   (uint32_t)__builtin_amdgcn_readlane((int)o1, last));
+  return h;
 }
 
 // Every workspace starts with a header of synchronization words shared by all
