@@ -13,26 +13,25 @@
 //
 // Tiling: 256 x 256 output tile per 256-thread workgroup (four 64-lane waves,
 // 2 x 2, each 128 x 128 = 4 x 4 blocks of v_mfma_i32_32x32x32_i8), K step 64.
-// Operands go from global memory straight into LDS (global_load_lds_dwordx4,
-// 16 bytes per lane, lane l landing at 16*l of a 1 KB block) through a
-// 4-stage ring of 32 KB stages (128 KB), three K steps in flight.  Nothing is
-// transposed on the way in:
-//   K-contiguous tile: 256 rows x 64 B; 16-byte chunk c of row r sits at
-//     position c ^ f(r), f(r) = ((r >> 1) ^ (r >> 3)) & 3; fragments are read
-//     with ds_read_b128 (lane: row l%32, 16 consecutive k).
-//   M/N-contiguous tile: 64 k-rows x 256 B; chunk c of k-row r sits at
+// Operands go from global memory straight into LDS (buffer_load_dwordx4 with
+// the LDS bit, 16 bytes per lane, lane l landing at 16*l of a 1 KB block);
+// nothing is transposed on the way in.  Two rings fill the CU's 160 KB:
+//   M-contiguous A (dW): five stages of 32 KB, each one K step of A and B,
+//     loads issued four steps ahead.
+//   K-contiguous A (dX): A in units of two K steps (whole 128-byte lines per
+//     row), three units of 32 KB beside four B stages of 16 KB.
+//   M/N-contiguous tiles: 64 k-rows x 256 B; chunk c of k-row r sits at
 //     c ^ swz_m(r), swz_m(r) = (r & 7) | ((r >> 4) & 1) << 3 (the two
 //     half-waves of a read use k-rows 16 apart and so land in different
 //     halves of the banks); fragments are read with two ds_read_b64_tr_b8: within each
 //     16-lane group, lane L fetches 8 bytes of k-row kb + L/2 at column
 //     nb + 8(L%2), and the hardware hands lane i the bytes of column nb + i
 //     from the 8 k-rows, so a lane ends up with 16 consecutive k of one
-//     column, the same k order the K-contiguous read gives.
+//     column, the same k order a K-contiguous ds_read_b128 gives.
 // The chunk position is chosen on the global side (which lane loads which
 // chunk), so the swizzles cost nothing at load time, and the 16-byte reads of
-// 8 or 16 consecutive rows / the 8 k-rows of a transpose read hit distinct
-// banks.  Tiles that cross the matrix edge (or the K tail) take a masked
-// register path that writes zeros past the edge.
+// 16 consecutive rows / the 8 k-rows of a transpose read hit distinct banks.
+// The descriptors' range checks return zeros past the operands' ends.
 // Workgroups are numbered so that the consecutive tiles of one XCD share rows
 // of A and columns of B (grouped order), for L2 reuse.
 #include "s3r_internal.h"
@@ -71,6 +70,35 @@ __device__ __forceinline__ uint8_t* stage() {
   else return g_stage4;
 }
 
+// With a K-contiguous A the rows of A bring 64 bytes per K step, half a cache
+// line: in one-step stages every line of A is fetched twice, in two halves,
+// which costs the dX GEMM 50 % more L2 requests than the dW GEMM and ~10 %
+// of its time.  That kernel keeps A in units of two K steps instead (256 rows
+// x 128 bytes, whole lines), loaded half a unit (128 rows) per K step, beside
+// B stages of one K step: three A units and four B stages fill the 160 KB.
+constexpr int kUnitBytes = 32768, kBStageBytes = 16384;
+__shared__ __attribute__((aligned(1024))) uint8_t g_unit0[kUnitBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t g_unit1[kUnitBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t g_unit2[kUnitBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t g_bst0[kBStageBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t g_bst1[kBStageBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t g_bst2[kBStageBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t g_bst3[kBStageBytes];
+
+template <int U>
+__device__ __forceinline__ uint8_t* a_unit() {
+  if constexpr (U == 0) return g_unit0;
+  else if constexpr (U == 1) return g_unit1;
+  else return g_unit2;
+}
+template <int S>
+__device__ __forceinline__ uint8_t* b_stage() {
+  if constexpr (S == 0) return g_bst0;
+  else if constexpr (S == 1) return g_bst1;
+  else if constexpr (S == 2) return g_bst2;
+  else return g_bst3;
+}
+
 struct EpiParams {
   const float* delta; int per_token;
   const float* row_scale;            // s_x (dX) or s_w (dW); null = 1
@@ -91,7 +119,6 @@ struct GemmParams {
   int tiles_m, tiles_n;
 };
 
-__device__ __forceinline__ int swz_k(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 __device__ __forceinline__ int swz_m(int r) { return (r & 7) | (((r >> 4) & 1) << 3); }
 
 // s_waitcnt immediates (gfx9 encoding): wait for at most n vector-memory ops / no LDS ops.
@@ -107,9 +134,8 @@ __device__ __forceinline__ int swz_m(int r) { return (r & 7) | (((r >> 4) & 1) <
 // always multiplies a zero; reads past the M or N edge inside the matrix only
 // reach output rows or columns that are never stored.
 // Each wave fills 4 of the 16 1-KB blocks of the A tile and 4 of the B tile.
-// Block blk, lane l:
-//   K-contiguous: row = 16 blk + l/4, position p = l%4 holds chunk c = p ^ swz_k(row)
-//   M/N-contiguous: k-row = 4 blk + l/16, position p = l%16 holds chunk c = p ^ swz_m(k-row)
+// Block blk, lane l (M/N-contiguous): k-row = 4 blk + l/16, position p = l%16
+// holds chunk c = p ^ swz_m(k-row).  (The K-contiguous A has its own ring below.)
 constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit dword format (gfx9 family)
 
 struct LoadMap {           // per-thread byte offsets (tile origin + position), for 4 blocks of A and of B
@@ -118,30 +144,20 @@ struct LoadMap {           // per-thread byte offsets (tile origin + position), 
   __amdgpu_buffer_rsrc_t ra, rb;
 };
 
-template <bool A_KMAJOR>
 __device__ __forceinline__ LoadMap make_loadmap(const GemmParams& g, int64_t m0, int64_t n0) {
   LoadMap m;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int blk = wave * 4 + q;
-    if constexpr (A_KMAJOR) {
-      const int row = blk * 16 + (lane >> 2);
-      const int c = (lane & 3) ^ swz_k(row);
-      m.a_off[q] = (uint32_t)((m0 + row) * g.lda + c * 16);
-    } else {
-      const int kr = blk * 4 + (lane >> 4);
-      const int c = (lane & 15) ^ swz_m(kr);
-      m.a_off[q] = (uint32_t)(kr * g.lda + m0 + c * 16);
-    }
     const int kr = blk * 4 + (lane >> 4);
     const int c = (lane & 15) ^ swz_m(kr);
+    m.a_off[q] = (uint32_t)(kr * g.lda + m0 + c * 16);
     m.b_off[q] = (uint32_t)(kr * g.ldb + n0 + c * 16);
   }
-  m.a_step = (uint32_t)(A_KMAJOR ? BK : BK * g.lda);
+  m.a_step = (uint32_t)(BK * g.lda);
   m.b_step = (uint32_t)(BK * g.ldb);
-  const int64_t a_rows = A_KMAJOR ? g.M : g.K;
-  m.ra = __builtin_amdgcn_make_buffer_rsrc((void*)g.A, (short)0, (int)(uint32_t)(a_rows * g.lda), kRsrcWord3);
+  m.ra = __builtin_amdgcn_make_buffer_rsrc((void*)g.A, (short)0, (int)(uint32_t)(g.K * g.lda), kRsrcWord3);
   m.rb = __builtin_amdgcn_make_buffer_rsrc((void*)g.B, (short)0, (int)(uint32_t)(g.K * g.ldb), kRsrcWord3);
   return m;
 }
@@ -162,22 +178,14 @@ __device__ __forceinline__ void load_stage(const LoadMap& m, int kt) {
 
 // ------------------------------------------------------------ fragments ----
 struct FragMap {
-  int a_k[2];      // K-contiguous A: byte offset for kk = 0, 1 (block i adds i * 2048)
   int a_t[4];      // M-contiguous A: byte offset of block i (kk adds 8192, second read 2048)
   int b_t[4];      // N-contiguous B (within the B half)
 };
 
-template <bool A_KMAJOR>
 __device__ __forceinline__ FragMap make_fragmap() {
   FragMap f;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int r = lane & 31;
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
-    const int c = kk * 2 + (lane >> 5);
-    f.a_k[kk] = (wm * 128 + r) * 64 + ((c ^ swz_k(r)) << 4);
-  }
   const int grp = lane >> 4, L = lane & 15;
   const int krow = 16 * (grp >> 1) + (L >> 1);        // k-row for kk = 0, first read
   const int x = swz_m(krow);                           // also the swizzle of krow + 8 and krow + 32
@@ -203,14 +211,11 @@ constexpr int kSgMfma = 0x008, kSgDsRead = 0x100, kSgVmem = 0x010;
 struct Frags { v4i a[4], b[4]; };
 
 // Fragments of half-step kk (k 32kk .. 32kk+31) of stage S.
-template <int S, bool A_KMAJOR>
+template <int S>
 __device__ __forceinline__ void read_frags(const FragMap& f, int kk, Frags& fr) {
   const uint8_t* st = stage<S>();
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if constexpr (A_KMAJOR) fr.a[i] = *reinterpret_cast<const v4i*>(st + f.a_k[kk] + i * 2048);
-    else fr.a[i] = tr_pair(st + f.a_t[i] + kk * 8192);
-  }
+  for (int i = 0; i < 4; ++i) fr.a[i] = tr_pair(st + f.a_t[i] + kk * 8192);
 #pragma unroll
   for (int j = 0; j < 4; ++j) fr.b[j] = tr_pair(st + kHalf + f.b_t[j] + kk * 8192);
 }
@@ -240,10 +245,10 @@ __device__ __forceinline__ void interleave_schedule() {
 // waited for its own loads of it) and retires stage kt-1, which is refilled
 // with step kt+4.  The second half-step's fragments are read during the first
 // half's MFMAs, and the next stage's first fragments during the second half's.
-template <int S, bool A_KMAJOR>
-__device__ __forceinline__ void k_step(const LoadMap& lm, const FragMap& fm, int kt, int nk, Frags& cur,
+template <int S>
+__device__ __forceinline__ void k_step(const LoadMap& lm, const FragMap& fm, int kt, Frags& cur,
                                        v16i (&acc)[4][4]) {
-  constexpr int NR = A_KMAJOR ? 12 : 16;   // LDS reads per half-step
+  constexpr int NR = 16;   // LDS reads per half-step
   // Every step refills one stage, also past the last step (those loads read past
   // the end of the data or land in retired stages), so exactly the loads of
   // stages kt+2 and kt+3 may still be in flight here.
@@ -252,13 +257,171 @@ __device__ __forceinline__ void k_step(const LoadMap& lm, const FragMap& fm, int
   __builtin_amdgcn_s_barrier();
   load_stage<(S + 4) % kStages>(lm, kt + 4);
   Frags nxt;
-  read_frags<S, A_KMAJOR>(fm, 1, nxt);
+  read_frags<S>(fm, 1, nxt);
   mfma16(cur, acc);
   interleave_schedule<NR, 8>();
   // next stage's first fragments (after the last step this reads a stale stage; unused)
-  read_frags<(S + 1) % kStages, A_KMAJOR>(fm, 0, cur);
+  read_frags<(S + 1) % kStages>(fm, 0, cur);
   mfma16(nxt, acc);
   interleave_schedule<NR, 0>();
+}
+
+// ------------------------------------- the unit ring (K-contiguous A) ----
+// A unit holds K steps 2u and 2u+1 of the tile's 256 rows: half h (16 KB) is
+// rows 128h .. 128h+127, each row 128 bytes (k 128u .. 128u+127), and 16-byte
+// chunk c of local row r sits at position c ^ swz_u(r), swz_u(r) = (r >> 1) & 7,
+// so the sixteen rows a ds_read_b128 quarter-wave touches hit sixteen different
+// bank groups.  Each 1 KB DMA block is eight whole rows: eight lanes fetch one
+// 128-byte line.  Wave wm only reads half wm.
+// Schedule: K step kt computes from unit kt/2 (slot (kt/2) % 3) and B stage kt
+// (slot kt % 4), and refills B stage kt+3 and half kt%2 of unit kt/2+2; the
+// slots refilled are those of B stage kt-1 and unit kt/2-1, retired by the
+// barrier.  Data for step kt+1 was issued at steps kt-2 or earlier, so the
+// loads of one step (8 per wave) may be in flight at the wait.
+__device__ __forceinline__ int swz_u(int r) { return (r >> 1) & 7; }
+
+// The unit ring issues its DMAs as inline assembly, which the compiler does not
+// see as LDS writes: tracking seven DMA targets, it otherwise drains every load
+// in flight (vmcnt(0)) before most of the K steps' fragment reads.  Every
+// ordering the ring needs is explicit: the waits, the barrier, and a fixed
+// instruction order inside a K step (sched_barrier after each MFMA group).
+struct UnitMap {
+  uint32_t a_off[2][4], b_off[4];
+  uint32_t b_step;
+  v4i ra, rb;            // buffer descriptors (raw words)
+};
+
+__device__ __forceinline__ v4i rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t p = (uint64_t)(uintptr_t)base;
+  return v4i{(int)(uint32_t)p, (int)((uint32_t)(p >> 32) & 0xFFFFu), (int)bytes, kRsrcWord3};
+}
+
+__device__ __forceinline__ UnitMap make_unitmap(const GemmParams& g, int64_t m0, int64_t n0) {
+  UnitMap m;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int blk = wave * 4 + q;                  // 1 KB block of a 16 KB half or B stage
+    const int row = blk * 8 + (lane >> 3);         // local row of the half
+    const int c = (lane & 7) ^ swz_u(row);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) m.a_off[h][q] = (uint32_t)((m0 + h * 128 + row) * g.lda + c * 16);
+    const int kr = blk * 4 + (lane >> 4);
+    const int cb = (lane & 15) ^ swz_m(kr);
+    m.b_off[q] = (uint32_t)(kr * g.ldb + n0 + cb * 16);
+  }
+  m.b_step = (uint32_t)(BK * g.ldb);
+  m.ra = rsrc_words(g.A, (uint32_t)(g.M * g.lda));
+  m.rb = rsrc_words(g.B, (uint32_t)(g.K * g.ldb));
+  return m;
+}
+
+// One 1 KB DMA: 16 bytes per lane from rsrc + voff + soff to LDS address lds + 16 * lane.
+// M0 holds the LDS address; nothing else in these kernels uses M0 (it is a
+// reserved register, which a clobber list cannot name).
+__device__ __forceinline__ void dma_1k(v4i rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff));
+}
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) { return (uint32_t)(uintptr_t)(const lds_void*)p; }
+
+// DMA q (0..7) of a K step: q < 4 fill B stage SB with K step kt_b, q >= 4 fill
+// half H of unit slot SU with unit u.
+template <int SB, int SU, int H>
+__device__ __forceinline__ void unit_dma(const UnitMap& m, int q, int wave, int kt_b, int u) {
+  if (q < 4)
+    dma_1k(m.rb, lds_addr(b_stage<SB>()) + (uint32_t)(wave * 4 + q) * 1024u, m.b_off[q], (uint32_t)kt_b * m.b_step);
+  else
+    dma_1k(m.ra, lds_addr(a_unit<SU>()) + (uint32_t)(H * 16384 + (wave * 4 + q - 4) * 1024), m.a_off[H][q - 4],
+           (uint32_t)u * 128u);
+}
+template <int SB>
+__device__ __forceinline__ void load_b_stage(const UnitMap& m, int kt) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) unit_dma<SB, 0, 0>(m, q, wave, kt, 0);
+}
+template <int SU, int H>
+__device__ __forceinline__ void load_a_half(const UnitMap& m, int u) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+  for (int q = 4; q < 8; ++q) unit_dma<0, SU, H>(m, q, wave, 0, u);
+}
+
+struct UnitFragMap {
+  int a[2][2];     // A: byte offset in the unit for (step parity, half-step kk); block i adds i * 4096
+  int b_t[4];      // B: as FragMap::b_t, within a B stage
+};
+
+__device__ __forceinline__ UnitFragMap make_unit_fragmap() {
+  UnitFragMap f;
+  const FragMap t = make_fragmap();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1;
+  const int r = lane & 31;
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int c = sub * 4 + kk * 2 + (lane >> 5);
+      f.a[sub][kk] = wm * 16384 + r * 128 + ((c ^ swz_u(r)) << 4);
+    }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) f.b_t[j] = t.b_t[j];
+  return f;
+}
+
+// Fragment read x (0..11) of half-step kk: x < 4 the A block x, then the two
+// transposed halves of B block (x - 4) / 2.
+template <int SU, int SUB, int SB>
+__device__ __forceinline__ void unit_read(const UnitFragMap& f, int kk, int x, Frags& fr) {
+  if (x < 4) {
+    fr.a[x] = *reinterpret_cast<const v4i*>(a_unit<SU>() + f.a[SUB][kk] + x * 4096);
+  } else {
+    const int j = (x - 4) >> 1, hi = (x - 4) & 1;
+    const v2i v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+        (lds_v2i*)(b_stage<SB>() + f.b_t[j] + kk * 8192 + hi * 2048));
+    if (hi) { fr.b[j].z = v.x; fr.b[j].w = v.y; }
+    else { fr.b[j].x = v.x; fr.b[j].y = v.y; }
+  }
+}
+template <int SU, int SUB, int SB>
+__device__ __forceinline__ void read_unit_frags(const UnitFragMap& f, int kk, Frags& fr) {
+#pragma unroll
+  for (int x = 0; x < 12; ++x) unit_read<SU, SUB, SB>(f, kk, x, fr);
+}
+
+// K step kt with P = kt % 12 (the schedule repeats every 12 steps).  First
+// half-step: MFMA x on `cur`, then fragment read x of the second half-step, and
+// after every other MFMA one of the step's 8 DMAs.  Second half-step: MFMA x on
+// `nxt`, then fragment read x of the next step's first half-step.
+template <int P>
+__device__ __forceinline__ void unit_step(const UnitMap& lm, const UnitFragMap& fm, int kt, Frags& cur,
+                                          v16i (&acc)[4][4]) {
+  constexpr int SU = (P / 2) % 3, SUB = P % 2, SB = P % 4;
+  constexpr int P1 = (P + 1) % 12;
+  constexpr int SU1 = (P1 / 2) % 3, SUB1 = P1 % 2, SB1 = P1 % 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kt_b = kt + 3, u = (kt >> 1) + 2;
+  S3R_WAIT_VM(8);
+  S3R_WAIT_LGKM0();
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  Frags nxt;
+#pragma unroll
+  for (int x = 0; x < 16; ++x) {
+    acc[x >> 2][x & 3] = __builtin_amdgcn_mfma_i32_32x32x32_i8(cur.a[x >> 2], cur.b[x & 3], acc[x >> 2][x & 3], 0, 0, 0);
+    if (x < 12) unit_read<SU, SUB, SB>(fm, 1, x, nxt);
+    if ((x & 1) == 0) unit_dma<(P + 3) % 4, (P / 2 + 2) % 3, SUB>(lm, x >> 1, wave, kt_b, u);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // the next step's first fragments (after the last step this reads a stale slot; unused)
+#pragma unroll
+  for (int x = 0; x < 16; ++x) {
+    acc[x >> 2][x & 3] = __builtin_amdgcn_mfma_i32_32x32x32_i8(nxt.a[x >> 2], nxt.b[x & 3], acc[x >> 2][x & 3], 0, 0, 0);
+    if (x < 12) unit_read<SU1, SUB1, SB1>(fm, 0, x, cur);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
 // ---------------------------------------------------------------- epilogue ----
@@ -279,7 +442,7 @@ __device__ __forceinline__ int row_in_block(int r) { return (r >> 2) * 8 + (r & 
 // so the per-element sum has no runtime trip count; slots b >= B hold zeros).
 template <int EPI, bool EC, bool GATHER, int NB>
 __device__ __forceinline__ void epilogue(const GemmParams& g, const EpiParams& ep, int64_t m0, int64_t n0,
-                                         v16i (&acc)[4][4]) {
+                                         const float4* rowf, const float* roweb, v16i (&acc)[4][4]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int rows_here = (int)min((int64_t)BM, g.M - m0);
@@ -287,8 +450,7 @@ __device__ __forceinline__ void epilogue(const GemmParams& g, const EpiParams& e
   const uint32_t ld4 = (uint32_t)ep.ld_out * esz;
   __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
       (void*)((char*)ep.out + (m0 * ep.ld_out) * esz), (short)0, (int)((uint32_t)rows_here * ld4), kRsrcWord3);
-  const float4* rowf = reinterpret_cast<const float4*>(g_stage0);   // per-row factors
-  const float* roweb = reinterpret_cast<const float*>(g_stage1);    // dW: ebar[b][row] / s_w[row]
+  // rowf: per-row factors; roweb (dW): ebar[b][row] / s_w[row]
   const int lane_row = wm * 128 + (lane >> 5) * 4;                  // + i*32 + row_in_block(r)
 
   // per-column values of this lane, one per column block j
@@ -472,30 +634,60 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmParams g, 
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = v16i{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
 
-  const LoadMap lm = make_loadmap<A_KMAJOR>(g, m0, n0);
-  const FragMap fm = make_fragmap<A_KMAJOR>();
-  load_stage<0>(lm, 0);
-  load_stage<1>(lm, 1);
-  load_stage<2>(lm, 2);
-  load_stage<3>(lm, 3);
-  Frags cur;
-  S3R_WAIT_VM(24);
-  __builtin_amdgcn_s_barrier();
-  read_frags<0, A_KMAJOR>(fm, 0, cur);
-  for (int kt = 0; kt < nk; kt += kStages) {
-    k_step<0, A_KMAJOR>(lm, fm, kt, nk, cur, acc);
-    if (kt + 1 < nk) k_step<1, A_KMAJOR>(lm, fm, kt + 1, nk, cur, acc);
-    if (kt + 2 < nk) k_step<2, A_KMAJOR>(lm, fm, kt + 2, nk, cur, acc);
-    if (kt + 3 < nk) k_step<3, A_KMAJOR>(lm, fm, kt + 3, nk, cur, acc);
-    if (kt + 4 < nk) k_step<4, A_KMAJOR>(lm, fm, kt + 4, nk, cur, acc);
+  if constexpr (A_KMAJOR) {
+    const UnitMap lm = make_unitmap(g, m0, n0);
+    const UnitFragMap fm = make_unit_fragmap();
+    load_a_half<0, 0>(lm, 0);
+    load_a_half<0, 1>(lm, 0);
+    load_b_stage<0>(lm, 0);
+    load_b_stage<1>(lm, 1);
+    load_a_half<1, 0>(lm, 1);
+    load_b_stage<2>(lm, 2);
+    load_a_half<1, 1>(lm, 1);
+    Frags cur;
+    S3R_WAIT_VM(16);
+    __builtin_amdgcn_s_barrier();
+    read_unit_frags<0, 0, 0>(fm, 0, cur);
+    for (int kt = 0; kt < nk; kt += 12) {
+      unit_step<0>(lm, fm, kt, cur, acc);
+      if (kt + 1 < nk) unit_step<1>(lm, fm, kt + 1, cur, acc);
+      if (kt + 2 < nk) unit_step<2>(lm, fm, kt + 2, cur, acc);
+      if (kt + 3 < nk) unit_step<3>(lm, fm, kt + 3, cur, acc);
+      if (kt + 4 < nk) unit_step<4>(lm, fm, kt + 4, cur, acc);
+      if (kt + 5 < nk) unit_step<5>(lm, fm, kt + 5, cur, acc);
+      if (kt + 6 < nk) unit_step<6>(lm, fm, kt + 6, cur, acc);
+      if (kt + 7 < nk) unit_step<7>(lm, fm, kt + 7, cur, acc);
+      if (kt + 8 < nk) unit_step<8>(lm, fm, kt + 8, cur, acc);
+      if (kt + 9 < nk) unit_step<9>(lm, fm, kt + 9, cur, acc);
+      if (kt + 10 < nk) unit_step<10>(lm, fm, kt + 10, cur, acc);
+      if (kt + 11 < nk) unit_step<11>(lm, fm, kt + 11, cur, acc);
+    }
+  } else {
+    const LoadMap lm = make_loadmap(g, m0, n0);
+    const FragMap fm = make_fragmap();
+    load_stage<0>(lm, 0);
+    load_stage<1>(lm, 1);
+    load_stage<2>(lm, 2);
+    load_stage<3>(lm, 3);
+    Frags cur;
+    S3R_WAIT_VM(24);
+    __builtin_amdgcn_s_barrier();
+    read_frags<0>(fm, 0, cur);
+    for (int kt = 0; kt < nk; kt += kStages) {
+      k_step<0>(lm, fm, kt, cur, acc);
+      if (kt + 1 < nk) k_step<1>(lm, fm, kt + 1, cur, acc);
+      if (kt + 2 < nk) k_step<2>(lm, fm, kt + 2, cur, acc);
+      if (kt + 3 < nk) k_step<3>(lm, fm, kt + 3, cur, acc);
+      if (kt + 4 < nk) k_step<4>(lm, fm, kt + 4, cur, acc);
+    }
   }
   S3R_WAIT_VM(0);
   S3R_WAIT_LGKM0();
   __builtin_amdgcn_s_barrier();
 
-  // per-row factors of the tile into LDS (the stages are free now)
-  float4* rowf = reinterpret_cast<float4*>(g_stage0);
-  float* roweb = reinterpret_cast<float*>(g_stage1);
+  // per-row factors of the tile into LDS (the ring is free now)
+  float4* rowf = reinterpret_cast<float4*>(A_KMAJOR ? g_unit0 : g_stage0);
+  float* roweb = reinterpret_cast<float*>(A_KMAJOR ? g_unit1 : g_stage1);
   if constexpr (is_dx(EPI)) {
     // x: Delta_t / s_x[t], y: 1 / s_x[t], z: (eps_t - mu_b) / s_x[t], w: example index
     for (int r = threadIdx.x; r < BM; r += kGemmThreads) {
@@ -534,10 +726,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmParams g, 
   __syncthreads();
   if constexpr (is_dx(EPI) && EC) {
     const int64_t last = min(m0 + BM, g.M) - 1;
-    if (m0 / ep.S == last / ep.S) epilogue<EPI, EC, false, NB>(g, ep, m0, n0, acc);
-    else epilogue<EPI, EC, true, NB>(g, ep, m0, n0, acc);
+    if (m0 / ep.S == last / ep.S) epilogue<EPI, EC, false, NB>(g, ep, m0, n0, rowf, roweb, acc);
+    else epilogue<EPI, EC, true, NB>(g, ep, m0, n0, rowf, roweb, acc);
   } else {
-    epilogue<EPI, EC, false, NB>(g, ep, m0, n0, acc);
+    epilogue<EPI, EC, false, NB>(g, ep, m0, n0, rowf, roweb, acc);
   }
 }
 
