@@ -138,10 +138,29 @@ __device__ __forceinline__ int swz_m(int r) { return (r & 7) | (((r >> 4) & 1) <
 // holds chunk c = p ^ swz_m(k-row).  (The K-contiguous A has its own ring below.)
 constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit dword format (gfx9 family)
 
+// The DMAs are issued as inline assembly, which the compiler does not see as
+// LDS writes; otherwise its tracking of the DMA targets drains every load in
+// flight (vmcnt(0)) before many of the fragment reads.  Every ordering the
+// rings need is explicit: the waits, the barrier, and a fixed instruction
+// order inside a K step (sched_barrier after each MFMA group).
+__device__ __forceinline__ v4i rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t p = (uint64_t)(uintptr_t)base;
+  return v4i{(int)(uint32_t)p, (int)((uint32_t)(p >> 32) & 0xFFFFu), (int)bytes, kRsrcWord3};
+}
+
+// One 1 KB DMA: 16 bytes per lane from rsrc + voff + soff to LDS address lds + 16 * lane.
+// M0 holds the LDS address; nothing else in these kernels uses M0 (it is a
+// reserved register, which a clobber list cannot name).
+__device__ __forceinline__ void dma_1k(v4i rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff));
+}
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) { return (uint32_t)(uintptr_t)(const lds_void*)p; }
+
 struct LoadMap {           // per-thread byte offsets (tile origin + position), for 4 blocks of A and of B
   uint32_t a_off[4], b_off[4];
   uint32_t a_step, b_step; // advance per K step (uniform)
-  __amdgpu_buffer_rsrc_t ra, rb;
+  v4i ra, rb;              // buffer descriptors (raw words)
 };
 
 __device__ __forceinline__ LoadMap make_loadmap(const GemmParams& g, int64_t m0, int64_t n0) {
@@ -157,23 +176,24 @@ __device__ __forceinline__ LoadMap make_loadmap(const GemmParams& g, int64_t m0,
   }
   m.a_step = (uint32_t)(BK * g.lda);
   m.b_step = (uint32_t)(BK * g.ldb);
-  m.ra = __builtin_amdgcn_make_buffer_rsrc((void*)g.A, (short)0, (int)(uint32_t)(g.K * g.lda), kRsrcWord3);
-  m.rb = __builtin_amdgcn_make_buffer_rsrc((void*)g.B, (short)0, (int)(uint32_t)(g.K * g.ldb), kRsrcWord3);
+  m.ra = rsrc_words(g.A, (uint32_t)(g.K * g.lda));
+  m.rb = rsrc_words(g.B, (uint32_t)(g.K * g.ldb));
   return m;
 }
 
 template <int S>
+__device__ __forceinline__ void stage_dma(const LoadMap& m, int q, int wave, int kt) {
+  if (q < 4)
+    dma_1k(m.ra, lds_addr(stage<S>()) + (uint32_t)(wave * 4 + q) * 1024u, m.a_off[q], (uint32_t)kt * m.a_step);
+  else
+    dma_1k(m.rb, lds_addr(stage<S>()) + (uint32_t)(kHalf + (wave * 4 + q - 4) * 1024), m.b_off[q - 4],
+           (uint32_t)kt * m.b_step);
+}
+template <int S>
 __device__ __forceinline__ void load_stage(const LoadMap& m, int kt) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // LDS DMA base must be wave-uniform
-  const uint32_t sa = (uint32_t)kt * m.a_step, sb = (uint32_t)kt * m.b_step;
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(m.ra, (lds_void*)(stage<S>() + (wave * 4 + q) * 1024), 16, m.a_off[q],
-                                             sa, 0, 0);
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(m.rb, (lds_void*)(stage<S>() + kHalf + (wave * 4 + q) * 1024), 16,
-                                             m.b_off[q], sb, 0, 0);
+  for (int q = 0; q < 8; ++q) stage_dma<S>(m, q, wave, kt);
 }
 
 // ------------------------------------------------------------ fragments ----
@@ -243,27 +263,46 @@ __device__ __forceinline__ void interleave_schedule() {
 // One K step on stage S = kt % kStages.  On entry `cur` holds the stage's
 // first half-step fragments.  The barrier publishes stage kt+1 (this wave has
 // waited for its own loads of it) and retires stage kt-1, which is refilled
-// with step kt+4.  The second half-step's fragments are read during the first
-// half's MFMAs, and the next stage's first fragments during the second half's.
+// with step kt+4.  First half-step: MFMA x on `cur`, then fragment read x of
+// the second half-step, and after every other MFMA one of the refill's 8
+// DMAs.  Second half-step: MFMA x on `nxt`, then fragment read x of the next
+// stage's first half-step.  Read x < 8 is a transposed half of A block x/2,
+// the rest of B block (x-8)/2.
+template <int S>
+__device__ __forceinline__ void stage_read(const FragMap& f, int kk, int x, Frags& fr) {
+  const int blk = (x & 7) >> 1, hi = x & 1;
+  const uint8_t* p = x < 8 ? stage<S>() + f.a_t[blk] : stage<S>() + kHalf + f.b_t[blk];
+  const v2i v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(p + kk * 8192 + hi * 2048));
+  v4i& d = x < 8 ? fr.a[blk] : fr.b[blk];
+  if (hi) { d.z = v.x; d.w = v.y; }
+  else { d.x = v.x; d.y = v.y; }
+}
 template <int S>
 __device__ __forceinline__ void k_step(const LoadMap& lm, const FragMap& fm, int kt, Frags& cur,
                                        v16i (&acc)[4][4]) {
-  constexpr int NR = 16;   // LDS reads per half-step
   // Every step refills one stage, also past the last step (those loads read past
   // the end of the data or land in retired stages), so exactly the loads of
   // stages kt+2 and kt+3 may still be in flight here.
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   S3R_WAIT_VM(16);
   S3R_WAIT_LGKM0();
   __builtin_amdgcn_s_barrier();
-  load_stage<(S + 4) % kStages>(lm, kt + 4);
+  __builtin_amdgcn_sched_barrier(0);
   Frags nxt;
-  read_frags<S>(fm, 1, nxt);
-  mfma16(cur, acc);
-  interleave_schedule<NR, 8>();
+#pragma unroll
+  for (int x = 0; x < 16; ++x) {
+    acc[x >> 2][x & 3] = __builtin_amdgcn_mfma_i32_32x32x32_i8(cur.a[x >> 2], cur.b[x & 3], acc[x >> 2][x & 3], 0, 0, 0);
+    stage_read<S>(fm, 1, x, nxt);
+    if ((x & 1) == 0) stage_dma<(S + 4) % kStages>(lm, x >> 1, wave, kt + 4);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   // next stage's first fragments (after the last step this reads a stale stage; unused)
-  read_frags<(S + 1) % kStages>(fm, 0, cur);
-  mfma16(nxt, acc);
-  interleave_schedule<NR, 0>();
+#pragma unroll
+  for (int x = 0; x < 16; ++x) {
+    acc[x >> 2][x & 3] = __builtin_amdgcn_mfma_i32_32x32x32_i8(nxt.a[x >> 2], nxt.b[x & 3], acc[x >> 2][x & 3], 0, 0, 0);
+    stage_read<(S + 1) % kStages>(fm, 0, x, cur);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
 // ------------------------------------- the unit ring (K-contiguous A) ----
@@ -291,11 +330,6 @@ struct UnitMap {
   v4i ra, rb;            // buffer descriptors (raw words)
 };
 
-__device__ __forceinline__ v4i rsrc_words(const void* base, uint32_t bytes) {
-  const uint64_t p = (uint64_t)(uintptr_t)base;
-  return v4i{(int)(uint32_t)p, (int)((uint32_t)(p >> 32) & 0xFFFFu), (int)bytes, kRsrcWord3};
-}
-
 __device__ __forceinline__ UnitMap make_unitmap(const GemmParams& g, int64_t m0, int64_t n0) {
   UnitMap m;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -315,15 +349,6 @@ __device__ __forceinline__ UnitMap make_unitmap(const GemmParams& g, int64_t m0,
   m.rb = rsrc_words(g.B, (uint32_t)(g.K * g.ldb));
   return m;
 }
-
-// One 1 KB DMA: 16 bytes per lane from rsrc + voff + soff to LDS address lds + 16 * lane.
-// M0 holds the LDS address; nothing else in these kernels uses M0 (it is a
-// reserved register, which a clobber list cannot name).
-__device__ __forceinline__ void dma_1k(v4i rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff));
-}
-__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) { return (uint32_t)(uintptr_t)(const lds_void*)p; }
 
 // DMA q (0..7) of a K step: q < 4 fill B stage SB with K step kt_b, q >= 4 fill
 // half H of unit slot SU with unit u.
