@@ -21,9 +21,11 @@
 //   K-contiguous A (dX): A in units of two K steps (whole 128-byte lines per
 //     row), three units of 32 KB beside four B stages of 16 KB.
 //   M/N-contiguous tiles: 64 k-rows x 256 B; chunk c of k-row r sits at
-//     c ^ swz_m(r), swz_m(r) = (r & 7) | ((r >> 4) & 1) << 3 (the two
-//     half-waves of a read use k-rows 16 apart and so land in different
-//     halves of the banks); fragments are read with two ds_read_b64_tr_b8: within each
+//     c ^ swz_m(r), swz_m(r) = (r & 7) << 1: a half-wave of a transpose read
+//     takes an aligned pair of chunks from each of 8 consecutive k-rows, and
+//     the swizzle puts those 8 pairs in the 8 different 32-byte bank groups
+//     (rocprofv3 counts no LDS bank conflicts); fragments are read with two
+//     ds_read_b64_tr_b8: within each
 //     16-lane group, lane L fetches 8 bytes of k-row kb + L/2 at column
 //     nb + 8(L%2), and the hardware hands lane i the bytes of column nb + i
 //     from the 8 k-rows, so a lane ends up with 16 consecutive k of one
@@ -119,7 +121,7 @@ struct GemmParams {
   int tiles_m, tiles_n;
 };
 
-__device__ __forceinline__ int swz_m(int r) { return (r & 7) | (((r >> 4) & 1) << 3); }
+__device__ __forceinline__ int swz_m(int r) { return (r & 7) << 1; }
 
 // s_waitcnt immediates (gfx9 encoding): wait for at most n vector-memory ops / no LDS ops.
 #define S3R_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | 0x70 | 0xF00)
