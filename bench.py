@@ -159,6 +159,15 @@ class Timeline:
         import numpy as np
         return float(np.mean([d[name][0].elapsed_time(d[name][1]) for d in self.ev])) * 1e3
 
+    def spread(self):
+        """[min, median, max] in us of every interval over the timed steps."""
+        import numpy as np
+        out = {}
+        for n in self.names:
+            v = np.array([d[n][0].elapsed_time(d[n][1]) for d in self.ev]) * 1e3
+            out[n] = [round(float(v.min()), 2), round(float(np.median(v)), 2), round(float(v.max()), 2)]
+        return out
+
 
 def main():
     ap = argparse.ArgumentParser()
@@ -346,6 +355,7 @@ def run_block(args, dev, torch, inputs, s3r):
         "kernels_us": {**{f"quantize_{n}": round(tl.avg_us(f"quantize_{n}"), 2) for n in st},
                        **{f"gemm_{k}": round(v, 2) for k, v in gemm_us.items()},
                        "glue": round(tl.avg_us("glue"), 2), "step_events": round(tl.avg_us("step"), 2)},
+        "kernels_us_min_median_max": tl.spread(),
         "gemm_tops": {k: round(gop / (v / 1e6) / 1e3, 1) for k, v in gemm_us.items()},
         "roofline": _roofline(gemm_us, b.name, gop),
     }
@@ -452,6 +462,7 @@ def run_moe(args, dev, torch, inputs, s3r):
                       "algorithmic_bytes": q_bytes},
         "kernels_us": {"quantize_call": round(t_q, 2), "gemm_dx": round(t_gx, 2), "gemm_dw": round(t_gw, 2),
                        "step_events": round(tl.avg_us("step"), 2)},
+        "kernels_us_min_median_max": tl.spread(),
         "gemm_tops": {"dx": round(gop / (t_gx / 1e6) / 1e3, 1), "dw": round(gop / (t_gw / 1e6) / 1e3, 1)},
         "roofline": _roofline({"dx": t_gx, "dw": t_gw}, m.name, gop),
     }
@@ -521,6 +532,7 @@ def run_linear(args, dev, torch, inputs, s3r):
                       "frac_of_hbm_peak": round(q_gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": q_bytes},
         "kernels_us": {"quantize_call": round(t_q, 2), "gemm_dx": round(t_gx, 2), "gemm_dw": round(t_gw, 2),
                        "step_events": round(tl.avg_us("step"), 2)},
+        "kernels_us_min_median_max": tl.spread(),
         "gemm_tops": {"dx": round(gop / (t_gx / 1e6) / 1e3, 1), "dw": round(gop / (t_gw / 1e6) / 1e3, 1)},
         "roofline": _roofline({"dx": t_gx, "dw": t_gw}, w.name, gop),
     }
@@ -622,6 +634,7 @@ def run_mx(args, dev, torch, inputs, s3r):
                       "frac_of_hbm_peak": round(q_gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": q_bytes},
         "kernels_us": {"quantize_call": round(t_q, 2), "gemm_dx": round(t_gx, 2), "gemm_dw": round(t_gw, 2),
                        "step_events": round(tl.avg_us("step"), 2)},
+        "kernels_us_min_median_max": tl.spread(),
         "gemm_tops": {"dx": round(gop / (t_gx / 1e6) / 1e3, 1), "dw": round(gop / (t_gw / 1e6) / 1e3, 1)},
         "roofline": {"kernel": f"mx gemm {key}", "bound": "mfma", "achieved": round(achieved, 1),
                      "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP4_TFLOPS, 4),

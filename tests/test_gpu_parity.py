@@ -40,8 +40,11 @@ def _padded_i8(a: np.ndarray) -> torch.Tensor:
 
 # ------------------------------------------------------------- GEMMs ----
 
-@pytest.mark.parametrize("M,N,K", [(256, 256, 64), (1, 17, 3), (300, 520, 200), (512, 768, 1024),
-                                   (257, 255, 4100)])
+# K steps of 64: 1, 2, 3 (the rings' prologues), 4, 5, 6 (the dW ring's five stages), 12, 13, 25 (the dX
+# ring's twelve-step schedule and its tail), 16, 65; ragged M, N and K.
+@pytest.mark.parametrize("M,N,K", [(256, 256, 64), (1, 17, 3), (64, 300, 128), (300, 64, 150), (300, 520, 200),
+                                   (257, 128, 320), (128, 257, 384), (256, 256, 768), (130, 260, 832),
+                                   (512, 768, 1024), (256, 512, 1600), (257, 255, 4100)])
 def test_gemm_raw_accumulators_exact(M, N, K):
     rng = np.random.default_rng(M * 7 + N * 3 + K)
     # dX-shaped: Q [M x K] . Wq [K x N]
