@@ -300,3 +300,32 @@ def test_product_path_does_not_import_oracle():
         if fn.endswith(".py"):
             src = open(os.path.join(pkg, fn)).read()
             assert "import oracle" not in src and "from oracle" not in src, fn
+
+
+def test_gemm_m0_written_only_by_its_dma_assembly(tmp_path):
+    """The GEMM rings issue their LDS DMAs as inline assembly that sets M0 (the LDS address) itself; the
+    compiler is not told, so no compiler-generated instruction of gemm.hip may read or write M0."""
+    from stochastic_rounding_quantization_amd import build
+    import subprocess
+    src = os.path.join(build.CSRC, "gemm.hip")
+    out = tmp_path / "gemm.s"
+    flags = [f for f in build.HIPCC_FLAGS if f not in ("-fPIC", "-shared")]
+    cmd = [build.hipcc(), *flags, "--cuda-device-only", "-S", "-I", os.path.join(build.ROOT, "include"), src,
+           "-o", str(out)]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-2000:]
+    inside, dma_blocks, stray = False, 0, []
+    for line in out.read_text().splitlines():
+        if "ASMSTART" in line:
+            inside = True
+            continue
+        if "ASMEND" in line:
+            inside = False
+            continue
+        code = line.split(";")[0]
+        if inside:
+            dma_blocks += "buffer_load_dwordx4" in code and " lds" in code
+        elif re.search(r"\bm0\b", code):
+            stray.append(line.strip())
+    assert dma_blocks > 0
+    assert not stray, stray[:5]
