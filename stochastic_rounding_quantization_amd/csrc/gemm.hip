@@ -151,8 +151,9 @@ __device__ __forceinline__ v4i rsrc_words(const void* base, uint32_t bytes) {
 }
 
 // One 1 KB DMA: 16 bytes per lane from rsrc + voff + soff to LDS address lds + 16 * lane.
-// M0 holds the LDS address; nothing else in these kernels uses M0 (it is a
-// reserved register, which a clobber list cannot name).
+// M0 holds the LDS address; no compiler-generated instruction of this file
+// reads or writes M0 (a reserved register, which a clobber list cannot name;
+// the CPU tests check the compiled assembly for it).
 __device__ __forceinline__ void dma_1k(v4i rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff));
@@ -321,11 +322,8 @@ __device__ __forceinline__ void k_step(const LoadMap& lm, const FragMap& fm, int
 // loads of one step (8 per wave) may be in flight at the wait.
 __device__ __forceinline__ int swz_u(int r) { return (r >> 1) & 7; }
 
-// The unit ring issues its DMAs as inline assembly, which the compiler does not
-// see as LDS writes: tracking seven DMA targets, it otherwise drains every load
-// in flight (vmcnt(0)) before most of the K steps' fragment reads.  Every
-// ordering the ring needs is explicit: the waits, the barrier, and a fixed
-// instruction order inside a K step (sched_barrier after each MFMA group).
+// Its DMAs are the inline assembly above (with seven DMA targets the compiler's
+// own tracking drained the loads in flight before most fragment reads).
 struct UnitMap {
   uint32_t a_off[2][4], b_off[4];
   uint32_t b_step;
