@@ -359,11 +359,50 @@ def run_block(args, dev, torch, inputs, s3r):
         "gemm_tops": {k: round(gop / (v / 1e6) / 1e3, 1) for k, v in gemm_us.items()},
         "roofline": _roofline(gemm_us, b.name, gop),
     }
+    del st, dv, dH, dX, Gg, Gu, ws_q, ws_g, ws_b, ws_b2
+    out["bf16_context"] = bf16_gemm_context(torch, dev, T, M, F, sum(gemm_us.values()), ms_step, args.steps)
     if args.cpu_rows != 0:
         rows = S if args.cpu_rows < 0 else max(S, min(args.cpu_rows, T) // S * S)
         log(f"CPU oracle baseline on the first {rows} tokens")
         out["cpu_baseline"] = block_cpu_baseline(inp, b, mode, ec, rows)
     return out
+
+
+def bf16_gemm_context(torch, dev, T, M, F, int8_gemm_us, int8_step_ms, steps):
+    """Context for the pages' speedups over BF16 (not the method): the FFN block's six backward products as
+    plain bf16 GEMMs (torch.matmul, hipBLASLt), fp32 accumulation and bf16 outputs, on random operands of the
+    same shapes, timed like the step."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    r = lambda *s_: torch.randn(*s_, device=dev, generator=g).to(torch.bfloat16)
+    Gd, Gg, Gu = r(T, M), r(T, F), r(T, F)
+    Wd, Wg, Wu = r(M, F), r(F, M), r(F, M)
+    H, X = r(T, F), r(T, M)
+    Gdt, Ggt, Gut = Gd.t().contiguous(), Gg.t().contiguous(), Gu.t().contiguous()
+
+    def six():
+        torch.matmul(Gd, Wd)        # dH = G_down . W_down      [T x F]
+        torch.matmul(Gdt, H)        # dW_down = G_down^T . H    [M x F]
+        torch.matmul(Gg, Wg)        # dX (gate)                 [T x M]
+        torch.matmul(Ggt, X)        # dW_gate                   [F x M]
+        torch.matmul(Gu, Wu)        # dX (up)
+        torch.matmul(Gut, X)        # dW_up
+
+    for _ in range(3):
+        six()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        six()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    return {"bf16_six_gemms_ms": round(ms, 4), "int8_six_gemms_ms": round(int8_gemm_us / 1e3, 4),
+            "gemm_speedup_over_bf16": round(ms / (int8_gemm_us / 1e3), 3),
+            "step_speedup_over_bf16_gemms_alone": round(ms / int8_step_ms, 3),
+            "note": "torch.matmul bf16 on the same shapes; context for the pages' ratios, not a measured baseline "
+                    "of the method"}
 
 
 def moe_cpu_baseline(inp, m, mode, ec, experts):
