@@ -896,21 +896,22 @@ hipError_t fill_zero(float* p, int64_t n, hipStream_t st) {
 }
 
 
-// out[i] = sum over bands c of part[c][i], in fp64.  tpi lanes share an output:
-// each adds every tpi-th band in order (eight loads in flight), then an xor
-// butterfly (the same order on every lane) adds the lanes.
+// out[i] = sum over bands c of part[c][i], in fp64.  A block takes 64
+// consecutive outputs, one per lane, so each load of a wave is 256 contiguous
+// bytes; wave w adds the bands c = w mod 4 in order (eight loads in flight),
+// and the four waves' sums are added in wave order.
 __global__ __launch_bounds__(256) void gemv_reduce_kernel(const float* __restrict__ part, int64_t nbands,
-                                                          int64_t count, int tpi, float* __restrict__ out) {
-  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t i = g / tpi;
-  const int sub = (int)(g % tpi);
+                                                          int64_t count, float* __restrict__ out) {
+  __shared__ double wsum[4][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t i = (int64_t)blockIdx.x * 64 + lane;
   double a = 0.0;
   if (i < count) {
-    for (int64_t c = sub; c < nbands; c += 8 * (int64_t)tpi) {
+    for (int64_t c = wave; c < nbands; c += 32) {
       float t[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int64_t cc = c + (int64_t)u * tpi;
+        const int64_t cc = c + (int64_t)u * 4;
         const float v = part[min(cc, nbands - 1) * count + i];
         t[u] = cc < nbands ? v : 0.f;
       }
@@ -918,8 +919,9 @@ __global__ __launch_bounds__(256) void gemv_reduce_kernel(const float* __restric
       for (int u = 0; u < 8; ++u) a += (double)t[u];
     }
   }
-  for (int o = 1; o < tpi; o <<= 1) a += __shfl_xor(a, o, 64);
-  if (i < count && sub == 0) out[i] = (float)a;
+  wsum[wave][lane] = a;
+  __syncthreads();
+  if (wave == 0 && i < count) out[i] = (float)(((wsum[0][lane] + wsum[1][lane]) + wsum[2][lane]) + wsum[3][lane]);
 }
 
 hipError_t run_gemv(const int8_t* P, int64_t ld, int64_t K, int64_t N, int64_t nb, int token_mode, const float* C,
@@ -933,11 +935,8 @@ hipError_t run_gemv(const int8_t* P, int64_t ld, int64_t K, int64_t N, int64_t n
     hipLaunchKernelGGL(gemv_partial_kernel<4>, grid, dim3(kGvThreads), 0, st, P, ld, K, N, nb, token_mode, C, ec_row,
                        ec_mean, S, part, (int64_t)0, (const int64_t*)nullptr, (const int32_t*)nullptr, (int64_t)0);
   const int64_t count = nb * N;
-  int tpi = 1;
-  while (tpi < 16 && tpi * 8 < nbands) tpi *= 2;
-  const int64_t threads = count * tpi;
-  hipLaunchKernelGGL(gemv_reduce_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, part, nbands,
-                     count, tpi, out);
+  hipLaunchKernelGGL(gemv_reduce_kernel, dim3((unsigned)((count + 63) / 64)), dim3(256), 0, st, part, nbands, count,
+                     out);
   return hipGetLastError();
 }
 
@@ -1300,10 +1299,8 @@ hipError_t launch_grouped_backward_dx(const DxArgs& a, int64_t G, const int64_t*
                          0, a.ec_col, (const float*)nullptr, (const float*)nullptr, (int64_t)1, part, w_stride,
                          (const int64_t*)nullptr, (const int32_t*)nullptr, (int64_t)0);
       const int64_t count = G * a.d_in;
-      int tpi = 1;
-      while (tpi < 16 && tpi * 8 < nbands) tpi *= 2;
-      hipLaunchKernelGGL(gemv_reduce_kernel, dim3((unsigned)((count * tpi + 255) / 256)), dim3(256), 0, st, part,
-                         nbands, count, tpi, v);
+      hipLaunchKernelGGL(gemv_reduce_kernel, dim3((unsigned)((count + 63) / 64)), dim3(256), 0, st, part, nbands,
+                         count, v);
     } else {
       e = fill_zero(v, G * a.d_in, st);
     }

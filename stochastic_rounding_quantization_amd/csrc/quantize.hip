@@ -531,7 +531,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
 // eps; the last row block to finish (counter reset to 0 by the quantize kernel)
 // adds the block sums of each example in order to get its grand mean mu_b.
 constexpr int kFinRows = 256;
-constexpr int kColLanes = 8;
+static_assert(kThreads / kWave == 4, "the finalize kernel's column blocks add four waves' sums");
 
 __global__ __launch_bounds__(kThreads) void finalize_kernel(
     int64_t B, int64_t D, int64_t S, int tiles_per_example, int n_ctiles, int per_token, int ncb,
@@ -540,25 +540,30 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(
     int32_t* __restrict__ code_colsum, float* __restrict__ ec_row, float* __restrict__ ec_mean,
     double* __restrict__ blk_sum, uint32_t* __restrict__ counter) {
   if ((int)blockIdx.x < ncb) {
-    // kColLanes lanes share an item: each adds every kColLanes-th row tile of the example in
-    // order, then a fixed xor butterfly adds the lanes
-    const int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    const int64_t idx = g / kColLanes;
-    const int sub = (int)(g % kColLanes);
-    const bool ok = idx < B * D;                 // uniform over a lane group
+    // A block takes 64 consecutive (example, column) items, one per lane, so a
+    // wave's loads are contiguous; wave w adds the example's row tiles k = w mod 4
+    // in order, and the four waves' sums are added in wave order.
+    __shared__ double csum[kThreads / kWave][kWave];
+    __shared__ int32_t qsum[kThreads / kWave][kWave];
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int64_t idx = (int64_t)blockIdx.x * kWave + lane;
+    const bool ok = idx < B * D;
     const int64_t b = ok ? idx / D : 0, j = ok ? idx % D : 0;
     double a = 0.0;
     int32_t aq = 0;
-    for (int k = sub; k < tiles_per_example; k += kColLanes) {
-      const int64_t at = (b * tiles_per_example + k) * D + j;
-      if (ec_col) a += (double)col_part[at];
-      if (code_colsum) aq += colq_part[at];
+    if (ok) {
+      for (int k = wave; k < tiles_per_example; k += kThreads / kWave) {
+        const int64_t at = (b * tiles_per_example + k) * D + j;
+        if (ec_col) a += (double)col_part[at];
+        if (code_colsum) aq += colq_part[at];
+      }
     }
-    for (int o = 1; o < kColLanes; o <<= 1) {
-      a += __shfl_xor(a, o, kWave);
-      aq += __shfl_xor(aq, o, kWave);
-    }
-    if (!ok || sub != 0) return;
+    csum[wave][lane] = a;
+    qsum[wave][lane] = aq;
+    __syncthreads();
+    if (!ok || wave != 0) return;
+    a = ((csum[0][lane] + csum[1][lane]) + csum[2][lane]) + csum[3][lane];
+    aq = qsum[0][lane] + qsum[1][lane] + qsum[2][lane] + qsum[3][lane];
     if (ec_col) {
       const double d = per_token ? 1.0 : (double)delta[0];
       ec_col[idx] = (float)(a * d / (double)S);
@@ -1257,7 +1262,7 @@ void run_quantize(const QuantArgs& a, const WsLayout& L, hipStream_t st) {
   dim3 grid((unsigned)(B * p.tiles_per_example), (unsigned)p.n_ctiles);
   dispatch_mode<TIn, VEC>(a, L, p, grid, st);
   if (a.ec || a.code_colsum) {
-    const int64_t ncb = (B * a.D * kColLanes + kThreads - 1) / kThreads;
+    const int64_t ncb = (B * a.D + kWave - 1) / kWave;
     const int bpe = (int)((a.S + kFinRows - 1) / kFinRows);
     const int64_t nrb = a.ec ? B * bpe : 0;
     hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)(ncb + nrb)), dim3(kThreads), 0, st, B, a.D, a.S,
