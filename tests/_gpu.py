@@ -3,6 +3,9 @@
 The GPU side goes only through the C ABI (via the thin binding); expected values
 come only from oracle/.
 """
+import json
+import os
+
 import numpy as np
 import torch
 
@@ -27,6 +30,50 @@ def rel_err(got, exp) -> float:
     exp = np.asarray(exp, np.float64)
     scale = np.abs(exp).max() if exp.size else 0.0
     return float(np.abs(got - exp).max() / scale) if scale > 0 else float(np.abs(got - exp).max() if got.size else 0)
+
+
+def row_rel_err(got, exp) -> float:
+    """Max over rows of max|got - exp| / max|exp| within the row.
+
+    A row is a token of dX and a channel of dW: each is held to the tolerance on its own
+    magnitude, so a small row beside outlier rows is not judged on the outliers' scale.  A row
+    whose reference is exactly zero is held to the absolute difference.
+    """
+    got = np.asarray(got, np.float64)
+    exp = np.asarray(exp, np.float64)
+    if got.size == 0:
+        return 0.0
+    g = got.reshape(got.shape[0], -1)
+    e = exp.reshape(exp.shape[0], -1)
+    diff = np.abs(g - e).max(axis=1)
+    scale = np.abs(e).max(axis=1)
+    return float(np.where(scale > 0, diff / np.where(scale > 0, scale, 1.0), diff).max())
+
+
+def elementwise_fail_frac(got, exp, tol) -> float:
+    """Fraction of elements with |got - exp| > tol * |exp| (each element on its own magnitude)."""
+    got = np.asarray(got, np.float64)
+    exp = np.asarray(exp, np.float64)
+    if got.size == 0:
+        return 0.0
+    return float((np.abs(got - exp) > tol * np.abs(exp)).mean())
+
+
+def assert_rows_close(got, exp, tol, what=""):
+    """Per-row relative bar (see row_rel_err); prints the elementwise failure fraction beside it.
+
+    With S3R_PARITY_LOG set, each comparison is also appended to that file as one JSON line.
+    """
+    err = row_rel_err(got, exp)
+    frac = elementwise_fail_frac(got, exp, tol)
+    print(f"[parity] {what}: max per-row rel err {err:.3g}; elements beyond {tol:g} relative: {frac:.3g}",
+          flush=True)
+    log = os.environ.get("S3R_PARITY_LOG")
+    if log:
+        with open(log, "a") as f:
+            f.write(json.dumps({"what": what, "shape": list(np.shape(got)), "row_rel_err": err,
+                                "elementwise_fail_frac": frac, "tol": tol}) + "\n")
+    assert err <= tol, f"{what}: per-row relative error {err:.3g} > {tol:g} (elementwise fraction {frac:.3g})"
 
 
 def gpu_linear(inp: dict, *, mode, ec, scale=s3r.PER_TENSOR, seed=0, layer_id=0, rows_per_example, dw=True):

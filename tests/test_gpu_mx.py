@@ -12,7 +12,7 @@ import torch
 
 from oracle import mx, quantize as oq
 from stochastic_rounding_quantization_amd import inputs, s3r
-from tests._gpu import DEV, host, rel_err, to_dev
+from tests._gpu import DEV, assert_rows_close, host, rel_err, to_dev
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-5
@@ -97,8 +97,8 @@ def test_mx_small_f32_modes(mode, ec):
                       seed=3, layer_id=2)
     _check_quant(gpu, ref)
     _check_stats(gpu, ref, S)
-    assert rel_err(host(gpu["dX"]), ref["dX"]) < TOL
-    assert rel_err(host(gpu["dW"]), ref["dW"]) < TOL
+    assert_rows_close(host(gpu["dX"]), ref["dX"], TOL, "mx dX")
+    assert_rows_close(host(gpu["dW"]), ref["dW"], TOL, "mx dW")
 
 
 @pytest.mark.parametrize("T,D,d_in,S", [(384, 256, 40, 128), (768, 640, 600, 256), (512, 128, 520, 512)])
@@ -110,8 +110,8 @@ def test_mx_tiles_and_tails_bf16(T, D, d_in, S):
                       rows_per_example=S, seed=11)
     _check_quant(gpu, ref)
     _check_stats(gpu, ref, S)
-    assert rel_err(host(gpu["dX"]), ref["dX"]) < TOL
-    assert rel_err(host(gpu["dW"]), ref["dW"]) < TOL
+    assert_rows_close(host(gpu["dX"]), ref["dX"], TOL, "mx dX")
+    assert_rows_close(host(gpu["dW"]), ref["dW"], TOL, "mx dW")
 
 
 def test_mx_many_examples_dx_correction():
@@ -124,8 +124,8 @@ def test_mx_many_examples_dx_correction():
                       rows_per_example=S, seed=4)
     _check_quant(gpu, ref)
     _check_stats(gpu, ref, S)
-    assert rel_err(host(gpu["dX"]), ref["dX"]) < TOL
-    assert rel_err(host(gpu["dW"]), ref["dW"]) < TOL
+    assert_rows_close(host(gpu["dX"]), ref["dX"], TOL, "mx dX")
+    assert_rows_close(host(gpu["dW"]), ref["dW"], TOL, "mx dW")
     q = s3r.mx_quantize(to_dev(inp["G"], "f32"), mode=s3r.S3R, ec=s3r.EC_TWO_WAY, rows_per_example=S)
     Xt, Xts, xs = s3r.mx_operand(to_dev(inp["X"], "f32"), rows_per_example=S)
     dW = torch.empty(D, d_in, device=DEV)
@@ -195,5 +195,5 @@ def test_mx_headline_workload_sampled():
     for nm, st in (("h", q.ec_h), ("t", q.ec_t)):
         assert rel_err(host(st[0]), ref["eps_" + nm]) < TOL, nm
         assert rel_err(host(st[1]), ref["ebar_" + nm]) < TOL, nm
-    assert rel_err(host(gpu["dX"])[np.ix_(rows, cols)], ref["dX"]) < TOL
-    assert rel_err(host(gpu["dW"])[np.ix_(crow, cols)], ref["dW"]) < TOL
+    assert_rows_close(host(gpu["dX"])[np.ix_(rows, cols)], ref["dX"], TOL, "mx headline dX (sampled)")
+    assert_rows_close(host(gpu["dW"])[np.ix_(crow, cols)], ref["dW"], TOL, "mx headline dW (sampled)")
