@@ -28,12 +28,10 @@
  *     reports a launch failure).
  *   - Results are bitwise deterministic: no floating-point atomics, all
  *     reductions in a fixed order.
- *   - Workspaces: the caller zero-fills a workspace once, before its first use
- *     (hipMemset, torch.zeros).  Its first 64 KiB hold the library's
- *     synchronization words, which every completed call leaves valid for the
- *     next call; do not write them.  One workspace may serve quantize and
- *     backward calls; calls that overlap in time (different streams) must not
- *     share a workspace.
+ *   - Workspaces hold scratch partial results only: their contents need no
+ *     initialisation and are not kept between calls.  One workspace may serve
+ *     quantize and backward calls; calls that overlap in time (different
+ *     streams) must not share a workspace.
  *   - Weight layout: W is stored [D x d_in] (PyTorch Linear layout, the
  *     page's W^T), Wq likewise; X is [T x d_in].
  */
@@ -83,8 +81,7 @@ typedef enum { S3R_PER_TENSOR = 0, S3R_PER_TOKEN = 1 } s3r_scale;
 /* Bits OR-ed into the optional device flags word by s3r_quantize. */
 #define S3R_FLAG_NONFINITE  1u  /* an amax was Inf/NaN: affected codes are 0 */
 #define S3R_FLAG_TINY_STEP  2u  /* an amax so small that 127*2^24/amax overflows fp32: codes 0 */
-#define S3R_FLAG_SYNC_TIMEOUT 4u /* the single-pass quantizer's grid-wide wait timed out (its
-                                    workgroups were not all resident): outputs invalid */
+/* bit 4u is unused (reserved) */
 #define S3R_FLAG_BAD_GROUPS 8u  /* grouped calls: the group offsets are not a non-decreasing
                                    sequence from 0 to the row count; nothing was computed */
 
@@ -129,14 +126,10 @@ typedef struct s3r_qdesc {
  *   flags    device uint32 or NULL: S3R_FLAG_* bits are OR-ed in (the caller
  *            clears it).
  *   ws       device workspace of at least s3r_quantize_workspace(desc) bytes,
- *            256-byte aligned, zero-filled before its first use (see above).
- * Per-tensor steps of bf16 G whose D is a power of two in [512, 8192] and that
- * fits on chip (T*D up to about 2^25 elements on MI355X) take a single-pass
- * kernel that reads G from HBM once; it needs every one of its workgroups
- * (at most one per CU) resident at the same time.  If other work holds CUs
- * for the whole call, its bounded wait expires, S3R_FLAG_SYNC_TIMEOUT is set
- * and the outputs are invalid.  Setting S3R_QUANTIZE_TWO_PASS=1 in the
- * environment selects the two-pass kernels instead (same results).
+ *            256-byte aligned.
+ * A per-tensor step reads G twice (the amax pass, then the code pass); no
+ * kernel waits on another workgroup, so the results do not depend on what
+ * else runs on the device.
  * Thresholds: SR element (t,j) uses Philox4x32-10 block e>>2 of e = t*D + j
  * (counter {lo,hi}(e>>2), layer_id, 0; key = seed), word e&3, r =
  * (2*(w>>9)+1)/2^24; S3R token t uses block t>>4 (counter ..., layer_id, 1),
@@ -193,8 +186,7 @@ int s3r_quantize_with_amax(const s3r_qdesc* desc,
  *   Wq [D x d_in] int8 (ld_w), s_x [T] f32 (NULL = 1),
  *   r_W [d_in] int32 (required iff the correction applies), ec_* as from
  *   s3r_quantize.
- *   ws: s3r_backward_workspace(desc, d_in) bytes (dX needs none without EC),
- *   zero-filled once.
+ *   ws: s3r_backward_workspace(desc, d_in) bytes (dX needs none without EC).
  */
 int s3r_backward_dx(const s3r_qdesc* desc,
                     const int8_t* Q, int64_t ld_q, const float* delta,
@@ -250,7 +242,7 @@ size_t s3r_backward_workspace(const s3r_qdesc* desc, int64_t d_in);
  *            used (pass 1); mode RTNE, SR or S3R (not S3R_BCAST); thresholds
  *            are keyed on the global row index exactly as in s3r_quantize.
  *   ws       s3r_grouped_workspace(desc, G, d_in) bytes serve all three calls
- *            (256-byte aligned, zero-filled once).
+ *            (256-byte aligned).
  * Empty groups are allowed: their step is 1, their statistics 0, their dW 0.
  */
 size_t s3r_grouped_workspace(const s3r_qdesc* desc, int64_t groups, int64_t d_in);

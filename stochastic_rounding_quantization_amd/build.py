@@ -35,19 +35,41 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
+def _filter(stderr: str) -> str:
+    noise = "not a recognized feature for this target"
+    return "\n".join(l for l in stderr.splitlines() if noise not in l and "(ignoring feature)" not in l)
+
+
 def build(verbose: bool = False, extra=()) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    """Compile every source to an object in parallel, then link libs3r.so."""
+    from concurrent.futures import ThreadPoolExecutor
+    objdir = os.path.join(ROOT, "_build", "s3r")
+    os.makedirs(objdir, exist_ok=True)
+    compile_flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+    inc = ["-I", os.path.join(ROOT, "include")]
+
+    def compile_one(src):
+        obj = os.path.join(objdir, src.replace(".hip", ".o"))
+        cmd = [hipcc(), *compile_flags, *extra, *inc, "-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        return obj, subprocess.run(cmd, capture_output=True, text=True)
+
+    with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
+        results = list(ex.map(compile_one, SOURCES))
+    for (obj, res), src in zip(results, SOURCES):
+        err = _filter(res.stderr)
+        if res.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src} ({res.returncode}):\n{err}")
+        if verbose and err.strip():
+            print(err)
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-I", os.path.join(ROOT, "include"), *srcs, "-o", tmp]
+    cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *[o for o, _ in results], "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
-    noise = "not a recognized feature for this target"
-    err = "\n".join(l for l in res.stderr.splitlines() if noise not in l and "(ignoring feature)" not in l)
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
-    if verbose and err.strip():
-        print(err)
+        raise RuntimeError(f"link failed ({res.returncode}):\n{_filter(res.stderr)}")
     os.replace(tmp, LIB)
     return LIB
 

@@ -1127,16 +1127,16 @@ GemmTiming& gemm_timing() {
 size_t dx_workspace(int64_t T, int64_t D, int64_t d_in, int64_t S, int ec) {
   if (!ec || S <= 0) return 0;
   const int64_t B = T / S;
-  return kWsHeaderBytes + gemv_part_bytes(D, d_in, B) + align_up((size_t)B * d_in * 4, 256);
+  return gemv_part_bytes(D, d_in, B) + align_up((size_t)B * d_in * 4, 256);
 }
 
-// dW workspace: header | two-way EC: GEMV band partials, u [d_in] | per-token
+// dW workspace: two-way EC: GEMV band partials, u [d_in] | per-token
 // steps: Zq [T x ldz], column maxima (bits) [d_in], column steps [d_in].
 struct DwLayout { size_t part, u, zq, cbits, cval, total; };
 
 DwLayout dw_layout(int64_t T, int64_t d_in, int ec, int per_token) {
   DwLayout L{};
-  size_t off = kWsHeaderBytes;
+  size_t off = 0;
   if (ec == S3R_EC_TWO_WAY || ec == S3R_EC_DW_ONLY) {
     L.part = off; off += gemv_part_bytes(T, d_in, 1);
     L.u = off;    off += align_up((size_t)d_in * 4, 256);
@@ -1146,7 +1146,7 @@ DwLayout dw_layout(int64_t T, int64_t d_in, int ec, int per_token) {
     L.cbits = off; off += align_up((size_t)d_in * 4, 256);
     L.cval = off;  off += align_up((size_t)d_in * 4, 256);
   }
-  L.total = off == kWsHeaderBytes ? 0 : off;
+  L.total = off;
   return L;
 }
 
@@ -1164,8 +1164,8 @@ hipError_t launch_backward_dx(const DxArgs& a, hipStream_t st) {
   ep.S = a.S; ep.B = B;
   ep.out = a.out; ep.ld_out = a.ld_out; ep.out_i32 = a.out_dt == S3R_I32_RAW;
   if (ep.ec && a.T > 0 && a.d_in > 0) {
-    float* part = (float*)(a.ws + kWsHeaderBytes);
-    float* v = (float*)(a.ws + kWsHeaderBytes + gemv_part_bytes(a.D, a.d_in, B));
+    float* part = (float*)(a.ws);
+    float* v = (float*)(a.ws + gemv_part_bytes(a.D, a.d_in, B));
     if (a.D > 0) {
       hipError_t e = run_gemv(a.W, a.ld_w, a.D, a.d_in, B, 0, a.ec_col, nullptr, nullptr, a.S, part, v, st);
       if (e != hipSuccess) return e;
@@ -1251,13 +1251,13 @@ hipError_t launch_backward_dw(const DwArgs& a, hipStream_t st) {
 }
 
 // ---------------------------------------------------------- grouped calls ----
-// Workspace: header | group tables | dX: v band partials [bands(D) x G x N], v [G x N]
+// Workspace: group tables | dX: v band partials [bands(D) x G x N], v [G x N]
 //                                  | dW: u band partials [R/64 + G bands x N], u [G x N]
 struct GroupedBwLayout { size_t tables, part, vec, total; };
 
 GroupedBwLayout grouped_bw_layout(int64_t R, int64_t D, int64_t d_in, int64_t G, bool dx, bool ec) {
   GroupedBwLayout L{};
-  size_t off = kWsHeaderBytes;
+  size_t off = 0;
   L.tables = off; off = align_up(off + group_tables_bytes(G), 256);
   if (ec) {
     const int64_t bands = dx ? (D + kGvRows - 1) / kGvRows : R / kGvRows + G;

@@ -923,7 +923,7 @@ bool al(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 struct MxQuantWs { size_t rph, cph, rpt, cpt, total; };
 MxQuantWs mx_quant_ws(int64_t T, int64_t D, bool ec) {
   MxQuantWs w{};
-  size_t off = kWsHeaderBytes;
+  size_t off = 0;
   if (ec) {
     const size_t n_ct = (size_t)((D + kFusedCols - 1) / kFusedCols);
     w.rph = off; off = align_up(off + (size_t)T * n_ct * 4, 256);
@@ -979,7 +979,7 @@ template <typename TIn>
 hipError_t mx_operand_t(const MxOperandArgs& a, hipStream_t st) {
   MxQuant p{};
   p.R = a.R; p.C = a.C; p.S = a.S; p.ld = a.ld; p.mode = 0; p.D_index = a.C;
-  float* vsp = (float*)(a.ws + kWsHeaderBytes);
+  float* vsp = (float*)(a.ws);
   const dim3 gt((unsigned)(a.R / 128), (unsigned)((a.C + 63) / 64));
   if (a.colsum) {
     hipLaunchKernelGGL((mx_operand_kernel<TIn, true>), gt, dim3(256), 0, st, p, (const TIn*)a.M, a.Mt, a.ld_t, a.Mts,
@@ -1015,11 +1015,11 @@ MxGemm make_mx_gemm(const uint8_t* A, int64_t lda, const uint8_t* As, int64_t ld
 }  // namespace
 
 size_t mx_quant_workspace(int64_t T, int64_t D, int ec) { return mx_quant_ws(T, D, ec != 0).total; }
-size_t mx_operand_workspace(int64_t R, int64_t C) { return kWsHeaderBytes + align_up((size_t)(R / 32) * C * 4, 256); }
+size_t mx_operand_workspace(int64_t R, int64_t C) { return align_up((size_t)(R / 32) * C * 4, 256); }
 // Backward workspace: v [B x d_in] (dX) | coef [T] and u [d_in] (dW) | the GEMVs' chunk partials.
 size_t mx_backward_workspace(int64_t T, int64_t D, int64_t d_in, int64_t B) {
   const int64_t parts = max(((D + kRdChunk - 1) / kRdChunk) * 4, (T + kRdChunk - 1) / kRdChunk);
-  return kWsHeaderBytes + align_up((size_t)B * d_in * 4, 256) + align_up((size_t)T * 4, 256) +
+  return align_up((size_t)B * d_in * 4, 256) + align_up((size_t)T * 4, 256) +
          align_up((size_t)d_in * 4, 256) + align_up((size_t)parts * d_in * 4, 256);
 }
 
@@ -1040,7 +1040,7 @@ void run_rowdot(const MxBwArgs& a, int64_t N, int64_t K, int nb, const float* co
 
 float* mx_parts(const MxBwArgs& a) {
   const int64_t B = a.T / a.S;
-  return (float*)(a.ws + kWsHeaderBytes + align_up((size_t)B * a.d_in * 4, 256) + align_up((size_t)a.T * 4, 256) +
+  return (float*)(a.ws + align_up((size_t)B * a.d_in * 4, 256) + align_up((size_t)a.T * 4, 256) +
                   align_up((size_t)a.d_in * 4, 256));
 }
 }  // namespace
@@ -1059,7 +1059,7 @@ hipError_t launch_mx_backward_dx(const MxBwArgs& a, hipStream_t st) {
   MxEpi ep{};
   ep.S = a.S; ep.B = B; ep.out = a.out; ep.ld_out = a.ld_out;
   if (a.ec) {
-    float* v = (float*)(a.ws + kWsHeaderBytes);
+    float* v = (float*)(a.ws);
     // v_b[i] = sum_j ebar_b[j] dq(W)[j][i]: rows of the K-major Wt [d_in x D], four examples per pass
     for (int64_t b0 = 0; b0 < B; b0 += 4)
       run_rowdot<4>(a, a.d_in, a.K, (int)min((int64_t)4, B - b0), a.ec_col + b0 * a.K, v + b0 * a.d_in, mx_parts(a),
@@ -1077,8 +1077,8 @@ hipError_t launch_mx_backward_dw(const MxBwArgs& a, hipStream_t st) {
   MxEpi ep{};
   ep.S = a.S; ep.B = B; ep.out = a.out; ep.ld_out = a.ld_out;
   if (a.ec) {
-    float* coef = (float*)(a.ws + kWsHeaderBytes + align_up((size_t)B * a.d_in * 4, 256));
-    float* u = (float*)(a.ws + kWsHeaderBytes + align_up((size_t)B * a.d_in * 4, 256) + align_up((size_t)a.T * 4, 256));
+    float* coef = (float*)(a.ws + align_up((size_t)B * a.d_in * 4, 256));
+    float* u = (float*)(a.ws + align_up((size_t)B * a.d_in * 4, 256) + align_up((size_t)a.T * 4, 256));
     hipLaunchKernelGGL(mx_token_coef_kernel, dim3((unsigned)((a.T + 255) / 256)), dim3(256), 0, st, a.T, a.S,
                        a.ec_row, a.ec_mean, coef);
     // u[i] = sum_t (eps_t - mu_b) dq(X)[t][i]: rows of the K-major Xt [d_in x T]

@@ -22,7 +22,6 @@
 #include "s3r_internal.h"
 
 #include <algorithm>
-#include <cstdlib>
 #include <type_traits>
 
 namespace s3r {
@@ -609,378 +608,6 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(
   }
 }
 
-// ------------------------------------------------------- resident path ----
-// Per-tensor quantizer with ONE read of G from HBM.  One workgroup of 1024
-// threads per CU holds its band of R rows of G on chip (half in VGPRs, half
-// in LDS) from the amax pass to the code pass; a grid-wide exchange between
-// them publishes the tensor's amax.  A second exchange publishes the per-block
-// EC partials, which the same launch then reduces.
-// The grid never exceeds the device's CU count times the kernel's occupancy
-// (one workgroup per CU), so on an otherwise idle device every workgroup is
-// resident at once.  (A cooperative launch would guarantee it, but costs about
-// 18 us per call here.)  Every wait is bounded: if workgroups were not
-// co-resident (another kernel holding CUs throughout), the waves still exit,
-// S3R_FLAG_SYNC_TIMEOUT is raised and the outputs are invalid.
-// Shapes: bf16 G, D a power of two in [512, 8192] (a row is D/8 threads, 8
-// elements each), at most 16 chunks of 8 per thread.
-constexpr int kResThreads = 1024;
-constexpr int kResRegChunks = 8;
-constexpr int kResLdsChunks = 8;
-constexpr int kResMaxRows = 256;          // R <= 16 * (1024 / 64)
-constexpr int kResMaxBlocks = 1024;
-constexpr uint32_t kBarrierSpinLimit = 1u << 18;
-
-struct ResParams {
-  int64_t T, D, S, ld_g, ld_q;
-  int rows_per_block;   // R, a multiple of TR = 1024 / (D/8)
-  int tc_log2;          // log2(D/8): threads per row
-  int nk;               // chunks per thread, R / TR (<= 16)
-  int nblocks;
-  uint32_t layer; uint64_t seed;
-  uint32_t stream_word;
-  int bcast;
-};
-
-// Block-to-block exchange through per-block slots in the workspace header:
-// slots[b] = (phase << 32) | payload.  A call with generation g (a header word,
-// advanced by one per call) uses phases 2g+1 and 2g+2, so a slot left by an
-// earlier call never matches; a zero-filled header starts at g = 0.  Cross-block
-// data is written and read with agent-scope atomics, which bypass the per-XCD
-// L2s, so no cache write-back or invalidation is needed; a slot per block avoids
-// a contended counter.
-__device__ __forceinline__ void store_coherent64(unsigned long long* p, unsigned long long v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ unsigned long long load_coherent64(const unsigned long long* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Publishes this block's payload under `phase`, waits until every block has
-// published, and returns the maximum payload.  The wait is bounded: on timeout
-// it raises S3R_FLAG_SYNC_TIMEOUT and returns what it has.
-__device__ uint32_t exchange_max(unsigned long long* slots, uint32_t phase, uint32_t payload, int nblocks,
-                                 uint32_t* flags, uint32_t* s_vote) {
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  __builtin_amdgcn_s_waitcnt(0);     // this wave's stores have completed
-  __syncthreads();
-  if (tid == 0) store_coherent64(&slots[blockIdx.x], ((unsigned long long)phase << 32) | payload);
-  uint32_t mine = 0;
-  for (uint32_t spins = 0;; ++spins) {
-    bool ok = true;
-    if (tid < nblocks) {
-      const unsigned long long v = load_coherent64(&slots[tid]);
-      ok = (uint32_t)(v >> 32) == phase;
-      mine = (uint32_t)v;
-    }
-    const bool wave_ok = __all(ok);
-    if (lane == 0) s_vote[wave] = wave_ok;
-    __syncthreads();
-    bool done = true;
-#pragma unroll
-    for (int w = 0; w < kResThreads / kWave; ++w) done = done && s_vote[w];
-    __syncthreads();
-    if (done) break;
-    if (spins == kBarrierSpinLimit) {
-      if (tid == 0 && flags) atomicOr(flags, S3R_FLAG_SYNC_TIMEOUT);
-      break;
-    }
-    __builtin_amdgcn_s_sleep(2);
-  }
-  uint32_t m = wave_max_u32(mine);
-  if (lane == 0) s_vote[wave] = m;
-  __syncthreads();
-  m = s_vote[0];
-#pragma unroll
-  for (int w = 1; w < kResThreads / kWave; ++w) m = m > s_vote[w] ? m : s_vote[w];
-  __syncthreads();
-  return m;
-}
-
-__device__ __forceinline__ void store_coherent(float* p, float v) {
-  __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_coherent(const float* p) {
-  return __uint_as_float(__hip_atomic_load(reinterpret_cast<const uint32_t*>(p), __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT));
-}
-__device__ __forceinline__ void store_coherent(double* p, double v) {
-  __hip_atomic_store(reinterpret_cast<unsigned long long*>(p), (unsigned long long)__double_as_longlong(v),
-                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ double load_coherent(const double* p) {
-  return __longlong_as_double((long long)__hip_atomic_load(reinterpret_cast<const unsigned long long*>(p),
-                                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-}
-
-__device__ __forceinline__ void decode_bf16x8(const uint4& u, float v[8]) {
-  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    v[2 * i] = __uint_as_float(w[i] << 16);
-    v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-  }
-}
-
-template <int MODE, bool EC>
-__global__ __launch_bounds__(kResThreads, 1) void quantize_resident_kernel(
-    ResParams p, const uint16_t* __restrict__ G, const float* __restrict__ sx, const float* __restrict__ sw,
-    int8_t* __restrict__ Q, float* __restrict__ delta_out, uint32_t* __restrict__ flags, uint32_t* gen_word,
-    unsigned long long* slots, float* __restrict__ col_part, double* __restrict__ blk_sum, float* __restrict__ ec_row,
-    float* __restrict__ ec_col, float* __restrict__ ec_mean) {
-  __shared__ uint4 s_chunk[kResLdsChunks][kResThreads];        // 128 KB; reused for column sums
-  __shared__ int32_t s_thr[kResMaxRows];
-  __shared__ float s_fx[kResMaxRows];                           // s_x of the band's rows
-  __shared__ float s_rs[kResMaxRows][16];                      // row partials per wave of the row
-  __shared__ double s_eps[kResMaxRows];
-  __shared__ uint32_t s_red[kResThreads / kWave];
-  __shared__ uint32_t s_vote[kResThreads / kWave];
-
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  const int TC = 1 << p.tc_log2, TR = kResThreads >> p.tc_log2;
-  const int tr = tid >> p.tc_log2, tc = tid & (TC - 1);
-  const int wpr = TC / kWave, wir = tc / kWave;               // waves per row, wave index in the row
-  const int64_t j0 = (int64_t)tc * 8;
-  const int64_t r0 = (int64_t)blockIdx.x * p.rows_per_block;
-  const int R = p.rows_per_block;
-
-  const uint32_t gen = __hip_atomic_load(gen_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  float sw8[8];
-  load8_scale(sw, j0, p.D, true, sw8);
-
-  // ---- pass 1: load the band, amax of G'
-  // Every chunk slot issues its load (slots past the band re-read a valid row
-  // and are zeroed), so the slots stay in registers.
-  const int64_t t_any = min(r0 + tr, p.T - 1);
-  auto load_slot = [&](int k) -> uint4 {
-    const int64_t t = r0 + tr + (int64_t)k * TR;
-    const bool ok = k < p.nk && t < p.T;
-    const uint4 u = *reinterpret_cast<const uint4*>(G + (ok ? t : t_any) * p.ld_g + j0);
-    return ok ? u : make_uint4(0u, 0u, 0u, 0u);
-  };
-  uint4 rv[kResRegChunks];
-  uint32_t m = 0;
-  {
-    uint4 tmp[kResLdsChunks];
-#pragma unroll
-    for (int k = 0; k < kResLdsChunks; ++k) tmp[k] = load_slot(kResRegChunks + k);
-#pragma unroll
-    for (int k = 0; k < kResRegChunks; ++k) rv[k] = load_slot(k);
-    for (int i = tid; i < R; i += kResThreads) {
-      const bool ok = r0 + i < p.T;
-      s_fx[i] = (sx && ok) ? sx[r0 + i] : 1.f;
-      if constexpr (MODE == 2)
-        s_thr[i] = ok ? row_threshold_units24(r0 + i, p.layer, p.seed, p.bcast, p.S, p.stream_word) : 0;
-    }
-    __syncthreads();
-    auto amax_slot = [&](int k, const uint4& u) {
-      const float fx = s_fx[min(tr + k * TR, R - 1)];
-      float v[8];
-      decode_bf16x8(u, v);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t b = abs_bits((v[i] * fx) * sw8[i]);
-        m = m > b ? m : b;
-      }
-    };
-#pragma unroll
-    for (int k = 0; k < kResLdsChunks; ++k) {
-      s_chunk[k][tid] = tmp[k];
-      amax_slot(kResRegChunks + k, tmp[k]);
-    }
-#pragma unroll
-    for (int k = 0; k < kResRegChunks; ++k) amax_slot(k, rv[k]);
-  }
-  m = wave_max_u32(m);
-  if (lane == 0) s_red[wave] = m;
-  __syncthreads();
-  uint32_t bmax = s_red[0];
-#pragma unroll
-  for (int w = 1; w < kResThreads / kWave; ++w) bmax = bmax > s_red[w] ? bmax : s_red[w];
-  const uint32_t abits = exchange_max(slots, 2u * gen + 1u, bmax, p.nblocks, flags, s_vote);
-  // every block read `gen` before publishing above, so the next call's generation can be set now
-  if (blockIdx.x == 0 && tid == 0)
-    __hip_atomic_store(gen_word, gen + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-
-  // ---- pass 2: codes from the held band
-  const Step st = make_step(abits);
-  if (blockIdx.x == 0 && tid == 0) {
-    delta_out[0] = (abits > 0x7F800000u) ? __uint_as_float(abits) : st.delta;
-    if (st.flag && flags) atomicOr(flags, st.flag);
-  }
-  float col[8], rs[kResRegChunks + kResLdsChunks];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) col[i] = 0.f;
-#pragma unroll
-  for (int k = 0; k < kResRegChunks + kResLdsChunks; ++k) rs[k] = 0.f;
-
-  // One chunk of 8 codes.  FLAGGED (a non-finite or too small amax): zero codes
-  // and errors.  In EC mode every row of the band is valid (T % R == 0).
-  auto code_slot = [&](auto flagged, int k, const uint4& u) {
-    const int rl = tr + k * TR;                 // row within the band
-    const int64_t t = r0 + rl;
-    int q[8];
-    if constexpr (decltype(flagged)::value) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) q[i] = 0;
-    } else {
-      float v[8];
-      decode_bf16x8(u, v);
-      const float fx = s_fx[rl];
-      if constexpr (MODE == 0) {
-        float e = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float x = ((v[i] * fx) * sw8[i]) * st.inv;
-          const float r = fminf(fmaxf(__builtin_rintf(x), -127.f), 127.f);
-          q[i] = (int)r;
-        }
-        (void)e;
-      } else {
-        int32_t Rt[8];
-        if constexpr (MODE == 2) {
-          const int32_t rt = s_thr[rl];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) Rt[i] = rt;
-        } else {
-          const uint64_t blk = ((uint64_t)t * (uint64_t)p.D + (uint64_t)j0) >> 2;
-          const U4 w0 = philox4x32_10((uint32_t)blk, (uint32_t)(blk >> 32), p.layer, kTagSR + p.stream_word,
-                                      (uint32_t)p.seed, (uint32_t)(p.seed >> 32));
-          const U4 w1 = philox4x32_10((uint32_t)(blk + 1), (uint32_t)((blk + 1) >> 32), p.layer, kTagSR + p.stream_word,
-                                      (uint32_t)p.seed, (uint32_t)(p.seed >> 32));
-          Rt[0] = sr_units24(w0.x); Rt[1] = sr_units24(w0.y); Rt[2] = sr_units24(w0.z); Rt[3] = sr_units24(w0.w);
-          Rt[4] = sr_units24(w1.x); Rt[5] = sr_units24(w1.y); Rt[6] = sr_units24(w1.z); Rt[7] = sr_units24(w1.w);
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float x24 = ((v[i] * fx) * sw8[i]) * st.inv24;
-          int32_t X;
-          asm("v_cvt_flr_i32_f32 %0, %1" : "=v"(X) : "v"(x24));   // floor; x24 is finite here
-          X = min(max(X, -(127 << 24)), 127 << 24);
-          q[i] = (X + Rt[i]) >> 24;
-          if constexpr (EC) {
-            const float e = fmaf(x24, -0x1p-24f, (float)q[i]);
-            rs[k] += e;
-            col[i] += e;
-          }
-        }
-      }
-    }
-    if (t < p.T) {
-      uint2 w;
-      w.x = (uint32_t)(q[0] & 0xFF) | ((uint32_t)(q[1] & 0xFF) << 8) | ((uint32_t)(q[2] & 0xFF) << 16) |
-            ((uint32_t)q[3] << 24);
-      w.y = (uint32_t)(q[4] & 0xFF) | ((uint32_t)(q[5] & 0xFF) << 8) | ((uint32_t)(q[6] & 0xFF) << 16) |
-            ((uint32_t)q[7] << 24);
-      *reinterpret_cast<uint2*>(Q + t * p.ld_q + j0) = w;
-    }
-  };
-  auto all_slots = [&](auto flagged) {
-#pragma unroll
-    for (int k = 0; k < kResRegChunks; ++k)
-      if (k < p.nk) code_slot(flagged, k, rv[k]);
-#pragma unroll
-    for (int k = 0; k < kResLdsChunks; ++k)
-      if (kResRegChunks + k < p.nk) code_slot(flagged, kResRegChunks + k, s_chunk[k][tid]);
-  };
-  if (st.flag) all_slots(std::true_type{});
-  else all_slots(std::false_type{});
-  if constexpr (!EC) return;
-
-  // Row sums of the 16 chunk rows across the wave (a wave lies in one row of
-  // each chunk): a reduce-scatter, after which lane l holds row chunk l >> 2.
-  {
-    float r8[8], r4[4], r2[2], r1;
-    const bool hi32 = lane & 32, hi16 = lane & 16, hi8 = lane & 8, hi4 = lane & 4;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float send = hi32 ? rs[i] : rs[i + 8];
-      r8[i] = (hi32 ? rs[i + 8] : rs[i]) + __shfl_xor(send, 32, kWave);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float send = hi16 ? r8[i] : r8[i + 4];
-      r4[i] = (hi16 ? r8[i + 4] : r8[i]) + __shfl_xor(send, 16, kWave);
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const float send = hi8 ? r4[i] : r4[i + 2];
-      r2[i] = (hi8 ? r4[i + 2] : r4[i]) + __shfl_xor(send, 8, kWave);
-    }
-    {
-      const float send = hi4 ? r2[0] : r2[1];
-      r1 = (hi4 ? r2[1] : r2[0]) + __shfl_xor(send, 4, kWave);
-    }
-    r1 += __shfl_xor(r1, 2, kWave);
-    r1 += __shfl_xor(r1, 1, kWave);
-    const int k = lane >> 2;
-    if ((lane & 3) == 0 && k < p.nk) s_rs[tr + k * TR][wir] = r1;
-  }
-
-  // ---- EC partials of the band: token means, block sum of eps, column sums
-  __syncthreads();
-  const double dlt = (double)st.delta;
-  if (tid < R) {
-    double a = 0.0;
-    for (int w = 0; w < wpr; ++w) a += (double)s_rs[tid][w];
-    const double eps = a * dlt / (double)p.D;
-    s_eps[tid] = eps;
-    if (r0 + tid < p.T) ec_row[r0 + tid] = (float)eps;
-  }
-  float* s_colf = reinterpret_cast<float*>(&s_chunk[0][0]);     // [TR][D], at most 32 KB
-#pragma unroll
-  for (int i = 0; i < 8; ++i) s_colf[(int64_t)tr * p.D + j0 + i] = col[i];
-  __syncthreads();
-  for (int64_t j = tid; j < p.D; j += kResThreads) {
-    float a = s_colf[j];
-    for (int r = 1; r < TR; ++r) a += s_colf[(int64_t)r * p.D + j];
-    store_coherent(&col_part[(int64_t)blockIdx.x * p.D + j], a);
-  }
-  if (wave == 0) {
-    double a = 0.0;
-    for (int i = lane; i < R; i += kWave) a += s_eps[i];
-    a = wave_sum(a);
-    if (lane == 0) store_coherent(&blk_sum[blockIdx.x], a);
-  }
-  exchange_max(slots + kResMaxBlocks, 2u * gen + 2u, 0u, p.nblocks, flags, s_vote);
-
-  // ---- per-example channel means and grand means (every band lies in one example).
-  // tpi threads of one wave share an output: each sums every tpi-th band in
-  // order, then an xor butterfly (the same fixed order on every lane) adds them.
-  const int64_t B = p.T / p.S;
-  const int64_t bpe = p.S / R;                                  // bands per example
-  const int64_t items = B * p.D;
-  const int64_t gthreads = (int64_t)p.nblocks * kResThreads;
-  int tpi = 1;
-  while (tpi < kWave && (int64_t)tpi * 2 * items <= gthreads && tpi * 2 <= bpe) tpi *= 2;
-  const int sub = lane & (tpi - 1);
-  for (int64_t it = ((int64_t)blockIdx.x * kResThreads + tid) / tpi; it < items; it += gthreads / tpi) {
-    const int64_t b = it / p.D, j = it - b * p.D;
-    double acc = 0.0;
-    for (int64_t k = sub; k < bpe; k += 4 * tpi) {          // four loads in flight, summed in k order
-      float t[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int64_t kk = k + u * tpi;
-        const float v = load_coherent(&col_part[(b * bpe + min(kk, bpe - 1)) * p.D + j]);
-        t[u] = kk < bpe ? v : 0.f;
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) acc += (double)t[u];
-    }
-    for (int o = 1; o < tpi; o <<= 1) acc += __shfl_xor(acc, o, kWave);
-    if (sub == 0) ec_col[it] = (float)(acc * dlt / (double)p.S);
-  }
-  if (blockIdx.x == 0) {
-    for (int64_t b = wave; b < B; b += kResThreads / kWave) {
-      double acc = 0.0;
-      for (int64_t k = lane; k < bpe; k += kWave) acc += load_coherent(&blk_sum[b * bpe + k]);
-      acc = wave_sum(acc);
-      if (lane == 0) ec_mean[b] = (float)(acc / (double)p.S);
-    }
-  }
-}
-
 // --------------------------------------------------------- grouped path ----
 // Pass 1 of a grouped per-tensor quantizer: one block per (64-row tile of a
 // group, 512 columns), the tiling of the code pass; the block's max of |G'|
@@ -1179,7 +806,6 @@ __global__ void empty_kernel(int64_t T, int64_t D, int64_t B, int per_token, flo
 
 struct WsLayout {
   size_t amax_part, amax_rows, row_part, col_part, colq_part, blk_sum, counter, total;
-  size_t res_col, res_blk;   // resident path (shares the space of the regions above)
 };
 
 WsLayout ws_layout(int64_t T, int64_t D, int64_t S, int ec, int scale, bool colsum) {
@@ -1188,7 +814,7 @@ WsLayout ws_layout(int64_t T, int64_t D, int64_t S, int ec, int scale, bool cols
   const int64_t tpe = (S + kRowsPerTile - 1) / kRowsPerTile;
   const int64_t n_rt = B * tpe;
   const int64_t n_ct = (D + kColsPerTile - 1) / kColsPerTile;
-  size_t off = kWsHeaderBytes;
+  size_t off = 0;
   w.amax_part = off; off = align_up(off + (scale == S3R_PER_TENSOR ? kAmaxBlocks * 4 : 0), 256);
   w.amax_rows = off; off = align_up(off + (scale == S3R_PER_TOKEN ? (size_t)T * 4 : 0), 256);
   w.row_part = off;  off = align_up(off + (ec ? (size_t)T * n_ct * 4 : 0), 256);
@@ -1197,12 +823,7 @@ WsLayout ws_layout(int64_t T, int64_t D, int64_t S, int ec, int scale, bool cols
   const int64_t bpe = (S + kFinRows - 1) / kFinRows;
   w.blk_sum = off;   off = align_up(off + (ec ? (size_t)B * bpe * 8 : 0), 256);
   w.counter = off;   off = align_up(off + 4, 256);
-  // resident path: sync words, [blocks x D] column partials, [blocks] eps sums
-  size_t r = kWsHeaderBytes;
-  const int64_t nb = std::min<int64_t>(T, kResMaxBlocks);
-  w.res_col = r;  r = align_up(r + (scale == S3R_PER_TENSOR && ec ? (size_t)nb * D * 4 : 0), 256);
-  w.res_blk = r;  r = align_up(r + (scale == S3R_PER_TENSOR && ec ? (size_t)nb * 8 : 0), 256);
-  w.total = std::max(off, r);
+  w.total = off;
   return w;
 }
 
@@ -1275,82 +896,13 @@ void run_quantize(const QuantArgs& a, const WsLayout& L, hipStream_t st) {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-// S3R_QUANTIZE_TWO_PASS=1 in the environment forces the two-pass kernels (both
-// paths give identical codes; the switch exists to compare them).
-bool resident_disabled() {
-  const char* v = getenv("S3R_QUANTIZE_TWO_PASS");
-  return v && v[0] == '1';
-}
-
-// Co-resident workgroups of the resident kernel on the current device (0: path unavailable).
-int resident_capacity() {
-  static int cap[64];
-  static bool known[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (!known[dev]) {
-    int ncu = 0, occ = 0;
-    if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) ncu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, quantize_resident_kernel<2, true>, kResThreads, 0) !=
-        hipSuccess)
-      occ = 0;
-    cap[dev] = std::min(ncu * std::min(occ, 1), kResMaxBlocks);
-    known[dev] = true;
-  }
-  return cap[dev];
-}
-
-// Band height R for the resident path, or 0 if the shape does not qualify.
-int resident_rows(const QuantArgs& a, int capacity) {
-  if (capacity <= 0 || a.g_dtype != S3R_BF16 || a.scale != S3R_PER_TENSOR || a.code_colsum) return 0;
-  if (a.D < 512 || a.D > 8192 || (a.D & (a.D - 1))) return 0;
-  const int64_t TC = a.D / 8, TR = kResThreads / TC;
-  for (int64_t nk = 1; nk <= kResRegChunks + kResLdsChunks; ++nk) {
-    const int64_t R = nk * TR;
-    if (a.ec && a.S % R) continue;
-    if ((a.T + R - 1) / R <= capacity) return (int)R;
-  }
-  return 0;
-}
-
-template <int MODE, bool EC>
-hipError_t launch_resident(const QuantArgs& a, const WsLayout& L, int R, hipStream_t st) {
-  ResParams p;
-  p.T = a.T; p.D = a.D; p.S = a.S; p.ld_g = a.ld_g; p.ld_q = a.ld_q;
-  p.rows_per_block = R;
-  p.tc_log2 = 0;
-  while ((int64_t(1) << p.tc_log2) < a.D / 8) ++p.tc_log2;
-  p.nk = (int)(R / (kResThreads >> p.tc_log2));
-  p.nblocks = (int)((a.T + R - 1) / R);
-  p.layer = a.layer; p.seed = a.seed;
-  p.stream_word = a.stream << 16;
-  p.bcast = a.mode == S3R_S3R_BCAST;
-  uint32_t* gen_word = (uint32_t*)(a.ws + kWsGenOffset);
-  unsigned long long* slots = (unsigned long long*)(a.ws + kWsSlotOffset);
-  const uint16_t* G = (const uint16_t*)a.G;
-  float* col = (float*)(a.ws + L.res_col);
-  double* blk = (double*)(a.ws + L.res_blk);
-  void* args[] = {&p, (void*)&G, (void*)&a.sx, (void*)&a.sw, (void*)&a.Q, (void*)&a.delta, (void*)&a.flags,
-                  &gen_word, &slots, &col, &blk, (void*)&a.ec_row, (void*)&a.ec_col, (void*)&a.ec_mean};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&quantize_resident_kernel<MODE, EC>),
-                         dim3((unsigned)p.nblocks), dim3(kResThreads), args, 0, st);
-}
-
-hipError_t run_resident(const QuantArgs& a, const WsLayout& L, int R, hipStream_t st) {
-  switch (a.mode) {
-    case S3R_RTNE: return launch_resident<0, false>(a, L, R, st);
-    case S3R_SR: return launch_resident<1, false>(a, L, R, st);
-    default: return a.ec ? launch_resident<2, true>(a, L, R, st) : launch_resident<2, false>(a, L, R, st);
-  }
-}
-
 struct GroupedWs { size_t tables, counter, amax_rows, row_part, col_part, colq_part, total; };
 
 GroupedWs grouped_ws(int64_t R, int64_t D, int64_t Gn, int ec, int scale, bool colsum) {
   GroupedWs w{};
   const int64_t n_rt = R / kRowsPerTile + Gn;                 // bound on the groups' 64-row tiles
   const int64_t n_ct = (D + kColsPerTile - 1) / kColsPerTile;
-  size_t off = kWsHeaderBytes;
+  size_t off = 0;
   w.tables = off;    off = align_up(off + group_tables_bytes(Gn), 256);
   w.counter = off;   off = align_up(off + 4, 256);
   w.amax_rows = off; off = align_up(off + (scale == S3R_PER_TOKEN ? (size_t)R * 4 : 0), 256);
@@ -1468,10 +1020,6 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t st) {
   const size_t es = a.g_dtype == S3R_BF16 ? 2 : 4;
   const bool vec = aligned(a.G, 16) && (a.ld_g * (int64_t)es) % 16 == 0 && aligned(a.Q, 8) && a.ld_q % 8 == 0 &&
                    (a.sw == nullptr || aligned(a.sw, 16));
-  if (vec && !a.amax_in && !resident_disabled()) {
-    const int R = resident_rows(a, resident_capacity());
-    if (R > 0) return run_resident(a, L, R, st);
-  }
   if (a.g_dtype == S3R_BF16) {
     if (vec) run_quantize<uint16_t, true>(a, L, st);
     else run_quantize<uint16_t, false>(a, L, st);

@@ -243,14 +243,4 @@ __device__ __forceinline__ GroupHit find_group_wave(const int32_t* __restrict__ 
   return h;
 }
 
-// Every workspace starts with a header of synchronization words shared by all
-// entry points (so one buffer may serve quantize and backward calls that do not
-// overlap in time).  The caller zero-fills a workspace once before its first
-// use; every completed call leaves the header valid for the next one.
-constexpr size_t kWsHeaderBytes = 65536;
-constexpr size_t kWsGenOffset = 0;           // uint32: single-pass quantizer call generation
-constexpr size_t kWsSlotOffset = 256;        // 2 x 1024 uint64: single-pass quantizer exchange slots
-constexpr size_t kWsCounterOffset = 32768;   // 8192 uint32: GEMV column-block arrival counters
-constexpr int kWsMaxCounters = 8192;
-
 }  // namespace s3r

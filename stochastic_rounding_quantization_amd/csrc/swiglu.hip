@@ -216,14 +216,14 @@ int64_t amax_blocks(int64_t T, int64_t F) {
 }  // namespace
 
 size_t swiglu_amax_workspace(int64_t T, int64_t F) {
-  return kWsHeaderBytes + align_up((size_t)std::max<int64_t>(amax_blocks(T, F), 1) * 2 * 4, 256);
+  return align_up((size_t)std::max<int64_t>(amax_blocks(T, F), 1) * 2 * 4, 256);
 }
 
 hipError_t launch_swiglu_backward_amax(int64_t T, int64_t F, const float* dH, int64_t ld_dh, const uint16_t* Ag,
                                        const uint16_t* Au, int64_t ld_a, uint16_t* Gg, uint16_t* Gu, int64_t ld_g,
                                        const float* sx, const float* swg, const float* swu, uint32_t* amax_bits,
                                        char* ws, hipStream_t st) {
-  uint32_t* part = (uint32_t*)(ws + kWsHeaderBytes);
+  uint32_t* part = (uint32_t*)(ws);
   const int64_t nblk = amax_blocks(T, F);
   if (nblk > 0) {
     const bool vec = aligned16(dH) && aligned16(Ag) && aligned16(Au) && aligned16(Gg) && aligned16(Gu) &&

@@ -25,7 +25,7 @@ S3R_F32, S3R_BF16, S3R_I32_RAW, S3R_F32_ACC = 0, 1, 2, 3
 RTNE, SR, S3R, S3R_BCAST = 0, 1, 2, 3
 EC_NONE, EC_DX_ONLY, EC_TWO_WAY, EC_DW_ONLY = 0, 1, 2, 3
 PER_TENSOR, PER_TOKEN = 0, 1
-FLAG_NONFINITE, FLAG_TINY_STEP, FLAG_SYNC_TIMEOUT, FLAG_BAD_GROUPS = 1, 2, 4, 8
+FLAG_NONFINITE, FLAG_TINY_STEP, FLAG_BAD_GROUPS = 1, 2, 8
 
 EXPORTED = ["s3r_quantize_workspace", "s3r_quantize", "s3r_quantize_with_amax", "s3r_backward_dx",
             "s3r_backward_dw", "s3r_backward_workspace", "s3r_swiglu_backward", "s3r_swiglu_amax_workspace",

@@ -131,14 +131,13 @@ def test_quantize_bit_exact(T, D, S, dtype, scale):
             assert np.abs(host(q.ec_mean) - mu).max() <= TOL * np.abs(E).max(), tag
 
 
-# Shapes the single-pass (resident) quantizer takes: bf16, per-tensor, D a power of two in
-# [512, 8192].  (T, D, S): the benchmark shape; a band of one row per block; one chunk per
-# thread; a ragged last band (no EC: S has no suitable divisor); EC falls back to two passes.
+# Per-tensor bf16 shapes: the benchmark's down projection; 1000-row and 96-row tensors whose rows do
+# not fill the 64-row tiles evenly; a ragged T = 4097 with one 4097-token example; a 300-row tensor.
 RCASES = [(8192, 4096, 2048), (1000, 8192, 1000), (96, 1024, 32), (4097, 2048, 4097), (300, 512, 300)]
 
 
 @pytest.mark.parametrize("T,D,S", RCASES)
-def test_quantize_single_pass_matches_oracle(T, D, S, monkeypatch):
+def test_quantize_bf16_per_tensor_matches_oracle(T, D, S):
     store, sx, sw = _grad(T, D, "bf16", T * 7 + D)
     if T == 96:
         store[5, 7] = 0x7FC0          # a NaN: flags, zero codes, NaN step
@@ -147,25 +146,23 @@ def test_quantize_single_pass_matches_oracle(T, D, S, monkeypatch):
     for mode, ec in MODES:
         ref = oq.quantize(store, "bf16", mode=mode, scale=s3r.PER_TENSOR, row_scale=sx, col_scale=sw, seed=77,
                           layer_id=5, rows_per_example=S)
-        for two_pass in ("0", "1"):
-            monkeypatch.setenv("S3R_QUANTIZE_TWO_PASS", two_pass)
-            q = s3r.quantize(G, mode=mode, ec=ec, row_scale=sx_d, col_scale=sw_d, seed=77, layer_id=5,
-                             rows_per_example=S)
-            torch.cuda.synchronize()
-            tag = f"T={T} D={D} S={S} mode={mode} ec={ec} two_pass={two_pass}"
-            np.testing.assert_array_equal(host(q.Q), ref["Q"], err_msg=tag)
-            assert_nan_equal(host(q.delta), ref["delta"], tag)
-            assert int(host(q.flags)[0]) == ref["flags"], tag
-            if ec != s3r.EC_NONE and not ref["flags"]:
-                from oracle import ec as oec
-                E = oec.rounding_error(ref["Q"], ref["x"], ref["delta"])
-                eps, ebar, mu = oec.statistics(E, S)
-                assert rel_err(host(q.ec_row), eps) <= TOL, tag
-                assert rel_err(host(q.ec_col), ebar) <= TOL, tag
-                assert np.abs(host(q.ec_mean) - mu).max() <= TOL * np.abs(E).max(), tag
+        q = s3r.quantize(G, mode=mode, ec=ec, row_scale=sx_d, col_scale=sw_d, seed=77, layer_id=5,
+                         rows_per_example=S)
+        torch.cuda.synchronize()
+        tag = f"T={T} D={D} S={S} mode={mode} ec={ec}"
+        np.testing.assert_array_equal(host(q.Q), ref["Q"], err_msg=tag)
+        assert_nan_equal(host(q.delta), ref["delta"], tag)
+        assert int(host(q.flags)[0]) == ref["flags"], tag
+        if ec != s3r.EC_NONE and not ref["flags"]:
+            from oracle import ec as oec
+            E = oec.rounding_error(ref["Q"], ref["x"], ref["delta"])
+            eps, ebar, mu = oec.statistics(E, S)
+            assert rel_err(host(q.ec_row), eps) <= TOL, tag
+            assert rel_err(host(q.ec_col), ebar) <= TOL, tag
+            assert np.abs(host(q.ec_mean) - mu).max() <= TOL * np.abs(E).max(), tag
 
 
-def test_quantize_single_pass_zero_tensor():
+def test_quantize_zero_tensor():
     G = torch.zeros(64, 512, dtype=torch.bfloat16, device=DEV)
     q = s3r.quantize(G, mode=s3r.S3R, ec=s3r.EC_TWO_WAY, rows_per_example=64)
     torch.cuda.synchronize()
@@ -395,7 +392,7 @@ def test_down_8192x14336x4096_bf16_per_token_sampled():
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_quantize_with_amax_equals_quantize(mode, ec, dtype):
     # with the amax supplied (here the oracle's), one pass over G gives the oracle's codes, step and
-    # statistics; a shape that would otherwise take the single-pass resident kernel
+    # statistics
     T, D, S = 1024, 2048, 256
     w = inputs.WORKLOADS["down-4096x11008x4096-bf16"].scaled(T, 64, D, rows_per_example=S)
     inp = inputs.make_linear_inputs(w)
@@ -431,8 +428,7 @@ def test_quantize_with_amax_equals_quantize(mode, ec, dtype):
                                      (s3r.S3R_BCAST, s3r.EC_DW_ONLY)])
 def test_ablation_configurations(mode, ec):
     # Phi_bcast (one threshold per example) and the dW-only correction: codes bit-exact, dX / dW
-    # within the tolerance; three examples with ragged shapes; both quantizer paths (a D that
-    # qualifies for the single-pass kernel, and one that does not)
+    # within the tolerance; three examples with ragged shapes, and a power-of-two D
     for (T, d_in, D, S) in ((384, 300, 700, 128), (1024, 96, 512, 256)):
         w = inputs.WORKLOADS["down-4096x11008x4096-bf16"].scaled(T, d_in, D, rows_per_example=S)
         inp = inputs.make_linear_inputs(w)

@@ -138,9 +138,10 @@ def test_swiglu_amax_and_quantize_with_amax_argument_errors(L):
 
     assert glue(T=-1) == -1 and glue(ldg=8) == -1 and glue(dH=None) == -1
     assert glue(amax=None) == -1                     # the amax output is required
-    assert glue(wsb=1024) == -3                      # workspace below s3r_swiglu_amax_workspace
+    need = s3r.s3r_swiglu_amax_workspace(4, 16)
+    assert need > 0 and glue(wsb=need - 1) == -3     # workspace below s3r_swiglu_amax_workspace
     assert glue(ws=P(4100)) == -1                    # workspace not 256-byte aligned
-    assert s3r.s3r_swiglu_amax_workspace(8192, 14336) > 65536
+    assert s3r.s3r_swiglu_amax_workspace(8192, 14336) > need
 
     def qa(desc, amax=P(64), G=P(1), Q=P(1), delta=P(1), ec=(None, None, None), wsb=0, ws=None):
         return L.s3r_quantize_with_amax(ctypes.byref(desc), G, 0, desc.cols, None, None, amax, Q, desc.cols, delta,
