@@ -167,6 +167,34 @@ int s3r_quantize_with_amax(const s3r_qdesc* desc,
                            uint32_t* flags,
                            void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* s3r_quantize_noalloc: s3r_quantize without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  Same arguments, checks,
+ * kernels and results as s3r_quantize; the partial results live in one
+ * library-owned device array of S3R_NOALLOC_SCRATCH_BYTES on each device the
+ * library runs on, held until the process ends.  The call allocates nothing:
+ * no hipMalloc, no hipFree, no allocating library routine.  The first call on
+ * a device looks up that device's array address (hipGetSymbolAddress).
+ *   Size limit: a call whose partials exceed S3R_NOALLOC_SCRATCH_BYTES (the
+ *   workspace s3r_quantize would need, counting the code column sums only
+ *   when code_colsum is not NULL) returns S3R_ERR_WORKSPACE and enqueues
+ *   nothing.  32 MiB covers, with EC, T = 8192 tokens up to D = 14336 with
+ *   code column sums, and larger T at smaller D.
+ *   Concurrency: every call on one device shares its array, so calls that
+ *   overlap in time on one device (different streams, or other threads'
+ *   streams) race and give undefined results.  Calls in one stream's order
+ *   are safe: nothing in the array has to start at zero, and no call depends
+ *   on what an earlier call left there.
+ */
+#define S3R_NOALLOC_SCRATCH_BYTES (32u << 20)
+int s3r_quantize_noalloc(const s3r_qdesc* desc,
+                         const void* G, int32_t g_dtype, int64_t ld_g,
+                         const float* row_scale, const float* col_scale,
+                         int8_t* Q, int64_t ld_q, float* delta,
+                         int32_t* code_colsum,
+                         float* ec_row, float* ec_col, float* ec_mean,
+                         uint32_t* flags, hipStream_t stream);
+
 /* ---- backward GEMMs ----------------------------------------------------
  * Common: Q [T x D] int8 codes with ld_q, delta as written by s3r_quantize
  * (desc->scale selects [1] or [T]).  INT8 GEMMs on the MFMA units with int32

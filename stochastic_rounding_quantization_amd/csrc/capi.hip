@@ -52,19 +52,11 @@ bool dw_corrected(int ec) { return ec == S3R_EC_TWO_WAY || ec == S3R_EC_DW_ONLY;
 
 int finish(hipError_t e) { return e == hipSuccess ? S3R_OK : S3R_ERR_HIP; }
 
-}  // namespace
-
-extern "C" {
-
-size_t s3r_quantize_workspace(const s3r_qdesc* d) {
-  if (check_desc(d) != S3R_OK) return 0;
-  return quant_workspace(d->rows, d->cols, d->rows_per_example, d->ec != S3R_EC_NONE, d->scale, true);
-}
-
-int s3r_quantize(const s3r_qdesc* d, const void* G, int32_t g_dtype, int64_t ld_g, const float* row_scale,
-                 const float* col_scale, int8_t* Q, int64_t ld_q, float* delta, int32_t* code_colsum,
-                 float* ec_row, float* ec_col, float* ec_mean, uint32_t* flags, void* ws, size_t ws_bytes,
-                 hipStream_t stream) {
+// s3r_quantize's checks and launch, for a workspace of ws_bytes of which the call needs `need`.
+int quantize_checked(const s3r_qdesc* d, const void* G, int32_t g_dtype, int64_t ld_g, const float* row_scale,
+                     const float* col_scale, int8_t* Q, int64_t ld_q, float* delta, int32_t* code_colsum,
+                     float* ec_row, float* ec_col, float* ec_mean, uint32_t* flags, void* ws, size_t ws_bytes,
+                     size_t need, hipStream_t stream) {
   int rc = check_desc(d);
   if (rc) return rc;
   if (g_dtype != S3R_F32 && g_dtype != S3R_BF16) return S3R_ERR_UNSUPPORTED;
@@ -81,7 +73,6 @@ int s3r_quantize(const s3r_qdesc* d, const void* G, int32_t g_dtype, int64_t ld_
   } else if (ec_row || ec_col || ec_mean) {
     return S3R_ERR_INVALID_ARG;
   }
-  const size_t need = s3r_quantize_workspace(d);
   if (ws_bytes < need) return S3R_ERR_WORKSPACE;
   if (need > 0 && (!ws || ((uintptr_t)ws & 255u))) return S3R_ERR_INVALID_ARG;
   if ((rc = check_arch())) return rc;
@@ -94,6 +85,62 @@ int s3r_quantize(const s3r_qdesc* d, const void* G, int32_t g_dtype, int64_t ld_
   a.stream = d->stream;
   a.ws = (char*)ws;
   return finish(launch_quantize(a, stream));
+}
+
+// Scratch of s3r_quantize_noalloc, for callers that cannot allocate: one array on every device the library
+// runs on, kept until the process ends.  Its host-side name is not a device address: host code uses only
+// the address hipGetSymbolAddress returns for the current device, taken once per device.  Every call on a
+// device shares that device's array; the quantize kernels write every partial they read (the finalize
+// counter is reset by the code pass), so nothing in it has to start at zero.
+__device__ __align__(256) uint8_t scratch[S3R_NOALLOC_SCRATCH_BYTES];
+
+int scratch_address(void** out) {
+  static std::mutex mu;
+  static void* addr[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return S3R_ERR_HIP;
+  if (dev < 0 || dev >= 64) return S3R_ERR_ARCH;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return S3R_ERR_HIP;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return S3R_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t s3r_quantize_workspace(const s3r_qdesc* d) {
+  if (check_desc(d) != S3R_OK) return 0;
+  return quant_workspace(d->rows, d->cols, d->rows_per_example, d->ec != S3R_EC_NONE, d->scale, true);
+}
+
+int s3r_quantize(const s3r_qdesc* d, const void* G, int32_t g_dtype, int64_t ld_g, const float* row_scale,
+                 const float* col_scale, int8_t* Q, int64_t ld_q, float* delta, int32_t* code_colsum,
+                 float* ec_row, float* ec_col, float* ec_mean, uint32_t* flags, void* ws, size_t ws_bytes,
+                 hipStream_t stream) {
+  return quantize_checked(d, G, g_dtype, ld_g, row_scale, col_scale, Q, ld_q, delta, code_colsum, ec_row, ec_col,
+                          ec_mean, flags, ws, ws_bytes, s3r_quantize_workspace(d), stream);
+}
+
+int s3r_quantize_noalloc(const s3r_qdesc* d, const void* G, int32_t g_dtype, int64_t ld_g, const float* row_scale,
+                         const float* col_scale, int8_t* Q, int64_t ld_q, float* delta, int32_t* code_colsum,
+                         float* ec_row, float* ec_col, float* ec_mean, uint32_t* flags, hipStream_t stream) {
+  int rc = check_desc(d);
+  if (rc) return rc;
+  // the scratch this call needs (its code column sums only if asked for), against the array's size
+  const size_t need = quant_workspace(d->rows, d->cols, d->rows_per_example, d->ec != S3R_EC_NONE, d->scale,
+                                      code_colsum != nullptr);
+  if (need > (size_t)S3R_NOALLOC_SCRATCH_BYTES) return S3R_ERR_WORKSPACE;
+  if ((rc = check_arch())) return rc;
+  void* ws = nullptr;
+  if ((rc = scratch_address(&ws))) return rc;
+  return quantize_checked(d, G, g_dtype, ld_g, row_scale, col_scale, Q, ld_q, delta, code_colsum, ec_row, ec_col,
+                          ec_mean, flags, ws, S3R_NOALLOC_SCRATCH_BYTES, need, stream);
 }
 
 int s3r_quantize_with_amax(const s3r_qdesc* d, const void* G, int32_t g_dtype, int64_t ld_g, const float* row_scale,

@@ -26,8 +26,9 @@ RTNE, SR, S3R, S3R_BCAST = 0, 1, 2, 3
 EC_NONE, EC_DX_ONLY, EC_TWO_WAY, EC_DW_ONLY = 0, 1, 2, 3
 PER_TENSOR, PER_TOKEN = 0, 1
 FLAG_NONFINITE, FLAG_TINY_STEP, FLAG_BAD_GROUPS = 1, 2, 8
+S3R_NOALLOC_SCRATCH_BYTES = 32 << 20    # include/s3r.h: the no-alloc quantizer's device array
 
-EXPORTED = ["s3r_quantize_workspace", "s3r_quantize", "s3r_quantize_with_amax", "s3r_backward_dx",
+EXPORTED = ["s3r_quantize_workspace", "s3r_quantize", "s3r_quantize_with_amax", "s3r_quantize_noalloc", "s3r_backward_dx",
             "s3r_backward_dw", "s3r_backward_workspace", "s3r_swiglu_backward", "s3r_swiglu_amax_workspace",
             "s3r_swiglu_backward_amax", "s3r_grouped_workspace", "s3r_grouped_quantize",
             "s3r_grouped_backward_dx", "s3r_grouped_backward_dw", "s3r_mx_workspace", "s3r_mx_operand_workspace",
@@ -73,6 +74,8 @@ def lib() -> ctypes.CDLL:
     L.s3r_quantize.restype = ctypes.c_int
     L.s3r_quantize_with_amax.argtypes = [DP, P, I32, I64, P, P, P, P, I64, P, P, P, P, P, P, SZ, P]
     L.s3r_quantize_with_amax.restype = ctypes.c_int
+    L.s3r_quantize_noalloc.argtypes = [DP, P, I32, I64, P, P, P, I64, P, P, P, P, P, P, P]
+    L.s3r_quantize_noalloc.restype = ctypes.c_int
     L.s3r_backward_dx.argtypes = [DP, P, I64, P, P, I64, I64, P, P, P, P, P, P, I32, I64, P, SZ, P]
     L.s3r_backward_dx.restype = ctypes.c_int
     L.s3r_backward_dw.argtypes = [DP, P, I64, P, P, I64, I64, P, P, P, P, P, P, I32, I64, P, SZ, P]
@@ -171,6 +174,17 @@ def s3r_quantize(desc: QDesc, G, row_scale, col_scale, Q, delta, code_colsum=Non
     if rc_only:
         return rc
     _check("s3r_quantize", rc)
+
+
+def s3r_quantize_noalloc(desc: QDesc, G, row_scale, col_scale, Q, delta, code_colsum=None, ec_row=None, ec_col=None,
+                         ec_mean=None, flags=None, stream=None, *, rc_only=False):
+    rc = lib().s3r_quantize_noalloc(ctypes.byref(desc), _ptr(G), _gdtype(G) if G is not None else S3R_F32,
+                                    _ld(G, desc.cols), _ptr(row_scale), _ptr(col_scale), _ptr(Q), _ld(Q, desc.cols),
+                                    _ptr(delta), _ptr(code_colsum), _ptr(ec_row), _ptr(ec_col), _ptr(ec_mean),
+                                    _ptr(flags), _stream(stream))
+    if rc_only:
+        return rc
+    _check("s3r_quantize_noalloc", rc)
 
 
 def s3r_quantize_with_amax(desc: QDesc, G, row_scale, col_scale, amax_bits, Q, delta, ec_row=None, ec_col=None,

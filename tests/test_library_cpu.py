@@ -330,3 +330,25 @@ def test_gemm_m0_written_only_by_its_dma_assembly(tmp_path):
             stray.append(line.strip())
     assert dma_blocks > 0
     assert not stray, stray[:5]
+
+
+def test_quantize_noalloc_size_limit(L):
+    # the no-alloc quantizer refuses, before touching the device, a call whose partials exceed its
+    # array: with EC the column partials of 2^20 tokens x 4096 channels need 1 GiB
+    P = ctypes.c_void_p
+    assert s3r.S3R_NOALLOC_SCRATCH_BYTES == 32 << 20
+
+    def call(T, D, S, ec, colsum=None):
+        d = s3r.qdesc(T, D, S, s3r.S3R, ec)
+        ecp = (P(1024), P(2048), P(4096)) if ec else (None, None, None)
+        return L.s3r_quantize_noalloc(ctypes.byref(d), P(256), s3r.S3R_BF16, D, None, None, P(512), D, P(768),
+                                      colsum, *ecp, None, None)
+
+    assert call(1 << 20, 4096, 1 << 20, s3r.EC_TWO_WAY) == -3
+    # within the limit the size check passes; without a GPU the call then stops at the device checks
+    assert call(8192, 4096, 2048, s3r.EC_TWO_WAY) in (-4, -5)
+    assert call(8192, 14336, 2048, s3r.EC_TWO_WAY, colsum=P(8192)) in (-4, -5)
+    # argument errors are still reported as for s3r_quantize
+    d = s3r.qdesc(64, 96, 31, s3r.S3R, s3r.EC_NONE)
+    assert L.s3r_quantize_noalloc(ctypes.byref(d), P(256), 1, 96, None, None, P(512), 96, P(768), None, None, None,
+                                  None, None, None) == -1
