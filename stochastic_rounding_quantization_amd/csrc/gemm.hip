@@ -478,7 +478,10 @@ __device__ __forceinline__ void epilogue(const GemmParams& g, const EpiParams& e
   // rowf: per-row factors; roweb (dW): ebar[b][row] / s_w[row]
   const int lane_row = wm * 128 + (lane >> 5) * 4;                  // + i*32 + row_in_block(r)
 
-  // per-column values of this lane, one per column block j
+  // per-column values of this lane, one per column block j.  Every lane loads from a valid
+  // column (its own, or column 0 past N, whose value is then discarded), outside any branch,
+  // and waits for the loads once here: a load still pending inside the store loop would make
+  // each group of stores wait for every store before it (vmcnt counts stores too).
   float colA[4], colV[4], colB[NB][4], colS[4];
   bool n_ok[4];
   uint32_t voff[4];
@@ -486,38 +489,43 @@ __device__ __forceinline__ void epilogue(const GemmParams& g, const EpiParams& e
   for (int j = 0; j < 4; ++j) {
     const int64_t n = n0 + wn * 128 + j * 32 + (lane & 31);
     n_ok[j] = n < g.N;
+    const int64_t nc = n_ok[j] ? n : 0;
     voff[j] = (uint32_t)(lane_row * ld4 + n * esz);
     colA[j] = 0.f; colV[j] = 0.f; colS[j] = 1.f;
 #pragma unroll
     for (int b = 0; b < NB; ++b) colB[b][j] = 0.f;
-    if constexpr (EPI == EPI_DWC) colS[j] = n_ok[j] ? ep.colstep[n] : 1.f;
-    if (EC && n_ok[j]) {
-      if constexpr (is_dx(EPI)) {
-        colA[j] = (float)ep.colsum[n];                                   // r_W[n]
-        if constexpr (!GATHER) colV[j] = ep.vec[(m0 / ep.S) * g.N + n];  // v_b[n], the tile's example
-      } else if constexpr (is_dw(EPI)) {
-        colA[j] = ep.u[n];
+    if constexpr (EPI == EPI_DWC) colS[j] = ep.colstep[nc];
+    if constexpr (EC && is_dx(EPI)) {
+      colA[j] = (float)ep.colsum[nc];                                    // r_W[n]
+      if constexpr (!GATHER) colV[j] = ep.vec[(m0 / ep.S) * g.N + nc];   // v_b[n], the tile's example
+    } else if constexpr (EC && is_dw(EPI)) {
+      colA[j] = ep.u[nc];
 #pragma unroll
-        for (int b = 0; b < NB; ++b)
-          if (b < ep.B) colB[b][j] = (float)ep.colsum[b * g.N + n];     // xs_b[n]
-      }
+      for (int b = 0; b < NB; ++b)                                       // xs_b[n]; slots past B hold 0
+        colB[b][j] = (float)ep.colsum[(b < ep.B ? b : 0) * g.N + nc] * (b < ep.B ? 1.f : 0.f);
     }
   }
+  S3R_WAIT_VM(0);
 
+  // EPI_DXA: the current output values of a block-row, loaded one block-row ahead: the loads of
+  // block-row i+1 are issued before the stores of block-row i, so waiting for them does not wait
+  // for those stores (vmcnt counts loads and stores in issue order)
+  float old[2][4][4][4];
+  auto load_old = [&](int i, float (&dst)[4][4][4]) {
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+          dst[rq][j][rr] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+              ro, voff[j], (uint32_t)(i * 32 + rq * 8 + rr) * ld4, 0));
+  };
+  if constexpr (EPI == EPI_DXA) load_old(0, old[0]);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    // EPI_DXA: this block-row's current output values, all loads issued before any is used
-    float old[4][4][4];
-    if constexpr (EPI == EPI_DXA) {
-#pragma unroll
-      for (int rq = 0; rq < 4; ++rq)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr)
-            old[rq][j][rr] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-                ro, voff[j], (uint32_t)(i * 32 + rq * 8 + rr) * ld4, 0));
-    }
+    if constexpr (EPI == EPI_DXA)
+      if (i + 1 < 4) load_old(i + 1, old[(i + 1) & 1]);
 #pragma unroll
     for (int rq = 0; rq < 4; ++rq) {
       // four consecutive rows of this lane: lr = lane_row + i*32 + rq*8 + rr
@@ -559,7 +567,7 @@ __device__ __forceinline__ void epilogue(const GemmParams& g, const EpiParams& e
             }
             const float scale = EPI == EPI_DWC ? f[rr].x * colS[j] : f[rr].x;
             float o = fmaf(scale, (float)v, -corr);
-            if constexpr (EPI == EPI_DXA) o = old[rq][j][rr] + o;
+            if constexpr (EPI == EPI_DXA) o = old[i & 1][rq][j][rr] + o;
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(o), ro, voff[j], soff, 0);
           }
         }
