@@ -88,34 +88,52 @@ def copy_calibration(device, nbytes=1 << 30, reps=4):
     print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}), flush=True)
 
 
-def cpu_baseline(inp, w, mode, ec, rows):
-    """Time the CPU oracle on a bounded sample: the first ``rows`` tokens of the workload."""
+def cpu_baseline(inp, w, mode, ec, rows, repeats=1, single_thread=False):
+    """Time the CPU oracle on a bounded sample: the first ``rows`` tokens of the workload.
+
+    ``repeats`` runs are timed and the median reported; ``single_thread`` adds the same sample
+    timed with every BLAS pool limited to one thread."""
     import numpy as np
     from oracle import backward, pipeline
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
+        threadpool_limits = None
         blas_threads = 1
     S = min(w.rows_per_example, rows)
     sample = {"G": inp["G"][:rows], "X": inp["X"][:rows], "W": inp["W"], "dtype": inp["dtype"]}
     fx, fw = pipeline.forward_operands(sample["X"], sample["W"], inp["dtype"], S)
-    t0 = time.perf_counter()
-    q = pipeline.quantize_gradient(sample["G"], inp["dtype"], fx, fw, mode=mode, scale=0, seed=0, layer_id=0,
-                                   rows_per_example=S)
-    dx = backward.backward_dx(q["Q"], q["delta"], fw["Q"], fx["scale"], ec=ec, r_W=fw["code_colsum"][0],
-                              eps=q["eps"], ebar=q["ebar"], mu=q["mu"], rows_per_example=S)
-    dw = backward.backward_dw(q["Q"], q["delta"], fx["Q"], fw["scale"], ec=ec, xs=fx["code_colsum"],
-                              eps=q["eps"], ebar=q["ebar"], mu=q["mu"], rows_per_example=S)
-    dt = time.perf_counter() - t0
-    assert np.isfinite(dx).all() and np.isfinite(dw).all()
+
+    def once():
+        t0 = time.perf_counter()
+        q = pipeline.quantize_gradient(sample["G"], inp["dtype"], fx, fw, mode=mode, scale=0, seed=0, layer_id=0,
+                                       rows_per_example=S)
+        dx = backward.backward_dx(q["Q"], q["delta"], fw["Q"], fx["scale"], ec=ec, r_W=fw["code_colsum"][0],
+                                  eps=q["eps"], ebar=q["ebar"], mu=q["mu"], rows_per_example=S)
+        dw = backward.backward_dw(q["Q"], q["delta"], fx["Q"], fw["scale"], ec=ec, xs=fx["code_colsum"],
+                                  eps=q["eps"], ebar=q["ebar"], mu=q["mu"], rows_per_example=S)
+        dt = time.perf_counter() - t0
+        assert np.isfinite(dx).all() and np.isfinite(dw).all()
+        return dt
+
     ops = 2 * 2.0 * rows * w.d_out * w.d_in
-    return {"value": ops / dt / 1e12, "unit": "TOP/s", "cores": int(blas_threads), "kind": "oracle",
-            "seconds": round(dt, 3),
-            "sample": ("the whole workload: " if rows == w.tokens else f"first {rows} tokens of the workload: ") +
-                      f"{rows} tokens ({rows // S} example(s) of {S}), "
-                      f"D={w.d_out} and d_in={w.d_in}: numpy quantizer (1 thread) + dX + dW with float64 BLAS "
-                      f"integer GEMMs ({blas_threads} BLAS threads); forward-operand prep untimed"}
+    runs = [once() for _ in range(repeats)]
+    dt = float(np.median(runs))
+    out = {"value": ops / dt / 1e12, "unit": "TOP/s", "cores": int(blas_threads), "kind": "oracle",
+           "seconds": round(dt, 4), "runs_s": [round(r, 4) for r in runs],
+           "sample": ("the whole workload: " if rows == w.tokens else f"first {rows} tokens of the workload: ") +
+                     f"{rows} tokens ({rows // S} example(s) of {S}), "
+                     f"D={w.d_out} and d_in={w.d_in}: numpy quantizer (1 thread) + dX + dW with float64 BLAS "
+                     f"integer GEMMs ({blas_threads} BLAS threads); forward-operand prep untimed; "
+                     f"median of {repeats} run(s)"}
+    if single_thread and threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            runs1 = [once() for _ in range(repeats)]
+        dt1 = float(np.median(runs1))
+        out["single_thread"] = {"value": ops / dt1 / 1e12, "unit": "TOP/s", "cores": 1, "seconds": round(dt1, 4),
+                                "runs_s": [round(r, 4) for r in runs1]}
+    return out
 
 
 def block_cpu_baseline(inp, b, mode, ec, rows):
@@ -257,23 +275,6 @@ def run_block(args, dev, torch, inputs, s3r):
         del dv[k]
     proj = {  # name: (rows of G, cols of G = D, d_in, layer, forward operand of X, of W)
         "down": (M, F, 0, fh, fwd), "gate": (F, M, 1, fx, fwg), "up": (F, M, 2, fx, fwu)}
-    st = {}
-    for name, (D, din, layer, fxx, fww) in proj.items():
-        d = s3r.qdesc(T, D, S, mode, ec, s3r.PER_TENSOR, layer_id=layer, seed=0)
-        st[name] = dict(desc=d, Q=s3r.q_buffer(T, D, dev), delta=torch.empty(1, dtype=torch.float32, device=dev),
-                        er=torch.empty(T, dtype=torch.float32, device=dev) if ec else None,
-                        ec=torch.empty(B, D, dtype=torch.float32, device=dev) if ec else None,
-                        em=torch.empty(B, dtype=torch.float32, device=dev) if ec else None,
-                        flags=torch.zeros(1, dtype=torch.int32, device=dev), din=din, fx=fxx, fw=fww)
-    ws_q = torch.zeros(max(s3r.s3r_quantize_workspace(st[n]["desc"]) for n in st), dtype=torch.uint8, device=dev)
-    ws_g = torch.zeros(s3r.s3r_swiglu_amax_workspace(T, F), dtype=torch.uint8, device=dev)
-    amax = torch.zeros(2, dtype=torch.int32, device=dev)     # gate, up: max|G'| bits from the glue
-    ws_b = torch.zeros(max(max(s3r.s3r_backward_workspace(st[n]["desc"], st[n]["din"]) for n in st), 1),
-                       dtype=torch.uint8, device=dev)
-    # dW products on a second stream (default priority), each after its quantize; dW of the down
-    # projection also waits for dH, so the dX GEMM that the roofline is taken on runs alone
-    s2 = torch.cuda.Stream() if args.streams == 2 else None
-    ws_b2 = torch.zeros_like(ws_b) if s2 is not None else ws_b
     dH = torch.empty(T, F, dtype=torch.float32, device=dev)
     Gg = torch.empty(T, F, dtype=torch.bfloat16, device=dev)
     Gu = torch.empty_like(Gg)
@@ -283,53 +284,78 @@ def run_block(args, dev, torch, inputs, s3r):
           "up": torch.empty(F, M, dtype=torch.float32, device=dev)}
     G_in = {"down": dv["G"], "gate": Gg, "up": Gu}
     dX_out = {"down": dH, "gate": dX, "up": dX}
-    names = ["step", "glue"] + [f"quantize_{n}" for n in st] + [f"dx_{n}" for n in st] + [f"dw_{n}" for n in st]
+    names = ["step", "glue"] + [f"quantize_{n}" for n in proj] + [f"dx_{n}" for n in proj] + [f"dw_{n}" for n in proj]
+
+    def make_step(mode, ec, streams):
+        """The block's backward step for one rounding mode / correction, with its own descriptors and workspaces."""
+        st = {}
+        for name, (D, din, layer, fxx, fww) in proj.items():
+            d = s3r.qdesc(T, D, S, mode, ec, s3r.PER_TENSOR, layer_id=layer, seed=0)
+            st[name] = dict(desc=d, Q=s3r.q_buffer(T, D, dev), delta=torch.empty(1, dtype=torch.float32, device=dev),
+                            er=torch.empty(T, dtype=torch.float32, device=dev) if ec else None,
+                            ec=torch.empty(B, D, dtype=torch.float32, device=dev) if ec else None,
+                            em=torch.empty(B, dtype=torch.float32, device=dev) if ec else None,
+                            flags=torch.zeros(1, dtype=torch.int32, device=dev), din=din, fx=fxx, fw=fww)
+        ws_q = torch.empty(max(s3r.s3r_quantize_workspace(st[n]["desc"]) for n in st), dtype=torch.uint8,
+                           device=dev)
+        ws_g = torch.empty(s3r.s3r_swiglu_amax_workspace(T, F), dtype=torch.uint8, device=dev)
+        amax = torch.zeros(2, dtype=torch.int32, device=dev)     # gate, up: max|G'| bits from the glue
+        ws_b = torch.empty(max(max(s3r.s3r_backward_workspace(st[n]["desc"], st[n]["din"]) for n in st), 1),
+                           dtype=torch.uint8, device=dev)
+        # dW products on a second stream (default priority), each after its dX; the dX GEMM that
+        # feeds the next stage runs first
+        s2 = torch.cuda.Stream() if streams == 2 else None
+        ws_b2 = torch.empty_like(ws_b) if s2 is not None else ws_b
+
+        def linear(name, ev):
+            p = st[name]
+            if ev:
+                ev[f"quantize_{name}"][0].record()
+            if name == "down":
+                s3r.s3r_quantize(p["desc"], G_in[name], p["fx"].delta, p["fw"].delta, p["Q"], p["delta"], None,
+                                 p["er"], p["ec"], p["em"], p["flags"], ws_q)
+            else:   # the glue already found the step's amax: one read of G
+                k = 0 if name == "gate" else 1
+                s3r.s3r_quantize_with_amax(p["desc"], G_in[name], p["fx"].delta, p["fw"].delta, amax[k:k + 1],
+                                           p["Q"], p["delta"], p["er"], p["ec"], p["em"], p["flags"], ws_q)
+            if ev:
+                ev[f"quantize_{name}"][1].record()
+                s3r.s3r_time_next_gemm(*ev[f"dx_{name}"])
+            s3r.s3r_backward_dx(p["desc"], p["Q"], p["delta"], p["fw"].Q, p["fx"].delta, p["fw"].code_colsum[0],
+                                p["er"], p["ec"], p["em"], dX_out[name], ws_b, accumulate=(name == "up"))
+            if s2 is not None:
+                e = torch.cuda.Event()
+                e.record()
+                s2.wait_event(e)
+            if ev:
+                s3r.s3r_time_next_gemm(*ev[f"dw_{name}"])
+            s3r.s3r_backward_dw(p["desc"], p["Q"], p["delta"], p["fx"].Q, p["fw"].delta, p["fx"].code_colsum,
+                                p["er"], p["ec"], p["em"], dW[name], ws_b2,
+                                stream=None if s2 is None else s2.cuda_stream)
+
+        def step(ev):
+            if ev:
+                ev["step"][0].record()
+            linear("down", ev)
+            if ev:
+                ev["glue"][0].record()
+            s3r.s3r_swiglu_backward_amax(dH, dv["A_gate"], dv["A_up"], Gg, Gu, fx.delta, fwg.delta, fwu.delta, amax,
+                                         ws_g)
+            if ev:
+                ev["glue"][1].record()
+            linear("gate", ev)
+            linear("up", ev)
+            if s2 is not None:
+                e = torch.cuda.Event()
+                e.record(s2)
+                torch.cuda.current_stream().wait_event(e)
+            if ev:
+                ev["step"][1].record()
+
+        return step, st
+
+    step, st = make_step(mode, ec, args.streams)
     tl = Timeline(torch, names, args.steps)
-
-    def linear(name, ev):
-        p = st[name]
-        if ev:
-            ev[f"quantize_{name}"][0].record()
-        if name == "down":
-            s3r.s3r_quantize(p["desc"], G_in[name], p["fx"].delta, p["fw"].delta, p["Q"], p["delta"], None, p["er"],
-                             p["ec"], p["em"], p["flags"], ws_q)
-        else:   # the glue already found the step's amax: one read of G
-            k = 0 if name == "gate" else 1
-            s3r.s3r_quantize_with_amax(p["desc"], G_in[name], p["fx"].delta, p["fw"].delta, amax[k:k + 1], p["Q"],
-                                       p["delta"], p["er"], p["ec"], p["em"], p["flags"], ws_q)
-        if ev:
-            ev[f"quantize_{name}"][1].record()
-            s3r.s3r_time_next_gemm(*ev[f"dx_{name}"])
-        s3r.s3r_backward_dx(p["desc"], p["Q"], p["delta"], p["fw"].Q, p["fx"].delta, p["fw"].code_colsum[0], p["er"],
-                            p["ec"], p["em"], dX_out[name], ws_b, accumulate=(name == "up"))
-        if s2 is not None:
-            e = torch.cuda.Event()
-            e.record()
-            s2.wait_event(e)
-        if ev:
-            s3r.s3r_time_next_gemm(*ev[f"dw_{name}"])
-        s3r.s3r_backward_dw(p["desc"], p["Q"], p["delta"], p["fx"].Q, p["fw"].delta, p["fx"].code_colsum, p["er"],
-                            p["ec"], p["em"], dW[name], ws_b2, stream=None if s2 is None else s2.cuda_stream)
-
-    def step(ev):
-        if ev:
-            ev["step"][0].record()
-        linear("down", ev)
-        if ev:
-            ev["glue"][0].record()
-        s3r.s3r_swiglu_backward_amax(dH, dv["A_gate"], dv["A_up"], Gg, Gu, fx.delta, fwg.delta, fwu.delta, amax,
-                                     ws_g)
-        if ev:
-            ev["glue"][1].record()
-        linear("gate", ev)
-        linear("up", ev)
-        if s2 is not None:
-            e = torch.cuda.Event()
-            e.record(s2)
-            torch.cuda.current_stream().wait_event(e)
-        if ev:
-            ev["step"][1].record()
-
     ms_step = _timed_steps(torch, step, tl, args.steps, args.warmup)
     for n in st:
         assert int(st[n]["flags"].item()) == 0, n
@@ -359,7 +385,19 @@ def run_block(args, dev, torch, inputs, s3r):
         "gemm_tops": {k: round(gop / (v / 1e6) / 1e3, 1) for k, v in gemm_us.items()},
         "roofline": _roofline(gemm_us, b.name, gop),
     }
-    del st, dv, dH, dX, Gg, Gu, ws_q, ws_g, ws_b, ws_b2
+    if (mode, ec) == MODES["s3r-ec-two-way"]:
+        # the correction's cost, measured in this run: the same step without it, and dX-only
+        ov = {"s3r_ec_two_way_ms": round(ms_step, 4)}
+        for label, (m2, e2) in (("s3r", MODES["s3r"]), ("s3r_ec_dx_only", MODES["s3r-ec-dx-only"])):
+            log(f"EC overhead: timing the {label} step")
+            step2, _ = make_step(m2, e2, args.streams)
+            ov[f"{label}_ms"] = round(_timed_steps(torch, step2, Timeline(torch, names, args.steps), args.steps,
+                                                   args.warmup), 4)
+        ov["two_way_over_s3r"] = round(ov["s3r_ec_two_way_ms"] / ov["s3r_ms"], 4)
+        ov["dx_only_over_s3r"] = round(ov["s3r_ec_dx_only_ms"] / ov["s3r_ms"], 4)
+        ov["note"] = "whole-step times of the same block, same streams, in this run; ratio 1.0 = free correction"
+        out["ec_overhead"] = ov
+    del st, step, dv, dH, dX, Gg, Gu, dW
     out["bf16_context"] = bf16_gemm_context(torch, dev, T, M, F, sum(gemm_us.values()), ms_step, args.steps)
     if args.cpu_rows != 0:
         rows = S if args.cpu_rows < 0 else max(S, min(args.cpu_rows, T) // S * S)
@@ -576,10 +614,15 @@ def run_linear(args, dev, torch, inputs, s3r):
         "roofline": _roofline({"dx": t_gx, "dw": t_gw}, w.name, gop),
     }
     if args.cpu_rows != 0:
-        rows = T if args.cpu_rows < 0 else min(args.cpu_rows, T)
-        rows = max(S, rows // S * S)
+        # a bounded sample: the whole of a small workload, else its first example (at least 1024
+        # tokens); three timed runs below 2^38 multiply-adds, and for a small layer one thread as well
+        small = T * D * K <= (1 << 28)
+        rows = (T if small else min(T, max(1024, S))) if args.cpu_rows < 0 else min(args.cpu_rows, T)
+        if rows >= S:
+            rows = rows // S * S
         log(f"CPU oracle baseline on the first {rows} tokens")
-        out["cpu_baseline"] = cpu_baseline(inp, w, mode, ec, rows)
+        out["cpu_baseline"] = cpu_baseline(inp, w, mode, ec, rows, repeats=3 if T * D * K <= (1 << 38) else 1,
+                                           single_thread=small)
     return out
 
 
