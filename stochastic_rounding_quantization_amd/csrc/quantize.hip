@@ -115,10 +115,13 @@ __device__ __forceinline__ Step make_step(uint32_t abits) {
 }
 
 // ---------------------------------------------------------------- pass 1 ----
-// kAmaxBlocks blocks, each a contiguous band of rows; a thread loads one
+// Up to kAmaxBlocks blocks (amax_blocks: at least kAmaxRows rows each), each a contiguous band of rows; a thread loads one
 // 16-byte column chunk of kAmaxRows rows at a time, straight-line when the band
 // and the chunk are full.
 constexpr int kAmaxRows = 8;
+// Blocks of the per-tensor amax pass: one per kAmaxRows rows, at most kAmaxBlocks (a small
+// tensor gets few blocks, and each code-pass block then reduces few partials).
+int amax_blocks(int64_t T) { return (int)std::max<int64_t>(1, std::min<int64_t>(kAmaxBlocks, (T + kAmaxRows - 1) / kAmaxRows)); }
 
 template <typename TIn, bool VEC>
 __global__ __launch_bounds__(kThreads) void amax_tensor_kernel(
@@ -127,35 +130,61 @@ __global__ __launch_bounds__(kThreads) void amax_tensor_kernel(
   const int64_t cpr = (D + 7) / 8;  // 8-element chunks per row
   const int64_t rpb = (T + gridDim.x - 1) / gridDim.x;   // rows per block
   const int64_t rb0 = (int64_t)blockIdx.x * rpb, rb1 = min(rb0 + rpb, T);
+  // |fl(fl(g * s_x) * s_w)|, its bits compared as unsigned (NaN above every number)
+  auto fold_bits = [](float g, float fx, float s) { return __float_as_uint((g * fx) * s) & 0x7FFFFFFFu; };
   uint32_t m = 0;
   for (int64_t t0 = rb0; t0 < rb1; t0 += kAmaxRows) {
     const bool rows_full = t0 + kAmaxRows <= rb1;
-    for (int64_t c = threadIdx.x; c < cpr; c += kThreads) {
-      float v[kAmaxRows][8];
-      float s[8];
-      load8_scale(sw, c * 8, D, VEC, s);
-      if (VEC && rows_full && c * 8 + 8 <= D) {
+    float fx[kAmaxRows];
 #pragma unroll
-        for (int u = 0; u < kAmaxRows; ++u) load8<TIn, true>(G + (t0 + u) * ld, c * 8, D, v[u]);
-      } else {
+    for (int u = 0; u < kAmaxRows; ++u) fx[u] = (t0 + u < rb1 && sx) ? sx[t0 + u] : 1.f;
+    int64_t c = threadIdx.x;
+    if constexpr (sizeof(TIn) == 2 && VEC) {
+      // full bands of bf16: two chunk columns per pass, their 16 rows' raw words all loaded
+      // before any is decoded (4 registers per 8 elements keeps every block resident)
+      if (rows_full) {
+        for (; c + kThreads < cpr && (c + kThreads) * 8 + 8 <= D; c += 2 * kThreads) {
+          uint4 raw[2][kAmaxRows];
 #pragma unroll
-        for (int u = 0; u < kAmaxRows; ++u) {
-          if (t0 + u < rb1) load8<TIn, VEC>(G + (t0 + u) * ld, c * 8, D, v[u]);
-          else {
+          for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int i = 0; i < 8; ++i) v[u][i] = 0.f;
+            for (int u = 0; u < kAmaxRows; ++u)
+              raw[h][u] = *reinterpret_cast<const uint4*>(G + (t0 + u) * ld + (c + h * kThreads) * 8);
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            float s[8];
+            load8_scale(sw, (c + h * kThreads) * 8, D, true, s);
+#pragma unroll
+            for (int u = 0; u < kAmaxRows; ++u) {
+              const uint32_t w[4] = {raw[h][u].x, raw[h][u].y, raw[h][u].z, raw[h][u].w};
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const uint32_t b0 = fold_bits(__uint_as_float(w[i] << 16), fx[u], s[2 * i]);
+                const uint32_t b1 = fold_bits(__uint_as_float(w[i] & 0xFFFF0000u), fx[u], s[2 * i + 1]);
+                m = max(m, max(b0, b1));
+              }
+            }
           }
         }
       }
+    }
+    // the rest (other dtypes, partial bands, ragged chunks): one chunk column at a time
+    for (; c < cpr; c += kThreads) {
+      float v[kAmaxRows][8];
+      float s[8];
+      load8_scale(sw, c * 8, D, VEC, s);
 #pragma unroll
       for (int u = 0; u < kAmaxRows; ++u) {
-        const float fx = (t0 + u < rb1 && sx) ? sx[t0 + u] : 1.f;
+        if (t0 + u < rb1) load8<TIn, VEC>(G + (t0 + u) * ld, c * 8, D, v[u]);
+        else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const uint32_t b = abs_bits((v[u][i] * fx) * s[i]);
-          m = m > b ? m : b;
+          for (int i = 0; i < 8; ++i) v[u][i] = 0.f;
         }
       }
+#pragma unroll
+      for (int u = 0; u < kAmaxRows; ++u)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) m = max(m, fold_bits(v[u][i], fx[u], s[i]));
     }
   }
   __shared__ uint32_t red[kThreads / kWave];
@@ -324,22 +353,26 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
           v[2 * i] = __uint_as_float(w[i] << 16);
           v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
         }
-        int q[8];
+        // Codes packed four to a word.  RTNE: clamp, then add 1.5 * 2^23, whose round-to-nearest-even
+        // sum holds rint(x) in its low byte.  SR / S3R: t = clamp(floor(x * 2^24)) + r * 2^24 holds
+        // floor(x + r) in its top byte, and t & 0xFF000000 is that code times 2^24; the error
+        // 2^24 (q - x) = fl(that - x * 2^24) is the rounding error on the 2^24 grid, one rounding
+        // (its sums are scaled back by 2^-24 below, exactly).
+        uint32_t pw[2];
         float es = 0.f;
         if (st.flag) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) q[i] = 0;
+          pw[0] = pw[1] = 0u;
         } else if constexpr (MODE == 0) {
+          uint32_t y[8];
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
             const float x = ((v[i] * fx) * sw8[i]) * st.inv;
-            q[i] = (int)fminf(fmaxf(__builtin_rintf(x), -127.f), 127.f);
-            if constexpr (EC) {
-              const float e = (float)q[i] - x;
-              es += e;
-              col[i] += e;
-            }
+            y[i] = __float_as_uint(fminf(fmaxf(x, -127.f), 127.f) + 12582912.f);
           }
+#pragma unroll
+          for (int h = 0; h < 2; ++h)   // low bytes of y[4h..4h+3]
+            pw[h] = __builtin_amdgcn_perm(y[4 * h + 1], y[4 * h], 0x0C0C0400u) |
+                    __builtin_amdgcn_perm(y[4 * h + 3], y[4 * h + 2], 0x04000C0Cu);
         } else {
           int32_t R[8];
           if constexpr (MODE == 2) {
@@ -355,22 +388,27 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
             R[0] = sr_units24(w0.x); R[1] = sr_units24(w0.y); R[2] = sr_units24(w0.z); R[3] = sr_units24(w0.w);
             R[4] = sr_units24(w1.x); R[5] = sr_units24(w1.y); R[6] = sr_units24(w1.z); R[7] = sr_units24(w1.w);
           }
+          uint32_t tv[8];
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
             const float x24 = ((v[i] * fx) * sw8[i]) * st.inv24;
             int32_t X;
             asm("v_cvt_flr_i32_f32 %0, %1" : "=v"(X) : "v"(x24));   // floor; x24 is finite here
             X = min(max(X, -(127 << 24)), 127 << 24);
-            q[i] = (X + R[i]) >> 24;
+            tv[i] = (uint32_t)(X + R[i]);
             if constexpr (EC) {
-              const float e = fmaf(x24, -0x1p-24f, (float)q[i]);
-              es += e;
-              col[i] += e;
+              const float e24 = (float)(int32_t)(tv[i] & 0xFF000000u) - x24;
+              es += e24;
+              col[i] += e24;
             }
           }
+#pragma unroll
+          for (int h = 0; h < 2; ++h)   // top bytes of tv[4h..4h+3]
+            pw[h] = __builtin_amdgcn_perm(tv[4 * h + 1], tv[4 * h], 0x0C0C0703u) |
+                    __builtin_amdgcn_perm(tv[4 * h + 3], tv[4 * h + 2], 0x07030C0Cu);
         }
         rsum[k] = es;
-        store8<true>(Q + t * p.ld_q, j0, p.D, q);
+        *reinterpret_cast<uint2*>(Q + t * p.ld_q + j0) = make_uint2(pw[0], pw[1]);
       }
       if constexpr (EC) {
         // reduce-scatter of the 16 row sums: afterwards lane l holds row k = l >> 2
@@ -397,7 +435,9 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
         }
         r1s += __shfl_xor(r1s, 2, kWave);
         r1s += __shfl_xor(r1s, 1, kWave);
-        if ((lane & 3) == 0) row_part[(r0 + wave + 4 * (lane >> 2)) * p.n_ctiles + ctile] = r1s;
+        if ((lane & 3) == 0) row_part[(r0 + wave + 4 * (lane >> 2)) * p.n_ctiles + ctile] = r1s * 0x1p-24f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) col[i] *= 0x1p-24f;   // to the units the slow path sums in
       }
     }
   }
@@ -831,7 +871,7 @@ template <typename TIn, bool VEC, int MODE, bool EC, bool PT, bool COLSUM>
 void launch_q(const QuantArgs& a, const WsLayout& L, const QuantTile& p, dim3 grid, hipStream_t st) {
   hipLaunchKernelGGL((quantize_kernel<TIn, VEC, MODE, EC, PT, COLSUM>), grid, dim3(kThreads), 0, st, p,
                      (const TIn*)a.G, a.sx, a.sw, a.Q, a.delta, a.flags,
-                     a.amax_in ? a.amax_in : (const uint32_t*)(a.ws + L.amax_part), a.amax_in ? 1 : kAmaxBlocks,
+                     a.amax_in ? a.amax_in : (const uint32_t*)(a.ws + L.amax_part), a.amax_in ? 1 : amax_blocks(a.T),
                      (const uint32_t*)(a.ws + L.amax_rows),
                      (float*)(a.ws + L.row_part), (float*)(a.ws + L.col_part), (int32_t*)(a.ws + L.colq_part),
                      (uint32_t*)(a.ws + L.counter), GroupArgs{});
@@ -865,7 +905,7 @@ void run_quantize(const QuantArgs& a, const WsLayout& L, hipStream_t st) {
   const TIn* G = (const TIn*)a.G;
   if (a.scale == S3R_PER_TENSOR) {
     if (!a.amax_in)   // otherwise the step comes from the caller's amax: G is read once
-      hipLaunchKernelGGL((amax_tensor_kernel<TIn, VEC>), dim3(kAmaxBlocks), dim3(kThreads), 0, st, G, a.ld_g,
+      hipLaunchKernelGGL((amax_tensor_kernel<TIn, VEC>), dim3(amax_blocks(a.T)), dim3(kThreads), 0, st, G, a.ld_g,
                          a.T, a.D, a.sx, a.sw, (uint32_t*)(a.ws + L.amax_part));
   } else {
     const unsigned nb = (unsigned)((a.T + kThreads / kWave - 1) / (kThreads / kWave));
