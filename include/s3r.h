@@ -450,7 +450,8 @@ int s3r_mx_backward_dx(const s3r_qdesc* desc, const uint8_t* Qh, int64_t ld_qh,
  * minus sum_b ebar'_b xs_b^T and 1 u'^T with u' = sum_t (eps'_t - mu'_b)
  * dq(X)[t,:] (the _t statistics); the correction only with ec TWO_WAY or
  * DW_ONLY, which need xs [B x d_in] (s3r_mx_operand's colsum of X with the
- * examples' length) and B = T / rows_per_example <= 8. */
+ * examples' length), B = T / rows_per_example.  The GEMM epilogue applies the
+ * first eight examples' terms and a rank-update pass the rest. */
 int s3r_mx_backward_dw(const s3r_qdesc* desc, const uint8_t* Qt, int64_t ld_qt,
                        const uint8_t* Qt_scales, int64_t ld_qts,
                        const uint8_t* Xt, int64_t ld_xt, const uint8_t* Xt_scales, int64_t ld_xts,

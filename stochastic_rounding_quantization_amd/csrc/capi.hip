@@ -502,7 +502,7 @@ int s3r_mx_backward_dw(const s3r_qdesc* d, const uint8_t* Qt, int64_t ld_qt, con
   if ((rc = check_mx_operand(Qt, ld_qt, Qt_scales, ld_qts, D, T))) return rc;
   if ((rc = check_mx_operand(Xt, ld_xt, Xt_scales, ld_xts, d_in, T))) return rc;
   const bool ec = d->ec == S3R_EC_TWO_WAY || d->ec == S3R_EC_DW_ONLY;
-  if (ec && (!xs || !ec_row_t || !ec_col_t || !ec_mean_t || B > 8)) return S3R_ERR_INVALID_ARG;
+  if (ec && (!xs || !ec_row_t || !ec_col_t || !ec_mean_t)) return S3R_ERR_INVALID_ARG;
   if (ws_bytes < mx_backward_workspace(T, D, d_in, B)) return S3R_ERR_WORKSPACE;
   if (!ws || ((uintptr_t)ws & 255u)) return S3R_ERR_INVALID_ARG;
   if ((rc = check_arch())) return rc;

@@ -807,23 +807,19 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_kernel(MxGemm g, MxEpi ep) {
 // ------------------------------------------------ correction products ----
 // part[kc][b][n] = sum over k in chunk kc of coef[b][k] * dequant(P[n][k]) for
 // b < nb, P an MXFP4 matrix [N x K] (K-major codes, scales [K/128][N][4]).
-// Block (x, y): rows 4 RPW x .. (RPW per wave), K chunk y of 2048, in
+// Block (x, y): RG groups of 4 RPW rows (RPW per wave, every group's loads
+// issued first, the coefficients staged once for all of them), K chunk y of 2048, in
 // which lane l takes the 32-element block l: its 16 code bytes, its scale and
 // the chunk's coefficients from LDS, stored [b][i4][lane] (float4 units) so a
-// wave's reads are conflict-free.  Codes decode branch-free to signed
-// multiples of 0.5 (the magnitudes 0 .. 6 are 0 1 2 3 4 6 8 12 halves); the
-// block scale / 2 multiplies the lane's sum.  Fixed order: per-lane sums, a
+// wave's reads are conflict-free.  Codes decode to signed multiples of 0.5,
+// counted in halves (exact integers), by the hardware conversion; the block
+// scale / 2 multiplies the lane's sum.  Fixed order: per-lane sums, a
 // reduce-scatter of the RPW x NB sums across the wave, and mx_sum_parts over
 // the chunks.
+typedef float v2f __attribute__((ext_vector_type(2)));
 constexpr int kRdChunk = 2048;
-constexpr uint32_t kE2M1Halves = 0xC8643210u;
 
-__device__ __forceinline__ float e2m1_halves(uint32_t c) {
-  const int u = (int)((kE2M1Halves >> (4u * (c & 7u))) & 15u);
-  return (float)((c & 8u) ? -u : u);
-}
-
-template <int NB, int RPW>
+template <int NB, int RPW, int RG>
 __global__ __launch_bounds__(256) void mx_rowdot_kernel(const uint8_t* __restrict__ P, int64_t ldp,
                                                         const uint8_t* __restrict__ Ps, int64_t ldps, int64_t N,
                                                         int64_t K, int nb, const float* __restrict__ coef,
@@ -832,67 +828,106 @@ __global__ __launch_bounds__(256) void mx_rowdot_kernel(const uint8_t* __restric
   static_assert(V == 4 || V == 8 || V == 16 || V == 32, "reduce-scatter shape");
   __shared__ float4 s_c[NB][8][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t n0 = ((int64_t)blockIdx.x * 4 + wave) * RPW;
   const int64_t kc = (int64_t)blockIdx.y * kRdChunk;
-  for (int x = threadIdx.x; x < NB * kRdChunk; x += 256) {
-    const int b = x / kRdChunk, e = x % kRdChunk;      // element e of the chunk -> lane e / 32, i4 (e % 32) / 4
-    const float v = (b < nb && kc + e < K) ? coef[(int64_t)b * K + kc + e] : 0.f;
-    reinterpret_cast<float*>(&s_c[b][(e & 31) >> 2][e >> 5])[e & 3] = v;
+  // the chunk's coefficients, staged once for the block's RG row groups: elements e .. e+3 of
+  // example b go to s_c[b][(e % 32) / 4][e / 32], one float4
+  for (int x = threadIdx.x; x < NB * (kRdChunk / 4); x += 256) {
+    const int b = x / (kRdChunk / 4), e = (x % (kRdChunk / 4)) * 4;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (b < nb) {
+      const float* src = coef + (int64_t)b * K + kc + e;
+      if (kc + e + 4 <= K && ((uintptr_t)src & 15u) == 0) {
+        v = *reinterpret_cast<const float4*>(src);
+      } else {
+        v.x = kc + e < K ? src[0] : 0.f;
+        v.y = kc + e + 1 < K ? src[1] : 0.f;
+        v.z = kc + e + 2 < K ? src[2] : 0.f;
+        v.w = kc + e + 3 < K ? src[3] : 0.f;
+      }
+    }
+    s_c[b][(e & 31) >> 2][e >> 5] = v;
   }
   __syncthreads();
   const int64_t k = kc + lane * 32;
   const bool kv = k < K;
-  // all rows' loads first (rows past N re-read row N - 1; their sums are not stored)
-  uint4 wr[RPW];
-  int sbr[RPW];
+  // every row of the block's RG groups loaded before any is used (rows past N re-read row N - 1;
+  // their sums are not stored)
+  uint4 wr[RG][RPW];
+  int sbr[RG][RPW];
 #pragma unroll
-  for (int r = 0; r < RPW; ++r) {
-    const int64_t n = min(n0 + r, N - 1);
-    wr[r] = kv ? *reinterpret_cast<const uint4*>(P + n * ldp + k / 2) : make_uint4(0u, 0u, 0u, 0u);
-    sbr[r] = kv ? (int)Ps[(k / 128) * ldps + n * 4 + ((k / 32) & 3)] : 127;
-  }
-  float acc[V];
+  for (int g = 0; g < RG; ++g)
 #pragma unroll
-  for (int r = 0; r < RPW; ++r) {
-    const uint32_t wv[4] = {wr[r].x, wr[r].y, wr[r].z, wr[r].w};
-    float a[NB];
+    for (int r = 0; r < RPW; ++r) {
+      const int64_t n = min((((int64_t)blockIdx.x * RG + g) * 4 + wave) * RPW + r, N - 1);
+      wr[g][r] = kv ? *reinterpret_cast<const uint4*>(P + n * ldp + k / 2) : make_uint4(0u, 0u, 0u, 0u);
+      sbr[g][r] = kv ? (int)Ps[(k / 128) * ldps + n * 4 + ((k / 32) & 3)] : 127;
+    }
 #pragma unroll
-    for (int b = 0; b < NB; ++b) a[b] = 0.f;
+  for (int g = 0; g < RG; ++g) {
+    const int64_t n0 = (((int64_t)blockIdx.x * RG + g) * 4 + wave) * RPW;
+    float acc[V];
 #pragma unroll
-    for (int i4 = 0; i4 < 8; ++i4) {
-      const uint32_t word = wv[i4 >> 1] >> (16 * (i4 & 1));
-      const float x0 = e2m1_halves(word), x1 = e2m1_halves(word >> 4);
-      const float x2 = e2m1_halves(word >> 8), x3 = e2m1_halves(word >> 12);
+    for (int r = 0; r < RPW; ++r) {
+      const uint32_t wv[4] = {wr[g][r].x, wr[g][r].y, wr[g][r].z, wr[g][r].w};
+      float a[NB];
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const float4 c = s_c[b][i4][lane];
-        a[b] = fmaf(c.x, x0, a[b]);
-        a[b] = fmaf(c.y, x1, a[b]);
-        a[b] = fmaf(c.z, x2, a[b]);
-        a[b] = fmaf(c.w, x3, a[b]);
+      for (int b = 0; b < NB; ++b) a[b] = 0.f;
+      // the hardware FP4 -> f32 conversion decodes one byte (two codes, the low nibble first) per
+      // instruction, times 2: signed multiples of 0.5 become exact integers of halves
+#pragma unroll
+      for (int wi = 0; wi < 4; ++wi) {
+        const v2f p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wv[wi], 2.f, 0);
+        const v2f p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wv[wi], 2.f, 1);
+        const v2f p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wv[wi], 2.f, 2);
+        const v2f p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wv[wi], 2.f, 3);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const float4 c0 = s_c[b][2 * wi][lane], c1 = s_c[b][2 * wi + 1][lane];
+          a[b] = fmaf(c0.x, p0.x, a[b]);
+          a[b] = fmaf(c0.y, p0.y, a[b]);
+          a[b] = fmaf(c0.z, p1.x, a[b]);
+          a[b] = fmaf(c0.w, p1.y, a[b]);
+          a[b] = fmaf(c1.x, p2.x, a[b]);
+          a[b] = fmaf(c1.y, p2.y, a[b]);
+          a[b] = fmaf(c1.z, p3.x, a[b]);
+          a[b] = fmaf(c1.w, p3.y, a[b]);
+        }
+      }
+      const float half_scale = __builtin_ldexpf(1.f, sbr[g][r] - 128);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) acc[r * NB + b] = a[b] * half_scale;
+    }
+    // reduce-scatter of the V sums over the lane bits 5 .. log2(64 / V), then the remaining low bits
+    constexpr int kLow = 64 / V;                        // lanes that end up sharing one sum
+#pragma unroll
+    for (int o = V / 2; o >= 1; o >>= 1) {
+      const int bit = o * kLow;
+      const bool hi = lane & bit;
+#pragma unroll
+      for (int i = 0; i < o; ++i) {
+        const float send = hi ? acc[i] : acc[i + o];
+        acc[i] = (hi ? acc[i + o] : acc[i]) + __shfl_xor(send, bit, 64);
       }
     }
-    const float half_scale = __builtin_ldexpf(1.f, sbr[r] - 128);
+    float tot = acc[0];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) acc[r * NB + b] = a[b] * half_scale;
+    for (int o = 1; o < kLow; o <<= 1) tot += __shfl_xor(tot, o, 64);
+    const int vi = lane / kLow, r = vi / NB, b = vi % NB;
+    if (lane % kLow == 0 && b < nb && n0 + r < N) part[((int64_t)blockIdx.y * NB + b) * N + n0 + r] = tot;
   }
-  // reduce-scatter of the V sums over the lane bits 5 .. log2(64 / V), then the remaining low bits
-  constexpr int kLow = 64 / V;                          // lanes that end up sharing one sum
-#pragma unroll
-  for (int o = V / 2; o >= 1; o >>= 1) {
-    const int bit = o * kLow;
-    const bool hi = lane & bit;
-#pragma unroll
-    for (int i = 0; i < o; ++i) {
-      const float send = hi ? acc[i] : acc[i + o];
-      acc[i] = (hi ? acc[i + o] : acc[i]) + __shfl_xor(send, bit, 64);
-    }
-  }
-  float tot = acc[0];
-#pragma unroll
-  for (int o = 1; o < kLow; o <<= 1) tot += __shfl_xor(tot, o, 64);
-  const int vi = lane / kLow, r = vi / NB, b = vi % NB;
-  if (lane % kLow == 0 && b < nb && n0 + r < N) part[((int64_t)blockIdx.y * NB + b) * N + n0 + r] = tot;
+}
+
+// dW correction terms of examples 8 .. B-1 (the GEMM epilogue applies examples 0 .. 7):
+// dW[j][n] -= sum_b ebar_b[j] * xs_b[n].
+__global__ __launch_bounds__(256) void mx_dw_rank_update_kernel(float* __restrict__ dW, int64_t ld, int64_t D,
+                                                                int64_t N, int64_t B, const float* __restrict__ ebar,
+                                                                const float* __restrict__ xs) {
+  const int64_t j = blockIdx.y;
+  const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (n >= N) return;
+  float s = 0.f;
+  for (int64_t b = 8; b < B; ++b) s = fmaf(ebar[b * D + j], xs[b * N + n], s);
+  dW[j * ld + n] -= s;
 }
 
 // out[b][n] = sum over the chunks kc (in order) of part[kc][b][n], b < nb, NB slots per chunk.
@@ -1030,9 +1065,11 @@ void run_rowdot(const MxBwArgs& a, int64_t N, int64_t K, int nb, const float* co
                 hipStream_t st) {
   const int nkc = (int)((K + kRdChunk - 1) / kRdChunk);
   float* dst = nkc == 1 ? out : part;
-  constexpr int RPW = 4;                               // 16 rows per block: enough blocks to hide latency
-  hipLaunchKernelGGL((mx_rowdot_kernel<NB, RPW>), dim3((unsigned)((N + 4 * RPW - 1) / (4 * RPW)), (unsigned)nkc),
-                     dim3(256), 0, st, a.B, a.ldb, a.Bs, a.ldbs, N, K, nb, coef, dst);
+  constexpr int RPW = 4;                               // 16 rows per group, each wave's loads in flight together
+  constexpr int RG = 4;                                // groups per block: the staged coefficients serve 64 rows
+  hipLaunchKernelGGL((mx_rowdot_kernel<NB, RPW, RG>),
+                     dim3((unsigned)((N + 4 * RPW * RG - 1) / (4 * RPW * RG)), (unsigned)nkc), dim3(256), 0, st,
+                     a.B, a.ldb, a.Bs, a.ldbs, N, K, nb, coef, dst);
   if (nkc > 1)
     hipLaunchKernelGGL(mx_sum_parts_kernel, dim3((unsigned)((nb * N + 255) / 256)), dim3(256), 0, st, N, nb, NB, nkc,
                        (const float*)part, out);
@@ -1092,6 +1129,9 @@ hipError_t launch_mx_backward_dw(const MxBwArgs& a, hipStream_t st) {
   else if (B <= 2) run_mx_gemm<true, true, 2>(g, ep, st);
   else if (B <= 4) run_mx_gemm<true, true, 4>(g, ep, st);
   else run_mx_gemm<true, true, 8>(g, ep, st);
+  if (a.ec && B > 8)
+    hipLaunchKernelGGL(mx_dw_rank_update_kernel, dim3((unsigned)((a.d_in + 255) / 256), (unsigned)a.D), dim3(256), 0,
+                       st, a.out, a.ld_out, a.D, a.d_in, B, a.ec_col, a.vcol);
   return hipGetLastError();
 }
 

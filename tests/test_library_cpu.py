@@ -251,7 +251,7 @@ def test_mx_argument_errors(L):
                                     1 << 24, None)
 
     assert dw(ok, xs=None) == -1
-    assert dw(s3r.qdesc(128 * 9, D, 128, s3r.S3R, s3r.EC_TWO_WAY)) == -1   # B = 9 > 8 with the dW correction
+    assert dw(s3r.qdesc(128 * 9, D, 128, s3r.S3R, s3r.EC_TWO_WAY)) in (-4, -5)  # nine examples: accepted
     assert dw(s3r.qdesc(128 * 9, D, 128, s3r.S3R, s3r.EC_DX_ONLY)) in (-4, -5)  # dW uncorrected: any B
 
     def op(rows=T, cols=d_in, S=T, ld_t=T // 2, wsb=1 << 20):
