@@ -42,9 +42,10 @@ PEAK_INT8_TOPS = 5000.0     # MI355X dense INT8 MFMA, TOP/s
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, GB/s
 PEAK_FP4_TFLOPS = 10100.0   # MI355X dense FP4 (MXFP4) MFMA, TFLOP/s
 
-# HBM byte counts of the GEMM kernels, taken with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE and
-# scaled by the same counters' reading for a plain copy of known size.  The file records the
-# sha256 of the kernel source it was measured on; a stale record is not reported.
+# Byte counts of the GEMM kernels, taken with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE and scaled by
+# the same counters' reading for a plain copy of known size.  Those counters see the L2's requests to
+# the fabric, last-level (MALL) hits included, so the figure bounds the HBM bytes from above.  The
+# file records the sha256 of the kernel source it was measured on; a stale record is not reported.
 TRAFFIC_FILES = {
     "down-8192x14336x4096-bf16": os.path.join(ROOT, "profiles", "traffic_gemm_down-8192x14336x4096.md"),
     "ffn-block-8192x4096x14336-bf16": os.path.join(ROOT, "profiles", "traffic_gemm_ffn-block-8192x4096x14336.md"),
@@ -61,7 +62,8 @@ def log(msg):
 
 
 def measured_traffic(kernel_key, workload):
-    """HBM bytes per launch of one GEMM kernel from the committed counter summary, or None."""
+    """L2-to-fabric bytes (reads + writes) per launch of one GEMM kernel from the committed counter
+    summary, or None."""
     import hashlib
     import re
     path = TRAFFIC_FILES.get(workload)
@@ -72,7 +74,7 @@ def measured_traffic(kernel_key, workload):
     src = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
     if not m or m.group(1) != src or f"workload: {workload}" not in text:
         return None
-    m = re.search(rf"{kernel_key}_hbm_bytes_per_launch:\s*([0-9]+)", text)
+    m = re.search(rf"{kernel_key}_l2_egress_bytes_per_launch:\s*([0-9]+)", text)
     return int(m.group(1)) if m else None
 
 
@@ -273,6 +275,7 @@ def _roofline(gemm_us, workload, gop):
     achieved = gop / (gemm_us[key] / 1e6) / 1e3
     return {"kernel": f"gemm {key}", "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_INT8_TOPS,
             "unit": "TOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4), "traffic": measured_traffic(key, workload),
+            "traffic_counts": "FETCH_SIZE + WRITE_SIZE bytes per launch: L2-to-fabric traffic, MALL hits included",
             "algorithmic": f"2*M*N*K = {gop:.1f} GOP per launch (int8 multiply-adds x 2)"}
 
 
