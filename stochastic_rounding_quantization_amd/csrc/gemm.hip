@@ -53,6 +53,10 @@ constexpr int kStageBytes = 32768;    // A tile (16 KB) + B tile (16 KB)
 constexpr int kHalf = 16384;
 constexpr int kGroupM = 8;            // grouped tile order: 8 tile-rows per group
 constexpr int kNumXcd = 8;
+// Cache-policy bits of the epilogue's output stores: nontemporal (bit 1 on gfx950). The outputs are
+// written once and not read back by this kernel; unmarked, they would fill the last-level cache with
+// dirty lines that the next kernels' reads must first evict.
+constexpr int kStoreNT = 2;
 
 // The pipeline stages are separate LDS objects so that the compiler can tell a
 // stage being read from the stages being filled by in-flight DMA.
@@ -568,7 +572,7 @@ __device__ __forceinline__ void epilogue(const GemmParams& g, const EpiParams& e
             const float scale = EPI == EPI_DWC ? f[rr].x * colS[j] : f[rr].x;
             float o = fmaf(scale, (float)v, -corr);
             if constexpr (EPI == EPI_DXA) o = old[i & 1][rq][j][rr] + o;
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(o), ro, voff[j], soff, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(o), ro, voff[j], soff, kStoreNT);
           }
         }
       }

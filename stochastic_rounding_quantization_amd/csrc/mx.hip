@@ -798,7 +798,8 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_kernel(MxGemm g, MxEpi ep) {
           }
           const uint32_t urow = (uint32_t)(wm * 128 + i * 32 + rq * 8 + rr);
           __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(o), ro,
-                                                (uint32_t)(hk * 4) * ld4 + (uint32_t)(cc * 4 + n0 * 4), urow * ld4, 0);
+                                                (uint32_t)(hk * 4) * ld4 + (uint32_t)(cc * 4 + n0 * 4), urow * ld4,
+                                                2 /* nontemporal: written once, kept out of the last-level cache */);
         }
       }
     }

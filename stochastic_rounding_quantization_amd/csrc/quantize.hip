@@ -149,7 +149,7 @@ __global__ __launch_bounds__(kThreads) void amax_tensor_kernel(
           for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int u = 0; u < kAmaxRows; ++u)
-              raw[h][u] = *reinterpret_cast<const uint4*>(G + (t0 + u) * ld + (c + h * kThreads) * 8);
+              raw[h][u] = ld_stream_u4(G + (t0 + u) * ld + (c + h * kThreads) * 8);
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
             float s[8];
@@ -334,14 +334,14 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
       const float sx_rows = (sx && lane < kWR) ? sx[r0 + wave + 4 * lane] : 1.f;
 #pragma unroll
       for (int kk = 0; kk < kGroup; ++kk)
-        raw[kk] = *reinterpret_cast<const uint4*>(G + (r0 + wave + 4 * kk) * p.ld_g + j0);
+        raw[kk] = ld_stream_u4(G + (r0 + wave + 4 * kk) * p.ld_g + j0);
 #pragma unroll
       for (int k = 0; k < kWR; ++k) {
         if (k % kGroup == 0 && k + kGroup < kWR) {
           __builtin_amdgcn_sched_barrier(0);        // the next group's loads, in row order
 #pragma unroll
           for (int kk = k + kGroup; kk < k + 2 * kGroup; ++kk)
-            raw[kk] = *reinterpret_cast<const uint4*>(G + (r0 + wave + 4 * kk) * p.ld_g + j0);
+            raw[kk] = ld_stream_u4(G + (r0 + wave + 4 * kk) * p.ld_g + j0);
           __builtin_amdgcn_sched_barrier(0);
         }
         const int64_t t = r0 + wave + 4 * k;

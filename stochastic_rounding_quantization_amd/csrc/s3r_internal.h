@@ -82,6 +82,22 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
+// 16-byte loads with the nontemporal hint, for streams read once. Regular loads of data that is
+// not cached allocate in the last-level cache (MALL) and first evict, and write back, the dirty
+// lines an earlier kernel's writes left there; marked loads do not, and read a cold stream about
+// 1.5x faster.
+typedef unsigned int v4u32 __attribute__((ext_vector_type(4)));
+typedef float v4f32 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_stream_u4(const void* p) {
+  const v4u32 t = __builtin_nontemporal_load(reinterpret_cast<const v4u32*>(p));
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+__device__ __forceinline__ float4 ld_stream_f4(const void* p) {
+  const v4f32 t = __builtin_nontemporal_load(reinterpret_cast<const v4f32*>(p));
+  return make_float4(t.x, t.y, t.z, t.w);
+}
+
+
 // ------------------------------------------------------------- launchers ----
 // Quantizer (quantize.hip).
 struct QuantArgs {

@@ -69,10 +69,10 @@ __global__ __launch_bounds__(256) void swiglu_backward_kernel(
     uint16_t* gg = Gg + t * ld_g + j0;
     uint16_t* gu = Gu + t * ld_g + j0;
     if (VEC && j0 + 8 <= F) {
-      const float4 h0 = *reinterpret_cast<const float4*>(dh);
-      const float4 h1 = *reinterpret_cast<const float4*>(dh + 4);
-      const uint4 va = *reinterpret_cast<const uint4*>(ag);
-      const uint4 vu = *reinterpret_cast<const uint4*>(au);
+      const float4 h0 = ld_stream_f4(dh);
+      const float4 h1 = ld_stream_f4(dh + 4);
+      const uint4 va = ld_stream_u4(ag);
+      const uint4 vu = ld_stream_u4(au);
       const float h[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
       const uint32_t wa[4] = {va.x, va.y, va.z, va.w}, wu[4] = {vu.x, vu.y, vu.z, vu.w};
       uint32_t og[4], ou[4];
@@ -130,10 +130,10 @@ __global__ __launch_bounds__(256) void swiglu_amax_kernel(
     uint16_t* gg = Gg + t * ld_g + j0;
     uint16_t* gu = Gu + t * ld_g + j0;
     if (VEC && j0 + 8 <= F) {
-      const float4 h0 = *reinterpret_cast<const float4*>(dh);
-      const float4 h1 = *reinterpret_cast<const float4*>(dh + 4);
-      const uint4 va = *reinterpret_cast<const uint4*>(ag);
-      const uint4 vu = *reinterpret_cast<const uint4*>(au);
+      const float4 h0 = ld_stream_f4(dh);
+      const float4 h1 = ld_stream_f4(dh + 4);
+      const uint4 va = ld_stream_u4(ag);
+      const uint4 vu = ld_stream_u4(au);
       float cg[8], cu[8];
       if (swg) {
         const float4 a = *reinterpret_cast<const float4*>(swg + j0), b = *reinterpret_cast<const float4*>(swg + j0 + 4);
