@@ -321,10 +321,13 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
   // the 16 rows of this wave (t = r0 + wave + 4k) are loaded as raw bf16 in groups of 4, each
   // group's loads issued when the previous group's coding starts (one group ahead); the 16 row
   // sums of the errors are one reduce-scatter across the wave at the end.
+  // The choice is per wave: both paths end in cross-lane sums of the row errors, which must see every
+  // lane of the wave on the same path.
   bool done = false;
   if constexpr (sizeof(TIn) == 2 && VEC && !PT && !COLSUM) {
     constexpr int kWR = kRowsPerTile / (kThreads / kWave);   // 16 rows per wave
-    if (r1 - r0 == kRowsPerTile && j0 + 8 <= p.D && (MODE != 1 || (p.D & 3) == 0)) {
+    const bool fast_lane = r1 - r0 == kRowsPerTile && j0 + 8 <= p.D && (MODE != 1 || (p.D & 3) == 0);
+    if (__builtin_amdgcn_ballot_w64(!fast_lane) == 0) {
       done = true;
       constexpr int kGroup = 4;
       uint4 raw[kWR];
