@@ -204,6 +204,8 @@ def main():
                          "call (beside the dX); a single linear or MoE layer: above 1 also times its dW on a second "
                          "stream after the quantize call and reports the faster schedule. Per-kernel fields always "
                          "come from a single-stream pass")
+    ap.add_argument("--dw-pair", type=int, default=1, choices=(0, 1),
+                    help="FFN block: the gate and up projections' dW as one launch (1) or two (0)")
     ap.add_argument("--cpu-rows", type=int, default=-1,
                     help="tokens in the CPU-oracle sample (-1: the default sample, 0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -271,7 +273,9 @@ def _pick_streams(torch, args, make_step, ms_single):
 
 
 def _roofline(gemm_us, workload, gop):
+    """The longest GEMM launch against the INT8 peak; gop: GOP per launch (a number, or one per key)."""
     key = max(gemm_us, key=lambda k: gemm_us[k])
+    gop = gop[key] if isinstance(gop, dict) else gop
     achieved = gop / (gemm_us[key] / 1e6) / 1e3
     return {"kernel": f"gemm {key}", "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_INT8_TOPS,
             "unit": "TOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4), "traffic": measured_traffic(key, workload),
@@ -306,10 +310,12 @@ def run_block(args, dev, torch, inputs, s3r):
           "up": torch.empty(F, M, dtype=torch.float32, device=dev)}
     G_in = {"down": dv["G"], "gate": Gg, "up": Gu}
     dX_out = {"down": dH, "gate": dX, "up": dX}
-    names = ["step", "glue"] + [f"quantize_{n}" for n in proj] + [f"dx_{n}" for n in proj] + [f"dw_{n}" for n in proj]
+    dw_keys = ["dw_down", "dw_gate_up"] if args.dw_pair else [f"dw_{n}" for n in proj]
+    names = ["step", "glue"] + [f"quantize_{n}" for n in proj] + [f"dx_{n}" for n in proj] + dw_keys
 
-    def make_step(mode, ec, streams):
-        """The block's backward step for one rounding mode / correction, with its own descriptors and workspaces."""
+    def make_step(mode, ec, streams, pair=True):
+        """The block's backward step for one rounding mode / correction, with its own descriptors and workspaces.
+        pair: the gate and up projections' dW as one launch (s3r_backward_dw_pair) after the up projection's dX."""
         st = {}
         for name, (D, din, layer, fxx, fww) in proj.items():
             d = s3r.qdesc(T, D, S, mode, ec, s3r.PER_TENSOR, layer_id=layer, seed=0)
@@ -329,6 +335,15 @@ def run_block(args, dev, torch, inputs, s3r):
         # so it runs beside that projection's v GEMV and dX GEMM
         s2 = torch.cuda.Stream() if streams >= 2 else None
         ws_b2 = torch.empty_like(ws_b) if s2 is not None else ws_b
+        ws_p = torch.empty(max(s3r.s3r_backward_dw_pair_workspace(st["gate"]["desc"], M), 1), dtype=torch.uint8,
+                           device=dev)
+
+        def side(after_dx):
+            # the second stream waits for the main stream's work so far (streams 2: after a dX; 3: after a quantize)
+            if s2 is not None and streams == (2 if after_dx else 3):
+                e = torch.cuda.Event()
+                e.record()
+                s2.wait_event(e)
 
         def linear(name, ev):
             p = st[name]
@@ -343,23 +358,28 @@ def run_block(args, dev, torch, inputs, s3r):
                                            p["Q"], p["delta"], p["er"], p["ec"], p["em"], p["flags"], ws_q)
             if ev:
                 ev[f"quantize_{name}"][1].record()
-            if streams == 3:
-                e = torch.cuda.Event()
-                e.record()
-                s2.wait_event(e)
+            if not (pair and name == "gate"):
+                side(after_dx=False)
             if ev:
                 s3r.s3r_time_next_gemm(*ev[f"dx_{name}"])
             s3r.s3r_backward_dx(p["desc"], p["Q"], p["delta"], p["fw"].Q, p["fx"].delta, p["fw"].code_colsum[0],
                                 p["er"], p["ec"], p["em"], dX_out[name], ws_b, accumulate=(name == "up"))
-            if streams == 2:
-                e = torch.cuda.Event()
-                e.record()
-                s2.wait_event(e)
+            if pair and name == "gate":
+                return
+            side(after_dx=True)
+            sid = None if s2 is None else s2.cuda_stream
+            if pair and name == "up":
+                g, u = st["gate"], st["up"]
+                if ev:
+                    s3r.s3r_time_next_gemm(*ev["dw_gate_up"])
+                s3r.s3r_backward_dw_pair(g["desc"], g["Q"], u["Q"], g["delta"], u["delta"], fx.Q, g["fw"].delta,
+                                         u["fw"].delta, fx.code_colsum, (g["er"], g["ec"], g["em"]),
+                                         (u["er"], u["ec"], u["em"]), dW["gate"], dW["up"], ws_p, stream=sid)
+                return
             if ev:
                 s3r.s3r_time_next_gemm(*ev[f"dw_{name}"])
             s3r.s3r_backward_dw(p["desc"], p["Q"], p["delta"], p["fx"].Q, p["fw"].delta, p["fx"].code_colsum,
-                                p["er"], p["ec"], p["em"], dW[name], ws_b2,
-                                stream=None if s2 is None else s2.cuda_stream)
+                                p["er"], p["ec"], p["em"], dW[name], ws_b2, stream=sid)
 
         def step(ev):
             if ev:
@@ -384,17 +404,17 @@ def run_block(args, dev, torch, inputs, s3r):
 
     # per-kernel times from a single-stream pass (an event pair around a kernel that shares the GPU
     # with another stream's work would time both); the step itself in the configured schedule
-    step, st = make_step(mode, ec, 1)
+    step, st = make_step(mode, ec, 1, args.dw_pair)
     tl = Timeline(torch, names, args.steps)
     ms_single = _timed_steps(torch, step, tl, args.steps, args.warmup)
     for n in st:
         assert int(st[n]["flags"].item()) == 0, n
 
-    def step_ms(m2, e2):
+    def step_ms(m2, e2, pair=args.dw_pair):
         """Whole-step time (no per-kernel events) in the configured stream schedule."""
-        if args.streams == 1 and (m2, e2) == (mode, ec):
+        if args.streams == 1 and (m2, e2, pair) == (mode, ec, args.dw_pair):
             return ms_single
-        stepn, _ = make_step(m2, e2, args.streams)
+        stepn, _ = make_step(m2, e2, args.streams, pair)
         return _timed_steps(torch, lambda ev: stepn(None), Timeline(torch, [], args.steps), args.steps,
                             args.warmup)
 
@@ -402,7 +422,8 @@ def run_block(args, dev, torch, inputs, s3r):
     ms_step = step_ms(mode, ec)
     gop = 2.0 * T * M * F / 1e9                      # each of the six GEMMs
     value = 6 * gop / (ms_step / 1e3) / 1e3
-    gemm_us = {f"{k}_{n}": tl.avg_us(f"{k}_{n}") for n in st for k in ("dx", "dw")}
+    gemm_us = {k: tl.avg_us(k) for k in [f"dx_{n}" for n in st] + dw_keys}
+    gemm_gop = {k: gop * (2 if k == "dw_gate_up" else 1) for k in gemm_us}
     q_us = sum(tl.avg_us(f"quantize_{n}") for n in st)
     q_bytes = (T * M + 2 * T * F) * 3                 # bf16 G read once + int8 Q written, three calls
     q_gbs = q_bytes / (q_us / 1e6) / 1e9
@@ -413,9 +434,11 @@ def run_block(args, dev, torch, inputs, s3r):
         "dtype": "i8", "data": "synthetic",
         "config": {"workload": b.name, "tokens": T, "d_model": M, "d_ff": F, "rows_per_example": S,
                    "mode": args.mode, "step_scale": "per-tensor", "g_dtype": "bf16", "streams": args.streams,
+                   "dw_pair": bool(args.dw_pair),
                    "stages": "down (quantize, dX=dH, dW), SwiGLU glue with the gate/up amax, gate and up "
-                             "(quantize with that amax, dX added, dW); with 2 streams each dW (its U GEMV and "
-                             "GEMM) runs on a second stream after its dX"},
+                             "(quantize with that amax, dX added), the gate and up dW as one launch (dw_pair); "
+                             "with 2 streams each dW launch (its U GEMVs and GEMM) runs on a second stream "
+                             "after the dX before it"},
         "ms_per_step_single_stream": round(ms_single, 4),
         "kernel_fields": "kernels_us, gemm_tops, roofline and quantizer come from a single-stream pass of the "
                          "same step, HIP events on the launch stream around each kernel",
@@ -427,8 +450,8 @@ def run_block(args, dev, torch, inputs, s3r):
                        **{f"gemm_{k}": round(v, 2) for k, v in gemm_us.items()},
                        "glue": round(tl.avg_us("glue"), 2), "step_events": round(tl.avg_us("step"), 2)},
         "kernels_us_min_median_max": tl.spread(),
-        "gemm_tops": {k: round(gop / (v / 1e6) / 1e3, 1) for k, v in gemm_us.items()},
-        "roofline": _roofline(gemm_us, b.name, gop),
+        "gemm_tops": {k: round(gemm_gop[k] / (v / 1e6) / 1e3, 1) for k, v in gemm_us.items()},
+        "roofline": _roofline(gemm_us, b.name, gemm_gop),
     }
     if (mode, ec) == MODES["s3r-ec-two-way"]:
         # the correction's cost, measured in this run: the same step without it, and dX-only
@@ -441,6 +464,11 @@ def run_block(args, dev, torch, inputs, s3r):
         ov["note"] = ("whole-step times of the same block in the same stream schedule, in this run; ratio 1.0 = "
                       "free correction")
         out["ec_overhead"] = ov
+    log("timing the step with the other dW launch arrangement")
+    other = round(step_ms(mode, ec, pair=not args.dw_pair), 4)
+    out["dw_pair_ablation"] = {"paired_ms": round(ms_step, 4) if args.dw_pair else other,
+                               "separate_ms": other if args.dw_pair else round(ms_step, 4),
+                               "note": "whole-step times in this run: the gate and up dW as one launch or two"}
     del st, step, dv, dH, dX, Gg, Gu, dW
     out["bf16_context"] = bf16_gemm_context(torch, dev, T, M, F, sum(gemm_us.values()), ms_step, args.steps)
     if args.cpu_rows != 0:

@@ -250,6 +250,30 @@ int s3r_backward_dw(const s3r_qdesc* desc,
                     void* dW, int32_t out_dt, int64_t ld_dw,
                     void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* s3r_backward_dw_pair: the dW products of two projections of the same input
+ * (the gate and up projections of a SwiGLU block), dW0 from (Q0, delta0, s_w0,
+ * ec_*0) and dW1 from (Q1, delta1, s_w1, ec_*1), both against the shared input
+ * codes Xq and column sums xs_b.  Each product is the one s3r_backward_dw
+ * defines (same page passages), bit for bit; the two run as one GEMM launch, so
+ * the GPU's compute units are filled by both products' tiles (a single product
+ * whose tile count is not a multiple of the CU count leaves CUs idle in its last
+ * round).  Both codes share desc (shape, ec, rows_per_example) and ld_q;
+ * desc->scale must be PER_TENSOR (else S3R_ERR_UNSUPPORTED).  out_dt: S3R_F32
+ * or S3R_I32_RAW; both outputs use ld_dw.
+ *   ws: s3r_backward_dw_pair_workspace(desc, d_in) bytes, 256-byte aligned
+ *   (the two correction GEMVs' halves; none without the dW correction).
+ */
+size_t s3r_backward_dw_pair_workspace(const s3r_qdesc* desc, int64_t d_in);
+int s3r_backward_dw_pair(const s3r_qdesc* desc,
+                         const int8_t* Q0, const int8_t* Q1, int64_t ld_q,
+                         const float* delta0, const float* delta1,
+                         const int8_t* Xq, int64_t ld_x, int64_t d_in,
+                         const float* s_w0, const float* s_w1, const int32_t* xs_b,
+                         const float* ec_row0, const float* ec_col0, const float* ec_mean0,
+                         const float* ec_row1, const float* ec_col1, const float* ec_mean1,
+                         void* dW0, void* dW1, int32_t out_dt, int64_t ld_dw,
+                         void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Workspace for either backward call (the larger of the two). */
 size_t s3r_backward_workspace(const s3r_qdesc* desc, int64_t d_in);
 

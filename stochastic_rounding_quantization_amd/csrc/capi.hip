@@ -189,6 +189,12 @@ size_t s3r_backward_workspace(const s3r_qdesc* d, int64_t d_in) {
   return a > b ? a : b;
 }
 
+size_t s3r_backward_dw_pair_workspace(const s3r_qdesc* d, int64_t d_in) {
+  if (check_desc(d) != S3R_OK || d_in < 0 || d->scale != S3R_PER_TENSOR) return 0;
+  return 2 * align_up(dw_workspace(d->rows, d->cols, d_in, d->rows_per_example, dw_corrected(d->ec) ? d->ec : 0, 0),
+                      256);
+}
+
 static int check_gemm_operand(const int8_t* p, int64_t ld, int64_t rows, int64_t cols, bool nonempty) {
   // the GEMM addresses each operand through a buffer descriptor with 32-bit byte
   // offsets, including up to one tile (256 rows, 64 k-rows) past the last row
@@ -251,6 +257,49 @@ int s3r_backward_dw(const s3r_qdesc* d, const int8_t* Q, int64_t ld_q, const flo
   a.sw = s_w; a.xs = xs_b; a.ec_row = ec_row; a.ec_col = ec_col; a.ec_mean = ec_mean; a.ec = ec ? d->ec : 0;
   a.out = dW; a.out_dt = out_dt; a.ld_out = ld_dw; a.ws = (char*)ws;
   return finish(launch_backward_dw(a, stream));
+}
+
+int s3r_backward_dw_pair(const s3r_qdesc* d, const int8_t* Q0, const int8_t* Q1, int64_t ld_q, const float* delta0,
+                         const float* delta1, const int8_t* Xq, int64_t ld_x, int64_t d_in, const float* s_w0,
+                         const float* s_w1, const int32_t* xs_b, const float* ec_row0, const float* ec_col0,
+                         const float* ec_mean0, const float* ec_row1, const float* ec_col1, const float* ec_mean1,
+                         void* dW0, void* dW1, int32_t out_dt, int64_t ld_dw, void* ws, size_t ws_bytes,
+                         hipStream_t stream) {
+  int rc = check_desc(d);
+  if (rc) return rc;
+  if (out_dt != S3R_F32 && out_dt != S3R_I32_RAW) return S3R_ERR_UNSUPPORTED;
+  if (d->scale != S3R_PER_TENSOR) return S3R_ERR_UNSUPPORTED;
+  const int64_t T = d->rows, D = d->cols;
+  if (d_in < 0 || T > kMaxK) return S3R_ERR_INVALID_ARG;
+  const bool out_nonempty = D > 0 && d_in > 0;
+  if (!delta0 || !delta1 || (out_nonempty && (!dW0 || !dW1)) || ld_dw < d_in || ld_dw >= kMaxLdOut)
+    return S3R_ERR_INVALID_ARG;
+  if (out_nonempty && (((uintptr_t)dW0 | (uintptr_t)dW1) & 3u)) return S3R_ERR_INVALID_ARG;
+  if ((rc = check_gemm_operand(Q0, ld_q, T, D, T > 0 && D > 0))) return rc;
+  if ((rc = check_gemm_operand(Q1, ld_q, T, D, T > 0 && D > 0))) return rc;
+  if ((rc = check_gemm_operand(Xq, ld_x, T, d_in, T > 0 && d_in > 0))) return rc;
+  const bool ec = dw_corrected(d->ec) && out_dt == S3R_F32;
+  if (ec && (!xs_b || !ec_row0 || !ec_col0 || !ec_mean0 || !ec_row1 || !ec_col1 || !ec_mean1))
+    return S3R_ERR_INVALID_ARG;
+  const size_t one = align_up(dw_workspace(T, D, d_in, d->rows_per_example, ec ? d->ec : 0, 0), 256);
+  if (ws_bytes < 2 * one || (one && (!ws || ((uintptr_t)ws & 255u)))) return S3R_ERR_WORKSPACE;
+  if ((rc = check_arch())) return rc;
+  DwArgs a[2]{};
+  const int8_t* Q[2] = {Q0, Q1};
+  const float* delta[2] = {delta0, delta1};
+  const float* s_w[2] = {s_w0, s_w1};
+  const float* er[2] = {ec_row0, ec_row1};
+  const float* ecol[2] = {ec_col0, ec_col1};
+  const float* em[2] = {ec_mean0, ec_mean1};
+  void* out[2] = {dW0, dW1};
+  for (int i = 0; i < 2; ++i) {
+    a[i].Q = Q[i]; a[i].ld_q = ld_q; a[i].delta = delta[i]; a[i].per_token = 0; a[i].X = Xq; a[i].ld_x = ld_x;
+    a[i].T = T; a[i].D = D; a[i].d_in = d_in; a[i].S = d->rows_per_example;
+    a[i].sw = s_w[i]; a[i].xs = xs_b; a[i].ec_row = er[i]; a[i].ec_col = ecol[i]; a[i].ec_mean = em[i];
+    a[i].ec = ec ? d->ec : 0;
+    a[i].out = out[i]; a[i].out_dt = out_dt; a[i].ld_out = ld_dw; a[i].ws = (char*)ws + i * one;
+  }
+  return finish(launch_backward_dw_pair(a[0], a[1], stream));
 }
 
 int s3r_swiglu_backward(int64_t T, int64_t F, const float* dH, int64_t ld_dh, const uint16_t* A_gate,

@@ -589,7 +589,10 @@ __device__ __forceinline__ void epilogue(const GemmParams& g, const EpiParams& e
 // first (order[]), so the longest K loops start first.  Each workgroup rebases
 // the operand, output and epilogue pointers to its group, after which the
 // dense kernel body runs unchanged.  Nothing runs if the offsets were invalid.
-enum { GRP_NONE = 0, GRP_DX = 1, GRP_DW = 2 };
+// GRP_PAIR: two problems of one shape that share the B operand (the dW products
+// of two projections of one input), tiles [0, per) of the first and [per, 2 per)
+// of the second; the second's A operand and epilogue come from gg.
+enum { GRP_NONE = 0, GRP_DX = 1, GRP_DW = 2, GRP_PAIR = 3 };
 template <typename T>
 __device__ __forceinline__ const T* advance(const T* p, int64_t k) { return p ? p + k : p; }
 struct GroupGemm {
@@ -598,6 +601,8 @@ struct GroupGemm {
   int64_t b_stride;      // GRP_DX: bytes between the groups' B operands
   int64_t out_stride;    // GRP_DW: elements between the groups' outputs
   int tiles_m_all;       // GRP_DX: the grid's row-tile bound
+  const int8_t* A2;      // GRP_PAIR: the second problem's A operand and epilogue
+  EpiParams ep2;
 };
 
 template <bool A_KMAJOR, int EPI, bool EC, int NB, int GRP = GRP_NONE>
@@ -638,6 +643,23 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmParams g, 
     ep.B = 1;
     tm = mt - h.t0;
     tn = bid % g.tiles_n;
+  } else if constexpr (GRP == GRP_PAIR) {
+    // XCD-aware numbering over both problems' tiles, then the grouped order within a problem
+    const int per = g.tiles_m * g.tiles_n;
+    const int nblocks = 2 * per;
+    int bid = blockIdx.x;
+    if (nblocks % kNumXcd == 0) bid = (bid % kNumXcd) * (nblocks / kNumXcd) + bid / kNumXcd;
+    int local = bid;
+    if (bid >= per) {
+      local = bid - per;
+      g.A = gg.A2;
+      ep = gg.ep2;
+    }
+    const int group = kGroupM * g.tiles_n;
+    const int first_m = (local / group) * kGroupM;
+    const int gsz = min(g.tiles_m - first_m, kGroupM);
+    tm = first_m + (local % group) % gsz;
+    tn = (local % group) / gsz;
   } else {
     if (gg.status[0] != 0) return;
     const int per = g.tiles_m * g.tiles_n;
@@ -1111,7 +1133,9 @@ hipError_t run_gemm(const GemmParams& g, const EpiParams& ep, hipStream_t st, co
   const GemmTiming ev = tm;
   tm = GemmTiming{};
   const int nblocks = GRP == GRP_NONE ? g.tiles_m * g.tiles_n
-                      : GRP == GRP_DX ? gg.tiles_m_all * g.tiles_n : (int)gg.G * g.tiles_m * g.tiles_n;
+                      : GRP == GRP_DX   ? gg.tiles_m_all * g.tiles_n
+                      : GRP == GRP_PAIR ? 2 * g.tiles_m * g.tiles_n
+                                        : (int)gg.G * g.tiles_m * g.tiles_n;
   if (ev.start && hipEventRecord(ev.start, st) != hipSuccess) return hipErrorInvalidValue;
   if (nblocks > 0)
     hipLaunchKernelGGL((gemm_i8_kernel<A_KMAJOR, EPI, EC, NB, GRP>), dim3((unsigned)nblocks), dim3(kGemmThreads), 0,
@@ -1195,10 +1219,13 @@ hipError_t launch_backward_dx(const DxArgs& a, hipStream_t st) {
   return run_gemm<true, EPI_DX, false>(g, ep, st);
 }
 
-hipError_t launch_backward_dw(const DwArgs& a, hipStream_t st) {
+namespace {
+// The dW epilogue's parameters, and (two-way correction) u = sum_t (eps_t - mu_b) Xq[t, :] by the
+// correction GEMV into the workspace.
+hipError_t dw_epilogue(const DwArgs& a, EpiParams& ep, hipStream_t st) {
   const int64_t B = a.S > 0 ? a.T / a.S : 0;
   const DwLayout L = dw_layout(a.T, a.d_in, a.ec, a.per_token);
-  EpiParams ep{};
+  ep = EpiParams{};
   ep.delta = a.delta; ep.per_token = 0; ep.row_scale = a.sw;
   ep.ec = (a.ec == S3R_EC_TWO_WAY || a.ec == S3R_EC_DW_ONLY) && a.out_dt == S3R_F32;
   ep.colsum = a.xs; ep.ebar = a.ec_col; ep.ec_row = a.ec_row; ep.ec_mean = a.ec_mean;
@@ -1215,6 +1242,27 @@ hipError_t launch_backward_dw(const DwArgs& a, hipStream_t st) {
       if (e != hipSuccess) return e;
     }
     ep.u = u;
+  }
+  return hipSuccess;
+}
+
+// Examples past the epilogue's NB slots: the rest of the correction's rank-B term, sum_b ebar_b[j] xs_b[i]
+// for b >= NB, subtracted by a pass over the output.
+hipError_t dw_rank_update(const DwArgs& a, const EpiParams& ep, hipStream_t st) {
+  if (!ep.ec || ep.B <= 8 || a.D == 0 || a.d_in == 0) return hipSuccess;
+  hipLaunchKernelGGL(dw_rank_update_kernel, dim3((unsigned)((a.d_in + 255) / 256), (unsigned)a.D), dim3(256), 0, st,
+                     (float*)a.out, a.ld_out, a.D, a.d_in, ep.B, a.ec_col, a.xs, a.sw);
+  return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_backward_dw(const DwArgs& a, hipStream_t st) {
+  const int64_t B = a.S > 0 ? a.T / a.S : 0;
+  const DwLayout L = dw_layout(a.T, a.d_in, a.ec, a.per_token);
+  EpiParams ep;
+  {
+    hipError_t e = dw_epilogue(a, ep, st);
+    if (e != hipSuccess) return e;
   }
   // B operand: the input codes, or (per-token steps) their per-column requantization Zq
   const int8_t* Bop = a.X;
@@ -1256,10 +1304,29 @@ hipError_t launch_backward_dw(const DwArgs& a, hipStream_t st) {
     else if (B <= 4) e = run_gemm<false, EPI_DW, true, 4>(g, ep, st);
     else e = run_gemm<false, EPI_DW, true, kMaxB>(g, ep, st);
   }
-  if (e != hipSuccess || !ep.ec || B <= 8 || a.D == 0 || a.d_in == 0) return e;
-  hipLaunchKernelGGL(dw_rank_update_kernel, dim3((unsigned)((a.d_in + 255) / 256), (unsigned)a.D), dim3(256), 0, st,
-                     (float*)a.out, a.ld_out, a.D, a.d_in, B, a.ec_col, a.xs, a.sw);
-  return hipGetLastError();
+  if (e != hipSuccess) return e;
+  return dw_rank_update(a, ep, st);
+}
+
+hipError_t launch_backward_dw_pair(const DwArgs& a0, const DwArgs& a1, hipStream_t st) {
+  const int64_t B = a0.S > 0 ? a0.T / a0.S : 0;
+  EpiParams ep0, ep1;
+  hipError_t e = dw_epilogue(a0, ep0, st);
+  if (e == hipSuccess) e = dw_epilogue(a1, ep1, st);
+  if (e != hipSuccess) return e;
+  const GemmParams g = make_gemm(a0.Q, a0.ld_q, a0.X, a0.ld_x, a0.D, a0.d_in, a0.T);
+  GroupGemm gg{};
+  gg.A2 = a1.Q;
+  gg.ep2 = ep1;
+  if (a0.out_dt == S3R_I32_RAW) e = run_gemm<false, EPI_RAW, false, 1, GRP_PAIR>(g, ep0, st, gg);
+  else if (!ep0.ec) e = run_gemm<false, EPI_DW, false, 1, GRP_PAIR>(g, ep0, st, gg);
+  else if (B <= 1) e = run_gemm<false, EPI_DW, true, 1, GRP_PAIR>(g, ep0, st, gg);
+  else if (B <= 2) e = run_gemm<false, EPI_DW, true, 2, GRP_PAIR>(g, ep0, st, gg);
+  else if (B <= 4) e = run_gemm<false, EPI_DW, true, 4, GRP_PAIR>(g, ep0, st, gg);
+  else e = run_gemm<false, EPI_DW, true, kMaxB, GRP_PAIR>(g, ep0, st, gg);
+  if (e == hipSuccess) e = dw_rank_update(a0, ep0, st);
+  if (e == hipSuccess) e = dw_rank_update(a1, ep1, st);
+  return e;
 }
 
 // ---------------------------------------------------------- grouped calls ----

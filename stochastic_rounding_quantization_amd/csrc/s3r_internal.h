@@ -147,6 +147,9 @@ size_t dx_workspace(int64_t T, int64_t D, int64_t d_in, int64_t S, int ec);
 size_t dw_workspace(int64_t T, int64_t D, int64_t d_in, int64_t S, int ec, int per_token);
 hipError_t launch_backward_dx(const DxArgs& a, hipStream_t st);
 hipError_t launch_backward_dw(const DwArgs& a, hipStream_t st);
+// Two per-tensor dW products of one shape sharing X (a0.X == a1.X, a0.ld_q == a1.ld_q), one GEMM launch;
+// each DwArgs brings its own workspace.
+hipError_t launch_backward_dw_pair(const DwArgs& a0, const DwArgs& a1, hipStream_t st);
 size_t grouped_dx_workspace(int64_t R, int64_t D, int64_t d_in, int64_t G, int ec);
 size_t grouped_dw_workspace(int64_t R, int64_t D, int64_t d_in, int64_t G, int ec);
 hipError_t launch_grouped_backward_dx(const DxArgs& a, int64_t G, const int64_t* offsets, int64_t w_stride,

@@ -29,7 +29,7 @@ FLAG_NONFINITE, FLAG_TINY_STEP, FLAG_BAD_GROUPS = 1, 2, 8
 S3R_NOALLOC_SCRATCH_BYTES = 32 << 20    # include/s3r.h: the no-alloc quantizer's device array
 
 EXPORTED = ["s3r_quantize_workspace", "s3r_quantize", "s3r_quantize_with_amax", "s3r_quantize_noalloc", "s3r_backward_dx",
-            "s3r_backward_dw", "s3r_backward_workspace", "s3r_swiglu_backward", "s3r_swiglu_amax_workspace",
+            "s3r_backward_dw", "s3r_backward_dw_pair", "s3r_backward_dw_pair_workspace", "s3r_backward_workspace", "s3r_swiglu_backward", "s3r_swiglu_amax_workspace",
             "s3r_swiglu_backward_amax", "s3r_grouped_workspace", "s3r_grouped_quantize",
             "s3r_grouped_backward_dx", "s3r_grouped_backward_dw", "s3r_mx_workspace", "s3r_mx_operand_workspace",
             "s3r_mx_operand", "s3r_mx_quantize", "s3r_mx_backward_dx", "s3r_mx_backward_dw", "s3r_time_next_gemm",
@@ -80,6 +80,11 @@ def lib() -> ctypes.CDLL:
     L.s3r_backward_dx.restype = ctypes.c_int
     L.s3r_backward_dw.argtypes = [DP, P, I64, P, P, I64, I64, P, P, P, P, P, P, I32, I64, P, SZ, P]
     L.s3r_backward_dw.restype = ctypes.c_int
+    L.s3r_backward_dw_pair.argtypes = [DP, P, P, I64, P, P, P, I64, I64, P, P, P, P, P, P, P, P, P, P, P, I32, I64,
+                                       P, SZ, P]
+    L.s3r_backward_dw_pair.restype = ctypes.c_int
+    L.s3r_backward_dw_pair_workspace.argtypes = [DP, I64]
+    L.s3r_backward_dw_pair_workspace.restype = SZ
     L.s3r_backward_workspace.argtypes = [DP, I64]
     L.s3r_backward_workspace.restype = SZ
     L.s3r_swiglu_backward.argtypes = [I64, I64, P, I64, P, P, I64, P, P, I64, P]
@@ -225,6 +230,27 @@ def s3r_backward_dw(desc: QDesc, Q, delta, Xq, s_w, xs_b, ec_row, ec_col, ec_mea
     if rc_only:
         return rc
     _check("s3r_backward_dw", rc)
+
+
+def s3r_backward_dw_pair_workspace(desc: QDesc, d_in: int) -> int:
+    return lib().s3r_backward_dw_pair_workspace(ctypes.byref(desc), d_in)
+
+
+def s3r_backward_dw_pair(desc: QDesc, Q0, Q1, delta0, delta1, Xq, s_w0, s_w1, xs_b, ec0, ec1, dW0, dW1, ws=None,
+                         stream=None, *, rc_only=False):
+    """Both dW products of two projections of one input in one launch; ec0 / ec1 are the
+    (ec_row, ec_col, ec_mean) triples of the two quantize calls."""
+    d_in = dW0.shape[1]
+    if _ld(Q1, desc.cols) != _ld(Q0, desc.cols) or _ld(dW1, d_in) != _ld(dW0, d_in) or dW1.dtype != dW0.dtype:
+        raise ValueError("the two products need codes and outputs of one layout")
+    rc = lib().s3r_backward_dw_pair(
+        ctypes.byref(desc), _ptr(Q0), _ptr(Q1), _ld(Q0, desc.cols), _ptr(delta0), _ptr(delta1), _ptr(Xq),
+        _ld(Xq, d_in), d_in, _ptr(s_w0), _ptr(s_w1), _ptr(xs_b), _ptr(ec0[0]), _ptr(ec0[1]), _ptr(ec0[2]),
+        _ptr(ec1[0]), _ptr(ec1[1]), _ptr(ec1[2]), _ptr(dW0), _ptr(dW1), _odtype(dW0), _ld(dW0, d_in), _ptr(ws),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+    if rc_only:
+        return rc
+    _check("s3r_backward_dw_pair", rc)
 
 
 def s3r_swiglu_backward(dH, A_gate, A_up, G_gate, G_up, stream=None, *, rc_only=False):
@@ -475,6 +501,20 @@ def backward_dw(q: Quantized, Xq, s_w=None, xs_b=None, out_dtype=None, stream=No
     ws = _workspace(s3r_backward_workspace(q.desc, d_in), Xq.device)
     s3r_backward_dw(q.desc, q.Q, q.delta, Xq, s_w, xs_b, q.ec_row, q.ec_col, q.ec_mean, dW, ws, stream)
     return dW
+
+
+def backward_dw_pair(qa: Quantized, qb: Quantized, Xq, s_w_a=None, s_w_b=None, xs_b=None, out_dtype=None,
+                     stream=None):
+    """dW of two projections of the input Xq (one GEMM launch); qa and qb share shape and layout."""
+    import torch
+    d_in = Xq.shape[1]
+    D = qa.desc.cols
+    dWa = torch.empty(D, d_in, dtype=out_dtype or torch.float32, device=Xq.device)
+    dWb = torch.empty_like(dWa)
+    ws = _workspace(s3r_backward_dw_pair_workspace(qa.desc, d_in), Xq.device)
+    s3r_backward_dw_pair(qa.desc, qa.Q, qb.Q, qa.delta, qb.delta, Xq, s_w_a, s_w_b, xs_b,
+                         (qa.ec_row, qa.ec_col, qa.ec_mean), (qb.ec_row, qb.ec_col, qb.ec_mean), dWa, dWb, ws, stream)
+    return dWa, dWb
 
 
 # ------------------------------------------------------------ MXFP4 helpers ----

@@ -332,6 +332,81 @@ def test_dx_accumulate_two_projections():
     assert_rows_close(host(dX), refs[0] + refs[1], TOL, "accumulated dX")
 
 
+@pytest.mark.parametrize("D", [136, 144, 200, 256, 264, 520])
+def test_ec_statistics_partial_column_tiles(D):
+    # D not a multiple of the quantizer's 512-column tiles: a wave of the last column tile holds both
+    # full 8-column chunks and chunks past D; the per-token error sums eps_t, their means and both
+    # corrected products still match the oracle
+    T, d_in, S = 192, 300, 64
+    w = inputs.WORKLOADS["down-4096x11008x4096-bf16"].scaled(T, d_in, D, rows_per_example=S)
+    inp = inputs.make_linear_inputs(w)
+    gpu, ref = _check_linear(inp, S, s3r.S3R, s3r.EC_TWO_WAY, seed=5, layer=1)
+    assert rel_err(host(gpu["q"].ec_mean), ref["q"]["mu"]) <= TOL
+
+
+def _two_projections(T, D, d_in, S):
+    # two projections of one input X (a SwiGLU block's gate and up): own G and W, shared X
+    w = inputs.WORKLOADS["down-4096x11008x4096-bf16"].scaled(T, d_in, D, rows_per_example=S)
+    a = inputs.make_linear_inputs(w)
+    raw = inputs.make_linear_inputs(inputs.WORKLOADS["linear-256x512x1024-f32"].scaled(T, d_in, D, S))
+    b = {"G": inputs.f32_to_bf16_bits(raw["G"]), "X": a["X"], "W": inputs.f32_to_bf16_bits(raw["W"]), "dtype": "bf16"}
+    return a, b
+
+
+@pytest.mark.parametrize("T,D,d_in,S,mode,ec,raw", [
+    (384, 300, 700, 128, s3r.S3R, s3r.EC_TWO_WAY, False),      # ragged, three examples
+    (440, 330, 200, 40, s3r.S3R, s3r.EC_TWO_WAY, False),       # eleven examples: the rank-update pass
+    (192, 136, 300, 64, s3r.S3R, s3r.EC_DW_ONLY, False),
+    (256, 512, 1024, 256, s3r.SR, s3r.EC_NONE, False),
+    (256, 520, 264, 128, s3r.S3R, s3r.EC_TWO_WAY, True),       # raw int32 accumulators
+])
+def test_dw_pair_equals_two_single_calls(T, D, d_in, S, mode, ec, raw):
+    # s3r_backward_dw_pair gives each product bit for bit as s3r_backward_dw does, and both match the oracle
+    a, b = _two_projections(T, D, d_in, S)
+    fx = s3r.forward_operand(to_dev(a["X"], "bf16"), rows_per_example=S)
+    qs, fws, refs = [], [], []
+    for layer, inp in ((1, a), (2, b)):
+        fw = s3r.forward_operand(to_dev(inp["W"], "bf16"), rows_per_example=inp["W"].shape[0])
+        qs.append(s3r.quantize(to_dev(inp["G"], "bf16"), mode=mode, ec=ec, row_scale=fx.delta, col_scale=fw.delta,
+                               seed=5, layer_id=layer, rows_per_example=S))
+        fws.append(fw)
+        if not raw:
+            refs.append(pipeline.linear_backward(inp, mode=mode, ec=ec, seed=5, layer_id=layer,
+                                                 rows_per_example=S)["dW"])
+    odt = torch.int32 if raw else None
+    single = [s3r.backward_dw(q, fx.Q, s_w=fw.delta, xs_b=fx.code_colsum, out_dtype=odt) for q, fw in zip(qs, fws)]
+    pair = s3r.backward_dw_pair(qs[0], qs[1], fx.Q, fws[0].delta, fws[1].delta, fx.code_colsum, out_dtype=odt)
+    torch.cuda.synchronize()
+    for k in range(2):
+        assert torch.equal(pair[k], single[k]), f"product {k}: the paired launch differs from the single call"
+        if not raw:
+            assert_rows_close(host(pair[k]), refs[k], TOL, f"paired dW {k} T={T} D={D} d_in={d_in}")
+
+
+def test_dw_pair_ffn_block_size():
+    # the FFN block's gate and up dW at full size (two 14336 x 4096 outputs, K = 8192): bit for bit the
+    # single calls', sampled rows against the oracle
+    T, M, F, S = 8192, 4096, 14336, 2048
+    a, b = _two_projections(T, F, M, S)
+    fx = s3r.forward_operand(to_dev(a["X"], "bf16"), rows_per_example=S)
+    qs, fws = [], []
+    for layer, inp in ((1, a), (2, b)):
+        fw = s3r.forward_operand(to_dev(inp["W"], "bf16"), rows_per_example=inp["W"].shape[0])
+        qs.append(s3r.quantize(to_dev(inp["G"], "bf16"), mode=s3r.S3R, ec=s3r.EC_TWO_WAY, row_scale=fx.delta,
+                               col_scale=fw.delta, seed=9, layer_id=layer, rows_per_example=S))
+        fws.append(fw)
+    pair = s3r.backward_dw_pair(qs[0], qs[1], fx.Q, fws[0].delta, fws[1].delta, fx.code_colsum)
+    for k in range(2):
+        single = s3r.backward_dw(qs[k], fx.Q, s_w=fws[k].delta, xs_b=fx.code_colsum)
+        torch.cuda.synchronize()
+        assert torch.equal(pair[k], single), f"product {k}: the paired launch differs from the single call"
+        del single
+    rows = _sample_rows(F, 4, 11)
+    ref = pipeline.linear_backward(a, mode=s3r.S3R, ec=s3r.EC_TWO_WAY, seed=9, layer_id=1, rows_per_example=S,
+                                   dx_rows=np.array([0]), dw_rows=rows)["dW"]
+    assert_rows_close(host(pair[0])[rows], ref, TOL, "paired dW gate, FFN block size")
+
+
 def test_gate_projection_ffn_block_size_sampled():
     # the FFN block's gate / up projection shape: G [8192 x 14336] (two-pass quantizer, 224 MiB of
     # bf16), W [14336 x 4096], X [8192 x 4096]; S3R-EC two-way, rows sampled

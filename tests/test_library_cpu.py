@@ -112,6 +112,35 @@ def test_backward_argument_errors(L):
     assert s3r.s3r_backward_workspace(d, 128) == 0
 
 
+def test_backward_dw_pair_argument_errors(L):
+    P = ctypes.c_void_p
+    d = s3r.qdesc(64, 96, 32, s3r.S3R, s3r.EC_NONE)
+    args = dict(Q0=P(4096), Q1=P(8192), ldq=96, X=P(16384), ldx=128, din=128, out0=P(32768), out1=P(65536), odt=0,
+                ldo=128, ec=(None,) * 6, xs=None, ws=None, wsb=0)
+
+    def pair(**kw):
+        a = {**args, **kw}
+        return L.s3r_backward_dw_pair(ctypes.byref(kw.get("d", d)), a["Q0"], a["Q1"], a["ldq"], P(16), P(32), a["X"],
+                                      a["ldx"], a["din"], None, None, a["xs"], *a["ec"], a["out0"], a["out1"],
+                                      a["odt"], a["ldo"], a["ws"], a["wsb"], None)
+
+    assert pair(Q1=P(4097)) == -1            # misaligned second operand
+    assert pair(out1=None) == -1             # second output missing
+    assert pair(odt=3) == -2                 # accumulation is dX only
+    pt = s3r.qdesc(64, 96, 32, s3r.S3R, s3r.EC_NONE, s3r.PER_TOKEN)
+    assert pair(d=pt) == -2                  # per-tensor steps only
+    ec = s3r.qdesc(64, 96, 32, s3r.S3R, s3r.EC_TWO_WAY)
+    assert pair(d=ec) == -1                  # correction inputs missing
+    full = dict(xs=P(1 << 20), ec=tuple(P(1 << 21 + i) for i in range(6)))
+    need = s3r.s3r_backward_dw_pair_workspace(ec, 128)
+    one = s3r.s3r_backward_workspace(s3r.qdesc(64, 96, 32, s3r.S3R, s3r.EC_DW_ONLY), 128)   # a dW's alone
+    assert need == 2 * ((one + 255) // 256 * 256) > 0                 # one correction GEMV's workspace per product
+    assert pair(d=ec, **full, ws=P(1 << 22), wsb=need - 1) == -3
+    assert pair(d=ec, **full, ws=P((1 << 22) + 64), wsb=need) == -3    # workspace not 256-byte aligned
+    assert s3r.s3r_backward_dw_pair_workspace(d, 128) == 0
+    assert s3r.s3r_backward_dw_pair_workspace(pt, 128) == 0
+
+
 def test_swiglu_argument_errors(L):
     P = ctypes.c_void_p
     ok = dict(T=4, F=16, dH=P(256), ldh=16, Ag=P(512), Au=P(768), lda=16, Gg=P(1024), Gu=P(1280), ldg=16)
