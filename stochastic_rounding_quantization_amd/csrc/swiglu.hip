@@ -53,37 +53,47 @@ __device__ __forceinline__ void glue1(float dh, float a, float u, uint32_t& gg, 
   gg = bf16_rne((dh * u) * ds);
 }
 
-// One thread: 8 consecutive elements of one row (16-byte loads and stores).
+// Thread mapping of both glue kernels: blockIdx.x * 256 + threadIdx.x is an 8-element chunk column
+// of the rows (16-byte loads and stores), fixed for the thread; blockIdx.y strides over the rows. A row
+// of a block is one contiguous span of 2048 columns, and the per-chunk index arithmetic is one add.
+
+// 8 elements of one row: G_gate and G_up as packed bf16 pairs (og, ou: elements 2i, 2i+1 in word i).
+__device__ __forceinline__ void glue8(const float* __restrict__ dh, const uint16_t* __restrict__ ag,
+                                      const uint16_t* __restrict__ au, uint32_t (&og)[4], uint32_t (&ou)[4]) {
+  const float4 h0 = ld_stream_f4(dh);
+  const float4 h1 = ld_stream_f4(dh + 4);
+  const uint4 va = ld_stream_u4(ag);
+  const uint4 vu = ld_stream_u4(au);
+  __builtin_amdgcn_sched_barrier(0);   // all four loads in flight before any is waited for
+  const float h[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+  const uint32_t wa[4] = {va.x, va.y, va.z, va.w}, wu[4] = {vu.x, vu.y, vu.z, vu.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t g0, u0, g1, u1;
+    glue1(h[2 * i], __uint_as_float(wa[i] << 16), __uint_as_float(wu[i] << 16), g0, u0);
+    glue1(h[2 * i + 1], __uint_as_float(wa[i] & 0xFFFF0000u), __uint_as_float(wu[i] & 0xFFFF0000u), g1, u1);
+    og[i] = g0 | (g1 << 16);
+    ou[i] = u0 | (u1 << 16);
+  }
+}
+
 template <bool VEC>
 __global__ __launch_bounds__(256) void swiglu_backward_kernel(
     int64_t T, int64_t F, const float* __restrict__ dH, int64_t ld_dh, const uint16_t* __restrict__ Ag,
     const uint16_t* __restrict__ Au, int64_t ld_a, uint16_t* __restrict__ Gg, uint16_t* __restrict__ Gu,
     int64_t ld_g) {
-  const int64_t cpr = (F + 7) / 8;
-  const int64_t total = T * cpr;
-  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < total; c += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t t = c / cpr, j0 = (c - t * cpr) * 8;
+  const int64_t j0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 8;
+  if (j0 >= F) return;
+  const bool full = VEC && j0 + 8 <= F;
+  for (int64_t t = blockIdx.y; t < T; t += gridDim.y) {
     const float* dh = dH + t * ld_dh + j0;
     const uint16_t* ag = Ag + t * ld_a + j0;
     const uint16_t* au = Au + t * ld_a + j0;
     uint16_t* gg = Gg + t * ld_g + j0;
     uint16_t* gu = Gu + t * ld_g + j0;
-    if (VEC && j0 + 8 <= F) {
-      const float4 h0 = ld_stream_f4(dh);
-      const float4 h1 = ld_stream_f4(dh + 4);
-      const uint4 va = ld_stream_u4(ag);
-      const uint4 vu = ld_stream_u4(au);
-      const float h[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
-      const uint32_t wa[4] = {va.x, va.y, va.z, va.w}, wu[4] = {vu.x, vu.y, vu.z, vu.w};
+    if (full) {
       uint32_t og[4], ou[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint32_t g0, u0, g1, u1;
-        glue1(h[2 * i], __uint_as_float(wa[i] << 16), __uint_as_float(wu[i] << 16), g0, u0);
-        glue1(h[2 * i + 1], __uint_as_float(wa[i] & 0xFFFF0000u), __uint_as_float(wu[i] & 0xFFFF0000u), g1, u1);
-        og[i] = g0 | (g1 << 16);
-        ou[i] = u0 | (u1 << 16);
-      }
+      glue8(dh, ag, au, og, ou);
       *reinterpret_cast<uint4*>(gg) = make_uint4(og[0], og[1], og[2], og[3]);
       *reinterpret_cast<uint4*>(gu) = make_uint4(ou[0], ou[1], ou[2], ou[3]);
     } else {
@@ -101,10 +111,9 @@ __global__ __launch_bounds__(256) void swiglu_backward_kernel(
 // The same glue, and in the same pass the per-tensor amax that the gate and up
 // projections' quantizers need: max |fl(fl(G * s_x[t]) * s_w[j])| over the
 // bf16-rounded results (the quantizer's fold of its own input), as ordered fp32
-// bits (NaN above every number).  Same thread mapping as the plain glue (8
-// consecutive elements of a row per thread, grid-stride over the chunks); each
-// block writes its two maxima to part[0][block] and part[1][block], and
-// swiglu_amax_finalize_kernel reduces them.
+// bits (NaN above every number).  Same thread mapping as the plain glue; block
+// b = blockIdx.y * gridDim.x + blockIdx.x writes its two maxima to part[0][b]
+// and part[1][b], and swiglu_amax_finalize_kernel reduces them.
 constexpr int kAmaxGlueBlocks = 4096;
 
 __device__ __forceinline__ uint32_t fold_abs_bits(uint32_t bf16, float fx, float sw) {
@@ -118,60 +127,53 @@ __global__ __launch_bounds__(256) void swiglu_amax_kernel(
     int64_t ld_g, const float* __restrict__ sx, const float* __restrict__ swg, const float* __restrict__ swu,
     uint32_t* __restrict__ part) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t cpr = (F + 7) / 8;
-  const int64_t total = T * cpr;
+  const int64_t j0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 8;
   uint32_t mg = 0, mu = 0;
-  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < total; c += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t t = c / cpr, j0 = (c - t * cpr) * 8;
-    const float fx = sx ? sx[t] : 1.f;
-    const float* dh = dH + t * ld_dh + j0;
-    const uint16_t* ag = Ag + t * ld_a + j0;
-    const uint16_t* au = Au + t * ld_a + j0;
-    uint16_t* gg = Gg + t * ld_g + j0;
-    uint16_t* gu = Gu + t * ld_g + j0;
-    if (VEC && j0 + 8 <= F) {
-      const float4 h0 = ld_stream_f4(dh);
-      const float4 h1 = ld_stream_f4(dh + 4);
-      const uint4 va = ld_stream_u4(ag);
-      const uint4 vu = ld_stream_u4(au);
-      float cg[8], cu[8];
-      if (swg) {
-        const float4 a = *reinterpret_cast<const float4*>(swg + j0), b = *reinterpret_cast<const float4*>(swg + j0 + 4);
-        cg[0] = a.x; cg[1] = a.y; cg[2] = a.z; cg[3] = a.w; cg[4] = b.x; cg[5] = b.y; cg[6] = b.z; cg[7] = b.w;
+  if (j0 < F) {
+    const bool full = VEC && j0 + 8 <= F;
+    for (int64_t t = blockIdx.y; t < T; t += gridDim.y) {
+      const float fx = sx ? sx[t] : 1.f;
+      const float* dh = dH + t * ld_dh + j0;
+      const uint16_t* ag = Ag + t * ld_a + j0;
+      const uint16_t* au = Au + t * ld_a + j0;
+      uint16_t* gg = Gg + t * ld_g + j0;
+      uint16_t* gu = Gu + t * ld_g + j0;
+      if (full) {
+        // the column scales are re-read per row (cache hits) rather than held in 16 registers across
+        // the loop, which made the compiler wait for the row's first loads before issuing the last
+        float cg[8], cu[8];
+        if (swg) {
+          const float4 a = *reinterpret_cast<const float4*>(swg + j0), b = *reinterpret_cast<const float4*>(swg + j0 + 4);
+          cg[0] = a.x; cg[1] = a.y; cg[2] = a.z; cg[3] = a.w; cg[4] = b.x; cg[5] = b.y; cg[6] = b.z; cg[7] = b.w;
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) cg[i] = 1.f;
+        }
+        if (swu) {
+          const float4 a = *reinterpret_cast<const float4*>(swu + j0), b = *reinterpret_cast<const float4*>(swu + j0 + 4);
+          cu[0] = a.x; cu[1] = a.y; cu[2] = a.z; cu[3] = a.w; cu[4] = b.x; cu[5] = b.y; cu[6] = b.z; cu[7] = b.w;
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) cu[i] = 1.f;
+        }
+        uint32_t og[4], ou[4];
+        glue8(dh, ag, au, og, ou);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          mg = max(mg, max(fold_abs_bits(og[i] & 0xFFFFu, fx, cg[2 * i]), fold_abs_bits(og[i] >> 16, fx, cg[2 * i + 1])));
+          mu = max(mu, max(fold_abs_bits(ou[i] & 0xFFFFu, fx, cu[2 * i]), fold_abs_bits(ou[i] >> 16, fx, cu[2 * i + 1])));
+        }
+        *reinterpret_cast<uint4*>(gg) = make_uint4(og[0], og[1], og[2], og[3]);
+        *reinterpret_cast<uint4*>(gu) = make_uint4(ou[0], ou[1], ou[2], ou[3]);
       } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) cg[i] = 1.f;
-      }
-      if (swu) {
-        const float4 a = *reinterpret_cast<const float4*>(swu + j0), b = *reinterpret_cast<const float4*>(swu + j0 + 4);
-        cu[0] = a.x; cu[1] = a.y; cu[2] = a.z; cu[3] = a.w; cu[4] = b.x; cu[5] = b.y; cu[6] = b.z; cu[7] = b.w;
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) cu[i] = 1.f;
-      }
-      const float h[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
-      const uint32_t wa[4] = {va.x, va.y, va.z, va.w}, wu[4] = {vu.x, vu.y, vu.z, vu.w};
-      uint32_t og[4], ou[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint32_t g0, u0, g1, u1;
-        glue1(h[2 * i], __uint_as_float(wa[i] << 16), __uint_as_float(wu[i] << 16), g0, u0);
-        glue1(h[2 * i + 1], __uint_as_float(wa[i] & 0xFFFF0000u), __uint_as_float(wu[i] & 0xFFFF0000u), g1, u1);
-        og[i] = g0 | (g1 << 16);
-        ou[i] = u0 | (u1 << 16);
-        mg = max(mg, max(fold_abs_bits(g0, fx, cg[2 * i]), fold_abs_bits(g1, fx, cg[2 * i + 1])));
-        mu = max(mu, max(fold_abs_bits(u0, fx, cu[2 * i]), fold_abs_bits(u1, fx, cu[2 * i + 1])));
-      }
-      *reinterpret_cast<uint4*>(gg) = make_uint4(og[0], og[1], og[2], og[3]);
-      *reinterpret_cast<uint4*>(gu) = make_uint4(ou[0], ou[1], ou[2], ou[3]);
-    } else {
-      for (int i = 0; i < 8 && j0 + i < F; ++i) {
-        uint32_t g, u;
-        glue1(dh[i], bf16_to_f32(ag[i]), bf16_to_f32(au[i]), g, u);
-        gg[i] = (uint16_t)g;
-        gu[i] = (uint16_t)u;
-        mg = max(mg, fold_abs_bits(g, fx, swg ? swg[j0 + i] : 1.f));
-        mu = max(mu, fold_abs_bits(u, fx, swu ? swu[j0 + i] : 1.f));
+        for (int i = 0; i < 8 && j0 + i < F; ++i) {
+          uint32_t g, u;
+          glue1(dh[i], bf16_to_f32(ag[i]), bf16_to_f32(au[i]), g, u);
+          gg[i] = (uint16_t)g;
+          gu[i] = (uint16_t)u;
+          mg = max(mg, fold_abs_bits(g, fx, swg ? swg[j0 + i] : 1.f));
+          mu = max(mu, fold_abs_bits(u, fx, swu ? swu[j0 + i] : 1.f));
+        }
       }
     }
   }
@@ -182,7 +184,8 @@ __global__ __launch_bounds__(256) void swiglu_amax_kernel(
   __syncthreads();
   if (threadIdx.x < 2) {
     const int k = threadIdx.x;
-    part[(int64_t)k * gridDim.x + blockIdx.x] = max(max(red[k][0], red[k][1]), max(red[k][2], red[k][3]));
+    const int64_t nblk = (int64_t)gridDim.x * gridDim.y, b = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+    part[k * nblk + b] = max(max(red[k][0], red[k][1]), max(red[k][2], red[k][3]));
   }
 }
 
@@ -209,8 +212,18 @@ __global__ __launch_bounds__(256) void swiglu_amax_finalize_kernel(const uint32_
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Grid of the glue kernels: x over the 256-chunk column blocks, y over rows (at most max_blocks in all,
+// unless the columns alone need more).
+dim3 glue_grid(int64_t T, int64_t F, int64_t max_blocks) {
+  if (T <= 0 || F <= 0) return dim3(0, 0, 1);
+  const int64_t gx = ((F + 7) / 8 + 255) / 256;
+  const int64_t gy = std::max<int64_t>(1, std::min<int64_t>({T, max_blocks / gx, 65535}));
+  return dim3((unsigned)gx, (unsigned)gy, 1);
+}
+
 int64_t amax_blocks(int64_t T, int64_t F) {
-  return std::min<int64_t>((T * ((F + 7) / 8) + 255) / 256, kAmaxGlueBlocks);
+  const dim3 g = glue_grid(T, F, kAmaxGlueBlocks);
+  return (int64_t)g.x * g.y;
 }
 
 }  // namespace
@@ -229,12 +242,13 @@ hipError_t launch_swiglu_backward_amax(int64_t T, int64_t F, const float* dH, in
     const bool vec = aligned16(dH) && aligned16(Ag) && aligned16(Au) && aligned16(Gg) && aligned16(Gu) &&
                      ld_dh % 4 == 0 && ld_a % 8 == 0 && ld_g % 8 == 0 && (!swg || aligned16(swg)) &&
                      (!swu || aligned16(swu));
+    const dim3 grid = glue_grid(T, F, kAmaxGlueBlocks);
     if (vec)
-      hipLaunchKernelGGL(swiglu_amax_kernel<true>, dim3((unsigned)nblk), dim3(256), 0, st, T, F, dH, ld_dh, Ag, Au,
-                         ld_a, Gg, Gu, ld_g, sx, swg, swu, part);
+      hipLaunchKernelGGL(swiglu_amax_kernel<true>, grid, dim3(256), 0, st, T, F, dH, ld_dh, Ag, Au, ld_a, Gg, Gu,
+                         ld_g, sx, swg, swu, part);
     else
-      hipLaunchKernelGGL(swiglu_amax_kernel<false>, dim3((unsigned)nblk), dim3(256), 0, st, T, F, dH, ld_dh, Ag, Au,
-                         ld_a, Gg, Gu, ld_g, sx, swg, swu, part);
+      hipLaunchKernelGGL(swiglu_amax_kernel<false>, grid, dim3(256), 0, st, T, F, dH, ld_dh, Ag, Au, ld_a, Gg, Gu,
+                         ld_g, sx, swg, swu, part);
   }
   hipLaunchKernelGGL(swiglu_amax_finalize_kernel, dim3(1), dim3(256), 0, st, part, (int)nblk, amax_bits);
   return hipGetLastError();
@@ -246,14 +260,13 @@ hipError_t launch_swiglu_backward(int64_t T, int64_t F, const float* dH, int64_t
   if (T == 0 || F == 0) return hipSuccess;
   const bool vec = aligned16(dH) && aligned16(Ag) && aligned16(Au) && aligned16(Gg) && aligned16(Gu) &&
                    ld_dh % 4 == 0 && ld_a % 8 == 0 && ld_g % 8 == 0;
-  const int64_t total = T * ((F + 7) / 8);
-  const unsigned blocks = (unsigned)std::min<int64_t>((total + 255) / 256, 8192);
+  const dim3 grid = glue_grid(T, F, 8192);
   if (vec)
-    hipLaunchKernelGGL(swiglu_backward_kernel<true>, dim3(blocks), dim3(256), 0, st, T, F, dH, ld_dh, Ag, Au, ld_a,
-                       Gg, Gu, ld_g);
+    hipLaunchKernelGGL(swiglu_backward_kernel<true>, grid, dim3(256), 0, st, T, F, dH, ld_dh, Ag, Au, ld_a, Gg, Gu,
+                       ld_g);
   else
-    hipLaunchKernelGGL(swiglu_backward_kernel<false>, dim3(blocks), dim3(256), 0, st, T, F, dH, ld_dh, Ag, Au, ld_a,
-                       Gg, Gu, ld_g);
+    hipLaunchKernelGGL(swiglu_backward_kernel<false>, grid, dim3(256), 0, st, T, F, dH, ld_dh, Ag, Au, ld_a, Gg, Gu,
+                       ld_g);
   return hipGetLastError();
 }
 
