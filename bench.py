@@ -345,7 +345,9 @@ def run_block(args, dev, torch, inputs, s3r):
                 e.record()
                 s2.wait_event(e)
 
-        def linear(name, ev):
+        sid = None if s2 is None else s2.cuda_stream
+
+        def quantize(name, ev):
             p = st[name]
             if ev:
                 ev[f"quantize_{name}"][0].record()
@@ -358,41 +360,65 @@ def run_block(args, dev, torch, inputs, s3r):
                                            p["Q"], p["delta"], p["er"], p["ec"], p["em"], p["flags"], ws_q)
             if ev:
                 ev[f"quantize_{name}"][1].record()
-            if not (pair and name == "gate"):
-                side(after_dx=False)
+
+        def dx(name, ev):
+            p = st[name]
             if ev:
                 s3r.s3r_time_next_gemm(*ev[f"dx_{name}"])
             s3r.s3r_backward_dx(p["desc"], p["Q"], p["delta"], p["fw"].Q, p["fx"].delta, p["fw"].code_colsum[0],
                                 p["er"], p["ec"], p["em"], dX_out[name], ws_b, accumulate=(name == "up"))
-            if pair and name == "gate":
-                return
-            side(after_dx=True)
-            sid = None if s2 is None else s2.cuda_stream
-            if pair and name == "up":
-                g, u = st["gate"], st["up"]
-                if ev:
-                    s3r.s3r_time_next_gemm(*ev["dw_gate_up"])
-                s3r.s3r_backward_dw_pair(g["desc"], g["Q"], u["Q"], g["delta"], u["delta"], fx.Q, g["fw"].delta,
-                                         u["fw"].delta, fx.code_colsum, (g["er"], g["ec"], g["em"]),
-                                         (u["er"], u["ec"], u["em"]), dW["gate"], dW["up"], ws_p, stream=sid)
-                return
+
+        def dw(name, ev):
+            p = st[name]
             if ev:
                 s3r.s3r_time_next_gemm(*ev[f"dw_{name}"])
             s3r.s3r_backward_dw(p["desc"], p["Q"], p["delta"], p["fx"].Q, p["fw"].delta, p["fx"].code_colsum,
                                 p["er"], p["ec"], p["em"], dW[name], ws_b2, stream=sid)
 
+        def dw_pair(ev):
+            g, u = st["gate"], st["up"]
+            if ev:
+                s3r.s3r_time_next_gemm(*ev["dw_gate_up"])
+            s3r.s3r_backward_dw_pair(g["desc"], g["Q"], u["Q"], g["delta"], u["delta"], fx.Q, g["fw"].delta,
+                                     u["fw"].delta, fx.code_colsum, (g["er"], g["ec"], g["em"]),
+                                     (u["er"], u["ec"], u["em"]), dW["gate"], dW["up"], ws_p, stream=sid)
+
         def step(ev):
             if ev:
                 ev["step"][0].record()
-            linear("down", ev)
+            quantize("down", ev)
+            side(after_dx=False)
+            dx("down", ev)
+            side(after_dx=True)
+            dw("down", ev)
             if ev:
                 ev["glue"][0].record()
             s3r.s3r_swiglu_backward_amax(dH, dv["A_gate"], dv["A_up"], Gg, Gu, fx.delta, fwg.delta, fwu.delta, amax,
                                          ws_g)
             if ev:
                 ev["glue"][1].record()
-            linear("gate", ev)
-            linear("up", ev)
+            if pair and streams == 3:
+                # both quantize calls first; the paired dW on the second stream beside both dX products
+                quantize("gate", ev)
+                quantize("up", ev)
+                side(after_dx=False)
+                dw_pair(ev)
+                dx("gate", ev)
+                dx("up", ev)
+            elif pair:
+                quantize("gate", ev)
+                dx("gate", ev)
+                quantize("up", ev)
+                dx("up", ev)
+                side(after_dx=True)
+                dw_pair(ev)
+            else:
+                for name in ("gate", "up"):
+                    quantize(name, ev)
+                    side(after_dx=False)
+                    dx(name, ev)
+                    side(after_dx=True)
+                    dw(name, ev)
             if s2 is not None:
                 e = torch.cuda.Event()
                 e.record(s2)
