@@ -807,8 +807,8 @@ def run_mx(args, dev, torch, inputs, s3r):
     desc = s3r.qdesc(T, D, S, mode, ec, s3r.PER_TENSOR, layer_id=0, seed=0)
     B = T // S
     u8 = dict(dtype=torch.uint8, device=dev)
-    Qh, Qhs = torch.empty(T, D // 2, **u8), torch.empty(D // 128, 4 * T, **u8)
-    Qt, Qts = torch.empty(D, T // 2, **u8), torch.empty(T // 128, 4 * D, **u8)
+    Qh, Qhs = s3r.mx_codes(T, D, dev), torch.empty(D // 128, 4 * T, **u8)
+    Qt, Qts = s3r.mx_codes(D, T, dev), torch.empty(T // 128, 4 * D, **u8)
     f32 = dict(dtype=torch.float32, device=dev)
     st_h = (torch.empty(T, **f32), torch.empty(B, D, **f32), torch.empty(B, **f32)) if ec else (None,) * 3
     st_t = (torch.empty(T, **f32), torch.empty(B, D, **f32), torch.empty(B, **f32)) if ec else (None,) * 3

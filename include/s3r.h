@@ -391,7 +391,16 @@ int s3r_swiglu_backward_amax(int64_t T, int64_t F, const float* dH, int64_t ld_d
  * readings (OCP microscaling MXFP4 with the page's rounding carried over):
  *   codes    E2M1 (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6; code = sign << 3 |
  *            index), two per byte, the first element in the low nibble;
- *            a matrix of R rows and K (contraction) columns is R x K/2 bytes;
+ *            a matrix of R rows and K (contraction) elements is stored in
+ *            blocks of 256 rows x 128 elements (64 bytes a row, 16384 bytes a
+ *            block, row-major inside): block (rb, kb) starts at rb * ld +
+ *            kb * 16384, so element (r, k) is the nibble k % 2 of byte
+ *            (r / 256) * ld + (k / 128) * 16384 + (r % 256) * 64 + (k % 128) / 2.
+ *            ld, the bytes between 256-row blocks, is a multiple of 16384 and
+ *            at least 128 K; the buffer holds ceil(R / 256) * ld bytes (rows
+ *            past R in the last block are never written and their contents
+ *            reach no result).  A GEMM step of a 256-row tile is then one
+ *            contiguous 16 KiB run;
  *   scales   one E8M0 byte per 32 consecutive elements along a GEMM's
  *            contraction, grouped by steps of 128: the K/128 steps are rows of
  *            ld_s bytes, step j holding R 4-byte words (row r's blocks 4j ..
@@ -417,10 +426,10 @@ int s3r_swiglu_backward_amax(int64_t T, int64_t F, const float* dH, int64_t ld_d
  *            block scales take its place).
  * Shapes: T, D and rows_per_example multiples of 128 (a 128-element step of
  * the FP4 matrix cores), T, D < 2^24; scale must be S3R_PER_TENSOR (it names
- * no scale here); mode RTNE, SR or S3R; ec requires S3R.  Byte leading
- * dimensions (ld_*) of codes are multiples of 16 with 16-byte aligned bases
- * (Q_h: a multiple of 4); of scales, multiples of 4 with 4-byte aligned
- * bases (a GEMM step reads its rows' scale words as one contiguous run).
+ * no scale here); mode RTNE, SR or S3R; ec requires S3R.  Codes: 16-byte
+ * aligned bases, ld_* as above, ceil(R / 256) * ld_* < 2^32.  Scales: byte
+ * leading dimensions that are multiples of 4 with 4-byte aligned bases (a GEMM
+ * step reads its rows' scale words as one contiguous run).
  * Device pointers throughout, row-major.
  */
 
@@ -430,9 +439,9 @@ size_t s3r_mx_workspace(const s3r_qdesc* desc, int64_t d_in);
 size_t s3r_mx_operand_workspace(int64_t rows, int64_t cols);
 
 /* s3r_mx_operand: the forward operand M [rows x cols] (f32 or bf16, ld
- * elements) to RTNE MXFP4 blocked along the rows, stored transposed: Mt
- * [cols x rows/2] codes (ld_t bytes), Mt_scales [rows/128][cols][4] (ld_ts
- * bytes per step).
+ * elements) to RTNE MXFP4 blocked along the rows, stored transposed: Mt, the
+ * codes of cols rows x rows elements (block layout, ld_t), Mt_scales
+ * [rows/128][cols][4] (ld_ts bytes per step).
  * W [D x d_in] gives Wt for dX, X [T x d_in] gives Xt for dW.  colsum
  * (optional, f32 [rows/rows_per_example x cols]): per-group column sums of the
  * dequantized operand in groups of rows_per_example rows (a multiple of 128
@@ -443,8 +452,9 @@ int s3r_mx_operand(int64_t rows, int64_t cols, int64_t rows_per_example,
                    uint8_t* Mt, int64_t ld_t, uint8_t* Mt_scales, int64_t ld_ts,
                    float* colsum, uint32_t* flags, void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* s3r_mx_quantize: G [T x D] (f32 or bf16) to Q_h (codes [T x D/2], scales
- * [D/128][T][4]) and Q_t (codes [D x T/2], scales [T/128][D][4]).  G is read
+/* s3r_mx_quantize: G [T x D] (f32 or bf16) to Q_h (codes of T rows x D
+ * elements, scales [D/128][T][4]) and Q_t (codes of D rows x T elements,
+ * scales [T/128][D][4]), codes in the block layout.  G is read
  * in 16-byte pieces: its base is 16-byte aligned and ld_g a multiple of 8
  * (bf16) or 4 (f32) elements.  With EC: the
  * statistics of each quantization's error, ec_row_* [T] (eps_t), ec_col_*

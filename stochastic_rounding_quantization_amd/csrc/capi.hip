@@ -462,6 +462,12 @@ size_t s3r_mx_workspace(const s3r_qdesc* d, int64_t d_in) {
                   mx_backward_workspace(d->rows, d->cols, d_in, d->rows / d->rows_per_example));
 }
 
+// Codes of an MXFP4 matrix in the 256-row block layout: ld (bytes between 256-row blocks) a multiple
+// of 16384 covering the K / 128 blocks of a row block, every block addressable with 32-bit offsets.
+static bool mx_codes_ok(const uint8_t* p, int64_t ld, int64_t rows, int64_t K) {
+  return p && al16(p) && ld % 16384 == 0 && ld >= 128 * K && ((rows + 255) / 256) * ld < ((int64_t)1 << 32);
+}
+
 int s3r_mx_operand(int64_t rows, int64_t cols, int64_t rows_per_example, const void* M, int32_t dtype, int64_t ld,
                    uint8_t* Mt, int64_t ld_t, uint8_t* Mt_scales, int64_t ld_ts, float* colsum, uint32_t* flags,
                    void* ws, size_t ws_bytes, hipStream_t stream) {
@@ -469,8 +475,8 @@ int s3r_mx_operand(int64_t rows, int64_t cols, int64_t rows_per_example, const v
   if (rows <= 0 || cols <= 0 || !mul_of(rows, 128) || rows >= ((int64_t)1 << 24) || cols >= ((int64_t)1 << 24))
     return S3R_ERR_INVALID_ARG;
   if (rows_per_example < 128 || rows % rows_per_example || rows_per_example % 128) return S3R_ERR_INVALID_ARG;
-  if (!M || !Mt || !Mt_scales || ld < cols || ld_t < rows / 2 || ld_ts < 4 * cols) return S3R_ERR_INVALID_ARG;
-  if ((ld_t & 15) || !al16(Mt)) return S3R_ERR_INVALID_ARG;
+  if (!M || !Mt || !Mt_scales || ld < cols || ld_ts < 4 * cols) return S3R_ERR_INVALID_ARG;
+  if (!mx_codes_ok(Mt, ld_t, cols, rows)) return S3R_ERR_INVALID_ARG;
   if (ws_bytes < s3r_mx_operand_workspace(rows, cols)) return S3R_ERR_WORKSPACE;
   if (!ws || ((uintptr_t)ws & 255u)) return S3R_ERR_INVALID_ARG;
   int rc;
@@ -491,9 +497,8 @@ int s3r_mx_quantize(const s3r_qdesc* d, const void* G, int32_t g_dtype, int64_t 
   const int64_t T = d->rows, D = d->cols;
   if (!G || !Qh || !Qh_scales || !Qt || !Qt_scales || ld_g < D) return S3R_ERR_INVALID_ARG;
   if (!al16(G) || (ld_g * (g_dtype == S3R_BF16 ? 2 : 4)) % 16) return S3R_ERR_INVALID_ARG;   // 16-byte row chunks
-  if (ld_qh < D / 2 || (ld_qh & 3) || ld_qhs < 4 * T || ld_qt < T / 2 || (ld_qt & 15) || ld_qts < 4 * D)
+  if (!mx_codes_ok(Qh, ld_qh, T, D) || ld_qhs < 4 * T || !mx_codes_ok(Qt, ld_qt, D, T) || ld_qts < 4 * D)
     return S3R_ERR_INVALID_ARG;
-  if (!al16(Qt) || ((uintptr_t)Qh & 3u)) return S3R_ERR_INVALID_ARG;
   const bool ec = d->ec != S3R_EC_NONE;
   if (ec != (ec_row_h && ec_col_h && ec_mean_h && ec_row_t && ec_col_t && ec_mean_t)) return S3R_ERR_INVALID_ARG;
   if (ws_bytes < mx_quant_workspace(T, D, ec)) return S3R_ERR_WORKSPACE;
@@ -511,9 +516,9 @@ int s3r_mx_quantize(const s3r_qdesc* d, const void* G, int32_t g_dtype, int64_t 
 }
 
 static int check_mx_operand(const uint8_t* p, int64_t ld, const uint8_t* s, int64_t lds, int64_t rows, int64_t K) {
-  if (!p || !s || !al16(p) || (ld & 15) || ld < K / 2 || ((uintptr_t)s & 3u) || (lds & 3) || lds < 4 * rows)
+  if (!mx_codes_ok(p, ld, rows, K) || !s || ((uintptr_t)s & 3u) || (lds & 3) || lds < 4 * rows)
     return S3R_ERR_INVALID_ARG;
-  if ((rows + 256) * ld >= ((int64_t)1 << 32) || (K / 128 + 1) * lds >= ((int64_t)1 << 32)) return S3R_ERR_INVALID_ARG;
+  if ((K / 128 + 1) * lds >= ((int64_t)1 << 32)) return S3R_ERR_INVALID_ARG;
   return S3R_OK;
 }
 

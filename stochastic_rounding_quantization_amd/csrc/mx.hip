@@ -32,6 +32,15 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
 constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit dword format
 
+// Code layout of every MXFP4 matrix (R rows, K contraction elements, two codes a byte): blocks of
+// 256 rows x 128 elements, 64 bytes a row and 16 KiB a block, row-major inside; block (rb, kb)
+// starts at rb * ld + kb * 16384 (ld >= 128 K, the stride between 256-row blocks). A GEMM step of
+// a 256-row tile is then one contiguous 16 KiB run, which its DMA reads in whole cache lines.
+constexpr int kMxBlkBytes = 16384;
+__device__ __forceinline__ int64_t mx_code_off(int64_t row, int64_t byte, int64_t ld) {
+  return (row >> 8) * ld + (byte >> 6) * kMxBlkBytes + (row & 255) * 64 + (byte & 63);
+}
+
 // ------------------------------------------------------ E2M1 rounding ----
 // Block exponent of amax bits (ordered fp32 bits): the smallest k with
 // a <= 6 * 2^k, clamped; returns 255 (NaN) for a non-finite max.
@@ -260,7 +269,7 @@ __global__ __launch_bounds__(256, sizeof(TIn) == 2 ? 3 : 2) void mx_quant_fused_
       }
     }
     if (act_a) {
-      *reinterpret_cast<uint4*>(Qh + t * ld_qh + ca / 2) = make_uint4(w[0], w[1], w[2], w[3]);
+      *reinterpret_cast<uint4*>(Qh + mx_code_off(t, ca / 2, ld_qh)) = make_uint4(w[0], w[1], w[2], w[3]);
       const int64_t blk = ca / 32;
       Qhs[(blk / 4) * ld_qhs + t * 4 + (blk & 3)] = (uint8_t)sb;
       any_bad |= sb == 255;
@@ -378,8 +387,8 @@ __global__ __launch_bounds__(256, sizeof(TIn) == 2 ? 3 : 2) void mx_quant_fused_
   }
   const int64_t tblk = t0 / 32 + tb;
   if (act_b) {
-    *reinterpret_cast<uint4*>(Qt + cpair * ld_qt + tblk * 16) = make_uint4(wa[0], wa[1], wa[2], wa[3]);
-    *reinterpret_cast<uint4*>(Qt + (cpair + 1) * ld_qt + tblk * 16) = make_uint4(wb[0], wb[1], wb[2], wb[3]);
+    *reinterpret_cast<uint4*>(Qt + mx_code_off(cpair, tblk * 16, ld_qt)) = make_uint4(wa[0], wa[1], wa[2], wa[3]);
+    *reinterpret_cast<uint4*>(Qt + mx_code_off(cpair + 1, tblk * 16, ld_qt)) = make_uint4(wb[0], wb[1], wb[2], wb[3]);
     uint8_t* sp = Qts + (tblk / 4) * ld_qts + cpair * 4 + (tblk & 3);
     sp[0] = (uint8_t)sba;
     sp[4] = (uint8_t)sbb;
@@ -426,7 +435,7 @@ __global__ __launch_bounds__(256) void mx_operand_kernel(MxQuant p, const TIn* _
   float e[32];
   const int sb = mx_block<VSUM, true>(v, R, w, e);
   if (active) {
-    *reinterpret_cast<uint4*>(out + c * ld_out + t0 / 2) = make_uint4(w[0], w[1], w[2], w[3]);
+    *reinterpret_cast<uint4*>(out + mx_code_off(c, t0 / 2, ld_out)) = make_uint4(w[0], w[1], w[2], w[3]);
     sc[(t0 / 128) * ld_s + c * 4 + ((t0 / 32) & 3)] = (uint8_t)sb;
     if (sb == 255 && flags) atomicOr(flags, S3R_FLAG_NONFINITE);
     if constexpr (VSUM) {
@@ -495,15 +504,16 @@ __global__ __launch_bounds__(256) void mx_mean_kernel(int64_t S, const float* __
 }
 
 // ------------------------------------------------------------- FP4 GEMM ----
-// out [M x N] (f32) = A [M x K] . B [N x K]^T with both operands MXFP4 and
-// K-major: codes 2 per byte (ld in bytes), E8M0 scales [K/128][rows][4].  256 x
-// 256 tile per 256-thread workgroup, four waves of 128 x 128 (4 x 4 blocks of
-// v_mfma_scale_f32_32x32x64_f8f6f4).  A stage covers 256 elements of K: the A
-// and B tiles are 256 rows x 128 bytes each (a whole cache line per row and
-// stage, 16-byte chunks swizzled as c ^ f(row)) plus the rows' scale words of
-// the stage's two 128-element steps, all moved global -> LDS by buffer-load
-// DMA; two stages alternate, the next one loading while the current one feeds
-// 64 MFMAs per wave.
+// out [M x N] (f32) = A [M x K] . B [N x K]^T with both operands MXFP4: codes in
+// the 256-row block layout (ld: the bytes between 256-row blocks), E8M0 scales
+// [K/128][rows][4].  256 x 256 tile per 256-thread workgroup, four waves of 128
+// x 128 (4 x 4 blocks of v_mfma_scale_f32_32x32x64_f8f6f4).  A stage covers 256
+// elements of K: the A and B tiles are two consecutive 16 KiB code blocks each,
+// one contiguous 32 KiB run per operand, plus the rows' scale words of the
+// stage's two 128-element steps, all moved global -> LDS by buffer-load DMA;
+// two stages alternate, the next one loading while the current one feeds 64
+// MFMAs per wave.  (Four single-step stages, loads issued three steps ahead,
+// were 6 % slower: half the MFMA work between barriers.)
 // Operand lane layout of the FP4 MFMA (checked on the device): lane l holds row
 // (or column) l % 32 and K elements 32 (l / 32) .. + 31, 16 bytes, the first in
 // the low nibble; byte 0 of its scale register is that (row, K block)'s E8M0.
@@ -537,32 +547,37 @@ struct MxEpi {
   float* out; int64_t ld_out;
 };
 
-// Position of 16-byte chunk c (0..7) of a 128-byte tile row: eight consecutive rows put a
-// given chunk in eight different 16-byte bank groups, and rows r, r + 8 in different ones.
-__device__ __forceinline__ int mx_pos(int r, int c) { return c ^ (r & 7) ^ ((r >> 3) & 1); }
+// LDS layout of a stage's A (and, 32 KiB on, B) tile: the two steps' 16 KiB blocks as they lie in
+// memory, [step][256 rows][64 bytes], with the four 16-byte chunks of a row at permuted positions:
+// chunk q of row r at position q ^ ((r >> 2) & 3), so the 16 rows of a quarter-wave's 16-byte read
+// hit 16 different bank groups.
+__device__ __forceinline__ int mx_pos(int r, int q) { return q ^ ((r >> 2) & 3); }
 
 struct MxRsrc { __amdgpu_buffer_rsrc_t a, b, sa, sb, z; int nk, ns; };
 
-// Stage ks (K elements 256 ks ..): each wave moves 8 row-blocks of 8 rows x 128 bytes of A
-// and of B (lane l: row 8 blk + l / 8, the chunk that belongs at position l % 8) and its
-// 64 rows' scale words of both steps.  Past the last stage every load goes through an empty
-// descriptor (zeros); a step past K within the last stage loads zero scales and codes that
-// are never multiplied (its MFMAs are skipped).
+// Stage ks (K elements 256 ks ..., code blocks 2 ks and 2 ks + 1 of the tile's 256-row block):
+// each wave moves 8 KiB of A and of B, eight 1 KiB pieces of 16 rows x 64 bytes (piece p: step
+// p >> 4, rows 16 (p & 15) ..; lane l lands at LDS offset 16 l of the piece and loads the chunk
+// that belongs there), and its 64 rows' scale words of both steps.  Past the last stage every load
+// goes through an empty descriptor (zeros); a step past K within the last stage loads zero scales
+// and codes that are never multiplied (its MFMAs are skipped).
 __device__ __forceinline__ void mx_load_stage(const MxGemm& g, uint8_t* st, int64_t m0, int64_t n0, int ks,
                                               const MxRsrc& r) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const bool live = ks < r.ns;
   const __amdgpu_buffer_rsrc_t ra = live ? r.a : r.z, rb = live ? r.b : r.z;
+  const uint32_t a_blk = (uint32_t)((m0 >> 8) * g.lda), b_blk = (uint32_t)((n0 >> 8) * g.ldb);
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
-    const int blk = wave * 8 + q;
-    const int row = blk * 8 + (lane >> 3);
-    const int c = mx_pos(row, lane & 7);             // the position map is an involution
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(st + blk * 1024), 16,
-                                             (uint32_t)((m0 + row) * g.lda + c * 16), (uint32_t)ks * 128u, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(st + 32768 + blk * 1024), 16,
-                                             (uint32_t)((n0 + row) * g.ldb + c * 16), (uint32_t)ks * 128u, 0, 0);
+    const int piece = wave * 8 + q;
+    const int step = piece >> 4;
+    const int row = (piece & 15) * 16 + (lane >> 2);
+    const uint32_t off = (uint32_t)(step * kMxBlkBytes + row * 64 + mx_pos(row, lane & 3) * 16);   // an involution
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(st + piece * 1024), 16, a_blk + off,
+                                             (uint32_t)ks * (2u * kMxBlkBytes), 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(st + 32768 + piece * 1024), 16, b_blk + off,
+                                             (uint32_t)ks * (2u * kMxBlkBytes), 0, 0);
   }
 #pragma unroll
   for (int sub = 0; sub < 2; ++sub) {
@@ -582,7 +597,8 @@ __device__ __forceinline__ void mx_load_stage(const MxGemm& g, uint8_t* st, int6
 constexpr int kMxSgMfma = 0x008, kMxSgDsRead = 0x100, kMxSgVmem = 0x010;
 
 // Fragments of half-step h (0..3: K elements 64 h .. 64 h + 63 of the stage): lane l holds
-// rows (columns) i * 32 + l % 32 of its wave's 128, the 16 bytes of chunk 2 h + l / 32.
+// rows (columns) i * 32 + l % 32 of its wave's 128, the 16 bytes of chunk 2 h + l / 32 of the
+// stage's row (chunk c in step c / 4).
 struct MxFrag { v8i a[4], b[4]; };
 
 __device__ __forceinline__ void mx_read_frag(const uint8_t* st, int h, MxFrag& f) {
@@ -592,8 +608,9 @@ __device__ __forceinline__ void mx_read_frag(const uint8_t* st, int h, MxFrag& f
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int ra_ = wm * 128 + i * 32 + r31, rb_ = wn * 128 + i * 32 + r31;
-    const uint4 x = *reinterpret_cast<const uint4*>(st + ra_ * 128 + (mx_pos(ra_, c) << 4));
-    const uint4 y = *reinterpret_cast<const uint4*>(st + 32768 + rb_ * 128 + (mx_pos(rb_, c) << 4));
+    const int blk = (c >> 2) * kMxBlkBytes;
+    const uint4 x = *reinterpret_cast<const uint4*>(st + blk + ra_ * 64 + (mx_pos(ra_, c & 3) << 4));
+    const uint4 y = *reinterpret_cast<const uint4*>(st + 32768 + blk + rb_ * 64 + (mx_pos(rb_, c & 3) << 4));
     f.a[i] = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
     f.b[i] = v8i{(int)y.x, (int)y.y, (int)y.z, (int)y.w, 0, 0, 0, 0};
   }
@@ -679,9 +696,12 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_kernel(MxGemm g, MxEpi ep) {
   const int tm = first_m + (bid % group) % gsz, tn = (bid % group) / gsz;
   const int64_t m0 = (int64_t)tm * 256, n0 = (int64_t)tn * 256;
   const int nk = (int)(g.K / 128);
-  // descriptors over whole operands: rows past M (N) read zeros
-  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)g.A, (short)0, (int)(uint32_t)(g.M * g.lda), kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc((void*)g.B, (short)0, (int)(uint32_t)(g.N * g.ldb), kRsrcWord3);
+  // descriptors over whole operands, every 256-row block of codes (rows past M or N inside the last
+  // block reach only outputs that are not stored)
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)g.A, (short)0, (int)(uint32_t)(((g.M + 255) >> 8) * g.lda), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)g.B, (short)0, (int)(uint32_t)(((g.N + 255) >> 8) * g.ldb), kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc((void*)g.As, (short)0, (int)(uint32_t)(nk * g.ldas), kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc((void*)g.Bs, (short)0, (int)(uint32_t)(nk * g.ldbs), kRsrcWord3);
 
@@ -740,24 +760,29 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_kernel(MxGemm g, MxEpi ep) {
   const uint32_t ld4 = (uint32_t)ep.ld_out * 4u;
   const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(ep.out + m0 * ep.ld_out), (short)0, (int)((uint32_t)rows_here * ld4), kRsrcWord3);
+  // per-column values, loaded from a clamped column without a branch and waited for once here: a
+  // load still pending inside the store loop would make each group of stores wait for every store
+  // before it (vmcnt counts stores too)
   float cA[4], cU[4], xsb[4][NB];
   bool n_ok[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int64_t n = n0 + wn * 128 + j * 32 + r31;
     n_ok[j] = n < g.N;
+    const int64_t nc = n_ok[j] ? n : 0;
     cA[j] = 0.f; cU[j] = 0.f;
 #pragma unroll
     for (int b = 0; b < NB; ++b) xsb[j][b] = 0.f;
-    if (EC && n_ok[j]) {
-      if constexpr (!DW) cA[j] = ep.rW[n];
+    if constexpr (EC) {
+      if constexpr (!DW) cA[j] = ep.rW[nc];
       else {
-        cU[j] = ep.u[n];
+        cU[j] = ep.u[nc];
 #pragma unroll
-        for (int b = 0; b < NB; ++b) xsb[j][b] = b < ep.B ? ep.xs[b * g.N + n] : 0.f;
+        for (int b = 0; b < NB; ++b) xsb[j][b] = ep.xs[(b < ep.B ? b : 0) * g.N + nc] * (b < ep.B ? 1.f : 0.f);
       }
     }
   }
+  S3R_MX_WAIT_VM(0);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -860,7 +885,7 @@ __global__ __launch_bounds__(256) void mx_rowdot_kernel(const uint8_t* __restric
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
       const int64_t n = min((((int64_t)blockIdx.x * RG + g) * 4 + wave) * RPW + r, N - 1);
-      wr[g][r] = kv ? *reinterpret_cast<const uint4*>(P + n * ldp + k / 2) : make_uint4(0u, 0u, 0u, 0u);
+      wr[g][r] = kv ? *reinterpret_cast<const uint4*>(P + mx_code_off(n, k / 2, ldp)) : make_uint4(0u, 0u, 0u, 0u);
       sbr[g][r] = kv ? (int)Ps[(k / 128) * ldps + n * 4 + ((k / 32) & 3)] : 127;
     }
 #pragma unroll

@@ -347,10 +347,10 @@ def s3r_mx_operand_workspace(rows: int, cols: int) -> int:
 
 def s3r_mx_operand(M, Mt, Mt_scales, colsum=None, rows_per_example=None, flags=None, ws=None, stream=None, *,
                    rc_only=False):
-    """M [rows x cols] f32/bf16 -> Mt uint8 [cols x rows/2], Mt_scales uint8 [rows/128 x 4*cols] (step-grouped)."""
+    """M [rows x cols] f32/bf16 -> Mt (mx_codes(cols, rows)), Mt_scales uint8 [rows/128 x 4*cols] (step-grouped)."""
     rows, cols = M.shape
     S = rows if rows_per_example is None else rows_per_example
-    rc = lib().s3r_mx_operand(rows, cols, S, _ptr(M), _gdtype(M), _ld(M, cols), _ptr(Mt), _ld(Mt, rows // 2),
+    rc = lib().s3r_mx_operand(rows, cols, S, _ptr(M), _gdtype(M), _ld(M, cols), _ptr(Mt), _ld(Mt),
                               _ptr(Mt_scales), _ld(Mt_scales, 4 * cols), _ptr(colsum), _ptr(flags), _ptr(ws),
                               _nbytes(ws), _stream(stream))
     if rc_only:
@@ -363,8 +363,8 @@ def s3r_mx_quantize(desc: QDesc, G, Qh, Qh_scales, Qt, Qt_scales, ec_row_h=None,
                     rc_only=False):
     T, D = desc.rows, desc.cols
     rc = lib().s3r_mx_quantize(ctypes.byref(desc), _ptr(G), _gdtype(G) if G is not None else S3R_F32, _ld(G, D),
-                               _ptr(Qh), _ld(Qh, D // 2), _ptr(Qh_scales), _ld(Qh_scales, 4 * T), _ptr(Qt),
-                               _ld(Qt, T // 2), _ptr(Qt_scales), _ld(Qt_scales, 4 * D), _ptr(ec_row_h),
+                               _ptr(Qh), _ld(Qh), _ptr(Qh_scales), _ld(Qh_scales, 4 * T), _ptr(Qt),
+                               _ld(Qt), _ptr(Qt_scales), _ld(Qt_scales, 4 * D), _ptr(ec_row_h),
                                _ptr(ec_col_h), _ptr(ec_mean_h), _ptr(ec_row_t), _ptr(ec_col_t), _ptr(ec_mean_t),
                                _ptr(flags), _ptr(ws), _nbytes(ws), _stream(stream))
     if rc_only:
@@ -374,11 +374,10 @@ def s3r_mx_quantize(desc: QDesc, G, Qh, Qh_scales, Qt, Qt_scales, ec_row_h=None,
 
 def s3r_mx_backward_dx(desc: QDesc, Qh, Qh_scales, Wt, Wt_scales, r_W, ec_row_h, ec_col_h, ec_mean_h, dX, ws=None,
                        stream=None, *, rc_only=False):
-    """Wt uint8 [d_in x D/2] codes, Wt_scales [D/128 x 4*d_in]; dX f32 [T x d_in]."""
+    """Wt: mx_codes(d_in, D), Wt_scales [D/128 x 4*d_in]; dX f32 [T x d_in]."""
     d_in = dX.shape[1]
-    D = desc.cols
-    rc = lib().s3r_mx_backward_dx(ctypes.byref(desc), _ptr(Qh), _ld(Qh, D // 2), _ptr(Qh_scales),
-                                  _ld(Qh_scales, 4 * desc.rows), _ptr(Wt), _ld(Wt, D // 2), _ptr(Wt_scales),
+    rc = lib().s3r_mx_backward_dx(ctypes.byref(desc), _ptr(Qh), _ld(Qh), _ptr(Qh_scales),
+                                  _ld(Qh_scales, 4 * desc.rows), _ptr(Wt), _ld(Wt), _ptr(Wt_scales),
                                   _ld(Wt_scales, 4 * d_in), d_in, _ptr(r_W), _ptr(ec_row_h), _ptr(ec_col_h),
                                   _ptr(ec_mean_h), _ptr(dX), _ld(dX, d_in), _ptr(ws), _nbytes(ws), _stream(stream))
     if rc_only:
@@ -388,11 +387,10 @@ def s3r_mx_backward_dx(desc: QDesc, Qh, Qh_scales, Wt, Wt_scales, r_W, ec_row_h,
 
 def s3r_mx_backward_dw(desc: QDesc, Qt, Qt_scales, Xt, Xt_scales, xs, ec_row_t, ec_col_t, ec_mean_t, dW, ws=None,
                        stream=None, *, rc_only=False):
-    """Xt uint8 [d_in x T/2] codes, Xt_scales [T/128 x 4*d_in]; dW f32 [D x d_in]."""
+    """Xt: mx_codes(d_in, T), Xt_scales [T/128 x 4*d_in]; dW f32 [D x d_in]."""
     d_in = dW.shape[1]
-    T = desc.rows
-    rc = lib().s3r_mx_backward_dw(ctypes.byref(desc), _ptr(Qt), _ld(Qt, T // 2), _ptr(Qt_scales),
-                                  _ld(Qt_scales, 4 * desc.cols), _ptr(Xt), _ld(Xt, T // 2), _ptr(Xt_scales),
+    rc = lib().s3r_mx_backward_dw(ctypes.byref(desc), _ptr(Qt), _ld(Qt), _ptr(Qt_scales),
+                                  _ld(Qt_scales, 4 * desc.cols), _ptr(Xt), _ld(Xt), _ptr(Xt_scales),
                                   _ld(Xt_scales, 4 * d_in), d_in, _ptr(xs), _ptr(ec_row_t), _ptr(ec_col_t),
                                   _ptr(ec_mean_t), _ptr(dW), _ld(dW, d_in), _ptr(ws), _nbytes(ws), _stream(stream))
     if rc_only:
@@ -519,11 +517,18 @@ def backward_dw_pair(qa: Quantized, qb: Quantized, Xq, s_w_a=None, s_w_b=None, x
 
 # ------------------------------------------------------------ MXFP4 helpers ----
 
+def mx_codes(rows: int, K: int, device):
+    """uint8 buffer for the MXFP4 codes of a rows x K matrix in the library's block layout:
+    [ceil(rows/256) x 128*K], one row per 256-row block (its stride is the layout's ld)."""
+    import torch
+    return torch.empty((rows + 255) // 256, 128 * K, dtype=torch.uint8, device=device)
+
+
 @dataclass
 class MxQuantized:
-    Qh: object           # uint8 [T x D/2] E2M1 codes, blocks along D
+    Qh: object           # mx_codes(T, D): E2M1 codes, blocks along D
     Qh_scales: object    # uint8 [D/128 x 4T] E8M0, step-grouped
-    Qt: object           # uint8 [D x T/2] codes of G^T, blocks along T
+    Qt: object           # mx_codes(D, T): codes of G^T, blocks along T
     Qt_scales: object    # uint8 [T/128 x 4D]
     desc: QDesc
     ec_h: tuple = (None, None, None)   # (eps_t [T], ebar [B x D], mu [B]) of Q_h's error
@@ -539,8 +544,8 @@ def mx_quantize(G, *, mode=S3R, ec=EC_NONE, seed=0, layer_id=0, rows_per_example
     dev = G.device
     B = T // desc.rows_per_example
     u8 = dict(dtype=torch.uint8, device=dev)
-    Qh, Qhs = torch.empty(T, D // 2, **u8), torch.empty(D // 128, 4 * T, **u8)
-    Qt, Qts = torch.empty(D, T // 2, **u8), torch.empty(T // 128, 4 * D, **u8)
+    Qh, Qhs = mx_codes(T, D, G.device), torch.empty(D // 128, 4 * T, **u8)
+    Qt, Qts = mx_codes(D, T, G.device), torch.empty(T // 128, 4 * D, **u8)
     ec_h = ec_t = (None, None, None)
     if ec != EC_NONE:
         f32 = dict(dtype=torch.float32, device=dev)
@@ -558,7 +563,7 @@ def mx_operand(M, rows_per_example=None, colsum=True, stream=None):
     rows, cols = M.shape
     S = rows if rows_per_example is None else rows_per_example
     dev = M.device
-    Mt = torch.empty(cols, rows // 2, dtype=torch.uint8, device=dev)
+    Mt = mx_codes(cols, rows, dev)
     Mts = torch.empty(rows // 128, 4 * cols, dtype=torch.uint8, device=dev)
     cs = torch.empty(rows // S, cols, dtype=torch.float32, device=dev) if colsum else None
     ws = _workspace(s3r_mx_operand_workspace(rows, cols), dev)
@@ -568,15 +573,17 @@ def mx_operand(M, rows_per_example=None, colsum=True, stream=None):
 
 def mx_backward_dx(q: MxQuantized, Wt, Wt_scales, r_W=None, stream=None):
     import torch
-    dX = torch.empty(q.desc.rows, Wt.shape[0], dtype=torch.float32, device=Wt.device)
-    ws = _workspace(s3r_mx_workspace(q.desc, Wt.shape[0]), Wt.device)
+    d_in = Wt_scales.shape[1] // 4
+    dX = torch.empty(q.desc.rows, d_in, dtype=torch.float32, device=Wt.device)
+    ws = _workspace(s3r_mx_workspace(q.desc, d_in), Wt.device)
     s3r_mx_backward_dx(q.desc, q.Qh, q.Qh_scales, Wt, Wt_scales, r_W, *q.ec_h, dX, ws, stream)
     return dX
 
 
 def mx_backward_dw(q: MxQuantized, Xt, Xt_scales, xs=None, stream=None):
     import torch
-    dW = torch.empty(q.desc.cols, Xt.shape[0], dtype=torch.float32, device=Xt.device)
-    ws = _workspace(s3r_mx_workspace(q.desc, Xt.shape[0]), Xt.device)
+    d_in = Xt_scales.shape[1] // 4
+    dW = torch.empty(q.desc.cols, d_in, dtype=torch.float32, device=Xt.device)
+    ws = _workspace(s3r_mx_workspace(q.desc, d_in), Xt.device)
     s3r_mx_backward_dw(q.desc, q.Qt, q.Qt_scales, Xt, Xt_scales, xs, *q.ec_t, dW, ws, stream)
     return dW

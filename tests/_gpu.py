@@ -91,6 +91,13 @@ def gpu_linear(inp: dict, *, mode, ec, scale=s3r.PER_TENSOR, seed=0, layer_id=0,
     return {"fx": fx, "fw": fw, "q": q, "dX": dX, "dW": dW}
 
 
+def mx_rows(codes, rows: int, K: int) -> np.ndarray:
+    """MXFP4 codes in the library's block layout (256-row x 128-element blocks of 16 KiB, one
+    256-row block per tensor row) as plain row-major bytes [rows x K/2], on the host."""
+    a = host(codes).reshape(-1, K // 128, 256, 64)
+    return a.transpose(0, 2, 1, 3).reshape(-1, K // 2)[:rows]
+
+
 def assert_nan_equal(got, exp, what=""):
     got = np.asarray(got)
     exp = np.asarray(exp)

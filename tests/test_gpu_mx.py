@@ -12,7 +12,7 @@ import torch
 
 from oracle import mx, quantize as oq
 from stochastic_rounding_quantization_amd import inputs, s3r
-from tests._gpu import DEV, assert_rows_close, host, rel_err, to_dev
+from tests._gpu import DEV, assert_rows_close, host, mx_rows, rel_err, to_dev
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-5
@@ -60,13 +60,15 @@ def step_grouped(scale):
 
 def _check_quant(gpu, ref):
     q = gpu["q"]
-    np.testing.assert_array_equal(host(q.Qh), mx.pack(ref["qh"]["codes"]))
+    T, D = q.desc.rows, q.desc.cols
+    d_in = gpu["Wts"].shape[1] // 4
+    np.testing.assert_array_equal(mx_rows(q.Qh, T, D), mx.pack(ref["qh"]["codes"]))
     np.testing.assert_array_equal(host(q.Qh_scales), step_grouped(ref["qh"]["scale"]))
-    np.testing.assert_array_equal(host(q.Qt), mx.pack(ref["qt"]["codes"].T))
+    np.testing.assert_array_equal(mx_rows(q.Qt, D, T), mx.pack(ref["qt"]["codes"].T))
     np.testing.assert_array_equal(host(q.Qt_scales), step_grouped(ref["qt"]["scale"]))
-    np.testing.assert_array_equal(host(gpu["Wt"]), mx.pack(ref["fw"]["codes"].T))
+    np.testing.assert_array_equal(mx_rows(gpu["Wt"], d_in, D), mx.pack(ref["fw"]["codes"].T))
     np.testing.assert_array_equal(host(gpu["Wts"]), step_grouped(ref["fw"]["scale"]))
-    np.testing.assert_array_equal(host(gpu["Xt"]), mx.pack(ref["fx"]["codes"].T))
+    np.testing.assert_array_equal(mx_rows(gpu["Xt"], d_in, T), mx.pack(ref["fx"]["codes"].T))
     np.testing.assert_array_equal(host(gpu["Xts"]), step_grouped(ref["fx"]["scale"]))
     assert int(host(q.flags)[0]) == 0
 
@@ -145,12 +147,12 @@ def test_mx_headline_workload_sampled():
     ref = mx.backward(_f32(inp, "G"), _f32(inp, "X"), _f32(inp, "W"), mode=oq.S3R, ec=oq.EC_TWO_WAY,
                       rows_per_example=S, seed=0, dx_rows=rows, dw_rows=crow, cols=cols)
     q = gpu["q"]
-    np.testing.assert_array_equal(host(q.Qh), mx.pack(ref["qh"]["codes"]))
+    np.testing.assert_array_equal(mx_rows(q.Qh, T, D), mx.pack(ref["qh"]["codes"]))
     np.testing.assert_array_equal(host(q.Qh_scales), step_grouped(ref["qh"]["scale"]))
-    np.testing.assert_array_equal(host(q.Qt), mx.pack(ref["qt"]["codes"].T))
+    np.testing.assert_array_equal(mx_rows(q.Qt, D, T), mx.pack(ref["qt"]["codes"].T))
     np.testing.assert_array_equal(host(q.Qt_scales), step_grouped(ref["qt"]["scale"]))
-    np.testing.assert_array_equal(host(gpu["Wt"][cols]), mx.pack(ref["fw"]["codes"].T))
-    np.testing.assert_array_equal(host(gpu["Xt"][cols]), mx.pack(ref["fx"]["codes"].T))
+    np.testing.assert_array_equal(mx_rows(gpu["Wt"], d_in, D)[cols], mx.pack(ref["fw"]["codes"].T))
+    np.testing.assert_array_equal(mx_rows(gpu["Xt"], d_in, T)[cols], mx.pack(ref["fx"]["codes"].T))
     for nm, st in (("h", q.ec_h), ("t", q.ec_t)):
         assert rel_err(host(st[0]), ref["eps_" + nm]) < TOL, nm
         assert rel_err(host(st[1]), ref["ebar_" + nm]) < TOL, nm

@@ -244,9 +244,10 @@ def test_mx_argument_errors(L):
     ok = s3r.qdesc(T, D, 128, s3r.S3R, s3r.EC_TWO_WAY)
     ec6 = [P(4096 * (i + 1)) for i in range(6)]
 
+    # codes: ld is the byte stride between 256-row blocks, a multiple of 16384 and at least 128 K
     def q(desc, G=P(1 << 20), Qh=P(1 << 21), Qt=P(1 << 22), ld_qt=None, ec=ec6, wsb=1 << 24, ws=P(1 << 23)):
-        return L.s3r_mx_quantize(ctypes.byref(desc), G, 0, desc.cols, Qh, desc.cols // 2, P(1 << 19),
-                                 4 * desc.rows, Qt, desc.rows // 2 if ld_qt is None else ld_qt, P(1 << 18),
+        return L.s3r_mx_quantize(ctypes.byref(desc), G, 0, desc.cols, Qh, 128 * desc.cols, P(1 << 19),
+                                 4 * desc.rows, Qt, 128 * desc.rows if ld_qt is None else ld_qt, P(1 << 18),
                                  4 * desc.cols, *ec, None, ws, wsb, None)
 
     assert q(s3r.qdesc(T, 96, 128, s3r.S3R)) == -1                      # D not a multiple of 128
@@ -255,19 +256,20 @@ def test_mx_argument_errors(L):
     assert q(s3r.qdesc(T, D, 128, s3r.SR, s3r.EC_TWO_WAY)) == -2        # EC needs S3R
     assert q(s3r.qdesc(T, D, 128, s3r.S3R, scale=s3r.PER_TOKEN)) == -2
     assert q(ok, ec=[None] * 6) == -1                                   # statistics outputs missing
-    assert q(s3r.qdesc(T, D, 128, s3r.S3R), ec=[None] * 6, ld_qt=T // 2 + 8) == -1   # Qt ld not 16-aligned
+    assert q(s3r.qdesc(T, D, 128, s3r.S3R), ec=[None] * 6, ld_qt=128 * T + 16) == -1   # block stride not 16 KiB-aligned
+    assert q(s3r.qdesc(T, D, 128, s3r.S3R), ec=[None] * 6, ld_qt=128 * T - 16384) == -1  # below 128 K
     assert q(ok, Qt=P((1 << 22) + 8)) == -1                              # Qt base not 16-aligned
     assert q(ok, G=P((1 << 20) + 4)) == -1                               # G not 16-byte aligned
     assert q(ok, wsb=16) == -3
     assert q(ok, ws=P((1 << 23) + 64)) == -1
     assert s3r.s3r_mx_workspace(s3r.qdesc(T, 96, 128), d_in) == 0
 
-    def dx(desc, ld_wt=D // 2, ldws=4 * d_in, Wt=P(1 << 24), ec=True, wsb=1 << 24):
+    def dx(desc, ld_wt=128 * D, ldws=4 * d_in, Wt=P(1 << 24), ec=True, wsb=1 << 24):
         e = ec6[:3] if ec else [None] * 3
-        return L.s3r_mx_backward_dx(ctypes.byref(desc), P(1 << 20), D // 2, P(1 << 19), 4 * T, Wt, ld_wt,
+        return L.s3r_mx_backward_dx(ctypes.byref(desc), P(1 << 20), 128 * D, P(1 << 19), 4 * T, Wt, ld_wt,
                                     P(1 << 18), ldws, d_in, ec6[3], *e, P(1 << 25), d_in, P(1 << 23), wsb, None)
 
-    assert dx(ok, ld_wt=D // 2 - 16) == -1                              # codes ld below K/2
+    assert dx(ok, ld_wt=D // 2) == -1                                   # a plain row stride is not the layout
     assert dx(ok, ldws=4 * d_in - 4) == -1                              # scale step stride below 4 rows
     assert dx(ok, Wt=P((1 << 24) + 4)) == -1
     assert dx(ok, ec=False) == -1                                       # TWO_WAY needs the statistics
@@ -275,19 +277,19 @@ def test_mx_argument_errors(L):
 
     def dw(desc, xs=ec6[3]):
         R = desc.rows
-        return L.s3r_mx_backward_dw(ctypes.byref(desc), P(1 << 20), R // 2, P(1 << 19), 4 * D, P(1 << 24),
-                                    R // 2, P(1 << 18), 4 * d_in, d_in, xs, *ec6[:3], P(1 << 25), d_in, P(1 << 23),
-                                    1 << 24, None)
+        return L.s3r_mx_backward_dw(ctypes.byref(desc), P(1 << 20), 128 * R, P(1 << 19), 4 * D, P(1 << 24),
+                                    128 * R, P(1 << 18), 4 * d_in, d_in, xs, *ec6[:3], P(1 << 25), d_in,
+                                    P(1 << 23), 1 << 24, None)
 
     assert dw(ok, xs=None) == -1
     assert dw(s3r.qdesc(128 * 9, D, 128, s3r.S3R, s3r.EC_TWO_WAY)) in (-4, -5)  # nine examples: accepted
     assert dw(s3r.qdesc(128 * 9, D, 128, s3r.S3R, s3r.EC_DX_ONLY)) in (-4, -5)  # dW uncorrected: any B
 
-    def op(rows=T, cols=d_in, S=T, ld_t=T // 2, wsb=1 << 20):
+    def op(rows=T, cols=d_in, S=T, ld_t=128 * T, wsb=1 << 20):
         return L.s3r_mx_operand(rows, cols, S, P(1 << 20), 0, cols, P(1 << 21), ld_t, P(1 << 19), 4 * cols,
                                 None, None, P(1 << 23), wsb, None)
 
-    assert op(rows=200) == -1 and op(S=96) == -1 and op(ld_t=T // 2 - 16) == -1 and op(ld_t=T // 2 + 4) == -1
+    assert op(rows=200) == -1 and op(S=96) == -1 and op(ld_t=T // 2) == -1 and op(ld_t=128 * T + 4) == -1
     assert op(wsb=8) == -3
     assert op() in (-4, -5)
 
@@ -301,16 +303,17 @@ def test_mx_binding_marshals_valid_arguments(L):
     ws = _FakeDev((s3r.s3r_mx_workspace(desc, d_in),), (1,), addr=1 << 24)
     f32 = lambda *shape: _FakeDev(shape, tuple(int(np.prod(shape[i + 1:])) for i in range(len(shape))), elem=4)
     u8 = lambda r, c: _FakeDev((r, c), (c, 1), dtype=torch.uint8)
+    codes = lambda rows, K: u8((rows + 255) // 256, 128 * K)     # the block layout's shape (s3r.mx_codes)
     st = (f32(T), f32(2, D), f32(2))
     expect = (-4, -5)
-    assert s3r.s3r_mx_quantize(desc, f32(T, D), u8(T, D // 2), u8(D // 128, 4 * T), u8(D, T // 2), u8(T // 128, 4 * D),
+    assert s3r.s3r_mx_quantize(desc, f32(T, D), codes(T, D), u8(D // 128, 4 * T), codes(D, T), u8(T // 128, 4 * D),
                                *st, *st, None, ws, 0, rc_only=True) in expect
-    assert s3r.s3r_mx_backward_dx(desc, u8(T, D // 2), u8(D // 128, 4 * T), u8(d_in, D // 2), u8(D // 128, 4 * d_in),
+    assert s3r.s3r_mx_backward_dx(desc, codes(T, D), u8(D // 128, 4 * T), codes(d_in, D), u8(D // 128, 4 * d_in),
                                   f32(d_in), *st, f32(T, d_in), ws, 0, rc_only=True) in expect
-    assert s3r.s3r_mx_backward_dw(desc, u8(D, T // 2), u8(T // 128, 4 * D), u8(d_in, T // 2), u8(T // 128, 4 * d_in),
+    assert s3r.s3r_mx_backward_dw(desc, codes(D, T), u8(T // 128, 4 * D), codes(d_in, T), u8(T // 128, 4 * d_in),
                                   f32(2, d_in), *st, f32(D, d_in), ws, 0, rc_only=True) in expect
     ows = _FakeDev((s3r.s3r_mx_operand_workspace(T, d_in),), (1,), addr=1 << 24)
-    assert s3r.s3r_mx_operand(f32(T, d_in), u8(d_in, T // 2), u8(T // 128, 4 * d_in), f32(2, d_in), 128, None, ows, 0,
+    assert s3r.s3r_mx_operand(f32(T, d_in), codes(d_in, T), u8(T // 128, 4 * d_in), f32(2, d_in), 128, None, ows, 0,
                               rc_only=True) in expect
 
 
