@@ -843,7 +843,7 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_kernel(MxGemm g, MxEpi ep) {
 // reduce-scatter of the RPW x NB sums across the wave, and mx_sum_parts over
 // the chunks.
 typedef float v2f __attribute__((ext_vector_type(2)));
-constexpr int kRdChunk = 2048;
+constexpr int kRdChunk = 2048;   // 64 lanes x one 32-element block each
 
 template <int NB, int RPW, int RG>
 __global__ __launch_bounds__(256) void mx_rowdot_kernel(const uint8_t* __restrict__ P, int64_t ldp,
@@ -1092,7 +1092,7 @@ void run_rowdot(const MxBwArgs& a, int64_t N, int64_t K, int nb, const float* co
   const int nkc = (int)((K + kRdChunk - 1) / kRdChunk);
   float* dst = nkc == 1 ? out : part;
   constexpr int RPW = 4;                               // 16 rows per group, each wave's loads in flight together
-  constexpr int RG = 4;                                // groups per block: the staged coefficients serve 64 rows
+  constexpr int RG = 1;                                // one group per block: 16 rows (4 or 2 groups: 16-20 % slower)
   hipLaunchKernelGGL((mx_rowdot_kernel<NB, RPW, RG>),
                      dim3((unsigned)((N + 4 * RPW * RG - 1) / (4 * RPW * RG)), (unsigned)nkc), dim3(256), 0, st,
                      a.B, a.ldb, a.Bs, a.ldbs, N, K, nb, coef, dst);
