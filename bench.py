@@ -206,6 +206,9 @@ def main():
                          "come from a single-stream pass")
     ap.add_argument("--dw-pair", type=int, default=1, choices=(0, 1),
                     help="FFN block: the gate and up projections' dW as one launch (1) or two (0)")
+    ap.add_argument("--fuse-glue", type=int, default=0, choices=(0, 1),
+                    help="FFN block: 1 computes the SwiGLU glue inside the gate and up quantizers "
+                         "(s3r_swiglu_quantize: G_gate and G_up are never written); 0 writes them in the glue pass")
     ap.add_argument("--cpu-rows", type=int, default=-1,
                     help="tokens in the CPU-oracle sample (-1: the default sample, 0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -313,9 +316,11 @@ def run_block(args, dev, torch, inputs, s3r):
     dw_keys = ["dw_down", "dw_gate_up"] if args.dw_pair else [f"dw_{n}" for n in proj]
     names = ["step", "glue"] + [f"quantize_{n}" for n in proj] + [f"dx_{n}" for n in proj] + dw_keys
 
-    def make_step(mode, ec, streams, pair=True):
+    def make_step(mode, ec, streams, pair=True, fused=False):
         """The block's backward step for one rounding mode / correction, with its own descriptors and workspaces.
-        pair: the gate and up projections' dW as one launch (s3r_backward_dw_pair) after the up projection's dX."""
+        pair: the gate and up projections' dW as one launch (s3r_backward_dw_pair) after the up projection's dX.
+        fused: the glue computed inside the gate and up quantizers (one s3r_swiglu_quantize call in place of the
+        glue pass and the two quantize calls; its time is the "glue" interval)."""
         st = {}
         for name, (D, din, layer, fxx, fww) in proj.items():
             d = s3r.qdesc(T, D, S, mode, ec, s3r.PER_TENSOR, layer_id=layer, seed=0)
@@ -326,7 +331,8 @@ def run_block(args, dev, torch, inputs, s3r):
                             flags=torch.zeros(1, dtype=torch.int32, device=dev), din=din, fx=fxx, fw=fww)
         ws_q = torch.empty(max(s3r.s3r_quantize_workspace(st[n]["desc"]) for n in st), dtype=torch.uint8,
                            device=dev)
-        ws_g = torch.empty(s3r.s3r_swiglu_amax_workspace(T, F), dtype=torch.uint8, device=dev)
+        ws_g = torch.empty(s3r.s3r_swiglu_quantize_workspace(st["gate"]["desc"]) if fused
+                           else s3r.s3r_swiglu_amax_workspace(T, F), dtype=torch.uint8, device=dev)
         amax = torch.zeros(2, dtype=torch.int32, device=dev)     # gate, up: max|G'| bits from the glue
         ws_b = torch.empty(max(max(s3r.s3r_backward_workspace(st[n]["desc"], st[n]["din"]) for n in st), 1),
                            dtype=torch.uint8, device=dev)
@@ -393,28 +399,40 @@ def run_block(args, dev, torch, inputs, s3r):
             dw("down", ev)
             if ev:
                 ev["glue"][0].record()
-            s3r.s3r_swiglu_backward_amax(dH, dv["A_gate"], dv["A_up"], Gg, Gu, fx.delta, fwg.delta, fwu.delta, amax,
-                                         ws_g)
+            if fused:
+                g, u = st["gate"], st["up"]
+                s3r.s3r_swiglu_quantize(g["desc"], u["desc"], dH, dv["A_gate"], dv["A_up"], fx.delta, fwg.delta,
+                                        fwu.delta, g["Q"], u["Q"], g["delta"], u["delta"], (g["er"], g["ec"], g["em"]),
+                                        (u["er"], u["ec"], u["em"]), g["flags"], ws_g)
+            else:
+                s3r.s3r_swiglu_backward_amax(dH, dv["A_gate"], dv["A_up"], Gg, Gu, fx.delta, fwg.delta, fwu.delta,
+                                             amax, ws_g)
             if ev:
                 ev["glue"][1].record()
+            if fused and ev:        # no separate quantize calls: empty intervals
+                for n in ("quantize_gate", "quantize_up"):
+                    ev[n][0].record()
+                    ev[n][1].record()
+            q_gate = (lambda ev_: None) if fused else (lambda ev_: quantize("gate", ev_))
+            q_up = (lambda ev_: None) if fused else (lambda ev_: quantize("up", ev_))
             if pair and streams == 3:
                 # both quantize calls first; the paired dW on the second stream beside both dX products
-                quantize("gate", ev)
-                quantize("up", ev)
+                q_gate(ev)
+                q_up(ev)
                 side(after_dx=False)
                 dw_pair(ev)
                 dx("gate", ev)
                 dx("up", ev)
             elif pair:
-                quantize("gate", ev)
+                q_gate(ev)
                 dx("gate", ev)
-                quantize("up", ev)
+                q_up(ev)
                 dx("up", ev)
                 side(after_dx=True)
                 dw_pair(ev)
             else:
                 for name in ("gate", "up"):
-                    quantize(name, ev)
+                    (q_gate if name == "gate" else q_up)(ev)
                     side(after_dx=False)
                     dx(name, ev)
                     side(after_dx=True)
@@ -430,17 +448,17 @@ def run_block(args, dev, torch, inputs, s3r):
 
     # per-kernel times from a single-stream pass (an event pair around a kernel that shares the GPU
     # with another stream's work would time both); the step itself in the configured schedule
-    step, st = make_step(mode, ec, 1, args.dw_pair)
+    step, st = make_step(mode, ec, 1, args.dw_pair, bool(args.fuse_glue))
     tl = Timeline(torch, names, args.steps)
     ms_single = _timed_steps(torch, step, tl, args.steps, args.warmup)
     for n in st:
         assert int(st[n]["flags"].item()) == 0, n
 
-    def step_ms(m2, e2, pair=args.dw_pair):
+    def step_ms(m2, e2, pair=args.dw_pair, fused=bool(args.fuse_glue)):
         """Whole-step time (no per-kernel events) in the configured stream schedule."""
-        if args.streams == 1 and (m2, e2, pair) == (mode, ec, args.dw_pair):
+        if args.streams == 1 and (m2, e2, pair, fused) == (mode, ec, args.dw_pair, bool(args.fuse_glue)):
             return ms_single
-        stepn, _ = make_step(m2, e2, args.streams, pair)
+        stepn, _ = make_step(m2, e2, args.streams, pair, fused)
         return _timed_steps(torch, lambda ev: stepn(None), Timeline(torch, [], args.steps), args.steps,
                             args.warmup)
 
@@ -452,6 +470,9 @@ def run_block(args, dev, torch, inputs, s3r):
     gemm_gop = {k: gop * (2 if k == "dw_gate_up" else 1) for k in gemm_us}
     q_us = sum(tl.avg_us(f"quantize_{n}") for n in st)
     q_bytes = (T * M + 2 * T * F) * 3                 # bf16 G read once + int8 Q written, three calls
+    if args.fuse_glue:   # the gate and up quantizers are the fused call: two passes over dH, A_gate, A_up
+        q_us += tl.avg_us("glue")
+        q_bytes = T * M * 3 + T * F * (2 * 8 + 2)
     q_gbs = q_bytes / (q_us / 1e6) / 1e9
     out = {
         "metric": "S3R-EC backward TOPS (quant+INT8 dX/dW) & quantizer GB/s, % of MI355X peak",
@@ -460,7 +481,7 @@ def run_block(args, dev, torch, inputs, s3r):
         "dtype": "i8", "data": "synthetic",
         "config": {"workload": b.name, "tokens": T, "d_model": M, "d_ff": F, "rows_per_example": S,
                    "mode": args.mode, "step_scale": "per-tensor", "g_dtype": "bf16", "streams": args.streams,
-                   "dw_pair": bool(args.dw_pair),
+                   "dw_pair": bool(args.dw_pair), "fuse_glue": bool(args.fuse_glue),
                    "stages": "down (quantize, dX=dH, dW), SwiGLU glue with the gate/up amax, gate and up "
                              "(quantize with that amax, dX added), the gate and up dW as one launch (dw_pair); "
                              "with 2 streams each dW launch (its U GEMVs and GEMM) runs on a second stream "
@@ -471,7 +492,9 @@ def run_block(args, dev, torch, inputs, s3r):
         "frac_of_int8_peak": round(value / PEAK_INT8_TOPS, 4),
         "quantizer": {"us": round(q_us, 2), "GB_s": round(q_gbs, 1), "frac_of_hbm_peak": round(q_gbs / PEAK_HBM_GBS, 4),
                       "algorithmic_bytes": q_bytes, "calls": 3,
-                      "note": "gate and up calls take their per-tensor amax from the glue pass (one read of G)"},
+                      "note": ("gate and up: the fused call (glue amax pass, then glue and both code passes: "
+                               "dH, A_gate, A_up read twice, G never written)" if args.fuse_glue else
+                               "gate and up calls take their per-tensor amax from the glue pass (one read of G)")},
         "kernels_us": {**{f"quantize_{n}": round(tl.avg_us(f"quantize_{n}"), 2) for n in st},
                        **{f"gemm_{k}": round(v, 2) for k, v in gemm_us.items()},
                        "glue": round(tl.avg_us("glue"), 2), "step_events": round(tl.avg_us("step"), 2)},
@@ -495,6 +518,15 @@ def run_block(args, dev, torch, inputs, s3r):
     out["dw_pair_ablation"] = {"paired_ms": round(ms_step, 4) if args.dw_pair else other,
                                "separate_ms": other if args.dw_pair else round(ms_step, 4),
                                "note": "whole-step times in this run: the gate and up dW as one launch or two"}
+    log("timing the step with the glue computed inside the gate and up quantizers" if not args.fuse_glue
+        else "timing the step with the glue as its own pass")
+    other = round(step_ms(mode, ec, fused=not args.fuse_glue), 4)
+    out["glue_fusion_ablation"] = {
+        "glue_pass_ms": other if args.fuse_glue else round(ms_step, 4),
+        "glue_in_quantizers_ms": round(ms_step, 4) if args.fuse_glue else other,
+        "note": "whole-step times in this run: G_gate and G_up written by the glue pass and read by the "
+                "quantizers, or never written (s3r_swiglu_quantize: one glue pass for the maxima, the glue again "
+                "in the code pass)"}
     del st, step, dv, dH, dX, Gg, Gu, dW
     out["bf16_context"] = bf16_gemm_context(torch, dev, T, M, F, sum(gemm_us.values()), ms_step, args.steps)
     if args.cpu_rows != 0:

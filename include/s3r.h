@@ -384,6 +384,41 @@ int s3r_swiglu_backward_amax(int64_t T, int64_t F, const float* dH, int64_t ld_d
                              const float* row_scale, const float* col_scale_gate, const float* col_scale_up,
                              uint32_t* amax_bits, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* s3r_swiglu_quantize: the gate and up projections' quantizers with the glue
+ * computed inside them, so that G_gate and G_up are never written to memory.
+ * S3R page, "Structured Subspace Randomness" (inter-operand sharing: the
+ * quantized gradient is produced once, by one fused pass) and "Quantized
+ * Backpropagation with Stochastic Rounding" (the per-tensor step of the folded
+ * gradient).  One glue pass finds the two per-tensor maxima without storing
+ * anything; a second pass computes the glue again and writes both projections'
+ * codes and error statistics.  The results are exactly those of
+ * s3r_swiglu_backward_amax followed by s3r_quantize_with_amax on G_gate (with
+ * desc_gate, col_scale_gate) and on G_up (desc_up, col_scale_up): codes,
+ * steps, flags and statistics, bit for bit.
+ *   desc_gate, desc_up: rows = T, cols = F; both PER_TENSOR (else
+ *     S3R_ERR_UNSUPPORTED); rows, cols, rows_per_example, mode and ec must be
+ *     equal (else S3R_ERR_INVALID_ARG); layer_id, seed and stream may differ.
+ *   dH, A_gate, A_up, ld_dh, ld_a: as s3r_swiglu_backward (device pointers).
+ *   row_scale [T] (s_x of the block input, shared by both projections) or NULL;
+ *   col_scale_gate, col_scale_up [F] (s_w of W_gate, W_up) or NULL.
+ *   Q_gate, Q_up [T x F] int8, one leading dim ld_q >= F; delta_gate,
+ *   delta_up [1]; ec_* as s3r_quantize for each projection (required iff
+ *   ec != NONE, NULL otherwise); flags: S3R_FLAG_* of both are OR-ed in.
+ *   ws: s3r_swiglu_quantize_workspace(desc_gate) bytes, 256-byte aligned.
+ * 16-byte-aligned dH, A_gate, A_up and column scales with ld_dh % 4 == 0,
+ * ld_a % 8 == 0, 8-byte-aligned codes with ld_q % 8 == 0 take the vector path;
+ * any layout is accepted.
+ */
+size_t s3r_swiglu_quantize_workspace(const s3r_qdesc* desc_gate);
+int s3r_swiglu_quantize(const s3r_qdesc* desc_gate, const s3r_qdesc* desc_up,
+                        const float* dH, int64_t ld_dh,
+                        const uint16_t* A_gate, const uint16_t* A_up, int64_t ld_a,
+                        const float* row_scale, const float* col_scale_gate, const float* col_scale_up,
+                        int8_t* Q_gate, int8_t* Q_up, int64_t ld_q, float* delta_gate, float* delta_up,
+                        float* ec_row_gate, float* ec_col_gate, float* ec_mean_gate,
+                        float* ec_row_up, float* ec_col_up, float* ec_mean_up,
+                        uint32_t* flags, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* ---- MXFP4 variant ------------------------------------------------------
  * The 4-bit setting the S3R page names as the one where deterministic
  * rounding of the backward fails (Introduction; Related Work, on NVFP4 /

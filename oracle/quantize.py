@@ -123,12 +123,14 @@ def thresholds(mode: int, seed: int, layer_id: int, T: int, D: int, row0: int = 
 
 def quantize(g_store: np.ndarray, dtype: str, *, mode: int, scale: int = PER_TENSOR,
              row_scale=None, col_scale=None, seed: int = 0, layer_id: int = 0,
-             rows_per_example: int | None = None, stream: int = 0, row0: int = 0) -> dict:
+             rows_per_example: int | None = None, stream: int = 0, row0: int = 0, amax=None) -> dict:
     """Quantize one gradient tensor; returns codes, steps and the fp32 values x.
 
     ``row0`` is the global index of the first row: thresholds are keyed on the
     global token (element) index, so a slice of rows quantized with its offset
-    draws the same thresholds as in the whole tensor.
+    draws the same thresholds as in the whole tensor.  ``amax`` (per-tensor step
+    only) is max|G'| over the whole tensor when ``g_store`` is a slice of it, so
+    the slice gets the whole tensor's step; by default it is the slice's own.
 
     Keys: "Q" int8 [T, D]; "delta" f32 ([1] per tensor, [T] per token);
     "x" f32 [T, D] (G'/Delta as the quantizer sees it, zero where flagged);
@@ -139,7 +141,10 @@ def quantize(g_store: np.ndarray, dtype: str, *, mode: int, scale: int = PER_TEN
     S = rows_per_example or max(T, 1)
     gp = fold(g, row_scale, col_scale)
     if scale == PER_TENSOR:
-        a = np.max(np.abs(gp)) if gp.size else F32(0)
+        if amax is not None:
+            a = F32(amax)
+        else:
+            a = np.max(np.abs(gp)) if gp.size else F32(0)
         delta, inv, fl = step_from_amax(np.array([a], F32))
         inv_rows = np.full(T, inv[0], F32)
         row_flags = np.full(T, fl[0], np.uint32)

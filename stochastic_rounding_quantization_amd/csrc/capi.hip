@@ -332,6 +332,58 @@ int s3r_swiglu_backward_amax(int64_t T, int64_t F, const float* dH, int64_t ld_d
                                             col_scale_gate, col_scale_up, amax_bits, (char*)ws, stream));
 }
 
+size_t s3r_swiglu_quantize_workspace(const s3r_qdesc* d) {
+  if (check_desc(d) != S3R_OK || d->scale != S3R_PER_TENSOR) return 0;
+  return swiglu_quant_workspace(d->rows, d->cols, d->rows_per_example, d->ec != S3R_EC_NONE);
+}
+
+int s3r_swiglu_quantize(const s3r_qdesc* dg, const s3r_qdesc* du, const float* dH, int64_t ld_dh,
+                        const uint16_t* A_gate, const uint16_t* A_up, int64_t ld_a, const float* row_scale,
+                        const float* col_scale_gate, const float* col_scale_up, int8_t* Q_gate, int8_t* Q_up,
+                        int64_t ld_q, float* delta_gate, float* delta_up, float* ec_row_gate, float* ec_col_gate,
+                        float* ec_mean_gate, float* ec_row_up, float* ec_col_up, float* ec_mean_up, uint32_t* flags,
+                        void* ws, size_t ws_bytes, hipStream_t stream) {
+  int rc;
+  if (!dg || !du) return S3R_ERR_INVALID_ARG;
+  if ((rc = check_desc(dg)) || (rc = check_desc(du))) return rc;
+  if (dg->scale != S3R_PER_TENSOR || du->scale != S3R_PER_TENSOR) return S3R_ERR_UNSUPPORTED;
+  if (dg->rows != du->rows || dg->cols != du->cols || dg->rows_per_example != du->rows_per_example ||
+      dg->mode != du->mode || dg->ec != du->ec)
+    return S3R_ERR_INVALID_ARG;
+  if (dg->ec != S3R_EC_NONE && !shared_threshold(dg->mode)) return S3R_ERR_UNSUPPORTED;
+  const int64_t T = dg->rows, F = dg->cols;
+  const int64_t B = T / dg->rows_per_example;
+  if (ld_dh < F || ld_a < F || ld_q < F) return S3R_ERR_INVALID_ARG;
+  if (T > 0 && F > 0 && (!dH || !A_gate || !A_up || !Q_gate || !Q_up)) return S3R_ERR_INVALID_ARG;
+  if (!delta_gate || !delta_up) return S3R_ERR_INVALID_ARG;
+  float* ec_row[2] = {ec_row_gate, ec_row_up};
+  float* ec_col[2] = {ec_col_gate, ec_col_up};
+  float* ec_mean[2] = {ec_mean_gate, ec_mean_up};
+  for (int k = 0; k < 2; ++k) {
+    if (dg->ec != S3R_EC_NONE) {
+      if ((T > 0 && !ec_row[k]) || (B * F > 0 && !ec_col[k]) || (B > 0 && !ec_mean[k])) return S3R_ERR_INVALID_ARG;
+    } else if (ec_row[k] || ec_col[k] || ec_mean[k]) {
+      return S3R_ERR_INVALID_ARG;
+    }
+  }
+  const size_t need = s3r_swiglu_quantize_workspace(dg);
+  if (ws_bytes < need) return S3R_ERR_WORKSPACE;
+  if (need > 0 && (!ws || ((uintptr_t)ws & 255u))) return S3R_ERR_INVALID_ARG;
+  if ((rc = check_arch())) return rc;
+  SwigluQuantArgs a{};
+  a.dH = dH; a.ld_dh = ld_dh; a.Ag = A_gate; a.Au = A_up; a.ld_a = ld_a;
+  a.sx = row_scale; a.sw[0] = col_scale_gate; a.sw[1] = col_scale_up;
+  a.Q[0] = Q_gate; a.Q[1] = Q_up; a.ld_q = ld_q; a.delta[0] = delta_gate; a.delta[1] = delta_up;
+  for (int k = 0; k < 2; ++k) { a.ec_row[k] = ec_row[k]; a.ec_col[k] = ec_col[k]; a.ec_mean[k] = ec_mean[k]; }
+  a.flags = flags;
+  a.T = T; a.D = F; a.S = dg->rows_per_example; a.mode = dg->mode; a.ec = dg->ec != S3R_EC_NONE;
+  a.layer[0] = dg->layer_id; a.layer[1] = du->layer_id;
+  a.seed[0] = dg->seed; a.seed[1] = du->seed;
+  a.stream[0] = dg->stream; a.stream[1] = du->stream;
+  a.ws = (char*)ws;
+  return finish(launch_swiglu_quantize(a, stream));
+}
+
 // ---- grouped (MoE expert) calls
 static int check_groups(const s3r_qdesc* d, int64_t groups, const int64_t* offsets) {
   if (groups < 1 || groups > kMaxGroups || !offsets) return S3R_ERR_INVALID_ARG;

@@ -20,6 +20,7 @@
 // is exact except where G'*inv is subnormal, and there both forms give the
 // same code.  The build disables FP contraction.
 #include "s3r_internal.h"
+#include "swiglu_math.h"
 
 #include <algorithm>
 #include <type_traits>
@@ -247,6 +248,148 @@ struct GroupArgs {
   const int64_t* offsets; const int32_t* tiles64; const uint32_t* amax; int64_t G;
 };
 
+// The SR thresholds of elements (t, j0 .. j0+7), r * 2^24, when D % 4 == 0: two Philox blocks.
+__device__ __forceinline__ void sr_thresholds8(const QuantTile& p, int64_t t, int64_t j0, int32_t (&R)[8]) {
+  const uint64_t blk = ((uint64_t)t * (uint64_t)p.D + (uint64_t)j0) >> 2;
+  const U4 w0 = philox4x32_10((uint32_t)blk, (uint32_t)(blk >> 32), p.layer, kTagSR + p.stream_word,
+                              (uint32_t)p.seed, (uint32_t)(p.seed >> 32));
+  const U4 w1 = philox4x32_10((uint32_t)(blk + 1), (uint32_t)((blk + 1) >> 32), p.layer, kTagSR + p.stream_word,
+                              (uint32_t)p.seed, (uint32_t)(p.seed >> 32));
+  R[0] = sr_units24(w0.x); R[1] = sr_units24(w0.y); R[2] = sr_units24(w0.z); R[3] = sr_units24(w0.w);
+  R[4] = sr_units24(w1.x); R[5] = sr_units24(w1.y); R[6] = sr_units24(w1.z); R[7] = sr_units24(w1.w);
+}
+
+// Fast-path codes of 8 elements v of row t (columns j0 .. j0+7, all in range; SR needs D % 4 == 0), packed
+// four to a word in pw.  rt: the row's S3R threshold (MODE 2; read only for a finite step).  With EC the rounding errors on the 2^24 grid
+// are added to es (the row) and col (each column).
+//   RTNE: clamp, then add 1.5 * 2^23, whose round-to-nearest-even sum holds rint(x) in its low byte.
+//   SR / S3R: t = clamp(floor(x * 2^24)) + r * 2^24 holds floor(x + r) in its top byte, and t & 0xFF000000
+//   is that code times 2^24; the error 2^24 (q - x) = fl(that - x * 2^24) is the rounding error on the
+//   2^24 grid, one rounding (its sums are scaled back by 2^-24 exactly).
+template <int MODE, bool EC>
+__device__ __forceinline__ void code8_packed(const QuantTile& p, const Step& st, const int32_t* rt, int64_t t, int64_t j0,
+                                             float fx, const float (&v)[8], const float (&sw8)[8],
+                                             uint32_t (&pw)[2], float& es, float (&col)[8]) {
+  if (st.flag) {
+    pw[0] = pw[1] = 0u;
+  } else if constexpr (MODE == 0) {
+    uint32_t y[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float x = ((v[i] * fx) * sw8[i]) * st.inv;
+      y[i] = __float_as_uint(fminf(fmaxf(x, -127.f), 127.f) + 12582912.f);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)   // low bytes of y[4h..4h+3]
+      pw[h] = __builtin_amdgcn_perm(y[4 * h + 1], y[4 * h], 0x0C0C0400u) |
+              __builtin_amdgcn_perm(y[4 * h + 3], y[4 * h + 2], 0x04000C0Cu);
+  } else {
+    int32_t R[8];
+    if constexpr (MODE == 2) {
+      const int32_t r = *rt;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) R[i] = r;
+    } else {
+      sr_thresholds8(p, t, j0, R);
+    }
+    uint32_t tv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float x24 = ((v[i] * fx) * sw8[i]) * st.inv24;
+      int32_t X;
+      asm("v_cvt_flr_i32_f32 %0, %1" : "=v"(X) : "v"(x24));   // floor; x24 is finite here
+      X = min(max(X, -(127 << 24)), 127 << 24);
+      tv[i] = (uint32_t)(X + R[i]);
+      if constexpr (EC) {
+        const float e24 = (float)(int32_t)(tv[i] & 0xFF000000u) - x24;
+        es += e24;
+        col[i] += e24;
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)   // top bytes of tv[4h..4h+3]
+      pw[h] = __builtin_amdgcn_perm(tv[4 * h + 1], tv[4 * h], 0x0C0C0703u) |
+              __builtin_amdgcn_perm(tv[4 * h + 3], tv[4 * h + 2], 0x07030C0Cu);
+  }
+}
+
+// Reduce-scatter of a wave's 16 row sums (rows k = 0..15 in rsum[k] of every lane): the result's lane l
+// holds the sum over the wave of row k = l >> 2.  Every lane of the wave must call it.
+__device__ __forceinline__ float row_sums16(const float (&rsum)[16], int lane) {
+  float r8[8], r4[4], r2[2], r1s;
+  const bool hi32 = lane & 32, hi16 = lane & 16, hi8 = lane & 8, hi4 = lane & 4;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float send = hi32 ? rsum[i] : rsum[i + 8];
+    r8[i] = (hi32 ? rsum[i + 8] : rsum[i]) + __shfl_xor(send, 32, kWave);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float send = hi16 ? r8[i] : r8[i + 4];
+    r4[i] = (hi16 ? r8[i + 4] : r8[i]) + __shfl_xor(send, 16, kWave);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const float send = hi8 ? r4[i] : r4[i + 2];
+    r2[i] = (hi8 ? r4[i + 2] : r4[i]) + __shfl_xor(send, 8, kWave);
+  }
+  {
+    const float send = hi4 ? r2[0] : r2[1];
+    r1s = (hi4 ? r2[1] : r2[0]) + __shfl_xor(send, 4, kWave);
+  }
+  r1s += __shfl_xor(r1s, 2, kWave);
+  r1s += __shfl_xor(r1s, 1, kWave);
+  return r1s;
+}
+
+// General-path codes q and errors e (q - x, in steps) of 8 elements v of row t, columns j0 .. j0+7 (values
+// past D are zeros, coded but not stored).  rt: the row's S3R threshold (MODE 2; read only for a finite step).
+template <int MODE>
+__device__ __forceinline__ void code8(const QuantTile& p, const Step& s, const int32_t* rt, int64_t t, int64_t j0, float fx,
+                                      const float* v, const float (&sw8)[8], int (&q)[8], float (&e)[8]) {
+  if (s.flag) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) { q[i] = 0; e[i] = 0.f; }
+  } else if constexpr (MODE == 0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float x = ((v[i] * fx) * sw8[i]) * s.inv;
+      const float r = fminf(fmaxf(__builtin_rintf(x), -127.f), 127.f);
+      q[i] = (int)r;
+      e[i] = (float)q[i] - x;
+    }
+  } else {
+    int32_t R[8];
+    if constexpr (MODE == 2) {
+      const int32_t r = *rt;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) R[i] = r;
+    } else {
+      if ((p.D & 3) == 0) {
+        sr_thresholds8(p, t, j0, R);   // elements e0 .. e0+7 with e0 % 4 == 0: exactly two Philox blocks
+      } else {
+        const uint64_t e0 = (uint64_t)t * (uint64_t)p.D + (uint64_t)j0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint64_t ei = e0 + i;
+          const uint64_t blk = ei >> 2;
+          const U4 w = philox4x32_10((uint32_t)blk, (uint32_t)(blk >> 32), p.layer, kTagSR + p.stream_word,
+                                     (uint32_t)p.seed, (uint32_t)(p.seed >> 32));
+          R[i] = sr_units24(u4_word(w, (uint32_t)ei & 3u));
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float x24 = ((v[i] * fx) * sw8[i]) * s.inv24;
+      int32_t X = (int32_t)floorf(x24);
+      X = min(max(X, -(127 << 24)), 127 << 24);
+      q[i] = (X + R[i]) >> 24;
+      e[i] = fmaf(x24, -0x1p-24f, (float)q[i]);
+    }
+  }
+}
+
 template <typename TIn, bool VEC, int MODE, bool EC, bool PT, bool COLSUM, bool GR = false>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(
     QuantTile p, const TIn* __restrict__ G, const float* __restrict__ sx, const float* __restrict__ sw,
@@ -356,88 +499,14 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
           v[2 * i] = __uint_as_float(w[i] << 16);
           v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
         }
-        // Codes packed four to a word.  RTNE: clamp, then add 1.5 * 2^23, whose round-to-nearest-even
-        // sum holds rint(x) in its low byte.  SR / S3R: t = clamp(floor(x * 2^24)) + r * 2^24 holds
-        // floor(x + r) in its top byte, and t & 0xFF000000 is that code times 2^24; the error
-        // 2^24 (q - x) = fl(that - x * 2^24) is the rounding error on the 2^24 grid, one rounding
-        // (its sums are scaled back by 2^-24 below, exactly).
         uint32_t pw[2];
         float es = 0.f;
-        if (st.flag) {
-          pw[0] = pw[1] = 0u;
-        } else if constexpr (MODE == 0) {
-          uint32_t y[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const float x = ((v[i] * fx) * sw8[i]) * st.inv;
-            y[i] = __float_as_uint(fminf(fmaxf(x, -127.f), 127.f) + 12582912.f);
-          }
-#pragma unroll
-          for (int h = 0; h < 2; ++h)   // low bytes of y[4h..4h+3]
-            pw[h] = __builtin_amdgcn_perm(y[4 * h + 1], y[4 * h], 0x0C0C0400u) |
-                    __builtin_amdgcn_perm(y[4 * h + 3], y[4 * h + 2], 0x04000C0Cu);
-        } else {
-          int32_t R[8];
-          if constexpr (MODE == 2) {
-            const int32_t rt = s_thr[t - r0];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) R[i] = rt;
-          } else {
-            const uint64_t blk = ((uint64_t)t * (uint64_t)p.D + (uint64_t)j0) >> 2;   // D % 4 == 0 here
-            const U4 w0 = philox4x32_10((uint32_t)blk, (uint32_t)(blk >> 32), p.layer, kTagSR + p.stream_word,
-                                        (uint32_t)p.seed, (uint32_t)(p.seed >> 32));
-            const U4 w1 = philox4x32_10((uint32_t)(blk + 1), (uint32_t)((blk + 1) >> 32), p.layer,
-                                        kTagSR + p.stream_word, (uint32_t)p.seed, (uint32_t)(p.seed >> 32));
-            R[0] = sr_units24(w0.x); R[1] = sr_units24(w0.y); R[2] = sr_units24(w0.z); R[3] = sr_units24(w0.w);
-            R[4] = sr_units24(w1.x); R[5] = sr_units24(w1.y); R[6] = sr_units24(w1.z); R[7] = sr_units24(w1.w);
-          }
-          uint32_t tv[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const float x24 = ((v[i] * fx) * sw8[i]) * st.inv24;
-            int32_t X;
-            asm("v_cvt_flr_i32_f32 %0, %1" : "=v"(X) : "v"(x24));   // floor; x24 is finite here
-            X = min(max(X, -(127 << 24)), 127 << 24);
-            tv[i] = (uint32_t)(X + R[i]);
-            if constexpr (EC) {
-              const float e24 = (float)(int32_t)(tv[i] & 0xFF000000u) - x24;
-              es += e24;
-              col[i] += e24;
-            }
-          }
-#pragma unroll
-          for (int h = 0; h < 2; ++h)   // top bytes of tv[4h..4h+3]
-            pw[h] = __builtin_amdgcn_perm(tv[4 * h + 1], tv[4 * h], 0x0C0C0703u) |
-                    __builtin_amdgcn_perm(tv[4 * h + 3], tv[4 * h + 2], 0x07030C0Cu);
-        }
+        code8_packed<MODE, EC>(p, st, &s_thr[t - r0], t, j0, fx, v, sw8, pw, es, col);
         rsum[k] = es;
         *reinterpret_cast<uint2*>(Q + t * p.ld_q + j0) = make_uint2(pw[0], pw[1]);
       }
       if constexpr (EC) {
-        // reduce-scatter of the 16 row sums: afterwards lane l holds row k = l >> 2
-        float r8[8], r4[4], r2[2], r1s;
-        const bool hi32 = lane & 32, hi16 = lane & 16, hi8 = lane & 8, hi4 = lane & 4;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float send = hi32 ? rsum[i] : rsum[i + 8];
-          r8[i] = (hi32 ? rsum[i + 8] : rsum[i]) + __shfl_xor(send, 32, kWave);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float send = hi16 ? r8[i] : r8[i + 4];
-          r4[i] = (hi16 ? r8[i + 4] : r8[i]) + __shfl_xor(send, 16, kWave);
-        }
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const float send = hi8 ? r4[i] : r4[i + 2];
-          r2[i] = (hi8 ? r4[i + 2] : r4[i]) + __shfl_xor(send, 8, kWave);
-        }
-        {
-          const float send = hi4 ? r2[0] : r2[1];
-          r1s = (hi4 ? r2[1] : r2[0]) + __shfl_xor(send, 4, kWave);
-        }
-        r1s += __shfl_xor(r1s, 2, kWave);
-        r1s += __shfl_xor(r1s, 1, kWave);
+        const float r1s = row_sums16(rsum, lane);   // lane l: row l >> 2
         if ((lane & 3) == 0) row_part[(r0 + wave + 4 * (lane >> 2)) * p.n_ctiles + ctile] = r1s * 0x1p-24f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) col[i] *= 0x1p-24f;   // to the units the slow path sums in
@@ -473,54 +542,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
     const float* v = vb[u];
     int q[8];
     float e[8];
-    if (s.flag) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) { q[i] = 0; e[i] = 0.f; }
-    } else if constexpr (MODE == 0) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float x = ((v[i] * fx) * sw8[i]) * s.inv;
-        const float r = fminf(fmaxf(__builtin_rintf(x), -127.f), 127.f);
-        q[i] = (int)r;
-        e[i] = (float)q[i] - x;
-      }
-    } else {
-      int32_t R[8];
-      if constexpr (MODE == 2) {
-        const int32_t rt = s_thr[t - r0];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) R[i] = rt;
-      } else {
-        const uint64_t e0 = (uint64_t)t * (uint64_t)p.D + (uint64_t)j0;
-        if ((p.D & 3) == 0) {
-          // elements e0 .. e0+7 with e0 % 4 == 0: exactly two Philox blocks
-          const uint64_t blk = e0 >> 2;
-          const U4 w0 = philox4x32_10((uint32_t)blk, (uint32_t)(blk >> 32), p.layer, kTagSR + p.stream_word,
-                                      (uint32_t)p.seed, (uint32_t)(p.seed >> 32));
-          const U4 w1 = philox4x32_10((uint32_t)(blk + 1), (uint32_t)((blk + 1) >> 32), p.layer, kTagSR + p.stream_word,
-                                      (uint32_t)p.seed, (uint32_t)(p.seed >> 32));
-          R[0] = sr_units24(w0.x); R[1] = sr_units24(w0.y); R[2] = sr_units24(w0.z); R[3] = sr_units24(w0.w);
-          R[4] = sr_units24(w1.x); R[5] = sr_units24(w1.y); R[6] = sr_units24(w1.z); R[7] = sr_units24(w1.w);
-        } else {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const uint64_t ei = e0 + i;
-            const uint64_t blk = ei >> 2;
-            const U4 w = philox4x32_10((uint32_t)blk, (uint32_t)(blk >> 32), p.layer, kTagSR + p.stream_word,
-                                       (uint32_t)p.seed, (uint32_t)(p.seed >> 32));
-            R[i] = sr_units24(u4_word(w, (uint32_t)ei & 3u));
-          }
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float x24 = ((v[i] * fx) * sw8[i]) * s.inv24;
-        int32_t X = (int32_t)floorf(x24);
-        X = min(max(X, -(127 << 24)), 127 << 24);
-        q[i] = (X + R[i]) >> 24;
-        e[i] = fmaf(x24, -0x1p-24f, (float)q[i]);
-      }
-    }
+    code8<MODE>(p, s, &s_thr[t - r0], t, j0, fx, v, sw8, q, e);
     if (j0 < p.D) store8<VEC>(Q + t * p.ld_q, j0, p.D, q);
     if constexpr (EC) {
       float rs = 0.f;
@@ -562,6 +584,220 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
         for (int w = 1; w < kThreads / kWave; ++w) a += s_colq[w][c];
         colq_part[(int64_t)rtile * p.D + j] = a;
       }
+    }
+  }
+}
+
+// ------------------------------------------- quantizer with the glue in it ----
+// The gate and up projections' code pass with the SwiGLU glue computed in it: per element the glue's two
+// bf16 results, from dH, A_gate and A_up, are coded at once for both projections, so G_gate and G_up are
+// never written.  The steps come from a glue pass that found the two per-tensor maxima only (amax[0] gate,
+// amax[1] up).  Same tiles, lane mapping, fast and general paths, code arithmetic and order of the error
+// sums as quantize_kernel, so codes, steps and statistics are exactly those of the glue followed by the two
+// quantizers.
+struct GlueIn {
+  const float* dH; int64_t ld_dh; const uint16_t* Ag; const uint16_t* Au; int64_t ld_a;
+};
+struct QuantOut {
+  const float* sw; int8_t* Q; float* delta; float* row_part; float* col_part; uint32_t* fin_counter;
+};
+
+template <bool VEC, int MODE, bool EC>
+__global__ __launch_bounds__(kThreads) void swiglu_quantize_kernel(QuantTile pg, QuantTile pu, GlueIn in,
+                                                                   const float* __restrict__ sx, QuantOut og,
+                                                                   QuantOut ou, const uint32_t* __restrict__ amax,
+                                                                   uint32_t* __restrict__ flags) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int rtile = blockIdx.x;
+  const int ctile = blockIdx.y;
+  const int64_t D = pg.D;
+  const int64_t b = rtile / pg.tiles_per_example;
+  const int64_t r0 = b * pg.S + (int64_t)(rtile % pg.tiles_per_example) * kRowsPerTile;
+  const int64_t r1 = min(r0 + kRowsPerTile, (b + 1) * pg.S);
+  const int64_t j0 = (int64_t)ctile * kColsPerTile + lane * 8;
+  if (EC && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+    *og.fin_counter = 0u;   // for the finalize kernels
+    *ou.fin_counter = 0u;
+  }
+  __shared__ int32_t s_thr[2][kRowsPerTile];
+  __shared__ float s_col[EC ? 2 : 1][kThreads / kWave][EC ? kColsPerTile : 1];
+
+  const uint32_t mg = amax[0], mu = amax[1];
+  const Step stg = make_step(mg), stu = make_step(mu);
+  if (rtile == 0 && ctile == 0 && threadIdx.x == 0) {
+    og.delta[0] = (mg > 0x7F800000u) ? __uint_as_float(mg) : stg.delta;
+    ou.delta[0] = (mu > 0x7F800000u) ? __uint_as_float(mu) : stu.delta;
+    if ((stg.flag | stu.flag) && flags) atomicOr(flags, stg.flag | stu.flag);
+  }
+  if constexpr (MODE == 2) {
+    if (threadIdx.x < r1 - r0) {
+      s_thr[0][threadIdx.x] = row_threshold_units24(r0 + threadIdx.x, pg.layer, pg.seed, pg.bcast, pg.S, pg.stream_word);
+      s_thr[1][threadIdx.x] = row_threshold_units24(r0 + threadIdx.x, pu.layer, pu.seed, pu.bcast, pu.S, pu.stream_word);
+    }
+    __syncthreads();
+  }
+
+  float swg[8], swu[8];
+  load8_scale(og.sw, j0, D, VEC, swg);
+  load8_scale(ou.sw, j0, D, VEC, swu);
+  float colg[8], colu[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) { colg[i] = 0.f; colu[i] = 0.f; }
+
+  // Fast path (a full 64-row tile, 8 columns in range, aligned rows), chosen per wave: the wave's 16 rows
+  // t = r0 + wave + 4k in four groups of 4, each group's dH, A_gate and A_up loaded while the group before
+  // it is coded.  The group loop is not unrolled (16 rows of glue would not fit); the 16 per-row error sums
+  // shift down by a group per iteration, so they end in row order without indexing registers.
+  bool done = false;
+  if constexpr (VEC) {
+    constexpr int kWR = kRowsPerTile / (kThreads / kWave);   // 16 rows per wave
+    constexpr int kGroup = 4;
+    const bool fast_lane = r1 - r0 == kRowsPerTile && j0 + 8 <= D && (MODE != 1 || (D & 3) == 0);
+    if (__builtin_amdgcn_ballot_w64(!fast_lane) == 0) {
+      done = true;
+      struct Raw { float4 h0, h1; uint4 a, u; };
+      Raw cur[kGroup], nxt[kGroup];
+      float rsg[kWR], rsu[kWR];
+#pragma unroll
+      for (int k = 0; k < kWR; ++k) { rsg[k] = 0.f; rsu[k] = 0.f; }
+      const float sx_rows = (sx && lane < kWR) ? sx[r0 + wave + 4 * lane] : 1.f;
+      auto load_group = [&](Raw (&dst)[kGroup], int g) {
+#pragma unroll
+        for (int u = 0; u < kGroup; ++u) {
+          const int64_t t = r0 + wave + 4 * (g * kGroup + u);
+          const float* dh = in.dH + t * in.ld_dh + j0;
+          dst[u].h0 = ld_stream_f4(dh);
+          dst[u].h1 = ld_stream_f4(dh + 4);
+          dst[u].a = ld_stream_u4(in.Ag + t * in.ld_a + j0);
+          dst[u].u = ld_stream_u4(in.Au + t * in.ld_a + j0);
+        }
+      };
+      load_group(cur, 0);
+#pragma unroll 1
+      for (int g = 0; g < kWR / kGroup; ++g) {
+        if (g + 1 < kWR / kGroup) {
+          __builtin_amdgcn_sched_barrier(0);        // the next group's loads, in row order
+          load_group(nxt, g + 1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        float ng[kGroup], nu[kGroup];
+#pragma unroll
+        for (int u = 0; u < kGroup; ++u) {
+          const int k = g * kGroup + u;
+          const int64_t t = r0 + wave + 4 * k;
+          const float fx = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sx_rows), k));
+          uint32_t gg[4], gu[4];
+          glue8_vals(cur[u].h0, cur[u].h1, cur[u].a, cur[u].u, gg, gu);
+          float vg[8], vu[8];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            vg[2 * i] = __uint_as_float(gg[i] << 16);
+            vg[2 * i + 1] = __uint_as_float(gg[i] & 0xFFFF0000u);
+            vu[2 * i] = __uint_as_float(gu[i] << 16);
+            vu[2 * i + 1] = __uint_as_float(gu[i] & 0xFFFF0000u);
+          }
+          uint32_t pwg[2], pwu[2];
+          float esg = 0.f, esu = 0.f;
+          code8_packed<MODE, EC>(pg, stg, &s_thr[0][t - r0], t, j0, fx, vg, swg, pwg, esg, colg);
+          code8_packed<MODE, EC>(pu, stu, &s_thr[1][t - r0], t, j0, fx, vu, swu, pwu, esu, colu);
+          ng[u] = esg;
+          nu[u] = esu;
+          *reinterpret_cast<uint2*>(og.Q + t * pg.ld_q + j0) = make_uint2(pwg[0], pwg[1]);
+          *reinterpret_cast<uint2*>(ou.Q + t * pu.ld_q + j0) = make_uint2(pwu[0], pwu[1]);
+        }
+#pragma unroll
+        for (int k = 0; k < kWR - kGroup; ++k) { rsg[k] = rsg[k + kGroup]; rsu[k] = rsu[k + kGroup]; }
+#pragma unroll
+        for (int u = 0; u < kGroup; ++u) {
+          rsg[kWR - kGroup + u] = ng[u];
+          rsu[kWR - kGroup + u] = nu[u];
+          cur[u] = nxt[u];
+        }
+      }
+      if constexpr (EC) {
+        const float sg = row_sums16(rsg, lane), su = row_sums16(rsu, lane);   // lane l: row l >> 2
+        if ((lane & 3) == 0) {
+          const int64_t t = r0 + wave + 4 * (lane >> 2);
+          og.row_part[t * pg.n_ctiles + ctile] = sg * 0x1p-24f;
+          ou.row_part[t * pu.n_ctiles + ctile] = su * 0x1p-24f;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) { colg[i] *= 0x1p-24f; colu[i] *= 0x1p-24f; }
+      }
+    }
+  }
+
+  // General path: rows t = r0 + wave + 4u one at a time, elements past D coded as zeros and not stored.
+  for (int64_t t = r0 + wave; t < r1 && !done; t += kThreads / kWave) {
+    float vg[8], vu[8];
+    if (VEC && j0 + 8 <= D) {
+      uint32_t gg[4], gu[4];
+      glue8(in.dH + t * in.ld_dh + j0, in.Ag + t * in.ld_a + j0, in.Au + t * in.ld_a + j0, gg, gu);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        vg[2 * i] = __uint_as_float(gg[i] << 16);
+        vg[2 * i + 1] = __uint_as_float(gg[i] & 0xFFFF0000u);
+        vu[2 * i] = __uint_as_float(gu[i] << 16);
+        vu[2 * i + 1] = __uint_as_float(gu[i] & 0xFFFF0000u);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        vg[i] = 0.f;
+        vu[i] = 0.f;
+        if (j0 + i < D) {
+          uint32_t g, u;
+          glue1(in.dH[t * in.ld_dh + j0 + i], bf16_to_f32(in.Ag[t * in.ld_a + j0 + i]),
+                bf16_to_f32(in.Au[t * in.ld_a + j0 + i]), g, u);
+          vg[i] = __uint_as_float(g << 16);
+          vu[i] = __uint_as_float(u << 16);
+        }
+      }
+    }
+    const float fx = sx ? sx[t] : 1.f;
+    int qg[8], qu[8];
+    float eg[8], eu[8];
+    code8<MODE>(pg, stg, &s_thr[0][t - r0], t, j0, fx, vg, swg, qg, eg);
+    code8<MODE>(pu, stu, &s_thr[1][t - r0], t, j0, fx, vu, swu, qu, eu);
+    if (j0 < D) {
+      store8<VEC>(og.Q + t * pg.ld_q, j0, D, qg);
+      store8<VEC>(ou.Q + t * pu.ld_q, j0, D, qu);
+    }
+    if constexpr (EC) {
+      float rg = 0.f, ru = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float a = (j0 + i < D) ? eg[i] : 0.f, c = (j0 + i < D) ? eu[i] : 0.f;
+        rg += a;
+        ru += c;
+        colg[i] += a;
+        colu[i] += c;
+      }
+      rg = wave_sum(rg);
+      ru = wave_sum(ru);
+      if (lane == 0) {
+        og.row_part[t * pg.n_ctiles + ctile] = rg;
+        ou.row_part[t * pu.n_ctiles + ctile] = ru;
+      }
+    }
+  }
+
+  if constexpr (EC) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      s_col[0][wave][lane * 8 + i] = colg[i];
+      s_col[1][wave][lane * 8 + i] = colu[i];
+    }
+    __syncthreads();
+    for (int c = threadIdx.x; c < 2 * kColsPerTile; c += kThreads) {
+      const int k = c / kColsPerTile, cc = c % kColsPerTile;
+      const int64_t j = (int64_t)ctile * kColsPerTile + cc;
+      if (j >= D) continue;
+      float a = s_col[k][0][cc];
+#pragma unroll
+      for (int w = 1; w < kThreads / kWave; ++w) a += s_col[k][w][cc];
+      (k ? ou.col_part : og.col_part)[(int64_t)rtile * D + j] = a;
     }
   }
 }
@@ -1069,6 +1305,81 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t st) {
   } else {
     if (vec) run_quantize<float, true>(a, L, st);
     else run_quantize<float, false>(a, L, st);
+  }
+  return hipGetLastError();
+}
+
+size_t swiglu_quant_workspace(int64_t T, int64_t D, int64_t S, int ec) {
+  const size_t per = ws_layout(T, D, S, ec, S3R_PER_TENSOR, false).total;
+  return align_up(swiglu_amax_workspace(T, D), 256) + 256 + 2 * per;
+}
+
+namespace {
+template <bool VEC, int MODE, bool EC>
+void launch_sq(const SwigluQuantArgs& a, const QuantTile (&p)[2], const QuantOut (&o)[2], const uint32_t* amax,
+               dim3 grid, hipStream_t st) {
+  hipLaunchKernelGGL((swiglu_quantize_kernel<VEC, MODE, EC>), grid, dim3(kThreads), 0, st, p[0], p[1],
+                     GlueIn{a.dH, a.ld_dh, a.Ag, a.Au, a.ld_a}, a.sx, o[0], o[1], amax, a.flags);
+}
+
+template <bool VEC>
+void dispatch_sq(const SwigluQuantArgs& a, const QuantTile (&p)[2], const QuantOut (&o)[2], const uint32_t* amax,
+                 dim3 grid, hipStream_t st) {
+  switch (a.mode) {
+    case S3R_RTNE: launch_sq<VEC, 0, false>(a, p, o, amax, grid, st); break;
+    case S3R_SR: launch_sq<VEC, 1, false>(a, p, o, amax, grid, st); break;
+    default:
+      if (a.ec) launch_sq<VEC, 2, true>(a, p, o, amax, grid, st);
+      else launch_sq<VEC, 2, false>(a, p, o, amax, grid, st);
+  }
+}
+}  // namespace
+
+// Workspace: the glue pass's per-block maxima, the two amax words, then one quantizer layout per projection.
+hipError_t launch_swiglu_quantize(const SwigluQuantArgs& a, hipStream_t st) {
+  const WsLayout L = ws_layout(a.T, a.D, a.S, a.ec, S3R_PER_TENSOR, false);
+  const int64_t B = a.S > 0 ? a.T / a.S : 0;
+  if (a.T == 0 || a.D == 0) {
+    const int64_t n = std::max<int64_t>({1, a.T, B * a.D});
+    for (int k = 0; k < 2; ++k)
+      hipLaunchKernelGGL(empty_kernel, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0, st, a.T,
+                         a.D, B, 0, a.delta[k], a.ec_row[k], a.ec_col[k], a.ec_mean[k], (int32_t*)nullptr);
+    return hipGetLastError();
+  }
+  uint32_t* amax = (uint32_t*)(a.ws + align_up(swiglu_amax_workspace(a.T, a.D), 256));
+  char* wk[2] = {(char*)amax + 256, (char*)amax + 256 + L.total};
+  hipError_t e = launch_swiglu_backward_amax(a.T, a.D, a.dH, a.ld_dh, a.Ag, a.Au, a.ld_a, nullptr, nullptr, 0, a.sx,
+                                             a.sw[0], a.sw[1], amax, a.ws, st);
+  if (e != hipSuccess) return e;
+  QuantTile p[2];
+  QuantOut o[2];
+  bool vec = aligned(a.dH, 16) && aligned(a.Ag, 16) && aligned(a.Au, 16) && a.ld_dh % 4 == 0 && a.ld_a % 8 == 0 &&
+             a.ld_q % 8 == 0;
+  for (int k = 0; k < 2; ++k) {
+    p[k] = QuantTile{};
+    p[k].T = a.T; p[k].D = a.D; p[k].S = a.S; p[k].ld_g = 0; p[k].ld_q = a.ld_q;
+    p[k].tiles_per_example = (int)((a.S + kRowsPerTile - 1) / kRowsPerTile);
+    p[k].n_ctiles = (int)((a.D + kColsPerTile - 1) / kColsPerTile);
+    p[k].layer = a.layer[k]; p[k].seed = a.seed[k];
+    p[k].stream_word = a.stream[k] << 16;
+    p[k].bcast = a.mode == S3R_S3R_BCAST;
+    o[k] = QuantOut{a.sw[k], a.Q[k], a.delta[k], (float*)(wk[k] + L.row_part), (float*)(wk[k] + L.col_part),
+                    (uint32_t*)(wk[k] + L.counter)};
+    vec = vec && aligned(a.Q[k], 8) && (a.sw[k] == nullptr || aligned(a.sw[k], 16));
+  }
+  const dim3 grid((unsigned)(B * p[0].tiles_per_example), (unsigned)p[0].n_ctiles);
+  if (vec) dispatch_sq<true>(a, p, o, amax, grid, st);
+  else dispatch_sq<false>(a, p, o, amax, grid, st);
+  if (a.ec) {
+    const int64_t ncb = (B * a.D + kWave - 1) / kWave;
+    const int bpe = (int)((a.S + kFinRows - 1) / kFinRows);
+    const int64_t nrb = B * bpe;
+    for (int k = 0; k < 2; ++k)
+      hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)(ncb + nrb)), dim3(kThreads), 0, st, B, a.D, a.S,
+                         p[k].tiles_per_example, p[k].n_ctiles, 0, (int)ncb, bpe, a.delta[k],
+                         (const float*)(wk[k] + L.col_part), (const int32_t*)(wk[k] + L.colq_part),
+                         (const float*)(wk[k] + L.row_part), a.ec_col[k], (int32_t*)nullptr, a.ec_row[k],
+                         a.ec_mean[k], (double*)(wk[k] + L.blk_sum), (uint32_t*)(wk[k] + L.counter));
   }
   return hipGetLastError();
 }

@@ -196,12 +196,30 @@ hipError_t launch_swiglu_backward(int64_t T, int64_t F, const float* dH, int64_t
                                   hipStream_t st);
 
 size_t swiglu_amax_workspace(int64_t T, int64_t F);
+// Gg == Gu == nullptr: the per-tensor maxima only, nothing else written.
 hipError_t launch_swiglu_backward_amax(int64_t T, int64_t F, const float* dH, int64_t ld_dh, const uint16_t* Ag,
                                        const uint16_t* Au, int64_t ld_a, uint16_t* Gg, uint16_t* Gu, int64_t ld_g,
                                        const float* sx, const float* swg, const float* swu, uint32_t* amax_bits,
                                        char* ws, hipStream_t st);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// The gate and up projections' quantizers with the SwiGLU glue computed in them (quantize.hip): G_gate
+// and G_up are never written.  Per-tensor steps; the two quantizers share the shape, mode and correction
+// and may differ in layer, seed and threshold stream.
+struct SwigluQuantArgs {
+  const float* dH; int64_t ld_dh; const uint16_t* Ag; const uint16_t* Au; int64_t ld_a;
+  const float* sx; const float* sw[2];              // [0] gate, [1] up
+  int8_t* Q[2]; int64_t ld_q; float* delta[2];
+  float* ec_row[2]; float* ec_col[2]; float* ec_mean[2];
+  uint32_t* flags;
+  int64_t T, D, S;
+  int mode, ec;
+  uint32_t layer[2]; uint64_t seed[2]; uint32_t stream[2];
+  char* ws;
+};
+size_t swiglu_quant_workspace(int64_t T, int64_t D, int64_t S, int ec);
+hipError_t launch_swiglu_quantize(const SwigluQuantArgs& a, hipStream_t st);
 
 // Grouped problems (groups.hip): tables derived on the device from the group
 // offsets, in a workspace region of group_tables_bytes(G).  At most kMaxGroups groups.

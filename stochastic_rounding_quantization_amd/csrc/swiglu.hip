@@ -1,81 +1,14 @@
 // SwiGLU backward glue of an FFN block, for gfx950 (an HBM-bound elementwise pass).
-//
-// The S3R page times a whole SwiGLU FFN block ("Setup", single-block FFN
-// benchmarks; Table III).  Between the down projection's backward (which gives
-// dH) and the gate / up projections' backward sit the gradients of
-// H = silu(A_gate) * A_up with respect to the two pre-activations:
-//   G_up   = dH * silu(A_gate)
-//   G_gate = dH * A_up * silu'(A_gate),  silu'(a) = s (1 + a (1 - s)),  s = 1 / (1 + exp(-a)).
-// The arithmetic is fixed here (the pages leave it open): fp32, one rounding
-// per operation in the order below (no contraction), an exponential built from
-// a Cody-Waite reduction by ln 2 and the degree-7 Taylor polynomial, results
-// rounded to bf16 (nearest, ties to even).  Every element is independent, so
-// the results do not depend on the launch shape.
-#include "s3r_internal.h"
+// The element arithmetic (swiglu_math.h) is fixed to one rounding per fp32
+// operation, so the results do not depend on the launch shape.
+#include "swiglu_math.h"
 
 namespace s3r {
 namespace {
 
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2Hi = 0.693145751953125f;        // 15 significant bits: n * kLn2Hi is exact for |n| < 512
-constexpr float kLn2Lo = 1.4286068203094173e-06f;   // ln 2 - kLn2Hi
-constexpr float kXMin = -104.f, kXMax = 89.f;        // exp under- / overflows fp32 beyond these
-
-__device__ __forceinline__ float exp32(float x) {
-  const float xc = x < kXMin ? kXMin : (x > kXMax ? kXMax : x);   // NaN passes through
-  const float n = __builtin_rintf(xc * kLog2e);
-  const float r = (xc - n * kLn2Hi) - n * kLn2Lo;
-  float p = (float)(1.0 / 5040.0);
-  p = p * r + (float)(1.0 / 720.0);
-  p = p * r + (float)(1.0 / 120.0);
-  p = p * r + (float)(1.0 / 24.0);
-  p = p * r + (float)(1.0 / 6.0);
-  p = p * r + 0.5f;
-  p = p * r + 1.f;
-  p = p * r + 1.f;
-  const int ni = n != n ? 0 : (int)n;
-  return __builtin_ldexpf(p, ni);
-}
-
-__device__ __forceinline__ uint32_t bf16_rne(float v) {
-  const uint32_t u = __float_as_uint(v);
-  if (v != v) return 0x7FC0u;
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
-// (G_gate, G_up) of one element, as bf16 bit patterns.
-__device__ __forceinline__ void glue1(float dh, float a, float u, uint32_t& gg, uint32_t& gu) {
-  const float e = exp32(-a);
-  const float s = __fdiv_rn(1.f, 1.f + e);
-  const float silu = a * s;
-  const float ds = s * (1.f + a * (1.f - s));
-  gu = bf16_rne(dh * silu);
-  gg = bf16_rne((dh * u) * ds);
-}
-
 // Thread mapping of both glue kernels: blockIdx.x * 256 + threadIdx.x is an 8-element chunk column
 // of the rows (16-byte loads and stores), fixed for the thread; blockIdx.y strides over the rows. A row
 // of a block is one contiguous span of 2048 columns, and the per-chunk index arithmetic is one add.
-
-// 8 elements of one row: G_gate and G_up as packed bf16 pairs (og, ou: elements 2i, 2i+1 in word i).
-__device__ __forceinline__ void glue8(const float* __restrict__ dh, const uint16_t* __restrict__ ag,
-                                      const uint16_t* __restrict__ au, uint32_t (&og)[4], uint32_t (&ou)[4]) {
-  const float4 h0 = ld_stream_f4(dh);
-  const float4 h1 = ld_stream_f4(dh + 4);
-  const uint4 va = ld_stream_u4(ag);
-  const uint4 vu = ld_stream_u4(au);
-  __builtin_amdgcn_sched_barrier(0);   // all four loads in flight before any is waited for
-  const float h[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
-  const uint32_t wa[4] = {va.x, va.y, va.z, va.w}, wu[4] = {vu.x, vu.y, vu.z, vu.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint32_t g0, u0, g1, u1;
-    glue1(h[2 * i], __uint_as_float(wa[i] << 16), __uint_as_float(wu[i] << 16), g0, u0);
-    glue1(h[2 * i + 1], __uint_as_float(wa[i] & 0xFFFF0000u), __uint_as_float(wu[i] & 0xFFFF0000u), g1, u1);
-    og[i] = g0 | (g1 << 16);
-    ou[i] = u0 | (u1 << 16);
-  }
-}
 
 template <bool VEC>
 __global__ __launch_bounds__(256) void swiglu_backward_kernel(
@@ -113,14 +46,16 @@ __global__ __launch_bounds__(256) void swiglu_backward_kernel(
 // bf16-rounded results (the quantizer's fold of its own input), as ordered fp32
 // bits (NaN above every number).  Same thread mapping as the plain glue; block
 // b = blockIdx.y * gridDim.x + blockIdx.x writes its two maxima to part[0][b]
-// and part[1][b], and swiglu_amax_finalize_kernel reduces them.
+// and part[1][b], and swiglu_amax_finalize_kernel reduces them.  STORE false
+// finds the maxima only (G_gate and G_up are never written: the quantizer that
+// follows computes them again).
 constexpr int kAmaxGlueBlocks = 4096;
 
 __device__ __forceinline__ uint32_t fold_abs_bits(uint32_t bf16, float fx, float sw) {
   return __float_as_uint((__uint_as_float(bf16 << 16) * fx) * sw) & 0x7FFFFFFFu;
 }
 
-template <bool VEC>
+template <bool VEC, bool STORE>
 __global__ __launch_bounds__(256) void swiglu_amax_kernel(
     int64_t T, int64_t F, const float* __restrict__ dH, int64_t ld_dh, const uint16_t* __restrict__ Ag,
     const uint16_t* __restrict__ Au, int64_t ld_a, uint16_t* __restrict__ Gg, uint16_t* __restrict__ Gu,
@@ -136,8 +71,8 @@ __global__ __launch_bounds__(256) void swiglu_amax_kernel(
       const float* dh = dH + t * ld_dh + j0;
       const uint16_t* ag = Ag + t * ld_a + j0;
       const uint16_t* au = Au + t * ld_a + j0;
-      uint16_t* gg = Gg + t * ld_g + j0;
-      uint16_t* gu = Gu + t * ld_g + j0;
+      uint16_t* gg = STORE ? Gg + t * ld_g + j0 : nullptr;
+      uint16_t* gu = STORE ? Gu + t * ld_g + j0 : nullptr;
       if (full) {
         // the column scales are re-read per row (cache hits) rather than held in 16 registers across
         // the loop, which made the compiler wait for the row's first loads before issuing the last
@@ -163,14 +98,18 @@ __global__ __launch_bounds__(256) void swiglu_amax_kernel(
           mg = max(mg, max(fold_abs_bits(og[i] & 0xFFFFu, fx, cg[2 * i]), fold_abs_bits(og[i] >> 16, fx, cg[2 * i + 1])));
           mu = max(mu, max(fold_abs_bits(ou[i] & 0xFFFFu, fx, cu[2 * i]), fold_abs_bits(ou[i] >> 16, fx, cu[2 * i + 1])));
         }
-        *reinterpret_cast<uint4*>(gg) = make_uint4(og[0], og[1], og[2], og[3]);
-        *reinterpret_cast<uint4*>(gu) = make_uint4(ou[0], ou[1], ou[2], ou[3]);
+        if constexpr (STORE) {
+          *reinterpret_cast<uint4*>(gg) = make_uint4(og[0], og[1], og[2], og[3]);
+          *reinterpret_cast<uint4*>(gu) = make_uint4(ou[0], ou[1], ou[2], ou[3]);
+        }
       } else {
         for (int i = 0; i < 8 && j0 + i < F; ++i) {
           uint32_t g, u;
           glue1(dh[i], bf16_to_f32(ag[i]), bf16_to_f32(au[i]), g, u);
-          gg[i] = (uint16_t)g;
-          gu[i] = (uint16_t)u;
+          if constexpr (STORE) {
+            gg[i] = (uint16_t)g;
+            gu[i] = (uint16_t)u;
+          }
           mg = max(mg, fold_abs_bits(g, fx, swg ? swg[j0 + i] : 1.f));
           mu = max(mu, fold_abs_bits(u, fx, swu ? swu[j0 + i] : 1.f));
         }
@@ -238,17 +177,15 @@ hipError_t launch_swiglu_backward_amax(int64_t T, int64_t F, const float* dH, in
                                        char* ws, hipStream_t st) {
   uint32_t* part = (uint32_t*)(ws);
   const int64_t nblk = amax_blocks(T, F);
+  const bool store = Gg != nullptr;   // the C ABI passes both outputs or (for the fused quantizer) neither
   if (nblk > 0) {
-    const bool vec = aligned16(dH) && aligned16(Ag) && aligned16(Au) && aligned16(Gg) && aligned16(Gu) &&
-                     ld_dh % 4 == 0 && ld_a % 8 == 0 && ld_g % 8 == 0 && (!swg || aligned16(swg)) &&
+    const bool vec = aligned16(dH) && aligned16(Ag) && aligned16(Au) && ld_dh % 4 == 0 && ld_a % 8 == 0 &&
+                     (!store || (aligned16(Gg) && aligned16(Gu) && ld_g % 8 == 0)) && (!swg || aligned16(swg)) &&
                      (!swu || aligned16(swu));
     const dim3 grid = glue_grid(T, F, kAmaxGlueBlocks);
-    if (vec)
-      hipLaunchKernelGGL(swiglu_amax_kernel<true>, grid, dim3(256), 0, st, T, F, dH, ld_dh, Ag, Au, ld_a, Gg, Gu,
-                         ld_g, sx, swg, swu, part);
-    else
-      hipLaunchKernelGGL(swiglu_amax_kernel<false>, grid, dim3(256), 0, st, T, F, dH, ld_dh, Ag, Au, ld_a, Gg, Gu,
-                         ld_g, sx, swg, swu, part);
+    auto kern = vec ? (store ? swiglu_amax_kernel<true, true> : swiglu_amax_kernel<true, false>)
+                    : (store ? swiglu_amax_kernel<false, true> : swiglu_amax_kernel<false, false>);
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, T, F, dH, ld_dh, Ag, Au, ld_a, Gg, Gu, ld_g, sx, swg, swu, part);
   }
   hipLaunchKernelGGL(swiglu_amax_finalize_kernel, dim3(1), dim3(256), 0, st, part, (int)nblk, amax_bits);
   return hipGetLastError();

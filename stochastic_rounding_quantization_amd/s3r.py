@@ -30,7 +30,7 @@ S3R_NOALLOC_SCRATCH_BYTES = 32 << 20    # include/s3r.h: the no-alloc quantizer'
 
 EXPORTED = ["s3r_quantize_workspace", "s3r_quantize", "s3r_quantize_with_amax", "s3r_quantize_noalloc", "s3r_backward_dx",
             "s3r_backward_dw", "s3r_backward_dw_pair", "s3r_backward_dw_pair_workspace", "s3r_backward_workspace", "s3r_swiglu_backward", "s3r_swiglu_amax_workspace",
-            "s3r_swiglu_backward_amax", "s3r_grouped_workspace", "s3r_grouped_quantize",
+            "s3r_swiglu_backward_amax", "s3r_swiglu_quantize_workspace", "s3r_swiglu_quantize", "s3r_grouped_workspace", "s3r_grouped_quantize",
             "s3r_grouped_backward_dx", "s3r_grouped_backward_dw", "s3r_mx_workspace", "s3r_mx_operand_workspace",
             "s3r_mx_operand", "s3r_mx_quantize", "s3r_mx_backward_dx", "s3r_mx_backward_dw", "s3r_time_next_gemm",
             "s3r_status_string", "s3r_version"]
@@ -93,6 +93,11 @@ def lib() -> ctypes.CDLL:
     L.s3r_swiglu_amax_workspace.restype = SZ
     L.s3r_swiglu_backward_amax.argtypes = [I64, I64, P, I64, P, P, I64, P, P, I64, P, P, P, P, P, SZ, P]
     L.s3r_swiglu_backward_amax.restype = ctypes.c_int
+    L.s3r_swiglu_quantize_workspace.argtypes = [DP]
+    L.s3r_swiglu_quantize_workspace.restype = SZ
+    L.s3r_swiglu_quantize.argtypes = [DP, DP, P, I64, P, P, I64, P, P, P, P, P, I64, P, P, P, P, P, P, P, P, P, P, SZ,
+                                      P]
+    L.s3r_swiglu_quantize.restype = ctypes.c_int
     L.s3r_grouped_workspace.argtypes = [DP, I64, I64]
     L.s3r_grouped_workspace.restype = SZ
     L.s3r_grouped_quantize.argtypes = [DP, I64, P, P, I32, I64, P, P, P, I64, P, P, P, P, P, P, P, SZ, P]
@@ -284,6 +289,29 @@ def s3r_swiglu_backward_amax(dH, A_gate, A_up, G_gate, G_up, row_scale, col_scal
     _check("s3r_swiglu_backward_amax", rc)
 
 
+def s3r_swiglu_quantize_workspace(desc: QDesc) -> int:
+    return lib().s3r_swiglu_quantize_workspace(ctypes.byref(desc))
+
+
+def s3r_swiglu_quantize(desc_gate: QDesc, desc_up: QDesc, dH, A_gate, A_up, row_scale, col_scale_gate, col_scale_up,
+                        Q_gate, Q_up, delta_gate, delta_up, ec_gate=(None, None, None), ec_up=(None, None, None),
+                        flags=None, ws=None, stream=None, *, rc_only=False):
+    """The gate and up quantizers with the glue inside (G_gate, G_up never written); ec_gate / ec_up are
+    (ec_row, ec_col, ec_mean) triples."""
+    F = desc_gate.cols
+    if A_up.stride() != A_gate.stride() or _ld(Q_up, F) != _ld(Q_gate, F):
+        raise ValueError("A_gate / A_up and Q_gate / Q_up must share their layouts")
+    rc = lib().s3r_swiglu_quantize(
+        ctypes.byref(desc_gate), ctypes.byref(desc_up), _ptr(dH), _ld(dH, F), _ptr(A_gate), _ptr(A_up),
+        _ld(A_gate, F), _ptr(row_scale), _ptr(col_scale_gate), _ptr(col_scale_up), _ptr(Q_gate), _ptr(Q_up),
+        _ld(Q_gate, F), _ptr(delta_gate), _ptr(delta_up), _ptr(ec_gate[0]), _ptr(ec_gate[1]), _ptr(ec_gate[2]),
+        _ptr(ec_up[0]), _ptr(ec_up[1]), _ptr(ec_up[2]), _ptr(flags), _ptr(ws),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+    if rc_only:
+        return rc
+    _check("s3r_swiglu_quantize", rc)
+
+
 def s3r_grouped_workspace(desc: QDesc, groups: int, d_in: int) -> int:
     return lib().s3r_grouped_workspace(ctypes.byref(desc), groups, d_in)
 
@@ -405,6 +433,31 @@ def swiglu_backward(dH, A_gate, A_up, stream=None):
     G_up = torch.empty_like(G_gate)
     s3r_swiglu_backward(dH, A_gate, A_up, G_gate, G_up, stream)
     return G_gate, G_up
+
+
+def swiglu_quantize(dH, A_gate, A_up, *, mode=S3R, ec=EC_NONE, row_scale=None, col_scale_gate=None,
+                    col_scale_up=None, seed=0, layer_gate=0, layer_up=0, rows_per_example=None, stream=None,
+                    threshold_stream=0):
+    """Allocate the outputs and run s3r_swiglu_quantize: (Quantized gate, Quantized up)."""
+    import torch
+    T, F = dH.shape
+    dev = dH.device
+    dg = qdesc(T, F, rows_per_example, mode, ec, PER_TENSOR, layer_gate, seed, threshold_stream)
+    du = qdesc(T, F, rows_per_example, mode, ec, PER_TENSOR, layer_up, seed, threshold_stream)
+    B = T // dg.rows_per_example
+    out = []
+    for d in (dg, du):
+        e = (None, None, None)
+        if ec != EC_NONE:
+            e = (torch.empty(T, dtype=torch.float32, device=dev), torch.empty(B, F, dtype=torch.float32, device=dev),
+                 torch.empty(B, dtype=torch.float32, device=dev))
+        out.append((q_buffer(T, F, dev), torch.empty(1, dtype=torch.float32, device=dev), e))
+    flags = torch.zeros(1, dtype=torch.int32, device=dev)
+    ws = _workspace(s3r_swiglu_quantize_workspace(dg), dev)
+    s3r_swiglu_quantize(dg, du, dH, A_gate, A_up, row_scale, col_scale_gate, col_scale_up, out[0][0], out[1][0],
+                        out[0][1], out[1][1], out[0][2], out[1][2], flags, ws, stream)
+    return (Quantized(out[0][0], out[0][1], dg, None, *out[0][2], flags),
+            Quantized(out[1][0], out[1][1], du, None, *out[1][2], flags))
 
 
 def s3r_time_next_gemm(start_event, stop_event) -> None:

@@ -184,6 +184,39 @@ def test_swiglu_amax_and_quantize_with_amax_argument_errors(L):
     assert qa(d, wsb=0) in (-3, -4, -5)                                           # workspace or no device
 
 
+def test_swiglu_quantize_argument_errors(L):
+    P = ctypes.c_void_p
+    T, F, S = 64, 96, 32
+
+    def call(dg=None, du=None, dH=P(256), ldh=F, Ag=P(512), Au=P(768), lda=F, Qg=P(1024), Qu=P(1280), ldq=F,
+             dlg=P(64), dlu=P(128), ecg=(None, None, None), ecu=(None, None, None), ws=P(4096), wsb=1 << 24):
+        dg = dg or s3r.qdesc(T, F, S, s3r.S3R, s3r.EC_NONE)
+        du = du or s3r.qdesc(T, F, S, s3r.S3R, s3r.EC_NONE, layer_id=1)
+        return L.s3r_swiglu_quantize(ctypes.byref(dg), ctypes.byref(du), dH, ldh, Ag, Au, lda, None, None, None, Qg,
+                                     Qu, ldq, dlg, dlu, *ecg, *ecu, None, ws, wsb, None)
+
+    pt = s3r.qdesc(T, F, S, s3r.S3R, s3r.EC_NONE, s3r.PER_TOKEN)
+    assert call(dg=pt, du=pt) == -2                                            # per-tensor steps only
+    assert call(du=s3r.qdesc(T, F, S, s3r.SR, s3r.EC_NONE)) == -1              # modes differ
+    assert call(du=s3r.qdesc(T, F + 8, S, s3r.S3R, s3r.EC_NONE)) == -1         # shapes differ
+    assert call(du=s3r.qdesc(T, F, 64, s3r.S3R, s3r.EC_NONE)) == -1            # examples differ
+    sr_ec = s3r.qdesc(T, F, S, s3r.SR, s3r.EC_TWO_WAY)
+    assert call(dg=sr_ec, du=sr_ec) == -2                                      # correction needs shared thresholds
+    assert call(ldh=F - 1) == -1 and call(lda=F - 1) == -1 and call(ldq=F - 1) == -1
+    assert call(dH=None) == -1 and call(Qu=None) == -1 and call(dlg=None) == -1
+    ec = s3r.qdesc(T, F, S, s3r.S3R, s3r.EC_TWO_WAY)
+    assert call(dg=ec, du=ec) == -1                                            # statistics outputs missing
+    assert call(ecg=(P(1), None, None)) == -1                                  # statistics without correction
+    need = s3r.s3r_swiglu_quantize_workspace(s3r.qdesc(T, F, S, s3r.S3R, s3r.EC_NONE))
+    assert need > 0 and call(wsb=need - 1) == -3
+    assert call(ws=P(4100)) == -1
+    assert s3r.s3r_swiglu_quantize_workspace(pt) == 0
+    # two quantizers' partial sums (1 + 1/512 floats per element each) and the glue pass's partial maxima
+    big = s3r.s3r_swiglu_quantize_workspace(s3r.qdesc(8192, 14336, 2048, s3r.S3R, s3r.EC_TWO_WAY))
+    assert big >= 2 * 4 * (8192 * 14336 // 64 + 8192 * 28) + s3r.s3r_swiglu_amax_workspace(8192, 14336)
+    assert call(wsb=need) in (-4, -5)                                          # valid: no device here
+
+
 class _FakeDev:
     """Stands in for a device tensor in the binding's marshalling (never dereferenced on the host)."""
 

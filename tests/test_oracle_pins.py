@@ -327,6 +327,27 @@ def test_per_tensor_step_and_range():
         assert out["Q"].min() >= -127
 
 
+def test_row_slice_with_whole_tensor_amax_equals_whole_tensor():
+    # A slice of rows quantized with its global row offset and the whole tensor's amax gets exactly the
+    # whole tensor's codes, values and step: the per-tensor step is one number for every row, and the
+    # thresholds are keyed on global indices.  Row 5 holds the maximum, outside the slice.
+    g = _heavy(9, 48, 36)
+    g[5, 7] = np.float32(40.0) * np.abs(g).max()
+    sx = np.linspace(0.5, 2.0, 48).astype(np.float32)
+    sw = np.linspace(2.0, 0.25, 36).astype(np.float32)
+    a = np.max(np.abs(oq.fold(g, sx, sw)))
+    for mode in (oq.RTNE, oq.SR, oq.S3R, oq.S3R_BCAST):
+        whole = oq.quantize(g, "f32", mode=mode, row_scale=sx, col_scale=sw, seed=4, layer_id=2, rows_per_example=12)
+        part = oq.quantize(g[20:44], "f32", mode=mode, row_scale=sx[20:44], col_scale=sw, seed=4, layer_id=2,
+                           rows_per_example=12, row0=20, amax=a)
+        assert part["delta"][0] == whole["delta"][0]
+        np.testing.assert_array_equal(part["Q"], whole["Q"][20:44])
+        np.testing.assert_array_equal(part["x"], whole["x"][20:44])
+        own = oq.quantize(g[20:44], "f32", mode=mode, row_scale=sx[20:44], col_scale=sw, seed=4, layer_id=2,
+                          rows_per_example=12, row0=20)
+        assert own["delta"][0] < whole["delta"][0]     # the slice's own step is smaller
+
+
 def test_per_token_step():
     g = _heavy(8, 40, 33)
     out = oq.quantize(g, "f32", mode=oq.S3R, scale=oq.PER_TOKEN, seed=1)
