@@ -1065,12 +1065,6 @@ __global__ __launch_bounds__(kThreads) void grouped_mean_kernel(const int64_t* _
   if (threadIdx.x == 0) ec_mean[e] = b > a ? (float)(red[0] / (double)(b - a)) : 0.f;
 }
 
-// Steps of 1 for empty groups under a per-tensor step (no code tile writes them).
-__global__ void grouped_empty_steps_kernel(const int64_t* __restrict__ offsets, int64_t G, float* __restrict__ delta) {
-  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (e < G && offsets[e + 1] == offsets[e]) delta[e] = 1.f;
-}
-
 // Degenerate shapes (T == 0 or D == 0): steps of 1, zero statistics.
 __global__ void empty_kernel(int64_t T, int64_t D, int64_t B, int per_token, float* delta,
                              float* ec_row, float* ec_col, float* ec_mean, int32_t* code_colsum) {
@@ -1210,8 +1204,6 @@ void run_grouped(const QuantArgs& a, const GroupedWs& L, const GroupArgs& gr, co
     hipLaunchKernelGGL((grouped_amax_kernel<TIn, VEC>),
                        dim3((unsigned)n_rt, (unsigned)((a.D + kColsPerTile - 1) / kColsPerTile)), dim3(kThreads), 0,
                        st, G, a.ld_g, a.D, a.sx, a.sw, gr, (uint32_t*)gr.amax);
-    hipLaunchKernelGGL(grouped_empty_steps_kernel, dim3((unsigned)((gr.G + 255) / 256)), dim3(256), 0, st,
-                       gr.offsets, gr.G, a.delta);
   } else {
     const unsigned nb = (unsigned)((a.T + kThreads / kWave - 1) / (kThreads / kWave));
     hipLaunchKernelGGL((amax_rows_kernel<TIn, VEC>), dim3(nb), dim3(kThreads), 0, st, G, a.ld_g, a.T, a.D,
@@ -1264,7 +1256,7 @@ size_t grouped_quant_workspace(int64_t R, int64_t D, int64_t Gn, int ec, int sca
 hipError_t launch_grouped_quantize(const QuantArgs& a, int64_t Gn, const int64_t* offsets, hipStream_t st) {
   const GroupedWs L = grouped_ws(a.T, a.D, Gn, a.ec, a.scale, a.code_colsum != nullptr);
   const GroupTables tab = group_tables(a.ws + L.tables, Gn, offsets);
-  hipError_t e = launch_group_tables(tab, a.T, a.flags, st);
+  hipError_t e = launch_group_tables(tab, a.T, a.flags, st, a.scale == S3R_PER_TENSOR ? a.delta : nullptr);
   if (e != hipSuccess) return e;
   GroupArgs gr{offsets, tab.tiles64, tab.amax, Gn};
   if (a.D == 0) return hipSuccess;

@@ -235,7 +235,9 @@ struct GroupTables {
 };
 size_t group_tables_bytes(int64_t G);
 GroupTables group_tables(char* base, int64_t G, const int64_t* offsets);
-hipError_t launch_group_tables(const GroupTables& t, int64_t R, uint32_t* flags, hipStream_t st);
+// empty_delta (a grouped per-tensor quantizer's steps, or null): 1 for every empty group.
+hipError_t launch_group_tables(const GroupTables& t, int64_t R, uint32_t* flags, hipStream_t st,
+                               float* empty_delta = nullptr);
 
 // The group e with tiles[e] <= i < tiles[e+1], its first tile tiles[e] and its
 // rows [offsets[e], offsets[e+1]), found by the whole wave in a 64-ary search:

@@ -127,7 +127,7 @@ def test_grouped_invalid_offsets_flagged_and_nothing_written():
     Q = torch.full((R, D), 9, dtype=torch.int8, device=DEV)
     delta = torch.full((E,), 5.0, device=DEV)
     ws = torch.zeros(s3r.s3r_grouped_workspace(desc, E, d_in), dtype=torch.uint8, device=DEV)
-    for bad in ([0, 40, 20, 64], [0, 10, 20, 63], [1, 10, 20, 64]):
+    for bad in ([0, 40, 20, 64], [0, 10, 20, 63], [1, 10, 20, 64], [0, 10, 10, 63]):
         flags = torch.zeros(1, dtype=torch.int32, device=DEV)
         off = torch.tensor(bad, dtype=torch.int64, device=DEV)
         s3r.s3r_grouped_quantize(desc, off, G, None, None, Q, delta, flags=flags, ws=ws)
@@ -136,7 +136,7 @@ def test_grouped_invalid_offsets_flagged_and_nothing_written():
         s3r.s3r_grouped_backward_dw(desc, off, Q, delta, Xq, None, None, None, None, None, dW, flags, ws)
         torch.cuda.synchronize()
         assert int(host(flags)[0]) & s3r.FLAG_BAD_GROUPS, bad
-        assert (host(Q) == 9).all() and (host(dW) == 7.0).all()
+        assert (host(Q) == 9).all() and (host(dW) == 7.0).all() and (host(delta) == 5.0).all()
 
 
 def test_moe_workload_sampled():
