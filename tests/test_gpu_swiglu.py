@@ -64,6 +64,23 @@ def test_glue_extremes_and_strides():
         assert (host(Gb[:, :, F:].float()) == 7.0).all()
 
 
+def test_glue_every_bf16_pre_activation():
+    # A_gate takes every one of the 65536 bf16 bit patterns (zeros, subnormals, the clamp bounds of the
+    # exponential and beyond, infinities, NaNs), so the exponential, the reciprocal and the bf16
+    # rounding see every value they can see in the glue; bit-exact against the oracle
+    T, F = 256, 256
+    ag = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16).reshape(T, F)
+    rng = np.random.default_rng(65536)
+    dH = (rng.standard_normal((T, F)) * np.float32(1e-3)).astype(np.float32)
+    dH[0, :8] = np.float32([1.0, -1.0, 3e38, -3e38, 1e-40, 0.0, np.inf, np.nan])
+    au = inputs.f32_to_bf16_bits(rng.standard_normal((T, F)).astype(np.float32))
+    gg, gu = s3r.swiglu_backward(torch.from_numpy(dH).to(DEV), _bf16_dev(ag), _bf16_dev(au))
+    torch.cuda.synchronize()
+    ref_g, ref_u = sg.glue(dH, ag, au)
+    np.testing.assert_array_equal(_bits(gg), ref_g)
+    np.testing.assert_array_equal(_bits(gu), ref_u)
+
+
 def test_glue_empty():
     z = torch.empty(0, 16, device=DEV)
     zb = torch.empty(0, 16, dtype=torch.bfloat16, device=DEV)
