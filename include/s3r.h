@@ -329,8 +329,9 @@ int s3r_grouped_backward_dx(const s3r_qdesc* desc, int64_t groups, const int64_t
 
 /* s3r_grouped_backward_dw: dW_e = diag(1/s_w,e)(Delta_e Q_e - P(E'_e))^T Xq_e for
  * every group, into dW + e * dw_group_stride elements (each [D x d_in] with
- * ld_dw, stride >= D * ld_dw).  s_w [G x D], xs [G x d_in] (per-group column
- * sums of Xq).  The groups run largest first.  PER_TENSOR only. */
+ * ld_dw below 2^21, stride >= D * ld_dw).  s_w [G x D], xs [G x d_in]
+ * (per-group column sums of Xq).  The groups run largest first.  PER_TENSOR
+ * only. */
 int s3r_grouped_backward_dw(const s3r_qdesc* desc, int64_t groups, const int64_t* offsets,
                             const int8_t* Q, int64_t ld_q, const float* delta,
                             const int8_t* Xq, int64_t ld_x, int64_t d_in,

@@ -473,7 +473,9 @@ int s3r_grouped_backward_dw(const s3r_qdesc* d, int64_t groups, const int64_t* o
   if (out_dt != S3R_F32 && out_dt != S3R_I32_RAW) return S3R_ERR_UNSUPPORTED;
   const int64_t R = d->rows, D = d->cols;
   if (d_in < 0 || R > kMaxK) return S3R_ERR_INVALID_ARG;
-  if (!delta || (D > 0 && d_in > 0 && !dW) || ld_dw < d_in || ld_dw >= kMaxLdOut) return S3R_ERR_INVALID_ARG;
+  // the grouped dW drops the stores of columns past d_in by an offset past its output descriptor, which
+  // must not wrap 32 bits: (256 + 127) rows of ld_dw floats
+  if (!delta || (D > 0 && d_in > 0 && !dW) || ld_dw < d_in || ld_dw >= kMaxLdOut / 2) return S3R_ERR_INVALID_ARG;
   if (D > 0 && d_in > 0 && (((uintptr_t)dW & 3u) || dw_group_stride < D * ld_dw)) return S3R_ERR_INVALID_ARG;
   if ((rc = check_gemm_operand(Q, ld_q, R, D, R > 0 && D > 0))) return rc;
   if ((rc = check_gemm_operand(Xq, ld_x, R, d_in, R > 0 && d_in > 0))) return rc;

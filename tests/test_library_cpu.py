@@ -269,6 +269,11 @@ def test_grouped_binding_marshals_valid_arguments(L):
     Xq = _FakeDev((R, d_in), (48, 1))
     assert s3r.s3r_grouped_backward_dw(desc, off, Q, f32(E), Xq, f32(E, D), f32(E, d_in), *st, dW, None, ws, 0,
                                        rc_only=True) in expect
+    # the grouped dW's output leading dimension stays below 2^21 (its dropped stores' offsets must not wrap)
+    for ld, rc in (((1 << 21) - 1, expect), (1 << 21, (-1,))):
+        wide = _FakeDev((E, D, d_in), (D * ld, ld, 1), elem=4)
+        assert s3r.s3r_grouped_backward_dw(desc, off, Q, f32(E), Xq, f32(E, D), f32(E, d_in), *st, wide, None, ws,
+                                           0, rc_only=True) in rc, ld
 
 
 def test_mx_argument_errors(L):
