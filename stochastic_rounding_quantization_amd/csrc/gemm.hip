@@ -473,9 +473,13 @@ __device__ __forceinline__ int row_in_block(int r) { return (r >> 2) * 8 + (r & 
 // output descriptor's range, where the hardware drops the store.  Measured faster for the grouped dW,
 // whose narrow outputs leave many tiles partial in N, and slower for the dense GEMMs, whose tiles are
 // whole.  Needs (rows + 127) * ld_out * 4 < 2^32 (the C ABI bounds ld_out for the grouped dW).
-template <int EPI, bool EC, bool GATHER, int NB, bool DROP = false>
+// NJ: 32-column blocks per wave (4 in the 256 x 256 tiles, 2 in the 256 x 128 tiles of the grouped dW).
+// pre (NB == 1 dW, optional): the column factors u[n], xs[n] of the wave's NJ column blocks, loaded by the
+// caller ahead of time; otherwise they are loaded here.
+template <int EPI, bool EC, bool GATHER, int NB, bool DROP = false, int NJ = 4>
 __device__ __forceinline__ void epilogue(const GemmParams& g, const EpiParams& ep, int64_t m0, int64_t n0,
-                                         const float4* rowf, const float* roweb, v16i (&acc)[4][4]) {
+                                         const float4* rowf, const float* roweb, v16i (&acc)[4][NJ],
+                                         const float (*pre)[NJ] = nullptr) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int rows_here = (int)min((int64_t)BM, g.M - m0);
@@ -490,13 +494,13 @@ __device__ __forceinline__ void epilogue(const GemmParams& g, const EpiParams& e
   // column (its own, or column 0 past N, whose value is then discarded), outside any branch,
   // and waits for the loads once here: a load still pending inside the store loop would make
   // each group of stores wait for every store before it (vmcnt counts stores too).
-  float colA[4], colV[4], colB[NB][4], colS[4];
-  bool n_ok[4];
-  uint32_t voff[4];
+  float colA[NJ], colV[NJ], colB[NB][NJ], colS[NJ];
+  bool n_ok[NJ];
+  uint32_t voff[NJ];
   const uint32_t off_none = (uint32_t)rows_here * ld4;   // DROP: past the descriptor's range
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int64_t n = n0 + wn * 128 + j * 32 + (lane & 31);
+  for (int j = 0; j < NJ; ++j) {
+    const int64_t n = n0 + wn * (NJ * 32) + j * 32 + (lane & 31);
     n_ok[j] = n < g.N;
     const int64_t nc = n_ok[j] ? n : 0;
     voff[j] = (DROP && !n_ok[j]) ? off_none : (uint32_t)(lane_row * ld4 + n * esz);
@@ -508,10 +512,15 @@ __device__ __forceinline__ void epilogue(const GemmParams& g, const EpiParams& e
       colA[j] = (float)ep.colsum[nc];                                    // r_W[n]
       if constexpr (!GATHER) colV[j] = ep.vec[(m0 / ep.S) * g.N + nc];   // v_b[n], the tile's example
     } else if constexpr (EC && is_dw(EPI)) {
-      colA[j] = ep.u[nc];
+      if (NB == 1 && pre) {
+        colA[j] = pre[0][j];
+        colB[0][j] = pre[1][j];
+      } else {
+        colA[j] = ep.u[nc];
 #pragma unroll
-      for (int b = 0; b < NB; ++b)                                       // xs_b[n]; slots past B hold 0
-        colB[b][j] = (float)ep.colsum[(b < ep.B ? b : 0) * g.N + nc] * (b < ep.B ? 1.f : 0.f);
+        for (int b = 0; b < NB; ++b)                                     // xs_b[n]; slots past B hold 0
+          colB[b][j] = (float)ep.colsum[(b < ep.B ? b : 0) * g.N + nc] * (b < ep.B ? 1.f : 0.f);
+      }
     }
   }
   S3R_WAIT_VM(0);
@@ -519,12 +528,12 @@ __device__ __forceinline__ void epilogue(const GemmParams& g, const EpiParams& e
   // EPI_DXA: the current output values of a block-row, loaded one block-row ahead: the loads of
   // block-row i+1 are issued before the stores of block-row i, so waiting for them does not wait
   // for those stores (vmcnt counts loads and stores in issue order)
-  float old[2][4][4][4];
-  auto load_old = [&](int i, float (&dst)[4][4][4]) {
+  float old[2][4][NJ][4];
+  auto load_old = [&](int i, float (&dst)[4][NJ][4]) {
 #pragma unroll
     for (int rq = 0; rq < 4; ++rq)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < NJ; ++j)
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr)
           dst[rq][j][rr] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(
@@ -550,11 +559,11 @@ __device__ __forceinline__ void epilogue(const GemmParams& g, const EpiParams& e
         }
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < NJ; ++j) {
         if (!DROP && !n_ok[j]) continue;
         float gv[4];
         if constexpr (is_dx(EPI) && EC && GATHER) {
-          const int64_t n = n0 + wn * 128 + j * 32 + (lane & 31);
+          const int64_t n = n0 + wn * (NJ * 32) + j * 32 + (lane & 31);
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) gv[rr] = ep.vec[(int64_t)__float_as_int(f[rr].w) * g.N + n];
         }
@@ -795,6 +804,233 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmParams g, 
   } else {
     epilogue<EPI, EC, false, NB, GRP == GRP_DW>(g, ep, m0, n0, rowf, roweb, acc);
   }
+}
+
+// --------------------------------------- grouped dW in 256 x 128 tiles ----
+// The grouped (MoE) dW writes one f32 matrix per expert from short K loops (an
+// expert's rows), so its time goes to the epilogue: a 256 x 256 tile's
+// 256 KiB of stores, during which the CU's matrix cores idle, because one
+// workgroup holding 256 accumulator registers per lane fills the CU.  Tiles of
+// 256 x 128 (four waves of 128 x 64, 128 accumulator registers) and a ring of
+// three 24 KiB stages let two workgroups share a CU, so one's epilogue runs
+// beside the other's K loop.  A is laid out as in the 256 x 256 ring; B's
+// k-rows are 128 bytes (8 chunks of 16), chunk c of k-row r at position
+// c ^ swz_n(r), swz_n(r) = ((r >> 1) & 3) << 1: the 8 k-rows of a transpose
+// read hold two k-rows per 256-byte bank row, and the swizzle puts their
+// aligned chunk pairs in the 8 different 32-byte bank groups.  A K step loads
+// the step two ahead into the slot of the step before (waiting for it at its
+// own start), and reads each half-step's fragments inside the step.
+constexpr int BN2 = 128;
+constexpr int kStage2Bytes = 24576;      // A tile (16 KB) + B tile (8 KB)
+static_assert(BM == kGemmThreads, "the grouped dW kernel loads one output row's factors per thread");
+__shared__ __attribute__((aligned(1024))) uint8_t g_nst0[kStage2Bytes];
+__shared__ __attribute__((aligned(1024))) uint8_t g_nst1[kStage2Bytes];
+__shared__ __attribute__((aligned(1024))) uint8_t g_nst2[kStage2Bytes];
+
+template <int S>
+__device__ __forceinline__ uint8_t* nstage() {
+  if constexpr (S == 0) return g_nst0;
+  else if constexpr (S == 1) return g_nst1;
+  else return g_nst2;
+}
+
+__device__ __forceinline__ int swz_n(int r) { return ((r >> 1) & 3) << 1; }
+
+struct LoadMap2 {          // per-thread byte offsets: 4 blocks of A, 2 of B
+  uint32_t a_off[4], b_off[2];
+  uint32_t a_step, b_step;
+  v4i ra, rb;
+};
+
+__device__ __forceinline__ LoadMap2 make_loadmap2(const GemmParams& g, int64_t m0, int64_t n0) {
+  LoadMap2 m;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {             // A block: 4 k-rows of 256 bytes
+    const int blk = wave * 4 + q;
+    const int kr = blk * 4 + (lane >> 4);
+    const int c = (lane & 15) ^ swz_m(kr);
+    m.a_off[q] = (uint32_t)(kr * g.lda + m0 + c * 16);
+  }
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {             // B block: 8 k-rows of 128 bytes
+    const int blk = wave * 2 + q;
+    const int kr = blk * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ swz_n(kr);
+    m.b_off[q] = (uint32_t)(kr * g.ldb + n0 + c * 16);
+  }
+  m.a_step = (uint32_t)(BK * g.lda);
+  m.b_step = (uint32_t)(BK * g.ldb);
+  m.ra = rsrc_words(g.A, (uint32_t)(g.K * g.lda));
+  m.rb = rsrc_words(g.B, (uint32_t)(g.K * g.ldb));
+  return m;
+}
+
+template <int S>
+__device__ __forceinline__ void stage_dma2(const LoadMap2& m, int q, int wave, int kt) {
+  if (q < 4)
+    dma_1k(m.ra, lds_addr(nstage<S>()) + (uint32_t)(wave * 4 + q) * 1024u, m.a_off[q], (uint32_t)kt * m.a_step);
+  else
+    dma_1k(m.rb, lds_addr(nstage<S>()) + (uint32_t)(kHalf + (wave * 2 + q - 4) * 1024), m.b_off[q - 4],
+           (uint32_t)kt * m.b_step);
+}
+template <int S>
+__device__ __forceinline__ void load_stage2(const LoadMap2& m, int kt) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+  for (int q = 0; q < 6; ++q) stage_dma2<S>(m, q, wave, kt);
+}
+
+struct FragMap2 { int a_t[4]; int b_t[2]; };
+
+__device__ __forceinline__ FragMap2 make_fragmap2() {
+  FragMap2 f;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int grp = lane >> 4, L = lane & 15;
+  const int krow = 16 * (grp >> 1) + (L >> 1);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ca = (wm * 128 + i * 32 + 16 * (grp & 1)) >> 4;
+    f.a_t[i] = krow * 256 + ((ca ^ swz_m(krow)) << 4) + 8 * (L & 1);
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int cb = (wn * 64 + j * 32 + 16 * (grp & 1)) >> 4;
+    f.b_t[j] = krow * 128 + ((cb ^ swz_n(krow)) << 4) + 8 * (L & 1);
+  }
+  return f;
+}
+
+struct Frags2 { v4i a[4], b[2]; };
+
+// Fragment x of half-step kk of stage S: x < 4 the A block x, else the B block x - 4.
+template <int S>
+__device__ __forceinline__ void read_frag2(const FragMap2& f, int kk, int x, Frags2& fr) {
+  if (x < 4) {
+    const uint8_t* p = nstage<S>() + f.a_t[x] + kk * 8192;
+    const v2i lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)p);
+    const v2i hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(p + 2048));   // k-rows + 8
+    fr.a[x] = v4i{lo.x, lo.y, hi.x, hi.y};
+  } else {
+    const uint8_t* p = nstage<S>() + kHalf + f.b_t[x - 4] + kk * 4096;
+    const v2i lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)p);
+    const v2i hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(p + 1024));   // k-rows + 8
+    fr.b[x - 4] = v4i{lo.x, lo.y, hi.x, hi.y};
+  }
+}
+
+// One K step on stage S = kt % 3.  The loads of step kt+1 may still be in flight at its start; the
+// barrier then publishes stage kt and retires stage kt-1, whose slot takes step kt+2.
+template <int S>
+__device__ __forceinline__ void k_step2(const LoadMap2& lm, const FragMap2& fm, int kt, v16i (&acc)[4][2]) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  S3R_WAIT_VM(6);
+  S3R_WAIT_LGKM0();
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  Frags2 cur, nxt;
+#pragma unroll
+  for (int x = 0; x < 6; ++x) read_frag2<S>(fm, 0, x, cur);
+#pragma unroll
+  for (int x = 0; x < 8; ++x) {
+    acc[x >> 1][x & 1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(cur.a[x >> 1], cur.b[x & 1], acc[x >> 1][x & 1], 0, 0, 0);
+    if (x < 6) {
+      read_frag2<S>(fm, 1, x, nxt);
+      stage_dma2<(S + 2) % 3>(lm, x, wave, kt + 2);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int x = 0; x < 8; ++x)
+    acc[x >> 1][x & 1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(nxt.a[x >> 1], nxt.b[x & 1], acc[x >> 1][x & 1], 0, 0, 0);
+}
+
+// The grouped dW (GRP_DW of gemm_i8_kernel) in 256 x 128 tiles, two workgroups per CU.  g.tiles_n counts
+// 128-column tiles.  EPI: EPI_DW or EPI_RAW.
+template <int EPI, bool EC>
+__global__ __launch_bounds__(kGemmThreads, 2) void gemm_dw128_kernel(GemmParams g, EpiParams ep, GroupGemm gg) {
+  if (gg.status[0] != 0) return;
+  const int per = g.tiles_m * g.tiles_n;
+  const int slot = blockIdx.x / per, local = blockIdx.x % per;
+  if (slot >= gg.G) return;
+  const int e = gg.order[slot];
+  const int64_t r0 = gg.offsets[e], n = gg.offsets[e + 1] - r0;
+  g.A += r0 * g.lda;
+  g.B += r0 * g.ldb;
+  g.K = n;
+  ep.delta += e;
+  ep.row_scale = advance(ep.row_scale, e * g.M);
+  ep.ebar = advance(ep.ebar, e * g.M);
+  ep.colsum = advance(ep.colsum, e * g.N);
+  ep.u = advance(ep.u, e * g.N);
+  ep.out = (char*)ep.out + e * gg.out_stride * 4;
+  ep.S = n > 0 ? n : 1;
+  ep.B = 1;
+  const int group = kGroupM * g.tiles_n;
+  const int first_m = (local / group) * kGroupM;
+  const int gsz = min(g.tiles_m - first_m, kGroupM);
+  const int tm = first_m + (local % group) % gsz;
+  const int tn = (local % group) / gsz;
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN2;
+  const int nk = (int)((g.K + BK - 1) / BK);
+
+  v16i acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = v16i{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+  // The epilogue's factors are loaded now, ahead of the ring's first loads, so their latency hides behind
+  // the K loop: this thread's row (x = Delta / s_w[j], y = 1 / s_w[j] and ebar[j]) and the lane's columns
+  // (u[n], xs[n] of its two column blocks).
+  const int64_t jrow = m0 + threadIdx.x;                    // BM == kGemmThreads
+  float pre_sw = 1.f, pre_eb = 0.f, pre_d = 1.f;
+  float pre[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+  if constexpr (EPI == EPI_DW) {
+    const int64_t jc = jrow < g.M ? jrow : 0;
+    pre_d = ep.delta[0];
+    if (ep.row_scale) pre_sw = ep.row_scale[jc];
+    if (EC) {
+      pre_eb = ep.ebar[jc];
+      const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 1;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int64_t nn = n0 + wn * 64 + j * 32 + (lane & 31);
+        const int64_t nc = nn < g.N ? nn : 0;
+        pre[0][j] = ep.u[nc];
+        pre[1][j] = (float)ep.colsum[nc];
+      }
+    }
+  }
+  const LoadMap2 lm = make_loadmap2(g, m0, n0);
+  const FragMap2 fm = make_fragmap2();
+  load_stage2<0>(lm, 0);
+  load_stage2<1>(lm, 1);
+  for (int kt = 0; kt < nk; kt += 3) {
+    k_step2<0>(lm, fm, kt, acc);
+    if (kt + 1 < nk) k_step2<1>(lm, fm, kt + 1, acc);
+    if (kt + 2 < nk) k_step2<2>(lm, fm, kt + 2, acc);
+  }
+  S3R_WAIT_VM(0);
+  S3R_WAIT_LGKM0();
+  __builtin_amdgcn_s_barrier();
+
+  // per-row factors of the tile into LDS (the ring is free now): x = Delta / s_w[j], y = 1 / s_w[j];
+  // roweb[r] = ebar[j] / s_w[j]
+  float4* rowf = reinterpret_cast<float4*>(g_nst0);
+  float* roweb = reinterpret_cast<float*>(g_nst1);
+  if constexpr (EPI == EPI_DW) {
+    float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (jrow < g.M) {
+      const float inv = ep.row_scale ? __fdiv_rn(1.f, pre_sw) : 1.f;
+      f.x = pre_d * inv;
+      f.y = inv;
+    }
+    if (EC) roweb[threadIdx.x] = jrow < g.M ? pre_eb * f.y : 0.f;
+    rowf[threadIdx.x] = f;
+  }
+  __syncthreads();
+  epilogue<EPI, EC, false, 1, true, 2>(g, ep, m0, n0, rowf, roweb, acc, pre);
 }
 
 // dW correction terms of examples 8 .. B-1 (the GEMM epilogue applies examples 0 .. 7):
@@ -1150,6 +1386,22 @@ hipError_t run_gemm(const GemmParams& g, const EpiParams& ep, hipStream_t st, co
   return e;
 }
 
+// The grouped dW in 256 x 128 tiles (gemm_dw128_kernel), with the same timing hook as run_gemm.
+template <int EPI, bool EC>
+hipError_t run_dw128(GemmParams g, const EpiParams& ep, hipStream_t st, const GroupGemm& gg) {
+  GemmTiming& tm = gemm_timing();
+  const GemmTiming ev = tm;
+  tm = GemmTiming{};
+  g.tiles_n = (int)((g.N + BN2 - 1) / BN2);
+  const int64_t nblocks = gg.G * g.tiles_m * g.tiles_n;
+  if (ev.start && hipEventRecord(ev.start, st) != hipSuccess) return hipErrorInvalidValue;
+  if (nblocks > 0)
+    hipLaunchKernelGGL((gemm_dw128_kernel<EPI, EC>), dim3((unsigned)nblocks), dim3(kGemmThreads), 0, st, g, ep, gg);
+  hipError_t e = hipGetLastError();
+  if (ev.stop && hipEventRecord(ev.stop, st) != hipSuccess && e == hipSuccess) e = hipErrorInvalidValue;
+  return e;
+}
+
 GemmParams make_gemm(const int8_t* A, int64_t lda, const int8_t* B, int64_t ldb, int64_t M, int64_t N, int64_t K) {
   GemmParams g;
   g.A = A; g.lda = lda; g.B = B; g.ldb = ldb; g.M = M; g.N = N; g.K = K;
@@ -1430,9 +1682,8 @@ hipError_t launch_grouped_backward_dw(const DwArgs& a, int64_t G, const int64_t*
   }
   GemmParams g = make_gemm(a.Q, a.ld_q, a.X, a.ld_x, a.D, a.d_in, a.T);
   GroupGemm gg{offsets, tab.tiles256, tab.order, tab.status, G, 0, out_stride, 0};
-  if (a.out_dt == S3R_I32_RAW) return run_gemm<false, EPI_RAW, false, 1, GRP_DW>(g, ep, st, gg);
-  return ep.ec ? run_gemm<false, EPI_DW, true, 1, GRP_DW>(g, ep, st, gg)
-               : run_gemm<false, EPI_DW, false, 1, GRP_DW>(g, ep, st, gg);
+  if (a.out_dt == S3R_I32_RAW) return run_dw128<EPI_RAW, false>(g, ep, st, gg);
+  return ep.ec ? run_dw128<EPI_DW, true>(g, ep, st, gg) : run_dw128<EPI_DW, false>(g, ep, st, gg);
 }
 
 }  // namespace s3r
