@@ -474,12 +474,39 @@ __device__ __forceinline__ int row_in_block(int r) { return (r >> 2) * 8 + (r & 
 // whose narrow outputs leave many tiles partial in N, and slower for the dense GEMMs, whose tiles are
 // whole.  Needs (rows + 127) * ld_out * 4 < 2^32 (the C ABI bounds ld_out for the grouped dW).
 // NJ: 32-column blocks per wave (4 in the 256 x 256 tiles, 2 in the 256 x 128 tiles of the grouped dW).
-// pre (NB == 1 dW, optional): the column factors u[n], xs[n] of the wave's NJ column blocks, loaded by the
-// caller ahead of time; otherwise they are loaded here.
+// Per-column factors of a lane's NJ column blocks: A (dX: r_W[n]; dW: u[n]), V (dX: v_b[n] of the tile's
+// example), B (dW: xs_b[n], slots past B hold 0), S (per-token dW: the column's step).  Every lane loads from
+// a valid column (its own, or column 0 past N, whose value is then discarded).
+template <int NB, int NJ> struct ColF { float A[NJ], V[NJ], B[NB][NJ], S[NJ]; };
+
+template <int EPI, bool EC, int NB, int NJ>
+__device__ __forceinline__ void load_cols(const GemmParams& g, const EpiParams& ep, int64_t m0, int64_t n0,
+                                          ColF<NB, NJ>& c) {
+  const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 1;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int64_t n = n0 + wn * (NJ * 32) + j * 32 + (lane & 31);
+    const int64_t nc = n < g.N ? n : 0;
+    c.A[j] = 0.f; c.V[j] = 0.f; c.S[j] = 1.f;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) c.B[b][j] = 0.f;
+    if constexpr (EPI == EPI_DWC) c.S[j] = ep.colstep[nc];
+    if constexpr (EC && is_dx(EPI)) {
+      c.A[j] = (float)ep.colsum[nc];
+      c.V[j] = ep.vec[(m0 / ep.S) * g.N + nc];       // the example of the tile's first row (unused when gathered)
+    } else if constexpr (EC && is_dw(EPI)) {
+      c.A[j] = ep.u[nc];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) c.B[b][j] = (float)ep.colsum[(b < ep.B ? b : 0) * g.N + nc] * (b < ep.B ? 1.f : 0.f);
+    }
+  }
+}
+
+// pre (optional): the column factors, loaded by the caller ahead of time; otherwise they are loaded here.
 template <int EPI, bool EC, bool GATHER, int NB, bool DROP = false, int NJ = 4>
 __device__ __forceinline__ void epilogue(const GemmParams& g, const EpiParams& ep, int64_t m0, int64_t n0,
                                          const float4* rowf, const float* roweb, v16i (&acc)[4][NJ],
-                                         const float (*pre)[NJ] = nullptr) {
+                                         const ColF<NB, NJ>* pre = nullptr) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int rows_here = (int)min((int64_t)BM, g.M - m0);
@@ -490,38 +517,25 @@ __device__ __forceinline__ void epilogue(const GemmParams& g, const EpiParams& e
   // rowf: per-row factors; roweb (dW): ebar[b][row] / s_w[row]
   const int lane_row = wm * 128 + (lane >> 5) * 4;                  // + i*32 + row_in_block(r)
 
-  // per-column values of this lane, one per column block j.  Every lane loads from a valid
-  // column (its own, or column 0 past N, whose value is then discarded), outside any branch,
-  // and waits for the loads once here: a load still pending inside the store loop would make
-  // each group of stores wait for every store before it (vmcnt counts stores too).
-  float colA[NJ], colV[NJ], colB[NB][NJ], colS[NJ];
+  // per-column values of this lane, one per column block j, loaded outside any branch (or ahead of time by
+  // the caller) and waited for once here: a load still pending inside the store loop would make each group
+  // of stores wait for every store before it (vmcnt counts stores too).
+  // DROP: a column past N gets an offset past the descriptor's range, where the hardware drops the store.
+  ColF<NB, NJ> cf;
+  if (pre) cf = *pre;
+  else load_cols<EPI, EC, NB, NJ>(g, ep, m0, n0, cf);
+  const float (&colA)[NJ] = cf.A;
+  const float (&colV)[NJ] = cf.V;
+  const float (&colS)[NJ] = cf.S;
+  const float (&colB)[NB][NJ] = cf.B;
   bool n_ok[NJ];
   uint32_t voff[NJ];
-  const uint32_t off_none = (uint32_t)rows_here * ld4;   // DROP: past the descriptor's range
+  const uint32_t off_none = (uint32_t)rows_here * ld4;
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int64_t n = n0 + wn * (NJ * 32) + j * 32 + (lane & 31);
     n_ok[j] = n < g.N;
-    const int64_t nc = n_ok[j] ? n : 0;
     voff[j] = (DROP && !n_ok[j]) ? off_none : (uint32_t)(lane_row * ld4 + n * esz);
-    colA[j] = 0.f; colV[j] = 0.f; colS[j] = 1.f;
-#pragma unroll
-    for (int b = 0; b < NB; ++b) colB[b][j] = 0.f;
-    if constexpr (EPI == EPI_DWC) colS[j] = ep.colstep[nc];
-    if constexpr (EC && is_dx(EPI)) {
-      colA[j] = (float)ep.colsum[nc];                                    // r_W[n]
-      if constexpr (!GATHER) colV[j] = ep.vec[(m0 / ep.S) * g.N + nc];   // v_b[n], the tile's example
-    } else if constexpr (EC && is_dw(EPI)) {
-      if (NB == 1 && pre) {
-        colA[j] = pre[0][j];
-        colB[0][j] = pre[1][j];
-      } else {
-        colA[j] = ep.u[nc];
-#pragma unroll
-        for (int b = 0; b < NB; ++b)                                     // xs_b[n]; slots past B hold 0
-          colB[b][j] = (float)ep.colsum[(b < ep.B ? b : 0) * g.N + nc] * (b < ep.B ? 1.f : 0.f);
-      }
-    }
   }
   S3R_WAIT_VM(0);
 
@@ -619,6 +633,8 @@ struct GroupGemm {
   EpiParams ep2;
 };
 
+static_assert(BM == kGemmThreads, "the GEMM kernels load one output row's epilogue factors per thread");
+
 template <bool A_KMAJOR, int EPI, bool EC, int NB, int GRP = GRP_NONE>
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmParams g, EpiParams ep, GroupGemm gg) {
   int tm, tn;
@@ -707,6 +723,33 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmParams g, 
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = v16i{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
 
+  // The dense dX kernels load the epilogue's factors now, ahead of the ring's first loads, so their latency
+  // hides behind the K loop: this thread's output row (BM == kGemmThreads) and the lane's columns.  (The
+  // dW ring and the grouped kernels keep their registers for the loop: there the values would spill.)
+  constexpr bool PRE = A_KMAJOR && GRP == GRP_NONE && EPI != EPI_RAW;
+  ColF<NB, 4> cf;
+  const int64_t prow = m0 + threadIdx.x;
+  const int64_t prc = prow < g.M ? prow : 0;
+  float p_d = 1.f, p_s = 1.f, p_er = 0.f, p_em = 0.f, p_eb[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) p_eb[b] = 0.f;
+  if constexpr (PRE) {
+    load_cols<EPI, EC, NB, 4>(g, ep, m0, n0, cf);
+    if (ep.row_scale) p_s = ep.row_scale[prc];
+    if constexpr (is_dx(EPI)) {
+      p_d = ep.per_token ? ep.delta[prc] : ep.delta[0];
+      if (EC) {
+        p_er = ep.ec_row[prc];
+        p_em = ep.ec_mean[prc / ep.S];
+      }
+    } else {
+      p_d = ep.delta[0];
+      if (EC)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) p_eb[b] = b < ep.B ? ep.ebar[b * g.M + prc] : 0.f;
+    }
+  }
+
   if constexpr (A_KMAJOR) {
     const UnitMap lm = make_unitmap(g, m0, n0);
     const UnitFragMap fm = make_unit_fragmap();
@@ -761,48 +804,57 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmParams g, 
   // per-row factors of the tile into LDS (the ring is free now)
   float4* rowf = reinterpret_cast<float4*>(A_KMAJOR ? g_unit0 : g_stage0);
   float* roweb = reinterpret_cast<float*>(A_KMAJOR ? g_unit1 : g_stage1);
+  const int r = threadIdx.x;
+  if constexpr (!PRE && EPI != EPI_RAW) {         // the row factors, loaded now
+    if (ep.row_scale) p_s = ep.row_scale[prc];
+    if constexpr (is_dx(EPI)) {
+      p_d = ep.per_token ? ep.delta[prc] : ep.delta[0];
+      if (EC) {
+        p_er = ep.ec_row[prc];
+        p_em = ep.ec_mean[prc / ep.S];
+      }
+    } else {
+      p_d = ep.delta[0];
+      if (EC)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) p_eb[b] = b < ep.B ? ep.ebar[b * g.M + prc] : 0.f;
+    }
+  }
   if constexpr (is_dx(EPI)) {
     // x: Delta_t / s_x[t], y: 1 / s_x[t], z: (eps_t - mu_b) / s_x[t], w: example index
-    for (int r = threadIdx.x; r < BM; r += kGemmThreads) {
-      const int64_t tt = m0 + r;
-      float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (tt < g.M) {
-        const float d = ep.per_token ? ep.delta[tt] : ep.delta[0];
-        const float inv = ep.row_scale ? __fdiv_rn(1.f, ep.row_scale[tt]) : 1.f;
-        f.x = d * inv;
-        f.y = inv;
-        if (EC) {
-          const int64_t b = tt / ep.S;
-          f.z = (ep.ec_row[tt] - ep.ec_mean[b]) * inv;
-          f.w = __int_as_float((int)b);
-        }
+    float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (prow < g.M) {
+      const float inv = ep.row_scale ? __fdiv_rn(1.f, p_s) : 1.f;
+      f.x = p_d * inv;
+      f.y = inv;
+      if (EC) {
+        f.z = (p_er - p_em) * inv;
+        f.w = __int_as_float((int)(prow / ep.S));
       }
-      rowf[r] = f;
     }
+    rowf[r] = f;
   } else if constexpr (is_dw(EPI)) {
     // x: Delta / s_w[j] (EPI_DWC: 1 / s_w[j], the step is per column), y: 1 / s_w[j];
     // roweb[b * BM + r] = ebar[b][j] / s_w[j]
-    for (int r = threadIdx.x; r < BM; r += kGemmThreads) {
-      const int64_t j = m0 + r;
-      float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (j < g.M) {
-        const float inv = ep.row_scale ? __fdiv_rn(1.f, ep.row_scale[j]) : 1.f;
-        f.x = EPI == EPI_DWC ? inv : ep.delta[0] * inv;
-        f.y = inv;
-      }
-      if (EC)
-#pragma unroll
-        for (int b = 0; b < NB; ++b) roweb[b * BM + r] = (b < ep.B && j < g.M) ? ep.ebar[b * g.M + j] * f.y : 0.f;
-      rowf[r] = f;
+    float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (prow < g.M) {
+      const float inv = ep.row_scale ? __fdiv_rn(1.f, p_s) : 1.f;
+      f.x = EPI == EPI_DWC ? inv : p_d * inv;
+      f.y = inv;
     }
+    if (EC)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) roweb[b * BM + r] = (b < ep.B && prow < g.M) ? p_eb[b] * f.y : 0.f;
+    rowf[r] = f;
   }
   __syncthreads();
+  const ColF<NB, 4>* pre = PRE ? &cf : nullptr;
   if constexpr (is_dx(EPI) && EC) {
     const int64_t last = min(m0 + BM, g.M) - 1;
-    if (m0 / ep.S == last / ep.S) epilogue<EPI, EC, false, NB>(g, ep, m0, n0, rowf, roweb, acc);
-    else epilogue<EPI, EC, true, NB>(g, ep, m0, n0, rowf, roweb, acc);
+    if (m0 / ep.S == last / ep.S) epilogue<EPI, EC, false, NB>(g, ep, m0, n0, rowf, roweb, acc, pre);
+    else epilogue<EPI, EC, true, NB>(g, ep, m0, n0, rowf, roweb, acc, pre);
   } else {
-    epilogue<EPI, EC, false, NB, GRP == GRP_DW>(g, ep, m0, n0, rowf, roweb, acc);
+    epilogue<EPI, EC, false, NB>(g, ep, m0, n0, rowf, roweb, acc, pre);
   }
 }
 
@@ -822,7 +874,6 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmParams g, 
 // own start), and reads each half-step's fragments inside the step.
 constexpr int BN2 = 128;
 constexpr int kStage2Bytes = 24576;      // A tile (16 KB) + B tile (8 KB)
-static_assert(BM == kGemmThreads, "the grouped dW kernel loads one output row's factors per thread");
 __shared__ __attribute__((aligned(1024))) uint8_t g_nst0[kStage2Bytes];
 __shared__ __attribute__((aligned(1024))) uint8_t g_nst1[kStage2Bytes];
 __shared__ __attribute__((aligned(1024))) uint8_t g_nst2[kStage2Bytes];
@@ -985,22 +1036,13 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_dw128_kernel(GemmParams 
   // (u[n], xs[n] of its two column blocks).
   const int64_t jrow = m0 + threadIdx.x;                    // BM == kGemmThreads
   float pre_sw = 1.f, pre_eb = 0.f, pre_d = 1.f;
-  float pre[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+  ColF<1, 2> pre;
   if constexpr (EPI == EPI_DW) {
     const int64_t jc = jrow < g.M ? jrow : 0;
     pre_d = ep.delta[0];
     if (ep.row_scale) pre_sw = ep.row_scale[jc];
-    if (EC) {
-      pre_eb = ep.ebar[jc];
-      const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 1;
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int64_t nn = n0 + wn * 64 + j * 32 + (lane & 31);
-        const int64_t nc = nn < g.N ? nn : 0;
-        pre[0][j] = ep.u[nc];
-        pre[1][j] = (float)ep.colsum[nc];
-      }
-    }
+    if (EC) pre_eb = ep.ebar[jc];
+    load_cols<EPI, EC, 1, 2>(g, ep, m0, n0, pre);
   }
   const LoadMap2 lm = make_loadmap2(g, m0, n0);
   const FragMap2 fm = make_fragmap2();
@@ -1030,7 +1072,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_dw128_kernel(GemmParams 
     rowf[threadIdx.x] = f;
   }
   __syncthreads();
-  epilogue<EPI, EC, false, 1, true, 2>(g, ep, m0, n0, rowf, roweb, acc, pre);
+  epilogue<EPI, EC, false, 1, true, 2>(g, ep, m0, n0, rowf, roweb, acc, EPI == EPI_DW ? &pre : nullptr);
 }
 
 // dW correction terms of examples 8 .. B-1 (the GEMM epilogue applies examples 0 .. 7):
