@@ -612,14 +612,15 @@ __device__ __forceinline__ void epilogue(const GemmParams& g, const EpiParams& e
 // Grouped launches (GRP != 0): rows sorted by group, group e owning rows
 // [offsets[e], offsets[e+1]).  GRP_DX: a row tile of one group's Q against
 // its own weight codes (B + e * b_stride); the grid is an upper bound on the
-// groups' row tiles times the column tiles.  GRP_DW: one output matrix per
-// group (out + e * out_stride), K = the group's rows; groups are taken largest
-// first (order[]), so the longest K loops start first.  Each workgroup rebases
-// the operand, output and epilogue pointers to its group, after which the
-// dense kernel body runs unchanged.  Nothing runs if the offsets were invalid.
-// GRP_PAIR: two problems of one shape that share the B operand (the dW products
-// of two projections of one input), tiles [0, per) of the first and [per, 2 per)
-// of the second; the second's A operand and epilogue come from gg.
+// groups' row tiles times the column tiles.  GRP_DW (gemm_dw128_kernel): one
+// output matrix per group (out + e * out_stride), K = the group's rows; groups
+// are taken largest first (order[]), so the longest K loops start first.  Each
+// workgroup rebases the operand, output and epilogue pointers to its group,
+// after which the dense kernel body runs unchanged.  Nothing runs if the
+// offsets were invalid.  GRP_PAIR: two problems of one shape that share the B
+// operand (the dW products of two projections of one input), tiles [0, per) of
+// the first and [per, 2 per) of the second; the second's A operand and
+// epilogue come from gg.
 enum { GRP_NONE = 0, GRP_DX = 1, GRP_DW = 2, GRP_PAIR = 3 };
 template <typename T>
 __device__ __forceinline__ const T* advance(const T* p, int64_t k) { return p ? p + k : p; }
@@ -673,7 +674,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmParams g, 
     ep.B = 1;
     tm = mt - h.t0;
     tn = bid % g.tiles_n;
-  } else if constexpr (GRP == GRP_PAIR) {
+  } else {
+    static_assert(GRP == GRP_PAIR, "the grouped dW runs in gemm_dw128_kernel");
     // XCD-aware numbering over both problems' tiles, then the grouped order within a problem
     const int per = g.tiles_m * g.tiles_n;
     const int nblocks = 2 * per;
@@ -685,29 +687,6 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmParams g, 
       g.A = gg.A2;
       ep = gg.ep2;
     }
-    const int group = kGroupM * g.tiles_n;
-    const int first_m = (local / group) * kGroupM;
-    const int gsz = min(g.tiles_m - first_m, kGroupM);
-    tm = first_m + (local % group) % gsz;
-    tn = (local % group) / gsz;
-  } else {
-    if (gg.status[0] != 0) return;
-    const int per = g.tiles_m * g.tiles_n;
-    const int slot = blockIdx.x / per, local = blockIdx.x % per;
-    if (slot >= gg.G) return;
-    const int e = gg.order[slot];
-    const int64_t r0 = gg.offsets[e], n = gg.offsets[e + 1] - r0;
-    g.A += r0 * g.lda;            // Q rows of the group: the K dimension of Q^T
-    g.B += r0 * g.ldb;
-    g.K = n;
-    ep.delta += e;
-    ep.row_scale = advance(ep.row_scale, e * g.M);
-    ep.ebar = advance(ep.ebar, e * g.M);
-    ep.colsum = advance(ep.colsum, e * g.N);
-    ep.u = advance(ep.u, e * g.N);
-    ep.out = (char*)ep.out + e * gg.out_stride * 4;
-    ep.S = n > 0 ? n : 1;
-    ep.B = 1;
     const int group = kGroupM * g.tiles_n;
     const int first_m = (local / group) * kGroupM;
     const int gsz = min(g.tiles_m - first_m, kGroupM);
@@ -725,7 +704,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmParams g, 
 
   // The dense dX kernels load the epilogue's factors now, ahead of the ring's first loads, so their latency
   // hides behind the K loop: this thread's output row (BM == kGemmThreads) and the lane's columns.  (The
-  // dW ring and the grouped kernels keep their registers for the loop: there the values would spill.)
+  // paired dW and the grouped dX keep their registers for the loop: there the values would spill.)
   constexpr bool PRE = A_KMAJOR && GRP == GRP_NONE && EPI != EPI_RAW;
   ColF<NB, 4> cf;
   const int64_t prow = m0 + threadIdx.x;
@@ -858,20 +837,24 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmParams g, 
   }
 }
 
-// --------------------------------------- grouped dW in 256 x 128 tiles ----
-// The grouped (MoE) dW writes one f32 matrix per expert from short K loops (an
-// expert's rows), so its time goes to the epilogue: a 256 x 256 tile's
-// 256 KiB of stores, during which the CU's matrix cores idle, because one
-// workgroup holding 256 accumulator registers per lane fills the CU.  Tiles of
+// ------------------------------------------------ dW in 256 x 128 tiles ----
+// With one workgroup per CU (256 accumulator registers per lane) a CU's matrix
+// cores idle while its tile's 256 KiB of f32 results are stored.  Tiles of
 // 256 x 128 (four waves of 128 x 64, 128 accumulator registers) and a ring of
 // three 24 KiB stages let two workgroups share a CU, so one's epilogue runs
-// beside the other's K loop.  A is laid out as in the 256 x 256 ring; B's
-// k-rows are 128 bytes (8 chunks of 16), chunk c of k-row r at position
-// c ^ swz_n(r), swz_n(r) = ((r >> 1) & 3) << 1: the 8 k-rows of a transpose
-// read hold two k-rows per 256-byte bank row, and the swizzle puts their
-// aligned chunk pairs in the 8 different 32-byte bank groups.  A K step loads
-// the step two ahead into the slot of the step before (waiting for it at its
-// own start), and reads each half-step's fragments inside the step.
+// beside the other's K loop.  That pays where the epilogue weighs most: the
+// grouped (MoE) dW, whose K loops are an expert's rows, and a single dW whose
+// 256 x 256 tiles leave the last round of the CUs part-filled (there a lone
+// workgroup has its CU to itself).  It costs LDS bandwidth (a K step reads
+// 1.5x the operand bytes per multiply of the 256 x 256 tile), so the paired
+// gate / up dW, whose 1792 tiles of 256 x 256 fill whole rounds, stays there.
+// A is laid out as in the 256 x 256 ring; B's k-rows are 128 bytes (8 chunks
+// of 16), chunk c of k-row r at position c ^ swz_n(r), swz_n(r) =
+// ((r >> 1) & 3) << 1: the 8 k-rows of a transpose read hold two k-rows per
+// 256-byte bank row, and the swizzle puts their aligned chunk pairs in the 8
+// different 32-byte bank groups.  A K step loads the step two ahead into the
+// slot of the step before (waiting for it at its own start), and reads each
+// half-step's fragments inside the step.
 constexpr int BN2 = 128;
 constexpr int kStage2Bytes = 24576;      // A tile (16 KB) + B tile (8 KB)
 __shared__ __attribute__((aligned(1024))) uint8_t g_nst0[kStage2Bytes];
@@ -997,27 +980,38 @@ __device__ __forceinline__ void k_step2(const LoadMap2& lm, const FragMap2& fm, 
     acc[x >> 1][x & 1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(nxt.a[x >> 1], nxt.b[x & 1], acc[x >> 1][x & 1], 0, 0, 0);
 }
 
-// The grouped dW (GRP_DW of gemm_i8_kernel) in 256 x 128 tiles, two workgroups per CU.  g.tiles_n counts
-// 128-column tiles.  EPI: EPI_DW or EPI_RAW.
-template <int EPI, bool EC>
+// The dW GEMMs in 256 x 128 tiles, two workgroups per CU.  g.tiles_n counts 128-column tiles.  GRP:
+// GRP_NONE (one product) or GRP_DW (one product per group).  EPI: EPI_DW, EPI_DWC or EPI_RAW; NB: the
+// examples whose correction terms the epilogue applies.
+template <int EPI, bool EC, int NB, int GRP>
 __global__ __launch_bounds__(kGemmThreads, 2) void gemm_dw128_kernel(GemmParams g, EpiParams ep, GroupGemm gg) {
-  if (gg.status[0] != 0) return;
-  const int per = g.tiles_m * g.tiles_n;
-  const int slot = blockIdx.x / per, local = blockIdx.x % per;
-  if (slot >= gg.G) return;
-  const int e = gg.order[slot];
-  const int64_t r0 = gg.offsets[e], n = gg.offsets[e + 1] - r0;
-  g.A += r0 * g.lda;
-  g.B += r0 * g.ldb;
-  g.K = n;
-  ep.delta += e;
-  ep.row_scale = advance(ep.row_scale, e * g.M);
-  ep.ebar = advance(ep.ebar, e * g.M);
-  ep.colsum = advance(ep.colsum, e * g.N);
-  ep.u = advance(ep.u, e * g.N);
-  ep.out = (char*)ep.out + e * gg.out_stride * 4;
-  ep.S = n > 0 ? n : 1;
-  ep.B = 1;
+  static_assert(GRP == GRP_NONE || GRP == GRP_DW, "one product, or one per group");
+  int local;
+  if constexpr (GRP == GRP_DW) {
+    if (gg.status[0] != 0) return;
+    const int per = g.tiles_m * g.tiles_n;
+    const int slot = blockIdx.x / per;
+    local = blockIdx.x % per;
+    if (slot >= gg.G) return;
+    const int e = gg.order[slot];
+    const int64_t r0 = gg.offsets[e], n = gg.offsets[e + 1] - r0;
+    g.A += r0 * g.lda;
+    g.B += r0 * g.ldb;
+    g.K = n;
+    ep.delta += e;
+    ep.row_scale = advance(ep.row_scale, e * g.M);
+    ep.ebar = advance(ep.ebar, e * g.M);
+    ep.colsum = advance(ep.colsum, e * g.N);
+    ep.u = advance(ep.u, e * g.N);
+    ep.out = (char*)ep.out + e * gg.out_stride * 4;
+    ep.S = n > 0 ? n : 1;
+    ep.B = 1;
+  } else {
+    // XCD-aware numbering, then the grouped order
+    const int nblocks = g.tiles_m * g.tiles_n;
+    local = blockIdx.x;
+    if (nblocks % kNumXcd == 0) local = (local % kNumXcd) * (nblocks / kNumXcd) + local / kNumXcd;
+  }
   const int group = kGroupM * g.tiles_n;
   const int first_m = (local / group) * kGroupM;
   const int gsz = min(g.tiles_m - first_m, kGroupM);
@@ -1032,17 +1026,21 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_dw128_kernel(GemmParams 
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = v16i{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
   // The epilogue's factors are loaded now, ahead of the ring's first loads, so their latency hides behind
-  // the K loop: this thread's row (x = Delta / s_w[j], y = 1 / s_w[j] and ebar[j]) and the lane's columns
-  // (u[n], xs[n] of its two column blocks).
+  // the K loop: this thread's row (Delta, s_w[j] and ebar[b][j]) and the lane's columns (u[n], xs[b][n] and
+  // the per-column steps of its two column blocks).
   const int64_t jrow = m0 + threadIdx.x;                    // BM == kGemmThreads
-  float pre_sw = 1.f, pre_eb = 0.f, pre_d = 1.f;
-  ColF<1, 2> pre;
-  if constexpr (EPI == EPI_DW) {
+  float pre_sw = 1.f, pre_d = 1.f, pre_eb[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) pre_eb[b] = 0.f;
+  ColF<NB, 2> pre;
+  if constexpr (EPI != EPI_RAW) {
     const int64_t jc = jrow < g.M ? jrow : 0;
     pre_d = ep.delta[0];
     if (ep.row_scale) pre_sw = ep.row_scale[jc];
-    if (EC) pre_eb = ep.ebar[jc];
-    load_cols<EPI, EC, 1, 2>(g, ep, m0, n0, pre);
+    if (EC)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) pre_eb[b] = b < ep.B ? ep.ebar[b * g.M + jc] : 0.f;
+    load_cols<EPI, EC, NB, 2>(g, ep, m0, n0, pre);
   }
   const LoadMap2 lm = make_loadmap2(g, m0, n0);
   const FragMap2 fm = make_fragmap2();
@@ -1057,22 +1055,26 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_dw128_kernel(GemmParams 
   S3R_WAIT_LGKM0();
   __builtin_amdgcn_s_barrier();
 
-  // per-row factors of the tile into LDS (the ring is free now): x = Delta / s_w[j], y = 1 / s_w[j];
-  // roweb[r] = ebar[j] / s_w[j]
+  // per-row factors of the tile into LDS (the ring is free now): x = Delta / s_w[j] (EPI_DWC: 1 / s_w[j], the
+  // step is per column), y = 1 / s_w[j]; roweb[b * BM + r] = ebar[b][j] / s_w[j]
   float4* rowf = reinterpret_cast<float4*>(g_nst0);
   float* roweb = reinterpret_cast<float*>(g_nst1);
-  if constexpr (EPI == EPI_DW) {
+  if constexpr (EPI != EPI_RAW) {
     float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
     if (jrow < g.M) {
       const float inv = ep.row_scale ? __fdiv_rn(1.f, pre_sw) : 1.f;
-      f.x = pre_d * inv;
+      f.x = EPI == EPI_DWC ? inv : pre_d * inv;
       f.y = inv;
     }
-    if (EC) roweb[threadIdx.x] = jrow < g.M ? pre_eb * f.y : 0.f;
+    if (EC)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) roweb[b * BM + threadIdx.x] = (b < ep.B && jrow < g.M) ? pre_eb[b] * f.y : 0.f;
     rowf[threadIdx.x] = f;
   }
   __syncthreads();
-  epilogue<EPI, EC, false, 1, true, 2>(g, ep, m0, n0, rowf, roweb, acc, EPI == EPI_DW ? &pre : nullptr);
+  // The grouped dW drops the stores of columns past N by an offset past the output descriptor (its callers bound
+  // ld so that offset cannot wrap); the others branch around them.
+  epilogue<EPI, EC, false, NB, GRP == GRP_DW, 2>(g, ep, m0, n0, rowf, roweb, acc, EPI != EPI_RAW ? &pre : nullptr);
 }
 
 // dW correction terms of examples 8 .. B-1 (the GEMM epilogue applies examples 0 .. 7):
@@ -1417,8 +1419,7 @@ hipError_t run_gemm(const GemmParams& g, const EpiParams& ep, hipStream_t st, co
   tm = GemmTiming{};
   const int nblocks = GRP == GRP_NONE ? g.tiles_m * g.tiles_n
                       : GRP == GRP_DX   ? gg.tiles_m_all * g.tiles_n
-                      : GRP == GRP_PAIR ? 2 * g.tiles_m * g.tiles_n
-                                        : (int)gg.G * g.tiles_m * g.tiles_n;
+                                        : 2 * g.tiles_m * g.tiles_n;
   if (ev.start && hipEventRecord(ev.start, st) != hipSuccess) return hipErrorInvalidValue;
   if (nblocks > 0)
     hipLaunchKernelGGL((gemm_i8_kernel<A_KMAJOR, EPI, EC, NB, GRP>), dim3((unsigned)nblocks), dim3(kGemmThreads), 0,
@@ -1428,17 +1429,19 @@ hipError_t run_gemm(const GemmParams& g, const EpiParams& ep, hipStream_t st, co
   return e;
 }
 
-// The grouped dW in 256 x 128 tiles (gemm_dw128_kernel), with the same timing hook as run_gemm.
-template <int EPI, bool EC>
-hipError_t run_dw128(GemmParams g, const EpiParams& ep, hipStream_t st, const GroupGemm& gg) {
+// The dW GEMMs in 256 x 128 tiles (gemm_dw128_kernel), with the same timing hook as run_gemm.
+template <int EPI, bool EC, int NB, int GRP>
+hipError_t run_dw128(GemmParams g, const EpiParams& ep, hipStream_t st, const GroupGemm& gg = GroupGemm{}) {
   GemmTiming& tm = gemm_timing();
   const GemmTiming ev = tm;
   tm = GemmTiming{};
   g.tiles_n = (int)((g.N + BN2 - 1) / BN2);
-  const int64_t nblocks = gg.G * g.tiles_m * g.tiles_n;
+  const int64_t per = (int64_t)g.tiles_m * g.tiles_n;
+  const int64_t nblocks = GRP == GRP_DW ? gg.G * per : per;
   if (ev.start && hipEventRecord(ev.start, st) != hipSuccess) return hipErrorInvalidValue;
   if (nblocks > 0)
-    hipLaunchKernelGGL((gemm_dw128_kernel<EPI, EC>), dim3((unsigned)nblocks), dim3(kGemmThreads), 0, st, g, ep, gg);
+    hipLaunchKernelGGL((gemm_dw128_kernel<EPI, EC, NB, GRP>), dim3((unsigned)nblocks), dim3(kGemmThreads), 0, st, g,
+                       ep, gg);
   hipError_t e = hipGetLastError();
   if (ev.stop && hipEventRecord(ev.stop, st) != hipSuccess && e == hipSuccess) e = hipErrorInvalidValue;
   return e;
@@ -1588,20 +1591,20 @@ hipError_t launch_backward_dw(const DwArgs& a, hipStream_t st) {
   }
   // dW = Q^T B: A[m=j][k=t] = Q[t][j] (M-contiguous), B [T x d_in] (N-contiguous)
   const GemmParams g = make_gemm(a.Q, a.ld_q, Bop, ldb, a.D, a.d_in, a.T);
-  if (a.out_dt == S3R_I32_RAW) return run_gemm<false, EPI_RAW, false>(g, ep, st);
+  if (a.out_dt == S3R_I32_RAW) return run_dw128<EPI_RAW, false, 1, GRP_NONE>(g, ep, st);
   hipError_t e;
   if (a.per_token) {
-    if (!ep.ec) e = run_gemm<false, EPI_DWC, false>(g, ep, st);
-    else if (B <= 1) e = run_gemm<false, EPI_DWC, true, 1>(g, ep, st);
-    else if (B <= 2) e = run_gemm<false, EPI_DWC, true, 2>(g, ep, st);
-    else if (B <= 4) e = run_gemm<false, EPI_DWC, true, 4>(g, ep, st);
-    else e = run_gemm<false, EPI_DWC, true, kMaxB>(g, ep, st);
+    if (!ep.ec) e = run_dw128<EPI_DWC, false, 1, GRP_NONE>(g, ep, st);
+    else if (B <= 1) e = run_dw128<EPI_DWC, true, 1, GRP_NONE>(g, ep, st);
+    else if (B <= 2) e = run_dw128<EPI_DWC, true, 2, GRP_NONE>(g, ep, st);
+    else if (B <= 4) e = run_dw128<EPI_DWC, true, 4, GRP_NONE>(g, ep, st);
+    else e = run_dw128<EPI_DWC, true, kMaxB, GRP_NONE>(g, ep, st);
   } else {
-    if (!ep.ec) e = run_gemm<false, EPI_DW, false>(g, ep, st);
-    else if (B <= 1) e = run_gemm<false, EPI_DW, true, 1>(g, ep, st);
-    else if (B <= 2) e = run_gemm<false, EPI_DW, true, 2>(g, ep, st);
-    else if (B <= 4) e = run_gemm<false, EPI_DW, true, 4>(g, ep, st);
-    else e = run_gemm<false, EPI_DW, true, kMaxB>(g, ep, st);
+    if (!ep.ec) e = run_dw128<EPI_DW, false, 1, GRP_NONE>(g, ep, st);
+    else if (B <= 1) e = run_dw128<EPI_DW, true, 1, GRP_NONE>(g, ep, st);
+    else if (B <= 2) e = run_dw128<EPI_DW, true, 2, GRP_NONE>(g, ep, st);
+    else if (B <= 4) e = run_dw128<EPI_DW, true, 4, GRP_NONE>(g, ep, st);
+    else e = run_dw128<EPI_DW, true, kMaxB, GRP_NONE>(g, ep, st);
   }
   if (e != hipSuccess) return e;
   return dw_rank_update(a, ep, st);
@@ -1724,8 +1727,8 @@ hipError_t launch_grouped_backward_dw(const DwArgs& a, int64_t G, const int64_t*
   }
   GemmParams g = make_gemm(a.Q, a.ld_q, a.X, a.ld_x, a.D, a.d_in, a.T);
   GroupGemm gg{offsets, tab.tiles256, tab.order, tab.status, G, 0, out_stride, 0};
-  if (a.out_dt == S3R_I32_RAW) return run_dw128<EPI_RAW, false>(g, ep, st, gg);
-  return ep.ec ? run_dw128<EPI_DW, true>(g, ep, st, gg) : run_dw128<EPI_DW, false>(g, ep, st, gg);
+  if (a.out_dt == S3R_I32_RAW) return run_dw128<EPI_RAW, false, 1, GRP_DW>(g, ep, st, gg);
+  return ep.ec ? run_dw128<EPI_DW, true, 1, GRP_DW>(g, ep, st, gg) : run_dw128<EPI_DW, false, 1, GRP_DW>(g, ep, st, gg);
 }
 
 }  // namespace s3r
