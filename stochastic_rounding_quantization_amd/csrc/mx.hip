@@ -506,29 +506,34 @@ __global__ __launch_bounds__(256) void mx_mean_kernel(int64_t S, const float* __
 // ------------------------------------------------------------- FP4 GEMM ----
 // out [M x N] (f32) = A [M x K] . B [N x K]^T with both operands MXFP4: codes in
 // the 256-row block layout (ld: the bytes between 256-row blocks), E8M0 scales
-// [K/128][rows][4].  256 x 256 tile per 256-thread workgroup, four waves of 128
-// x 128 (4 x 4 blocks of v_mfma_scale_f32_32x32x64_f8f6f4).  A stage covers 256
-// elements of K: the A and B tiles are two consecutive 16 KiB code blocks each,
-// one contiguous 32 KiB run per operand, plus the rows' scale words of the
-// stage's two 128-element steps, all moved global -> LDS by buffer-load DMA;
-// two stages alternate, the next one loading while the current one feeds 64
-// MFMAs per wave.  (Four single-step stages, loads issued three steps ahead,
-// were 6 % slower: half the MFMA work between barriers.)
+// [K/128][rows][4].  256 x 128 tile per 256-thread workgroup, four waves of 128
+// x 64 (4 x 2 blocks of v_mfma_scale_f32_32x32x64_f8f6f4, 128 accumulator
+// registers a lane), so two workgroups share a CU and one's epilogue (128 KiB of
+// f32 results) runs beside the other's K loop.  A 256 x 256 tile with one
+// workgroup per CU left the matrix cores idle while its results were stored,
+// which at the dX's short K loop (K = d_out) was much of the time: the down
+// projection's dX took 357 against 308 us in 256 x 128 tiles, its dW 290 against
+// 264 us.  A stage holds one 128-element step: the A tile's 256 rows and the B
+// tile's 128 rows of 64 bytes as they lie in their code blocks (16 + 8 KiB), and
+// both operands' scale words; three stages (78 KiB a workgroup) form a ring in
+// which a step waits for its own stage and loads the step two ahead into the
+// slot of the step before, all moved global -> LDS by buffer-load DMA.
 // Operand lane layout of the FP4 MFMA (checked on the device): lane l holds row
 // (or column) l % 32 and K elements 32 (l / 32) .. + 31, 16 bytes, the first in
 // the low nibble; byte 0 of its scale register is that (row, K block)'s E8M0.
 // Output: lane l, register r -> row (r / 4) 8 + (l / 32) 4 + r % 4, column l % 32.
-constexpr int kMxStageBytes = 65536 + 4096;
-constexpr int kMxScaleA = 65536, kMxScaleB = 65536 + 2048;   // [step][row] words per operand
-// Two separate LDS objects rather than one indexed array: the compiler then
-// sees that a stage's LDS reads and the DMA filling the other stage touch
-// different memory, and does not drain every outstanding load before the reads.
+constexpr int kMxB = 16384, kMxSA = 24576, kMxSB = 25600, kMxSBSpare = 26112, kMxStageBytes = 26624;
+// Separate LDS objects rather than one indexed array: the compiler then sees that
+// a stage's LDS reads and the DMA filling another stage touch different memory,
+// and does not drain every outstanding load before the reads.
 __shared__ __attribute__((aligned(1024))) uint8_t g_mx0[kMxStageBytes];
 __shared__ __attribute__((aligned(1024))) uint8_t g_mx1[kMxStageBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t g_mx2[kMxStageBytes];
 template <int S>
 __device__ __forceinline__ uint8_t* mx_stage() {
   if constexpr (S == 0) return g_mx0;
-  else return g_mx1;
+  else if constexpr (S == 1) return g_mx1;
+  else return g_mx2;
 }
 
 struct MxGemm {
@@ -547,47 +552,48 @@ struct MxEpi {
   float* out; int64_t ld_out;
 };
 
-// LDS layout of a stage's A (and, 32 KiB on, B) tile: the two steps' 16 KiB blocks as they lie in
-// memory, [step][256 rows][64 bytes], with the four 16-byte chunks of a row at permuted positions:
-// chunk q of row r at position q ^ ((r >> 2) & 3), so the 16 rows of a quarter-wave's 16-byte read
-// hit 16 different bank groups.
+// LDS layout of a stage's A tile (and, 16 KiB on, B's): [rows][64 bytes] as in the step's code block,
+// with the four 16-byte chunks of a row at permuted positions: chunk q of row r at position
+// q ^ ((r >> 2) & 3), so the 16 rows of a quarter-wave's 16-byte read hit 16 different bank groups.
 __device__ __forceinline__ int mx_pos(int r, int q) { return q ^ ((r >> 2) & 3); }
 
-struct MxRsrc { __amdgpu_buffer_rsrc_t a, b, sa, sb, z; int nk, ns; };
+struct MxRsrc { __amdgpu_buffer_rsrc_t a, b, sa, sb, z; int nk; };
 
-// Stage ks (K elements 256 ks ..., code blocks 2 ks and 2 ks + 1 of the tile's 256-row block):
-// each wave moves 8 KiB of A and of B, eight 1 KiB pieces of 16 rows x 64 bytes (piece p: step
-// p >> 4, rows 16 (p & 15) ..; lane l lands at LDS offset 16 l of the piece and loads the chunk
-// that belongs there), and its 64 rows' scale words of both steps.  Past the last stage every load
-// goes through an empty descriptor (zeros); a step past K within the last stage loads zero scales
-// and codes that are never multiplied (its MFMAs are skipped).
-__device__ __forceinline__ void mx_load_stage(const MxGemm& g, uint8_t* st, int64_t m0, int64_t n0, int ks,
-                                              const MxRsrc& r) {
+// Step kt (K elements 128 kt .., code block kt of the tiles' 256-row blocks) into stage st.  Every
+// wave issues 8 loads: four 1 KiB pieces of A and two of B (16 rows x 64 bytes each; lane l lands at
+// LDS offset 16 l of its piece and loads the chunk that belongs there), 64 of A's 256 scale words,
+// and 64 of B's 128 (waves 2 and 3 load the same words as waves 0 and 1, into a spare copy, so the
+// wait counts are the same in every wave).  Past the last step every load reads zeros.
+__device__ __forceinline__ void mx_load(const MxGemm& g, uint8_t* st, int64_t m0, int64_t n0, int kt,
+                                        const MxRsrc& r) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const bool live = ks < r.ns;
+  const bool live = kt < r.nk;
   const __amdgpu_buffer_rsrc_t ra = live ? r.a : r.z, rb = live ? r.b : r.z;
-  const uint32_t a_blk = (uint32_t)((m0 >> 8) * g.lda), b_blk = (uint32_t)((n0 >> 8) * g.ldb);
+  const __amdgpu_buffer_rsrc_t rsa = live ? r.sa : r.z, rsb = live ? r.sb : r.z;
+  // A: the tile's 256-row block; B: the 128 rows from n0 of its 256-row block (n0 % 256 is 0 or 128,
+  // so a row's chunk permutation is the same counted from either)
+  const uint32_t a_blk = (uint32_t)((m0 >> 8) * g.lda), b_blk = (uint32_t)((n0 >> 8) * g.ldb + (n0 & 255) * 64);
+  const uint32_t koff = (uint32_t)kt * (uint32_t)kMxBlkBytes;
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int piece = wave * 8 + q;
-    const int step = piece >> 4;
-    const int row = (piece & 15) * 16 + (lane >> 2);
-    const uint32_t off = (uint32_t)(step * kMxBlkBytes + row * 64 + mx_pos(row, lane & 3) * 16);   // an involution
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(st + piece * 1024), 16, a_blk + off,
-                                             (uint32_t)ks * (2u * kMxBlkBytes), 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(st + 32768 + piece * 1024), 16, b_blk + off,
-                                             (uint32_t)ks * (2u * kMxBlkBytes), 0, 0);
+  for (int q = 0; q < 4; ++q) {
+    const int piece = wave * 4 + q;
+    const int row = piece * 16 + (lane >> 2);
+    const uint32_t off = (uint32_t)(row * 64 + mx_pos(row, lane & 3) * 16);   // an involution
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(st + piece * 1024), 16, a_blk + off, koff, 0, 0);
   }
 #pragma unroll
-  for (int sub = 0; sub < 2; ++sub) {
-    const int kt = 2 * ks + sub;
-    const bool lk = kt < r.nk;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(lk ? r.sa : r.z, (lds_void*)(st + kMxScaleA + sub * 1024 + wave * 256), 4,
-                                             (uint32_t)((m0 + wave * 64 + lane) * 4), (uint32_t)(kt * g.ldas), 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(lk ? r.sb : r.z, (lds_void*)(st + kMxScaleB + sub * 1024 + wave * 256), 4,
-                                             (uint32_t)((n0 + wave * 64 + lane) * 4), (uint32_t)(kt * g.ldbs), 0, 0);
+  for (int q = 0; q < 2; ++q) {
+    const int piece = wave * 2 + q;
+    const int row = piece * 16 + (lane >> 2);
+    const uint32_t off = (uint32_t)(row * 64 + mx_pos(row, lane & 3) * 16);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(st + kMxB + piece * 1024), 16, b_blk + off, koff, 0, 0);
   }
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void*)(st + kMxSA + wave * 256), 4,
+                                           (uint32_t)((m0 + wave * 64 + lane) * 4), (uint32_t)(kt * g.ldas), 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void*)(st + (wave < 2 ? kMxSB : kMxSBSpare) + (wave & 1) * 256),
+                                           4, (uint32_t)((n0 + (wave & 1) * 64 + lane) * 4), (uint32_t)(kt * g.ldbs),
+                                           0, 0);
 }
 
 // s_waitcnt: at most n vector-memory ops outstanding, no LDS ops.
@@ -596,10 +602,9 @@ __device__ __forceinline__ void mx_load_stage(const MxGemm& g, uint8_t* st, int6
 
 constexpr int kMxSgMfma = 0x008, kMxSgDsRead = 0x100, kMxSgVmem = 0x010;
 
-// Fragments of half-step h (0..3: K elements 64 h .. 64 h + 63 of the stage): lane l holds
-// rows (columns) i * 32 + l % 32 of its wave's 128, the 16 bytes of chunk 2 h + l / 32 of the
-// stage's row (chunk c in step c / 4).
-struct MxFrag { v8i a[4], b[4]; };
+// Fragments of half-step h (K elements 64 h .. 64 h + 63 of the step): lane l holds rows (columns)
+// i * 32 + l % 32 of its wave's, the 16 bytes of chunk 2 h + l / 32 of the row.
+struct MxFrag { v8i a[4], b[2]; };
 
 __device__ __forceinline__ void mx_read_frag(const uint8_t* st, int h, MxFrag& f) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -607,129 +612,81 @@ __device__ __forceinline__ void mx_read_frag(const uint8_t* st, int h, MxFrag& f
   const int r31 = lane & 31, c = h * 2 + (lane >> 5);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int ra_ = wm * 128 + i * 32 + r31, rb_ = wn * 128 + i * 32 + r31;
-    const int blk = (c >> 2) * kMxBlkBytes;
-    const uint4 x = *reinterpret_cast<const uint4*>(st + blk + ra_ * 64 + (mx_pos(ra_, c & 3) << 4));
-    const uint4 y = *reinterpret_cast<const uint4*>(st + 32768 + blk + rb_ * 64 + (mx_pos(rb_, c & 3) << 4));
+    const int ra_ = wm * 128 + i * 32 + r31;
+    const uint4 x = *reinterpret_cast<const uint4*>(st + ra_ * 64 + (mx_pos(ra_, c) << 4));
     f.a[i] = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
-    f.b[i] = v8i{(int)y.x, (int)y.y, (int)y.z, (int)y.w, 0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int rb_ = wn * 64 + j * 32 + r31;
+    const uint4 y = *reinterpret_cast<const uint4*>(st + kMxB + rb_ * 64 + (mx_pos(rb_, c) << 4));
+    f.b[j] = v8i{(int)y.x, (int)y.y, (int)y.z, (int)y.w, 0, 0, 0, 0};
   }
 }
 
-__device__ __forceinline__ void mx_read_scales(const uint8_t* st, int sub, uint32_t (&sa)[4], uint32_t (&sb)[4]) {
+__device__ __forceinline__ void mx_read_scales(const uint8_t* st, uint32_t (&sa)[4], uint32_t (&sb)[2]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int r31 = lane & 31;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    sa[i] = *reinterpret_cast<const uint32_t*>(st + kMxScaleA + sub * 1024 + (wm * 128 + i * 32 + r31) * 4);
-    sb[i] = *reinterpret_cast<const uint32_t*>(st + kMxScaleB + sub * 1024 + (wn * 128 + i * 32 + r31) * 4);
-  }
+  for (int i = 0; i < 4; ++i)
+    sa[i] = *reinterpret_cast<const uint32_t*>(st + kMxSA + (wm * 128 + i * 32 + r31) * 4);
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    sb[j] = *reinterpret_cast<const uint32_t*>(st + kMxSB + (wn * 64 + j * 32 + r31) * 4);
 }
 
-__device__ __forceinline__ void mx_mfma16(const MxFrag& f, const uint32_t (&sa)[4], const uint32_t (&sb)[4], int kk,
-                                          v16f (&acc)[4][4]) {
+__device__ __forceinline__ void mx_mfma8(const MxFrag& f, const uint32_t (&sa)[4], const uint32_t (&sb)[2], int kk,
+                                         v16f (&acc)[4][2]) {
   const int sh = 8 * (kk * 2 + ((threadIdx.x & 63) >> 5));
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
       acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], 4, 4, 0,
                                                                   (int)((sa[i] >> sh) & 0xFFu), 0,
                                                                   (int)((sb[j] >> sh) & 0xFFu));
 }
 
-// 16 MFMAs with NR LDS reads and NV buffer loads spread between them.
-template <int NR, int NV>
-__device__ __forceinline__ void mx_interleave() {
-#pragma unroll
-  for (int x = 0; x < 16; ++x) {
-    __builtin_amdgcn_sched_group_barrier(kMxSgMfma, 1, 0);
-    if (x < NR) __builtin_amdgcn_sched_group_barrier(kMxSgDsRead, 1, 0);
-    if (x < NV) __builtin_amdgcn_sched_group_barrier(kMxSgVmem, 1, 0);
-  }
-}
-
-// Stage ks on buffer S = ks % 2.  This wave's loads of it have landed (the wait) and the
-// barrier makes every wave's visible and retires the other buffer (read in the previous
-// stage), which is refilled with stage ks + 1 while this one feeds 4 x 16 MFMAs, each
-// group's fragments read during the previous group.  The second step's MFMAs are skipped
-// when it lies past K.
+// Step kt on stage S = kt % 3.  Its loads were issued two steps ago and step kt + 1's since; the wait
+// leaves those 8 in flight.  The barrier makes every wave's loads of step kt visible and retires step
+// kt - 1's stage, which takes step kt + 2.
 template <int S>
-__device__ __forceinline__ void mx_stage_step(const MxGemm& g, int64_t m0, int64_t n0, int ks, const MxRsrc& rs,
-                                              v16f (&acc)[4][4]) {
-  S3R_MX_WAIT_VM(0);
+__device__ __forceinline__ void mx_step(const MxGemm& g, int64_t m0, int64_t n0, int kt, const MxRsrc& rs,
+                                        v16f (&acc)[4][2]) {
+  S3R_MX_WAIT_VM(8);
   S3R_MX_WAIT_LGKM0();
   __builtin_amdgcn_s_barrier();
   const uint8_t* st = mx_stage<S>();
-  uint32_t sa0[4], sb0[4], sa1[4], sb1[4];
+  uint32_t sa[4], sb[2];
   MxFrag f0, f1;
   mx_read_frag(st, 0, f0);
-  mx_read_scales(st, 0, sa0, sb0);
-  mx_load_stage(g, mx_stage<S ^ 1>(), m0, n0, ks + 1, rs);
+  mx_read_scales(st, sa, sb);
+  mx_load(g, mx_stage<(S + 2) % 3>(), m0, n0, kt + 2, rs);
   mx_read_frag(st, 1, f1);
-  mx_read_scales(st, 1, sa1, sb1);
-  mx_mfma16(f0, sa0, sb0, 0, acc);
-  __builtin_amdgcn_sched_group_barrier(kMxSgDsRead, 16, 0);
-  mx_interleave<16, 10>();
-  mx_read_frag(st, 2, f0);
-  mx_mfma16(f1, sa0, sb0, 1, acc);
-  mx_interleave<8, 10>();
-  if (2 * ks + 1 < rs.nk) {
-    mx_read_frag(st, 3, f1);
-    mx_mfma16(f0, sa1, sb1, 0, acc);
-    mx_interleave<8, 0>();
-    mx_mfma16(f1, sa1, sb1, 1, acc);
+  mx_mfma8(f0, sa, sb, 0, acc);
+  mx_mfma8(f1, sa, sb, 1, acc);
+  // order: the loads of step kt + 2, the first half-step's 12 reads, then its 8 MFMAs each followed (the
+  // first six) by one fragment read of the second half-step, then the second half-step's MFMAs
+  __builtin_amdgcn_sched_group_barrier(kMxSgVmem, 8, 0);
+  __builtin_amdgcn_sched_group_barrier(kMxSgDsRead, 12, 0);
+#pragma unroll
+  for (int x = 0; x < 8; ++x) {
+    __builtin_amdgcn_sched_group_barrier(kMxSgMfma, 1, 0);
+    if (x < 6) __builtin_amdgcn_sched_group_barrier(kMxSgDsRead, 1, 0);
   }
+  __builtin_amdgcn_sched_group_barrier(kMxSgMfma, 8, 0);
 }
 
+// Epilogue of a tile: out = acc - correction, per-row values of the tile staged in LDS (two stages of
+// the ring, free now), per-column values in registers.
 template <bool DW, bool EC, int NB>
-__global__ __launch_bounds__(256, 1) void mx_gemm_kernel(MxGemm g, MxEpi ep) {
+__device__ __forceinline__ void mx_epilogue(const MxGemm& g, const MxEpi& ep, int64_t m0, int64_t n0,
+                                            v16f (&acc)[4][2]) {
+  constexpr int TN = 128;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  int bid = blockIdx.x;
-  const int nblocks = g.tiles_m * g.tiles_n;
-  if (nblocks % 8 == 0) bid = (bid % 8) * (nblocks / 8) + bid / 8;   // a contiguous range of tiles per XCD
-  const int group = 8 * g.tiles_n;
-  const int first_m = (bid / group) * 8;
-  const int gsz = min(g.tiles_m - first_m, 8);
-  const int tm = first_m + (bid % group) % gsz, tn = (bid % group) / gsz;
-  const int64_t m0 = (int64_t)tm * 256, n0 = (int64_t)tn * 256;
-  const int nk = (int)(g.K / 128);
-  // descriptors over whole operands, every 256-row block of codes (rows past M or N inside the last
-  // block reach only outputs that are not stored)
-  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)g.A, (short)0, (int)(uint32_t)(((g.M + 255) >> 8) * g.lda), kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)g.B, (short)0, (int)(uint32_t)(((g.N + 255) >> 8) * g.ldb), kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc((void*)g.As, (short)0, (int)(uint32_t)(nk * g.ldas), kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc((void*)g.Bs, (short)0, (int)(uint32_t)(nk * g.ldbs), kRsrcWord3);
-
-  v16f acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  // Stage 0 up front; each stage loads the next.  The stage count is rounded up to
-  // even (the two buffers' period): a stage past K multiplies zeros.
-  const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc((void*)g.A, (short)0, 0, kRsrcWord3);
-  const int ns = (int)((g.K + 255) / 256);
-  const MxRsrc rs{ra, rb, rsa, rsb, rz, nk, ns};
-  mx_load_stage(g, mx_stage<0>(), m0, n0, 0, rs);
-  for (int ks = 0; ks < ns; ks += 2) {
-    mx_stage_step<0>(g, m0, n0, ks, rs, acc);
-    mx_stage_step<1>(g, m0, n0, ks + 1, rs, acc);
-  }
-  S3R_MX_WAIT_VM(0);
-  S3R_MX_WAIT_LGKM0();
-  __builtin_amdgcn_s_barrier();
   const int r31 = lane & 31, hk = lane >> 5;
-
-  // epilogue: per-row values of the tile staged in LDS (the stages are free now),
-  // per-column values in registers
   float* s_rowc = reinterpret_cast<float*>(mx_stage<0>());            // dX: eps_t - mu_b; dW: ebar[b][row] (b-major)
   int* s_rowb = reinterpret_cast<int*>(mx_stage<1>());                // dX: the row's example, relative to the tile's first
   float* s_v = reinterpret_cast<float*>(mx_stage<1>() + 4096);        // dX: v[b0 + b][tile column], b < NB
@@ -748,8 +705,8 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_kernel(MxGemm g, MxEpi ep) {
     }
     if constexpr (!DW) {
       const int64_t nbt = min((int64_t)NB, ep.B - b_first);
-      for (int x = threadIdx.x; x < NB * 256; x += 256) {
-        const int b = x / 256, cc = x % 256;
+      for (int x = threadIdx.x; x < NB * TN; x += 256) {
+        const int b = x / TN, cc = x % TN;
         const int64_t n = n0 + cc;
         s_v[x] = (b < nbt && n < g.N) ? ep.vec[(b_first + b) * g.N + n] : 0.f;
       }
@@ -763,11 +720,11 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_kernel(MxGemm g, MxEpi ep) {
   // per-column values, loaded from a clamped column without a branch and waited for once here: a
   // load still pending inside the store loop would make each group of stores wait for every store
   // before it (vmcnt counts stores too)
-  float cA[4], cU[4], xsb[4][NB];
-  bool n_ok[4];
+  float cA[2], cU[2], xsb[2][NB];
+  bool n_ok[2];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int64_t n = n0 + wn * 128 + j * 32 + r31;
+  for (int j = 0; j < 2; ++j) {
+    const int64_t n = n0 + wn * 64 + j * 32 + r31;
     n_ok[j] = n < g.N;
     const int64_t nc = n_ok[j] ? n : 0;
     cA[j] = 0.f; cU[j] = 0.f;
@@ -805,15 +762,15 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_kernel(MxGemm g, MxEpi ep) {
         }
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < 2; ++j) {
         if (!n_ok[j]) continue;
-        const int cc = wn * 128 + j * 32 + r31;
+        const int cc = wn * 64 + j * 32 + r31;
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           float o = acc[i][j][rq * 4 + rr];
           if constexpr (EC) {
             if constexpr (!DW) {
-              o -= s_v[rb[rr] * 256 + cc] + rc[rr] * cA[j];
+              o -= s_v[rb[rr] * TN + cc] + rc[rr] * cA[j];
             } else {
               float t = cU[j];
 #pragma unroll
@@ -828,6 +785,49 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_kernel(MxGemm g, MxEpi ep) {
         }
       }
     }
+}
+
+template <bool DW, bool EC, int NB>
+__global__ __launch_bounds__(256, 2) void mx_gemm_kernel(MxGemm g, MxEpi ep) {
+  int bid = blockIdx.x;
+  const int nblocks = g.tiles_m * g.tiles_n;
+  if (nblocks % 8 == 0) bid = (bid % 8) * (nblocks / 8) + bid / 8;   // a contiguous range of tiles per XCD
+  const int group = 8 * g.tiles_n;
+  const int first_m = (bid / group) * 8;
+  const int gsz = min(g.tiles_m - first_m, 8);
+  const int tm = first_m + (bid % group) % gsz, tn = (bid % group) / gsz;
+  const int64_t m0 = (int64_t)tm * 256, n0 = (int64_t)tn * 128;
+  const int nk = (int)(g.K / 128);
+  // descriptors over whole operands, every 256-row block of codes (rows past M or N inside the last
+  // block reach only outputs that are not stored)
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)g.A, (short)0, (int)(uint32_t)(((g.M + 255) >> 8) * g.lda), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)g.B, (short)0, (int)(uint32_t)(((g.N + 255) >> 8) * g.ldb), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc((void*)g.As, (short)0, (int)(uint32_t)(nk * g.ldas), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc((void*)g.Bs, (short)0, (int)(uint32_t)(nk * g.ldbs), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc((void*)g.A, (short)0, 0, kRsrcWord3);
+  const MxRsrc rs{ra, rb, rsa, rsb, rz, nk};
+
+  v16f acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  mx_load(g, mx_stage<0>(), m0, n0, 0, rs);
+  mx_load(g, mx_stage<1>(), m0, n0, 1, rs);
+  for (int kt = 0; kt < nk; kt += 3) {
+    mx_step<0>(g, m0, n0, kt, rs, acc);
+    if (kt + 1 < nk) mx_step<1>(g, m0, n0, kt + 1, rs, acc);
+    if (kt + 2 < nk) mx_step<2>(g, m0, n0, kt + 2, rs, acc);
+  }
+  S3R_MX_WAIT_VM(0);
+  S3R_MX_WAIT_LGKM0();
+  __builtin_amdgcn_s_barrier();
+  mx_epilogue<DW, EC, NB>(g, ep, m0, n0, acc);
 }
 
 // ------------------------------------------------ correction products ----
@@ -1069,7 +1069,7 @@ void run_mx_gemm(const MxGemm& g, const MxEpi& ep, hipStream_t st) {
 
 MxGemm make_mx_gemm(const uint8_t* A, int64_t lda, const uint8_t* As, int64_t ldas, const uint8_t* B, int64_t ldb,
                     const uint8_t* Bs, int64_t ldbs, int64_t M, int64_t N, int64_t K) {
-  MxGemm g{A, lda, As, ldas, B, ldb, Bs, ldbs, M, N, K, (int)((M + 255) / 256), (int)((N + 255) / 256)};
+  MxGemm g{A, lda, As, ldas, B, ldb, Bs, ldbs, M, N, K, (int)((M + 255) / 256), (int)((N + 127) / 128)};
   return g;
 }
 
