@@ -842,12 +842,13 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmParams g, 
 // cores idle while its tile's 256 KiB of f32 results are stored.  Tiles of
 // 256 x 128 (four waves of 128 x 64, 128 accumulator registers) and a ring of
 // three 24 KiB stages let two workgroups share a CU, so one's epilogue runs
-// beside the other's K loop.  That pays where the epilogue weighs most: the
-// grouped (MoE) dW, whose K loops are an expert's rows, and a single dW whose
-// 256 x 256 tiles leave the last round of the CUs part-filled (there a lone
-// workgroup has its CU to itself).  It costs LDS bandwidth (a K step reads
-// 1.5x the operand bytes per multiply of the 256 x 256 tile), so the paired
-// gate / up dW, whose 1792 tiles of 256 x 256 fill whole rounds, stays there.
+// beside the other's K loop.  The grouped (MoE) dW, whose K loops are an
+// expert's rows, and every single dW run here (measured faster at the FFN
+// block's down projection, whose 896 tiles of 256 x 256 leave the last round of
+// the CUs half empty: here a lone workgroup of that round has its CU to
+// itself).  It costs LDS bandwidth (a K step reads 1.5x the operand bytes per
+// multiply of the 256 x 256 tile), so the paired gate / up dW, whose 1792 tiles
+// of 256 x 256 fill whole rounds, stays there.
 // A is laid out as in the 256 x 256 ring; B's k-rows are 128 bytes (8 chunks
 // of 16), chunk c of k-row r at position c ^ swz_n(r), swz_n(r) =
 // ((r >> 1) & 3) << 1: the 8 k-rows of a transpose read hold two k-rows per
