@@ -811,6 +811,35 @@ __global__ __launch_bounds__(kThreads) void swiglu_quantize_kernel(QuantTile pg,
 constexpr int kFinRows = 256;
 static_assert(kThreads / kWave == 4, "the finalize kernel's column blocks add four waves' sums");
 
+// Sums of partials in a fixed order: the n values p[0], p[stride], ... added one after another (fp64 for the
+// float partials), their loads issued eight at a time so that they are in flight together.
+__device__ __forceinline__ double sum_in_order(const float* __restrict__ p, int64_t stride, int n) {
+  double a = 0.0;
+  int k = 0;
+  for (; k + 8 <= n; k += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = p[(int64_t)(k + u) * stride];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) a += (double)v[u];
+  }
+  for (; k < n; ++k) a += (double)p[(int64_t)k * stride];
+  return a;
+}
+__device__ __forceinline__ int32_t sum_in_order(const int32_t* __restrict__ p, int64_t stride, int n) {
+  int32_t a = 0;
+  int k = 0;
+  for (; k + 8 <= n; k += 8) {
+    int32_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = p[(int64_t)(k + u) * stride];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) a += v[u];
+  }
+  for (; k < n; ++k) a += p[(int64_t)k * stride];
+  return a;
+}
+
 __global__ __launch_bounds__(kThreads) void finalize_kernel(
     int64_t B, int64_t D, int64_t S, int tiles_per_example, int n_ctiles, int per_token, int ncb,
     int blocks_per_example, const float* __restrict__ delta, const float* __restrict__ col_part,
@@ -830,11 +859,11 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(
     double a = 0.0;
     int32_t aq = 0;
     if (ok) {
-      for (int k = wave; k < tiles_per_example; k += kThreads / kWave) {
-        const int64_t at = (b * tiles_per_example + k) * D + j;
-        if (ec_col) a += (double)col_part[at];
-        if (code_colsum) aq += colq_part[at];
-      }
+      constexpr int kStep = kThreads / kWave;
+      const int n = wave < tiles_per_example ? (tiles_per_example - wave + kStep - 1) / kStep : 0;
+      const int64_t at = (b * tiles_per_example + wave) * D + j;
+      if (ec_col) a = sum_in_order(col_part + at, (int64_t)kStep * D, n);
+      if (code_colsum) aq = sum_in_order(colq_part + at, (int64_t)kStep * D, n);
     }
     csum[wave][lane] = a;
     qsum[wave][lane] = aq;
@@ -857,8 +886,7 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(
   const int64_t t = r0 + threadIdx.x;
   double eps = 0.0;
   if (t < r1) {
-    double a = 0.0;
-    for (int k = 0; k < n_ctiles; ++k) a += (double)row_part[t * n_ctiles + k];
+    const double a = sum_in_order(row_part + t * n_ctiles, 1, n_ctiles);
     const double d = per_token ? (double)delta[t] : (double)delta[0];
     eps = D > 0 ? a * d / (double)D : 0.0;
     ec_row[t] = (float)eps;
@@ -1018,10 +1046,9 @@ __global__ __launch_bounds__(kThreads) void grouped_finalize_kernel(
     const int k0 = ok ? gr.tiles64[e] : 0, k1 = ok ? gr.tiles64[e + 1] : 0;
     double a = 0.0;
     int32_t aq = 0;
-    for (int k = k0 + sub; k < k1; k += kFinLanes) {
-      if (ec_col) a += (double)col_part[(int64_t)k * D + j];
-      if (code_colsum) aq += colq_part[(int64_t)k * D + j];
-    }
+    const int cnt = k0 + sub < k1 ? (k1 - k0 - sub + kFinLanes - 1) / kFinLanes : 0;
+    if (ec_col) a = sum_in_order(col_part + (int64_t)(k0 + sub) * D + j, (int64_t)kFinLanes * D, cnt);
+    if (code_colsum) aq = sum_in_order(colq_part + (int64_t)(k0 + sub) * D + j, (int64_t)kFinLanes * D, cnt);
     for (int o = 1; o < kFinLanes; o <<= 1) {
       a += __shfl_xor(a, o, kWave);
       aq += __shfl_xor(aq, o, kWave);
@@ -1038,27 +1065,37 @@ __global__ __launch_bounds__(kThreads) void grouped_finalize_kernel(
   const int64_t t = (int64_t)(blockIdx.x - ncb) * kThreads + threadIdx.x;
   if (t >= R) return;
   const int e = row_group(gr.offsets, gr.G, t);
-  double a = 0.0;
-  for (int k = 0; k < n_ctiles; ++k) a += (double)row_part[t * n_ctiles + k];
+  const double a = sum_in_order(row_part + t * n_ctiles, 1, n_ctiles);
   const double d = per_token ? (double)delta[t] : (double)delta[e];
   ec_row[t] = D > 0 ? (float)(a * d / (double)D) : 0.f;
 }
 
-// ec_mean[e]: mean of the group's token means, one block per group, fixed order.
-// Nothing is read when the offsets were found invalid.
-__global__ __launch_bounds__(kThreads) void grouped_mean_kernel(const int64_t* __restrict__ offsets,
-                                                                const uint32_t* __restrict__ status,
-                                                                const float* __restrict__ ec_row,
-                                                                float* __restrict__ ec_mean) {
+// ec_mean[e]: mean of the group's token means, one block per group, in fp64, in a fixed order (each thread's
+// rows in four interleaved partial sums, so a thread's loads are in flight together, then a tree over the
+// block); 1024 threads, since the largest groups' rows are the kernel's time.  Nothing is read when the
+// offsets were found invalid.
+constexpr int kMeanThreads = 1024;
+__global__ __launch_bounds__(kMeanThreads) void grouped_mean_kernel(const int64_t* __restrict__ offsets,
+                                                                    const uint32_t* __restrict__ status,
+                                                                    const float* __restrict__ ec_row,
+                                                                    float* __restrict__ ec_mean) {
   const int64_t e = blockIdx.x;
   const bool ok = status[0] == 0;
   const int64_t a = ok ? offsets[e] : 0, b = ok ? offsets[e + 1] : 0;
-  double s = 0.0;
-  for (int64_t t = a + threadIdx.x; t < b; t += kThreads) s += (double)ec_row[t];
-  __shared__ double red[kThreads];
-  red[threadIdx.x] = s;
+  double p[4] = {0.0, 0.0, 0.0, 0.0};
+  int64_t t = a + threadIdx.x;
+  for (; t + 3 * kMeanThreads < b; t += 4 * kMeanThreads) {
+    float v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = ec_row[t + u * kMeanThreads];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) p[u] += (double)v[u];
+  }
+  for (int u = 0; t < b; t += kMeanThreads, ++u) p[u & 3] += (double)ec_row[t];
+  __shared__ double red[kMeanThreads];
+  red[threadIdx.x] = (p[0] + p[1]) + (p[2] + p[3]);
   __syncthreads();
-  for (int o = kThreads / 2; o > 0; o >>= 1) {
+  for (int o = kMeanThreads / 2; o > 0; o >>= 1) {
     if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
     __syncthreads();
   }
@@ -1238,7 +1275,7 @@ void run_grouped(const QuantArgs& a, const GroupedWs& L, const GroupArgs& gr, co
                        (const int32_t*)(a.ws + L.colq_part), (const float*)(a.ws + L.row_part),
                        a.ec ? a.ec_col : nullptr, a.code_colsum, a.ec_row);
     if (a.ec)
-      hipLaunchKernelGGL(grouped_mean_kernel, dim3((unsigned)gr.G), dim3(kThreads), 0, st, gr.offsets, status,
+      hipLaunchKernelGGL(grouped_mean_kernel, dim3((unsigned)gr.G), dim3(kMeanThreads), 0, st, gr.offsets, status,
                          a.ec_row, a.ec_mean);
   }
 }
