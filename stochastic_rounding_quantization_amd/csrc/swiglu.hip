@@ -134,7 +134,21 @@ __global__ __launch_bounds__(256) void swiglu_amax_finalize_kernel(const uint32_
   __shared__ uint32_t red[2][4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t m[2] = {0u, 0u};
-  for (int i = threadIdx.x; i < nblk; i += 256) {
+  int i = threadIdx.x;
+  for (; i + 7 * 256 < nblk; i += 8 * 256) {       // eight loads of each array in flight together
+    uint32_t a[8], b[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      a[u] = part[i + u * 256];
+      b[u] = part[nblk + i + u * 256];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      m[0] = max(m[0], a[u]);
+      m[1] = max(m[1], b[u]);
+    }
+  }
+  for (; i < nblk; i += 256) {
     m[0] = max(m[0], part[i]);
     m[1] = max(m[1], part[nblk + i]);
   }
