@@ -1205,6 +1205,79 @@ __global__ __launch_bounds__(kGvThreads) void gemv_partial_kernel(
   }
 }
 
+// The dense VEC-mode GEMV of up to four vectors (the examples' channel means ebar_b against the weight codes,
+// the dX correction's v_b) on the matrix cores: its multiply-adds (four per weight byte) otherwise issue as
+// many VALU instructions as the whole band takes to load.  v_mfma_f32_4x4x1f32 runs 16 blocks of a 4 x 4
+// outer product: D[i][j] of block k / 4 is lane 4 (k / 4) + j, register i, its A[i] from lane 4 (k / 4) + i
+// and its B[j] from lane k.  With A = the four coefficients of one row (lane m holds vector m % 4) and B =
+// lane l's weight of that row in one of its 8 columns, register b of accumulator c holds vector b at the
+// lane's column c.  Same blocks, bands, partial sums and reduction as gemv_partial_kernel.
+typedef float v4f_t __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(kGvThreads) void gemv_mfma_kernel(const int8_t* __restrict__ P, int64_t ld, int64_t K,
+                                                              int64_t N, int64_t nb, const float* __restrict__ C,
+                                                              float* __restrict__ part) {
+  __shared__ float red[4][4][kGvCols];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t n0 = (int64_t)blockIdx.x * kGvCols + lane * kGvColsPerLane;
+  const int64_t k0 = (int64_t)blockIdx.y * kGvRows;
+  const int rows = (int)min((int64_t)kGvRows, K - k0);
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(P + k0 * ld), (short)0, (int)((uint32_t)rows * (uint32_t)ld), kRsrcWord3);
+  const uint32_t voff = (uint32_t)n0;
+  uint2 mask = make_uint2(0xFFFFFFFFu, 0xFFFFFFFFu);
+  if (n0 + kGvColsPerLane > N) {
+    const int64_t keep = max((int64_t)0, N - n0);
+    mask.x = keep >= 4 ? 0xFFFFFFFFu : (uint32_t)((1ull << (8 * keep)) - 1);
+    mask.y = keep >= 8 ? 0xFFFFFFFFu : keep <= 4 ? 0u : (uint32_t)((1ull << (8 * (keep - 4))) - 1);
+  }
+  for (int64_t b0 = 0; b0 < nb; b0 += 4) {
+    uint2 u[kGvRowsPerWave];
+#pragma unroll
+    for (int i = 0; i < kGvRowsPerWave; ++i) {
+      // rows past the band repeat its last row; their coefficients are 0
+      const uint32_t soff = (uint32_t)min(wave + 4 * i, rows - 1) * (uint32_t)ld;
+      const auto w = __builtin_amdgcn_raw_buffer_load_b64(rsrc, voff, soff, 0);
+      u[i] = make_uint2(w[0], w[1]);
+    }
+    // lane m: vector b0 + m % 4 at this wave's row i = m / 4 (row wave + 4 i of the band)
+    float cf = 0.f;
+    {
+      const int b = lane & 3, r = wave + 4 * (lane >> 2);
+      if (r < rows && b0 + b < nb) cf = C[(b0 + b) * K + k0 + r];
+    }
+    v4f_t acc[kGvColsPerLane];
+#pragma unroll
+    for (int c = 0; c < kGvColsPerLane; ++c) acc[c] = v4f_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < kGvRowsPerWave; ++i) {
+      // A: lane m takes the coefficient of vector m % 4 at row i (from lane 4 i + m % 4)
+      const float a = __builtin_bit_cast(
+          float, __builtin_amdgcn_ds_bpermute((4 * i + (lane & 3)) * 4, __builtin_bit_cast(int, cf)));
+      const uint32_t w[2] = {u[i].x & mask.x, u[i].y & mask.y};
+#pragma unroll
+      for (int c = 0; c < kGvColsPerLane; ++c) {
+        const float x = (float)(int8_t)(w[c >> 2] >> (8 * (c & 3)));
+        acc[c] = __builtin_amdgcn_mfma_f32_4x4x1f32(a, x, acc[c], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int c = 0; c < kGvColsPerLane; ++c) red[wave][b][lane * kGvColsPerLane + c] = acc[c][b];
+    __syncthreads();
+    for (int i = threadIdx.x; i < 4 * kGvCols; i += kGvThreads) {
+      const int b = i / kGvCols, c = i % kGvCols;
+      const int64_t n = (int64_t)blockIdx.x * kGvCols + c;
+      if (b0 + b < nb && n < N) {
+        const float v = ((red[0][b][c] + red[1][b][c]) + red[2][b][c]) + red[3][b][c];
+        part[((int64_t)blockIdx.y * nb + b0 + b) * N + n] = v;
+      }
+    }
+    __syncthreads();                              // red is reused by the next pass
+  }
+}
+
 __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i < n) p[i] = 0.f;
@@ -1252,8 +1325,7 @@ hipError_t run_gemv(const int8_t* P, int64_t ld, int64_t K, int64_t N, int64_t n
     hipLaunchKernelGGL(gemv_partial_kernel<1>, grid, dim3(kGvThreads), 0, st, P, ld, K, N, nb, token_mode, C, ec_row,
                        ec_mean, S, part, (int64_t)0, (const int64_t*)nullptr, (const int32_t*)nullptr, (int64_t)0);
   else
-    hipLaunchKernelGGL(gemv_partial_kernel<4>, grid, dim3(kGvThreads), 0, st, P, ld, K, N, nb, token_mode, C, ec_row,
-                       ec_mean, S, part, (int64_t)0, (const int64_t*)nullptr, (const int32_t*)nullptr, (int64_t)0);
+    hipLaunchKernelGGL(gemv_mfma_kernel, grid, dim3(kGvThreads), 0, st, P, ld, K, N, nb, C, part);
   const int64_t count = nb * N;
   hipLaunchKernelGGL(gemv_reduce_kernel, dim3((unsigned)((count + 63) / 64)), dim3(256), 0, st, part, nbands, count,
                      out);
