@@ -943,6 +943,101 @@ __global__ __launch_bounds__(256) void mx_rowdot_kernel(const uint8_t* __restric
   }
 }
 
+// The four-example product (nb <= 4) on the matrix cores.  Block (x, y) takes rows 4 G x .. 4 G x + 4 G - 1
+// (G groups of four) and K chunk y, wave w the chunk's quarter w (512 elements), in which lane l = 4 j + i
+// takes the 32-element block j.  The lane carries, as the A operand of v_mfma_f32_4x4x1f32, coefficient
+// row i over its block (registers, read once for all groups) and, as the B operand, the decoded codes of
+// row i of the current group over the same block.  The instruction forms, in each group of four lanes, the
+// outer product D[4 j + c][r] = A(4 j + r) B(4 j + c), so after the block's 32 elements the lane's four
+// accumulators hold the products of its row with the four coefficient rows, counted in halves; the
+// block scale / 2 multiplies them.  Fixed order: the two interleaved accumulator chains (even and odd
+// elements), a reduce-scatter over the 16 blocks of the wave, the four quarters of the chunk in wave
+// order, and mx_sum_parts over the chunks.
+typedef float v4f __attribute__((ext_vector_type(4)));
+constexpr int kRdQuarter = kRdChunk / 4;
+
+template <int G>
+__global__ __launch_bounds__(256) void mx_rowdot4_mfma_kernel(const uint8_t* __restrict__ P, int64_t ldp,
+                                                              const uint8_t* __restrict__ Ps, int64_t ldps,
+                                                              int64_t N, int64_t K, int nb,
+                                                              const float* __restrict__ coef,
+                                                              float* __restrict__ part) {
+  __shared__ float red[4][G * 16];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i = lane & 3;
+  const int64_t k = (int64_t)blockIdx.y * kRdChunk + wave * kRdQuarter + (lane >> 2) * 32;
+  const bool kv = k < K;
+  float cf[32];
+  {
+    const float* src = coef + (int64_t)i * K + k;
+    if (i < nb && k + 32 <= K && ((uintptr_t)src & 15u) == 0) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float4 v = reinterpret_cast<const float4*>(src)[q];
+        cf[4 * q] = v.x; cf[4 * q + 1] = v.y; cf[4 * q + 2] = v.z; cf[4 * q + 3] = v.w;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 32; ++e) cf[e] = i < nb && k + e < K ? src[e] : 0.f;
+    }
+  }
+  // every group's codes loaded before any is used (rows past N re-read row N - 1; their sums are not stored)
+  uint4 wr[G];
+  int sbr[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const int64_t n = min(((int64_t)blockIdx.x * G + g) * 4 + i, N - 1);
+    wr[g] = kv ? *reinterpret_cast<const uint4*>(P + mx_code_off(n, k / 2, ldp)) : make_uint4(0u, 0u, 0u, 0u);
+    sbr[g] = kv ? (int)Ps[(k / 128) * ldps + n * 4 + ((k / 32) & 3)] : 127;
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const uint32_t wv[4] = {wr[g].x, wr[g].y, wr[g].z, wr[g].w};
+    v4f a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int wi = 0; wi < 4; ++wi) {
+      // byte s of word wi: elements 8 wi + 2 s (low nibble) and 8 wi + 2 s + 1, as exact halves
+      const v2f p[4] = {__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wv[wi], 2.f, 0),
+                        __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wv[wi], 2.f, 1),
+                        __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wv[wi], 2.f, 2),
+                        __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wv[wi], 2.f, 3)};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        a0 = __builtin_amdgcn_mfma_f32_4x4x1f32(cf[8 * wi + 2 * s], p[s].x, a0, 0, 0, 0);
+        a1 = __builtin_amdgcn_mfma_f32_4x4x1f32(cf[8 * wi + 2 * s + 1], p[s].y, a1, 0, 0, 0);
+      }
+    }
+    const float half_scale = __builtin_ldexpf(1.f, sbr[g] - 128);
+    float v[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] = (a0[r] + a1[r]) * half_scale;
+    // lane bit 5 splits the four sums in pairs, bit 4 within the pair (the lane keeps example lane >> 4),
+    // then bits 3 and 2 finish the sum over the wave's 16 blocks
+    {
+      const bool hi = lane & 32;
+      const float s0 = hi ? v[0] : v[2], s1 = hi ? v[1] : v[3];
+      v[0] = (hi ? v[2] : v[0]) + __shfl_xor(s0, 32, 64);
+      v[1] = (hi ? v[3] : v[1]) + __shfl_xor(s1, 32, 64);
+    }
+    {
+      const bool hi = lane & 16;
+      const float s0 = hi ? v[0] : v[1];
+      v[0] = (hi ? v[1] : v[0]) + __shfl_xor(s0, 16, 64);
+    }
+    float t = v[0];
+    t += __shfl_xor(t, 8, 64);
+    t += __shfl_xor(t, 4, 64);
+    if ((lane & 12) == 0) red[wave][g * 16 + (lane >> 4) * 4 + i] = t;
+  }
+  __syncthreads();
+  if (threadIdx.x < G * 16) {
+    const int x = threadIdx.x, g = x >> 4, r = (x >> 2) & 3, c = x & 3;
+    const float s = red[0][x] + red[1][x] + red[2][x] + red[3][x];
+    const int64_t n = ((int64_t)blockIdx.x * G + g) * 4 + c;
+    if (r < nb && n < N) part[((int64_t)blockIdx.y * 4 + r) * N + n] = s;
+  }
+}
+
 // dW correction terms of examples 8 .. B-1 (the GEMM epilogue applies examples 0 .. 7):
 // dW[j][n] -= sum_b ebar_b[j] * xs_b[n].
 __global__ __launch_bounds__(256) void mx_dw_rank_update_kernel(float* __restrict__ dW, int64_t ld, int64_t D,
@@ -1091,11 +1186,17 @@ void run_rowdot(const MxBwArgs& a, int64_t N, int64_t K, int nb, const float* co
                 hipStream_t st) {
   const int nkc = (int)((K + kRdChunk - 1) / kRdChunk);
   float* dst = nkc == 1 ? out : part;
-  constexpr int RPW = 4;                               // 16 rows per group, each wave's loads in flight together
-  constexpr int RG = 1;                                // one group per block: 16 rows (4 or 2 groups: 16-20 % slower)
-  hipLaunchKernelGGL((mx_rowdot_kernel<NB, RPW, RG>),
-                     dim3((unsigned)((N + 4 * RPW * RG - 1) / (4 * RPW * RG)), (unsigned)nkc), dim3(256), 0, st,
-                     a.B, a.ldb, a.Bs, a.ldbs, N, K, nb, coef, dst);
+  if constexpr (NB == 4) {
+    constexpr int G = 8;                               // 32 rows per block (16: same time)
+    hipLaunchKernelGGL((mx_rowdot4_mfma_kernel<G>), dim3((unsigned)((N + 4 * G - 1) / (4 * G)), (unsigned)nkc),
+                       dim3(256), 0, st, a.B, a.ldb, a.Bs, a.ldbs, N, K, nb, coef, dst);
+  } else {
+    constexpr int RPW = 4;                             // 16 rows per group, each wave's loads in flight together
+    constexpr int RG = 1;                              // one group per block: 16 rows (4 or 2 groups: 16-20 % slower)
+    hipLaunchKernelGGL((mx_rowdot_kernel<NB, RPW, RG>),
+                       dim3((unsigned)((N + 4 * RPW * RG - 1) / (4 * RPW * RG)), (unsigned)nkc), dim3(256), 0, st,
+                       a.B, a.ldb, a.Bs, a.ldbs, N, K, nb, coef, dst);
+  }
   if (nkc > 1)
     hipLaunchKernelGGL(mx_sum_parts_kernel, dim3((unsigned)((nb * N + 255) / 256)), dim3(256), 0, st, N, nb, NB, nkc,
                        (const float*)part, out);
