@@ -103,9 +103,12 @@ def test_mx_small_f32_modes(mode, ec):
     assert_rows_close(host(gpu["dW"]), ref["dW"], TOL, "mx dW")
 
 
-@pytest.mark.parametrize("T,D,d_in,S", [(384, 256, 40, 128), (768, 640, 600, 256), (512, 128, 520, 512)])
+@pytest.mark.parametrize("T,D,d_in,S", [(384, 256, 40, 128), (768, 640, 600, 256), (512, 128, 520, 512),
+                                         (256, 2304, 100, 128)])
 def test_mx_tiles_and_tails_bf16(T, D, d_in, S):
-    # partial 256-row tiles (T = 384), several tiles both ways, outlier tokens
+    # partial 256-row tiles (T = 384), several tiles both ways, outlier tokens; D = 2304 gives the v
+    # correction product one whole 2048-element chunk and a partial one (8 of 64 blocks), d_in = 100 a
+    # partial group of 32 rows
     inp = _problem(T, D, d_in, "bf16", 2, outliers=3)
     gpu = gpu_mx(inp, mode=oq.S3R, ec=oq.EC_TWO_WAY, S=S, seed=11)
     ref = mx.backward(_f32(inp, "G"), _f32(inp, "X"), _f32(inp, "W"), mode=oq.S3R, ec=oq.EC_TWO_WAY,
