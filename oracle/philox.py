@@ -4,7 +4,7 @@ Generator: Philox4x32 with 10 rounds, the counter-based generator of Salmon,
 Moraes, Dror and Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3" (SC'11),
 which the S3R page cites as its reference [16] beside Threefry (Related Work,
 "The Cost of Randomness": each random word is a keyed function of a counter).
-The pages use partitionable Threefry; this build uses Philox4x32-10 with its
+The pages use partitionable Threefry; this oracle (like the kernels) uses Philox4x32-10 with its
 own counter layout, so thresholds are a pure function of (seed, layer, index)
 and do not depend on how the work is split.
 
