@@ -512,8 +512,9 @@ size_t s3r_mx_operand_workspace(int64_t rows, int64_t cols) {
 
 size_t s3r_mx_workspace(const s3r_qdesc* d, int64_t d_in) {
   if (check_mx_desc(d) != S3R_OK || d_in < 0) return 0;
-  return std::max(mx_quant_workspace(d->rows, d->cols, d->ec != S3R_EC_NONE),
-                  mx_backward_workspace(d->rows, d->cols, d_in, d->rows / d->rows_per_example));
+  // at least one 256-byte block: every MX call takes a non-null, aligned ws, also where it uses none
+  return std::max({mx_quant_workspace(d->rows, d->cols, d->ec != S3R_EC_NONE),
+                   mx_backward_workspace(d->rows, d->cols, d_in, d->rows / d->rows_per_example), (size_t)256});
 }
 
 // Codes of an MXFP4 matrix in the 256-row block layout: ld (bytes between 256-row blocks) a multiple

@@ -849,6 +849,7 @@ template <int NB, int RPW, int RG>
 __global__ __launch_bounds__(256) void mx_rowdot_kernel(const uint8_t* __restrict__ P, int64_t ldp,
                                                         const uint8_t* __restrict__ Ps, int64_t ldps, int64_t N,
                                                         int64_t K, int nb, const float* __restrict__ coef,
+                                                        const float* __restrict__ mean, int64_t S,
                                                         float* __restrict__ part) {
   constexpr int V = RPW * NB;                           // sums per wave
   static_assert(V == 4 || V == 8 || V == 16 || V == 32, "reduce-scatter shape");
@@ -869,6 +870,13 @@ __global__ __launch_bounds__(256) void mx_rowdot_kernel(const uint8_t* __restric
         v.y = kc + e + 1 < K ? src[1] : 0.f;
         v.z = kc + e + 2 < K ? src[2] : 0.f;
         v.w = kc + e + 3 < K ? src[3] : 0.f;
+      }
+      if (mean) {                                       // per-token coefficients c_t = eps_t - mu_(t / S)
+        const int64_t t = kc + e;
+        if (t < K) v.x -= mean[t / S];
+        if (t + 1 < K) v.y -= mean[(t + 1) / S];
+        if (t + 2 < K) v.z -= mean[(t + 2) / S];
+        if (t + 3 < K) v.w -= mean[(t + 3) / S];
       }
     }
     s_c[b][(e & 31) >> 2][e >> 5] = v;
@@ -1062,13 +1070,6 @@ __global__ void mx_sum_parts_kernel(int64_t N, int nb, int NB, int nkc, const fl
   out[x] = s;
 }
 
-// c[t] = ec_row[t] - ec_mean[t / S]
-__global__ void mx_token_coef_kernel(int64_t T, int64_t S, const float* __restrict__ ec_row,
-                                     const float* __restrict__ ec_mean, float* __restrict__ c) {
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (t < T) c[t] = ec_row[t] - ec_mean[t / S];
-}
-
 }  // namespace
 
 // ------------------------------------------------------------- launchers ----
@@ -1172,18 +1173,18 @@ MxGemm make_mx_gemm(const uint8_t* A, int64_t lda, const uint8_t* As, int64_t ld
 
 size_t mx_quant_workspace(int64_t T, int64_t D, int ec) { return mx_quant_ws(T, D, ec != 0).total; }
 size_t mx_operand_workspace(int64_t R, int64_t C) { return align_up((size_t)(R / 32) * C * 4, 256); }
-// Backward workspace: v [B x d_in] (dX) | coef [T] and u [d_in] (dW) | the GEMVs' chunk partials.
+// Backward workspace: v [B x d_in] (dX) | u [d_in] (dW) | the correction products' chunk partials.
 size_t mx_backward_workspace(int64_t T, int64_t D, int64_t d_in, int64_t B) {
   const int64_t parts = max(((D + kRdChunk - 1) / kRdChunk) * 4, (T + kRdChunk - 1) / kRdChunk);
-  return align_up((size_t)B * d_in * 4, 256) + align_up((size_t)T * 4, 256) +
-         align_up((size_t)d_in * 4, 256) + align_up((size_t)parts * d_in * 4, 256);
+  return align_up((size_t)B * d_in * 4, 256) + align_up((size_t)d_in * 4, 256) +
+         align_up((size_t)parts * d_in * 4, 256);
 }
 
 namespace {
 // coef [nb x K] (row stride K) against the rows of P [N x K] into out [nb x N], NB <= 4 or 1.
 template <int NB>
 void run_rowdot(const MxBwArgs& a, int64_t N, int64_t K, int nb, const float* coef, float* out, float* part,
-                hipStream_t st) {
+                hipStream_t st, const float* mean = nullptr, int64_t S = 1) {
   const int nkc = (int)((K + kRdChunk - 1) / kRdChunk);
   float* dst = nkc == 1 ? out : part;
   if constexpr (NB == 4) {
@@ -1195,7 +1196,7 @@ void run_rowdot(const MxBwArgs& a, int64_t N, int64_t K, int nb, const float* co
     constexpr int RG = 1;                              // one group per block: 16 rows (4 or 2 groups: 16-20 % slower)
     hipLaunchKernelGGL((mx_rowdot_kernel<NB, RPW, RG>),
                        dim3((unsigned)((N + 4 * RPW * RG - 1) / (4 * RPW * RG)), (unsigned)nkc), dim3(256), 0, st,
-                       a.B, a.ldb, a.Bs, a.ldbs, N, K, nb, coef, dst);
+                       a.B, a.ldb, a.Bs, a.ldbs, N, K, nb, coef, mean, S, dst);
   }
   if (nkc > 1)
     hipLaunchKernelGGL(mx_sum_parts_kernel, dim3((unsigned)((nb * N + 255) / 256)), dim3(256), 0, st, N, nb, NB, nkc,
@@ -1204,8 +1205,7 @@ void run_rowdot(const MxBwArgs& a, int64_t N, int64_t K, int nb, const float* co
 
 float* mx_parts(const MxBwArgs& a) {
   const int64_t B = a.T / a.S;
-  return (float*)(a.ws + align_up((size_t)B * a.d_in * 4, 256) + align_up((size_t)a.T * 4, 256) +
-                  align_up((size_t)a.d_in * 4, 256));
+  return (float*)(a.ws + align_up((size_t)B * a.d_in * 4, 256) + align_up((size_t)a.d_in * 4, 256));
 }
 }  // namespace
 
@@ -1241,12 +1241,10 @@ hipError_t launch_mx_backward_dw(const MxBwArgs& a, hipStream_t st) {
   MxEpi ep{};
   ep.S = a.S; ep.B = B; ep.out = a.out; ep.ld_out = a.ld_out;
   if (a.ec) {
-    float* coef = (float*)(a.ws + align_up((size_t)B * a.d_in * 4, 256));
-    float* u = (float*)(a.ws + align_up((size_t)B * a.d_in * 4, 256) + align_up((size_t)a.T * 4, 256));
-    hipLaunchKernelGGL(mx_token_coef_kernel, dim3((unsigned)((a.T + 255) / 256)), dim3(256), 0, st, a.T, a.S,
-                       a.ec_row, a.ec_mean, coef);
-    // u[i] = sum_t (eps_t - mu_b) dq(X)[t][i]: rows of the K-major Xt [d_in x T]
-    run_rowdot<1>(a, a.d_in, a.T, 1, coef, u, mx_parts(a), st);
+    float* u = (float*)(a.ws + align_up((size_t)B * a.d_in * 4, 256));
+    // u[i] = sum_t (eps_t - mu_b) dq(X)[t][i]: rows of the K-major Xt [d_in x T], the coefficients formed
+    // as they are staged
+    run_rowdot<1>(a, a.d_in, a.T, 1, a.ec_row, u, mx_parts(a), st, a.ec_mean, a.S);
     ep.ebar = a.ec_col; ep.xs = a.vcol; ep.u = u;
   }
   // dW [D x d_in] = Qt [D x T] . Xt [d_in x T]^T
