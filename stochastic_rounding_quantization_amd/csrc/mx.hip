@@ -856,6 +856,20 @@ __global__ __launch_bounds__(256) void mx_rowdot_kernel(const uint8_t* __restric
   __shared__ float4 s_c[NB][8][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t kc = (int64_t)blockIdx.y * kRdChunk;
+  const int64_t k = kc + lane * 32;
+  const bool kv = k < K;
+  // every row of the block's RG groups loaded first, their latency overlapping the staging (rows past N
+  // re-read row N - 1; their sums are not stored)
+  uint4 wr[RG][RPW];
+  int sbr[RG][RPW];
+#pragma unroll
+  for (int g = 0; g < RG; ++g)
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      const int64_t n = min((((int64_t)blockIdx.x * RG + g) * 4 + wave) * RPW + r, N - 1);
+      wr[g][r] = kv ? *reinterpret_cast<const uint4*>(P + mx_code_off(n, k / 2, ldp)) : make_uint4(0u, 0u, 0u, 0u);
+      sbr[g][r] = kv ? (int)Ps[(k / 128) * ldps + n * 4 + ((k / 32) & 3)] : 127;
+    }
   // the chunk's coefficients, staged once for the block's RG row groups: elements e .. e+3 of
   // example b go to s_c[b][(e % 32) / 4][e / 32], one float4
   for (int x = threadIdx.x; x < NB * (kRdChunk / 4); x += 256) {
@@ -872,30 +886,18 @@ __global__ __launch_bounds__(256) void mx_rowdot_kernel(const uint8_t* __restric
         v.w = kc + e + 3 < K ? src[3] : 0.f;
       }
       if (mean) {                                       // per-token coefficients c_t = eps_t - mu_(t / S)
-        const int64_t t = kc + e;
-        if (t < K) v.x -= mean[t / S];
-        if (t + 1 < K) v.y -= mean[(t + 1) / S];
-        if (t + 2 < K) v.z -= mean[(t + 2) / S];
-        if (t + 3 < K) v.w -= mean[(t + 3) / S];
+        const int64_t t = kc + e, q = t / S, r = t - q * S;  // one division; t + i crosses into q + 1 at most
+        const float m0 = t < K ? mean[q] : 0.f;
+        const float m1 = r + 3 >= S && t + (S - r) < K ? mean[q + 1] : m0;   // t + S - r: example q + 1's first
+        if (t < K) v.x -= m0;
+        if (t + 1 < K) v.y -= r + 1 < S ? m0 : m1;
+        if (t + 2 < K) v.z -= r + 2 < S ? m0 : m1;
+        if (t + 3 < K) v.w -= r + 3 < S ? m0 : m1;
       }
     }
     s_c[b][(e & 31) >> 2][e >> 5] = v;
   }
   __syncthreads();
-  const int64_t k = kc + lane * 32;
-  const bool kv = k < K;
-  // every row of the block's RG groups loaded before any is used (rows past N re-read row N - 1;
-  // their sums are not stored)
-  uint4 wr[RG][RPW];
-  int sbr[RG][RPW];
-#pragma unroll
-  for (int g = 0; g < RG; ++g)
-#pragma unroll
-    for (int r = 0; r < RPW; ++r) {
-      const int64_t n = min((((int64_t)blockIdx.x * RG + g) * 4 + wave) * RPW + r, N - 1);
-      wr[g][r] = kv ? *reinterpret_cast<const uint4*>(P + mx_code_off(n, k / 2, ldp)) : make_uint4(0u, 0u, 0u, 0u);
-      sbr[g][r] = kv ? (int)Ps[(k / 128) * ldps + n * 4 + ((k / 32) & 3)] : 127;
-    }
 #pragma unroll
   for (int g = 0; g < RG; ++g) {
     const int64_t n0 = (((int64_t)blockIdx.x * RG + g) * 4 + wave) * RPW;
